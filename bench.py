@@ -1,0 +1,223 @@
+"""Benchmark of the gated delta-rule forward engine on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one dn_chunk_fwd call (the fused chunked forward: gains, intra-chunk
+products, triangular solve, output and state propagation) over the KLA bf16
+workload B=8, H=16, T=4096, d_k=d_v=128, C=64, inputs resident in HBM.
+`value` is tokens/s (B*T tokens per call).  The same line also reports the
+PGDN and diagonal-KDN forwards and the batched decode step (HBM GB/s), the
+roofline of the chunked-forward kernel, and the fp64 oracle timed on a
+bounded sample on the host CPU.
+"""
+import argparse
+import json
+import os
+import resource
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix (256 CU x 2.4 GHz x 4096 flop/clk)
+METRIC = "delta-rule fwd tokens/s + %MFMA peak (T=4096,d=128); decode GB/s vs HBM peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def chunk_bytes(wl):
+    """Algorithmic HBM bytes of one chunked forward: every input read once,
+    every output written once (q, k, v, o, gates, S0, S_T, aux)."""
+    es = 2 if wl.io == "bf16" else 4
+    ht = wl.B * wl.H * wl.T
+    per_ht = es * (2 * wl.dk + 2 * wl.dv)  # q, k, v, o
+    if wl.decay == "scalar":
+        per_ht += 4  # alpha
+    else:
+        per_ht += es * wl.dk
+    per_ht += {"kla": 4, "gdn": 4, "pgdn": 12, "kdn": 4 + es * wl.dk, "explicit": es * wl.dk}[wl.gain]
+    state = 2 * wl.B * wl.H * wl.dk * wl.dv * 4
+    aux = 2 * wl.B * wl.H * wl.dk * 4 if wl.gain in ("pgdn", "kdn") else 0
+    return ht * per_ht + state + aux
+
+
+def chunk_flops(wl):
+    """Counted flops of the chunk form per head-token (dense C x C products and
+    a forward-substitution solve): 6 dk dv + 4 C dk + 3 C dv."""
+    return wl.B * wl.H * wl.T * (6 * wl.dk * wl.dv + 4 * wl.C * wl.dk + 3 * wl.C * wl.dv)
+
+
+def decode_bytes(dwl):
+    """Per step: read + write S, read q, k, v (bf16) and eta, alpha, write o."""
+    nh = dwl.N * dwl.H
+    return nh * (2 * dwl.dk * dwl.dv * 4 + 2 * (2 * dwl.dk + dwl.dv) + 8 + 2 * dwl.dv)
+
+
+def time_chunk(wl, steps, warmup):
+    import torch
+    from recurrent_sequence_mixer_amd import dn
+    from recurrent_sequence_mixer_amd import workloads as W
+    t0 = time.time()
+    inp = W.generate(wl)
+    t = dn.to_device(inp, torch.bfloat16 if wl.io == "bf16" else torch.float32)
+    log(f"[bench] {wl.name}: inputs ready in {time.time() - t0:.1f}s")
+    gates = {n: t[n] for n in ("alpha", "eta", "alphaP", "betaP", "mu_log", "omega", "r") if n in t}
+    o = torch.empty_like(t["v"])
+    S = torch.empty_like(t["S0"])
+    aux = torch.empty((wl.B, wl.H, wl.dk), device="cuda") if wl.gain in ("pgdn", "kdn") else None
+    call = lambda: dn.chunk_fwd(t["q"], t["k"], t["v"], gates, gain=wl.gain, eps=wl.eps, x=wl.x,
+                                mu_info=wl.mu_info, S0=t["S0"], out=o, S_final=S, aux_final=aux)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    # dn launches on torch's current stream, so these events bracket exactly its kernels
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        per.append((a, b))
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(steps):
+        call()
+    ev1.record()
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    each = sorted(x.elapsed_time(y) for x, y in per)
+    return total_ms / steps, each
+
+
+def time_decode(dwl, steps_timed):
+    import torch
+    from recurrent_sequence_mixer_amd import dn
+    from recurrent_sequence_mixer_amd import workloads as W
+    t0 = time.time()
+    S = torch.from_numpy(W.generate_decode_state(dwl)).cuda()
+    ins = []
+    for s in range(dwl.steps):
+        st = dn.to_device(W.generate_decode_step(dwl, s), torch.bfloat16)
+        ins.append((st["q"], st["k"], st["v"], {"alpha": st["alpha"], "eta": st["eta"]}))
+    log(f"[bench] decode: {dwl.steps} steps of inputs ready in {time.time() - t0:.1f}s")
+    o = torch.empty((dwl.N, dwl.H, dwl.dv), dtype=torch.bfloat16, device="cuda")
+    for s in range(3):  # warm-up steps on a scratch copy of the state
+        q, k, v, g = ins[s]
+        dn.decode_step(q, k, v, g, S.clone(), gain="kla", eps=dwl.eps, out=o)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for s in range(steps_timed):
+        q, k, v, g = ins[s % dwl.steps]
+        dn.decode_step(q, k, v, g, S, gain="kla", eps=dwl.eps, out=o)
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps_timed
+
+
+def cpu_baseline(wl, heads=2, T=1024):
+    """The fp64 oracle on a bounded sample: `heads` heads x `T` tokens."""
+    from oracle.recurrence import run_workload
+    from recurrent_sequence_mixer_amd import workloads as W
+    sample = wl.replace(B=1, H=heads, T=T)
+    inp = W.generate(sample)
+    r0 = resource.getrusage(resource.RUSAGE_SELF)
+    t0 = time.time()
+    run_workload(sample, inp)
+    wall = time.time() - t0
+    r1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    head_tok_s = heads * T / wall
+    return {
+        "value": head_tok_s / wl.H,  # workload tokens/s: every token passes H heads
+        "unit": "tokens/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"{wl.name}: {heads} heads x {T} tokens (of {wl.B * wl.H} x {wl.T}), "
+                  f"{wall:.1f}s wall; value scaled to workload tokens/s ({wl.H} heads per token)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the forward engine shards "
+              "(batch, head) pairs with no exchange, so multi-GPU runs are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from recurrent_sequence_mixer_amd import workloads as W
+    torch.cuda.set_device(0)
+
+    wl = W.WORKLOADS[1]
+    ms, each = time_chunk(wl, args.steps, args.warmup)
+    bytes_ = chunk_bytes(wl)
+    flops = chunk_flops(wl)
+    achieved = bytes_ / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": wl.tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "gain": wl.gain, "B": wl.B, "H": wl.H, "T": wl.T,
+                   "dk": wl.dk, "dv": wl.dv, "C": wl.C},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "chunk_fwd_kernel<bf16,128,64,KLA,scalar>",
+                     "bytes_per_launch": bytes_},
+        "mfma": {"counted_tflops": flops / (ms * 1e-3) / 1e12,
+                 "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                 "counted_flops_per_launch": flops},
+        "step_ms_p10_p50_p90": [each[len(each) // 10], each[len(each) // 2], each[9 * len(each) // 10]],
+    }
+    log(f"[bench] {wl.name}: {ms:.3f} ms/step")
+    if not args.no_extra:
+        extra = {}
+        for idx in (2, 3):
+            w2 = W.WORKLOADS[idx]
+            ms2, _ = time_chunk(w2, max(5, args.steps // 2), args.warmup)
+            b2 = chunk_bytes(w2)
+            extra[w2.gain] = {"workload": w2.name, "ms": ms2, "tokens_per_s": w2.tokens / (ms2 * 1e-3),
+                              "hbm_gbs": b2 / (ms2 * 1e-3) / 1e9,
+                              "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              "mfma_frac": chunk_flops(w2) / (ms2 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+            log(f"[bench] {w2.name}: {ms2:.3f} ms/step")
+        dwl = W.WORKLOADS[4]
+        dms = time_decode(dwl, args.decode_steps)
+        gbs = decode_bytes(dwl) / (dms * 1e-3) / 1e9
+        extra["decode"] = {"workload": dwl.name, "ms_per_step": dms,
+                           "seq_tokens_per_s": dwl.N / (dms * 1e-3), "hbm_gbs": gbs,
+                           "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_step": decode_bytes(dwl)}
+        log(f"[bench] decode: {dms:.3f} ms/step, {gbs:.0f} GB/s")
+        out["extra"] = extra
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+        log(f"[bench] cpu baseline: {out['cpu_baseline']}")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

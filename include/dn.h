@@ -1,0 +1,173 @@
+/*
+ * dn.h — C ABI of the MI355X (gfx950) forward engine for the gated
+ * delta-rule recurrence (library libdn.so).
+ *
+ * The recurrence, per batch row b and head h, token t = 0 .. T-1
+ * (Kalman Delta Networks reading notes §1.1, unified family; Kaczmarz Linear
+ * Attention reading notes §2.1 and Algorithm 1; Preconditioned DeltaNet
+ * reading notes §2.4-2.5, Eq. 9, transposed to this orientation):
+ *
+ *     S_dec = D_t S_{t-1}                 D_t = alpha_t I  or  diag(alpha_t)
+ *     e_t   = v_t - S_dec^T k_t           residual from the decayed state
+ *     S_t   = S_dec + w_t e_t^T           rank-1 write with write vector w_t
+ *     o_t   = S_t^T q_t                   readout after the write
+ *
+ * S is d_k x d_v (key channels are rows).  The write vector w_t (the write key
+ * including its gain) depends on the gain:
+ *
+ *   DN_GAIN_KLA       w = eta / (||k||^2 + eps) * k
+ *                     (Kaczmarz Linear Attention §2.1, boxed formula)
+ *   DN_GAIN_GDN       w = eta * k            (same page §1.1)
+ *   DN_GAIN_PGDN      A_t = alphaP A_{t-1} + betaP (k*k);  r = log A_t - mu_h;
+ *                     s = r / (1 + |r|);  B = exp(-log(x) s);  w = eta B * k
+ *                     (Preconditioned DeltaNet §2.4, Eq. 9)
+ *   DN_GAIN_KDN       p_hat = alpha^2 p_{t-1} + omega;  z = sum p_hat k^2;
+ *                     w = p_hat * k / (r + z);  u = (mu_info / r) k^2;
+ *                     p_t = p_hat / (1 + u p_hat)
+ *                     (Kalman Delta Networks §2.4 Eqs. 23-30 and §2.5)
+ *   DN_GAIN_EXPLICIT  w_t read from gates->w (e.g. the exact ATK write key of
+ *                     Preconditioned DeltaNet §2.2)
+ *
+ * q is used as given: normalising it (Kaczmarz Linear Attention §2.1 reads
+ * S^T q / ||q||) is the caller's job.
+ *
+ * LAYOUT.  All tensors are dense and row-major with the last index
+ * contiguous:
+ *   q, k, o       [B, H, T, dk] / [B, H, T, dv]   io dtype
+ *   v             [B, H, T, dv]                   io dtype
+ *   alpha         scalar decay: fp32 [B, H, T];  channel decay: io [B, H, T, dk]
+ *   eta           fp32 [B, H, T]   (KLA eta, GDN/PGDN beta; unused by KDN)
+ *   alphaP, betaP fp32 [B, H, T]   (PGDN statistic gates)
+ *   mu_log        fp32 [H]         (PGDN per-head log-centre)
+ *   omega         io   [B, H, T, dk] (KDN process noise)
+ *   r             fp32 [B, H, T]   (KDN observation noise, > 0)
+ *   w             io   [B, H, T, dk] (EXPLICIT write vectors)
+ *   S0, S_final   fp32 [B, H, dk, dv]
+ *   aux0, aux_final fp32 [B, H, dk] (PGDN statistic A; KDN variance p)
+ *
+ * OWNERSHIP.  Every pointer except the descriptor and the gate table (host
+ * structs, read before the call returns) is a device pointer owned by the
+ * caller.  The library allocates no device memory, never synchronises, and
+ * enqueues all work on `stream` (a hipStream_t; NULL = the null stream).
+ *
+ * ERRORS.  Arguments are validated on the host before anything is launched;
+ * on a negative status nothing has been enqueued.  DN_ERR_HIP reports a
+ * failed launch.  NaN/Inf in the data are not checked and propagate.
+ * Preconditions on values (not checked): alpha in (0, 1]; PGDN A_0 > 0 and
+ * alphaP, betaP >= 0; KDN r > 0, omega >= 0, p_0 > 0; for channel decay the
+ * sum of -log(alpha) over any 32 consecutive tokens of one channel stays
+ * below 80 (fp32 range of the in-chunk decay factors).
+ *
+ * Thread safety: all entry points are reentrant; there is no mutable global
+ * state.
+ */
+#ifndef DN_H
+#define DN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DN_VERSION 1
+
+typedef enum dn_status {
+  DN_OK = 0,
+  DN_ERR_NULL = -1,        /* a required pointer is NULL                      */
+  DN_ERR_SHAPE = -2,       /* B, H, T, dk, dv or C outside the supported set  */
+  DN_ERR_DTYPE = -3,       /* unknown io dtype                                 */
+  DN_ERR_GAIN = -4,        /* unknown gain / decay, or invalid gain parameter  */
+  DN_ERR_UNSUPPORTED = -6, /* valid but not built (e.g. fp32 io with dk = 128) */
+  DN_ERR_HIP = -7,         /* a kernel launch failed                           */
+  DN_ERR_ALIAS = -8        /* forbidden overlap between buffers                */
+} dn_status;
+
+typedef enum dn_dtype { DN_F32 = 0, DN_BF16 = 1 } dn_dtype;
+
+typedef enum dn_gain {
+  DN_GAIN_KLA = 0,
+  DN_GAIN_GDN = 1,
+  DN_GAIN_PGDN = 2,
+  DN_GAIN_KDN = 3,
+  DN_GAIN_EXPLICIT = 4
+} dn_gain;
+
+typedef enum dn_decay { DN_DECAY_SCALAR = 0, DN_DECAY_CHANNEL = 1 } dn_decay;
+
+/* Problem descriptor (host struct).
+ *   B, H >= 1; T >= 0 (T = 0: S_final = S0, aux_final = aux0, o untouched);
+ *   dk, dv in {64, 128}; C = 64 (chunk length of the chunked forward);
+ *   io: dn_dtype of q, k, v, o and of per-channel gates;
+ *   gain: dn_gain; decay: dn_decay (KDN requires DN_DECAY_CHANNEL or SCALAR);
+ *   eps >= 0 (KLA), x > 1 (PGDN bound: B in [1/x, x]), mu_info > 0 (KDN). */
+typedef struct dn_desc {
+  int32_t B, H, T, dk, dv, C;
+  int32_t io;
+  int32_t gain;
+  int32_t decay;
+  float eps;
+  float x;
+  float mu_info;
+} dn_desc;
+
+/* Gate table (host struct of device pointers); unused entries may be NULL. */
+typedef struct dn_gates {
+  const void* alpha;   /* required                                   */
+  const float* eta;    /* KLA, GDN, PGDN                             */
+  const float* alphaP; /* PGDN                                       */
+  const float* betaP;  /* PGDN                                       */
+  const float* mu_log; /* PGDN                                       */
+  const void* omega;   /* KDN                                        */
+  const float* r;      /* KDN                                        */
+  const void* w;       /* EXPLICIT                                   */
+} dn_gates;
+
+/* Chunked forward over a whole sequence batch (Kaczmarz Linear Attention
+ * §2.5 Eqs. 7-9 and Preconditioned DeltaNet §2.6 Eq. 6 give the chunk form;
+ * results equal the token recurrence above up to rounding).
+ *   S0        initial state, NULL = zeros.
+ *   aux0      PGDN A_0 / KDN p_0, NULL = ones; ignored by other gains.
+ *   o         output [B, H, T, dv], io dtype (round to nearest even).
+ *   S_final   final state, nullable.  May alias S0 exactly (in-place resume).
+ *   aux_final final A_T / p_T, nullable.  Must not overlap aux0 (every value
+ *             slice of a head reads aux0 while one of them writes aux_final).
+ * No other buffers may overlap (DN_ERR_ALIAS is returned for the overlaps
+ * the host can see from the pointer ranges).  With T = 0 the tensors q, k, v,
+ * o and the gate table may be NULL. */
+int dn_chunk_fwd(const dn_desc* desc, const void* q, const void* k, const void* v,
+                 const dn_gates* gates, const float* S0, const float* aux0, void* o,
+                 float* S_final, float* aux_final, void* stream);
+
+/* One token for N = desc->B independent sequences (desc->T must be 1), the
+ * tokenwise step of Kaczmarz Linear Attention Algorithm 1 (and its PGDN/KDN
+ * analogues).  S [N, H, dk, dv] and aux [N, H, dk] (PGDN, KDN; NULL
+ * otherwise) are updated in place; o [N, H, dv] receives S_t^T q_t.
+ * q, k, v, gates are laid out as for dn_chunk_fwd with T = 1. */
+int dn_decode_step(const dn_desc* desc, const void* q, const void* k, const void* v,
+                   const dn_gates* gates, float* S, float* aux, void* o, void* stream);
+
+/* The write-gain scans alone, for inspection and testing.
+ *   w_out     fp32 [B, H, T, dk]: write vectors w_t (required).
+ *   g_out     fp32 cumulative log-decay within each chunk of C tokens
+ *             (G_t = sum of log alpha from the chunk start through t):
+ *             [B, H, T] (scalar decay) or [B, H, T, dk] (channel); nullable.
+ *   aux_chunk fp32 [B, H, ceil(T/C), dk]: PGDN A / KDN p entering each
+ *             chunk; nullable (ignored by gains without state).
+ *   aux_final fp32 [B, H, dk]: A_T / p_T; nullable.
+ *   aux0      as for dn_chunk_fwd. */
+int dn_gain_prep(const dn_desc* desc, const void* k, const dn_gates* gates, const float* aux0,
+                 float* w_out, float* g_out, float* aux_chunk, float* aux_final, void* stream);
+
+/* Static text for a status code. */
+const char* dn_status_string(int status);
+
+/* DN_VERSION of the library. */
+int dn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DN_H */

@@ -1,0 +1,796 @@
+// Chunked forward of the gated delta-rule recurrence on gfx950.
+//
+// One workgroup owns one (batch, head) and a slice of BV value columns; it
+// walks the sequence in chunks of C = 64 tokens and keeps its d_k x BV slice
+// of the fp32 state in registers for the whole sequence.  Value columns of S
+// evolve independently (the residual e_t is per column, and every column
+// shares the same key-space write: Kalman Delta Networks §2.1), so slices of
+// one head need no communication.
+//
+// Chunk form (our statement of Kaczmarz Linear Attention §2.5 Eqs. 7-9 and
+// Preconditioned DeltaNet §2.6 Eq. 6, extended to per-channel decay).  With
+// G_t the cumulative log-decay inside the chunk and g_t = exp(G_t):
+//
+//   khat_i = g_i * k_i,  qhat_i = g_i * q_i,  wchk_j = w_j / g_j,
+//   wtil_j = (g_n / g_j) * w_j
+//   L = strict_lower(Khat Wchk^T),   M = lower_incl(Qhat Wchk^T)
+//   (I + L) U = V - Khat S_in        (row i of U is the residual e_i)
+//   O = Qhat S_in + M U,             S_out = diag(g_n) S_in + Wtil^T U
+//
+// Per chunk, in this order (barriers between the numbered steps):
+//   1. the chunk's k, q, v slice and gates move from staging registers (loaded
+//      from HBM during the previous chunk) into LDS, and the next chunk's
+//      loads are issued;
+//   2. gains: write vectors w_t (KLA/GDN/PGDN/KDN/explicit) and cumulative
+//      log2-decay; the PGDN statistic A and the KDN variance p are carried
+//      across chunks in registers of the thread owning the key channel;
+//   3. the transposed write operand Wtil^T;
+//   4. L and M as lower-triangular 16x16 tile pairs on the matrix cores;
+//   5. each wavefront inverts one 16x16 diagonal block of I + L (fp32
+//      forward substitution) and forms Khat S and Qhat S for its 16 value
+//      columns;
+//   6. per wavefront: blocked forward substitution
+//      U_b = T_bb (R_b - sum_{m<b} L_bm U_m), O = Qhat S + M U and
+//      S = diag(g_n) S + Wtil^T U.  With bf16 operands the solve and M U run
+//      on 16x16x16 MFMAs whose B operand is the accumulator layout of U, so U
+//      never leaves registers;
+//   7. the output tile goes to HBM in 16-byte rows.
+// Operands are bf16 (fp32 for fp32 io) with fp32 accumulation; S, the
+// diagonal-block inverses and all gain arithmetic stay fp32.
+//
+// Scalar decay: decay factors exp(G_i - G_j) are applied per element to the
+// products of the raw k, q and w (no overflow for any decay).  Channel decay:
+// khat, qhat and wchk are referenced to the chunk midpoint, which keeps each
+// factor within exp of the decay accumulated over 32 tokens.
+#include "common.hpp"
+#include "gains.hpp"
+#include "launch.hpp"
+
+namespace dn {
+
+constexpr int CH = 64;  // chunk length
+
+// Phase-timing hook: a no-op unless the library is built with
+// -DDN_PHASE_TIMING, in which case every wavefront accumulates shader-clock
+// cycles per phase of the chunk loop into dn_phase_cycles[wave][phase].
+#ifdef DN_PHASE_TIMING
+constexpr int DN_NPHASE = 8;
+__device__ unsigned long long dn_phase_cycles[4][DN_NPHASE];
+#define DN_PHASE_DECL unsigned long long ph_acc[DN_NPHASE] = {}, ph_last = __builtin_readcyclecounter();
+#define DN_PHASE(i)                                              \
+  do {                                                           \
+    const unsigned long long now = __builtin_readcyclecounter(); \
+    ph_acc[i] += now - ph_last;                                  \
+    ph_last = now;                                               \
+  } while (0)
+#define DN_PHASE_FLUSH \
+  if (lane == 0)       \
+    for (int i = 0; i < DN_NPHASE; ++i) atomicAdd(&dn_phase_cycles[wave][i], ph_acc[i]);
+#else
+#define DN_PHASE_DECL
+#define DN_PHASE(i) \
+  do {              \
+  } while (0)
+#define DN_PHASE_FLUSH
+#endif
+
+// Synchronisation of LDS traffic between lanes of one wavefront: LDS
+// instructions of a wavefront complete in order; the fences keep the
+// compiler from moving LDS accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Hardware exp2 / log2 (v_exp_f32, v_log_f32).  Arguments here are decay
+// sums and their differences (finite, and exp2 of very negative values
+// underflowing to 0 is the right limit).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// bf16 16x16x16 MFMA pieces.  Lane l: A row l % 16, k = 4 (l / 16) .. +3;
+// B column l % 16, k = 4 (l / 16) .. +3; accumulator rows 4 (l / 16) .. +3 of
+// column l % 16.  The accumulator of one product is therefore, packed to
+// bf16, directly the B operand of the next.
+__device__ __forceinline__ s16x4 frag16(const uint16_t* p, int ld, int lane) {
+  return __builtin_bit_cast(
+      s16x4, *reinterpret_cast<const u32x2*>(p + (lane & 15) * ld + 4 * (lane >> 4)));
+}
+__device__ __forceinline__ s16x4 pack16(f32x4 c) {
+  const u32x2 v = {pack_bf2(c[0], c[1]), pack_bf2(c[2], c[3])};
+  return __builtin_bit_cast(s16x4, v);
+}
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+template <typename E> struct Pad;
+template <> struct Pad<uint16_t> { static constexpr int v = 8; };
+template <> struct Pad<float> { static constexpr int v = 4; };
+
+template <typename E, int DK, int BV, bool HAS_W>
+struct ChunkSmem {
+  static constexpr int PAD = Pad<E>::v;
+  static constexpr int PK = DK + PAD;     // pitch of [token][d_k] operands
+  static constexpr int PT = CH + PAD;     // pitch of [*][token] operands
+  static constexpr int P16 = 16 + PAD;    // pitch of 16-wide blocks
+  static constexpr int NW = BV / 16;
+  alignas(16) E k[CH * PK];              // raw k (scalar decay) or khat (channel decay)
+  alignas(16) E q[CH * PK];              // raw q or qhat
+  alignas(16) E w[HAS_W ? CH * PK : 8];  // B operand of L, M: raw w (scalar) or wchk
+  alignas(16) E wt[DK * PT];             // Wtil^T: [d][t]; stages channel alpha first
+  alignas(16) E v[CH * BV];              // value slice [t][c]
+  alignas(16) E lm[2 * CH * PT];         // -L (strictly lower) and M (lower incl.
+                                         // diagonal), [i][j]; stages KDN omega first
+  alignas(16) E tb[4 * 16 * P16];        // inverses of the diagonal blocks of I + L
+  alignas(16) E sb[NW * 16 * PK];        // per wave: its 16 state columns, [c][d]
+  alignas(16) E ub[NW * 16 * PT];        // per wave: U columns, [c][t]
+  alignas(16) E xb[NW * 16 * P16];       // per wave: right-hand side of one block solve
+  alignas(16) E o[CH * BV];              // output tile [t][c]
+  alignas(16) float ld[4 * 16 * 16];     // diagonal 16x16 blocks of L, fp32
+  alignas(16) float g2[CH];              // scalar decay: cumulative log2-decay
+  alignas(16) float gmid[DK];            // channel decay: 2^Gmid per channel
+  alignas(16) float gn[DK];              // channel decay: 2^Gn per channel
+  float cs[CH];                          // column scale of the L, M products
+  float eta[CH], alpha[CH], ap[CH], bp[CH], mur[CH], r[CH];
+  float zp[4][CH];                       // KDN: per-wavefront partial sums of z_t
+  float red[CH];                         // KDN: 1 / (r_t + z_t)
+};
+
+template <typename E, int DK, int BV, int GAIN, bool CHANNEL>
+__global__ __launch_bounds__(BV * 4) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void chunk_fwd_kernel(ChunkArgs a) {
+  constexpr int NW = BV / 16;
+  constexpr int NT = 64 * NW;
+  constexpr bool BF16 = sizeof(E) == 2;
+  constexpr bool HAS_W = CHANNEL || GAIN == GAIN_PGDN || GAIN == GAIN_KDN || GAIN == GAIN_EXPLICIT;
+  constexpr bool SCAN = CHANNEL || GAIN == GAIN_PGDN || GAIN == GAIN_KDN;
+  using Sm = ChunkSmem<E, DK, BV, HAS_W>;
+  constexpr int PK = Sm::PK, PT = Sm::PT, P16 = Sm::P16;
+  constexpr int VEC = 16 / sizeof(E);            // elements per 16-byte access
+  constexpr int KV_LOADS = CH * DK / (NT * VEC); // 16-byte loads per thread (k or q)
+  constexpr int V_LOADS = (CH * BV + NT * VEC - 1) / (NT * VEC);
+  constexpr int CPT = (DK + NT - 1) / NT;        // key channels per thread
+  constexpr int KS = DK / MmaK<E>::v;            // k-steps of a d_k contraction
+  static_assert(KV_LOADS * NT * VEC == CH * DK, "k/q tile split");
+  using EL = Elem<E>;
+  using MM = Mma<E>;
+  using Frag = typename MM::Frag;
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
+  E* const sL = sm.lm;            // -L
+  E* const sM = sm.lm + CH * PT;  // M
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y;
+  const int h = bh % a.H;
+  const int col0 = blockIdx.x * BV;  // first value column of this slice
+  const int T = a.T;
+  const int nchunks = (T + CH - 1) / CH;
+  const long qk_base = static_cast<long>(bh) * T * DK;
+  const long v_base = static_cast<long>(bh) * T * a.dv;
+  const E* gk = static_cast<const E*>(a.k) + qk_base;
+  const E* gq = static_cast<const E*>(a.q) + qk_base;
+  const E* gv = static_cast<const E*>(a.v) + v_base;
+  E* go = static_cast<E*>(a.o) + v_base;
+
+  // ---- state slice in registers: tile dt holds rows 16 dt + 4 g4 + i, column c16
+  f32x4 S[DK / 16];
+  {
+    const int col = col0 + 16 * wave + c16;
+#pragma unroll
+    for (int dt = 0; dt < DK / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * dt + 4 * g4 + i;
+        S[dt][i] = a.S0 ? a.S0[(static_cast<long>(bh) * DK + row) * a.dv + col] : 0.f;
+      }
+  }
+  // ---- per-channel gain state (PGDN statistic A, KDN variance p)
+  float aux[CPT];
+#pragma unroll
+  for (int cc = 0; cc < CPT; ++cc) {
+    const int d = tid + cc * NT;
+    aux[cc] = (d < DK && a.aux0) ? a.aux0[static_cast<long>(bh) * DK + d] : 1.f;
+  }
+
+  // ---- register staging of one chunk's inputs
+  u32x4 pk[KV_LOADS], pq[KV_LOADS], pw[GAIN == GAIN_EXPLICIT ? KV_LOADS : 1];
+  u32x4 pal[CHANNEL ? KV_LOADS : 1], pom[GAIN == GAIN_KDN ? KV_LOADS : 1];
+  u32x4 pv[V_LOADS];
+  float p_eta = 0.f, p_alpha = 1.f, p_ap = 1.f, p_bp = 0.f, p_r = 1.f;
+
+  // Loads are branch-free: out-of-range tokens read row 0 of the chunk
+  // (in range whenever the chunk exists) and are replaced by neutral values.
+  auto fetch = [&](int c) __attribute__((always_inline)) {
+    const int t0 = c * CH;
+    const int n = min(CH, T - t0);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < KV_LOADS; ++j) {
+      const int e = (tid + j * NT) * VEC;  // element index inside the [CH][DK] tile
+      const int t = e / DK, d = e % DK;
+      const bool ok = t < n;
+      const long off = static_cast<long>(t0 + (ok ? t : 0)) * DK + d;
+      const u32x4 kk = *reinterpret_cast<const u32x4*>(gk + off);
+      const u32x4 qq = *reinterpret_cast<const u32x4*>(gq + off);
+      pk[j] = ok ? kk : z;
+      pq[j] = ok ? qq : z;
+      if constexpr (GAIN == GAIN_EXPLICIT) {
+        const u32x4 ww =
+            *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g.w) + qk_base + off);
+        pw[j] = ok ? ww : z;
+      }
+      if constexpr (CHANNEL) {
+        // padded tokens decay by exactly 1
+        const u32x4 one4 = BF16 ? u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}
+                                : u32x4{0x3F800000u, 0x3F800000u, 0x3F800000u, 0x3F800000u};
+        const u32x4 al =
+            *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g.alpha) + qk_base + off);
+        pal[j] = ok ? al : one4;
+      }
+      if constexpr (GAIN == GAIN_KDN) {
+        const u32x4 om =
+            *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g.omega) + qk_base + off);
+        pom[j] = ok ? om : z;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < V_LOADS; ++j) {
+      const int e = (tid + j * NT) * VEC;
+      const int t = e / BV, cc = e % BV;
+      const bool ok = e < CH * BV && t < n;
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(
+          gv + static_cast<long>(t0 + (ok ? t : 0)) * a.dv + col0 + (ok ? cc : 0));
+      pv[j] = ok ? vv : z;
+    }
+    if (tid < CH) {
+      const bool ok = tid < n;
+      const long ti = static_cast<long>(bh) * T + t0 + (ok ? tid : 0);
+      if (GAIN != GAIN_KDN && GAIN != GAIN_EXPLICIT) {
+        const float x = a.g.eta[ti];
+        p_eta = ok ? x : 0.f;
+      }
+      if (!CHANNEL) {
+        const float x = static_cast<const float*>(a.g.alpha)[ti];
+        p_alpha = ok ? x : 1.f;
+      }
+      if (GAIN == GAIN_PGDN) {
+        const float x = a.g.alphaP[ti], y = a.g.betaP[ti];
+        p_ap = ok ? x : 1.f;
+        p_bp = ok ? y : 0.f;
+      }
+      if (GAIN == GAIN_KDN) {
+        const float x = a.g.r[ti];
+        p_r = ok ? x : 1.f;  // padded tokens: k = 0 gives u = 0
+      }
+    }
+  };
+
+  auto stash = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < KV_LOADS; ++j) {
+      const int e = (tid + j * NT) * VEC;
+      const int t = e / DK, d = e % DK;
+      *reinterpret_cast<u32x4*>(&sm.k[t * PK + d]) = pk[j];
+      *reinterpret_cast<u32x4*>(&sm.q[t * PK + d]) = pq[j];
+      if constexpr (GAIN == GAIN_EXPLICIT) *reinterpret_cast<u32x4*>(&sm.w[t * PK + d]) = pw[j];
+    }
+#pragma unroll
+    for (int j = 0; j < V_LOADS; ++j) {
+      const int e = (tid + j * NT) * VEC;
+      if (e < CH * BV) *reinterpret_cast<u32x4*>(&sm.v[e]) = pv[j];
+    }
+    if (tid < CH) {
+      sm.eta[tid] = p_eta;
+      sm.alpha[tid] = p_alpha;
+      sm.ap[tid] = p_ap;
+      sm.bp[tid] = p_bp;
+      sm.r[tid] = p_r;
+      sm.mur[tid] = a.g.mu_info / p_r;
+    }
+  };
+
+  if (nchunks > 0) fetch(0);
+  DN_PHASE_DECL
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int t0 = c * CH;
+    const int n = min(CH, T - t0);
+    stash();
+    // per-channel gates of this chunk, consumed in step 2
+    u32x4 cal[CHANNEL ? KV_LOADS : 1], com[GAIN == GAIN_KDN ? KV_LOADS : 1];
+#pragma unroll
+    for (int j = 0; j < (CHANNEL ? KV_LOADS : 0); ++j) cal[j] = pal[j];
+#pragma unroll
+    for (int j = 0; j < (GAIN == GAIN_KDN ? KV_LOADS : 0); ++j) com[j] = pom[j];
+    __syncthreads();  // (A) chunk inputs visible
+    // the next chunk's inputs travel from HBM while this chunk is processed
+    if (c + 1 < nchunks) fetch(c + 1);
+    DN_PHASE(0);
+
+    // ================= 2. gains =================
+    if constexpr (!CHANNEL) {
+      // cumulative log2-decay by a wavefront inclusive scan; tokens >= n have alpha = 1
+      if (wave == NW - 1) {
+        float x = fast_log2(sm.alpha[lane]);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(x, off, 64);
+          if (lane >= off) x += y;
+        }
+        sm.g2[lane] = x;
+      }
+    }
+    if constexpr (GAIN == GAIN_KLA || GAIN == GAIN_GDN) {
+      // ||k_t||^2 (KLA) with NT/64 threads per token, 16-byte LDS reads; column scale beta_t
+      constexpr int TPT = NT / CH;
+      const int t = tid / TPT, part = tid % TPT;
+      float s = 0.f;
+      if (GAIN == GAIN_KLA) {
+        constexpr int PER = DK / TPT;
+#pragma unroll
+        for (int d0 = 0; d0 < PER; d0 += VEC) {
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(&sm.k[t * PK + part * PER + d0]);
+          if constexpr (BF16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float lo = __uint_as_float(raw[i] << 16);
+              const float hi = __uint_as_float(raw[i] & 0xFFFF0000u);
+              s = fmaf(lo, lo, s);
+              s = fmaf(hi, hi, s);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x = __uint_as_float(raw[i]);
+              s = fmaf(x, x, s);
+            }
+          }
+        }
+#pragma unroll
+        for (int off = 1; off < TPT; off <<= 1) s += __shfl_xor(s, off, 64);
+      }
+      if (part == 0)
+        sm.cs[t] = (GAIN == GAIN_KLA) ? kla_beta(sm.eta[t], s, a.g.eps) : sm.eta[t];
+    }
+    if constexpr (GAIN == GAIN_PGDN || GAIN == GAIN_KDN || GAIN == GAIN_EXPLICIT) {
+      if (tid < CH) sm.cs[tid] = 1.f;
+    }
+
+    // per-channel scans: channel decay G, PGDN statistic A, KDN variance p.
+    // Threads own key channels; the carried A / p live in their registers.
+    float gch[CHANNEL ? CPT : 1][CHANNEL ? CH : 1];
+    float pkr[GAIN == GAIN_KDN ? CPT : 1][GAIN == GAIN_KDN ? CH : 1];  // KDN: p_hat * k
+    if constexpr (SCAN) {
+      E* s_al = sm.wt;  // channel alpha staged as [t][d] (wt is built after barrier B)
+      E* s_om = sm.lm;  // KDN omega staged as [t][d] (lm is built after barrier C)
+      if constexpr (CHANNEL || GAIN == GAIN_KDN) {
+#pragma unroll
+        for (int j = 0; j < KV_LOADS; ++j) {
+          const int e = (tid + j * NT) * VEC;
+          if constexpr (CHANNEL) *reinterpret_cast<u32x4*>(&s_al[e]) = cal[j];
+          if constexpr (GAIN == GAIN_KDN) *reinterpret_cast<u32x4*>(&s_om[e]) = com[j];
+        }
+        __syncthreads();
+      }
+      const float mu = GAIN == GAIN_PGDN ? a.g.mu_log[h] : 0.f;
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc) {
+        const int d = tid + cc * NT;
+        if (d < DK) {
+          float G = 0.f, st = aux[cc];
+#pragma unroll
+          for (int t = 0; t < CH; ++t) {
+            const float al = CHANNEL ? EL::get(s_al[t * DK + d]) : sm.alpha[t];
+            if constexpr (CHANNEL) {
+              G += fast_log2(al);
+              gch[cc][t] = G;
+            }
+            const float kk = EL::get(sm.k[t * PK + d]);
+            if constexpr (GAIN == GAIN_PGDN) {
+              st = pgdn_stat(st, sm.ap[t], sm.bp[t], kk);
+              const float wv = sm.eta[t] * pgdn_scale(st, mu, a.g.log2x) * kk;
+              sm.w[t * PK + d] = EL::put(wv);
+            }
+            if constexpr (GAIN == GAIN_KDN) {
+              const float ph = kdn_predict(al, st, EL::get(s_om[t * DK + d]));
+              pkr[cc][t] = ph * kk;
+              st = kdn_update(ph, kk, sm.mur[t]);
+            }
+          }
+          aux[cc] = st;
+        }
+      }
+      if constexpr (GAIN == GAIN_KDN) {
+        // z_t = sum_d p_hat k^2: wavefront sums, combined in a fixed order
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+          float z = 0.f;
+#pragma unroll
+          for (int cc = 0; cc < CPT; ++cc) {
+            const int d = tid + cc * NT;
+            if (d < DK) z += pkr[cc][t] * EL::get(sm.k[t * PK + d]);
+          }
+          z = wave_sum(z);
+          if (lane == 0) sm.zp[wave][t] = z;
+        }
+        __syncthreads();
+        if (tid < CH) {
+          float z = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < NW; ++ww) z += sm.zp[ww][tid];
+          sm.red[tid] = 1.f / (sm.r[tid] + z);
+        }
+      }
+    }
+    __syncthreads();  // (B) gains visible
+    DN_PHASE(1);
+
+    // ================= 3. write-vector operands =================
+    if constexpr (!CHANNEL) {
+      if constexpr (GAIN == GAIN_KDN) {
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) {
+          const int d = tid + cc * NT;
+          if (d < DK)
+#pragma unroll
+            for (int t = 0; t < CH; ++t) sm.w[t * PK + d] = EL::put(pkr[cc][t] * sm.red[t]);
+        }
+        __syncthreads();
+      }
+      // Wtil^T[d][t] = 2^(G_{n-1} - G_t) w_t[d], in 4-token x VEC-channel blocks:
+      // 16-byte row reads of w (or k), transposed 8/16-byte writes.
+      const float gl = sm.g2[CH - 1];
+      const E* src = HAS_W ? sm.w : sm.k;
+      for (int blk = tid; blk < (CH / 4) * (DK / VEC); blk += NT) {
+        const int tb4 = blk % (CH / 4), db = blk / (CH / 4);
+        const int tt0 = 4 * tb4, dd0 = db * VEC;
+        float val[4][VEC];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = tt0 + i;
+          const float f = sm.cs[t] * fast_exp2(gl - sm.g2[t]);
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(&src[t * PK + dd0]);
+          if constexpr (BF16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              val[i][2 * j] = f * __uint_as_float(raw[j] << 16);
+              val[i][2 * j + 1] = f * __uint_as_float(raw[j] & 0xFFFF0000u);
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) val[i][j] = f * __uint_as_float(raw[j]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+          E* dst = &sm.wt[(dd0 + j) * PT + tt0];
+          if constexpr (BF16) {
+            const u32x2 p2 = {pack_bf2(val[0][j], val[1][j]), pack_bf2(val[2][j], val[3][j])};
+            *reinterpret_cast<u32x2*>(dst) = p2;
+          } else {
+            const f32x4 v4 = {val[0][j], val[1][j], val[2][j], val[3][j]};
+            *reinterpret_cast<f32x4*>(dst) = v4;
+          }
+        }
+      }
+    } else {
+      // channel decay: rescale k, q in place to the chunk midpoint, build wchk and Wtil^T
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc) {
+        const int d = tid + cc * NT;
+        if (d < DK) {
+          const float gm = gch[cc][CH / 2 - 1], gl = gch[cc][CH - 1];
+          sm.gmid[d] = fast_exp2(gm);
+          sm.gn[d] = fast_exp2(gl);
+#pragma unroll
+          for (int t = 0; t < CH; ++t) {
+            const float kk = EL::get(sm.k[t * PK + d]);
+            float wv;
+            if constexpr (GAIN == GAIN_KDN) wv = pkr[cc][t] * sm.red[t];
+            else if constexpr (GAIN == GAIN_PGDN || GAIN == GAIN_EXPLICIT) wv = EL::get(sm.w[t * PK + d]);
+            else wv = sm.cs[t] * kk;
+            const float up = fast_exp2(gch[cc][t] - gm);
+            sm.k[t * PK + d] = EL::put(up * kk);
+            sm.q[t * PK + d] = EL::put(up * EL::get(sm.q[t * PK + d]));
+            sm.w[t * PK + d] = EL::put(fast_exp2(gm - gch[cc][t]) * wv);
+            sm.wt[d * PT + t] = EL::put(fast_exp2(gl - gch[cc][t]) * wv);
+          }
+        }
+      }
+    }
+    __syncthreads();  // (C) operands of the intra-chunk products ready
+    DN_PHASE(2);
+
+    // ================= 4. L and M, lower-triangular 16x16 tile pairs =================
+    {
+      const E* Bop = HAS_W ? sm.w : sm.k;
+      for (int pair = wave; pair < 10; pair += NW) {
+        int tt = pair, bi = 0;  // 0..9 -> (bi, bj), bj <= bi
+        while (tt > bi) {
+          tt -= bi + 1;
+          ++bi;
+        }
+        const int bj = tt;
+        Frag fb[KS], fk[KS], fq[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          fb[s] = MM::frag(Bop + 16 * bj * PK, PK, lane, s);
+          fk[s] = MM::frag(sm.k + 16 * bi * PK, PK, lane, s);
+          fq[s] = MM::frag(sm.q + 16 * bi * PK, PK, lane, s);
+        }
+        f32x4 accL = zero4(), accM = zero4();
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          accL = MM::mma(fk[s], fb[s], accL);
+          accM = MM::mma(fq[s], fb[s], accM);
+        }
+        const int j = 16 * bj + c16;
+        const f32x4 gi = *reinterpret_cast<const f32x4*>(&sm.g2[16 * bi + 4 * g4]);
+        const float gj = sm.g2[j], csj = sm.cs[j];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int i = 16 * bi + 4 * g4 + ii;
+          const float f = CHANNEL ? 1.f : fast_exp2(gi[ii] - gj) * csj;
+          const float lv = j < i ? accL[ii] * f : 0.f;
+          const float mv = j <= i ? accM[ii] * f : 0.f;
+          sM[i * PT + j] = EL::put(mv);
+          sL[i * PT + j] = EL::put(bi == bj ? 0.f : -lv);
+          if (bi == bj) sm.ld[(bi * 16 + (i & 15)) * 16 + (j & 15)] = lv;
+        }
+      }
+      // zero the strictly-upper tiles of -L and M
+      for (int e = tid; e < 6 * 256; e += NT) {
+        const int tile = e >> 8, w = e & 255;
+        const int bi = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
+        const int bj = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
+        const int i = 16 * bi + (w >> 4), jj = 16 * bj + (w & 15);
+        sL[i * PT + jj] = EL::put(0.f);
+        sM[i * PT + jj] = EL::put(0.f);
+      }
+    }
+    __syncthreads();  // (D) L, M ready
+    DN_PHASE(3);
+
+    // ================= 5. diagonal-block inverses and Khat S, Qhat S =================
+    // wavefront w inverts diagonal block(s) w, w + NW, ...: lane c < 16
+    // computes column c of (I + L_bb)^-1 by forward substitution (rows of
+    // L_bb are broadcast LDS reads).
+    for (int b = wave; b < 4; b += NW) {
+      if (lane < 16) {
+        const float* Lb = sm.ld + b * 256;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float row[16];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 r4 = *reinterpret_cast<const f32x4*>(&Lb[i * 16 + 4 * q4]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) row[4 * q4 + u] = r4[u];
+          }
+          float s0 = (i == lane) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+          for (int j = 0; j < i; ++j) {
+            if (j & 1) s1 = fmaf(-row[j], x[j], s1);
+            else s0 = fmaf(-row[j], x[j], s0);
+          }
+          x[i] = s0 + s1;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sm.tb[(b * 16 + i) * P16 + lane] = EL::put(x[i]);
+      }
+    }
+
+    E* sb = sm.sb + wave * 16 * PK;
+    E* ub = sm.ub + wave * 16 * PT;
+    E* xb = sm.xb + wave * 16 * P16;
+    // S columns -> [c][d] operand (channel decay: rows scaled by 2^Gmid)
+#pragma unroll
+    for (int dt = 0; dt < DK / 16; ++dt) {
+      f32x4 s4 = S[dt];
+      if constexpr (CHANNEL) {
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.gmid[16 * dt + 4 * g4]);
+        s4 = s4 * gm;
+      }
+      E* dst = &sb[c16 * PK + 16 * dt + 4 * g4];
+      if constexpr (BF16) {
+        const u32x2 p2 = {pack_bf2(s4[0], s4[1]), pack_bf2(s4[2], s4[3])};
+        *reinterpret_cast<u32x2*>(dst) = p2;
+      } else {
+        *reinterpret_cast<f32x4*>(dst) = s4;
+      }
+    }
+    wave_lds_sync();
+
+    f32x4 R[4], O[4];
+    {
+      Frag fs[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) fs[s] = MM::frag(sb, PK, lane, s);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        Frag fk[KS], fq[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          fk[s] = MM::frag(sm.k + 16 * rt * PK, PK, lane, s);
+          fq[s] = MM::frag(sm.q + 16 * rt * PK, PK, lane, s);
+        }
+        f32x4 kacc = zero4(), qacc = zero4();
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          kacc = MM::mma(fk[s], fs[s], kacc);
+          qacc = MM::mma(fq[s], fs[s], qacc);
+        }
+        const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.g2[16 * rt + 4 * g4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * rt + 4 * g4 + i;
+          const float sc = CHANNEL ? 1.f : fast_exp2(gt[i]);
+          R[rt][i] = EL::get(sm.v[t * BV + 16 * wave + c16]) - sc * kacc[i];
+          O[rt][i] = sc * qacc[i];
+        }
+      }
+    }
+    __syncthreads();  // (E) block inverses ready
+    DN_PHASE(4);
+
+    // ================= 6. solve, output, state update (per wavefront) =================
+    if constexpr (BF16) {
+      s16x4 Ub[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        f32x4 acc = R[b];
+#pragma unroll
+        for (int m = 0; m < b; ++m)
+          acc = mfma16(frag16(sL + 16 * b * PT + 16 * m, PT, lane), Ub[m], acc);
+        const f32x4 u = mfma16(frag16(sm.tb + 16 * b * P16, P16, lane), pack16(acc), zero4());
+        Ub[b] = pack16(u);
+      }
+      // O = Qhat S + M U
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+        for (int m = 0; m <= rt; ++m)
+          O[rt] = mfma16(frag16(sM + 16 * rt * PT + 16 * m, PT, lane), Ub[m], O[rt]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sm.o[(16 * rt + 4 * g4 + i) * BV + 16 * wave + c16] = EL::put(O[rt][i]);
+      }
+      // U columns -> [c][t] operand of Wtil^T U
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        *reinterpret_cast<s16x4*>(&ub[c16 * PT + 16 * b + 4 * g4]) = Ub[b];
+    } else {
+      for (int e = lane; e < 16 * PT; e += 64) ub[e] = EL::put(0.f);
+      wave_lds_sync();
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        f32x4 acc = R[b];
+        if (b > 0) MM::run(acc, sL + 16 * b * PT, PT, ub, PT, b >= 3 ? 64 : 32, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xb[c16 * P16 + 4 * g4 + i] = EL::put(acc[i]);
+        wave_lds_sync();
+        f32x4 u = zero4();
+        MM::run(u, sm.tb + b * 16 * P16, P16, xb, P16, 16, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ub[c16 * PT + 16 * b + 4 * g4 + i] = EL::put(u[i]);
+        wave_lds_sync();
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        MM::run(O[rt], sM + 16 * rt * PT, PT, ub, PT, rt >= 2 ? 64 : 32, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sm.o[(16 * rt + 4 * g4 + i) * BV + 16 * wave + c16] = EL::put(O[rt][i]);
+      }
+    }
+    wave_lds_sync();
+    // S = diag(g_n) S + Wtil^T U
+    {
+      constexpr int KT = CH / MmaK<E>::v;
+      Frag fu[KT];
+#pragma unroll
+      for (int s = 0; s < KT; ++s) fu[s] = MM::frag(ub, PT, lane, s);
+      const float gsc = CHANNEL ? 1.f : fast_exp2(sm.g2[CH - 1]);
+#pragma unroll
+      for (int dt = 0; dt < DK / 16; ++dt) {
+        Frag fw[KT];
+#pragma unroll
+        for (int s = 0; s < KT; ++s) fw[s] = MM::frag(sm.wt + 16 * dt * PT, PT, lane, s);
+        if constexpr (CHANNEL) {
+          const f32x4 gn = *reinterpret_cast<const f32x4*>(&sm.gn[16 * dt + 4 * g4]);
+          S[dt] = S[dt] * gn;
+        } else {
+          S[dt] = S[dt] * gsc;
+        }
+#pragma unroll
+        for (int s = 0; s < KT; ++s) S[dt] = MM::mma(fw[s], fu[s], S[dt]);
+      }
+    }
+    __syncthreads();  // (F) output tile complete; chunk operands free
+    DN_PHASE(5);
+
+    // ================= 7. output tile -> HBM, 16-byte rows =================
+    for (int e = tid * VEC; e < CH * BV; e += NT * VEC) {
+      const int t = e / BV, cc = e % BV;
+      if (t < n)
+        *reinterpret_cast<u32x4*>(go + static_cast<long>(t0 + t) * a.dv + col0 + cc) =
+            *reinterpret_cast<const u32x4*>(&sm.o[e]);
+    }
+    DN_PHASE(6);
+  }
+  DN_PHASE_FLUSH
+
+  // ---- final state and auxiliary state
+  if (a.S_final) {
+    const int col = col0 + 16 * wave + c16;
+#pragma unroll
+    for (int dt = 0; dt < DK / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * dt + 4 * g4 + i;
+        a.S_final[(static_cast<long>(bh) * DK + row) * a.dv + col] = S[dt][i];
+      }
+  }
+  if ((GAIN == GAIN_PGDN || GAIN == GAIN_KDN) && a.aux_final && blockIdx.x == 0) {
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      const int d = tid + cc * NT;
+      if (d < DK) a.aux_final[static_cast<long>(bh) * DK + d] = aux[cc];
+    }
+  }
+}
+
+template <typename E, int DK, int BV, int GAIN, bool CHANNEL>
+static hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
+  constexpr bool HAS_W = CHANNEL || GAIN == GAIN_PGDN || GAIN == GAIN_KDN || GAIN == GAIN_EXPLICIT;
+  using Sm = ChunkSmem<E, DK, BV, HAS_W>;
+  auto kern = chunk_fwd_kernel<E, DK, BV, GAIN, CHANNEL>;
+  const size_t smem = sizeof(Sm);
+  static_assert(sizeof(Sm) <= 160 * 1024, "LDS budget");
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(smem));
+  if (err != hipSuccess) return err;
+  dim3 grid(static_cast<unsigned>(a.dv / BV), static_cast<unsigned>(a.B * a.H));
+  hipLaunchKernelGGL(kern, grid, dim3(BV * 4), smem, st, a);
+  return hipGetLastError();
+}
+
+template <typename E, int DK, int BV>
+static hipError_t launch_gain(const ChunkArgs& a, int gain, bool channel, hipStream_t st) {
+  if (channel) {
+    switch (gain) {
+      case GAIN_KLA: return launch_one<E, DK, BV, GAIN_KLA, true>(a, st);
+      case GAIN_GDN: return launch_one<E, DK, BV, GAIN_GDN, true>(a, st);
+      case GAIN_PGDN: return launch_one<E, DK, BV, GAIN_PGDN, true>(a, st);
+      case GAIN_KDN: return launch_one<E, DK, BV, GAIN_KDN, true>(a, st);
+      default: return launch_one<E, DK, BV, GAIN_EXPLICIT, true>(a, st);
+    }
+  }
+  switch (gain) {
+    case GAIN_KLA: return launch_one<E, DK, BV, GAIN_KLA, false>(a, st);
+    case GAIN_GDN: return launch_one<E, DK, BV, GAIN_GDN, false>(a, st);
+    case GAIN_PGDN: return launch_one<E, DK, BV, GAIN_PGDN, false>(a, st);
+    case GAIN_KDN: return launch_one<E, DK, BV, GAIN_KDN, false>(a, st);
+    default: return launch_one<E, DK, BV, GAIN_EXPLICIT, false>(a, st);
+  }
+}
+
+hipError_t launch_chunk_fwd(const ChunkArgs& a, int io_bf16, int gain, bool channel,
+                            hipStream_t st) {
+  if (io_bf16) {
+    if (a.dk == 128) return launch_gain<uint16_t, 128, 64>(a, gain, channel, st);
+    return launch_gain<uint16_t, 64, 64>(a, gain, channel, st);
+  }
+  if (a.dk == 64) return launch_gain<float, 64, 32>(a, gain, channel, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dn

@@ -1,0 +1,267 @@
+// Host side of libdn.so: argument validation, aliasing checks and kernel
+// dispatch for the C ABI declared in include/dn.h.  Validation happens before
+// anything is enqueued; every entry point returns a dn_status.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "dn.h"
+#include "launch.hpp"
+
+#define DN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool valid_dim(int d) { return d == 64 || d == 128; }
+
+size_t io_size(int io) { return io == DN_BF16 ? 2 : 4; }
+
+struct Range {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Common descriptor checks.  `chunked` = the call walks chunks of C tokens.
+int check_desc(const dn_desc* d, bool chunked) {
+  if (!d) return DN_ERR_NULL;
+  if (d->B < 1 || d->H < 1 || d->T < 0) return DN_ERR_SHAPE;
+  if (!valid_dim(d->dk) || !valid_dim(d->dv)) return DN_ERR_SHAPE;
+  if (chunked && d->C != 64) return DN_ERR_SHAPE;
+  if (static_cast<long long>(d->B) * d->H > 65535) return DN_ERR_SHAPE;
+  if (static_cast<long long>(d->B) * d->H * d->T * (d->dk > d->dv ? d->dk : d->dv) >
+      (1LL << 40))
+    return DN_ERR_SHAPE;
+  if (d->io != DN_F32 && d->io != DN_BF16) return DN_ERR_DTYPE;
+  if (d->gain < DN_GAIN_KLA || d->gain > DN_GAIN_EXPLICIT) return DN_ERR_GAIN;
+  if (d->decay != DN_DECAY_SCALAR && d->decay != DN_DECAY_CHANNEL) return DN_ERR_GAIN;
+  if (d->gain == DN_GAIN_KLA && !(d->eps >= 0.f && std::isfinite(d->eps))) return DN_ERR_GAIN;
+  if (d->gain == DN_GAIN_PGDN && !(d->x >= 1.f && std::isfinite(d->x))) return DN_ERR_GAIN;
+  if (d->gain == DN_GAIN_KDN && !(d->mu_info > 0.f && std::isfinite(d->mu_info)))
+    return DN_ERR_GAIN;
+  return DN_OK;
+}
+
+int check_gates(const dn_desc* d, const dn_gates* g) {
+  if (!g || !g->alpha) return DN_ERR_NULL;
+  switch (d->gain) {
+    case DN_GAIN_KLA:
+    case DN_GAIN_GDN:
+      if (!g->eta) return DN_ERR_NULL;
+      break;
+    case DN_GAIN_PGDN:
+      if (!g->eta || !g->alphaP || !g->betaP || !g->mu_log) return DN_ERR_NULL;
+      break;
+    case DN_GAIN_KDN:
+      if (!g->omega || !g->r) return DN_ERR_NULL;
+      break;
+    default:
+      if (!g->w) return DN_ERR_NULL;
+  }
+  return DN_OK;
+}
+
+dn::GateArgs gate_args(const dn_desc* d, const dn_gates* g) {
+  dn::GateArgs a;
+  a.alpha = g->alpha;
+  a.eta = g->eta;
+  a.alphaP = g->alphaP;
+  a.betaP = g->betaP;
+  a.mu_log = g->mu_log;
+  a.omega = g->omega;
+  a.r = g->r;
+  a.w = g->w;
+  a.eps = d->eps;
+  a.log2x = d->gain == DN_GAIN_PGDN ? std::log2(d->x) : 0.f;
+  a.mu_info = d->mu_info;
+  return a;
+}
+
+// Byte ranges of every input a call reads, for the aliasing checks.
+int gate_ranges(const dn_desc* d, const dn_gates* g, Range* out) {
+  const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
+  const size_t es = io_size(d->io);
+  int n = 0;
+  out[n++] = {g->alpha, d->decay == DN_DECAY_CHANNEL ? bht * d->dk * es : bht * 4};
+  out[n++] = {g->eta, bht * 4};
+  out[n++] = {g->alphaP, bht * 4};
+  out[n++] = {g->betaP, bht * 4};
+  out[n++] = {g->mu_log, static_cast<size_t>(d->H) * 4};
+  out[n++] = {g->omega, bht * d->dk * es};
+  out[n++] = {g->r, bht * 4};
+  out[n++] = {g->w, bht * d->dk * es};
+  return n;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DN_OK : DN_ERR_HIP; }
+
+}  // namespace
+
+DN_EXPORT int dn_version(void) { return DN_VERSION; }
+
+DN_EXPORT const char* dn_status_string(int s) {
+  switch (s) {
+    case DN_OK: return "ok";
+    case DN_ERR_NULL: return "a required pointer is NULL";
+    case DN_ERR_SHAPE: return "unsupported shape (B, H, T, dk, dv or C)";
+    case DN_ERR_DTYPE: return "unknown io dtype";
+    case DN_ERR_GAIN: return "unknown gain or decay, or invalid gain parameter";
+    case DN_ERR_UNSUPPORTED: return "combination not built (fp32 io chunked forward needs dk = 64)";
+    case DN_ERR_HIP: return "kernel launch failed";
+    case DN_ERR_ALIAS: return "forbidden overlap between buffers";
+    default: return "unknown status";
+  }
+}
+
+DN_EXPORT int dn_chunk_fwd(const dn_desc* d, const void* q, const void* k, const void* v,
+                           const dn_gates* g, const float* S0, const float* aux0, void* o,
+                           float* S_final, float* aux_final, void* stream) {
+  int st = check_desc(d, true);
+  if (st != DN_OK) return st;
+  if (d->T > 0) {
+    if ((st = check_gates(d, g)) != DN_OK) return st;
+    if (!q || !k || !v || !o) return DN_ERR_NULL;
+  }
+  if (d->io == DN_F32 && d->dk != 64) return DN_ERR_UNSUPPORTED;
+
+  const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
+  const size_t es = io_size(d->io);
+  const size_t sbytes = static_cast<size_t>(d->B) * d->H * d->dk * d->dv * 4;
+  const size_t abytes = static_cast<size_t>(d->B) * d->H * d->dk * 4;
+  const bool has_aux = d->gain == DN_GAIN_PGDN || d->gain == DN_GAIN_KDN;
+  Range in[16];
+  const dn_gates nog{};
+  int n = gate_ranges(d, g ? g : &nog, in);
+  in[n++] = {q, bht * d->dk * es};
+  in[n++] = {k, bht * d->dk * es};
+  in[n++] = {v, bht * d->dv * es};
+  in[n++] = {S0, S0 ? sbytes : 0};
+  in[n++] = {has_aux ? aux0 : nullptr, abytes};
+  const Range ro{o, bht * d->dv * es}, rs{S_final, S_final ? sbytes : 0},
+      ra{has_aux ? aux_final : nullptr, abytes};
+  for (int i = 0; i < n; ++i) {
+    if (overlap(ro, in[i])) return DN_ERR_ALIAS;
+    // S may be updated in place: each workgroup reads and writes only its own
+    // value columns.  aux may not: every value slice of a head reads aux0.
+    const bool s_in_place = in[i].p == S0 && S_final == S0;
+    if (!s_in_place && overlap(rs, in[i])) return DN_ERR_ALIAS;
+    if (overlap(ra, in[i])) return DN_ERR_ALIAS;
+  }
+  if (overlap(ro, rs) || overlap(ro, ra) || overlap(rs, ra)) return DN_ERR_ALIAS;
+
+  dn::ChunkArgs a;
+  a.B = d->B;
+  a.H = d->H;
+  a.T = d->T;
+  a.dk = d->dk;
+  a.dv = d->dv;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = gate_args(d, g ? g : &nog);
+  a.S0 = S0;
+  a.aux0 = has_aux ? aux0 : nullptr;
+  a.o = o;
+  a.S_final = S_final;
+  a.aux_final = has_aux ? aux_final : nullptr;
+  return hip_status(dn::launch_chunk_fwd(a, d->io == DN_BF16, d->gain,
+                                         d->decay == DN_DECAY_CHANNEL,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+DN_EXPORT int dn_decode_step(const dn_desc* d, const void* q, const void* k, const void* v,
+                             const dn_gates* g, float* S, float* aux, void* o, void* stream) {
+  int st = check_desc(d, false);
+  if (st != DN_OK) return st;
+  if (d->T != 1) return DN_ERR_SHAPE;
+  if ((st = check_gates(d, g)) != DN_OK) return st;
+  const bool has_aux = d->gain == DN_GAIN_PGDN || d->gain == DN_GAIN_KDN;
+  if (!q || !k || !v || !o || !S || (has_aux && !aux)) return DN_ERR_NULL;
+
+  const size_t bh = static_cast<size_t>(d->B) * d->H;
+  const size_t es = io_size(d->io);
+  Range in[16];
+  int n = gate_ranges(d, g, in);
+  in[n++] = {q, bh * d->dk * es};
+  in[n++] = {k, bh * d->dk * es};
+  in[n++] = {v, bh * d->dv * es};
+  const Range ro{o, bh * d->dv * es}, rs{S, bh * d->dk * d->dv * 4},
+      ra{has_aux ? aux : nullptr, bh * d->dk * 4};
+  for (int i = 0; i < n; ++i)
+    if (overlap(ro, in[i]) || overlap(rs, in[i]) || overlap(ra, in[i])) return DN_ERR_ALIAS;
+  if (overlap(ro, rs) || overlap(ro, ra) || overlap(rs, ra)) return DN_ERR_ALIAS;
+
+  dn::DecodeArgs a;
+  a.N = d->B;
+  a.H = d->H;
+  a.dk = d->dk;
+  a.dv = d->dv;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  const dn::GateArgs ga = gate_args(d, g);
+  a.alpha = ga.alpha;
+  a.eta = ga.eta;
+  a.alphaP = ga.alphaP;
+  a.betaP = ga.betaP;
+  a.mu_log = ga.mu_log;
+  a.omega = ga.omega;
+  a.r = ga.r;
+  a.w = ga.w;
+  a.eps = ga.eps;
+  a.log2x = ga.log2x;
+  a.mu_info = ga.mu_info;
+  a.S = S;
+  a.aux = has_aux ? aux : nullptr;
+  a.o = o;
+  return hip_status(dn::launch_decode(a, d->io == DN_BF16, d->gain, d->decay == DN_DECAY_CHANNEL,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+DN_EXPORT int dn_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, const float* aux0,
+                           float* w_out, float* g_out, float* aux_chunk, float* aux_final,
+                           void* stream) {
+  int st = check_desc(d, true);
+  if (st != DN_OK) return st;
+  if ((st = check_gates(d, g)) != DN_OK) return st;
+  if (!k || !w_out) return DN_ERR_NULL;
+  const bool has_aux = d->gain == DN_GAIN_PGDN || d->gain == DN_GAIN_KDN;
+  const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
+  const size_t es = io_size(d->io);
+  const size_t nch = (static_cast<size_t>(d->T) + d->C - 1) / d->C;
+  Range in[16];
+  int n = gate_ranges(d, g, in);
+  in[n++] = {k, bht * d->dk * es};
+  in[n++] = {has_aux ? aux0 : nullptr, static_cast<size_t>(d->B) * d->H * d->dk * 4};
+  Range outs[4] = {{w_out, bht * d->dk * 4},
+                   {g_out, g_out ? bht * (d->decay == DN_DECAY_CHANNEL ? d->dk : 1) * 4 : 0},
+                   {has_aux ? aux_chunk : nullptr, static_cast<size_t>(d->B) * d->H * nch * d->dk * 4},
+                   {has_aux ? aux_final : nullptr, static_cast<size_t>(d->B) * d->H * d->dk * 4}};
+  for (int j = 0; j < 4; ++j) {
+    for (int i = 0; i < n; ++i)
+      if (overlap(outs[j], in[i])) return DN_ERR_ALIAS;
+    for (int i = j + 1; i < 4; ++i)
+      if (overlap(outs[j], outs[i])) return DN_ERR_ALIAS;
+  }
+  dn::GainPrepArgs a;
+  a.B = d->B;
+  a.H = d->H;
+  a.T = d->T;
+  a.dk = d->dk;
+  a.k = k;
+  a.g = gate_args(d, g);
+  a.aux0 = has_aux ? aux0 : nullptr;
+  a.w_out = w_out;
+  a.g_out = g_out;
+  a.aux_chunk = has_aux ? aux_chunk : nullptr;
+  a.aux_final = has_aux ? aux_final : nullptr;
+  return hip_status(dn::launch_gain_prep(a, d->io == DN_BF16, d->gain,
+                                         d->decay == DN_DECAY_CHANNEL,
+                                         static_cast<hipStream_t>(stream)));
+}

@@ -1,0 +1,39 @@
+// Per-element write-gain arithmetic shared by the decode, gain-prep and
+// chunked-forward kernels, so all three evaluate the gains identically.
+#pragma once
+
+#include "common.hpp"
+
+namespace dn {
+
+enum Gain { GAIN_KLA = 0, GAIN_GDN = 1, GAIN_PGDN = 2, GAIN_KDN = 3, GAIN_EXPLICIT = 4 };
+
+// KLA step size eta / (||k||^2 + eps)  (Kaczmarz Linear Attention §2.1).
+__device__ __forceinline__ float kla_beta(float eta, float knorm2, float eps) {
+  return eta / (knorm2 + eps);
+}
+
+// PGDN statistic update A_t = alphaP A_{t-1} + betaP k^2 and the bounded
+// write scale B = exp(-log(x) * softsign(log A_t - mu))  (Preconditioned
+// DeltaNet §2.4, Eq. 9).  log2x = log2(x), so exp(-ln x * s) = 2^(-log2x * s).
+__device__ __forceinline__ float pgdn_stat(float A, float aP, float bP, float k) {
+  return fmaf(aP, A, bP * k * k);
+}
+__device__ __forceinline__ float pgdn_scale(float A, float mu, float log2x) {
+  const float r = logf(A) - mu;
+  const float s = r / (1.0f + fabsf(r));
+  return exp2f(-log2x * s);
+}
+
+// Diagonal KDN predicted variance p_hat = alpha^2 p + omega and the
+// reverse-KL update with information scaling p = p_hat / (1 + u p_hat),
+// u = (mu / r) k^2  (Kalman Delta Networks §2.4 Eqs. 23-30, §2.5).
+__device__ __forceinline__ float kdn_predict(float a, float p, float om) {
+  return fmaf(a * a, p, om);
+}
+__device__ __forceinline__ float kdn_update(float p_hat, float k, float mu_over_r) {
+  const float u = mu_over_r * k * k;
+  return p_hat / fmaf(u, p_hat, 1.0f);
+}
+
+}  // namespace dn

@@ -1,0 +1,134 @@
+"""The C-ABI library: it loads, exports what include/dn.h declares, and rejects
+invalid arguments on the host before launching anything.
+
+These run without a GPU: every call here fails validation, so no HIP call is
+made (the pointers are never dereferenced).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from recurrent_sequence_mixer_amd import dn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dn.LIB_PATH),
+                                reason="libdn.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    decl = declared_functions()
+    assert decl == sorted(dn.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", dn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if " T dn_" in ln})
+    assert exported == decl
+    L = dn.lib()
+    for name in decl:
+        assert hasattr(L, name)
+
+
+def test_version_and_status_strings():
+    assert dn.lib().dn_version() == 1
+    for code in dn.STATUS:
+        assert dn.status_string(code)
+    assert dn.status_string(12345) == "unknown status"
+
+
+FAKE = 1 << 40  # a host integer that is never dereferenced
+
+
+def _gates(**kw):
+    g = dict(alpha=FAKE, eta=FAKE + (1 << 30), alphaP=None, betaP=None, mu_log=None, omega=None,
+             r=None, w=None)
+    g.update(kw)
+    return dn.DnGates(*[g[n] for n in ("alpha", "eta", "alphaP", "betaP", "mu_log", "omega", "r", "w")])
+
+
+def _chunk(desc, gates=None, q=FAKE + (2 << 30), k=FAKE + (3 << 30), v=FAKE + (4 << 30),
+           o=FAKE + (5 << 30), S0=None, aux0=None, S_final=None, aux_final=None):
+    gates = gates or _gates()
+    return dn.lib().dn_chunk_fwd(ctypes.byref(desc), q, k, v, ctypes.byref(gates), S0, aux0, o,
+                                 S_final, aux_final, None)
+
+
+def _desc(**kw):
+    base = dict(B=2, H=3, T=100, dk=128, dv=128, io=1, gain="kla", decay="scalar")
+    base.update(kw)
+    return dn.make_desc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=96), -2), (dict(dv=32), -2), (dict(B=0), -2), (dict(H=0), -2), (dict(T=-1), -2),
+    (dict(B=300, H=300), -2), (dict(io=7), -3), (dict(gain=9), -4), (dict(decay=3), -4),
+    (dict(eps=-1.0), -4), (dict(gain="pgdn", x=0.5), -4), (dict(gain="kdn", mu_info=0.0), -4),
+    (dict(io=0, dk=128), -6),
+])
+def test_chunk_fwd_rejects_bad_descriptor(kw, status):
+    assert _chunk(_desc(**kw)) == status
+
+
+def test_chunk_fwd_rejects_bad_chunk_length():
+    d = _desc()
+    d.C = 32
+    assert _chunk(d) == -2
+
+
+def test_chunk_fwd_rejects_missing_pointers():
+    assert _chunk(_desc(), q=None) == -1
+    assert _chunk(_desc(), o=None) == -1
+    assert _chunk(_desc(), gates=_gates(alpha=None)) == -1
+    assert _chunk(_desc(), gates=_gates(eta=None)) == -1
+    assert _chunk(_desc(gain="pgdn")) == -1  # alphaP, betaP, mu_log missing
+    assert _chunk(_desc(gain="kdn")) == -1  # omega, r missing
+    assert _chunk(_desc(gain="explicit")) == -1  # w missing
+    assert dn.lib().dn_chunk_fwd(None, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None,
+                                 None) == -1
+
+
+def test_chunk_fwd_rejects_overlaps():
+    d = _desc(B=1, H=1, T=64, dk=128, dv=128)
+    qbytes = 64 * 128 * 2
+    q = FAKE + (2 << 30)
+    # output overlapping an input
+    assert _chunk(d, q=q, o=q + qbytes // 2) == -8
+    # S_final overlapping S0 without being the same buffer
+    S0 = FAKE + (8 << 30)
+    assert _chunk(d, S0=S0, S_final=S0 + 4) == -8
+    # S_final overlapping the output
+    assert _chunk(d, S_final=FAKE + (5 << 30)) == -8
+
+
+def test_decode_rejects_bad_arguments():
+    L = dn.lib()
+    g = _gates()
+    f = lambda desc, S=FAKE + (9 << 30), aux=None: L.dn_decode_step(
+        ctypes.byref(desc), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30), ctypes.byref(g),
+        S, aux, FAKE + (5 << 30), None)
+    assert f(_desc(T=2)) == -2
+    assert f(_desc(T=1), S=None) == -1
+    assert f(_desc(T=1, gain="pgdn")) == -1
+    assert f(_desc(T=1, dk=48)) == -2
+
+
+def test_gain_prep_rejects_bad_arguments():
+    L = dn.lib()
+    g = _gates()
+    d = _desc()
+    assert L.dn_gain_prep(ctypes.byref(d), FAKE, ctypes.byref(g), None, None, None, None, None,
+                          None) == -1
+    assert L.dn_gain_prep(ctypes.byref(_desc(dk=80)), FAKE, ctypes.byref(g), None, FAKE + (7 << 30),
+                          None, None, None, None) == -2
+    # w_out overlapping k
+    assert L.dn_gain_prep(ctypes.byref(d), FAKE + (3 << 30), ctypes.byref(g), None, FAKE + (3 << 30),
+                          None, None, None, None) == -8

@@ -1,0 +1,154 @@
+"""GPU parity of the batched decode step and of the standalone gain scans
+against the fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle.recurrence import forward, run_workload
+from parity import TOL, flat_heads, gpu_chunk, max_rel_err
+from recurrent_sequence_mixer_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _dn():
+    from recurrent_sequence_mixer_amd import dn
+    return dn
+
+
+def test_workload0_as_decode_steps_f32():
+    """Workload 0 (KLA fp32) token by token through dn_decode_step, 256 steps."""
+    dn = _dn()
+    wl = W.WORKLOADS[0]
+    inp = W.generate(wl)
+    t = dn.to_device(inp, torch.float32)
+    S = t["S0"].clone()  # N = B = 1 sequence, H = 1 head
+    outs = []
+    for s in range(wl.T):
+        step = lambda name: t[name][:, :, s].contiguous()
+        o = dn.decode_step(step("q"), step("k"), step("v"), {"alpha": step("alpha"), "eta": step("eta")},
+                           S, gain="kla", eps=wl.eps)
+        outs.append(o)
+    torch.cuda.synchronize()
+    o = torch.stack(outs, dim=2).cpu().numpy()
+    o_ref, S_ref, _, _ = run_workload(wl, inp)
+    eo, es = max_rel_err(flat_heads(o), o_ref), max_rel_err(flat_heads(S.cpu().numpy()), S_ref)
+    print(f"decode f32: o {eo:.2e} S {es:.2e}")
+    assert eo <= TOL["f32"] and es <= TOL["f32"]
+
+
+@pytest.mark.parametrize("gain,decay", [("kla", "scalar"), ("gdn", "scalar"), ("pgdn", "scalar"),
+                                        ("kdn", "channel"), ("kdn", "scalar"), ("kla", "channel")])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128)])
+def test_decode_gains(gain, decay, io, dk, dv):
+    """A short prefill-free decode (12 steps) over 6 sequences x 3 heads."""
+    dn = _dn()
+    keys = "unit" if gain in ("gdn", "pgdn") else "scaled"
+    wl = W.Workload("dec", gain, decay, io, 6, 3, 12, dk, dv, keys=keys, seed=21)
+    inp = W.generate(wl)
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    t = dn.to_device(inp, dt)
+    S = t["S0"].clone()
+    aux = torch.ones((6, 3, dk), device="cuda") if gain in ("pgdn", "kdn") else None
+    outs = []
+    for s in range(wl.T):
+        gates = {n: t[n][:, :, s].contiguous() for n in ("alpha", "eta", "alphaP", "betaP", "omega", "r")
+                 if n in t}
+        if "mu_log" in t:
+            gates["mu_log"] = t["mu_log"]
+        outs.append(dn.decode_step(t["q"][:, :, s].contiguous(), t["k"][:, :, s].contiguous(),
+                                   t["v"][:, :, s].contiguous(), gates, S, aux, gain=gain, eps=wl.eps,
+                                   x=wl.x, mu_info=wl.mu_info))
+    torch.cuda.synchronize()
+    o = torch.stack(outs, dim=2).float().cpu().numpy()
+    o_ref, S_ref, aux_ref, _ = run_workload(wl, inp)
+    eo, es = max_rel_err(flat_heads(o), o_ref), max_rel_err(flat_heads(S.cpu().numpy()), S_ref)
+    tol = TOL[io]
+    print(f"decode {gain}/{decay}/{io} {dk}x{dv}: o {eo:.2e} S {es:.2e}")
+    assert eo <= tol and es <= tol
+    if aux is not None:
+        assert max_rel_err(flat_heads(aux.cpu().numpy()), aux_ref) <= 1e-5
+
+
+def test_decode_full_size_sampled():
+    """Workload 4 at its full size (512 sequences x 16 heads), 8 steps, sampled heads."""
+    dn = _dn()
+    wl = W.WORKLOADS[4]
+    S0 = W.generate_decode_state(wl)
+    S = torch.from_numpy(S0).cuda()
+    steps = [W.generate_decode_step(wl, s) for s in range(8)]
+    outs = []
+    for st in steps:
+        t = dn.to_device(st, torch.bfloat16)
+        outs.append(dn.decode_step(t["q"], t["k"], t["v"], {"alpha": t["alpha"], "eta": t["eta"]}, S,
+                                   gain="kla", eps=wl.eps))
+    torch.cuda.synchronize()
+    heads = [0, 4097, 8191]
+    sel = lambda a: a.reshape((wl.N * wl.H,) + a.shape[2:])[heads]
+    stack = lambda name: np.stack([sel(st[name]) for st in steps], axis=1)
+    o_ref, S_ref, _, _ = forward(stack("q"), stack("k"), stack("v"), "kla", stack("alpha"),
+                                 eta=stack("eta"), eps=wl.eps, S0=sel(S0))
+    o = np.stack([sel(x.float().cpu().numpy()) for x in outs], axis=1)
+    eo, es = max_rel_err(o, o_ref), max_rel_err(sel(S.cpu().numpy()), S_ref)
+    print(f"decode full size: o {eo:.2e} S {es:.2e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_prefill_then_decode_equals_one_pass():
+    """dn_chunk_fwd over a prefix, then dn_decode_step token by token, against
+    the oracle over the whole sequence."""
+    dn = _dn()
+    wl = W.Workload("kdn_pd", "kdn", "channel", "bf16", 2, 2, 140, 128, 128, seed=9)
+    inp = W.generate(wl)
+    t = dn.to_device(inp, torch.bfloat16)
+    P = 100
+    pre = {n: t[n][:, :, :P].contiguous() for n in ("alpha", "omega", "r")}
+    o_pre, S, aux = dn.chunk_fwd(t["q"][:, :, :P].contiguous(), t["k"][:, :, :P].contiguous(),
+                                 t["v"][:, :, :P].contiguous(), pre, gain="kdn", mu_info=wl.mu_info,
+                                 S0=t["S0"])
+    outs = [o_pre]
+    for s in range(P, wl.T):
+        g = {n: t[n][:, :, s].contiguous() for n in ("alpha", "omega", "r")}
+        outs.append(dn.decode_step(t["q"][:, :, s].contiguous(), t["k"][:, :, s].contiguous(),
+                                   t["v"][:, :, s].contiguous(), g, S, aux, gain="kdn",
+                                   mu_info=wl.mu_info)[:, :, None])
+    torch.cuda.synchronize()
+    o = torch.cat(outs, dim=2).float().cpu().numpy()
+    o_ref, S_ref, aux_ref, _ = run_workload(wl, inp)
+    assert max_rel_err(flat_heads(o), o_ref) <= TOL["bf16"]
+    assert max_rel_err(flat_heads(S.cpu().numpy()), S_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("gain,decay,io", [("kla", "scalar", "bf16"), ("pgdn", "scalar", "bf16"),
+                                           ("kdn", "channel", "bf16"), ("kdn", "channel", "f32"),
+                                           ("gdn", "channel", "f32")])
+def test_gain_prep_per_token(gain, decay, io):
+    """dn_gain_prep's per-token write vectors, chunk-start aux and in-chunk
+    cumulative log-decay against the oracle's trace."""
+    dn = _dn()
+    keys = "unit" if gain in ("gdn", "pgdn") else "scaled"
+    wl = W.Workload("gp", gain, decay, io, 2, 3, 150, 128 if io == "bf16" else 64,
+                    128 if io == "bf16" else 64, keys=keys, seed=31)
+    inp = W.generate(wl)
+    t = dn.to_device(inp, torch.float32 if io == "f32" else torch.bfloat16)
+    gates = {n: t[n] for n in ("alpha", "eta", "alphaP", "betaP", "mu_log", "omega", "r") if n in t}
+    w, g, aux_chunk, aux_final = dn.gain_prep(t["k"], gates, gain=gain, eps=wl.eps, x=wl.x,
+                                              mu_info=wl.mu_info)
+    torch.cuda.synchronize()
+    _, _, aux_ref, tr = run_workload(wl, inp, record=True)
+    ew = max_rel_err(flat_heads(w.cpu().numpy()), tr["w"])
+    print(f"gain_prep {gain}: w {ew:.2e}")
+    assert ew <= 1e-5
+    alpha = flat_heads(inp["alpha"]).astype(np.float64)
+    T = wl.T
+    G = np.zeros_like(alpha)
+    for c0 in range(0, T, 64):
+        G[:, c0:c0 + 64] = np.cumsum(np.log(alpha[:, c0:c0 + 64]), axis=1)
+    np.testing.assert_allclose(flat_heads(g.cpu().numpy()), G, rtol=1e-5, atol=1e-5)
+    if aux_ref is not None:
+        assert max_rel_err(flat_heads(aux_final.cpu().numpy()), aux_ref) <= 1e-5
+        key = "A" if gain == "pgdn" else "p"
+        ac = flat_heads(aux_chunk.cpu().numpy())
+        for ci, c0 in enumerate(range(64, T, 64)):
+            assert max_rel_err(ac[:, ci + 1], tr[key][:, c0 - 1]) <= 1e-5

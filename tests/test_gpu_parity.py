@@ -1,0 +1,159 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Bar: max relative error per (b, h) slice of o and of S_T within 1e-4 for
+fp32 io and 2e-2 for bf16 io (fp32 accumulation and state).  Small cases are
+compared element by element over every head; the full-size workloads run in
+the launch configuration the benchmark times and are compared on sampled
+heads, each evaluated in full by the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from parity import TOL, flat_heads, gpu_chunk, max_rel_err, oracle_chunk
+from recurrent_sequence_mixer_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(wl, inp, heads=None, o_gpu=None, S_gpu=None, aux_gpu=None, tol=None):
+    tol = TOL[wl.io] if tol is None else tol
+    o_ref, S_ref, aux_ref = oracle_chunk(wl, inp, heads)
+    eo = max_rel_err(flat_heads(o_gpu, heads), o_ref)
+    es = max_rel_err(flat_heads(S_gpu, heads), S_ref)
+    print(f"{wl.name} T={wl.T}: o {eo:.2e} S {es:.2e} (tol {tol:g})", flush=True)
+    assert eo <= tol and es <= tol
+    if aux_ref is not None and aux_gpu is not None:
+        ea = max_rel_err(flat_heads(aux_gpu, heads), aux_ref)
+        print(f"   aux {ea:.2e}", flush=True)
+        assert ea <= (1e-5 if wl.io == "f32" else 1e-3)
+    return eo, es
+
+
+# ---------------------------------------------------------------- fp32 (workload 0)
+
+def test_kla_f32_workload0():
+    wl = W.WORKLOADS[0]
+    inp = W.generate(wl)
+    o, S, _ = gpu_chunk(wl, inp)
+    _check(wl, inp, None, o, S)
+
+
+@pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 130, 200])
+@pytest.mark.parametrize("gain", ["kla", "gdn", "pgdn", "kdn"])
+def test_f32_gains_ragged(gain, T):
+    decay = "channel" if gain == "kdn" else "scalar"
+    keys = "unit" if gain in ("gdn", "pgdn") else "scaled"
+    wl = W.Workload(f"{gain}_f32", gain, decay, "f32", 2, 3, T, 64, 64, keys=keys, seed=10 + T)
+    inp = W.generate(wl)
+    o, S, aux = gpu_chunk(wl, inp)
+    _check(wl, inp, None, o, S, aux)
+
+
+# ---------------------------------------------------------------- bf16, small
+
+@pytest.mark.parametrize("T", [1, 63, 65, 200, 333])
+@pytest.mark.parametrize("gain,decay,keys", [("kla", "scalar", "scaled"), ("gdn", "scalar", "unit"),
+                                             ("pgdn", "scalar", "unit"), ("kdn", "channel", "scaled"),
+                                             ("kla", "channel", "scaled"), ("kdn", "scalar", "scaled"),
+                                             ("pgdn", "channel", "unit")])
+def test_bf16_gains_ragged(gain, decay, keys, T):
+    wl = W.Workload(f"{gain}_{decay}_bf16", gain, decay, "bf16", 2, 2, T, 128, 128, keys=keys,
+                    seed=100 + T)
+    inp = W.generate(wl)
+    o, S, aux = gpu_chunk(wl, inp)
+    _check(wl, inp, None, o, S, aux)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+def test_bf16_other_head_dims(dk, dv):
+    wl = W.Workload("kla_dims", "kla", "scalar", "bf16", 2, 2, 150, dk, dv, seed=7)
+    inp = W.generate(wl)
+    o, S, _ = gpu_chunk(wl, inp)
+    _check(wl, inp, None, o, S)
+
+
+# ---------------------------------------------------------------- full size workloads
+
+@pytest.mark.parametrize("idx", [1, 2, 3])
+def test_full_size_sampled_heads(idx):
+    wl = W.WORKLOADS[idx]
+    inp = W.generate(wl)
+    o, S, aux = gpu_chunk(wl, inp)
+    nheads = wl.B * wl.H
+    heads = [0, nheads // 3, nheads - 1]
+    _check(wl, inp, heads, o, S, aux)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_empty_sequence_copies_state():
+    wl = W.Workload("kdn_empty", "kdn", "channel", "bf16", 1, 2, 0, 128, 128, seed=3)
+    inp = W.generate(wl.replace(T=5))
+    inp = {k: (v[:, :, :0] if v.ndim >= 3 and k not in ("S0",) else v) for k, v in inp.items()}
+    inp["aux0"] = np.random.default_rng(0).uniform(0.5, 2, size=(1, 2, 128)).astype(np.float32)
+    o, S, aux = gpu_chunk(wl, inp)
+    np.testing.assert_array_equal(S, inp["S0"])
+    np.testing.assert_array_equal(aux, inp["aux0"])
+
+
+def test_resume_equals_single_call():
+    """chunk_fwd(T1) -> (S, aux) -> chunk_fwd(T2) against one oracle pass."""
+    from recurrent_sequence_mixer_amd import dn
+    wl = W.Workload("pgdn_resume", "pgdn", "scalar", "bf16", 2, 2, 300, 128, 128, keys="unit", seed=5)
+    inp = W.generate(wl)
+    t = dn.to_device(inp, torch.bfloat16)
+    T1 = 130
+    part = lambda x, s: x[:, :, s].contiguous()
+    g = lambda s: {n: part(t[n], s) for n in ("alpha", "eta", "alphaP", "betaP")} | {"mu_log": t["mu_log"]}
+    kw = dict(gain="pgdn", x=wl.x)
+    S = t["S0"].clone()
+    aux_a = torch.ones((2, 2, 128), device="cuda")
+    aux_b = torch.empty_like(aux_a)
+    o1, _, _ = dn.chunk_fwd(part(t["q"], slice(0, T1)), part(t["k"], slice(0, T1)),
+                            part(t["v"], slice(0, T1)), g(slice(0, T1)), S0=S, aux0=aux_a,
+                            S_final=S, aux_final=aux_b, **kw)  # state in place
+    o2, _, _ = dn.chunk_fwd(part(t["q"], slice(T1, None)), part(t["k"], slice(T1, None)),
+                            part(t["v"], slice(T1, None)), g(slice(T1, None)), S0=S, aux0=aux_b,
+                            S_final=S, aux_final=aux_a, **kw)
+    torch.cuda.synchronize()
+    o = torch.cat([o1, o2], dim=2).float().cpu().numpy()
+    _check(wl, inp, None, o, S.cpu().numpy(), aux_a.cpu().numpy())
+
+
+def test_deterministic_run_to_run():
+    wl = W.WORKLOADS[3].replace(B=1, H=4, T=700)
+    inp = W.generate(wl)
+    a = gpu_chunk(wl, inp)
+    b = gpu_chunk(wl, inp)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_explicit_gain_reads_out_ridge_solution():
+    """Exact ATK write keys (Sherman-Morrison, Preconditioned DeltaNet §2.2)
+    with no decay: the readout is the ridge solution at every step."""
+    from oracle import kalman
+    from recurrent_sequence_mixer_amd import dn
+    T, d, lam = 150, 64, 2.0
+    rng = np.random.default_rng(11)
+    K = rng.standard_normal((T, d)).astype(np.float32)
+    V = rng.standard_normal((T, d)).astype(np.float32)
+    Qr = rng.standard_normal((T, d)).astype(np.float32)
+    Wv, _ = kalman.atk_write_vectors(K.astype(np.float64), lam)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()[None, None]
+    o, S, _ = dn.chunk_fwd(dev(Qr), dev(K), dev(V), {"alpha": torch.ones((1, 1, T), device="cuda"),
+                                                    "w": dev(Wv)}, gain="explicit")
+    torch.cuda.synchronize()
+    S_ridge = kalman.ridge(K.astype(np.float64), V.astype(np.float64), lam)
+    err = np.abs(S.cpu().numpy()[0, 0] - S_ridge).max() / np.abs(S_ridge).max()
+    print(f"ridge S err {err:.2e}")
+    assert err < 1e-4
+    o = o.cpu().numpy()[0, 0]
+    for t in (0, 63, 64, 149):
+        ref = kalman.ridge(K[:t + 1].astype(np.float64), V[:t + 1].astype(np.float64), lam).T @ Qr[t]
+        assert np.abs(o[t] - ref).max() <= 1e-4 * np.abs(ref).max() + 1e-5
