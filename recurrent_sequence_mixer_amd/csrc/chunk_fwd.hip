@@ -19,8 +19,8 @@
 //
 // Per chunk, in this order (barriers between the numbered steps):
 //   1. the chunk's k, q, v slice and gates move from staging registers (loaded
-//      from HBM during the previous chunk) into LDS, and the next chunk's
-//      loads are issued;
+//      from HBM during the previous chunk) into LDS, the next chunk's loads
+//      are issued, and the previous chunk's output tile is stored;
 //   2. gains: write vectors w_t (KLA/GDN/PGDN/KDN/explicit) and cumulative
 //      log2-decay; the PGDN statistic A and the KDN variance p are carried
 //      across chunks in registers of the thread owning the key channel;
@@ -34,7 +34,8 @@
 //      S = diag(g_n) S + Wtil^T U.  With bf16 operands the solve and M U run
 //      on 16x16x16 MFMAs whose B operand is the accumulator layout of U, so U
 //      never leaves registers;
-//   7. the output tile goes to HBM in 16-byte rows.
+//   7. the output tile is staged in LDS and leaves in 16-byte rows at the
+//      start of the next chunk.
 // Operands are bf16 (fp32 for fp32 io) with fp32 accumulation; S, the
 // diagonal-block inverses and all gain arithmetic stay fp32.
 //
@@ -89,6 +90,14 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// PGDN write scale B(A) = exp(-ln(x) s), s = r / (1 + |r|), r = ln A - mu
+// (Preconditioned DeltaNet §2.4, Eq. 9) on the hardware log2 / rcp / exp2.
+__device__ __forceinline__ float pgdn_scale_fast(float A, float mu, float log2x) {
+  const float r = fast_log2(A) * 0.69314718055994531f - mu;
+  const float sft = r * __builtin_amdgcn_rcpf(1.0f + fabsf(r));
+  return fast_exp2(-log2x * sft);
+}
+
 // bf16 16x16x16 MFMA pieces.  Lane l: A row l % 16, k = 4 (l / 16) .. +3;
 // B column l % 16, k = 4 (l / 16) .. +3; accumulator rows 4 (l / 16) .. +3 of
 // column l % 16.  The accumulator of one product is therefore, packed to
@@ -130,6 +139,10 @@ struct ChunkSmem {
   alignas(16) E o[CH * BV];              // output tile [t][c]
   alignas(16) float ld[4 * 16 * 16];     // diagonal 16x16 blocks of L, fp32
   alignas(16) float g2[CH];              // scalar decay: cumulative log2-decay
+  alignas(16) float gam[CH];             // scalar decay: 2^g2
+  alignas(16) float ah[DK];              // PGDN: statistic after the first half-chunk
+  alignas(16) float aprod[CH];           // PGDN: prefix products of alphaP over the second half
+  alignas(16) float acarry[DK];          // PGDN: statistic carried between chunks
   alignas(16) float gmid[DK];            // channel decay: 2^Gmid per channel
   alignas(16) float gn[DK];              // channel decay: 2^Gn per channel
   float cs[CH];                          // column scale of the L, M products
@@ -145,7 +158,10 @@ void chunk_fwd_kernel(ChunkArgs a) {
   constexpr int NT = 64 * NW;
   constexpr bool BF16 = sizeof(E) == 2;
   constexpr bool HAS_W = CHANNEL || GAIN == GAIN_PGDN || GAIN == GAIN_KDN || GAIN == GAIN_EXPLICIT;
-  constexpr bool SCAN = CHANNEL || GAIN == GAIN_PGDN || GAIN == GAIN_KDN;
+  // PGDN with scalar decay: the statistic scan is split in two half-chunks
+  // over 2 DK threads and the transcendental work is spread over all of them
+  constexpr bool PG2 = GAIN == GAIN_PGDN && !CHANNEL && NT >= 2 * DK;
+  constexpr bool SCAN = CHANNEL || (GAIN == GAIN_PGDN && !PG2) || GAIN == GAIN_KDN;
   using Sm = ChunkSmem<E, DK, BV, HAS_W>;
   constexpr int PK = Sm::PK, PT = Sm::PT, P16 = Sm::P16;
   constexpr int VEC = 16 / sizeof(E);            // elements per 16-byte access
@@ -164,11 +180,27 @@ void chunk_fwd_kernel(ChunkArgs a) {
   E* const sM = sm.lm + CH * PT;  // M
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
-  const int bh = blockIdx.y;
+  // XCD-aware mapping of the 1-D grid: consecutive workgroups are dealt to
+  // the 8 XCDs in turn, so the value slices of one head get ids that are
+  // equal modulo 8 and share that XCD's L2 (k and q are read once from HBM).
+  const int ns = a.dv / BV;
+  const int nwg = ns * a.B * a.H;
+  int bh, slice;
+  {
+    const int L = blockIdx.x;
+    if (nwg % 8 == 0 && (nwg / 8) % ns == 0) {
+      const int xcd = L % 8, r = L / 8;
+      slice = r % ns;
+      bh = xcd * (nwg / 8 / ns) + r / ns;
+    } else {
+      slice = L % ns;
+      bh = L / ns;
+    }
+  }
   const int h = bh % a.H;
-  const int col0 = blockIdx.x * BV;  // first value column of this slice
+  const int col0 = slice * BV;  // first value column of this slice
   const int T = a.T;
   const int nchunks = (T + CH - 1) / CH;
   const long qk_base = static_cast<long>(bh) * T * DK;
@@ -198,120 +230,138 @@ void chunk_fwd_kernel(ChunkArgs a) {
     aux[cc] = (d < DK && a.aux0) ? a.aux0[static_cast<long>(bh) * DK + d] : 1.f;
   }
 
+  if constexpr (PG2) {
+    if (tid < DK) sm.acarry[tid] = aux[0];
+  }
+
   // ---- register staging of one chunk's inputs
   u32x4 pk[KV_LOADS], pq[KV_LOADS], pw[GAIN == GAIN_EXPLICIT ? KV_LOADS : 1];
   u32x4 pal[CHANNEL ? KV_LOADS : 1], pom[GAIN == GAIN_KDN ? KV_LOADS : 1];
   u32x4 pv[V_LOADS];
   float p_eta = 0.f, p_alpha = 1.f, p_ap = 1.f, p_bp = 0.f, p_r = 1.f;
 
-  // Loads are branch-free: out-of-range tokens read row 0 of the chunk
-  // (in range whenever the chunk exists) and are replaced by neutral values.
-  auto fetch = [&](int c) __attribute__((always_inline)) {
+  // Loads are unconditional: out-of-range tokens read row 0 of the chunk (in
+  // range whenever the chunk exists) and are replaced by neutral values when
+  // the registers are stashed into LDS, so no load result is consumed before
+  // the next chunk.  A chunk is fetched in three parts issued at different
+  // points of the previous chunk: part 0 = k (and explicit w, channel alpha),
+  // 1 = q (and KDN omega), 2 = v and the per-token gates.
+  auto fetch = [&](int c, int part) __attribute__((always_inline)) {
     const int t0 = c * CH;
     const int n = min(CH, T - t0);
-    const u32x4 z = {0u, 0u, 0u, 0u};
+    if (part < 2) {
 #pragma unroll
-    for (int j = 0; j < KV_LOADS; ++j) {
-      const int e = (tid + j * NT) * VEC;  // element index inside the [CH][DK] tile
-      const int t = e / DK, d = e % DK;
-      const bool ok = t < n;
-      const long off = static_cast<long>(t0 + (ok ? t : 0)) * DK + d;
-      const u32x4 kk = *reinterpret_cast<const u32x4*>(gk + off);
-      const u32x4 qq = *reinterpret_cast<const u32x4*>(gq + off);
-      pk[j] = ok ? kk : z;
-      pq[j] = ok ? qq : z;
-      if constexpr (GAIN == GAIN_EXPLICIT) {
-        const u32x4 ww =
-            *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g.w) + qk_base + off);
-        pw[j] = ok ? ww : z;
+      for (int j = 0; j < KV_LOADS; ++j) {
+        const int e = (tid + j * NT) * VEC;  // element index inside the [CH][DK] tile
+        const int t = e / DK, d = e % DK;
+        const long off = static_cast<long>(t0 + (t < n ? t : 0)) * DK + d;
+        if (part == 0) {
+          pk[j] = *reinterpret_cast<const u32x4*>(gk + off);
+          if constexpr (GAIN == GAIN_EXPLICIT)
+            pw[j] = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g.w) + qk_base + off);
+          if constexpr (CHANNEL)
+            pal[j] = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g.alpha) + qk_base + off);
+        } else {
+          pq[j] = *reinterpret_cast<const u32x4*>(gq + off);
+          if constexpr (GAIN == GAIN_KDN)
+            pom[j] = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g.omega) + qk_base + off);
+        }
       }
-      if constexpr (CHANNEL) {
-        // padded tokens decay by exactly 1
-        const u32x4 one4 = BF16 ? u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}
-                                : u32x4{0x3F800000u, 0x3F800000u, 0x3F800000u, 0x3F800000u};
-        const u32x4 al =
-            *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g.alpha) + qk_base + off);
-        pal[j] = ok ? al : one4;
-      }
-      if constexpr (GAIN == GAIN_KDN) {
-        const u32x4 om =
-            *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g.omega) + qk_base + off);
-        pom[j] = ok ? om : z;
-      }
+      return;
     }
 #pragma unroll
     for (int j = 0; j < V_LOADS; ++j) {
       const int e = (tid + j * NT) * VEC;
       const int t = e / BV, cc = e % BV;
       const bool ok = e < CH * BV && t < n;
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(
-          gv + static_cast<long>(t0 + (ok ? t : 0)) * a.dv + col0 + (ok ? cc : 0));
-      pv[j] = ok ? vv : z;
+      pv[j] = *reinterpret_cast<const u32x4*>(gv + static_cast<long>(t0 + (ok ? t : 0)) * a.dv +
+                                              col0 + (ok ? cc : 0));
     }
     if (tid < CH) {
-      const bool ok = tid < n;
-      const long ti = static_cast<long>(bh) * T + t0 + (ok ? tid : 0);
-      if (GAIN != GAIN_KDN && GAIN != GAIN_EXPLICIT) {
-        const float x = a.g.eta[ti];
-        p_eta = ok ? x : 0.f;
-      }
-      if (!CHANNEL) {
-        const float x = static_cast<const float*>(a.g.alpha)[ti];
-        p_alpha = ok ? x : 1.f;
-      }
+      const long ti = static_cast<long>(bh) * T + t0 + (tid < n ? tid : 0);
+      if (GAIN != GAIN_KDN && GAIN != GAIN_EXPLICIT) p_eta = a.g.eta[ti];
+      if (!CHANNEL) p_alpha = static_cast<const float*>(a.g.alpha)[ti];
       if (GAIN == GAIN_PGDN) {
-        const float x = a.g.alphaP[ti], y = a.g.betaP[ti];
-        p_ap = ok ? x : 1.f;
-        p_bp = ok ? y : 0.f;
+        p_ap = a.g.alphaP[ti];
+        p_bp = a.g.betaP[ti];
       }
-      if (GAIN == GAIN_KDN) {
-        const float x = a.g.r[ti];
-        p_r = ok ? x : 1.f;  // padded tokens: k = 0 gives u = 0
-      }
+      if (GAIN == GAIN_KDN) p_r = a.g.r[ti];
     }
   };
 
-  auto stash = [&]() __attribute__((always_inline)) {
+  // registers -> LDS for chunk c, substituting neutral values past the end:
+  // k = q = v = w = omega = 0, alpha = alphaP = 1, betaP = eta = 0, r = 1
+  auto stash = [&](int n) __attribute__((always_inline)) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < KV_LOADS; ++j) {
       const int e = (tid + j * NT) * VEC;
       const int t = e / DK, d = e % DK;
-      *reinterpret_cast<u32x4*>(&sm.k[t * PK + d]) = pk[j];
-      *reinterpret_cast<u32x4*>(&sm.q[t * PK + d]) = pq[j];
-      if constexpr (GAIN == GAIN_EXPLICIT) *reinterpret_cast<u32x4*>(&sm.w[t * PK + d]) = pw[j];
+      const bool ok = t < n;
+      *reinterpret_cast<u32x4*>(&sm.k[t * PK + d]) = ok ? pk[j] : z;
+      *reinterpret_cast<u32x4*>(&sm.q[t * PK + d]) = ok ? pq[j] : z;
+      if constexpr (GAIN == GAIN_EXPLICIT)
+        *reinterpret_cast<u32x4*>(&sm.w[t * PK + d]) = ok ? pw[j] : z;
+      if constexpr (CHANNEL) {
+        const u32x4 one4 = BF16 ? u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}
+                                : u32x4{0x3F800000u, 0x3F800000u, 0x3F800000u, 0x3F800000u};
+        pal[j] = ok ? pal[j] : one4;
+      }
+      if constexpr (GAIN == GAIN_KDN) pom[j] = ok ? pom[j] : z;
     }
 #pragma unroll
     for (int j = 0; j < V_LOADS; ++j) {
       const int e = (tid + j * NT) * VEC;
-      if (e < CH * BV) *reinterpret_cast<u32x4*>(&sm.v[e]) = pv[j];
+      if (e < CH * BV) *reinterpret_cast<u32x4*>(&sm.v[e]) = (e / BV < n) ? pv[j] : z;
     }
     if (tid < CH) {
-      sm.eta[tid] = p_eta;
-      sm.alpha[tid] = p_alpha;
-      sm.ap[tid] = p_ap;
-      sm.bp[tid] = p_bp;
-      sm.r[tid] = p_r;
-      sm.mur[tid] = a.g.mu_info / p_r;
+      const bool ok = tid < n;
+      const float r = ok ? p_r : 1.f;
+      sm.eta[tid] = ok ? p_eta : 0.f;
+      sm.alpha[tid] = ok ? p_alpha : 1.f;
+      sm.ap[tid] = ok ? p_ap : 1.f;
+      sm.bp[tid] = ok ? p_bp : 0.f;
+      sm.r[tid] = r;
+      sm.mur[tid] = a.g.mu_info / r;
     }
   };
 
-  if (nchunks > 0) fetch(0);
+  // output tile of a chunk (in sm.o) -> HBM, 16-byte rows
+  auto store_out = [&](int ts, int nn) __attribute__((always_inline)) {
+    for (int e = tid * VEC; e < CH * BV; e += NT * VEC) {
+      const int t = e / BV, cc = e % BV;
+      if (t < nn)
+        *reinterpret_cast<u32x4*>(go + static_cast<long>(ts + t) * a.dv + col0 + cc) =
+            *reinterpret_cast<const u32x4*>(&sm.o[e]);
+    }
+  };
+
+  if (nchunks > 0) {
+    fetch(0, 0);
+    fetch(0, 1);
+    fetch(0, 2);
+  }
   DN_PHASE_DECL
 
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * CH;
     const int n = min(CH, T - t0);
-    stash();
+    stash(n);
     // per-channel gates of this chunk, consumed in step 2
     u32x4 cal[CHANNEL ? KV_LOADS : 1], com[GAIN == GAIN_KDN ? KV_LOADS : 1];
 #pragma unroll
     for (int j = 0; j < (CHANNEL ? KV_LOADS : 0); ++j) cal[j] = pal[j];
 #pragma unroll
     for (int j = 0; j < (GAIN == GAIN_KDN ? KV_LOADS : 0); ++j) com[j] = pom[j];
-    __syncthreads();  // (A) chunk inputs visible
-    // the next chunk's inputs travel from HBM while this chunk is processed
-    if (c + 1 < nchunks) fetch(c + 1);
     DN_PHASE(0);
+    __syncthreads();  // (A) chunk inputs visible
+    DN_PHASE(6);
+    // the next chunk's inputs travel from HBM while this chunk is processed;
+    // the previous chunk's output tile leaves after them, so that waiting for
+    // these loads at the next stash never waits on the stores
+    if (c + 1 < nchunks) fetch(c + 1, 0);
+    if (c > 0) store_out(t0 - CH, CH);
+    DN_PHASE(7);
 
     // ================= 2. gains =================
     if constexpr (!CHANNEL) {
@@ -324,6 +374,48 @@ void chunk_fwd_kernel(ChunkArgs a) {
           if (lane >= off) x += y;
         }
         sm.g2[lane] = x;
+        sm.gam[lane] = fast_exp2(x);
+        if constexpr (PG2) {
+          // prefix products of alphaP over tokens 32..63
+          float pr = lane >= CH / 2 ? sm.ap[lane] : 1.f;
+#pragma unroll
+          for (int off = 1; off < CH / 2; off <<= 1) {
+            const float y = __shfl_up(pr, off, 64);
+            if (lane - off >= CH / 2) pr *= y;
+          }
+          sm.aprod[lane] = pr;
+        }
+      }
+    }
+    if constexpr (PG2) {
+      // half 0 (tokens 0..31) starts from the carried statistic, half 1
+      // (tokens 32..63) from 0; half 1 adds aprod_t * A_31 afterwards
+      constexpr int HT = CH / 2;
+      const int d = tid % DK, half = tid / DK;
+      float A[HT];
+      if (tid < 2 * DK) {
+        float st = half == 0 ? sm.acarry[d] : 0.f;
+#pragma unroll
+        for (int i = 0; i < HT; ++i) {
+          const int t = half * HT + i;
+          st = pgdn_stat(st, sm.ap[t], sm.bp[t], EL::get(sm.k[t * PK + d]));
+          A[i] = st;
+        }
+        if (half == 0) sm.ah[d] = st;
+      }
+      __syncthreads();
+      if (tid < 2 * DK) {
+        const float base = half == 1 ? sm.ah[d] : 0.f;
+        const float mu = a.g.mu_log[h];
+        float At = 0.f;
+#pragma unroll
+        for (int i = 0; i < HT; ++i) {
+          const int t = half * HT + i;
+          At = half == 1 ? fmaf(sm.aprod[t], base, A[i]) : A[i];
+          const float kk = EL::get(sm.k[t * PK + d]);
+          sm.w[t * PK + d] = EL::put(sm.eta[t] * pgdn_scale_fast(At, mu, a.g.log2x) * kk);
+        }
+        if (half == 1) sm.acarry[d] = At;
       }
     }
     if constexpr (GAIN == GAIN_KLA || GAIN == GAIN_GDN) {
@@ -429,6 +521,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();  // (B) gains visible
+    if (c + 1 < nchunks) fetch(c + 1, 1);
     DN_PHASE(1);
 
     // ================= 3. write-vector operands =================
@@ -505,6 +598,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();  // (C) operands of the intra-chunk products ready
+    if (c + 1 < nchunks) fetch(c + 1, 2);
     DN_PHASE(2);
 
     // ================= 4. L and M, lower-triangular 16x16 tile pairs =================
@@ -517,6 +611,8 @@ void chunk_fwd_kernel(ChunkArgs a) {
           ++bi;
         }
         const int bj = tt;
+        // transposed tiles: C[j][i] = wchk_j . khat_i (qhat_i); lane (g4, c16)
+        // then holds row i = 16 bi + c16, columns j = 16 bj + 4 g4 .. +3
         Frag fb[KS], fk[KS], fq[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -527,22 +623,33 @@ void chunk_fwd_kernel(ChunkArgs a) {
         f32x4 accL = zero4(), accM = zero4();
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          accL = MM::mma(fk[s], fb[s], accL);
-          accM = MM::mma(fq[s], fb[s], accM);
+          accL = MM::mma(fb[s], fk[s], accL);
+          accM = MM::mma(fb[s], fq[s], accM);
         }
-        const int j = 16 * bj + c16;
-        const f32x4 gi = *reinterpret_cast<const f32x4*>(&sm.g2[16 * bi + 4 * g4]);
-        const float gj = sm.g2[j], csj = sm.cs[j];
+        const int i = 16 * bi + c16, j0 = 16 * bj + 4 * g4;
+        f32x4 f = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (!CHANNEL) {
+          const float gi = sm.g2[i];
+          const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.g2[j0]);
+          const f32x4 csj = *reinterpret_cast<const f32x4*>(&sm.cs[j0]);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int i = 16 * bi + 4 * g4 + ii;
-          const float f = CHANNEL ? 1.f : fast_exp2(gi[ii] - gj) * csj;
-          const float lv = j < i ? accL[ii] * f : 0.f;
-          const float mv = j <= i ? accM[ii] * f : 0.f;
-          sM[i * PT + j] = EL::put(mv);
-          sL[i * PT + j] = EL::put(bi == bj ? 0.f : -lv);
-          if (bi == bj) sm.ld[(bi * 16 + (i & 15)) * 16 + (j & 15)] = lv;
+          for (int u = 0; u < 4; ++u) f[u] = fast_exp2(gi - gj[u]) * csj[u];
         }
+        f32x4 lv, mv;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          lv[u] = j0 + u < i ? accL[u] * f[u] : 0.f;
+          mv[u] = j0 + u <= i ? accM[u] * f[u] : 0.f;
+        }
+        const f32x4 nl = (bi == bj) ? zero4() : -lv;
+        if constexpr (BF16) {
+          *reinterpret_cast<u32x2*>(&sM[i * PT + j0]) = u32x2{pack_bf2(mv[0], mv[1]), pack_bf2(mv[2], mv[3])};
+          *reinterpret_cast<u32x2*>(&sL[i * PT + j0]) = u32x2{pack_bf2(nl[0], nl[1]), pack_bf2(nl[2], nl[3])};
+        } else {
+          *reinterpret_cast<f32x4*>(&sM[i * PT + j0]) = mv;
+          *reinterpret_cast<f32x4*>(&sL[i * PT + j0]) = nl;
+        }
+        if (bi == bj) *reinterpret_cast<f32x4*>(&sm.ld[(bi * 16 + c16) * 16 + 4 * g4]) = lv;
       }
       // zero the strictly-upper tiles of -L and M
       for (int e = tid; e < 6 * 256; e += NT) {
@@ -627,11 +734,11 @@ void chunk_fwd_kernel(ChunkArgs a) {
           kacc = MM::mma(fk[s], fs[s], kacc);
           qacc = MM::mma(fq[s], fs[s], qacc);
         }
-        const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.g2[16 * rt + 4 * g4]);
+        const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.gam[16 * rt + 4 * g4]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = 16 * rt + 4 * g4 + i;
-          const float sc = CHANNEL ? 1.f : fast_exp2(gt[i]);
+          const float sc = CHANNEL ? 1.f : gt[i];
           R[rt][i] = EL::get(sm.v[t * BV + 16 * wave + c16]) - sc * kacc[i];
           O[rt][i] = sc * qacc[i];
         }
@@ -697,7 +804,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
       Frag fu[KT];
 #pragma unroll
       for (int s = 0; s < KT; ++s) fu[s] = MM::frag(ub, PT, lane, s);
-      const float gsc = CHANNEL ? 1.f : fast_exp2(sm.g2[CH - 1]);
+      const float gsc = CHANNEL ? 1.f : sm.gam[CH - 1];
 #pragma unroll
       for (int dt = 0; dt < DK / 16; ++dt) {
         Frag fw[KT];
@@ -716,14 +823,11 @@ void chunk_fwd_kernel(ChunkArgs a) {
     __syncthreads();  // (F) output tile complete; chunk operands free
     DN_PHASE(5);
 
-    // ================= 7. output tile -> HBM, 16-byte rows =================
-    for (int e = tid * VEC; e < CH * BV; e += NT * VEC) {
-      const int t = e / BV, cc = e % BV;
-      if (t < n)
-        *reinterpret_cast<u32x4*>(go + static_cast<long>(t0 + t) * a.dv + col0 + cc) =
-            *reinterpret_cast<const u32x4*>(&sm.o[e]);
-    }
-    DN_PHASE(6);
+  }
+  // the last chunk's output tile
+  if (nchunks > 0) {
+    const int cl = nchunks - 1;
+    store_out(cl * CH, min(CH, T - cl * CH));
   }
   DN_PHASE_FLUSH
 
@@ -738,7 +842,10 @@ void chunk_fwd_kernel(ChunkArgs a) {
         a.S_final[(static_cast<long>(bh) * DK + row) * a.dv + col] = S[dt][i];
       }
   }
-  if ((GAIN == GAIN_PGDN || GAIN == GAIN_KDN) && a.aux_final && blockIdx.x == 0) {
+  if constexpr (PG2) {
+    if (a.aux_final && slice == 0 && tid < DK)
+      a.aux_final[static_cast<long>(bh) * DK + tid] = nchunks > 0 ? sm.acarry[tid] : aux[0];
+  } else if ((GAIN == GAIN_PGDN || GAIN == GAIN_KDN) && a.aux_final && slice == 0) {
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) {
       const int d = tid + cc * NT;
@@ -758,7 +865,7 @@ static hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(smem));
   if (err != hipSuccess) return err;
-  dim3 grid(static_cast<unsigned>(a.dv / BV), static_cast<unsigned>(a.B * a.H));
+  dim3 grid(static_cast<unsigned>((a.dv / BV) * a.B * a.H));
   hipLaunchKernelGGL(kern, grid, dim3(BV * 4), smem, st, a);
   return hipGetLastError();
 }
