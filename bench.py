@@ -11,6 +11,7 @@ roofline of the chunked-forward kernel, and the fp64 oracle timed on a
 bounded sample on the host CPU.
 """
 import argparse
+import hashlib
 import json
 import os
 import resource
@@ -25,6 +26,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix (256 CU x 2.4 GHz x 4096 flop/clk)
 METRIC = "delta-rule fwd tokens/s + %MFMA peak (T=4096,d=128); decode GB/s vs HBM peak"
+KERNEL_SOURCES = ("recurrent_sequence_mixer_amd/csrc/chunk_fwd.hip",
+                  "recurrent_sequence_mixer_amd/csrc/common.hpp",
+                  "recurrent_sequence_mixer_amd/csrc/gains.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_kla_B8H16T4096d128_traffic.txt")
 
 
 def log(msg):
@@ -122,6 +127,46 @@ def time_decode(dwl, steps_timed):
     return ev0.elapsed_time(ev1) / steps_timed
 
 
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the chunked-forward kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the kernel
+    sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calib_copy(mib):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy: {mib} MiB read + {mib} MiB written, 3 launches")
+
+
 def cpu_baseline(wl, heads=2, T=1024):
     """The fp64 oracle on a bounded sample: `heads` heads x `T` tokens."""
     from oracle.recurrence import run_workload
@@ -153,6 +198,10 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--cpu-heads", type=int, default=128, help="oracle sample: heads")
+    ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample: tokens per head")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a device copy of this size (byte-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the forward engine shards "
@@ -185,7 +234,7 @@ def main():
         "config": {"workload": wl.name, "gain": wl.gain, "B": wl.B, "H": wl.H, "T": wl.T,
                    "dk": wl.dk, "dv": wl.dv, "C": wl.C},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "chunk_fwd_kernel<bf16,128,64,KLA,scalar>",
                      "bytes_per_launch": bytes_},
         "mfma": {"counted_tflops": flops / (ms * 1e-3) / 1e12,
@@ -214,8 +263,10 @@ def main():
         log(f"[bench] decode: {dms:.3f} ms/step, {gbs:.0f} GB/s")
         out["extra"] = extra
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads, args.cpu_tokens)
         log(f"[bench] cpu baseline: {out['cpu_baseline']}")
+    if args.calib_copy_mib:
+        calib_copy(args.calib_copy_mib)
     print(json.dumps(out), flush=True)
 
 
