@@ -893,6 +893,7 @@ static hipError_t launch_gain(const ChunkArgs& a, int gain, bool channel, hipStr
 hipError_t launch_chunk_fwd(const ChunkArgs& a, int io_bf16, int gain, bool channel,
                             hipStream_t st) {
   if (io_bf16) {
+    if (!channel && gain != GAIN_KDN) return launch_chunk_fwd_bf16_scalar(a, gain, st);
     if (a.dk == 128) return launch_gain<uint16_t, 128, 64>(a, gain, channel, st);
     return launch_gain<uint16_t, 64, 64>(a, gain, channel, st);
   }

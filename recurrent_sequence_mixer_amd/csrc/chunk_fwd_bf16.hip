@@ -1,0 +1,587 @@
+// Chunked forward, bf16 operands, scalar decay (KLA, GDN, PGDN, explicit
+// write vectors): the throughput kernel for d_k = 128 (and 64) heads.
+//
+// Same chunk form as chunk_fwd.hip (our statement of Kaczmarz Linear
+// Attention §2.5 Eqs. 7-9 and Preconditioned DeltaNet §2.6 Eq. 6):
+//   L = strict_lower(K W^T) * exp(G_i - G_j),  M = lower(Q W^T) * exp(G_i - G_j)
+//   (I + L) U = V - diag(g) K S_in,   O = diag(g) Q S_in + M U,
+//   S_out = g_n S_in + Wtil^T U,  Wtil_j = (g_n / g_j) w_j.
+//
+// Work split.  A workgroup owns one (batch, head) and BV value columns, i.e.
+// NCT = BV / 16 column tiles of 16 columns, and runs 2 NCT wavefronts (two
+// per SIMD for BV = 64), so that each SIMD always has a second wavefront to
+// issue from.  The wavefronts of column tile c:
+//   role A (waves 0 .. NCT-1): holds S rows [0, d_k/2) of tile c, computes
+//     K S, the L tiles, the diagonal-block inverses and the triangular solve;
+//   role B (waves NCT .. 2 NCT-1): holds S rows [d_k/2, d_k), computes Q S,
+//     the M tiles, Wtil^T and M U.
+// Both update their half of S with Wtil^T U.  k and q MFMA fragments are read
+// from LDS once per wavefront and serve both the L/M tiles (as the B operand
+// of the transposed tile product) and K S / Q S (as the A operand).
+//
+// Per chunk c (barriers between the phases):
+//   P2  gains of c (||k||^2, cumulative log2-decay, PGDN statistic and
+//       scale); both halves of S -> LDS (bf16); the output tile of c - 1
+//       leaves for HBM.
+//   P3  L tiles + K S (role A), M tiles + Q S (role B).
+//   P4  role A: diagonal-block inverses of I + L (fp32), blocked forward
+//       substitution on 16x16x16 MFMAs with U in registers, U -> LDS.
+//       role B: Wtil^T.
+//   P5  role B: O += M U -> output tile in LDS; all: S = g_n S + Wtil^T U;
+//       then chunk c + 1 (loaded during chunk c - 1) is stashed into LDS and
+//       the loads of chunk c + 2 are issued.
+#include "common.hpp"
+#include "gains.hpp"
+#include "launch.hpp"
+
+namespace dn {
+
+namespace fast {
+
+constexpr int CH = 64;
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// PGDN write scale on the hardware log2 / rcp / exp2 (Preconditioned DeltaNet
+// §2.4, Eq. 9): B(A) = exp(-ln(x) s), s = r / (1 + |r|), r = ln A - mu.
+__device__ __forceinline__ float pgdn_scale_hw(float A, float mu, float log2x) {
+  const float r = log2_hw(A) * 0.69314718055994531f - mu;
+  const float s = r * __builtin_amdgcn_rcpf(1.0f + fabsf(r));
+  return exp2_hw(-log2x * s);
+}
+
+// 16x16x16 bf16 MFMA: the accumulator layout (rows 4 (l/16)..+3, column
+// l % 16) equals the B-operand layout, so a packed accumulator feeds the next
+// product directly.
+__device__ __forceinline__ s16x4 frag16(const uint16_t* p, int ld, int lane) {
+  return __builtin_bit_cast(
+      s16x4, *reinterpret_cast<const u32x2*>(p + (lane & 15) * ld + 4 * (lane >> 4)));
+}
+__device__ __forceinline__ s16x4 pack16(f32x4 c) {
+  const u32x2 v = {pack_bf2(c[0], c[1]), pack_bf2(c[2], c[3])};
+  return __builtin_bit_cast(s16x4, v);
+}
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 frag32(const uint16_t* p, int ld, int lane, int s) {
+  return __builtin_bit_cast(
+      bf16x8, *reinterpret_cast<const u32x4*>(p + (lane & 15) * ld + 32 * s + 8 * (lane >> 4)));
+}
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int DK, int BV, int GAIN>
+struct Smem {
+  static constexpr int PK = DK + 8;  // [token][d_k] rows, bf16
+  static constexpr int PT = CH + 8;  // [*][token] rows, bf16
+  static constexpr int P16 = 16 + 8;
+  static constexpr int NCT = BV / 16;
+  static constexpr bool HAS_W = GAIN == GAIN_PGDN || GAIN == GAIN_EXPLICIT;
+  alignas(16) uint16_t k[CH * PK];
+  alignas(16) uint16_t q[CH * PK];
+  alignas(16) uint16_t w[HAS_W ? CH * PK : 8];
+  alignas(16) uint16_t wt[DK * PT];          // Wtil^T [d][t]
+  alignas(16) uint16_t v[CH * BV];           // value slice [t][c]
+  alignas(16) uint16_t lm[2 * CH * PT];      // -L, M [i][j]
+  alignas(16) uint16_t tbw[NCT * 4 * 16 * P16];  // per role-A wave: (I + L_bb)^-1
+  alignas(16) uint16_t sb[NCT * 16 * PK];    // per column tile: S^T [c][d]
+  alignas(16) uint16_t ub[NCT * 16 * PT];    // per column tile: U^T [c][t]
+  alignas(16) uint16_t o[CH * BV];           // output tile [t][c]
+  alignas(16) float ld[4 * 256];             // diagonal blocks of L, fp32
+  alignas(16) float g2[CH];                  // cumulative log2-decay
+  alignas(16) float gam[CH];                 // 2^g2
+  alignas(16) float cs[CH];                  // column scale beta_j (1 with stored w)
+  alignas(16) float aprod[CH];               // PGDN: prefix products of alphaP per segment
+  alignas(16) float ah[8 * DK];              // PGDN: statistic at each segment end
+  alignas(16) float acarry[DK];              // PGDN: statistic carried between chunks
+  float eta[CH], alpha[CH], ap[CH], bp[CH];
+};
+
+template <int DK, int BV, int GAIN>
+__global__ __launch_bounds__(BV * 8) void chunk_fwd_bf16_kernel(ChunkArgs a) {
+  constexpr int NCT = BV / 16;        // column tiles
+  constexpr int NW = 2 * NCT;         // wavefronts
+  constexpr int NT = 64 * NW;         // threads
+  constexpr int NTB = 64 * NCT;       // threads of one role
+  constexpr int HR = DK / 2;          // state rows per wavefront
+  constexpr int HTL = HR / 16;        // state tiles per wavefront
+  constexpr int KS = DK / 32;         // k-steps of a d_k contraction
+  constexpr int VEC = 8;              // bf16 per 16-byte access
+  constexpr int KV_LOADS = CH * DK / (NT * VEC);
+  constexpr int V_LOADS = CH * BV / (NT * VEC);
+  constexpr bool HAS_W = GAIN == GAIN_PGDN || GAIN == GAIN_EXPLICIT;
+  constexpr bool PG = GAIN == GAIN_PGDN;
+  static_assert(KV_LOADS * NT * VEC == CH * DK && V_LOADS * NT * VEC == CH * BV, "tile split");
+  static_assert(!PG || NT == 4 * DK || NT == 8 * DK, "PGDN scan layout");
+  using Sm = Smem<DK, BV, GAIN>;
+  constexpr int PK = Sm::PK, PT = Sm::PT, P16 = Sm::P16;
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
+  uint16_t* const sL = sm.lm;
+  uint16_t* const sM = sm.lm + CH * PT;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int ct = wave % NCT;          // column tile
+  const int half = wave / NCT;        // 0: role A, 1: role B
+  const bool roleA = half == 0;
+  const int tr = tid - NTB * half;    // thread index within the role
+
+  // XCD-aware mapping (see chunk_fwd.hip): value slices of a head share an XCD
+  const int ns = a.dv / BV;
+  const int nwg = ns * a.B * a.H;
+  int bh, slice;
+  {
+    const int Lid = blockIdx.x;
+    if (nwg % 8 == 0 && (nwg / 8) % ns == 0) {
+      const int xcd = Lid % 8, r = Lid / 8;
+      slice = r % ns;
+      bh = xcd * (nwg / 8 / ns) + r / ns;
+    } else {
+      slice = Lid % ns;
+      bh = Lid / ns;
+    }
+  }
+  const int h = bh % a.H;
+  const int col0 = slice * BV;
+  const int T = a.T;
+  const int nchunks = (T + CH - 1) / CH;
+  const long qk_base = static_cast<long>(bh) * T * DK;
+  const long v_base = static_cast<long>(bh) * T * a.dv;
+  const uint16_t* gk = static_cast<const uint16_t*>(a.k) + qk_base;
+  const uint16_t* gq = static_cast<const uint16_t*>(a.q) + qk_base;
+  const uint16_t* gv = static_cast<const uint16_t*>(a.v) + v_base;
+  uint16_t* go = static_cast<uint16_t*>(a.o) + v_base;
+
+  // ---- state: tiles dt hold rows half * HR + 16 dt + 4 g4 + i, column 16 ct + c16
+  // (per-lane base + wave-uniform row offsets: no 64-bit addresses stay live)
+  const long s_lane = (static_cast<long>(bh) * DK + half * HR + 4 * g4) * a.dv + col0 + 16 * ct + c16;
+  f32x4 S[HTL];
+  if (a.S0) {
+    const float* base = a.S0 + s_lane;
+#pragma unroll
+    for (int dt = 0; dt < HTL; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[dt][i] = base[(16 * dt + i) * a.dv];
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < HTL; ++dt) S[dt] = zero4();
+  }
+  if constexpr (PG) {
+    if (tid < DK) sm.acarry[tid] = a.aux0 ? a.aux0[static_cast<long>(bh) * DK + tid] : 1.f;
+  }
+
+  // ---- staging registers of one chunk (all threads)
+  u32x4 pk[KV_LOADS], pq[KV_LOADS], pw[GAIN == GAIN_EXPLICIT ? KV_LOADS : 1], pv[V_LOADS];
+  float p_eta = 0.f, p_alpha = 1.f, p_ap = 1.f, p_bp = 0.f;
+
+  // unconditional loads (rows past the end read row 0 of the chunk); the
+  // neutral values are substituted by stash()
+  auto fetch = [&](int c) __attribute__((always_inline)) {
+    const int t0 = c * CH;
+    const int n = min(CH, T - t0);
+#pragma unroll
+    for (int j = 0; j < KV_LOADS; ++j) {
+      const int e = (tid + j * NT) * VEC;
+      const int t = e / DK, d = e % DK;
+      const long off = static_cast<long>(t0 + (t < n ? t : 0)) * DK + d;
+      pk[j] = *reinterpret_cast<const u32x4*>(gk + off);
+      pq[j] = *reinterpret_cast<const u32x4*>(gq + off);
+      if constexpr (GAIN == GAIN_EXPLICIT)
+        pw[j] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.g.w) + qk_base + off);
+    }
+#pragma unroll
+    for (int j = 0; j < V_LOADS; ++j) {
+      const int e = (tid + j * NT) * VEC;
+      const int t = e / BV, cc = e % BV;
+      pv[j] = *reinterpret_cast<const u32x4*>(gv + static_cast<long>(t0 + (t < n ? t : 0)) * a.dv +
+                                              col0 + cc);
+    }
+    if (tid < CH) {
+      const long ti = static_cast<long>(bh) * T + t0 + (tid < n ? tid : 0);
+      p_eta = a.g.eta[ti];
+      p_alpha = static_cast<const float*>(a.g.alpha)[ti];
+      if constexpr (PG) {
+        p_ap = a.g.alphaP[ti];
+        p_bp = a.g.betaP[ti];
+      }
+    }
+  };
+  auto stash = [&](int n) __attribute__((always_inline)) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < KV_LOADS; ++j) {
+      const int e = (tid + j * NT) * VEC;
+      const int t = e / DK, d = e % DK;
+      const bool ok = t < n;
+      *reinterpret_cast<u32x4*>(&sm.k[t * PK + d]) = ok ? pk[j] : z;
+      *reinterpret_cast<u32x4*>(&sm.q[t * PK + d]) = ok ? pq[j] : z;
+      if constexpr (GAIN == GAIN_EXPLICIT)
+        *reinterpret_cast<u32x4*>(&sm.w[t * PK + d]) = ok ? pw[j] : z;
+    }
+#pragma unroll
+    for (int j = 0; j < V_LOADS; ++j) {
+      const int e = (tid + j * NT) * VEC;
+      *reinterpret_cast<u32x4*>(&sm.v[e]) = (e / BV < n) ? pv[j] : z;
+    }
+    if (tid < CH) {
+      const bool ok = tid < n;
+      sm.eta[tid] = ok ? p_eta : 0.f;
+      sm.alpha[tid] = ok ? p_alpha : 1.f;
+      sm.ap[tid] = ok ? p_ap : 1.f;
+      sm.bp[tid] = ok ? p_bp : 0.f;
+    }
+  };
+  auto store_out = [&](int ts, int nn) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < V_LOADS; ++j) {
+      const int e = (tid + j * NT) * VEC;
+      const int t = e / BV, cc = e % BV;
+      if (t < nn)
+        *reinterpret_cast<u32x4*>(go + static_cast<long>(ts + t) * a.dv + col0 + cc) =
+            *reinterpret_cast<const u32x4*>(&sm.o[e]);
+    }
+  };
+
+  if (nchunks > 0) {
+    fetch(0);
+    stash(min(CH, T));
+    if (nchunks > 1) fetch(1);
+  }
+  __syncthreads();
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int t0 = c * CH;
+    const int n = min(CH, T - t0);
+
+    // ================= P2: gains, S -> LDS, previous output tile =================
+    if (wave == NW - 1) {
+      float x = log2_hw(sm.alpha[lane]);
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      sm.g2[lane] = x;
+      sm.gam[lane] = exp2_hw(x);
+      if constexpr (PG) {
+        // inclusive prefix products of alphaP within each scan segment
+        constexpr int SL = CH / (NT / DK);
+        float pr = sm.ap[lane];
+#pragma unroll
+        for (int off = 1; off < SL; off <<= 1) {
+          const float y = __shfl_up(pr, off, 64);
+          if ((lane % SL) >= off) pr *= y;
+        }
+        sm.aprod[lane] = pr;
+      }
+    }
+    if constexpr (GAIN == GAIN_KLA || GAIN == GAIN_GDN) {
+      constexpr int TPT = NT / CH;      // threads per token
+      constexpr int PER = DK / TPT;     // channels per thread
+      const int t = tid / TPT, part = tid % TPT;
+      float s = 0.f;
+      if constexpr (GAIN == GAIN_KLA) {
+#pragma unroll
+        for (int d0 = 0; d0 < PER; d0 += VEC) {
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(&sm.k[t * PK + part * PER + d0]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float lo = __uint_as_float(raw[i] << 16), hi = __uint_as_float(raw[i] & 0xFFFF0000u);
+            s = fmaf(lo, lo, s);
+            s = fmaf(hi, hi, s);
+          }
+        }
+#pragma unroll
+        for (int off = 1; off < TPT; off <<= 1) s += __shfl_xor(s, off, 64);
+      }
+      if (part == 0) sm.cs[t] = GAIN == GAIN_KLA ? kla_beta(sm.eta[t], s, a.g.eps) : sm.eta[t];
+    } else {
+      if (tid < CH) sm.cs[tid] = 1.f;
+    }
+    if constexpr (PG) {
+      // the statistic scan in NSEG segments of the chunk over NSEG d_k threads:
+      // segment g starts from 0 (segment 0 from the carried statistic) and adds
+      // (prod of alphaP over the segment up to t) * A_(end of segment g-1)
+      constexpr int NSEG = NT / DK, SL = CH / NSEG;
+      const int d = tid % DK, g = tid / DK;
+      float A[SL];
+      float st = g == 0 ? sm.acarry[d] : 0.f;
+#pragma unroll
+      for (int i = 0; i < SL; ++i) {
+        const int t = g * SL + i;
+        st = pgdn_stat(st, sm.ap[t], sm.bp[t], bf2f(sm.k[t * PK + d]));
+        A[i] = st;
+      }
+      sm.ah[g * DK + d] = st;
+      __syncthreads();
+      // carry into segment g: fold the ends of segments 0..g-1 with the segment
+      // products of alphaP (prefix products within each segment, in sm.aprod)
+      float carry = 0.f;
+      for (int gg = 0; gg < g; ++gg) carry = fmaf(sm.aprod[(gg + 1) * SL - 1], carry, sm.ah[gg * DK + d]);
+      const float mu = a.g.mu_log[h];
+      float At = 0.f;
+#pragma unroll
+      for (int i = 0; i < SL; ++i) {
+        const int t = g * SL + i;
+        At = fmaf(sm.aprod[t], carry, A[i]);
+        sm.w[t * PK + d] = f2bf(sm.eta[t] * pgdn_scale_hw(At, mu, a.g.log2x) * bf2f(sm.k[t * PK + d]));
+      }
+      if (g == NSEG - 1) sm.acarry[d] = At;
+    }
+    // this wavefront's half of S -> S^T rows of its column tile
+    {
+      uint16_t* sbt = sm.sb + ct * 16 * PK;
+#pragma unroll
+      for (int dt = 0; dt < HTL; ++dt) {
+        const u32x2 p2 = {pack_bf2(S[dt][0], S[dt][1]), pack_bf2(S[dt][2], S[dt][3])};
+        *reinterpret_cast<u32x2*>(&sbt[c16 * PK + half * HR + 16 * dt + 4 * g4]) = p2;
+      }
+    }
+    if (c > 0) store_out(t0 - CH, CH);
+    __syncthreads();  // (B)
+
+    // ================= P3: L + K S (A), M + Q S (B) =================
+    // this wavefront's operand: k (role A) or q (role B), all 4 row tiles
+    bf16x8 X[4][KS];
+    {
+      const uint16_t* src = roleA ? sm.k : sm.q;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) X[rt][s] = frag32(src + 16 * rt * PK, PK, lane, s);
+    }
+    // L tiles (role A) / M tiles (role B): transposed products C[j][i] = w_j . x_i,
+    // tiles p = ct, ct + NCT, ... of the 10 lower-triangular (bi, bj)
+    // (unrolled over all ten with a uniform guard, so that X is indexed by
+    // constants and stays in registers)
+#pragma unroll
+    for (int p = 0; p < 10; ++p) {
+      if (p % NCT != ct) continue;
+      const int bi = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+      const int bj = p - bi * (bi + 1) / 2;
+      const uint16_t* wsrc = HAS_W ? sm.w : sm.k;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 wa = (!HAS_W && roleA) ? X[bj][s] : frag32(wsrc + 16 * bj * PK, PK, lane, s);
+        acc = mfma32(wa, X[bi][s], acc);
+      }
+      const int i = 16 * bi + c16, j0 = 16 * bj + 4 * g4;
+      const float gi = sm.g2[i];
+      const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.g2[j0]);
+      const f32x4 csj = *reinterpret_cast<const f32x4*>(&sm.cs[j0]);
+      f32x4 val;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float f = exp2_hw(gi - gj[u]) * csj[u];
+        const bool keep = roleA ? (j0 + u < i) : (j0 + u <= i);
+        val[u] = keep ? acc[u] * f : 0.f;
+      }
+      if (roleA) {
+        const f32x4 nl = (bi == bj) ? zero4() : -val;
+        *reinterpret_cast<u32x2*>(&sL[i * PT + j0]) = u32x2{pack_bf2(nl[0], nl[1]), pack_bf2(nl[2], nl[3])};
+        if (bi == bj) *reinterpret_cast<f32x4*>(&sm.ld[(bi * 16 + c16) * 16 + 4 * g4]) = val;
+      } else {
+        *reinterpret_cast<u32x2*>(&sM[i * PT + j0]) = u32x2{pack_bf2(val[0], val[1]), pack_bf2(val[2], val[3])};
+      }
+      if constexpr (HAS_W) __builtin_amdgcn_sched_barrier(0);  // no hoisting of the next tile's w loads
+    }
+    // zero the strictly upper tiles: role A of -L, role B of M
+    for (int e = tr; e < 6 * 256; e += NTB) {
+      const int tile = e >> 8, w = e & 255;
+      const int bi = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
+      const int bj = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
+      (roleA ? sL : sM)[(16 * bi + (w >> 4)) * PT + 16 * bj + (w & 15)] = 0;
+    }
+    // K S (role A) -> R = V - g K S;  Q S (role B) -> O = g Q S
+    f32x4 RO[4];
+    {
+      bf16x8 fs[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) fs[s] = frag32(sm.sb + ct * 16 * PK, PK, lane, s);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = mfma32(X[rt][s], fs[s], acc);
+        const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.gam[16 * rt + 4 * g4]);
+        if (roleA) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            RO[rt][i] = bf2f(sm.v[(16 * rt + 4 * g4 + i) * BV + 16 * ct + c16]) - gt[i] * acc[i];
+        } else {
+          RO[rt] = gt * acc;
+        }
+      }
+    }
+    __syncthreads();  // (C)
+
+    // ================= P4: solve (A) | Wtil^T (B) =================
+    if (roleA) {
+      // (I + L_bb)^-1 for the four diagonal blocks: lane (b, c) -> column c of block b
+      uint16_t* tb = sm.tbw + ct * 4 * 16 * P16;
+      {
+        const float* Lb = sm.ld + g4 * 256;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float row[16];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 r4 = *reinterpret_cast<const f32x4*>(&Lb[i * 16 + 4 * q4]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) row[4 * q4 + u] = r4[u];
+          }
+          float s0 = (i == c16) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+          for (int j = 0; j < i; ++j) {
+            if (j & 1) s1 = fmaf(-row[j], x[j], s1);
+            else s0 = fmaf(-row[j], x[j], s0);
+          }
+          x[i] = s0 + s1;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tb[(g4 * 16 + i) * P16 + c16] = f2bf(x[i]);
+      }
+      wave_lds_sync();
+      // U_b = T_bb (R_b - sum_{m<b} L_bm U_m)
+      s16x4 Ub[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        f32x4 acc = RO[b];
+#pragma unroll
+        for (int m = 0; m < b; ++m) acc = mfma16(frag16(sL + 16 * b * PT + 16 * m, PT, lane), Ub[m], acc);
+        Ub[b] = pack16(mfma16(frag16(tb + 16 * b * P16, P16, lane), pack16(acc), zero4()));
+      }
+      uint16_t* ubt = sm.ub + ct * 16 * PT;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) *reinterpret_cast<s16x4*>(&ubt[c16 * PT + 16 * b + 4 * g4]) = Ub[b];
+    } else {
+      {
+        // Wtil^T[d][t] = 2^(G_{n-1} - G_t) cs_t w_t[d] in 4-token x 8-channel blocks
+        const float gl = sm.g2[CH - 1];
+        const uint16_t* src = HAS_W ? sm.w : sm.k;
+        for (int blk = tr; blk < (CH / 4) * (DK / VEC); blk += NTB) {
+          const int tt0 = 4 * (blk % (CH / 4)), dd0 = VEC * (blk / (CH / 4));
+          float val[4][VEC];
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = tt0 + i;
+            const float f = sm.cs[t] * exp2_hw(gl - sm.g2[t]);
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(&src[t * PK + dd0]);
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              val[i][2 * j] = f * __uint_as_float(raw[j] << 16);
+              val[i][2 * j + 1] = f * __uint_as_float(raw[j] & 0xFFFF0000u);
+            }
+          }
+  #pragma unroll
+          for (int j = 0; j < VEC; ++j)
+            *reinterpret_cast<u32x2*>(&sm.wt[(dd0 + j) * PT + tt0]) =
+                u32x2{pack_bf2(val[0][j], val[1][j]), pack_bf2(val[2][j], val[3][j])};
+        }
+      }
+    }
+    __syncthreads();  // (D)
+
+    // ================= P5: O += M U (B), S = g_n S + Wtil^T U =================
+    {
+      const uint16_t* ubt = sm.ub + ct * 16 * PT;
+      if (!roleA) {
+        s16x4 Uf[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          Uf[m] = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(&ubt[c16 * PT + 16 * m + 4 * g4]));
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+          for (int m = 0; m <= rt; ++m)
+            RO[rt] = mfma16(frag16(sM + 16 * rt * PT + 16 * m, PT, lane), Uf[m], RO[rt]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sm.o[(16 * rt + 4 * g4 + i) * BV + 16 * ct + c16] = f2bf(RO[rt][i]);
+        }
+      }
+      constexpr int KT = CH / 32;
+      bf16x8 fu[KT];
+#pragma unroll
+      for (int s = 0; s < KT; ++s) fu[s] = frag32(ubt, PT, lane, s);
+      const float gn = sm.gam[CH - 1];
+#pragma unroll
+      for (int dt = 0; dt < HTL; ++dt) {
+        f32x4 acc = S[dt] * gn;
+#pragma unroll
+        for (int s = 0; s < KT; ++s)
+          acc = mfma32(frag32(sm.wt + (half * HR + 16 * dt) * PT, PT, lane, s), fu[s], acc);
+        S[dt] = acc;
+      }
+    }
+    if (c + 1 < nchunks) {
+      stash(min(CH, T - t0 - CH));
+      if (c + 2 < nchunks) fetch(c + 2);
+    }
+    __syncthreads();  // (E)
+  }
+
+  // ---- the last output tile, final state and statistic
+  if (nchunks > 0) {
+    const int cl = nchunks - 1;
+    store_out(cl * CH, min(CH, T - cl * CH));
+  }
+  if (a.S_final) {
+    float* base = a.S_final + s_lane;
+#pragma unroll
+    for (int dt = 0; dt < HTL; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) base[(16 * dt + i) * a.dv] = S[dt][i];
+  }
+  if constexpr (PG) {
+    if (a.aux_final && slice == 0 && tid < DK) a.aux_final[static_cast<long>(bh) * DK + tid] = sm.acarry[tid];
+  }
+}
+
+}  // namespace fast
+
+template <int DK, int BV, int GAIN>
+static hipError_t launch_fast_one(const ChunkArgs& a, hipStream_t st) {
+  using Sm = fast::Smem<DK, BV, GAIN>;
+  static_assert(sizeof(Sm) <= 160 * 1024, "LDS budget");
+  auto kern = fast::chunk_fwd_bf16_kernel<DK, BV, GAIN>;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(sizeof(Sm)));
+  if (err != hipSuccess) return err;
+  dim3 grid(static_cast<unsigned>((a.dv / BV) * a.B * a.H));
+  hipLaunchKernelGGL(kern, grid, dim3(BV * 8), sizeof(Sm), st, a);
+  return hipGetLastError();
+}
+
+// bf16 io, scalar decay, gains KLA / GDN / PGDN / explicit.
+hipError_t launch_chunk_fwd_bf16_scalar(const ChunkArgs& a, int gain, hipStream_t st) {
+#define DN_FAST(DK)                                                          \
+  switch (gain) {                                                            \
+    case GAIN_KLA: return launch_fast_one<DK, 64, GAIN_KLA>(a, st);           \
+    case GAIN_GDN: return launch_fast_one<DK, 64, GAIN_GDN>(a, st);           \
+    case GAIN_PGDN: return launch_fast_one<DK, 64, GAIN_PGDN>(a, st);         \
+    case GAIN_EXPLICIT: return launch_fast_one<DK, 64, GAIN_EXPLICIT>(a, st); \
+    default: return hipErrorInvalidValue;                                    \
+  }
+  if (a.dk == 128) {
+    DN_FAST(128)
+  }
+  DN_FAST(64)
+#undef DN_FAST
+}
+
+}  // namespace dn

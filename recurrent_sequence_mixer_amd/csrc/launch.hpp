@@ -63,6 +63,8 @@ struct GainPrepArgs {
 hipError_t launch_decode(const DecodeArgs& a, int io_bf16, int gain, bool channel, hipStream_t st);
 hipError_t launch_chunk_fwd(const ChunkArgs& a, int io_bf16, int gain, bool channel,
                             hipStream_t st);
+// bf16 io, scalar decay, gains KLA / GDN / PGDN / explicit (chunk_fwd_bf16.hip)
+hipError_t launch_chunk_fwd_bf16_scalar(const ChunkArgs& a, int gain, hipStream_t st);
 hipError_t launch_gain_prep(const GainPrepArgs& a, int io_bf16, int gain, bool channel,
                             hipStream_t st);
 
