@@ -49,6 +49,48 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// DPP lane moves within rows of 16 lanes (gfx9 encodings: row_shr:n = 0x110 + n,
+// row_half_mirror = 0x141, row_bcast:15 = 0x142, row_bcast:31 = 0x143,
+// quad_perm = 2-bit lane selectors).  Lanes that are masked off, or whose
+// source lies outside the row, return `old`.
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+__device__ __forceinline__ float dpp(float x, float old) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL,
+                                                    ROW_MASK, BANK_MASK, false));
+}
+// inclusive prefix sum over the 64 lanes of a wavefront
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  float s = x + dpp<0x111>(x, 0.f);
+  s += dpp<0x112>(x, 0.f);
+  s += dpp<0x113>(x, 0.f);
+  s += dpp<0x114, 0xF, 0xE>(s, 0.f);
+  s += dpp<0x118, 0xF, 0xC>(s, 0.f);
+  s += dpp<0x142, 0xA, 0xF>(s, 0.f);
+  s += dpp<0x143, 0xC, 0xF>(s, 0.f);
+  return s;
+}
+// inclusive prefix product within each row of 16 lanes
+__device__ __forceinline__ float row_prefix_prod(float x) {
+  float p = x * dpp<0x111>(x, 1.f);
+  p *= dpp<0x112>(x, 1.f);
+  p *= dpp<0x113>(x, 1.f);
+  p *= dpp<0x114, 0xF, 0xE>(p, 1.f);
+  p *= dpp<0x118, 0xF, 0xC>(p, 1.f);
+  return p;
+}
+// sum over each group of 8 consecutive lanes, in every lane of the group
+__device__ __forceinline__ float oct_sum(float x) {
+  x += dpp<0xB1>(x, 0.f);   // quad_perm(1,0,3,2)
+  x += dpp<0x4E>(x, 0.f);   // quad_perm(2,3,0,1)
+  x += dpp<0x141>(x, 0.f);  // the other quad of the half-row
+  return x;
+}
+
+template <bool B>
+struct Role {
+  static constexpr bool a = B;
+};
+
 // PGDN write scale on the hardware log2 / rcp / exp2 (Preconditioned DeltaNet
 // §2.4, Eq. 9): B(A) = exp(-ln(x) s), s = r / (1 + |r|), r = ln A - mu.
 __device__ __forceinline__ float pgdn_scale_hw(float A, float mu, float log2x) {
@@ -84,24 +126,26 @@ struct Smem {
   static constexpr int PK = DK + 8;  // [token][d_k] rows, bf16
   static constexpr int PT = CH + 8;  // [*][token] rows, bf16
   static constexpr int P16 = 16 + 8;
+  static constexpr int PV = BV + 8;  // [token][value] rows, bf16 (row groups 4 apart in distinct banks)
+  static constexpr int PL = 20;      // rows of the fp32 diagonal blocks
   static constexpr int NCT = BV / 16;
   static constexpr bool HAS_W = GAIN == GAIN_PGDN || GAIN == GAIN_EXPLICIT;
   alignas(16) uint16_t k[CH * PK];
   alignas(16) uint16_t q[CH * PK];
   alignas(16) uint16_t w[HAS_W ? CH * PK : 8];
   alignas(16) uint16_t wt[DK * PT];          // Wtil^T [d][t]
-  alignas(16) uint16_t v[CH * BV];           // value slice [t][c]
+  alignas(16) uint16_t v[CH * PV];           // value slice [t][c]
   alignas(16) uint16_t lm[2 * CH * PT];      // -L, M [i][j]
-  alignas(16) uint16_t tbw[NCT * 4 * 16 * P16];  // per role-A wave: (I + L_bb)^-1
+  alignas(16) uint16_t tb[4 * 16 * P16];     // (I + L_bb)^-1 of the four diagonal blocks
   alignas(16) uint16_t sb[NCT * 16 * PK];    // per column tile: S^T [c][d]
   alignas(16) uint16_t ub[NCT * 16 * PT];    // per column tile: U^T [c][t]
-  alignas(16) uint16_t o[CH * BV];           // output tile [t][c]
-  alignas(16) float ld[4 * 256];             // diagonal blocks of L, fp32
+  alignas(16) uint16_t o[CH * PV];           // output tile [t][c]
+  alignas(16) float ld[4 * 16 * PL];         // diagonal blocks of L, fp32
   alignas(16) float g2[CH];                  // cumulative log2-decay
   alignas(16) float gam[CH];                 // 2^g2
   alignas(16) float cs[CH];                  // column scale beta_j (1 with stored w)
   alignas(16) float aprod[CH];               // PGDN: prefix products of alphaP per segment
-  alignas(16) float ah[8 * DK];              // PGDN: statistic at each segment end
+  alignas(16) float ah[4 * DK];              // PGDN: statistic at each segment end
   alignas(16) float acarry[DK];              // PGDN: statistic carried between chunks
   float eta[CH], alpha[CH], ap[CH], bp[CH];
 };
@@ -121,9 +165,10 @@ __global__ __launch_bounds__(BV * 8) void chunk_fwd_bf16_kernel(ChunkArgs a) {
   constexpr bool HAS_W = GAIN == GAIN_PGDN || GAIN == GAIN_EXPLICIT;
   constexpr bool PG = GAIN == GAIN_PGDN;
   static_assert(KV_LOADS * NT * VEC == CH * DK && V_LOADS * NT * VEC == CH * BV, "tile split");
-  static_assert(!PG || NT == 4 * DK || NT == 8 * DK, "PGDN scan layout");
+  static_assert(!PG || NT >= 4 * DK, "PGDN scan layout");
   using Sm = Smem<DK, BV, GAIN>;
-  constexpr int PK = Sm::PK, PT = Sm::PT, P16 = Sm::P16;
+  constexpr int PK = Sm::PK, PT = Sm::PT, P16 = Sm::P16, PV = Sm::PV, PL = Sm::PL;
+  static_assert(NCT == 4, "tile ownership below assumes four column tiles");
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
@@ -134,9 +179,7 @@ __global__ __launch_bounds__(BV * 8) void chunk_fwd_bf16_kernel(ChunkArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int ct = wave % NCT;          // column tile
-  const int half = wave / NCT;        // 0: role A, 1: role B
-  const bool roleA = half == 0;
-  const int tr = tid - NTB * half;    // thread index within the role
+  const bool roleA = wave < NCT;      // role A: waves 0 .. NCT-1
 
   // XCD-aware mapping (see chunk_fwd.hip): value slices of a head share an XCD
   const int ns = a.dv / BV;
@@ -163,6 +206,14 @@ __global__ __launch_bounds__(BV * 8) void chunk_fwd_bf16_kernel(ChunkArgs a) {
   const uint16_t* gq = static_cast<const uint16_t*>(a.q) + qk_base;
   const uint16_t* gv = static_cast<const uint16_t*>(a.v) + v_base;
   uint16_t* go = static_cast<uint16_t*>(a.o) + v_base;
+
+  // The chunk loop is specialised per role at compile time (both
+  // specialisations pass the same sequence of workgroup barriers), so that a
+  // wavefront holds only its own role's registers.
+  auto run = [&](auto role) __attribute__((always_inline)) {
+  constexpr bool RA = decltype(role)::a;
+  constexpr int half = RA ? 0 : 1;    // which half of the state rows
+  const int tr = tid - NTB * half;    // thread index within the role
 
   // ---- state: tiles dt hold rows half * HR + 16 dt + 4 g4 + i, column 16 ct + c16
   // (per-lane base + wave-uniform row offsets: no 64-bit addresses stay live)
@@ -233,7 +284,7 @@ __global__ __launch_bounds__(BV * 8) void chunk_fwd_bf16_kernel(ChunkArgs a) {
 #pragma unroll
     for (int j = 0; j < V_LOADS; ++j) {
       const int e = (tid + j * NT) * VEC;
-      *reinterpret_cast<u32x4*>(&sm.v[e]) = (e / BV < n) ? pv[j] : z;
+      *reinterpret_cast<u32x4*>(&sm.v[(e / BV) * PV + e % BV]) = (e / BV < n) ? pv[j] : z;
     }
     if (tid < CH) {
       const bool ok = tid < n;
@@ -250,7 +301,7 @@ __global__ __launch_bounds__(BV * 8) void chunk_fwd_bf16_kernel(ChunkArgs a) {
       const int t = e / BV, cc = e % BV;
       if (t < nn)
         *reinterpret_cast<u32x4*>(go + static_cast<long>(ts + t) * a.dv + col0 + cc) =
-            *reinterpret_cast<const u32x4*>(&sm.o[e]);
+            *reinterpret_cast<const u32x4*>(&sm.o[t * PV + cc]);
     }
   };
 
@@ -266,30 +317,17 @@ __global__ __launch_bounds__(BV * 8) void chunk_fwd_bf16_kernel(ChunkArgs a) {
     const int n = min(CH, T - t0);
 
     // ================= P2: gains, S -> LDS, previous output tile =================
-    if (wave == NW - 1) {
-      float x = log2_hw(sm.alpha[lane]);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-      }
+    if (!RA && wave == NW - 1) {
+      const float x = wave_prefix_sum(log2_hw(sm.alpha[lane]));
       sm.g2[lane] = x;
       sm.gam[lane] = exp2_hw(x);
-      if constexpr (PG) {
-        // inclusive prefix products of alphaP within each scan segment
-        constexpr int SL = CH / (NT / DK);
-        float pr = sm.ap[lane];
-#pragma unroll
-        for (int off = 1; off < SL; off <<= 1) {
-          const float y = __shfl_up(pr, off, 64);
-          if ((lane % SL) >= off) pr *= y;
-        }
-        sm.aprod[lane] = pr;
-      }
+      // PGDN: inclusive prefix products of alphaP within each 16-token segment
+      if constexpr (PG) sm.aprod[lane] = row_prefix_prod(sm.ap[lane]);
     }
     if constexpr (GAIN == GAIN_KLA || GAIN == GAIN_GDN) {
       constexpr int TPT = NT / CH;      // threads per token
       constexpr int PER = DK / TPT;     // channels per thread
+      static_assert(TPT == 8, "eight threads per token");
       const int t = tid / TPT, part = tid % TPT;
       float s = 0.f;
       if constexpr (GAIN == GAIN_KLA) {
@@ -303,42 +341,49 @@ __global__ __launch_bounds__(BV * 8) void chunk_fwd_bf16_kernel(ChunkArgs a) {
             s = fmaf(hi, hi, s);
           }
         }
-#pragma unroll
-        for (int off = 1; off < TPT; off <<= 1) s += __shfl_xor(s, off, 64);
+        s = oct_sum(s);
       }
       if (part == 0) sm.cs[t] = GAIN == GAIN_KLA ? kla_beta(sm.eta[t], s, a.g.eps) : sm.eta[t];
     } else {
       if (tid < CH) sm.cs[tid] = 1.f;
     }
     if constexpr (PG) {
-      // the statistic scan in NSEG segments of the chunk over NSEG d_k threads:
-      // segment g starts from 0 (segment 0 from the carried statistic) and adds
-      // (prod of alphaP over the segment up to t) * A_(end of segment g-1)
-      constexpr int NSEG = NT / DK, SL = CH / NSEG;
+      // the statistic scan in four 16-token segments over 4 d_k threads.
+      // Pass 1: each segment runs from 0, segment 0 from the carried statistic,
+      // which makes the end of segment 0 exact.  The end of segment g is then
+      // E_g = P_g E_(g-1) + (pass-1 end of g), P_g = product of alphaP over g.
+      // Pass 2 replays each segment from its exact start E_(g-1).
+      constexpr int NSEG = 4, SL = CH / NSEG;
       const int d = tid % DK, g = tid / DK;
-      float A[SL];
-      float st = g == 0 ? sm.acarry[d] : 0.f;
+      const bool scan = tid < NSEG * DK;
+      float start = 0.f;
+      if (scan) {
+        if (g == 0) start = sm.acarry[d];
+        float st = start;
 #pragma unroll
-      for (int i = 0; i < SL; ++i) {
-        const int t = g * SL + i;
-        st = pgdn_stat(st, sm.ap[t], sm.bp[t], bf2f(sm.k[t * PK + d]));
-        A[i] = st;
+        for (int i = 0; i < SL; ++i) {
+          const int t = g * SL + i;
+          st = pgdn_stat(st, sm.ap[t], sm.bp[t], bf2f(sm.k[t * PK + d]));
+        }
+        sm.ah[g * DK + d] = st;
       }
-      sm.ah[g * DK + d] = st;
       __syncthreads();
-      // carry into segment g: fold the ends of segments 0..g-1 with the segment
-      // products of alphaP (prefix products within each segment, in sm.aprod)
-      float carry = 0.f;
-      for (int gg = 0; gg < g; ++gg) carry = fmaf(sm.aprod[(gg + 1) * SL - 1], carry, sm.ah[gg * DK + d]);
-      const float mu = a.g.mu_log[h];
-      float At = 0.f;
+      if (scan) {
+        if (g > 0) {
+          start = sm.ah[d];
+          for (int gg = 1; gg < g; ++gg) start = fmaf(sm.aprod[(gg + 1) * SL - 1], start, sm.ah[gg * DK + d]);
+        }
+        const float mu = a.g.mu_log[h];
+        float At = start;
 #pragma unroll
-      for (int i = 0; i < SL; ++i) {
-        const int t = g * SL + i;
-        At = fmaf(sm.aprod[t], carry, A[i]);
-        sm.w[t * PK + d] = f2bf(sm.eta[t] * pgdn_scale_hw(At, mu, a.g.log2x) * bf2f(sm.k[t * PK + d]));
+        for (int i = 0; i < SL; ++i) {
+          const int t = g * SL + i;
+          const float kk = bf2f(sm.k[t * PK + d]);
+          At = pgdn_stat(At, sm.ap[t], sm.bp[t], kk);
+          sm.w[t * PK + d] = f2bf(sm.eta[t] * pgdn_scale_hw(At, mu, a.g.log2x) * kk);
+        }
+        if (g == NSEG - 1) sm.acarry[d] = At;  // read again only in the next chunk
       }
-      if (g == NSEG - 1) sm.acarry[d] = At;
     }
     // this wavefront's half of S -> S^T rows of its column tile
     {
@@ -353,94 +398,97 @@ __global__ __launch_bounds__(BV * 8) void chunk_fwd_bf16_kernel(ChunkArgs a) {
     __syncthreads();  // (B)
 
     // ================= P3: L + K S (A), M + Q S (B) =================
-    // this wavefront's operand: k (role A) or q (role B), all 4 row tiles
-    bf16x8 X[4][KS];
-    {
-      const uint16_t* src = roleA ? sm.k : sm.q;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int s = 0; s < KS; ++s) X[rt][s] = frag32(src + 16 * rt * PK, PK, lane, s);
-    }
-    // L tiles (role A) / M tiles (role B): transposed products C[j][i] = w_j . x_i,
-    // tiles p = ct, ct + NCT, ... of the 10 lower-triangular (bi, bj)
-    // (unrolled over all ten with a uniform guard, so that X is indexed by
-    // constants and stays in registers)
-#pragma unroll
-    for (int p = 0; p < 10; ++p) {
-      if (p % NCT != ct) continue;
-      const int bi = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
-      const int bj = p - bi * (bi + 1) / 2;
-      const uint16_t* wsrc = HAS_W ? sm.w : sm.k;
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 wa = (!HAS_W && roleA) ? X[bj][s] : frag32(wsrc + 16 * bj * PK, PK, lane, s);
-        acc = mfma32(wa, X[bi][s], acc);
-      }
-      const int i = 16 * bi + c16, j0 = 16 * bj + 4 * g4;
-      const float gi = sm.g2[i];
-      const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.g2[j0]);
-      const f32x4 csj = *reinterpret_cast<const f32x4*>(&sm.cs[j0]);
-      f32x4 val;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float f = exp2_hw(gi - gj[u]) * csj[u];
-        const bool keep = roleA ? (j0 + u < i) : (j0 + u <= i);
-        val[u] = keep ? acc[u] * f : 0.f;
-      }
-      if (roleA) {
-        const f32x4 nl = (bi == bj) ? zero4() : -val;
-        *reinterpret_cast<u32x2*>(&sL[i * PT + j0]) = u32x2{pack_bf2(nl[0], nl[1]), pack_bf2(nl[2], nl[3])};
-        if (bi == bj) *reinterpret_cast<f32x4*>(&sm.ld[(bi * 16 + c16) * 16 + 4 * g4]) = val;
-      } else {
-        *reinterpret_cast<u32x2*>(&sM[i * PT + j0]) = u32x2{pack_bf2(val[0], val[1]), pack_bf2(val[2], val[3])};
-      }
-      if constexpr (HAS_W) __builtin_amdgcn_sched_barrier(0);  // no hoisting of the next tile's w loads
-    }
-    // zero the strictly upper tiles: role A of -L, role B of M
-    for (int e = tr; e < 6 * 256; e += NTB) {
-      const int tile = e >> 8, w = e & 255;
-      const int bi = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
-      const int bj = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
-      (roleA ? sL : sM)[(16 * bi + (w >> 4)) * PT + 16 * bj + (w & 15)] = 0;
-    }
-    // K S (role A) -> R = V - g K S;  Q S (role B) -> O = g Q S
+    // (specialised per role at compile time: no role test inside the products)
     f32x4 RO[4];
     {
-      bf16x8 fs[KS];
+      uint16_t* const dst = RA ? sL : sM;
+      // this wavefront's operand: k (role A) or q (role B), all 4 row tiles
+      bf16x8 X[4][KS];
+      {
+        const uint16_t* src = RA ? sm.k : sm.q;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) fs[s] = frag32(sm.sb + ct * 16 * PK, PK, lane, s);
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
+          for (int s = 0; s < KS; ++s) X[rt][s] = frag32(src + 16 * rt * PK, PK, lane, s);
+      }
+      // L tiles (role A) / M tiles (role B): transposed products C[j][i] = w_j . x_i
+      // over the 10 lower-triangular tiles p -> (bi, bj).  Column tile ct owns
+      // diagonal tile (ct, ct) and one or two off-diagonal tiles.  (Unrolled
+      // over all ten with a uniform guard, so that X is indexed by constants.)
+      constexpr int OWNER[10] = {0, 0, 1, 1, 2, 2, 0, 1, 3, 3};
+#pragma unroll
+      for (int p = 0; p < 10; ++p) {
+        if (OWNER[p] != ct) continue;
+        const int bi = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+        const int bj = p - bi * (bi + 1) / 2;
+        bf16x8 Wf[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          if constexpr (RA && !HAS_W) Wf[s] = X[bj][s];
+          else Wf[s] = frag32((HAS_W ? sm.w : sm.k) + 16 * bj * PK, PK, lane, s);
+        }
         f32x4 acc = zero4();
 #pragma unroll
-        for (int s = 0; s < KS; ++s) acc = mfma32(X[rt][s], fs[s], acc);
-        const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.gam[16 * rt + 4 * g4]);
-        if (roleA) {
+        for (int s = 0; s < KS; ++s) acc = mfma32(Wf[s], X[bi][s], acc);
+        const int i = 16 * bi + c16, j0 = 16 * bj + 4 * g4;
+        const float gi = sm.g2[i];
+        const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.g2[j0]);
+        const f32x4 csj = *reinterpret_cast<const f32x4*>(&sm.cs[j0]);
+        f32x4 val;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            RO[rt][i] = bf2f(sm.v[(16 * rt + 4 * g4 + i) * BV + 16 * ct + c16]) - gt[i] * acc[i];
+        for (int u = 0; u < 4; ++u) {
+          const float f = exp2_hw(gi - gj[u]) * csj[u];
+          const bool keep = RA ? (j0 + u < i) : (j0 + u <= i);
+          val[u] = keep ? acc[u] * f : 0.f;
+        }
+        if constexpr (RA) {
+          const f32x4 nl = (bi == bj) ? zero4() : -val;
+          *reinterpret_cast<u32x2*>(&dst[i * PT + j0]) = u32x2{pack_bf2(nl[0], nl[1]), pack_bf2(nl[2], nl[3])};
+          if (bi == bj) *reinterpret_cast<f32x4*>(&sm.ld[(bi * 16 + c16) * PL + 4 * g4]) = val;
         } else {
-          RO[rt] = gt * acc;
+          *reinterpret_cast<u32x2*>(&dst[i * PT + j0]) = u32x2{pack_bf2(val[0], val[1]), pack_bf2(val[2], val[3])};
         }
       }
-    }
-    __syncthreads();  // (C)
-
-    // ================= P4: solve (A) | Wtil^T (B) =================
-    if (roleA) {
-      // (I + L_bb)^-1 for the four diagonal blocks: lane (b, c) -> column c of block b
-      uint16_t* tb = sm.tbw + ct * 4 * 16 * P16;
+      // zero the strictly upper tiles of -L (role A) or M (role B)
+      for (int e = tr; e < 6 * 256; e += NTB) {
+        const int tile = e >> 8, w = e & 255;
+        const int bi = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
+        const int bj = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
+        dst[(16 * bi + (w >> 4)) * PT + 16 * bj + (w & 15)] = 0;
+      }
+      // K S (role A) -> R = V - g K S;  Q S (role B) -> O = g Q S
       {
-        const float* Lb = sm.ld + g4 * 256;
+        bf16x8 fs[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) fs[s] = frag32(sm.sb + ct * 16 * PK, PK, lane, s);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int s = 0; s < KS; ++s) acc = mfma32(X[rt][s], fs[s], acc);
+          const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.gam[16 * rt + 4 * g4]);
+          if constexpr (RA) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              RO[rt][i] = bf2f(sm.v[(16 * rt + 4 * g4 + i) * PV + 16 * ct + c16]) - gt[i] * acc[i];
+          } else {
+            RO[rt] = gt * acc;
+          }
+        }
+      }
+      if constexpr (RA) {
+        // (I + L_bb)^-1 of this wavefront's diagonal block b = ct: lane c16 solves
+        // for column c16 by forward substitution over the rows of L_bb (every
+        // lane reads the same row: broadcast reads; only the j < i part is read)
+        wave_lds_sync();
+        const float* Lb = sm.ld + ct * 16 * PL;
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float row[16];
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 r4 = *reinterpret_cast<const f32x4*>(&Lb[i * 16 + 4 * q4]);
+          for (int q4 = 0; q4 < (i + 3) / 4; ++q4) {
+            const f32x4 r4 = *reinterpret_cast<const f32x4*>(&Lb[i * PL + 4 * q4]);
 #pragma unroll
             for (int u = 0; u < 4; ++u) row[4 * q4 + u] = r4[u];
           }
@@ -452,10 +500,18 @@ __global__ __launch_bounds__(BV * 8) void chunk_fwd_bf16_kernel(ChunkArgs a) {
           }
           x[i] = s0 + s1;
         }
+        // lane group g4 writes rows 4 g4 .. 4 g4 + 3 of column c16
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tb[(g4 * 16 + i) * P16 + c16] = f2bf(x[i]);
+        for (int u = 0; u < 4; ++u) {
+          const float y = g4 == 0 ? x[u] : g4 == 1 ? x[4 + u] : g4 == 2 ? x[8 + u] : x[12 + u];
+          sm.tb[(16 * ct + 4 * g4 + u) * P16 + c16] = f2bf(y);
+        }
       }
-      wave_lds_sync();
+    }
+    __syncthreads();  // (C)
+
+    // ================= P4: solve (A) | Wtil^T (B) =================
+    if constexpr (RA) {
       // U_b = T_bb (R_b - sum_{m<b} L_bm U_m)
       s16x4 Ub[4];
 #pragma unroll
@@ -463,7 +519,7 @@ __global__ __launch_bounds__(BV * 8) void chunk_fwd_bf16_kernel(ChunkArgs a) {
         f32x4 acc = RO[b];
 #pragma unroll
         for (int m = 0; m < b; ++m) acc = mfma16(frag16(sL + 16 * b * PT + 16 * m, PT, lane), Ub[m], acc);
-        Ub[b] = pack16(mfma16(frag16(tb + 16 * b * P16, P16, lane), pack16(acc), zero4()));
+        Ub[b] = pack16(mfma16(frag16(sm.tb + 16 * b * P16, P16, lane), pack16(acc), zero4()));
       }
       uint16_t* ubt = sm.ub + ct * 16 * PT;
 #pragma unroll
@@ -499,7 +555,7 @@ __global__ __launch_bounds__(BV * 8) void chunk_fwd_bf16_kernel(ChunkArgs a) {
     // ================= P5: O += M U (B), S = g_n S + Wtil^T U =================
     {
       const uint16_t* ubt = sm.ub + ct * 16 * PT;
-      if (!roleA) {
+      if constexpr (!RA) {
         s16x4 Uf[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m)
@@ -510,7 +566,7 @@ __global__ __launch_bounds__(BV * 8) void chunk_fwd_bf16_kernel(ChunkArgs a) {
           for (int m = 0; m <= rt; ++m)
             RO[rt] = mfma16(frag16(sM + 16 * rt * PT + 16 * m, PT, lane), Uf[m], RO[rt]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sm.o[(16 * rt + 4 * g4 + i) * BV + 16 * ct + c16] = f2bf(RO[rt][i]);
+          for (int i = 0; i < 4; ++i) sm.o[(16 * rt + 4 * g4 + i) * PV + 16 * ct + c16] = f2bf(RO[rt][i]);
         }
       }
       constexpr int KT = CH / 32;
@@ -549,6 +605,9 @@ __global__ __launch_bounds__(BV * 8) void chunk_fwd_bf16_kernel(ChunkArgs a) {
   if constexpr (PG) {
     if (a.aux_final && slice == 0 && tid < DK) a.aux_final[static_cast<long>(bh) * DK + tid] = sm.acarry[tid];
   }
+  };
+  if (roleA) run(Role<true>{});
+  else run(Role<false>{});
 }
 
 }  // namespace fast
