@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix (256 CU x 2.4 GHz x 4096 flop/clk)
 METRIC = "delta-rule fwd tokens/s + %MFMA peak (T=4096,d=128); decode GB/s vs HBM peak"
-KERNEL_SOURCES = ("recurrent_sequence_mixer_amd/csrc/chunk_fwd_bf16.hip",
+KERNEL_SOURCES = ("recurrent_sequence_mixer_amd/csrc/chunk_fwd_ws.hip",
                   "recurrent_sequence_mixer_amd/csrc/common.hpp",
                   "recurrent_sequence_mixer_amd/csrc/gains.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_kla_B8H16T4096d128_traffic.txt")
@@ -235,7 +235,7 @@ def main():
                    "dk": wl.dk, "dv": wl.dv, "C": wl.C},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "chunk_fwd_bf16_kernel<128,64,KLA>",
+                     "kernel": "chunk_fwd_ws_kernel<128,KLA>",
                      "bytes_per_launch": bytes_},
         "mfma": {"counted_tflops": flops / (ms * 1e-3) / 1e12,
                  "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,

@@ -1,0 +1,805 @@
+// Chunked forward, bf16 operands, scalar decay (KLA, GDN, PGDN, explicit
+// write vectors): producer and consumer wavefronts.
+//
+// Chunk form (our statement of Kaczmarz Linear Attention §2.5 Eqs. 7-9 and
+// Preconditioned DeltaNet §2.6 Eq. 6), per chunk of 64 tokens with G the
+// in-chunk cumulative log2-decay, g = 2^G and c_j the column scale (beta_j
+// for KLA / GDN, whose write vector is c_j k_j; 1 where w is stored):
+//   L = strict_lower(K W^T) 2^(G_i - G_j) c_j,  M = lower(Q W^T) 2^(G_i - G_j) c_j,
+//   (I + L) U = V - diag(g) K S,   O = diag(g) Q S + M U,
+//   S_out = g_n S + W^T diag(f) U,   f_j = 2^(G_n - G_j) c_j.
+//
+// A workgroup owns one (batch, head) and 64 value columns and runs eight
+// wavefronts, two per SIMD:
+//   consumers (waves 0..3): wave ct owns value columns 16 ct .. 16 ct + 15 and
+//     keeps the whole d_k x 16 slice of S in registers.  Per chunk it forms
+//     K S and (Q S)^T, runs the blocked triangular solve, adds M U, writes the
+//     output tile and updates S.
+//   producers (waves 4..7): build the chunk-local operands (the L and M
+//     tiles, the inverses of the diagonal blocks of I + L, the gains) and move
+//     the inputs HBM -> registers -> LDS.
+// Per chunk c, three phases separated by workgroup barriers:
+//   P1  consumers: K S -> R = V - g K S, and (Q S)^T.
+//       producers: (I + L_bb)^-1 of c; the gains of chunk c + 1 from its
+//       staging registers, its k and q into LDS, their loads for c + 2.
+//   P2  consumers: solve -> U; O = g Q S + M U -> HBM.
+//       producers: v of chunk c + 1 into LDS and its loads for c + 2; the
+//       raw L and M tile products of chunk c + 1.
+//   P3  consumers: S = g_n S + W^T diag(f) U.
+//       producers: scale and store the L and M tiles of chunk c + 1.
+// PGDN, whose write vectors come out of a statistic scan over the LDS copy
+// of k, stages chunk c + 1 in P2, scans in P3 (split around the scan's
+// synchronisation) and forms its tiles in P1.  Every load has a whole chunk
+// step to arrive.  k, q, w and the gains are double buffered by chunk parity;
+// every other LDS buffer is single: it is rewritten only after its last
+// reader of the previous chunk has passed a barrier.
+//
+// Register-resident operands.  In v_mfma_f32_16x16x32_bf16 lane l supplies
+// k = 8 (l / 16) .. +7 of its row (A) or column (B), and the accumulator holds
+// rows 4 (l / 16) + i of column l % 16.  The contraction of one MFMA may use
+// any pairing of k slots that A and B share, so the pair of accumulator tiles
+// holding rows 32 s + 4 g + i and 32 s + 16 + 4 g + i (i < 4) of S or U is
+// taken as the operand of k-block s as it stands, and the other operand reads
+// the same two groups of 4 indices (two 8-byte LDS reads, or two transposing
+// ds_read_b64_tr_b16 reads where the contraction runs along the rows of the
+// stored matrix).  With 16x16x16 operands the accumulator layout already is
+// the B layout (used by the solve).
+#include "common.hpp"
+#include "gains.hpp"
+#include "launch.hpp"
+
+namespace dn {
+
+namespace ws {
+
+constexpr int CH = 64;  // chunk length
+constexpr int BV = 64;  // value columns per workgroup
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// DPP lane moves within rows of 16 lanes (gfx9 encodings: row_shr:n = 0x110 + n,
+// row_bcast:15 = 0x142, row_bcast:31 = 0x143, quad_perm = 2-bit lane
+// selectors).  Lanes masked off, or whose source lies outside the row, return
+// `old`.
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+__device__ __forceinline__ float dpp(float x, float old) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL,
+                                                    ROW_MASK, BANK_MASK, false));
+}
+// inclusive prefix sum over the 64 lanes of a wavefront
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  float s = x + dpp<0x111>(x, 0.f);
+  s += dpp<0x112>(x, 0.f);
+  s += dpp<0x113>(x, 0.f);
+  s += dpp<0x114, 0xF, 0xE>(s, 0.f);
+  s += dpp<0x118, 0xF, 0xC>(s, 0.f);
+  s += dpp<0x142, 0xA, 0xF>(s, 0.f);
+  s += dpp<0x143, 0xC, 0xF>(s, 0.f);
+  return s;
+}
+// sum over each group of 4 consecutive lanes, in every lane of the group
+__device__ __forceinline__ float quad_sum(float x) {
+  x += dpp<0xB1>(x, 0.f);  // quad_perm(1,0,3,2)
+  x += dpp<0x4E>(x, 0.f);  // quad_perm(2,3,0,1)
+  return x;
+}
+// sum over each group of N = 8 or 16 consecutive lanes (N | 16), in every lane
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x = quad_sum(x);
+  x += dpp<0x141>(x, 0.f);  // row_half_mirror: the other quad of the 8
+  if constexpr (N == 16) x += dpp<0x140>(x, 0.f);  // row_mirror: the other 8 of the 16
+  return x;
+}
+
+// PGDN write scale on the hardware log2 / rcp / exp2 (Preconditioned DeltaNet
+// §2.4, Eq. 9): B(A) = exp(-ln(x) s), s = r / (1 + |r|), r = ln A - mu.
+__device__ __forceinline__ float pgdn_scale_hw(float A, float mu, float log2x) {
+  const float r = log2_hw(A) * 0.69314718055994531f - mu;
+  const float s = r * __builtin_amdgcn_rcpf(1.0f + fabsf(r));
+  return exp2_hw(-log2x * s);
+}
+
+// Raw buffer resource (stride 0, 32-bit data format) over nbytes from base:
+// loads at offsets >= nbytes return 0 and stores there are dropped, which
+// zero-fills the rows of a partial chunk and masks its output rows.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), nbytes,
+                                           0x00020000);
+}
+
+// ---- MFMA operands
+typedef short s16x4_lds __attribute__((ext_vector_type(4), address_space(3)));
+
+__device__ __forceinline__ bf16x8 cat8(s16x4 lo, s16x4 hi) {
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  const u32x4 v = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+// row (lane % 16) of a 16-row tile, k = 32 s + 8 (lane / 16) .. +7: one 16-byte read
+__device__ __forceinline__ bf16x8 frag32(const uint16_t* p, int ld, int lane, int s) {
+  return __builtin_bit_cast(
+      bf16x8, *reinterpret_cast<const u32x4*>(p + (lane & 15) * ld + 32 * s + 8 * (lane >> 4)));
+}
+// row (lane % 16), k = 32 s + 4 g .. +3 and 32 s + 16 + 4 g .. +3 (g = lane / 16):
+// the partner of a register-resident accumulator tile pair
+__device__ __forceinline__ bf16x8 frag32p(const uint16_t* p, int ld, int lane, int s) {
+  const uint16_t* r = p + (lane & 15) * ld + 32 * s + 4 * (lane >> 4);
+  return cat8(__builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(r)),
+              __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(r + 16)));
+}
+// Transposing read (ds_read_b64_tr_b16): within each group of 16 lanes, lane
+// l receives element l % 4 of the 8-byte chunk addressed by lane 4 j + l / 4,
+// j = 0..3.  With lane (g, l) addressing row r0 + 4 g + l / 4, column
+// c0 + 4 (l % 4) of a row-major matrix X, lane (g, l) receives X[r0 + 4 g + j]
+// [c0 + l], j = 0..3: four consecutive rows of one column.
+__device__ __forceinline__ s16x4 read_tr(const uint16_t* p, int ld, int lane, int r0, int c0) {
+  const uint16_t* a = p + (r0 + 4 * (lane >> 4) + ((lane & 15) >> 2)) * ld + c0 + 4 * (lane & 3);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds*)(a));
+}
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ s16x4 frag16(const uint16_t* p, int ld, int lane) {
+  return __builtin_bit_cast(
+      s16x4, *reinterpret_cast<const u32x2*>(p + (lane & 15) * ld + 4 * (lane >> 4)));
+}
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ s16x4 pack16(f32x4 c) {
+  const u32x2 v = {pack_bf2(c[0], c[1]), pack_bf2(c[2], c[3])};
+  return __builtin_bit_cast(s16x4, v);
+}
+__device__ __forceinline__ f32x4 unpack16(s16x4 p) {
+  const u32x2 v = __builtin_bit_cast(u32x2, p);
+  return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u),
+               __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xFFFF0000u)};
+}
+
+// A 16x16 fp32 accumulator tile as a sum of two bf16 tiles (hi + lo), and the
+// product X^T Y of two such tiles on three 16x16x16 MFMAs (the lo * lo term is
+// below fp32 rounding of the result).  Packed, an accumulator tile acc(X) is
+// the A operand of X^T and the B operand of X.
+struct Split {
+  s16x4 hi, lo;
+};
+__device__ __forceinline__ Split split(f32x4 x) {
+  Split r;
+  r.hi = pack16(x);
+  r.lo = pack16(x - unpack16(r.hi));
+  return r;
+}
+__device__ __forceinline__ f32x4 prod_t(const Split& x, const Split& y) {
+  f32x4 c = mfma16(x.hi, y.hi, zero4());
+  c = mfma16(x.hi, y.lo, c);
+  return mfma16(x.lo, y.hi, c);
+}
+__device__ __forceinline__ f32x4 add_identity(f32x4 x, int g4, int c16) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (4 * g4 + u == c16) x[u] += 1.f;
+  return x;
+}
+
+template <bool B>
+struct Role {
+  static constexpr bool consumer = B;
+};
+
+template <int DK, int GAIN>
+struct Smem {
+  static constexpr int PK = DK + 8;   // [token][d_k] rows, bf16
+  static constexpr int PV = BV + 16;  // [token][value] rows, bf16
+  static constexpr int PT = CH + 8;   // [token][token] rows, bf16
+  static constexpr int P16 = 16 + 8;  // rows of 16-wide blocks
+  static constexpr bool HAS_W = GAIN == GAIN_PGDN || GAIN == GAIN_EXPLICIT;
+  alignas(16) uint16_t k[2][CH * PK];           // k, by chunk parity
+  alignas(16) uint16_t w[HAS_W ? 2 : 1][HAS_W ? CH * PK : 8];  // write vectors, by parity
+  alignas(16) uint16_t q[2][CH * PK];           // q, by chunk parity
+  alignas(16) uint16_t v[CH * PV];              // value slice
+  alignas(16) uint16_t ln[CH * PT];             // -L [i][j], the off-diagonal 16x16 tiles
+  alignas(16) uint16_t mp[CH * PT];             // M [i][j]
+  alignas(16) uint16_t tb[4 * 16 * P16];        // (I + L_bb)^-1 [r][c], blocks b = 0..3
+  alignas(16) float g2[2][CH];                  // cumulative log2-decay, by chunk parity
+  alignas(16) float gam[2][CH];                 // 2^g2, by chunk parity
+  alignas(16) float cs[2][CH];                  // column scale c_j, by chunk parity
+  alignas(16) float fs[CH];                     // S-update scale f_j
+  float eta[CH], alpha[CH], ap[CH], bp[CH];     // per-token gates
+  alignas(16) float ah[4 * DK];                 // PGDN: statistic at the segment ends
+  alignas(16) float acarry[DK];                 // PGDN: statistic carried between chunks
+  float segp[4];                                // PGDN: product of alphaP over each segment
+};
+
+template <int DK, int GAIN>
+__global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
+  constexpr int NT = 512;               // threads
+  constexpr int NP = 256;               // producer threads
+  constexpr int NDT = DK / 16;          // state tiles of a consumer
+  constexpr int KS = DK / 32;           // k-blocks of a d_k contraction
+  constexpr int VEC = 8;                // bf16 per 16-byte access
+  constexpr int KV_LOADS = CH * DK / (NP * VEC);  // 16-byte pieces of k (q, w) per producer
+  constexpr int V_LOADS = CH * BV / (NP * VEC);
+  constexpr bool HAS_W = GAIN == GAIN_PGDN || GAIN == GAIN_EXPLICIT;
+  constexpr bool PG = GAIN == GAIN_PGDN;
+  constexpr bool HAS_ETA = GAIN != GAIN_EXPLICIT;
+  // Gains straight from the staging registers (no per-channel scan): the
+  // gains of chunk c + 1 are formed in P2 as it is staged, and its tiles in
+  // P3.  PGDN scans its statistic over the LDS copy of k in P3 and forms its
+  // tiles in P1, once its write vectors exist.
+  constexpr bool REG = !PG;
+  using Sm = Smem<DK, GAIN>;
+  constexpr int PK = Sm::PK, PV = Sm::PV, PT = Sm::PT, P16 = Sm::P16;
+  static_assert(KV_LOADS * NP * VEC == CH * DK && V_LOADS * NP * VEC == CH * BV, "tile split");
+  static_assert(NP % DK == 0 && CH % (NP / DK) == 0, "statistic scan layout");
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g4 = lane >> 4, c16 = lane & 15;
+
+  // XCD-aware mapping of the 1-D grid: consecutive workgroups are dealt to the
+  // 8 XCDs in turn, so the value slices of one head get ids that are equal
+  // modulo 8 and share that XCD's L2 (k and q come from HBM once).
+  const int ns = a.dv / BV;
+  const int nwg = ns * a.B * a.H;
+  int bh, slice;
+  {
+    const int id = blockIdx.x;
+    if (nwg % 8 == 0 && (nwg / 8) % ns == 0) {
+      const int xcd = id % 8, r = id / 8;
+      slice = r % ns;
+      bh = xcd * (nwg / 8 / ns) + r / ns;
+    } else {
+      slice = id % ns;
+      bh = id / ns;
+    }
+  }
+  const int h = bh % a.H;
+  const int col0 = slice * BV;
+  const int T = a.T;
+  const int nchunks = (T + CH - 1) / CH;
+  const long qk_base = static_cast<long>(bh) * T * DK;
+  const long v_base = static_cast<long>(bh) * T * a.dv;
+
+  // the M tiles above the diagonal that M U reads with its 32-token k-blocks
+  // (rows 0..15 x tokens 16..31, rows 32..47 x tokens 48..63) are zeros
+  for (int e = tid; e < 2 * 256; e += NT) {
+    const int bi = 2 * (e >> 8), r = (e >> 4) & 15, x = e & 15;
+    sm.mp[(16 * bi + r) * PT + 16 * (bi + 1) + x] = 0;
+  }
+
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    constexpr bool CONS = decltype(role)::consumer;
+    const int ct = wave;           // consumers: column tile
+    const int pw = wave - 4;       // producers: wavefront index
+    const int ptid = tid - 256;    // producers: thread index
+
+    // consumers: byte offsets of the output pieces (token 16 rt + c16, value
+    // columns col0 + 16 ct + 4 g4 .. +3) inside a chunk
+    int ooff[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) ooff[rt] = 2 * ((16 * rt + c16) * a.dv + col0 + 16 * ct + 4 * g4);
+
+    // ---------------- consumer state: tile dt = rows 16 dt + 4 g4 + i, column c16
+    f32x4 S[CONS ? NDT : 1];
+    const long s_lane = (static_cast<long>(bh) * DK + 4 * g4) * a.dv + col0 + 16 * ct + c16;
+    if constexpr (CONS) {
+      if (a.S0) {
+        const float* base = a.S0 + s_lane;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[dt][i] = base[(16 * dt + i) * a.dv];
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) S[dt] = zero4();
+      }
+    } else {
+      if (PG && ptid < DK) sm.acarry[ptid] = a.aux0 ? a.aux0[static_cast<long>(bh) * DK + ptid] : 1.f;
+    }
+
+    // ---------------- producer staging of one chunk: 16-byte pieces, rows
+    // of k / q / w in consecutive lanes (coalesced), likewise for v
+    u32x4 pk[KV_LOADS], pq[KV_LOADS], pwv[GAIN == GAIN_EXPLICIT ? KV_LOADS : 1], pv[V_LOADS];
+    float p_eta = 0.f, p_alpha = 1.f, p_ap = 1.f, p_bp = 0.f;
+    float p_etaj[KV_LOADS];  // eta of the token of each staged k piece (REG)
+    float pg_start = 0.f;  // PGDN: carried statistic read by pass 1 (segment 0)
+
+    // per-lane byte offsets inside a chunk: the k / q / w pieces (row-major
+    // [CH][DK]) and the value pieces (row t, columns col0 + cc of [T][dv])
+    int koff[KV_LOADS], voff[V_LOADS];
+#pragma unroll
+    for (int j = 0; j < KV_LOADS; ++j) koff[j] = 2 * (ptid + j * NP) * VEC;
+#pragma unroll
+    for (int j = 0; j < V_LOADS; ++j) {
+      const int e = (ptid + j * NP) * VEC;
+      voff[j] = 2 * ((e / BV) * a.dv + col0 + e % BV);
+    }
+    // loads of chunk c through buffer resources that end at its last token:
+    // past the end k = q = w = v = eta = alphaP = betaP = 0 (alpha, alphaP are
+    // replaced by 1 where they are used)
+    // k (w, gates) and q, v are loaded, and staged, at different points
+    auto fetch_k = [&](int c) __attribute__((always_inline)) {
+      const int t0 = c * CH;
+      const int n = min(CH, T - t0);
+      const long tok = static_cast<long>(bh) * T + t0;
+      const auto rk = rsrc(static_cast<const uint16_t*>(a.k) + qk_base + static_cast<long>(t0) * DK, 2 * n * DK);
+#pragma unroll
+      for (int j = 0; j < KV_LOADS; ++j) {
+        pk[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[j], 0, 0);
+        if constexpr (GAIN == GAIN_EXPLICIT) {
+          const auto rw = rsrc(static_cast<const uint16_t*>(a.g.w) + qk_base + static_cast<long>(t0) * DK, 2 * n * DK);
+          pwv[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, koff[j], 0, 0);
+        }
+      }
+      if constexpr (REG && HAS_ETA) {
+        const auto re = rsrc(a.g.eta + tok, 4 * n);
+#pragma unroll
+        for (int j = 0; j < KV_LOADS; ++j)
+          p_etaj[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(re, 4 * (koff[j] / (2 * DK)), 0, 0));
+      }
+      if (ptid < CH) {
+        p_alpha = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rsrc(static_cast<const float*>(a.g.alpha) + tok, 4 * n), 4 * ptid, 0, 0));
+        if constexpr (PG) {
+          p_eta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.eta + tok, 4 * n), 4 * ptid, 0, 0));
+          p_ap = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.alphaP + tok, 4 * n), 4 * ptid, 0, 0));
+          p_bp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.betaP + tok, 4 * n), 4 * ptid, 0, 0));
+        }
+      }
+    };
+    auto fetch_q = [&](int c) __attribute__((always_inline)) {
+      const int t0 = c * CH;
+      const int n = min(CH, T - t0);
+      const auto rq = rsrc(static_cast<const uint16_t*>(a.q) + qk_base + static_cast<long>(t0) * DK, 2 * n * DK);
+#pragma unroll
+      for (int j = 0; j < KV_LOADS; ++j) pq[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, koff[j], 0, 0);
+    };
+    auto fetch_v = [&](int c) __attribute__((always_inline)) {
+      const int t0 = c * CH;
+      const int n = min(CH, T - t0);
+      const auto rv = rsrc(static_cast<const uint16_t*>(a.v) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv);
+#pragma unroll
+      for (int j = 0; j < V_LOADS; ++j) pv[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[j], 0, 0);
+    };
+    // registers -> LDS for chunk c of n tokens (the loads already hold zeros
+    // past the end; alpha = alphaP = 1 there)
+    auto stash_q = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < KV_LOADS; ++j) {
+        const int e = (ptid + j * NP) * VEC;
+        *reinterpret_cast<u32x4*>(&sm.q[c & 1][(e / DK) * PK + e % DK]) = pq[j];
+      }
+    };
+    auto stash_v = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < V_LOADS; ++j) {
+        const int e = (ptid + j * NP) * VEC;
+        *reinterpret_cast<u32x4*>(&sm.v[(e / BV) * PV + e % BV]) = pv[j];
+      }
+    };
+    auto stash_k = [&](int c, int n) __attribute__((always_inline)) {
+      uint16_t* kb = sm.k[c & 1];
+#pragma unroll
+      for (int j = 0; j < KV_LOADS; ++j) {
+        const int e = (ptid + j * NP) * VEC;
+        const int t = e / DK, d = e % DK;
+        *reinterpret_cast<u32x4*>(&kb[t * PK + d]) = pk[j];
+        if constexpr (GAIN == GAIN_EXPLICIT) *reinterpret_cast<u32x4*>(&sm.w[c & 1][t * PK + d]) = pwv[j];
+      }
+      if (PG && ptid < CH) {
+        const bool ok = ptid < n;
+        sm.eta[ptid] = p_eta;
+        sm.alpha[ptid] = ok ? p_alpha : 1.f;
+        sm.ap[ptid] = ok ? p_ap : 1.f;
+        sm.bp[ptid] = p_bp;
+      }
+    };
+
+    // ---------------- producers: gains of chunk c of n tokens from the
+    // staging registers (REG): cumulative decay (wavefront 0 holds the alpha
+    // of token = lane), column scales (the lanes of a k row sum its squares)
+    auto regains = [&](int c, int n) __attribute__((always_inline)) {
+      float* g2 = sm.g2[c & 1];
+      float* cs = sm.cs[c & 1];
+      if (pw == 0) {
+        const float x = wave_prefix_sum(log2_hw(lane < n ? p_alpha : 1.f));
+        g2[lane] = x;
+        sm.gam[c & 1][lane] = exp2_hw(x);
+      }
+      if constexpr (GAIN == GAIN_KLA || GAIN == GAIN_GDN) {
+        constexpr int RL = DK / VEC;  // lanes per k row
+#pragma unroll
+        for (int j = 0; j < KV_LOADS; ++j) {
+          const int t = (ptid + j * NP) * VEC / DK;
+          float s2 = 0.f;
+          if constexpr (GAIN == GAIN_KLA) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float lo = __uint_as_float(pk[j][i] << 16), hi = __uint_as_float(pk[j][i] & 0xFFFF0000u);
+              s2 = fmaf(lo, lo, s2);
+              s2 = fmaf(hi, hi, s2);
+            }
+            s2 = group_sum<RL>(s2);
+          }
+          if (ptid % RL == 0)
+            cs[t] = t < n ? (GAIN == GAIN_KLA ? kla_beta(p_etaj[j], s2, a.g.eps) : p_etaj[j]) : 0.f;
+        }
+      } else {
+        if (ptid < CH) cs[ptid] = 1.f;
+      }
+    };
+
+    // ---------------- producers: gains of a staged chunk c of n tokens from
+    // its LDS copy (PGDN)
+    // part 1: cumulative decay, column scales, PGDN statistic pass 1
+    auto gains1 = [&](int c) __attribute__((always_inline)) {
+      const uint16_t* kb = sm.k[c & 1];
+      if (pw == 0) {
+        const float x = wave_prefix_sum(log2_hw(sm.alpha[lane]));
+        sm.g2[c & 1][lane] = x;
+        sm.gam[c & 1][lane] = exp2_hw(x);
+      }
+      if (ptid < CH) sm.cs[c & 1][ptid] = 1.f;
+      if constexpr (PG) {
+        // the statistic scan in NP / DK segments of the chunk: pass 1 runs
+        // each segment from 0 (segment 0 from the carried statistic)
+        constexpr int NSEG = NP / DK, SL = CH / NSEG;
+        const int d = ptid % DK, g = ptid / DK;
+        pg_start = g == 0 ? sm.acarry[d] : 0.f;
+        float st = pg_start, pr = 1.f;
+#pragma unroll
+        for (int i = 0; i < SL; ++i) {
+          const int t = g * SL + i;
+          st = pgdn_stat(st, sm.ap[t], sm.bp[t], bf2f(kb[t * PK + d]));
+          pr *= sm.ap[t];
+        }
+        sm.ah[g * DK + d] = st;
+        if (d == 0) sm.segp[g] = pr;
+      }
+    };
+    // part 2 (PGDN, after a barrier): the exact start of segment g is
+    // E_(g-1), E_0 = end of segment 0, E_g = P_g E_(g-1) + (pass-1 end of g);
+    // each segment is replayed from it and writes its w = eta B(A) k
+    auto gains2 = [&](int c) __attribute__((always_inline)) {
+      if constexpr (PG) {
+        constexpr int NSEG = NP / DK, SL = CH / NSEG;
+        const int d = ptid % DK, g = ptid / DK;
+        const uint16_t* kb = sm.k[c & 1];
+        uint16_t* wb = sm.w[c & 1];
+        float At = pg_start;
+        if (g > 0) {
+          At = sm.ah[d];
+          for (int gg = 1; gg < g; ++gg) At = fmaf(sm.segp[gg], At, sm.ah[gg * DK + d]);
+        }
+        const float mu = a.g.mu_log[h];
+#pragma unroll
+        for (int i = 0; i < SL; ++i) {
+          const int t = g * SL + i;
+          const float kk = bf2f(kb[t * PK + d]);
+          At = pgdn_stat(At, sm.ap[t], sm.bp[t], kk);
+          wb[t * PK + d] = f2bf(sm.eta[t] * pgdn_scale_hw(At, mu, a.g.log2x) * kk);
+        }
+        // the carried statistic is read again only by the next chunk's pass 1
+        if (g == NSEG - 1) sm.acarry[d] = At;
+      }
+    };
+
+    // ---------------- producers: tile products of chunk c (raw, in registers)
+    // Producer p owns the diagonal block p (L_pp in both orientations, M_pp)
+    // and three of the twelve off-diagonal tiles (L or M of (bi, bj), bj < bi).
+    // item it: kind it % 2 (0: L, 1: M) of tile (bi, bj) = pair it / 2 of
+    // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+    auto item_is_m = [](int it) { return (it & 1) != 0; };
+    auto item_bi = [](int it) { const int pr = it >> 1; return pr < 1 ? 1 : pr < 3 ? 2 : 3; };
+    auto item_bj = [](int it) { const int pr = it >> 1; return pr < 1 ? 0 : pr < 3 ? pr - 1 : pr - 3; };
+    f32x4 at = zero4(), an = zero4(), mt = zero4(), off[3] = {zero4(), zero4(), zero4()};
+    auto tiles = [&](int c) __attribute__((always_inline)) {
+      const uint16_t* kb = sm.k[c & 1];
+      const uint16_t* wb = HAS_W ? sm.w[c & 1] : kb;
+      const int p = pw;
+      at = an = mt = zero4();
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 kp = frag32(kb + 16 * p * PK, PK, lane, s);
+        const bf16x8 qp = frag32(sm.q[c & 1] + 16 * p * PK, PK, lane, s);
+        const bf16x8 wp = HAS_W ? frag32(wb + 16 * p * PK, PK, lane, s) : kp;
+        at = mfma32(wp, kp, at);  // lane: [j = 16p + 4 g4 + u][i = 16p + c16]
+        mt = mfma32(wp, qp, mt);
+        an = mfma32(kp, wp, an);  // lane: [i = 16p + 4 g4 + u][j = 16p + c16]
+      }
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int it = 3 * pw + k;  // wave-uniform
+        const int bi = item_bi(it), bj = item_bj(it);
+        const uint16_t* xsrc = item_is_m(it) ? sm.q[c & 1] : kb;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          acc = mfma32(frag32(wb + 16 * bj * PK, PK, lane, s), frag32(xsrc + 16 * bi * PK, PK, lane, s), acc);
+        off[k] = acc;
+      }
+    };
+
+    // ---------------- producers: scale the raw tile products with the gains
+    // in LDS (2^(G_i - G_j) c_j, masks), store M_pp and the off-diagonal -L
+    // and M tiles; at, an keep the scaled L_pp for the inverse
+    auto scale_tiles = [&](int c) __attribute__((always_inline)) {
+      const int p = pw;
+      const float* g2 = sm.g2[c & 1];
+      const float* cs = sm.cs[c & 1];
+      const float gd_i = g2[16 * p + c16], cd_i = cs[16 * p + c16];
+      const f32x4 gd_j = *reinterpret_cast<const f32x4*>(&g2[16 * p + 4 * g4]);
+      const f32x4 cd_j = *reinterpret_cast<const f32x4*>(&cs[16 * p + 4 * g4]);
+      float go_i[3];
+      f32x4 go_j[3], co_j[3];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int it = 3 * pw + k;
+        go_i[k] = g2[16 * item_bi(it) + c16];
+        go_j[k] = *reinterpret_cast<const f32x4*>(&g2[16 * item_bj(it) + 4 * g4]);
+        co_j[k] = *reinterpret_cast<const f32x4*>(&cs[16 * item_bj(it) + 4 * g4]);
+      }
+      // diagonal block p: at = A^T (row i = 16p + c16, columns j = 16p + 4 g4 + u),
+      // an = A (transposed roles), mt = M_pp like at
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float f = exp2_hw(gd_i - gd_j[u]) * cd_j[u];
+        at[u] = (4 * g4 + u < c16) ? at[u] * f : 0.f;
+        mt[u] = (4 * g4 + u <= c16) ? mt[u] * f : 0.f;
+        an[u] = (c16 < 4 * g4 + u) ? an[u] * (exp2_hw(gd_j[u] - gd_i) * cd_i) : 0.f;
+      }
+      *reinterpret_cast<u32x2*>(&sm.mp[(16 * p + c16) * PT + 16 * p + 4 * g4]) =
+          u32x2{pack_bf2(mt[0], mt[1]), pack_bf2(mt[2], mt[3])};
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int it = 3 * pw + k;
+        const bool m = item_is_m(it);
+        const float sg = m ? 1.f : -1.f;
+        f32x4 val;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) val[u] = sg * off[k][u] * (exp2_hw(go_i[k] - go_j[k][u]) * co_j[k][u]);
+        uint16_t* dst = (m ? sm.mp : sm.ln) + (16 * item_bi(it) + c16) * PT + 16 * item_bj(it) + 4 * g4;
+        *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf2(val[0], val[1]), pack_bf2(val[2], val[3])};
+      }
+    };
+    // ---------------- producers: (I + L_pp)^-1 from at = acc(A^T), an = acc(A),
+    // A = L_pp strictly lower: (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8),
+    // with prod_t(X, Y) = X^T Y; and the S-update scale f_j = 2^(G_n - G_j) c_j
+    auto invert = [&](int c) __attribute__((always_inline)) {
+      if (pw == 1) sm.fs[lane] = sm.cs[c & 1][lane] * exp2_hw(sm.g2[c & 1][CH - 1] - sm.g2[c & 1][lane]);
+      const Split sat = split(at), san = split(an);
+      const f32x4 A2 = prod_t(sat, san), A2t = prod_t(san, sat);
+      const Split sA2 = split(A2), sA2t = split(A2t);
+      const f32x4 A4 = prod_t(sA2t, sA2), A4t = prod_t(sA2, sA2t);
+      const Split sA4 = split(A4), sA4t = split(A4t);
+      const f32x4 A8 = prod_t(sA4t, sA4);
+      const f32x4 p1t = prod_t(split(add_identity(A2, g4, c16)), split(add_identity(-at, g4, c16)));
+      const f32x4 p2t = prod_t(split(add_identity(A4, g4, c16)), split(p1t));
+      const f32x4 tt_ = prod_t(split(add_identity(A8, g4, c16)), split(p2t));  // acc(T^T)
+      // lane holds T[c16][4 g4 + u]: row c16 of block p
+      *reinterpret_cast<u32x2*>(&sm.tb[(16 * pw + c16) * P16 + 4 * g4]) =
+          u32x2{pack_bf2(tt_[0], tt_[1]), pack_bf2(tt_[2], tt_[3])};
+    };
+
+    // ---------------- prologue: chunk 0 staged, its gains (and, REG, tiles)
+    if constexpr (!CONS) {
+      if (nchunks > 0) {
+        fetch_k(0);
+        fetch_q(0);
+        fetch_v(0);
+        if constexpr (REG) regains(0, min(CH, T));
+        stash_k(0, min(CH, T));
+        stash_q(0);
+        stash_v();
+        if (nchunks > 1) {
+          fetch_k(1);
+          fetch_q(1);
+          fetch_v(1);
+        }
+      }
+    }
+    __syncthreads();
+    if constexpr (!CONS) {
+      if (nchunks > 0) {
+        if constexpr (REG) {
+          tiles(0);
+          scale_tiles(0);
+        } else {
+          gains1(0);
+        }
+      }
+    }
+    if constexpr (PG) {
+      __syncthreads();
+      if constexpr (!CONS) {
+        if (nchunks > 0) gains2(0);
+      }
+    }
+    __syncthreads();
+
+    for (int c = 0; c < nchunks; ++c) {
+      const int t0 = c * CH;
+      const int n = min(CH, T - t0);
+      const int n1 = min(CH, T - t0 - CH);  // tokens of chunk c + 1 (if any)
+      const uint16_t* kb = sm.k[c & 1];
+      const uint16_t* wb = HAS_W ? sm.w[c & 1] : kb;
+
+      // ================= P1 =================
+      f32x4 R[4], OQ[4];
+      float gn = 1.f;  // g_n of chunk c (gam is rewritten in P2 / P3)
+      if constexpr (CONS) {
+        // packed state: k-block s = tiles 2 s and 2 s + 1
+        bf16x8 Spk[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) Spk[s] = cat8(pack16(S[2 * s]), pack16(S[2 * s + 1]));
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          f32x4 ak = zero4(), aq = zero4();
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            ak = mfma32(frag32p(kb + 16 * rt * PK, PK, lane, s), Spk[s], ak);
+            aq = mfma32(Spk[s], frag32p(sm.q[c & 1] + 16 * rt * PK, PK, lane, s), aq);
+          }
+          // R[t][c] = V[t][c] - g_t (K S)[t][c], rows t = 16 rt + 4 g4 + i
+          const f32x4 vv = unpack16(read_tr(sm.v, PV, lane, 16 * rt, 16 * ct));
+          const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.gam[c & 1][16 * rt + 4 * g4]);
+          R[rt] = vv - gt * ak;
+          // (Q S)^T[c][t] scaled by g_t, token t = 16 rt + c16
+          OQ[rt] = aq * sm.gam[c & 1][16 * rt + c16];
+        }
+        gn = sm.gam[c & 1][CH - 1];
+      } else {
+        if constexpr (!REG) {
+          tiles(c);
+          scale_tiles(c);
+        }
+        invert(c);
+        // REG: gains of chunk c + 1 from its staged registers; its k and q to
+        // LDS; the loads of k and q of chunk c + 2
+        if (REG && c + 1 < nchunks) {
+          regains(c + 1, n1);
+          stash_k(c + 1, n1);
+          stash_q(c + 1);
+          if (c + 2 < nchunks) {
+            fetch_k(c + 2);
+            fetch_q(c + 2);
+          }
+        }
+      }
+      __syncthreads();  // (1) L, M, (I + L_bb)^-1, f of chunk c ready
+
+      // ================= P2 =================
+      bf16x8 U0, U1, F0, F1;  // U and diag(f) U, k-blocks 0 and 1 (tiles 0,1 and 2,3)
+      if constexpr (CONS) {
+        // U_b = (I + L_bb)^-1 (R_b - sum_{m<b} L_bm U_m)
+        s16x4 Ub[4], Fb[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          f32x4 acc = R[b];
+#pragma unroll
+          for (int m = 0; m < b; ++m) acc = mfma16(frag16(sm.ln + 16 * b * PT + 16 * m, PT, lane), Ub[m], acc);
+          const f32x4 u = mfma16(frag16(sm.tb + 16 * b * P16, P16, lane), pack16(acc), zero4());
+          Ub[b] = pack16(u);
+          Fb[b] = pack16(u * *reinterpret_cast<const f32x4*>(&sm.fs[16 * b + 4 * g4]));
+        }
+        U0 = cat8(Ub[0], Ub[1]);
+        U1 = cat8(Ub[2], Ub[3]);
+        F0 = cat8(Fb[0], Fb[1]);
+        F1 = cat8(Fb[2], Fb[3]);
+        // O^T = g (Q S)^T + (M U)^T: lane holds value columns 16 ct + 4 g4 .. +3
+        // of token 16 rt + c16; rows past the end fall outside the resource
+        const auto ro = rsrc(static_cast<uint16_t*>(a.o) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          f32x4 o = mfma32(U0, frag32p(sm.mp + 16 * rt * PT, PT, lane, 0), OQ[rt]);
+          if (rt >= 2) o = mfma32(U1, frag32p(sm.mp + 16 * rt * PT, PT, lane, 1), o);
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])}, ro,
+                                                ooff[rt], 0, 0);
+        }
+      } else {
+        if (c + 1 < nchunks) {
+          if constexpr (!REG) {
+            stash_k(c + 1, n1);
+            stash_q(c + 1);
+          }
+          stash_v();
+          if constexpr (REG) {
+            if (c + 2 < nchunks) fetch_v(c + 2);
+            tiles(c + 1);  // raw products, scaled in P3
+          }
+        }
+      }
+      __syncthreads();  // (2) the inputs of chunk c + 1 ready
+
+      // ================= P3 =================
+      if constexpr (CONS) {
+        // S_dt = g_n S_dt + W^T diag(f) U: A = W^T read transposed from the
+        // [token][d_k] rows of chunk c (tokens 32 s + 4 g4 + j and + 16)
+        auto update = [&](int dt) __attribute__((always_inline)) {
+          f32x4 acc = S[dt] * gn;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const bf16x8 wa = cat8(read_tr(wb, PK, lane, 32 * s, 16 * dt), read_tr(wb, PK, lane, 32 * s + 16, 16 * dt));
+            acc = mfma32(wa, s == 0 ? F0 : F1, acc);
+          }
+          S[dt] = acc;
+        };
+#pragma unroll
+        for (int dt = 0; dt < NDT / 2; ++dt) update(dt);
+        if constexpr (PG) __syncthreads();  // (3a) PGDN statistic pass 1 done
+#pragma unroll
+        for (int dt = NDT / 2; dt < NDT; ++dt) update(dt);
+      } else {
+        if constexpr (REG) {
+          if (c + 1 < nchunks) scale_tiles(c + 1);
+        } else {
+          if (c + 2 < nchunks) {
+            fetch_k(c + 2);
+            fetch_q(c + 2);
+            fetch_v(c + 2);
+          }
+          if (c + 1 < nchunks) gains1(c + 1);
+          __syncthreads();  // (3a)
+          if (c + 1 < nchunks) gains2(c + 1);
+        }
+      }
+      __syncthreads();  // (3) chunk c + 1: tiles (REG) or gains (PGDN) ready; S updated
+    }
+
+    // ---------------- final state and statistic
+    if constexpr (CONS) {
+      if (a.S_final) {
+        float* base = a.S_final + s_lane;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) base[(16 * dt + i) * a.dv] = S[dt][i];
+      }
+    } else {
+      if (PG && a.aux_final && slice == 0 && ptid < DK)
+        a.aux_final[static_cast<long>(bh) * DK + ptid] = sm.acarry[ptid];
+    }
+  };
+  if (wave < 4) run(Role<true>{});
+  else run(Role<false>{});
+}
+
+}  // namespace ws
+
+template <int DK, int GAIN>
+static hipError_t launch_ws_one(const ChunkArgs& a, hipStream_t st) {
+  using Sm = ws::Smem<DK, GAIN>;
+  static_assert(sizeof(Sm) <= 160 * 1024, "LDS budget");
+  auto kern = ws::chunk_fwd_ws_kernel<DK, GAIN>;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(sizeof(Sm)));
+  if (err != hipSuccess) return err;
+  dim3 grid(static_cast<unsigned>((a.dv / ws::BV) * a.B * a.H));
+  hipLaunchKernelGGL(kern, grid, dim3(512), sizeof(Sm), st, a);
+  return hipGetLastError();
+}
+
+// bf16 io, scalar decay, gains KLA / GDN / PGDN / explicit.
+hipError_t launch_chunk_fwd_bf16_scalar(const ChunkArgs& a, int gain, hipStream_t st) {
+#define DN_WS(DK)                                                        \
+  switch (gain) {                                                        \
+    case GAIN_KLA: return launch_ws_one<DK, GAIN_KLA>(a, st);             \
+    case GAIN_GDN: return launch_ws_one<DK, GAIN_GDN>(a, st);             \
+    case GAIN_PGDN: return launch_ws_one<DK, GAIN_PGDN>(a, st);           \
+    case GAIN_EXPLICIT: return launch_ws_one<DK, GAIN_EXPLICIT>(a, st);   \
+    default: return hipErrorInvalidValue;                                \
+  }
+  if (a.dk == 128) {
+    DN_WS(128)
+  }
+  DN_WS(64)
+#undef DN_WS
+}
+
+}  // namespace dn

@@ -23,8 +23,12 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   bf16 h = static_cast<bf16>(f);
   return __builtin_bit_cast(uint16_t, h);
 }
+// Two floats -> two bf16 (RNE) in one word, a in the low half: a single
+// v_cvt_pk_bf16_f32 (a vector conversion; element-wise casts would not fuse).
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-  return static_cast<uint32_t>(f2bf(a)) | (static_cast<uint32_t>(f2bf(b)) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // Element-type traits of the operand buffers kept in LDS.
