@@ -499,7 +499,10 @@ void chunk_fwd_kernel(ChunkArgs a) {
         }
       }
       if constexpr (GAIN == GAIN_KDN) {
-        // z_t = sum_d p_hat k^2: wavefront sums, combined in a fixed order
+        // z_t = sum_d p_hat k^2: per-wavefront sums (reduce-scattered, lane t
+        // gets token t), combined over the wavefronts in a fixed order
+        static_assert(CH == 64, "one token per lane");
+        float zt[CH];
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
           float z = 0.f;
@@ -508,9 +511,9 @@ void chunk_fwd_kernel(ChunkArgs a) {
             const int d = tid + cc * NT;
             if (d < DK) z += pkr[cc][t] * EL::get(sm.k[t * PK + d]);
           }
-          z = wave_sum(z);
-          if (lane == 0) sm.zp[wave][t] = z;
+          zt[t] = z;
         }
+        sm.zp[wave][lane] = wave_reduce_scatter64(zt, lane);
         __syncthreads();
         if (tid < CH) {
           float z = 0.f;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dn {
 
 typedef __bf16 bf16;
@@ -102,6 +104,39 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
+}
+
+// DPP move within rows of 16 lanes (gfx9 encodings: quad_perm = 2-bit lane
+// selectors, row_mirror = 0x140, row_half_mirror = 0x141).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sums of 64 per-lane vectors across the 64 lanes of a wavefront,
+// reduce-scattered: on return lane l holds the total of element l.  Each
+// halving step pairs a lane with one whose bit D differs and whose higher
+// bits agree (xor 32 and 16 by cross-lane shuffles, the row mirrors for 8
+// and 4, quad permutes for 2 and 1): the lane keeps half D of its block and
+// adds the partner's copy of it.  v is overwritten.
+__device__ __forceinline__ float wave_reduce_scatter64(float (&v)[64], int lane) {
+  auto step = [&](auto dtag, auto partner) __attribute__((always_inline)) {
+    constexpr int D = decltype(dtag)::value;
+    const bool hi = (lane & D) != 0;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const float send = hi ? v[i] : v[D + i];
+      const float keep = hi ? v[D + i] : v[i];
+      v[i] = keep + partner(send);
+    }
+  };
+  step(std::integral_constant<int, 32>{}, [](float x) { return __shfl_xor(x, 32, 64); });
+  step(std::integral_constant<int, 16>{}, [](float x) { return __shfl_xor(x, 16, 64); });
+  step(std::integral_constant<int, 8>{}, [](float x) { return dpp_move<0x140>(x); });
+  step(std::integral_constant<int, 4>{}, [](float x) { return dpp_move<0x141>(x); });
+  step(std::integral_constant<int, 2>{}, [](float x) { return dpp_move<0x4E>(x); });
+  step(std::integral_constant<int, 1>{}, [](float x) { return dpp_move<0xB1>(x); });
+  return v[0];
 }
 
 }  // namespace dn

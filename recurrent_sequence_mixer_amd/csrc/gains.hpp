@@ -31,9 +31,11 @@ __device__ __forceinline__ float pgdn_scale(float A, float mu, float log2x) {
 __device__ __forceinline__ float kdn_predict(float a, float p, float om) {
   return fmaf(a * a, p, om);
 }
+// The division is the hardware reciprocal (v_rcp_f32, within 1 ulp): the
+// update is contractive, so the rounding does not accumulate along the scan.
 __device__ __forceinline__ float kdn_update(float p_hat, float k, float mu_over_r) {
   const float u = mu_over_r * k * k;
-  return p_hat / fmaf(u, p_hat, 1.0f);
+  return p_hat * __builtin_amdgcn_rcpf(fmaf(u, p_hat, 1.0f));
 }
 
 }  // namespace dn
