@@ -183,6 +183,39 @@ __device__ __forceinline__ f32x4 add_identity(f32x4 x, int g4, int c16) {
   return x;
 }
 
+// Layout of the [token][d_k] tiles k, q, w in LDS.  For d_k = 128 the rows
+// are unpadded and the 4-element groups of row r are XOR-swizzled by
+// f(r) = 4 (r mod 8) ^ 2 (floor(r / 8) mod 2).  Measured on gfx950, this
+// keeps the 16-byte row writes of the staging, the 8-byte fragment halves
+// (every product over d_k reads its operands as two halves: any k order
+// shared by both operands is exact) and the transposing reads of W^T free of
+// bank conflicts.  f is even, so 16-byte pieces stay contiguous, and it
+// depends on r mod 16 only.  d_k = 64 uses padded rows.
+template <int DK>
+struct KLay {
+  static constexpr bool SWZ = DK == 128;
+  static constexpr int P = SWZ ? DK : DK + 8;
+  static __device__ __forceinline__ int f(int r) { return SWZ ? ((4 * (r & 7)) ^ (2 * ((r >> 3) & 1))) : 0; }
+  static __device__ __forceinline__ int idx(int r, int d) {
+    return r * P + ((((d >> 2) ^ f(r)) << 2) | (d & 3));
+  }
+  // row0 + lane % 16, k = 32 s + 8 (lane / 16) .. +7: one 16-byte read
+  static __device__ __forceinline__ bf16x8 frag32(const uint16_t* b, int row0, int lane, int s) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(b + idx(row0 + (lane & 15), 32 * s + 8 * (lane >> 4))));
+  }
+  // row0 + lane % 16, k = 32 s + 4 g .. +3 and 32 s + 16 + 4 g .. +3
+  static __device__ __forceinline__ bf16x8 frag32p(const uint16_t* b, int row0, int lane, int s) {
+    const int r = row0 + (lane & 15);
+    return cat8(__builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(b + idx(r, 32 * s + 4 * (lane >> 4)))),
+                __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(b + idx(r, 32 * s + 16 + 4 * (lane >> 4)))));
+  }
+  // transposing read of rows r0 + 4 g + j, column c0 + lane % 16 (see read_tr)
+  static __device__ __forceinline__ s16x4 read_tr(const uint16_t* b, int r0, int c0, int lane) {
+    const int r = r0 + 4 * (lane >> 4) + ((lane & 15) >> 2);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds*)(b + idx(r, c0 + 4 * (lane & 3))));
+  }
+};
+
 template <bool B>
 struct Role {
   static constexpr bool consumer = B;
@@ -190,7 +223,7 @@ struct Role {
 
 template <int DK, int GAIN>
 struct Smem {
-  static constexpr int PK = DK + 8;   // [token][d_k] rows, bf16
+  static constexpr int PK = KLay<DK>::P;  // [token][d_k] rows, bf16 (see KLay)
   static constexpr int PV = BV + 16;  // [token][value] rows, bf16
   static constexpr int PT = CH + 8;   // [token][token] rows, bf16
   static constexpr int P16 = 16 + 8;  // rows of 16-wide blocks
@@ -230,7 +263,8 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
   // tiles in P1, once its write vectors exist.
   constexpr bool REG = !PG;
   using Sm = Smem<DK, GAIN>;
-  constexpr int PK = Sm::PK, PV = Sm::PV, PT = Sm::PT, P16 = Sm::P16;
+  constexpr int PV = Sm::PV, PT = Sm::PT, P16 = Sm::P16;
+  using KL = KLay<DK>;
   static_assert(KV_LOADS * NP * VEC == CH * DK && V_LOADS * NP * VEC == CH * BV, "tile split");
   static_assert(NP % DK == 0 && CH % (NP / DK) == 0, "statistic scan layout");
 
@@ -372,7 +406,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
       for (int j = 0; j < KV_LOADS; ++j) {
         const int e = (ptid + j * NP) * VEC;
-        *reinterpret_cast<u32x4*>(&sm.q[c & 1][(e / DK) * PK + e % DK]) = pq[j];
+        *reinterpret_cast<u32x4*>(&sm.q[c & 1][KL::idx(e / DK, e % DK)]) = pq[j];
       }
     };
     auto stash_v = [&]() __attribute__((always_inline)) {
@@ -388,8 +422,8 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
       for (int j = 0; j < KV_LOADS; ++j) {
         const int e = (ptid + j * NP) * VEC;
         const int t = e / DK, d = e % DK;
-        *reinterpret_cast<u32x4*>(&kb[t * PK + d]) = pk[j];
-        if constexpr (GAIN == GAIN_EXPLICIT) *reinterpret_cast<u32x4*>(&sm.w[c & 1][t * PK + d]) = pwv[j];
+        *reinterpret_cast<u32x4*>(&kb[KL::idx(t, d)]) = pk[j];
+        if constexpr (GAIN == GAIN_EXPLICIT) *reinterpret_cast<u32x4*>(&sm.w[c & 1][KL::idx(t, d)]) = pwv[j];
       }
       if (PG && ptid < CH) {
         const bool ok = ptid < n;
@@ -418,16 +452,22 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
           const int t = (ptid + j * NP) * VEC / DK;
           float s2 = 0.f;
           if constexpr (GAIN == GAIN_KLA) {
+            // sum of squares of the 8 channels (bf16 products are exact in fp32)
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float lo = __uint_as_float(pk[j][i] << 16), hi = __uint_as_float(pk[j][i] & 0xFFFF0000u);
-              s2 = fmaf(lo, lo, s2);
-              s2 = fmaf(hi, hi, s2);
+              // through a scalar: bit-casting the vector element itself reads
+              // element 0 whatever i is (hipcc 7.2)
+              const uint32_t x = pk[j][i];
+              const bf16x2 two = __builtin_bit_cast(bf16x2, x);
+              s2 = __builtin_amdgcn_fdot2_f32_bf16(two, two, s2, false);
             }
             s2 = group_sum<RL>(s2);
           }
+          // KLA step size eta / (||k||^2 + eps) (Kaczmarz Linear Attention §2.1),
+          // with the hardware reciprocal
           if (ptid % RL == 0)
-            cs[t] = t < n ? (GAIN == GAIN_KLA ? kla_beta(p_etaj[j], s2, a.g.eps) : p_etaj[j]) : 0.f;
+            cs[t] = t < n ? (GAIN == GAIN_KLA ? p_etaj[j] * __builtin_amdgcn_rcpf(s2 + a.g.eps) : p_etaj[j]) : 0.f;
         }
       } else {
         if (ptid < CH) cs[ptid] = 1.f;
@@ -455,7 +495,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
         for (int i = 0; i < SL; ++i) {
           const int t = g * SL + i;
-          st = pgdn_stat(st, sm.ap[t], sm.bp[t], bf2f(kb[t * PK + d]));
+          st = pgdn_stat(st, sm.ap[t], sm.bp[t], bf2f(kb[KL::idx(t, d)]));
           pr *= sm.ap[t];
         }
         sm.ah[g * DK + d] = st;
@@ -480,9 +520,9 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
         for (int i = 0; i < SL; ++i) {
           const int t = g * SL + i;
-          const float kk = bf2f(kb[t * PK + d]);
+          const float kk = bf2f(kb[KL::idx(t, d)]);
           At = pgdn_stat(At, sm.ap[t], sm.bp[t], kk);
-          wb[t * PK + d] = f2bf(sm.eta[t] * pgdn_scale_hw(At, mu, a.g.log2x) * kk);
+          wb[KL::idx(t, d)] = f2bf(sm.eta[t] * pgdn_scale_hw(At, mu, a.g.log2x) * kk);
         }
         // the carried statistic is read again only by the next chunk's pass 1
         if (g == NSEG - 1) sm.acarry[d] = At;
@@ -505,9 +545,9 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
       at = an = mt = zero4();
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 kp = frag32(kb + 16 * p * PK, PK, lane, s);
-        const bf16x8 qp = frag32(sm.q[c & 1] + 16 * p * PK, PK, lane, s);
-        const bf16x8 wp = HAS_W ? frag32(wb + 16 * p * PK, PK, lane, s) : kp;
+        const bf16x8 kp = KL::frag32p(kb, 16 * p, lane, s);
+        const bf16x8 qp = KL::frag32p(sm.q[c & 1], 16 * p, lane, s);
+        const bf16x8 wp = HAS_W ? KL::frag32p(wb, 16 * p, lane, s) : kp;
         at = mfma32(wp, kp, at);  // lane: [j = 16p + 4 g4 + u][i = 16p + c16]
         mt = mfma32(wp, qp, mt);
         an = mfma32(kp, wp, an);  // lane: [i = 16p + 4 g4 + u][j = 16p + c16]
@@ -520,7 +560,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-          acc = mfma32(frag32(wb + 16 * bj * PK, PK, lane, s), frag32(xsrc + 16 * bi * PK, PK, lane, s), acc);
+          acc = mfma32(KL::frag32p(wb, 16 * bj, lane, s), KL::frag32p(xsrc, 16 * bi, lane, s), acc);
         off[k] = acc;
       }
     };
@@ -642,8 +682,8 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
           f32x4 ak = zero4(), aq = zero4();
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
-            ak = mfma32(frag32p(kb + 16 * rt * PK, PK, lane, s), Spk[s], ak);
-            aq = mfma32(Spk[s], frag32p(sm.q[c & 1] + 16 * rt * PK, PK, lane, s), aq);
+            ak = mfma32(KL::frag32p(kb, 16 * rt, lane, s), Spk[s], ak);
+            aq = mfma32(Spk[s], KL::frag32p(sm.q[c & 1], 16 * rt, lane, s), aq);
           }
           // R[t][c] = V[t][c] - g_t (K S)[t][c], rows t = 16 rt + 4 g4 + i
           const f32x4 vv = unpack16(read_tr(sm.v, PV, lane, 16 * rt, 16 * ct));
@@ -724,7 +764,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
           f32x4 acc = S[dt] * gn;
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            const bf16x8 wa = cat8(read_tr(wb, PK, lane, 32 * s, 16 * dt), read_tr(wb, PK, lane, 32 * s + 16, 16 * dt));
+            const bf16x8 wa = cat8(KL::read_tr(wb, 32 * s, 16 * dt, lane), KL::read_tr(wb, 32 * s + 16, 16 * dt, lane));
             acc = mfma32(wa, s == 0 ? F0 : F1, acc);
           }
           S[dt] = acc;
