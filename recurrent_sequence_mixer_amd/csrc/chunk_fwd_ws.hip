@@ -20,11 +20,12 @@
 //     the inputs HBM -> registers -> LDS.
 // Per chunk c, three phases separated by workgroup barriers:
 //   P1  consumers: K S -> R = V - g K S, and (Q S)^T.
-//       producers: (I + L_bb)^-1 of c; the gains of chunk c + 1 from its
+//       producers: (I + L_bb)^-1 of c; the decay of chunk c + 1 from its
 //       staging registers, its k and q into LDS, their loads for c + 2.
 //   P2  consumers: solve -> U; O = g Q S + M U -> HBM.
 //       producers: v of chunk c + 1 into LDS and its loads for c + 2; the
-//       raw L and M tile products of chunk c + 1.
+//       raw L and M tile products of chunk c + 1, and its column scales
+//       (the key norms of KLA are the diagonal of the raw K K^T).
 //   P3  consumers: S = g_n S + W^T diag(f) U.
 //       producers: scale and store the L and M tiles of chunk c + 1.
 // PGDN, whose write vectors come out of a statistic scan over the LDS copy
@@ -37,13 +38,13 @@
 // Register-resident operands.  In v_mfma_f32_16x16x32_bf16 lane l supplies
 // k = 8 (l / 16) .. +7 of its row (A) or column (B), and the accumulator holds
 // rows 4 (l / 16) + i of column l % 16.  The contraction of one MFMA may use
-// any pairing of k slots that A and B share, so the pair of accumulator tiles
-// holding rows 32 s + 4 g + i and 32 s + 16 + 4 g + i (i < 4) of S or U is
-// taken as the operand of k-block s as it stands, and the other operand reads
-// the same two groups of 4 indices (two 8-byte LDS reads, or two transposing
-// ds_read_b64_tr_b16 reads where the contraction runs along the rows of the
-// stored matrix).  With 16x16x16 operands the accumulator layout already is
-// the B layout (used by the solve).
+// any pairing of k slots that A and B share, so a pair of packed accumulator
+// tiles is the operand of one k-block as it stands, and the other operand is
+// read in the matching order: the state tiles hold their key channels in the
+// order of the 16-byte fragments of K and Q (see KLay), W^T comes from
+// transposing ds_read_b64_tr_b16 reads, and M is stored with its token columns
+// in the order of the packed U tiles (see mcol).  With 16x16x16 operands the
+// accumulator layout already is the B layout (used by the solve).
 #include "common.hpp"
 #include "gains.hpp"
 #include "launch.hpp"
@@ -117,18 +118,6 @@ __device__ __forceinline__ bf16x8 cat8(s16x4 lo, s16x4 hi) {
   const u32x4 v = {a[0], a[1], b[0], b[1]};
   return __builtin_bit_cast(bf16x8, v);
 }
-// row (lane % 16) of a 16-row tile, k = 32 s + 8 (lane / 16) .. +7: one 16-byte read
-__device__ __forceinline__ bf16x8 frag32(const uint16_t* p, int ld, int lane, int s) {
-  return __builtin_bit_cast(
-      bf16x8, *reinterpret_cast<const u32x4*>(p + (lane & 15) * ld + 32 * s + 8 * (lane >> 4)));
-}
-// row (lane % 16), k = 32 s + 4 g .. +3 and 32 s + 16 + 4 g .. +3 (g = lane / 16):
-// the partner of a register-resident accumulator tile pair
-__device__ __forceinline__ bf16x8 frag32p(const uint16_t* p, int ld, int lane, int s) {
-  const uint16_t* r = p + (lane & 15) * ld + 32 * s + 4 * (lane >> 4);
-  return cat8(__builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(r)),
-              __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(r + 16)));
-}
 // Transposing read (ds_read_b64_tr_b16): within each group of 16 lanes, lane
 // l receives element l % 4 of the 8-byte chunk addressed by lane 4 j + l / 4,
 // j = 0..3.  With lane (g, l) addressing row r0 + 4 g + l / 4, column
@@ -158,10 +147,12 @@ __device__ __forceinline__ f32x4 unpack16(s16x4 p) {
                __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xFFFF0000u)};
 }
 
-// A 16x16 fp32 accumulator tile as a sum of two bf16 tiles (hi + lo), and the
-// product X^T Y of two such tiles on three 16x16x16 MFMAs (the lo * lo term is
-// below fp32 rounding of the result).  Packed, an accumulator tile acc(X) is
-// the A operand of X^T and the B operand of X.
+// A 16x16 fp32 accumulator tile as a sum of two bf16 tiles (hi + lo), and
+// C + X^T Y for two such tiles (the lo * lo term is below fp32 rounding of the
+// result).  Packed, an accumulator tile acc(X) is the A operand of X^T and the
+// B operand of X.  hi^T hi + lo^T hi runs as one 16x16x32 MFMA whose k slots
+// pair (x.hi, x.lo) with (y.hi, y.hi); hi^T lo is a 16x16x16 MFMA (same cost
+// per instruction as the x32 form on gfx950).
 struct Split {
   s16x4 hi, lo;
 };
@@ -171,50 +162,58 @@ __device__ __forceinline__ Split split(f32x4 x) {
   r.lo = pack16(x - unpack16(r.hi));
   return r;
 }
-__device__ __forceinline__ f32x4 prod_t(const Split& x, const Split& y) {
-  f32x4 c = mfma16(x.hi, y.hi, zero4());
-  c = mfma16(x.hi, y.lo, c);
-  return mfma16(x.lo, y.hi, c);
-}
-__device__ __forceinline__ f32x4 add_identity(f32x4 x, int g4, int c16) {
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    if (4 * g4 + u == c16) x[u] += 1.f;
-  return x;
+__device__ __forceinline__ f32x4 prod_t(const Split& x, const Split& y, f32x4 c) {
+  c = mfma32(cat8(x.hi, x.lo), cat8(y.hi, y.hi), c);
+  return mfma16(x.hi, y.lo, c);
 }
 
-// Layout of the [token][d_k] tiles k, q, w in LDS.  For d_k = 128 the rows
-// are unpadded and the 4-element groups of row r are XOR-swizzled by
-// f(r) = 4 (r mod 8) ^ 2 (floor(r / 8) mod 2).  Measured on gfx950, this
-// keeps the 16-byte row writes of the staging, the 8-byte fragment halves
-// (every product over d_k reads its operands as two halves: any k order
-// shared by both operands is exact) and the transposing reads of W^T free of
-// bank conflicts.  f is even, so 16-byte pieces stay contiguous, and it
-// depends on r mod 16 only.  d_k = 64 uses padded rows.
+// Layout of the [token][d_k] tiles k, q, w in LDS: row-major rows of
+// d_k + 16 bf16.  Measured on gfx950, the 16-byte fragment reads of 16 rows
+// by 4 lane groups are free of bank conflicts at this pitch (the 8-byte
+// half reads are not), and every fragment address is one per-lane base plus a
+// compile-time offset.
+//
+// State tile rows.  A consumer's packed state operand of k-block s (the
+// accumulator tiles 2 s and 2 s + 1, rows 4 g + i) must meet one 16-byte
+// fragment of K or Q, i.e. key channels 32 s + 8 g .. +7.  So row 4 g + i of
+// state tile 2 s + h holds key channel 32 s + 8 g + 4 h + i; the update's
+// transposing reads of W^T fetch those channels (sigma_channel).
 template <int DK>
 struct KLay {
-  static constexpr bool SWZ = DK == 128;
-  static constexpr int P = SWZ ? DK : DK + 8;
-  static __device__ __forceinline__ int f(int r) { return SWZ ? ((4 * (r & 7)) ^ (2 * ((r >> 3) & 1))) : 0; }
-  static __device__ __forceinline__ int idx(int r, int d) {
-    return r * P + ((((d >> 2) ^ f(r)) << 2) | (d & 3));
+  static constexpr int P = DK + 16;
+  static __device__ __forceinline__ int idx(int r, int d) { return r * P + d; }
+  // per-lane base of the fragment reads: row lane % 16, k-group lane / 16
+  static __device__ __forceinline__ int frag_base(int lane) { return (lane & 15) * P + 8 * (lane >> 4); }
+  // row0 + lane % 16 (row0 a multiple of 16), k = 32 s + 8 (lane / 16) .. +7
+  static __device__ __forceinline__ bf16x8 frag32(const uint16_t* b, int fb, int row0, int s) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(b + fb + row0 * P + 32 * s));
   }
-  // row0 + lane % 16, k = 32 s + 8 (lane / 16) .. +7: one 16-byte read
-  static __device__ __forceinline__ bf16x8 frag32(const uint16_t* b, int row0, int lane, int s) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(b + idx(row0 + (lane & 15), 32 * s + 8 * (lane >> 4))));
+  // per-lane base of the transposing reads: addressing lane a = 4 j + q of
+  // group g reads row 4 g + j, channel group 8 q
+  static __device__ __forceinline__ int tr_base(int lane) {
+    const int a = lane & 15;
+    return (4 * (lane >> 4) + (a >> 2)) * P + 8 * (a & 3);
   }
-  // row0 + lane % 16, k = 32 s + 4 g .. +3 and 32 s + 16 + 4 g .. +3
-  static __device__ __forceinline__ bf16x8 frag32p(const uint16_t* b, int row0, int lane, int s) {
-    const int r = row0 + (lane & 15);
-    return cat8(__builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(b + idx(r, 32 * s + 4 * (lane >> 4)))),
-                __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(b + idx(r, 32 * s + 16 + 4 * (lane >> 4)))));
+  // A operand of W^T for state tile 2 s + h over tokens r0 + 4 g + j (r0 a
+  // multiple of 16): lane (g, l) receives W[r0 + 4 g + j][sigma(l)], j = 0..3,
+  // sigma(l) = 32 s + 8 (l / 4) + 4 h + l % 4 (see read_tr); tb = tr_base(lane)
+  static __device__ __forceinline__ s16x4 read_tr(const uint16_t* b, int tb, int r0, int s, int h) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds*)(b + tb + r0 * P + 32 * s + 4 * h));
   }
-  // transposing read of rows r0 + 4 g + j, column c0 + lane % 16 (see read_tr)
-  static __device__ __forceinline__ s16x4 read_tr(const uint16_t* b, int r0, int c0, int lane) {
-    const int r = r0 + 4 * (lane >> 4) + ((lane & 15) >> 2);
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds*)(b + idx(r, c0 + 4 * (lane & 3))));
+  // key channel of row 4 g + i of state tile dt
+  static __device__ __forceinline__ int sigma_channel(int dt, int g, int i) {
+    return 32 * (dt >> 1) + 8 * g + 4 * (dt & 1) + i;
   }
 };
+
+// Column order of the M tiles in LDS: within each block of 32 tokens, token
+// group (4 tokens) gr sits at position 2 (gr mod 4) + gr / 4, so that M U
+// reads the token pairs {32 s + 4 g .. +3, 32 s + 16 + 4 g .. +3} that the
+// packed U tiles hold as one 16-byte piece at 32 s + 8 g.
+__device__ __forceinline__ int mcol(int j) {
+  const int gr = (j >> 2) & 7;
+  return (j & ~31) + 4 * (2 * (gr & 3) + (gr >> 2)) + (j & 3);
+}
 
 template <bool B>
 struct Role {
@@ -238,6 +237,7 @@ struct Smem {
   alignas(16) float g2[2][CH];                  // cumulative log2-decay, by chunk parity
   alignas(16) float gam[2][CH];                 // 2^g2, by chunk parity
   alignas(16) float cs[2][CH];                  // column scale c_j, by chunk parity
+  alignas(16) float kap[2][CH];                 // 2^(E_b(j) - G_j) c_j, E_b = G at the end of j's block
   alignas(16) float fs[CH];                     // S-update scale f_j
   float eta[CH], alpha[CH], ap[CH], bp[CH];     // per-token gates
   alignas(16) float ah[4 * DK];                 // PGDN: statistic at the segment ends
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
   // (rows 0..15 x tokens 16..31, rows 32..47 x tokens 48..63) are zeros
   for (int e = tid; e < 2 * 256; e += NT) {
     const int bi = 2 * (e >> 8), r = (e >> 4) & 15, x = e & 15;
-    sm.mp[(16 * bi + r) * PT + 16 * (bi + 1) + x] = 0;
+    sm.mp[(16 * bi + r) * PT + mcol(16 * (bi + 1) + x)] = 0;
   }
 
   auto run = [&](auto role) __attribute__((always_inline)) {
@@ -311,6 +311,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
     const int ct = wave;           // consumers: column tile
     const int pw = wave - 4;       // producers: wavefront index
     const int ptid = tid - 256;    // producers: thread index
+    const int fb = KL::frag_base(lane), trb = KL::tr_base(lane);  // LDS operand bases
 
     // consumers: byte offsets of the output pieces (token 16 rt + c16, value
     // columns col0 + 16 ct + 4 g4 .. +3) inside a chunk
@@ -318,16 +319,17 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) ooff[rt] = 2 * ((16 * rt + c16) * a.dv + col0 + 16 * ct + 4 * g4);
 
-    // ---------------- consumer state: tile dt = rows 16 dt + 4 g4 + i, column c16
+    // ---------------- consumer state: element i of tile dt = key channel
+    // sigma_channel(dt, g4, i), value column c16 of the wave's 16
     f32x4 S[CONS ? NDT : 1];
-    const long s_lane = (static_cast<long>(bh) * DK + 4 * g4) * a.dv + col0 + 16 * ct + c16;
+    const long s_lane = (static_cast<long>(bh) * DK + 8 * g4) * a.dv + col0 + 16 * ct + c16;
     if constexpr (CONS) {
       if (a.S0) {
         const float* base = a.S0 + s_lane;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) S[dt][i] = base[(16 * dt + i) * a.dv];
+          for (int i = 0; i < 4; ++i) S[dt][i] = base[(KL::sigma_channel(dt, 0, i)) * a.dv];
       } else {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) S[dt] = zero4();
@@ -340,7 +342,9 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
     // of k / q / w in consecutive lanes (coalesced), likewise for v
     u32x4 pk[KV_LOADS], pq[KV_LOADS], pwv[GAIN == GAIN_EXPLICIT ? KV_LOADS : 1], pv[V_LOADS];
     float p_eta = 0.f, p_alpha = 1.f, p_ap = 1.f, p_bp = 0.f;
-    float p_etaj[KV_LOADS];  // eta of the token of each staged k piece (REG)
+    float p_etad = 0.f;  // eta of token 16 pw + lane % 16 (REG: its diagonal lane sets the gain)
+    float p_etag = 0.f;  // the same for the chunk whose gains are being formed (the next
+                         // fetch overwrites p_etad before its diagonal is known)
     float pg_start = 0.f;  // PGDN: carried statistic read by pass 1 (segment 0)
 
     // per-lane byte offsets inside a chunk: the k / q / w pieces (row-major
@@ -355,11 +359,13 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
     }
     // loads of chunk c through buffer resources that end at its last token:
     // past the end k = q = w = v = eta = alphaP = betaP = 0 (alpha, alphaP are
-    // replaced by 1 where they are used)
+    // replaced by 1 where they are used).  Chunks past the last one get empty
+    // resources, so the loads ahead are issued unconditionally: a load under a
+    // branch leaves a register merge after it that waits for the load.
     // k (w, gates) and q, v are loaded, and staged, at different points
     auto fetch_k = [&](int c) __attribute__((always_inline)) {
       const int t0 = c * CH;
-      const int n = min(CH, T - t0);
+      const int n = max(0, min(CH, T - t0));
       const long tok = static_cast<long>(bh) * T + t0;
       const auto rk = rsrc(static_cast<const uint16_t*>(a.k) + qk_base + static_cast<long>(t0) * DK, 2 * n * DK);
 #pragma unroll
@@ -370,32 +376,27 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
           pwv[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, koff[j], 0, 0);
         }
       }
-      if constexpr (REG && HAS_ETA) {
-        const auto re = rsrc(a.g.eta + tok, 4 * n);
-#pragma unroll
-        for (int j = 0; j < KV_LOADS; ++j)
-          p_etaj[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(re, 4 * (koff[j] / (2 * DK)), 0, 0));
-      }
-      if (ptid < CH) {
-        p_alpha = __uint_as_float(
-            __builtin_amdgcn_raw_buffer_load_b32(rsrc(static_cast<const float*>(a.g.alpha) + tok, 4 * n), 4 * ptid, 0, 0));
-        if constexpr (PG) {
-          p_eta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.eta + tok, 4 * n), 4 * ptid, 0, 0));
-          p_ap = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.alphaP + tok, 4 * n), 4 * ptid, 0, 0));
-          p_bp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.betaP + tok, 4 * n), 4 * ptid, 0, 0));
-        }
+      if constexpr (REG && HAS_ETA)
+        p_etad = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.eta + tok, 4 * n), 4 * (16 * pw + c16), 0, 0));
+      // per-token gates: lanes ptid >= n (all of waves 5..7) read zeros
+      p_alpha = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rsrc(static_cast<const float*>(a.g.alpha) + tok, 4 * n), 4 * ptid, 0, 0));
+      if constexpr (PG) {
+        p_eta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.eta + tok, 4 * n), 4 * ptid, 0, 0));
+        p_ap = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.alphaP + tok, 4 * n), 4 * ptid, 0, 0));
+        p_bp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.betaP + tok, 4 * n), 4 * ptid, 0, 0));
       }
     };
     auto fetch_q = [&](int c) __attribute__((always_inline)) {
       const int t0 = c * CH;
-      const int n = min(CH, T - t0);
+      const int n = max(0, min(CH, T - t0));
       const auto rq = rsrc(static_cast<const uint16_t*>(a.q) + qk_base + static_cast<long>(t0) * DK, 2 * n * DK);
 #pragma unroll
       for (int j = 0; j < KV_LOADS; ++j) pq[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, koff[j], 0, 0);
     };
     auto fetch_v = [&](int c) __attribute__((always_inline)) {
       const int t0 = c * CH;
-      const int n = min(CH, T - t0);
+      const int n = max(0, min(CH, T - t0));
       const auto rv = rsrc(static_cast<const uint16_t*>(a.v) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv);
 #pragma unroll
       for (int j = 0; j < V_LOADS; ++j) pv[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[j], 0, 0);
@@ -434,46 +435,16 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
       }
     };
 
-    // ---------------- producers: gains of chunk c of n tokens from the
-    // staging registers (REG): cumulative decay (wavefront 0 holds the alpha
-    // of token = lane), column scales (the lanes of a k row sum its squares)
+    // ---------------- producers (REG): cumulative decay of chunk c of n tokens
+    // from the staging registers (wavefront 0 holds the alpha of token = lane)
     auto regains = [&](int c, int n) __attribute__((always_inline)) {
-      float* g2 = sm.g2[c & 1];
-      float* cs = sm.cs[c & 1];
+      p_etag = p_etad;
       if (pw == 0) {
         const float x = wave_prefix_sum(log2_hw(lane < n ? p_alpha : 1.f));
-        g2[lane] = x;
+        sm.g2[c & 1][lane] = x;
         sm.gam[c & 1][lane] = exp2_hw(x);
       }
-      if constexpr (GAIN == GAIN_KLA || GAIN == GAIN_GDN) {
-        constexpr int RL = DK / VEC;  // lanes per k row
-#pragma unroll
-        for (int j = 0; j < KV_LOADS; ++j) {
-          const int t = (ptid + j * NP) * VEC / DK;
-          float s2 = 0.f;
-          if constexpr (GAIN == GAIN_KLA) {
-            // sum of squares of the 8 channels (bf16 products are exact in fp32)
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              // through a scalar: bit-casting the vector element itself reads
-              // element 0 whatever i is (hipcc 7.2)
-              const uint32_t x = pk[j][i];
-              const bf16x2 two = __builtin_bit_cast(bf16x2, x);
-              s2 = __builtin_amdgcn_fdot2_f32_bf16(two, two, s2, false);
-            }
-            s2 = group_sum<RL>(s2);
-          }
-          // KLA step size eta / (||k||^2 + eps) (Kaczmarz Linear Attention §2.1),
-          // with the hardware reciprocal
-          if (ptid % RL == 0)
-            cs[t] = t < n ? (GAIN == GAIN_KLA ? p_etaj[j] * __builtin_amdgcn_rcpf(s2 + a.g.eps) : p_etaj[j]) : 0.f;
-        }
-      } else {
-        if (ptid < CH) cs[ptid] = 1.f;
-      }
     };
-
     // ---------------- producers: gains of a staged chunk c of n tokens from
     // its LDS copy (PGDN)
     // part 1: cumulative decay, column scales, PGDN statistic pass 1
@@ -483,6 +454,8 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
         const float x = wave_prefix_sum(log2_hw(sm.alpha[lane]));
         sm.g2[c & 1][lane] = x;
         sm.gam[c & 1][lane] = exp2_hw(x);
+        // kap_t = 2^(E_b - G_t), E_b = G at the end of t's block of 16
+        sm.kap[c & 1][lane] = exp2_hw(__shfl(x, lane | 15) - x);
       }
       if (ptid < CH) sm.cs[c & 1][ptid] = 1.f;
       if constexpr (PG) {
@@ -545,9 +518,9 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
       at = an = mt = zero4();
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 kp = KL::frag32p(kb, 16 * p, lane, s);
-        const bf16x8 qp = KL::frag32p(sm.q[c & 1], 16 * p, lane, s);
-        const bf16x8 wp = HAS_W ? KL::frag32p(wb, 16 * p, lane, s) : kp;
+        const bf16x8 kp = KL::frag32(kb, fb, 16 * p, s);
+        const bf16x8 qp = KL::frag32(sm.q[c & 1], fb, 16 * p, s);
+        const bf16x8 wp = HAS_W ? KL::frag32(wb, fb, 16 * p, s) : kp;
         at = mfma32(wp, kp, at);  // lane: [j = 16p + 4 g4 + u][i = 16p + c16]
         mt = mfma32(wp, qp, mt);
         an = mfma32(kp, wp, an);  // lane: [i = 16p + 4 g4 + u][j = 16p + c16]
@@ -560,14 +533,35 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-          acc = mfma32(KL::frag32p(wb, 16 * bj, lane, s), KL::frag32p(xsrc, 16 * bi, lane, s), acc);
+          acc = mfma32(KL::frag32(wb, fb, 16 * bj, s), KL::frag32(xsrc, fb, 16 * bi, s), acc);
         off[k] = acc;
+      }
+    };
+
+    // ---------------- producers (REG): the column scales of chunk c, set by
+    // the lane of each token t = 16 p + (lane % 16) that holds the diagonal
+    // entry w_t . k_t of the raw product at (for KLA ||k_t||^2, exact: bf16
+    // products are exact in fp32); also kap_t = 2^(E_p - G_t) c_t
+    auto diag_gains = [&](int c, int n) __attribute__((always_inline)) {
+      if (g4 == (c16 >> 2)) {
+        const int u = c16 & 3, t = 16 * pw + c16;
+        const float nk = u == 0 ? at[0] : u == 1 ? at[1] : u == 2 ? at[2] : at[3];
+        // KLA step size eta / (||k||^2 + eps) (Kaczmarz Linear Attention §2.1),
+        // with the hardware reciprocal; GDN: eta; stored write vectors: 1
+        float cv = GAIN == GAIN_KLA ? p_etag * __builtin_amdgcn_rcpf(nk + a.g.eps)
+                 : GAIN == GAIN_GDN ? p_etag : 1.f;
+        cv = t < n ? cv : 0.f;
+        sm.cs[c & 1][t] = cv;
+        sm.kap[c & 1][t] = cv * exp2_hw(sm.g2[c & 1][16 * pw + 15] - sm.g2[c & 1][t]);
       }
     };
 
     // ---------------- producers: scale the raw tile products with the gains
     // in LDS (2^(G_i - G_j) c_j, masks), store M_pp and the off-diagonal -L
-    // and M tiles; at, an keep the scaled L_pp for the inverse
+    // and M tiles; at, an keep the scaled L_pp for the inverse.  Off the
+    // diagonal (j in block bj < bi) the factor is 2^(G_i - E_bj) kap_j with
+    // E_bj = G at the end of block bj: both factors are at most c_j, so
+    // neither overflows however strong the decay
     auto scale_tiles = [&](int c) __attribute__((always_inline)) {
       const int p = pw;
       const float* g2 = sm.g2[c & 1];
@@ -575,14 +569,14 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
       const float gd_i = g2[16 * p + c16], cd_i = cs[16 * p + c16];
       const f32x4 gd_j = *reinterpret_cast<const f32x4*>(&g2[16 * p + 4 * g4]);
       const f32x4 cd_j = *reinterpret_cast<const f32x4*>(&cs[16 * p + 4 * g4]);
-      float go_i[3];
-      f32x4 go_j[3], co_j[3];
+      float rho[3];
+      f32x4 ko_j[3];
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
         const int it = 3 * pw + k;
-        go_i[k] = g2[16 * item_bi(it) + c16];
-        go_j[k] = *reinterpret_cast<const f32x4*>(&g2[16 * item_bj(it) + 4 * g4]);
-        co_j[k] = *reinterpret_cast<const f32x4*>(&cs[16 * item_bj(it) + 4 * g4]);
+        const float sg = item_is_m(it) ? 1.f : -1.f;
+        rho[k] = sg * exp2_hw(g2[16 * item_bi(it) + c16] - g2[16 * item_bj(it) + 15]);
+        ko_j[k] = *reinterpret_cast<const f32x4*>(&sm.kap[c & 1][16 * item_bj(it) + 4 * g4]);
       }
       // diagonal block p: at = A^T (row i = 16p + c16, columns j = 16p + 4 g4 + u),
       // an = A (transposed roles), mt = M_pp like at
@@ -593,34 +587,38 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
         mt[u] = (4 * g4 + u <= c16) ? mt[u] * f : 0.f;
         an[u] = (c16 < 4 * g4 + u) ? an[u] * (exp2_hw(gd_j[u] - gd_i) * cd_i) : 0.f;
       }
-      *reinterpret_cast<u32x2*>(&sm.mp[(16 * p + c16) * PT + 16 * p + 4 * g4]) =
+      *reinterpret_cast<u32x2*>(&sm.mp[(16 * p + c16) * PT + mcol(16 * p + 4 * g4)]) =
           u32x2{pack_bf2(mt[0], mt[1]), pack_bf2(mt[2], mt[3])};
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
         const int it = 3 * pw + k;
         const bool m = item_is_m(it);
-        const float sg = m ? 1.f : -1.f;
         f32x4 val;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) val[u] = sg * off[k][u] * (exp2_hw(go_i[k] - go_j[k][u]) * co_j[k][u]);
-        uint16_t* dst = (m ? sm.mp : sm.ln) + (16 * item_bi(it) + c16) * PT + 16 * item_bj(it) + 4 * g4;
+        for (int u = 0; u < 4; ++u) val[u] = off[k][u] * (rho[k] * ko_j[k][u]);
+        const int jc = 16 * item_bj(it) + 4 * g4;
+        uint16_t* dst = (m ? sm.mp : sm.ln) + (16 * item_bi(it) + c16) * PT + (m ? mcol(jc) : jc);
         *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf2(val[0], val[1]), pack_bf2(val[2], val[3])};
       }
     };
     // ---------------- producers: (I + L_pp)^-1 from at = acc(A^T), an = acc(A),
     // A = L_pp strictly lower: (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8),
     // with prod_t(X, Y) = X^T Y; and the S-update scale f_j = 2^(G_n - G_j) c_j
+    // (I + Z)^T Y = Y + Z^T Y: each identity is the accumulator's start value
+    const int ud = c16 - 4 * g4;  // the slot of this lane's diagonal entry, if 0..3
+    const f32x4 idm = {ud == 0 ? 1.f : 0.f, ud == 1 ? 1.f : 0.f, ud == 2 ? 1.f : 0.f, ud == 3 ? 1.f : 0.f};
     auto invert = [&](int c) __attribute__((always_inline)) {
       if (pw == 1) sm.fs[lane] = sm.cs[c & 1][lane] * exp2_hw(sm.g2[c & 1][CH - 1] - sm.g2[c & 1][lane]);
       const Split sat = split(at), san = split(an);
-      const f32x4 A2 = prod_t(sat, san), A2t = prod_t(san, sat);
+      const f32x4 A2 = prod_t(sat, san, zero4()), A2t = prod_t(san, sat, zero4());
       const Split sA2 = split(A2), sA2t = split(A2t);
-      const f32x4 A4 = prod_t(sA2t, sA2), A4t = prod_t(sA2, sA2t);
+      const f32x4 A4 = prod_t(sA2t, sA2, zero4()), A4t = prod_t(sA2, sA2t, zero4());
       const Split sA4 = split(A4), sA4t = split(A4t);
-      const f32x4 A8 = prod_t(sA4t, sA4);
-      const f32x4 p1t = prod_t(split(add_identity(A2, g4, c16)), split(add_identity(-at, g4, c16)));
-      const f32x4 p2t = prod_t(split(add_identity(A4, g4, c16)), split(p1t));
-      const f32x4 tt_ = prod_t(split(add_identity(A8, g4, c16)), split(p2t));  // acc(T^T)
+      const f32x4 A8 = prod_t(sA4t, sA4, zero4());
+      const f32x4 imt = idm - at;                            // (I - A)^T
+      const f32x4 p1t = prod_t(sA2, split(imt), imt);        // ((I - A)(I + A^2))^T
+      const f32x4 p2t = prod_t(sA4, split(p1t), p1t);        // ... (I + A^4)
+      const f32x4 tt_ = prod_t(split(A8), split(p2t), p2t);  // acc(T^T)
       // lane holds T[c16][4 g4 + u]: row c16 of block p
       *reinterpret_cast<u32x2*>(&sm.tb[(16 * pw + c16) * P16 + 4 * g4]) =
           u32x2{pack_bf2(tt_[0], tt_[1]), pack_bf2(tt_[2], tt_[3])};
@@ -636,11 +634,9 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
         stash_k(0, min(CH, T));
         stash_q(0);
         stash_v();
-        if (nchunks > 1) {
-          fetch_k(1);
-          fetch_q(1);
-          fetch_v(1);
-        }
+        fetch_k(1);
+        fetch_q(1);
+        fetch_v(1);
       }
     }
     __syncthreads();
@@ -648,16 +644,17 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
       if (nchunks > 0) {
         if constexpr (REG) {
           tiles(0);
-          scale_tiles(0);
+          diag_gains(0, min(CH, T));
         } else {
           gains1(0);
         }
       }
     }
-    if constexpr (PG) {
-      __syncthreads();
-      if constexpr (!CONS) {
-        if (nchunks > 0) gains2(0);
+    __syncthreads();
+    if constexpr (!CONS) {
+      if (nchunks > 0) {
+        if constexpr (REG) scale_tiles(0);
+        else gains2(0);
       }
     }
     __syncthreads();
@@ -677,13 +674,35 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
         bf16x8 Spk[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) Spk[s] = cat8(pack16(S[2 * s]), pack16(S[2 * s + 1]));
+        // K and Q fragments of row tile rt + 1 are read while rt multiplies
+        bf16x8 kf[KS], qf[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          kf[s] = KL::frag32(kb, fb, 0, s);
+          qf[s] = KL::frag32(sm.q[c & 1], fb, 0, s);
+        }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
+          bf16x8 kn[KS], qn[KS];
+          if (rt < 3) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+              kn[s] = KL::frag32(kb, fb, 16 * (rt + 1), s);
+              qn[s] = KL::frag32(sm.q[c & 1], fb, 16 * (rt + 1), s);
+            }
+          }
           f32x4 ak = zero4(), aq = zero4();
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
-            ak = mfma32(KL::frag32p(kb, 16 * rt, lane, s), Spk[s], ak);
-            aq = mfma32(Spk[s], KL::frag32p(sm.q[c & 1], 16 * rt, lane, s), aq);
+            ak = mfma32(kf[s], Spk[s], ak);
+            aq = mfma32(Spk[s], qf[s], aq);
+          }
+          if (rt < 3) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+              kf[s] = kn[s];
+              qf[s] = qn[s];
+            }
           }
           // R[t][c] = V[t][c] - g_t (K S)[t][c], rows t = 16 rt + 4 g4 + i
           const f32x4 vv = unpack16(read_tr(sm.v, PV, lane, 16 * rt, 16 * ct));
@@ -701,14 +720,14 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
         invert(c);
         // REG: gains of chunk c + 1 from its staged registers; its k and q to
         // LDS; the loads of k and q of chunk c + 2
-        if (REG && c + 1 < nchunks) {
-          regains(c + 1, n1);
-          stash_k(c + 1, n1);
-          stash_q(c + 1);
-          if (c + 2 < nchunks) {
-            fetch_k(c + 2);
-            fetch_q(c + 2);
+        if constexpr (REG) {
+          if (c + 1 < nchunks) {
+            regains(c + 1, n1);
+            stash_k(c + 1, n1);
+            stash_q(c + 1);
           }
+          fetch_k(c + 2);
+          fetch_q(c + 2);
         }
       }
       __syncthreads();  // (1) L, M, (I + L_bb)^-1, f of chunk c ready
@@ -736,8 +755,9 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
         const auto ro = rsrc(static_cast<uint16_t*>(a.o) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          f32x4 o = mfma32(U0, frag32p(sm.mp + 16 * rt * PT, PT, lane, 0), OQ[rt]);
-          if (rt >= 2) o = mfma32(U1, frag32p(sm.mp + 16 * rt * PT, PT, lane, 1), o);
+          const uint16_t* mrow = sm.mp + (16 * rt + c16) * PT + 8 * g4;
+          f32x4 o = mfma32(U0, __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(mrow)), OQ[rt]);
+          if (rt >= 2) o = mfma32(U1, __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(mrow + 32)), o);
           __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])}, ro,
                                                 ooff[rt], 0, 0);
         }
@@ -748,9 +768,12 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
             stash_q(c + 1);
           }
           stash_v();
-          if constexpr (REG) {
-            if (c + 2 < nchunks) fetch_v(c + 2);
+        }
+        if constexpr (REG) {
+          fetch_v(c + 2);
+          if (c + 1 < nchunks) {
             tiles(c + 1);  // raw products, scaled in P3
+            diag_gains(c + 1, n1);
           }
         }
       }
@@ -764,7 +787,8 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
           f32x4 acc = S[dt] * gn;
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            const bf16x8 wa = cat8(KL::read_tr(wb, 32 * s, 16 * dt, lane), KL::read_tr(wb, 32 * s + 16, 16 * dt, lane));
+            const bf16x8 wa = cat8(KL::read_tr(wb, trb, 32 * s, dt >> 1, dt & 1),
+                                   KL::read_tr(wb, trb, 32 * s + 16, dt >> 1, dt & 1));
             acc = mfma32(wa, s == 0 ? F0 : F1, acc);
           }
           S[dt] = acc;
@@ -778,11 +802,9 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
         if constexpr (REG) {
           if (c + 1 < nchunks) scale_tiles(c + 1);
         } else {
-          if (c + 2 < nchunks) {
-            fetch_k(c + 2);
-            fetch_q(c + 2);
-            fetch_v(c + 2);
-          }
+          fetch_k(c + 2);
+          fetch_q(c + 2);
+          fetch_v(c + 2);
           if (c + 1 < nchunks) gains1(c + 1);
           __syncthreads();  // (3a)
           if (c + 1 < nchunks) gains2(c + 1);
@@ -798,7 +820,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) base[(16 * dt + i) * a.dv] = S[dt][i];
+          for (int i = 0; i < 4; ++i) base[(KL::sigma_channel(dt, 0, i)) * a.dv] = S[dt][i];
       }
     } else {
       if (PG && a.aux_final && slice == 0 && ptid < DK)
