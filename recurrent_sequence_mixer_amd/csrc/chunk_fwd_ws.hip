@@ -14,22 +14,26 @@
 //   consumers (waves 0..3): wave ct owns value columns 16 ct .. 16 ct + 15 and
 //     keeps the whole d_k x 16 slice of S in registers.  Per chunk it forms
 //     K S and (Q S)^T, runs the blocked triangular solve, adds M U, writes the
-//     output tile and updates S.
+//     output tile and updates S; the consumers also move q and v
+//     HBM -> registers -> LDS.
 //   producers (waves 4..7): build the chunk-local operands (the L and M
 //     tiles, the inverses of the diagonal blocks of I + L, the gains) and move
-//     the inputs HBM -> registers -> LDS.
+//     k (w) and the gates HBM -> registers -> LDS.
 // Per chunk c, three phases separated by workgroup barriers:
-//   P1  consumers: K S -> R = V - g K S, and (Q S)^T.
-//       producers: (I + L_bb)^-1 of c; the decay of chunk c + 1 from its
-//       staging registers, its k and q into LDS, their loads for c + 2.
-//   P2  consumers: solve -> U; O = g Q S + M U -> HBM.
-//       producers: v of chunk c + 1 into LDS and its loads for c + 2; the
-//       raw L and M tile products of chunk c + 1, and its column scales
-//       (the key norms of KLA are the diagonal of the raw K K^T).
+//   P1  consumers: K S -> R = V - g K S, and (Q S)^T; q of chunk c + 1 into
+//       LDS and its loads for c + 2.
+//       producers: the decay of chunk c + 1 from its staging registers, its
+//       k into LDS and its loads for c + 2; the off-diagonal L and M tiles
+//       of c and (I + L_bb)^-1 of c.
+//   P2  consumers: solve -> U; O = g Q S + M U -> HBM; v of chunk c + 1
+//       into LDS and its loads for c + 2.
+//       producers: the raw L and M tile products of chunk c + 1, and its
+//       column scales (the key norms of KLA are the diagonal of the raw
+//       K K^T).
 //   P3  consumers: S = g_n S + W^T diag(f) U.
-//       producers: scale and store the L and M tiles of chunk c + 1.
+//       producers: scale the diagonal L and M blocks of chunk c + 1.
 // PGDN, whose write vectors come out of a statistic scan over the LDS copy
-// of k, stages chunk c + 1 in P2, scans in P3 (split around the scan's
+// of k, stages k of chunk c + 1 in P2, scans in P3 (split around the scan's
 // synchronisation) and forms its tiles in P1.  Every load has a whole chunk
 // step to arrive.  k, q, w and the gains are double buffered by chunk parity;
 // every other LDS buffer is single: it is rewritten only after its last
@@ -215,10 +219,19 @@ __device__ __forceinline__ int mcol(int j) {
   return (j & ~31) + 4 * (2 * (gr & 3) + (gr >> 2)) + (j & 3);
 }
 
-template <bool B>
+// wavefront roles: 0 consumer, 1 producer, 2 loader
+template <int R>
 struct Role {
-  static constexpr bool consumer = B;
+  static constexpr int role = R;
 };
+// Scalar-decay gains with stored or register-formed gains (all but PGDN) run
+// twelve wavefronts, three per SIMD: loaders (waves 8..11) issue every load
+// and stage it into LDS, so that no consumer or producer ever waits on the
+// memory pipeline.  PGDN, whose statistic scan needs more registers than a
+// third wavefront per SIMD leaves, runs eight: its producers load k and the
+// gates and its consumers q and v.
+__host__ __device__ constexpr bool ws_loaders(int gain) { return gain != GAIN_PGDN; }
+__host__ __device__ constexpr int ws_threads(int gain) { return ws_loaders(gain) ? 768 : 512; }
 
 template <int DK, int GAIN>
 struct Smem {
@@ -239,6 +252,8 @@ struct Smem {
   alignas(16) float cs[2][CH];                  // column scale c_j, by chunk parity
   alignas(16) float kap[2][CH];                 // 2^(E_b(j) - G_j) c_j, E_b = G at the end of j's block
   alignas(16) float fs[CH];                     // S-update scale f_j
+  alignas(16) float galpha[2][CH];              // staged alpha, eta by chunk parity (loaders)
+  alignas(16) float geta[2][CH];
   float eta[CH], alpha[CH], ap[CH], bp[CH];     // per-token gates
   alignas(16) float ah[4 * DK];                 // PGDN: statistic at the segment ends
   alignas(16) float acarry[DK];                 // PGDN: statistic carried between chunks
@@ -246,8 +261,9 @@ struct Smem {
 };
 
 template <int DK, int GAIN>
-__global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
-  constexpr int NT = 512;               // threads
+__global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArgs a) {
+  constexpr bool LOADERS = ws_loaders(GAIN);
+  constexpr int NT = ws_threads(GAIN);  // threads
   constexpr int NP = 256;               // producer threads
   constexpr int NDT = DK / 16;          // state tiles of a consumer
   constexpr int KS = DK / 32;           // k-blocks of a d_k contraction
@@ -307,10 +323,13 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
   }
 
   auto run = [&](auto role) __attribute__((always_inline)) {
-    constexpr bool CONS = decltype(role)::consumer;
+    constexpr int RO = decltype(role)::role;
+    constexpr bool CONS = RO == 0, PROD = RO == 1, LOAD = RO == 2;
     const int ct = wave;           // consumers: column tile
     const int pw = wave - 4;       // producers: wavefront index
     const int ptid = tid - 256;    // producers: thread index
+    // the role's own thread index (its share of the staging)
+    const int ltid = tid - 256 * RO;
     const int fb = KL::frag_base(lane), trb = KL::tr_base(lane);  // LDS operand bases
 
     // consumers: byte offsets of the output pieces (token 16 rt + c16, value
@@ -334,7 +353,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) S[dt] = zero4();
       }
-    } else {
+    } else if constexpr (PROD) {
       if (PG && ptid < DK) sm.acarry[ptid] = a.aux0 ? a.aux0[static_cast<long>(bh) * DK + ptid] : 1.f;
     }
 
@@ -342,19 +361,17 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
     // of k / q / w in consecutive lanes (coalesced), likewise for v
     u32x4 pk[KV_LOADS], pq[KV_LOADS], pwv[GAIN == GAIN_EXPLICIT ? KV_LOADS : 1], pv[V_LOADS];
     float p_eta = 0.f, p_alpha = 1.f, p_ap = 1.f, p_bp = 0.f;
-    float p_etad = 0.f;  // eta of token 16 pw + lane % 16 (REG: its diagonal lane sets the gain)
-    float p_etag = 0.f;  // the same for the chunk whose gains are being formed (the next
-                         // fetch overwrites p_etad before its diagonal is known)
+    float l_alpha = 1.f, l_eta = 0.f;  // loaders: alpha, eta of token ltid of a chunk
     float pg_start = 0.f;  // PGDN: carried statistic read by pass 1 (segment 0)
 
     // per-lane byte offsets inside a chunk: the k / q / w pieces (row-major
     // [CH][DK]) and the value pieces (row t, columns col0 + cc of [T][dv])
     int koff[KV_LOADS], voff[V_LOADS];
 #pragma unroll
-    for (int j = 0; j < KV_LOADS; ++j) koff[j] = 2 * (ptid + j * NP) * VEC;
+    for (int j = 0; j < KV_LOADS; ++j) koff[j] = 2 * (ltid + j * NP) * VEC;
 #pragma unroll
     for (int j = 0; j < V_LOADS; ++j) {
-      const int e = (ptid + j * NP) * VEC;
+      const int e = (ltid + j * NP) * VEC;
       voff[j] = 2 * ((e / BV) * a.dv + col0 + e % BV);
     }
     // loads of chunk c through buffer resources that end at its last token:
@@ -376,12 +393,10 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
           pwv[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, koff[j], 0, 0);
         }
       }
-      if constexpr (REG && HAS_ETA)
-        p_etad = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.eta + tok, 4 * n), 4 * (16 * pw + c16), 0, 0));
-      // per-token gates: lanes ptid >= n (all of waves 5..7) read zeros
-      p_alpha = __uint_as_float(
-          __builtin_amdgcn_raw_buffer_load_b32(rsrc(static_cast<const float*>(a.g.alpha) + tok, 4 * n), 4 * ptid, 0, 0));
+      // PGDN per-token gates: lanes ptid >= n (all of waves 5..7) read zeros
       if constexpr (PG) {
+        p_alpha = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rsrc(static_cast<const float*>(a.g.alpha) + tok, 4 * n), 4 * ptid, 0, 0));
         p_eta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.eta + tok, 4 * n), 4 * ptid, 0, 0));
         p_ap = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.alphaP + tok, 4 * n), 4 * ptid, 0, 0));
         p_bp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.betaP + tok, 4 * n), 4 * ptid, 0, 0));
@@ -406,14 +421,14 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
     auto stash_q = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < KV_LOADS; ++j) {
-        const int e = (ptid + j * NP) * VEC;
+        const int e = (ltid + j * NP) * VEC;
         *reinterpret_cast<u32x4*>(&sm.q[c & 1][KL::idx(e / DK, e % DK)]) = pq[j];
       }
     };
     auto stash_v = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < V_LOADS; ++j) {
-        const int e = (ptid + j * NP) * VEC;
+        const int e = (ltid + j * NP) * VEC;
         *reinterpret_cast<u32x4*>(&sm.v[(e / BV) * PV + e % BV]) = pv[j];
       }
     };
@@ -421,7 +436,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
       uint16_t* kb = sm.k[c & 1];
 #pragma unroll
       for (int j = 0; j < KV_LOADS; ++j) {
-        const int e = (ptid + j * NP) * VEC;
+        const int e = (ltid + j * NP) * VEC;
         const int t = e / DK, d = e % DK;
         *reinterpret_cast<u32x4*>(&kb[KL::idx(t, d)]) = pk[j];
         if constexpr (GAIN == GAIN_EXPLICIT) *reinterpret_cast<u32x4*>(&sm.w[c & 1][KL::idx(t, d)]) = pwv[j];
@@ -435,12 +450,29 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
       }
     };
 
+    // ---------------- loaders (REG): per-token gates of chunk c (the first
+    // loader wavefront, token = lane) into registers, then into LDS
+    auto fetch_gates = [&](int c) __attribute__((always_inline)) {
+      const int t0 = c * CH;
+      const int n = max(0, min(CH, T - t0));
+      const long tok = static_cast<long>(bh) * T + t0;
+      l_alpha = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rsrc(static_cast<const float*>(a.g.alpha) + tok, 4 * n), 4 * ltid, 0, 0));
+      if constexpr (HAS_ETA)
+        l_eta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.eta + tok, 4 * n), 4 * ltid, 0, 0));
+    };
+    auto stash_gates = [&](int c) __attribute__((always_inline)) {
+      if (ltid < CH) {
+        sm.galpha[c & 1][ltid] = l_alpha;
+        sm.geta[c & 1][ltid] = l_eta;
+      }
+    };
+
     // ---------------- producers (REG): cumulative decay of chunk c of n tokens
-    // from the staging registers (wavefront 0 holds the alpha of token = lane)
+    // (wavefront 0, token = lane; alpha past the end counts as 1)
     auto regains = [&](int c, int n) __attribute__((always_inline)) {
-      p_etag = p_etad;
       if (pw == 0) {
-        const float x = wave_prefix_sum(log2_hw(lane < n ? p_alpha : 1.f));
+        const float x = wave_prefix_sum(log2_hw(lane < n ? sm.galpha[c & 1][lane] : 1.f));
         sm.g2[c & 1][lane] = x;
         sm.gam[c & 1][lane] = exp2_hw(x);
       }
@@ -548,8 +580,9 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
         const float nk = u == 0 ? at[0] : u == 1 ? at[1] : u == 2 ? at[2] : at[3];
         // KLA step size eta / (||k||^2 + eps) (Kaczmarz Linear Attention §2.1),
         // with the hardware reciprocal; GDN: eta; stored write vectors: 1
-        float cv = GAIN == GAIN_KLA ? p_etag * __builtin_amdgcn_rcpf(nk + a.g.eps)
-                 : GAIN == GAIN_GDN ? p_etag : 1.f;
+        const float et = sm.geta[c & 1][t];
+        float cv = GAIN == GAIN_KLA ? et * __builtin_amdgcn_rcpf(nk + a.g.eps)
+                 : GAIN == GAIN_GDN ? et : 1.f;
         cv = t < n ? cv : 0.f;
         sm.cs[c & 1][t] = cv;
         sm.kap[c & 1][t] = cv * exp2_hw(sm.g2[c & 1][16 * pw + 15] - sm.g2[c & 1][t]);
@@ -562,22 +595,15 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
     // diagonal (j in block bj < bi) the factor is 2^(G_i - E_bj) kap_j with
     // E_bj = G at the end of block bj: both factors are at most c_j, so
     // neither overflows however strong the decay
-    auto scale_tiles = [&](int c) __attribute__((always_inline)) {
+    // diagonal block (scale_diag) and off-diagonal tiles (scale_off): the
+    // inverse needs the first, the consumers' solve and M U the second
+    auto scale_diag = [&](int c) __attribute__((always_inline)) {
       const int p = pw;
       const float* g2 = sm.g2[c & 1];
       const float* cs = sm.cs[c & 1];
       const float gd_i = g2[16 * p + c16], cd_i = cs[16 * p + c16];
       const f32x4 gd_j = *reinterpret_cast<const f32x4*>(&g2[16 * p + 4 * g4]);
       const f32x4 cd_j = *reinterpret_cast<const f32x4*>(&cs[16 * p + 4 * g4]);
-      float rho[3];
-      f32x4 ko_j[3];
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const int it = 3 * pw + k;
-        const float sg = item_is_m(it) ? 1.f : -1.f;
-        rho[k] = sg * exp2_hw(g2[16 * item_bi(it) + c16] - g2[16 * item_bj(it) + 15]);
-        ko_j[k] = *reinterpret_cast<const f32x4*>(&sm.kap[c & 1][16 * item_bj(it) + 4 * g4]);
-      }
       // diagonal block p: at = A^T (row i = 16p + c16, columns j = 16p + 4 g4 + u),
       // an = A (transposed roles), mt = M_pp like at
 #pragma unroll
@@ -589,6 +615,18 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
       }
       *reinterpret_cast<u32x2*>(&sm.mp[(16 * p + c16) * PT + mcol(16 * p + 4 * g4)]) =
           u32x2{pack_bf2(mt[0], mt[1]), pack_bf2(mt[2], mt[3])};
+    };
+    auto scale_off = [&](int c) __attribute__((always_inline)) {
+      const float* g2 = sm.g2[c & 1];
+      float rho[3];
+      f32x4 ko_j[3];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int it = 3 * pw + k;
+        const float sg = item_is_m(it) ? 1.f : -1.f;
+        rho[k] = sg * exp2_hw(g2[16 * item_bi(it) + c16] - g2[16 * item_bj(it) + 15]);
+        ko_j[k] = *reinterpret_cast<const f32x4*>(&sm.kap[c & 1][16 * item_bj(it) + 4 * g4]);
+      }
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
         const int it = 3 * pw + k;
@@ -625,22 +663,45 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
     };
 
     // ---------------- prologue: chunk 0 staged, its gains (and, REG, tiles)
-    if constexpr (!CONS) {
-      if (nchunks > 0) {
+    if (nchunks > 0) {
+      if constexpr (LOADERS) {
+        // chunk 0 and the gates of chunk 1 into LDS; the loads the loop
+        // stages first (k, q, v of chunk 1, the gates of chunk 2)
+        if constexpr (LOAD) {
+          fetch_k(0);
+          fetch_q(0);
+          fetch_v(0);
+          fetch_gates(0);
+          stash_k(0, min(CH, T));
+          stash_q(0);
+          stash_v();
+          stash_gates(0);
+          fetch_gates(1);
+          stash_gates(1);
+          fetch_k(1);
+          fetch_q(1);
+          fetch_v(1);
+          fetch_gates(2);
+        }
+      } else if constexpr (PROD) {
         fetch_k(0);
+        stash_k(0, min(CH, T));
+        fetch_k(1);
+      } else if constexpr (CONS) {
         fetch_q(0);
         fetch_v(0);
-        if constexpr (REG) regains(0, min(CH, T));
-        stash_k(0, min(CH, T));
         stash_q(0);
         stash_v();
-        fetch_k(1);
         fetch_q(1);
         fetch_v(1);
       }
     }
     __syncthreads();
-    if constexpr (!CONS) {
+    if constexpr (REG) {
+      if (PROD && nchunks > 0) regains(0, min(CH, T));
+      __syncthreads();
+    }
+    if constexpr (PROD) {
       if (nchunks > 0) {
         if constexpr (REG) {
           tiles(0);
@@ -651,9 +712,9 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
-    if constexpr (!CONS) {
+    if constexpr (PROD) {
       if (nchunks > 0) {
-        if constexpr (REG) scale_tiles(0);
+        if constexpr (REG) scale_diag(0);
         else gains2(0);
       }
     }
@@ -712,23 +773,28 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
           OQ[rt] = aq * sm.gam[c & 1][16 * rt + c16];
         }
         gn = sm.gam[c & 1][CH - 1];
+        // PGDN: q of chunk c + 1 into LDS (its parity's last readers are done)
+        if constexpr (!LOADERS) {
+          if (c + 1 < nchunks) stash_q(c + 1);
+        }
+      } else if constexpr (LOAD) {
+        // k, q of chunk c + 1 into LDS; the loads of k of chunk c + 2
+        if (c + 1 < nchunks) {
+          stash_k(c + 1, n1);
+          stash_q(c + 1);
+        }
+        fetch_k(c + 2);
       } else {
         if constexpr (!REG) {
           tiles(c);
-          scale_tiles(c);
+          scale_diag(c);
         }
-        invert(c);
-        // REG: gains of chunk c + 1 from its staged registers; its k and q to
-        // LDS; the loads of k and q of chunk c + 2
+        // REG: the decay of chunk c + 1 from its staged gates
         if constexpr (REG) {
-          if (c + 1 < nchunks) {
-            regains(c + 1, n1);
-            stash_k(c + 1, n1);
-            stash_q(c + 1);
-          }
-          fetch_k(c + 2);
-          fetch_q(c + 2);
+          if (c + 1 < nchunks) regains(c + 1, n1);
         }
+        scale_off(c);
+        invert(c);
       }
       __syncthreads();  // (1) L, M, (I + L_bb)^-1, f of chunk c ready
 
@@ -761,16 +827,23 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
           __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])}, ro,
                                                 ooff[rt], 0, 0);
         }
+        // PGDN: v of chunk c + 1 into LDS (chunk c's was last read in P1),
+        // the loads of q and v of chunk c + 2 (the loads of k go out in P3)
+        if constexpr (!LOADERS) {
+          if (c + 1 < nchunks) stash_v();
+          fetch_q(c + 2);
+          fetch_v(c + 2);
+        }
+      } else if constexpr (LOAD) {
+        // v of chunk c + 1 into LDS (chunk c's was last read in P1); the
+        // loads of q of chunk c + 2
+        if (c + 1 < nchunks) stash_v();
+        fetch_q(c + 2);
       } else {
-        if (c + 1 < nchunks) {
-          if constexpr (!REG) {
-            stash_k(c + 1, n1);
-            stash_q(c + 1);
-          }
-          stash_v();
+        if constexpr (!REG) {
+          if (c + 1 < nchunks) stash_k(c + 1, n1);
         }
         if constexpr (REG) {
-          fetch_v(c + 2);
           if (c + 1 < nchunks) {
             tiles(c + 1);  // raw products, scaled in P3
             diag_gains(c + 1, n1);
@@ -798,13 +871,18 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
         if constexpr (PG) __syncthreads();  // (3a) PGDN statistic pass 1 done
 #pragma unroll
         for (int dt = NDT / 2; dt < NDT; ++dt) update(dt);
+      } else if constexpr (LOAD) {
+        // the gates of chunk c + 2 into LDS (their parity's last readers,
+        // regains and diag_gains of chunk c, are done); the loads of v of
+        // chunk c + 2 and of the gates of chunk c + 3
+        stash_gates(c + 2);
+        fetch_v(c + 2);
+        fetch_gates(c + 3);
       } else {
         if constexpr (REG) {
-          if (c + 1 < nchunks) scale_tiles(c + 1);
+          if (c + 1 < nchunks) scale_diag(c + 1);
         } else {
           fetch_k(c + 2);
-          fetch_q(c + 2);
-          fetch_v(c + 2);
           if (c + 1 < nchunks) gains1(c + 1);
           __syncthreads();  // (3a)
           if (c + 1 < nchunks) gains2(c + 1);
@@ -822,13 +900,18 @@ __global__ __launch_bounds__(512) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) base[(KL::sigma_channel(dt, 0, i)) * a.dv] = S[dt][i];
       }
-    } else {
+    } else if constexpr (PROD) {
       if (PG && a.aux_final && slice == 0 && ptid < DK)
         a.aux_final[static_cast<long>(bh) * DK + ptid] = sm.acarry[ptid];
     }
   };
-  if (wave < 4) run(Role<true>{});
-  else run(Role<false>{});
+  if (wave < 4) {
+    run(Role<0>{});
+  } else if (wave < 8) {
+    run(Role<1>{});
+  } else {
+    if constexpr (LOADERS) run(Role<2>{});
+  }
 }
 
 }  // namespace ws
@@ -843,7 +926,7 @@ static hipError_t launch_ws_one(const ChunkArgs& a, hipStream_t st) {
                                        static_cast<int>(sizeof(Sm)));
   if (err != hipSuccess) return err;
   dim3 grid(static_cast<unsigned>((a.dv / ws::BV) * a.B * a.H));
-  hipLaunchKernelGGL(kern, grid, dim3(512), sizeof(Sm), st, a);
+  hipLaunchKernelGGL(kern, grid, dim3(ws::ws_threads(GAIN)), sizeof(Sm), st, a);
   return hipGetLastError();
 }
 
