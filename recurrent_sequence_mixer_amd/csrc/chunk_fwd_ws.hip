@@ -227,7 +227,10 @@ struct Role {
 // Scalar-decay gains with stored or register-formed gains (all but PGDN) run
 // twelve wavefronts, three per SIMD: loaders (waves 8..11) issue every load
 // and stage it into LDS, so that no consumer or producer ever waits on the
-// memory pipeline.  PGDN, whose statistic scan needs more registers than a
+// memory pipeline (which backs up when all CUs ask for their next chunk at
+// once).  Per chunk c the loaders stage k, q of c + 1 and load k and the gates
+// of c + 2 in P1, stage v of c + 1 and load q, v of c + 2 in P2, and stage the
+// gates of c + 2 in P3.  PGDN, whose statistic scan needs more registers than a
 // third wavefront per SIMD leaves, runs eight: its producers load k and the
 // gates and its consumers q and v.
 __host__ __device__ constexpr bool ws_loaders(int gain) { return gain != GAIN_PGDN; }
@@ -666,7 +669,7 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
     if (nchunks > 0) {
       if constexpr (LOADERS) {
         // chunk 0 and the gates of chunk 1 into LDS; the loads the loop
-        // stages first (k, q, v of chunk 1, the gates of chunk 2)
+        // stages first (k, q, v of chunk 1)
         if constexpr (LOAD) {
           fetch_k(0);
           fetch_q(0);
@@ -681,7 +684,6 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
           fetch_k(1);
           fetch_q(1);
           fetch_v(1);
-          fetch_gates(2);
         }
       } else if constexpr (PROD) {
         fetch_k(0);
@@ -778,12 +780,14 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
           if (c + 1 < nchunks) stash_q(c + 1);
         }
       } else if constexpr (LOAD) {
-        // k, q of chunk c + 1 into LDS; the loads of k of chunk c + 2
+        // k, q of chunk c + 1 into LDS; the loads of k and of the gates of
+        // chunk c + 2
         if (c + 1 < nchunks) {
           stash_k(c + 1, n1);
           stash_q(c + 1);
         }
         fetch_k(c + 2);
+        fetch_gates(c + 2);
       } else {
         if constexpr (!REG) {
           tiles(c);
@@ -836,9 +840,10 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
         }
       } else if constexpr (LOAD) {
         // v of chunk c + 1 into LDS (chunk c's was last read in P1); the
-        // loads of q of chunk c + 2
+        // loads of q and v of chunk c + 2
         if (c + 1 < nchunks) stash_v();
         fetch_q(c + 2);
+        fetch_v(c + 2);
       } else {
         if constexpr (!REG) {
           if (c + 1 < nchunks) stash_k(c + 1, n1);
@@ -873,11 +878,8 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
         for (int dt = NDT / 2; dt < NDT; ++dt) update(dt);
       } else if constexpr (LOAD) {
         // the gates of chunk c + 2 into LDS (their parity's last readers,
-        // regains and diag_gains of chunk c, are done); the loads of v of
-        // chunk c + 2 and of the gates of chunk c + 3
+        // regains and diag_gains of chunk c, are done)
         stash_gates(c + 2);
-        fetch_v(c + 2);
-        fetch_gates(c + 3);
       } else {
         if constexpr (REG) {
           if (c + 1 < nchunks) scale_diag(c + 1);
