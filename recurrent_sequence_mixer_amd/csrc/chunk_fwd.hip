@@ -114,6 +114,20 @@ __device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// Four consecutive rows r0 .. r0 + 3 of column cb + lane of a row-major bf16
+// tile of pitch ld, as fp32, in one ds_read_b64_tr_b16: within each group of
+// 16 lanes, lane l receives element l % 4 of the 8-byte piece addressed by
+// lane 4 j + l / 4, so lane 4 j + q addresses row r0 + j, columns
+// cb + 16 g + 4 q .. +3 (g = lane / 16) and every lane gets its own column.
+typedef short s16x4_lds __attribute__((ext_vector_type(4), address_space(3)));
+__device__ __forceinline__ f32x4 col4(const uint16_t* base, int ld, int r0, int cb, int lane) {
+  const int a = lane & 15;
+  const uint16_t* p = base + (r0 + (a >> 2)) * ld + cb + 16 * (lane >> 4) + 4 * (a & 3);
+  const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds*)p));
+  return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u),
+               __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xFFFF0000u)};
+}
+
 template <typename E> struct Pad;
 template <> struct Pad<uint16_t> { static constexpr int v = 8; };
 template <> struct Pad<float> { static constexpr int v = 4; };
@@ -162,6 +176,10 @@ void chunk_fwd_kernel(ChunkArgs a) {
   // over 2 DK threads and the transcendental work is spread over all of them
   constexpr bool PG2 = GAIN == GAIN_PGDN && !CHANNEL && NT >= 2 * DK;
   constexpr bool SCAN = CHANNEL || (GAIN == GAIN_PGDN && !PG2) || GAIN == GAIN_KDN;
+  // bf16 KDN with channel decay, one key channel per thread: the scans, the
+  // z sums and the operand rescaling read four tokens of a channel per
+  // transposing LDS read (col4) instead of one element at a time
+  constexpr bool FASTCD = BF16 && CHANNEL && GAIN == GAIN_KDN && DK <= NT && DK % 64 == 0;
   using Sm = ChunkSmem<E, DK, BV, HAS_W>;
   constexpr int PK = Sm::PK, PT = Sm::PT, P16 = Sm::P16;
   constexpr int VEC = 16 / sizeof(E);            // elements per 16-byte access
@@ -471,6 +489,28 @@ void chunk_fwd_kernel(ChunkArgs a) {
         __syncthreads();
       }
       const float mu = GAIN == GAIN_PGDN ? a.g.mu_log[h] : 0.f;
+      if constexpr (FASTCD) {
+        if (tid < DK) {  // wavefronts 0 .. DK / 64 - 1, channel = tid
+          const int cb = 64 * wave;
+          float G = 0.f, st = aux[0];
+#pragma unroll
+          for (int t4 = 0; t4 < CH; t4 += 4) {
+            const f32x4 al = col4(reinterpret_cast<const uint16_t*>(s_al), DK, t4, cb, lane);
+            const f32x4 om = col4(reinterpret_cast<const uint16_t*>(s_om), DK, t4, cb, lane);
+            const f32x4 kk = col4(reinterpret_cast<const uint16_t*>(sm.k), PK, t4, cb, lane);
+            const f32x4 mr = *reinterpret_cast<const f32x4*>(&sm.mur[t4]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              G += fast_log2(al[j]);
+              gch[0][t4 + j] = G;
+              const float ph = kdn_predict(al[j], st, om[j]);
+              pkr[0][t4 + j] = ph * kk[j];
+              st = kdn_update(ph, kk[j], mr[j]);
+            }
+          }
+          aux[0] = st;
+        }
+      } else
 #pragma unroll
       for (int cc = 0; cc < CPT; ++cc) {
         const int d = tid + cc * NT;
@@ -503,6 +543,19 @@ void chunk_fwd_kernel(ChunkArgs a) {
         // gets token t), combined over the wavefronts in a fixed order
         static_assert(CH == 64, "one token per lane");
         float zt[CH];
+        if constexpr (FASTCD) {
+          if (tid < DK) {
+#pragma unroll
+            for (int t4 = 0; t4 < CH; t4 += 4) {
+              const f32x4 kk = col4(reinterpret_cast<const uint16_t*>(sm.k), PK, t4, 64 * wave, lane);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) zt[t4 + j] = pkr[0][t4 + j] * kk[j];
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < CH; ++t) zt[t] = 0.f;
+          }
+        } else
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
           float z = 0.f;
@@ -577,6 +630,33 @@ void chunk_fwd_kernel(ChunkArgs a) {
       }
     } else {
       // channel decay: rescale k, q in place to the chunk midpoint, build wchk and Wtil^T
+      if constexpr (FASTCD) {
+        if (tid < DK) {
+          const int d = tid, cb = 64 * wave;
+          const float gm = gch[0][CH / 2 - 1], gl = gch[0][CH - 1];
+          sm.gmid[d] = fast_exp2(gm);
+          sm.gn[d] = fast_exp2(gl);
+          const float fl = fast_exp2(gl - gm);  // 2^(Gn - Gmid)
+#pragma unroll
+          for (int t4 = 0; t4 < CH; t4 += 4) {
+            const f32x4 kk = col4(reinterpret_cast<const uint16_t*>(sm.k), PK, t4, cb, lane);
+            const f32x4 qq = col4(reinterpret_cast<const uint16_t*>(sm.q), PK, t4, cb, lane);
+            const f32x4 rd = *reinterpret_cast<const f32x4*>(&sm.red[t4]);
+            float wtv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int t = t4 + j;
+              const float up = fast_exp2(gch[0][t] - gm), down = fast_exp2(gm - gch[0][t]);
+              const float wv = pkr[0][t] * rd[j];
+              sm.k[t * PK + d] = EL::put(up * kk[j]);
+              sm.q[t * PK + d] = EL::put(up * qq[j]);
+              sm.w[t * PK + d] = EL::put(down * wv);
+              wtv[j] = fl * down * wv;  // 2^(Gn - G_t) w_t
+            }
+            *reinterpret_cast<u32x2*>(&sm.wt[d * PT + t4]) = u32x2{pack_bf2(wtv[0], wtv[1]), pack_bf2(wtv[2], wtv[3])};
+          }
+        }
+      } else
 #pragma unroll
       for (int cc = 0; cc < CPT; ++cc) {
         const int d = tid + cc * NT;
