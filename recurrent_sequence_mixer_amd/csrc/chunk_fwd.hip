@@ -162,6 +162,8 @@ struct ChunkSmem {
   float cs[CH];                          // column scale of the L, M products
   float eta[CH], alpha[CH], ap[CH], bp[CH], mur[CH], r[CH];
   float zp[4][CH];                       // KDN: per-wavefront partial sums of z_t
+  float pmid[DK], g31[DK];               // KDN, two segments: variance and log-decay after token 31
+  float pcar[DK], g63[DK];               //   and after token 63 (the carry)
   float red[CH];                         // KDN: 1 / (r_t + z_t)
 };
 
@@ -180,6 +182,12 @@ void chunk_fwd_kernel(ChunkArgs a) {
   // z sums and the operand rescaling read four tokens of a channel per
   // transposing LDS read (col4) instead of one element at a time
   constexpr bool FASTCD = BF16 && CHANNEL && GAIN == GAIN_KDN && DK <= NT && DK % 64 == 0;
+  // with 2 d_k threads, two per channel: segment 0 (tokens 0..31) scans the
+  // variance from the carry while segment 1 (tokens 32..63) forms its decay
+  // prefix, then segment 1 replays its variance scan from segment 0's end;
+  // the z sums and the operands use all threads
+  constexpr bool FASTCD2 = FASTCD && NT == 2 * DK;
+  constexpr int HT = CH / 2;
   using Sm = ChunkSmem<E, DK, BV, HAS_W>;
   constexpr int PK = Sm::PK, PT = Sm::PT, P16 = Sm::P16;
   constexpr int VEC = 16 / sizeof(E);            // elements per 16-byte access
@@ -476,6 +484,8 @@ void chunk_fwd_kernel(ChunkArgs a) {
     // Threads own key channels; the carried A / p live in their registers.
     float gch[CHANNEL ? CPT : 1][CHANNEL ? CH : 1];
     float pkr[GAIN == GAIN_KDN ? CPT : 1][GAIN == GAIN_KDN ? CH : 1];  // KDN: p_hat * k
+    float gs[FASTCD2 ? HT : 1], ps[FASTCD2 ? HT : 1];  // two segments: G and p_hat * k of 32 tokens
+    const int seg = tid / DK, dch = tid % DK, cbs = 64 * (dch / 64), tbs = seg * HT;
     if constexpr (SCAN) {
       E* s_al = sm.wt;  // channel alpha staged as [t][d] (wt is built after barrier B)
       E* s_om = sm.lm;  // KDN omega staged as [t][d] (lm is built after barrier C)
@@ -489,7 +499,57 @@ void chunk_fwd_kernel(ChunkArgs a) {
         __syncthreads();
       }
       const float mu = GAIN == GAIN_PGDN ? a.g.mu_log[h] : 0.f;
-      if constexpr (FASTCD) {
+      if constexpr (FASTCD2) {
+        const uint16_t* al16 = reinterpret_cast<const uint16_t*>(s_al);
+        const uint16_t* om16 = reinterpret_cast<const uint16_t*>(s_om);
+        const uint16_t* k16 = reinterpret_cast<const uint16_t*>(sm.k);
+        float G = 0.f, st = aux[0];
+#pragma unroll
+        for (int t4 = 0; t4 < HT; t4 += 4) {
+          const f32x4 al = col4(al16, DK, tbs + t4, cbs, lane);
+          if (seg == 0) {
+            const f32x4 om = col4(om16, DK, t4, cbs, lane);
+            const f32x4 kk = col4(k16, PK, t4, cbs, lane);
+            const f32x4 mr = *reinterpret_cast<const f32x4*>(&sm.mur[t4]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float ph = kdn_predict(al[j], st, om[j]);
+              ps[t4 + j] = ph * kk[j];
+              st = kdn_update(ph, kk[j], mr[j]);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            G += fast_log2(al[j]);
+            gs[t4 + j] = G;
+          }
+        }
+        if (seg == 0) {
+          sm.pmid[dch] = st;
+          sm.g31[dch] = G;
+        }
+        __syncthreads();
+        if (seg == 1) {
+          const float g0 = sm.g31[dch];
+          st = sm.pmid[dch];
+#pragma unroll
+          for (int t4 = 0; t4 < HT; t4 += 4) {
+            const f32x4 al = col4(al16, DK, HT + t4, cbs, lane);
+            const f32x4 om = col4(om16, DK, HT + t4, cbs, lane);
+            const f32x4 kk = col4(k16, PK, HT + t4, cbs, lane);
+            const f32x4 mr = *reinterpret_cast<const f32x4*>(&sm.mur[HT + t4]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float ph = kdn_predict(al[j], st, om[j]);
+              ps[t4 + j] = ph * kk[j];
+              st = kdn_update(ph, kk[j], mr[j]);
+              gs[t4 + j] += g0;
+            }
+          }
+          sm.pcar[dch] = st;
+          sm.g63[dch] = gs[HT - 1];
+        }
+      } else if constexpr (FASTCD) {
         if (tid < DK) {  // wavefronts 0 .. DK / 64 - 1, channel = tid
           const int cb = 64 * wave;
           float G = 0.f, st = aux[0];
@@ -542,6 +602,28 @@ void chunk_fwd_kernel(ChunkArgs a) {
         // z_t = sum_d p_hat k^2: per-wavefront sums (reduce-scattered, lane t
         // gets token t), combined over the wavefronts in a fixed order
         static_assert(CH == 64, "one token per lane");
+        if constexpr (FASTCD2) {
+          // z partial sums of this wavefront's 64 channels over its segment's
+          // 32 tokens; lanes l < 32 get token tbs + l
+          float zt[HT];
+#pragma unroll
+          for (int t4 = 0; t4 < HT; t4 += 4) {
+            const f32x4 kk = col4(reinterpret_cast<const uint16_t*>(sm.k), PK, tbs + t4, cbs, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) zt[t4 + j] = ps[t4 + j] * kk[j];
+          }
+          const float zs = wave_reduce_scatter32(zt, lane);
+          if (lane < HT) sm.zp[wave][lane] = zs;
+          __syncthreads();
+          if (tid < CH) {
+            const int sg = tid / HT;
+            float z = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < DK / 64; ++ww) z += sm.zp[sg * (DK / 64) + ww][tid % HT];
+            sm.red[tid] = 1.f / (sm.r[tid] + z);
+          }
+          if (seg == 0) aux[0] = sm.pcar[dch];  // the variance carried to the next chunk
+        } else {
         float zt[CH];
         if constexpr (FASTCD) {
           if (tid < DK) {
@@ -573,6 +655,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
           for (int ww = 0; ww < NW; ++ww) z += sm.zp[ww][tid];
           sm.red[tid] = 1.f / (sm.r[tid] + z);
+        }
         }
       }
     }
@@ -630,7 +713,35 @@ void chunk_fwd_kernel(ChunkArgs a) {
       }
     } else {
       // channel decay: rescale k, q in place to the chunk midpoint, build wchk and Wtil^T
-      if constexpr (FASTCD) {
+      if constexpr (FASTCD2) {
+        // thread (channel dch, segment seg): its 32 tokens; G at tokens 31
+        // and 63 from the scan's boundary values
+        const float gm = seg == 0 ? gs[HT - 1] : sm.g31[dch], gl = sm.g63[dch];
+        if (seg == 0) {
+          sm.gmid[dch] = fast_exp2(gm);
+          sm.gn[dch] = fast_exp2(gl);
+        }
+        const float fl = fast_exp2(gl - gm);  // 2^(Gn - Gmid)
+#pragma unroll
+        for (int t4 = 0; t4 < HT; t4 += 4) {
+          const int tt = tbs + t4;
+          const f32x4 kk = col4(reinterpret_cast<const uint16_t*>(sm.k), PK, tt, cbs, lane);
+          const f32x4 qq = col4(reinterpret_cast<const uint16_t*>(sm.q), PK, tt, cbs, lane);
+          const f32x4 rd = *reinterpret_cast<const f32x4*>(&sm.red[tt]);
+          float wtv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = tt + j;
+            const float up = fast_exp2(gs[t4 + j] - gm), down = fast_exp2(gm - gs[t4 + j]);
+            const float wv = ps[t4 + j] * rd[j];
+            sm.k[t * PK + dch] = EL::put(up * kk[j]);
+            sm.q[t * PK + dch] = EL::put(up * qq[j]);
+            sm.w[t * PK + dch] = EL::put(down * wv);
+            wtv[j] = fl * down * wv;  // 2^(Gn - G_t) w_t
+          }
+          *reinterpret_cast<u32x2*>(&sm.wt[dch * PT + tt]) = u32x2{pack_bf2(wtv[0], wtv[1]), pack_bf2(wtv[2], wtv[3])};
+        }
+      } else if constexpr (FASTCD) {
         if (tid < DK) {
           const int d = tid, cb = 64 * wave;
           const float gm = gch[0][CH / 2 - 1], gl = gch[0][CH - 1];

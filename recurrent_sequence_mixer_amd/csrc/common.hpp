@@ -138,5 +138,27 @@ __device__ __forceinline__ float wave_reduce_scatter64(float (&v)[64], int lane)
   step(std::integral_constant<int, 1>{}, [](float x) { return dpp_move<0xB1>(x); });
   return v[0];
 }
+// The same for 32 values: lanes l and l + 32 both end with the wavefront's
+// total of element l % 32.
+__device__ __forceinline__ float wave_reduce_scatter32(float (&v)[32], int lane) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] += __shfl_xor(v[i], 32, 64);
+  auto step = [&](auto dtag, auto partner) __attribute__((always_inline)) {
+    constexpr int D = decltype(dtag)::value;
+    const bool hi = (lane & D) != 0;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const float send = hi ? v[i] : v[D + i];
+      const float keep = hi ? v[D + i] : v[i];
+      v[i] = keep + partner(send);
+    }
+  };
+  step(std::integral_constant<int, 16>{}, [](float x) { return __shfl_xor(x, 16, 64); });
+  step(std::integral_constant<int, 8>{}, [](float x) { return dpp_move<0x140>(x); });
+  step(std::integral_constant<int, 4>{}, [](float x) { return dpp_move<0x141>(x); });
+  step(std::integral_constant<int, 2>{}, [](float x) { return dpp_move<0x4E>(x); });
+  step(std::integral_constant<int, 1>{}, [](float x) { return dpp_move<0xB1>(x); });
+  return v[0];
+}
 
 }  // namespace dn
