@@ -204,6 +204,14 @@ struct KLay {
   static __device__ __forceinline__ s16x4 read_tr(const uint16_t* b, int tb, int r0, int s, int h) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds*)(b + tb + r0 * P + 32 * s + 4 * h));
   }
+  // four consecutive tokens r0 .. r0 + 3 of channel cb + lane as fp32, one
+  // transposing read: lane 4 j + q of group g addresses token r0 + j,
+  // channels cb + 16 g + 4 q .. +3, so every lane receives its own channel
+  static __device__ __forceinline__ f32x4 col4(const uint16_t* b, int r0, int cb, int lane) {
+    const int a = lane & 15;
+    const uint16_t* p = b + (r0 + (a >> 2)) * P + cb + 16 * (lane >> 4) + 4 * (a & 3);
+    return unpack16(__builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds*)p));
+  }
   // key channel of row 4 g + i of state tile dt
   static __device__ __forceinline__ int sigma_channel(int dt, int g, int i) {
     return 32 * (dt >> 1) + 8 * g + 4 * (dt & 1) + i;
@@ -257,7 +265,10 @@ struct Smem {
   alignas(16) float fs[CH];                     // S-update scale f_j
   alignas(16) float galpha[2][CH];              // staged alpha, eta by chunk parity (loaders)
   alignas(16) float geta[2][CH];
-  float eta[CH], alpha[CH], ap[CH], bp[CH];     // per-token gates
+  alignas(16) float eta[CH];                    // per-token gates (PGDN)
+  alignas(16) float alpha[CH];
+  alignas(16) float ap[CH];
+  alignas(16) float bp[CH];
   alignas(16) float ah[4 * DK];                 // PGDN: statistic at the segment ends
   alignas(16) float acarry[DK];                 // PGDN: statistic carried between chunks
   float segp[4];                                // PGDN: product of alphaP over each segment
@@ -497,14 +508,20 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
         // the statistic scan in NP / DK segments of the chunk: pass 1 runs
         // each segment from 0 (segment 0 from the carried statistic)
         constexpr int NSEG = NP / DK, SL = CH / NSEG;
-        const int d = ptid % DK, g = ptid / DK;
+        const int d = ptid % DK, g = ptid / DK, cb = d & ~63;  // the wavefront's 64 channels
         pg_start = g == 0 ? sm.acarry[d] : 0.f;
         float st = pg_start, pr = 1.f;
 #pragma unroll
-        for (int i = 0; i < SL; ++i) {
-          const int t = g * SL + i;
-          st = pgdn_stat(st, sm.ap[t], sm.bp[t], bf2f(kb[KL::idx(t, d)]));
-          pr *= sm.ap[t];
+        for (int t4 = 0; t4 < SL; t4 += 4) {
+          const int t = g * SL + t4;
+          const f32x4 kk = KL::col4(kb, t, cb, lane);
+          const f32x4 ap4 = *reinterpret_cast<const f32x4*>(&sm.ap[t]);
+          const f32x4 bp4 = *reinterpret_cast<const f32x4*>(&sm.bp[t]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            st = pgdn_stat(st, ap4[j], bp4[j], kk[j]);
+            pr *= ap4[j];
+          }
         }
         sm.ah[g * DK + d] = st;
         if (d == 0) sm.segp[g] = pr;
@@ -525,12 +542,19 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
           for (int gg = 1; gg < g; ++gg) At = fmaf(sm.segp[gg], At, sm.ah[gg * DK + d]);
         }
         const float mu = a.g.mu_log[h];
+        const int cb = d & ~63;
 #pragma unroll
-        for (int i = 0; i < SL; ++i) {
-          const int t = g * SL + i;
-          const float kk = bf2f(kb[KL::idx(t, d)]);
-          At = pgdn_stat(At, sm.ap[t], sm.bp[t], kk);
-          wb[KL::idx(t, d)] = f2bf(sm.eta[t] * pgdn_scale_hw(At, mu, a.g.log2x) * kk);
+        for (int t4 = 0; t4 < SL; t4 += 4) {
+          const int t = g * SL + t4;
+          const f32x4 kk = KL::col4(kb, t, cb, lane);
+          const f32x4 ap4 = *reinterpret_cast<const f32x4*>(&sm.ap[t]);
+          const f32x4 bp4 = *reinterpret_cast<const f32x4*>(&sm.bp[t]);
+          const f32x4 et4 = *reinterpret_cast<const f32x4*>(&sm.eta[t]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            At = pgdn_stat(At, ap4[j], bp4[j], kk[j]);
+            wb[KL::idx(t + j, d)] = f2bf(et4[j] * pgdn_scale_hw(At, mu, a.g.log2x) * kk[j]);
+          }
         }
         // the carried statistic is read again only by the next chunk's pass 1
         if (g == NSEG - 1) sm.acarry[d] = At;
