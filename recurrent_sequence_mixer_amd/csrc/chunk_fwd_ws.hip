@@ -232,17 +232,13 @@ template <int R>
 struct Role {
   static constexpr int role = R;
 };
-// Scalar-decay gains with stored or register-formed gains (all but PGDN) run
-// twelve wavefronts, three per SIMD: loaders (waves 8..11) issue every load
+// Twelve wavefronts, three per SIMD: loaders (waves 8..11) issue every load
 // and stage it into LDS, so that no consumer or producer ever waits on the
 // memory pipeline (which backs up when all CUs ask for their next chunk at
-// once).  Per chunk c the loaders stage k, q of c + 1 and load k and the gates
-// of c + 2 in P1, stage v of c + 1 and load q, v of c + 2 in P2, and stage the
-// gates of c + 2 in P3.  PGDN, whose statistic scan needs more registers than a
-// third wavefront per SIMD leaves, runs eight: its producers load k and the
-// gates and its consumers q and v.
-__host__ __device__ constexpr bool ws_loaders(int gain) { return gain != GAIN_PGDN; }
-__host__ __device__ constexpr int ws_threads(int gain) { return ws_loaders(gain) ? 768 : 512; }
+// once).  Per chunk c the loaders stage k, q of c + 1 (PGDN: and its gates) and
+// load k and the gates of c + 2 in P1, stage v of c + 1 and load q, v of c + 2
+// in P2, and (the other gains) stage the gates of c + 2 in P3.
+constexpr int WS_THREADS = 768;
 
 template <int DK, int GAIN>
 struct Smem {
@@ -269,15 +265,14 @@ struct Smem {
   alignas(16) float alpha[CH];
   alignas(16) float ap[CH];
   alignas(16) float bp[CH];
-  alignas(16) float ah[4 * DK];                 // PGDN: statistic at the segment ends
+  alignas(16) float ah[512];                    // PGDN: statistic at the segment ends [seg][d_k]
   alignas(16) float acarry[DK];                 // PGDN: statistic carried between chunks
-  float segp[4];                                // PGDN: product of alphaP over each segment
+  float segp[8];                                // PGDN: product of alphaP over each segment
 };
 
 template <int DK, int GAIN>
-__global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArgs a) {
-  constexpr bool LOADERS = ws_loaders(GAIN);
-  constexpr int NT = ws_threads(GAIN);  // threads
+__global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
+  constexpr int NT = WS_THREADS;        // threads
   constexpr int NP = 256;               // producer threads
   constexpr int NDT = DK / 16;          // state tiles of a consumer
   constexpr int KS = DK / 32;           // k-blocks of a d_k contraction
@@ -296,7 +291,8 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
   constexpr int PV = Sm::PV, PT = Sm::PT, P16 = Sm::P16;
   using KL = KLay<DK>;
   static_assert(KV_LOADS * NP * VEC == CH * DK && V_LOADS * NP * VEC == CH * BV, "tile split");
-  static_assert(NP % DK == 0 && CH % (NP / DK) == 0, "statistic scan layout");
+  static_assert(NP % DK == 0 && CH % (2 * NP / DK) == 0 && (CH / (2 * NP / DK)) % 4 == 0 && 2 * NP / DK <= 8,
+                "statistic scan layout");
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
@@ -374,8 +370,7 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
     // ---------------- producer staging of one chunk: 16-byte pieces, rows
     // of k / q / w in consecutive lanes (coalesced), likewise for v
     u32x4 pk[KV_LOADS], pq[KV_LOADS], pwv[GAIN == GAIN_EXPLICIT ? KV_LOADS : 1], pv[V_LOADS];
-    float p_eta = 0.f, p_alpha = 1.f, p_ap = 1.f, p_bp = 0.f;
-    float l_alpha = 1.f, l_eta = 0.f;  // loaders: alpha, eta of token ltid of a chunk
+    float l_alpha = 1.f, l_eta = 0.f, l_ap = 1.f, l_bp = 0.f;  // loaders: gates of token ltid
     float pg_start = 0.f;  // PGDN: carried statistic read by pass 1 (segment 0)
 
     // per-lane byte offsets inside a chunk: the k / q / w pieces (row-major
@@ -406,14 +401,6 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
           const auto rw = rsrc(static_cast<const uint16_t*>(a.g.w) + qk_base + static_cast<long>(t0) * DK, 2 * n * DK);
           pwv[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, koff[j], 0, 0);
         }
-      }
-      // PGDN per-token gates: lanes ptid >= n (all of waves 5..7) read zeros
-      if constexpr (PG) {
-        p_alpha = __uint_as_float(
-            __builtin_amdgcn_raw_buffer_load_b32(rsrc(static_cast<const float*>(a.g.alpha) + tok, 4 * n), 4 * ptid, 0, 0));
-        p_eta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.eta + tok, 4 * n), 4 * ptid, 0, 0));
-        p_ap = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.alphaP + tok, 4 * n), 4 * ptid, 0, 0));
-        p_bp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.betaP + tok, 4 * n), 4 * ptid, 0, 0));
       }
     };
     auto fetch_q = [&](int c) __attribute__((always_inline)) {
@@ -455,16 +442,11 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
         *reinterpret_cast<u32x4*>(&kb[KL::idx(t, d)]) = pk[j];
         if constexpr (GAIN == GAIN_EXPLICIT) *reinterpret_cast<u32x4*>(&sm.w[c & 1][KL::idx(t, d)]) = pwv[j];
       }
-      if (PG && ptid < CH) {
-        const bool ok = ptid < n;
-        sm.eta[ptid] = p_eta;
-        sm.alpha[ptid] = ok ? p_alpha : 1.f;
-        sm.ap[ptid] = ok ? p_ap : 1.f;
-        sm.bp[ptid] = p_bp;
-      }
     };
 
-    // ---------------- loaders (REG): per-token gates of chunk c (the first
+    // tokens of chunk c (0 past the end)
+    auto ntok = [&](int c) __attribute__((always_inline)) { return max(0, min(CH, T - c * CH)); };
+    // ---------------- loaders: per-token gates of chunk c (the first
     // loader wavefront, token = lane) into registers, then into LDS
     auto fetch_gates = [&](int c) __attribute__((always_inline)) {
       const int t0 = c * CH;
@@ -474,11 +456,25 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
           __builtin_amdgcn_raw_buffer_load_b32(rsrc(static_cast<const float*>(a.g.alpha) + tok, 4 * n), 4 * ltid, 0, 0));
       if constexpr (HAS_ETA)
         l_eta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.eta + tok, 4 * n), 4 * ltid, 0, 0));
+      if constexpr (PG) {
+        l_ap = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.alphaP + tok, 4 * n), 4 * ltid, 0, 0));
+        l_bp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.betaP + tok, 4 * n), 4 * ltid, 0, 0));
+      }
     };
-    auto stash_gates = [&](int c) __attribute__((always_inline)) {
+    // REG: alpha, eta by chunk parity; PGDN: the per-token gate arrays of the
+    // statistic scan (alpha, alphaP past the end of n tokens are 1)
+    auto stash_gates = [&](int c, int n) __attribute__((always_inline)) {
       if (ltid < CH) {
-        sm.galpha[c & 1][ltid] = l_alpha;
-        sm.geta[c & 1][ltid] = l_eta;
+        if constexpr (PG) {
+          const bool ok = ltid < n;
+          sm.eta[ltid] = l_eta;
+          sm.alpha[ltid] = ok ? l_alpha : 1.f;
+          sm.ap[ltid] = ok ? l_ap : 1.f;
+          sm.bp[ltid] = l_bp;
+        } else {
+          sm.galpha[c & 1][ltid] = l_alpha;
+          sm.geta[c & 1][ltid] = l_eta;
+        }
       }
     };
 
@@ -493,22 +489,26 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
     };
     // ---------------- producers: gains of a staged chunk c of n tokens from
     // its LDS copy (PGDN)
-    // part 1: cumulative decay, column scales, PGDN statistic pass 1
+    // part 1: cumulative decay and column scales (producers), PGDN statistic
+    // pass 1 (producers and loaders: scan thread sid of 2 NP)
+    constexpr int NSEG = 2 * NP / DK, SL = CH / NSEG;  // PGDN scan segments of SL tokens
+    const int sid = CONS ? 0 : (PROD ? ptid : NP + ltid);
     auto gains1 = [&](int c) __attribute__((always_inline)) {
       const uint16_t* kb = sm.k[c & 1];
-      if (pw == 0) {
-        const float x = wave_prefix_sum(log2_hw(sm.alpha[lane]));
-        sm.g2[c & 1][lane] = x;
-        sm.gam[c & 1][lane] = exp2_hw(x);
-        // kap_t = 2^(E_b - G_t), E_b = G at the end of t's block of 16
-        sm.kap[c & 1][lane] = exp2_hw(__shfl(x, lane | 15) - x);
+      if constexpr (PROD) {
+        if (pw == 0) {
+          const float x = wave_prefix_sum(log2_hw(sm.alpha[lane]));
+          sm.g2[c & 1][lane] = x;
+          sm.gam[c & 1][lane] = exp2_hw(x);
+          // kap_t = 2^(E_b - G_t), E_b = G at the end of t's block of 16
+          sm.kap[c & 1][lane] = exp2_hw(__shfl(x, lane | 15) - x);
+        }
+        if (ptid < CH) sm.cs[c & 1][ptid] = 1.f;
       }
-      if (ptid < CH) sm.cs[c & 1][ptid] = 1.f;
       if constexpr (PG) {
-        // the statistic scan in NP / DK segments of the chunk: pass 1 runs
+        // the statistic scan in NSEG segments of the chunk: pass 1 runs
         // each segment from 0 (segment 0 from the carried statistic)
-        constexpr int NSEG = NP / DK, SL = CH / NSEG;
-        const int d = ptid % DK, g = ptid / DK, cb = d & ~63;  // the wavefront's 64 channels
+        const int d = sid % DK, g = sid / DK, cb = d & ~63;  // the wavefront's 64 channels
         pg_start = g == 0 ? sm.acarry[d] : 0.f;
         float st = pg_start, pr = 1.f;
 #pragma unroll
@@ -532,8 +532,7 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
     // each segment is replayed from it and writes its w = eta B(A) k
     auto gains2 = [&](int c) __attribute__((always_inline)) {
       if constexpr (PG) {
-        constexpr int NSEG = NP / DK, SL = CH / NSEG;
-        const int d = ptid % DK, g = ptid / DK;
+        const int d = sid % DK, g = sid / DK;
         const uint16_t* kb = sm.k[c & 1];
         uint16_t* wb = sm.w[c & 1];
         float At = pg_start;
@@ -691,33 +690,20 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
 
     // ---------------- prologue: chunk 0 staged, its gains (and, REG, tiles)
     if (nchunks > 0) {
-      if constexpr (LOADERS) {
-        // chunk 0 and the gates of chunk 1 into LDS; the loads the loop
-        // stages first (k, q, v of chunk 1)
-        if constexpr (LOAD) {
-          fetch_k(0);
-          fetch_q(0);
-          fetch_v(0);
-          fetch_gates(0);
-          stash_k(0, min(CH, T));
-          stash_q(0);
-          stash_v();
-          stash_gates(0);
-          fetch_gates(1);
-          stash_gates(1);
-          fetch_k(1);
-          fetch_q(1);
-          fetch_v(1);
-        }
-      } else if constexpr (PROD) {
+      // loaders: chunk 0 (REG: and the gates of chunk 1) into LDS; the loads
+      // the loop stages first (k, q, v and, PGDN, the gates of chunk 1)
+      if constexpr (LOAD) {
         fetch_k(0);
-        stash_k(0, min(CH, T));
-        fetch_k(1);
-      } else if constexpr (CONS) {
         fetch_q(0);
         fetch_v(0);
+        fetch_gates(0);
+        stash_k(0, min(CH, T));
         stash_q(0);
         stash_v();
+        stash_gates(0, min(CH, T));
+        fetch_gates(1);
+        if constexpr (REG) stash_gates(1, ntok(1));
+        fetch_k(1);
         fetch_q(1);
         fetch_v(1);
       }
@@ -727,21 +713,22 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
       if (PROD && nchunks > 0) regains(0, min(CH, T));
       __syncthreads();
     }
-    if constexpr (PROD) {
-      if (nchunks > 0) {
-        if constexpr (REG) {
+    if (nchunks > 0) {
+      if constexpr (REG) {
+        if constexpr (PROD) {
           tiles(0);
           diag_gains(0, min(CH, T));
-        } else {
-          gains1(0);
         }
+      } else if constexpr (!CONS) {
+        gains1(0);
       }
     }
     __syncthreads();
-    if constexpr (PROD) {
-      if (nchunks > 0) {
-        if constexpr (REG) scale_diag(0);
-        else gains2(0);
+    if (nchunks > 0) {
+      if constexpr (REG) {
+        if constexpr (PROD) scale_diag(0);
+      } else if constexpr (!CONS) {
+        gains2(0);
       }
     }
     __syncthreads();
@@ -799,16 +786,13 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
           OQ[rt] = aq * sm.gam[c & 1][16 * rt + c16];
         }
         gn = sm.gam[c & 1][CH - 1];
-        // PGDN: q of chunk c + 1 into LDS (its parity's last readers are done)
-        if constexpr (!LOADERS) {
-          if (c + 1 < nchunks) stash_q(c + 1);
-        }
       } else if constexpr (LOAD) {
-        // k, q of chunk c + 1 into LDS; the loads of k and of the gates of
-        // chunk c + 2
+        // k, q (PGDN: and the gates) of chunk c + 1 into LDS; the loads of k
+        // and of the gates of chunk c + 2
         if (c + 1 < nchunks) {
           stash_k(c + 1, n1);
           stash_q(c + 1);
+          if constexpr (PG) stash_gates(c + 1, n1);
         }
         fetch_k(c + 2);
         fetch_gates(c + 2);
@@ -857,29 +841,26 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
         }
         // PGDN: v of chunk c + 1 into LDS (chunk c's was last read in P1),
         // the loads of q and v of chunk c + 2 (the loads of k go out in P3)
-        if constexpr (!LOADERS) {
-          if (c + 1 < nchunks) stash_v();
-          fetch_q(c + 2);
-          fetch_v(c + 2);
-        }
       } else if constexpr (LOAD) {
         // v of chunk c + 1 into LDS (chunk c's was last read in P1); the
-        // loads of q and v of chunk c + 2
+        // loads of q and v of chunk c + 2; PGDN: their share of pass 1
         if (c + 1 < nchunks) stash_v();
         fetch_q(c + 2);
         fetch_v(c + 2);
-      } else {
-        if constexpr (!REG) {
-          if (c + 1 < nchunks) stash_k(c + 1, n1);
+        if constexpr (PG) {
+          if (c + 1 < nchunks) gains1(c + 1);
         }
-        if constexpr (REG) {
-          if (c + 1 < nchunks) {
+      } else {
+        if (c + 1 < nchunks) {
+          if constexpr (REG) {
             tiles(c + 1);  // raw products, scaled in P3
             diag_gains(c + 1, n1);
+          } else {
+            gains1(c + 1);  // PGDN statistic pass 1 (and the decay) of chunk c + 1
           }
         }
       }
-      __syncthreads();  // (2) the inputs of chunk c + 1 ready
+      __syncthreads();  // (2) REG: raw tiles of chunk c + 1; PGDN: its pass 1
 
       // ================= P3 =================
       if constexpr (CONS) {
@@ -896,22 +877,17 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
           S[dt] = acc;
         };
 #pragma unroll
-        for (int dt = 0; dt < NDT / 2; ++dt) update(dt);
-        if constexpr (PG) __syncthreads();  // (3a) PGDN statistic pass 1 done
-#pragma unroll
-        for (int dt = NDT / 2; dt < NDT; ++dt) update(dt);
+        for (int dt = 0; dt < NDT; ++dt) update(dt);
       } else if constexpr (LOAD) {
-        // the gates of chunk c + 2 into LDS (their parity's last readers,
-        // regains and diag_gains of chunk c, are done)
-        stash_gates(c + 2);
+        // REG: the gates of chunk c + 2 into LDS (their parity's last
+        // readers, regains and diag_gains of chunk c, are done); PGDN: their
+        // share of pass 2
+        if constexpr (REG) stash_gates(c + 2, ntok(c + 2));
+        else if (c + 1 < nchunks) gains2(c + 1);
       } else {
-        if constexpr (REG) {
-          if (c + 1 < nchunks) scale_diag(c + 1);
-        } else {
-          fetch_k(c + 2);
-          if (c + 1 < nchunks) gains1(c + 1);
-          __syncthreads();  // (3a)
-          if (c + 1 < nchunks) gains2(c + 1);
+        if (c + 1 < nchunks) {
+          if constexpr (REG) scale_diag(c + 1);
+          else gains2(c + 1);  // PGDN pass 2: the write vectors of chunk c + 1
         }
       }
       __syncthreads();  // (3) chunk c + 1: tiles (REG) or gains (PGDN) ready; S updated
@@ -936,7 +912,7 @@ __global__ __launch_bounds__(ws_threads(GAIN)) void chunk_fwd_ws_kernel(ChunkArg
   } else if (wave < 8) {
     run(Role<1>{});
   } else {
-    if constexpr (LOADERS) run(Role<2>{});
+    run(Role<2>{});
   }
 }
 
@@ -952,7 +928,7 @@ static hipError_t launch_ws_one(const ChunkArgs& a, hipStream_t st) {
                                        static_cast<int>(sizeof(Sm)));
   if (err != hipSuccess) return err;
   dim3 grid(static_cast<unsigned>((a.dv / ws::BV) * a.B * a.H));
-  hipLaunchKernelGGL(kern, grid, dim3(ws::ws_threads(GAIN)), sizeof(Sm), st, a);
+  hipLaunchKernelGGL(kern, grid, dim3(ws::WS_THREADS), sizeof(Sm), st, a);
   return hipGetLastError();
 }
 
