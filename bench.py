@@ -64,7 +64,22 @@ def decode_bytes(dwl):
     return nh * (2 * dwl.dk * dwl.dv * 4 + 2 * (2 * dwl.dk + dwl.dv) + 8 + 2 * dwl.dv)
 
 
-def time_chunk(wl, steps, warmup):
+def settle(call, seconds):
+    """Run `call` untimed for about `seconds` of wall time before the warm-up
+    steps.  Under sustained load the GPU's clocks ramp up over the first tens
+    of milliseconds (back-to-back launches of the chunk kernel go from
+    0.25 ms to a steady 0.17-0.18 ms); this puts the W warm-up and the K timed
+    steps at that steady state.  Synchronises every few calls so that the
+    queue stays short."""
+    import torch
+    end = time.time() + seconds
+    while time.time() < end:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
+
+
+def time_chunk(wl, steps, warmup, settle_s=0.0):
     import torch
     from recurrent_sequence_mixer_amd import dn
     from recurrent_sequence_mixer_amd import workloads as W
@@ -78,6 +93,7 @@ def time_chunk(wl, steps, warmup):
     aux = torch.empty((wl.B, wl.H, wl.dk), device="cuda") if wl.gain in ("pgdn", "kdn") else None
     call = lambda: dn.chunk_fwd(t["q"], t["k"], t["v"], gates, gain=wl.gain, eps=wl.eps, x=wl.x,
                                 mu_info=wl.mu_info, S0=t["S0"], out=o, S_final=S, aux_final=aux)
+    settle(call, settle_s)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -101,7 +117,7 @@ def time_chunk(wl, steps, warmup):
     return total_ms / steps, each
 
 
-def time_decode(dwl, steps_timed):
+def time_decode(dwl, steps_timed, settle_s=0.0):
     import torch
     from recurrent_sequence_mixer_amd import dn
     from recurrent_sequence_mixer_amd import workloads as W
@@ -113,6 +129,9 @@ def time_decode(dwl, steps_timed):
         ins.append((st["q"], st["k"], st["v"], {"alpha": st["alpha"], "eta": st["eta"]}))
     log(f"[bench] decode: {dwl.steps} steps of inputs ready in {time.time() - t0:.1f}s")
     o = torch.empty((dwl.N, dwl.H, dwl.dv), dtype=torch.bfloat16, device="cuda")
+    Sw = S.clone()  # scratch state for the untimed steps
+    q0, k0, v0, g0 = ins[0]
+    settle(lambda: dn.decode_step(q0, k0, v0, g0, Sw, gain="kla", eps=dwl.eps, out=o), settle_s)
     for s in range(3):  # warm-up steps on a scratch copy of the state
         q, k, v, g = ins[s]
         dn.decode_step(q, k, v, g, S.clone(), gain="kla", eps=dwl.eps, out=o)
@@ -198,6 +217,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="untimed run of each workload before its warm-up steps (GPU clock ramp)")
     ap.add_argument("--cpu-heads", type=int, default=128, help="oracle sample: heads")
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample: tokens per head")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -214,7 +235,7 @@ def main():
     torch.cuda.set_device(0)
 
     wl = W.WORKLOADS[1]
-    ms, each = time_chunk(wl, args.steps, args.warmup)
+    ms, each = time_chunk(wl, args.steps, args.warmup, args.settle_s)
     bytes_ = chunk_bytes(wl)
     flops = chunk_flops(wl)
     achieved = bytes_ / (ms * 1e-3) / 1e9
@@ -241,13 +262,14 @@ def main():
                  "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                  "counted_flops_per_launch": flops},
         "step_ms_p10_p50_p90": [each[len(each) // 10], each[len(each) // 2], each[9 * len(each) // 10]],
+        "settle_s": args.settle_s,
     }
     log(f"[bench] {wl.name}: {ms:.3f} ms/step")
     if not args.no_extra:
         extra = {}
         for idx in (2, 3):
             w2 = W.WORKLOADS[idx]
-            ms2, _ = time_chunk(w2, max(5, args.steps // 2), args.warmup)
+            ms2, _ = time_chunk(w2, max(5, args.steps // 2), args.warmup, args.settle_s)
             b2 = chunk_bytes(w2)
             extra[w2.gain] = {"workload": w2.name, "ms": ms2, "tokens_per_s": w2.tokens / (ms2 * 1e-3),
                               "hbm_gbs": b2 / (ms2 * 1e-3) / 1e9,
@@ -255,7 +277,7 @@ def main():
                               "mfma_frac": chunk_flops(w2) / (ms2 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
             log(f"[bench] {w2.name}: {ms2:.3f} ms/step")
         dwl = W.WORKLOADS[4]
-        dms = time_decode(dwl, args.decode_steps)
+        dms = time_decode(dwl, args.decode_steps, args.settle_s)
         gbs = decode_bytes(dwl) / (dms * 1e-3) / 1e9
         extra["decode"] = {"workload": dwl.name, "ms_per_step": dms,
                            "seq_tokens_per_s": dwl.N / (dms * 1e-3), "hbm_gbs": gbs,
