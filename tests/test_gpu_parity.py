@@ -76,6 +76,21 @@ def test_bf16_other_head_dims(dk, dv):
     _check(wl, inp, None, o, S)
 
 
+# d_k = 64 changes the work split of the per-channel scans: the PGDN
+# statistic runs in eight 8-token segments, the KDN channel-decay scan on one
+# thread per channel; ragged lengths cover the partial last chunk
+@pytest.mark.parametrize("T", [37, 200])
+@pytest.mark.parametrize("dv", [64, 128])
+@pytest.mark.parametrize("gain,decay,keys", [("gdn", "scalar", "unit"), ("pgdn", "scalar", "unit"),
+                                             ("kdn", "channel", "scaled")])
+def test_bf16_gains_dk64(gain, decay, keys, dv, T):
+    wl = W.Workload(f"{gain}_{decay}_bf16_dk64", gain, decay, "bf16", 2, 2, T, 64, dv, keys=keys,
+                    seed=300 + T + dv)
+    inp = W.generate(wl)
+    o, S, aux = gpu_chunk(wl, inp)
+    _check(wl, inp, None, o, S, aux)
+
+
 # ---------------------------------------------------------------- full size workloads
 
 @pytest.mark.parametrize("idx", [1, 2, 3])
