@@ -151,26 +151,6 @@ __device__ __forceinline__ f32x4 unpack16(s16x4 p) {
                __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xFFFF0000u)};
 }
 
-// A 16x16 fp32 accumulator tile as a sum of two bf16 tiles (hi + lo), and
-// C + X^T Y for two such tiles (the lo * lo term is below fp32 rounding of the
-// result).  Packed, an accumulator tile acc(X) is the A operand of X^T and the
-// B operand of X.  hi^T hi + lo^T hi runs as one 16x16x32 MFMA whose k slots
-// pair (x.hi, x.lo) with (y.hi, y.hi); hi^T lo is a 16x16x16 MFMA (same cost
-// per instruction as the x32 form on gfx950).
-struct Split {
-  s16x4 hi, lo;
-};
-__device__ __forceinline__ Split split(f32x4 x) {
-  Split r;
-  r.hi = pack16(x);
-  r.lo = pack16(x - unpack16(r.hi));
-  return r;
-}
-__device__ __forceinline__ f32x4 prod_t(const Split& x, const Split& y, f32x4 c) {
-  c = mfma32(cat8(x.hi, x.lo), cat8(y.hi, y.hi), c);
-  return mfma16(x.hi, y.lo, c);
-}
-
 // Layout of the [token][d_k] tiles k, q, w in LDS: row-major rows of
 // d_k + 16 bf16.  Measured on gfx950, the 16-byte fragment reads of 16 rows
 // by 4 lane groups are free of bank conflicts at this pitch (the 8-byte
@@ -383,6 +363,12 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
       const int e = (ltid + j * NP) * VEC;
       voff[j] = 2 * ((e / BV) * a.dv + col0 + e % BV);
     }
+    // tokens of chunk c (0 past the end).  The clamp lowers to a vector
+    // v_med3; read back as a scalar, the buffer resources built from it stay
+    // in scalar registers (else every load becomes a readfirstlane loop)
+    auto ntok = [&](int c) __attribute__((always_inline)) {
+      return __builtin_amdgcn_readfirstlane(max(0, min(CH, T - c * CH)));
+    };
     // loads of chunk c through buffer resources that end at its last token:
     // past the end k = q = w = v = eta = alphaP = betaP = 0 (alpha, alphaP are
     // replaced by 1 where they are used).  Chunks past the last one get empty
@@ -391,7 +377,7 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
     // k (w, gates) and q, v are loaded, and staged, at different points
     auto fetch_k = [&](int c) __attribute__((always_inline)) {
       const int t0 = c * CH;
-      const int n = max(0, min(CH, T - t0));
+      const int n = ntok(c);
       const long tok = static_cast<long>(bh) * T + t0;
       const auto rk = rsrc(static_cast<const uint16_t*>(a.k) + qk_base + static_cast<long>(t0) * DK, 2 * n * DK);
 #pragma unroll
@@ -405,14 +391,14 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
     };
     auto fetch_q = [&](int c) __attribute__((always_inline)) {
       const int t0 = c * CH;
-      const int n = max(0, min(CH, T - t0));
+      const int n = ntok(c);
       const auto rq = rsrc(static_cast<const uint16_t*>(a.q) + qk_base + static_cast<long>(t0) * DK, 2 * n * DK);
 #pragma unroll
       for (int j = 0; j < KV_LOADS; ++j) pq[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, koff[j], 0, 0);
     };
     auto fetch_v = [&](int c) __attribute__((always_inline)) {
       const int t0 = c * CH;
-      const int n = max(0, min(CH, T - t0));
+      const int n = ntok(c);
       const auto rv = rsrc(static_cast<const uint16_t*>(a.v) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv);
 #pragma unroll
       for (int j = 0; j < V_LOADS; ++j) pv[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[j], 0, 0);
@@ -444,13 +430,11 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
       }
     };
 
-    // tokens of chunk c (0 past the end)
-    auto ntok = [&](int c) __attribute__((always_inline)) { return max(0, min(CH, T - c * CH)); };
     // ---------------- loaders: per-token gates of chunk c (the first
     // loader wavefront, token = lane) into registers, then into LDS
     auto fetch_gates = [&](int c) __attribute__((always_inline)) {
       const int t0 = c * CH;
-      const int n = max(0, min(CH, T - t0));
+      const int n = ntok(c);
       const long tok = static_cast<long>(bh) * T + t0;
       l_alpha = __uint_as_float(
           __builtin_amdgcn_raw_buffer_load_b32(rsrc(static_cast<const float*>(a.g.alpha) + tok, 4 * n), 4 * ltid, 0, 0));
@@ -666,23 +650,27 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
       }
     };
     // ---------------- producers: (I + L_pp)^-1 from at = acc(A^T), an = acc(A),
-    // A = L_pp strictly lower: (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8),
-    // with prod_t(X, Y) = X^T Y; and the S-update scale f_j = 2^(G_n - G_j) c_j
-    // (I + Z)^T Y = Y + Z^T Y: each identity is the accumulator's start value
+    // A = L_pp strictly lower: (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8);
+    // and the S-update scale f_j = 2^(G_n - G_j) c_j.  Packed, an accumulator
+    // tile acc(X) is the A operand of X^T and the B operand of X, so one
+    // 16x16x16 MFMA gives C + X^T Y.  The powers and partial products enter as
+    // bf16 (fp32 accumulation), the rounding the stored inverse gets anyway;
+    // (I + Z)^T Y = Y + Z^T Y: each identity term is the exact fp32 start value
+    // of the accumulator
     const int ud = c16 - 4 * g4;  // the slot of this lane's diagonal entry, if 0..3
     const f32x4 idm = {ud == 0 ? 1.f : 0.f, ud == 1 ? 1.f : 0.f, ud == 2 ? 1.f : 0.f, ud == 3 ? 1.f : 0.f};
     auto invert = [&](int c) __attribute__((always_inline)) {
       if (pw == 1) sm.fs[lane] = sm.cs[c & 1][lane] * exp2_hw(sm.g2[c & 1][CH - 1] - sm.g2[c & 1][lane]);
-      const Split sat = split(at), san = split(an);
-      const f32x4 A2 = prod_t(sat, san, zero4()), A2t = prod_t(san, sat, zero4());
-      const Split sA2 = split(A2), sA2t = split(A2t);
-      const f32x4 A4 = prod_t(sA2t, sA2, zero4()), A4t = prod_t(sA2, sA2t, zero4());
-      const Split sA4 = split(A4), sA4t = split(A4t);
-      const f32x4 A8 = prod_t(sA4t, sA4, zero4());
-      const f32x4 imt = idm - at;                            // (I - A)^T
-      const f32x4 p1t = prod_t(sA2, split(imt), imt);        // ((I - A)(I + A^2))^T
-      const f32x4 p2t = prod_t(sA4, split(p1t), p1t);        // ... (I + A^4)
-      const f32x4 tt_ = prod_t(split(A8), split(p2t), p2t);  // acc(T^T)
+      const s16x4 sat = pack16(at), san = pack16(an);
+      const f32x4 A2 = mfma16(sat, san, zero4()), A2t = mfma16(san, sat, zero4());
+      const s16x4 sA2 = pack16(A2), sA2t = pack16(A2t);
+      const f32x4 A4 = mfma16(sA2t, sA2, zero4()), A4t = mfma16(sA2, sA2t, zero4());
+      const s16x4 sA4 = pack16(A4), sA4t = pack16(A4t);
+      const f32x4 A8 = mfma16(sA4t, sA4, zero4());
+      const f32x4 imt = idm - at;                               // (I - A)^T
+      const f32x4 p1t = mfma16(sA2, pack16(imt), imt);          // ((I - A)(I + A^2))^T
+      const f32x4 p2t = mfma16(sA4, pack16(p1t), p1t);          // ... (I + A^4)
+      const f32x4 tt_ = mfma16(pack16(A8), pack16(p2t), p2t);   // acc(T^T)
       // lane holds T[c16][4 g4 + u]: row c16 of block p
       *reinterpret_cast<u32x2*>(&sm.tb[(16 * pw + c16) * P16 + 4 * g4]) =
           u32x2{pack_bf2(tt_[0], tt_[1]), pack_bf2(tt_[2], tt_[3])};
