@@ -227,8 +227,12 @@ struct Smem {
   static constexpr int PT = CH + 8;   // [token][token] rows, bf16
   static constexpr int P16 = 16 + 8;  // rows of 16-wide blocks
   static constexpr bool HAS_W = GAIN == GAIN_PGDN || GAIN == GAIN_EXPLICIT;
+  static constexpr bool CD = GAIN == GAIN_KDN;  // KDN with per-channel decay
+  static constexpr bool PG = GAIN == GAIN_PGDN;
+  // KDN: k holds raw k, then (in place) the scaled write vectors W^, by parity;
+  // q[0] raw q, then Q^ in place; q[1] K^; w[0], w[1] the raw alpha, omega
   alignas(16) uint16_t k[2][CH * PK];           // k, by chunk parity
-  alignas(16) uint16_t w[HAS_W ? 2 : 1][HAS_W ? CH * PK : 8];  // write vectors, by parity
+  alignas(16) uint16_t w[HAS_W || CD ? 2 : 1][HAS_W || CD ? CH * PK : 8];  // write vectors, by parity
   alignas(16) uint16_t q[2][CH * PK];           // q, by chunk parity
   alignas(16) uint16_t v[CH * PV];              // value slice
   alignas(16) uint16_t ln[CH * PT];             // -L [i][j], the off-diagonal 16x16 tiles
@@ -241,13 +245,19 @@ struct Smem {
   alignas(16) float fs[CH];                     // S-update scale f_j
   alignas(16) float galpha[2][CH];              // staged alpha, eta by chunk parity (loaders)
   alignas(16) float geta[2][CH];
-  alignas(16) float eta[CH];                    // per-token gates (PGDN)
-  alignas(16) float alpha[CH];
-  alignas(16) float ap[CH];
-  alignas(16) float bp[CH];
-  alignas(16) float ah[512];                    // PGDN: statistic at the segment ends [seg][d_k]
-  alignas(16) float acarry[DK];                 // PGDN: statistic carried between chunks
+  alignas(16) float eta[PG ? CH : 4];           // per-token gates (PGDN)
+  alignas(16) float alpha[PG ? CH : 4];
+  alignas(16) float ap[PG ? CH : 4];
+  alignas(16) float bp[PG ? CH : 4];
+  alignas(16) float ah[PG ? 512 : 4];           // PGDN: statistic at the segment ends [seg][d_k]
+  alignas(16) float acarry[DK];                 // PGDN / KDN: statistic / variance carried between chunks
   float segp[8];                                // PGDN: product of alphaP over each segment
+  // KDN: per [segment][d_k] the variance map of the segment (m00, m01, m10,
+  // m11) and its decay product; per d_k and chunk parity the decay to the
+  // reference token and from it to the chunk end
+  alignas(16) float msum[CD ? 5 : 1][CD ? 512 : 4];
+  alignas(16) float gref[CD ? 2 : 1][CD ? DK : 4];
+  alignas(16) float gnr[CD ? 2 : 1][CD ? DK : 4];
 };
 
 template <int DK, int GAIN>
@@ -261,12 +271,13 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
   constexpr int V_LOADS = CH * BV / (NP * VEC);
   constexpr bool HAS_W = GAIN == GAIN_PGDN || GAIN == GAIN_EXPLICIT;
   constexpr bool PG = GAIN == GAIN_PGDN;
-  constexpr bool HAS_ETA = GAIN != GAIN_EXPLICIT;
+  constexpr bool CD = GAIN == GAIN_KDN;  // KDN, per-channel decay
+  constexpr bool HAS_ETA = GAIN != GAIN_EXPLICIT && !CD;
   // Gains straight from the staging registers (no per-channel scan): the
   // gains of chunk c + 1 are formed in P2 as it is staged, and its tiles in
   // P3.  PGDN scans its statistic over the LDS copy of k in P3 and forms its
   // tiles in P1, once its write vectors exist.
-  constexpr bool REG = !PG;
+  constexpr bool REG = !PG && !CD;
   using Sm = Smem<DK, GAIN>;
   constexpr int PV = Sm::PV, PT = Sm::PT, P16 = Sm::P16;
   using KL = KLay<DK>;
@@ -344,12 +355,18 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
         for (int dt = 0; dt < NDT; ++dt) S[dt] = zero4();
       }
     } else if constexpr (PROD) {
-      if (PG && ptid < DK) sm.acarry[ptid] = a.aux0 ? a.aux0[static_cast<long>(bh) * DK + ptid] : 1.f;
+      if ((PG || CD) && ptid < DK) sm.acarry[ptid] = a.aux0 ? a.aux0[static_cast<long>(bh) * DK + ptid] : 1.f;
+      // KDN: the decay lives in the operands, the token-decay arrays stay 0 / 1
+      if (CD && ptid < 2 * CH) {
+        sm.g2[ptid >> 6][ptid & 63] = 0.f;
+        sm.gam[ptid >> 6][ptid & 63] = 1.f;
+      }
     }
 
     // ---------------- producer staging of one chunk: 16-byte pieces, rows
     // of k / q / w in consecutive lanes (coalesced), likewise for v
     u32x4 pk[KV_LOADS], pq[KV_LOADS], pwv[GAIN == GAIN_EXPLICIT ? KV_LOADS : 1], pv[V_LOADS];
+    u32x4 pa[CD ? KV_LOADS : 1], po[CD ? KV_LOADS : 1];  // KDN: alpha, omega pieces
     float l_alpha = 1.f, l_eta = 0.f, l_ap = 1.f, l_bp = 0.f;  // loaders: gates of token ltid
     float pg_start = 0.f;  // PGDN: carried statistic read by pass 1 (segment 0)
 
@@ -396,6 +413,21 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
       for (int j = 0; j < KV_LOADS; ++j) pq[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, koff[j], 0, 0);
     };
+    // KDN: the per-channel alpha and omega of chunk c (laid out like k)
+    auto fetch_ao = [&](int c) __attribute__((always_inline)) {
+      if constexpr (CD) {
+        const int t0 = c * CH;
+        const int n = ntok(c);
+        const long off = qk_base + static_cast<long>(t0) * DK;
+        const auto ra = rsrc(static_cast<const uint16_t*>(a.g.alpha) + off, 2 * n * DK);
+        const auto rw = rsrc(static_cast<const uint16_t*>(a.g.omega) + off, 2 * n * DK);
+#pragma unroll
+        for (int j = 0; j < KV_LOADS; ++j) {
+          pa[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, koff[j], 0, 0);
+          po[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, koff[j], 0, 0);
+        }
+      }
+    };
     auto fetch_v = [&](int c) __attribute__((always_inline)) {
       const int t0 = c * CH;
       const int n = ntok(c);
@@ -409,7 +441,22 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
       for (int j = 0; j < KV_LOADS; ++j) {
         const int e = (ltid + j * NP) * VEC;
-        *reinterpret_cast<u32x4*>(&sm.q[c & 1][KL::idx(e / DK, e % DK)]) = pq[j];
+        *reinterpret_cast<u32x4*>(&sm.q[CD ? 0 : c & 1][KL::idx(e / DK, e % DK)]) = pq[j];
+      }
+    };
+    // KDN: alpha, omega of a chunk of n tokens into LDS; alpha past the end
+    // is 1 (omega, k and the information scale are 0 there), so the variance
+    // and the decay pass through the padding unchanged
+    auto stash_ao = [&](int n) __attribute__((always_inline)) {
+      if constexpr (CD) {
+#pragma unroll
+        for (int j = 0; j < KV_LOADS; ++j) {
+          const int e = (ltid + j * NP) * VEC;
+          const int t = e / DK, d = e % DK;
+          const u32x4 one = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+          *reinterpret_cast<u32x4*>(&sm.w[0][KL::idx(t, d)]) = t < n ? pa[j] : one;
+          *reinterpret_cast<u32x4*>(&sm.w[1][KL::idx(t, d)]) = po[j];
+        }
       }
     };
     auto stash_v = [&]() __attribute__((always_inline)) {
@@ -436,6 +483,11 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
       const int t0 = c * CH;
       const int n = ntok(c);
       const long tok = static_cast<long>(bh) * T + t0;
+      if constexpr (CD) {
+        // KDN: the observation noise r_t (alpha is per channel, in its own tile)
+        l_eta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.r + tok, 4 * n), 4 * ltid, 0, 0));
+        return;
+      }
       l_alpha = __uint_as_float(
           __builtin_amdgcn_raw_buffer_load_b32(rsrc(static_cast<const float*>(a.g.alpha) + tok, 4 * n), 4 * ltid, 0, 0));
       if constexpr (HAS_ETA)
@@ -449,7 +501,12 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
     // statistic scan (alpha, alphaP past the end of n tokens are 1)
     auto stash_gates = [&](int c, int n) __attribute__((always_inline)) {
       if (ltid < CH) {
-        if constexpr (PG) {
+        if constexpr (CD) {
+          // r_t, and the information scale mu / r_t of the variance update
+          // (0 past the end)
+          sm.geta[c & 1][ltid] = l_eta;
+          sm.galpha[c & 1][ltid] = ltid < n ? a.g.mu_info * __builtin_amdgcn_rcpf(l_eta) : 0.f;
+        } else if constexpr (PG) {
           const bool ok = ltid < n;
           sm.eta[ltid] = l_eta;
           sm.alpha[ltid] = ok ? l_alpha : 1.f;
@@ -544,6 +601,123 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
       }
     };
 
+    // ---------------- KDN (per-channel decay): the variance scan of a staged
+    // chunk c in NSEG segments of SL tokens per key channel (scan thread sid:
+    // channel sid % DK, segment sid / DK; producers and loaders).  One token
+    // maps the variance p to p_hat / (1 + u p_hat), p_hat = alpha^2 p + omega,
+    // u = (mu / r) k^2 (Kalman Delta Networks §2.4-2.5): the Mobius map with
+    // coefficients (alpha^2, omega; u alpha^2, 1 + u omega), and a segment's
+    // updates compose to one such map.  Pass 1 composes each segment's map and
+    // its decay product; pass 2 starts each segment from the carried variance
+    // through the maps of the segments before it, replays its tokens and
+    // writes the decay-scaled operands of the chunk form,
+    //   K^ = k 2^(G_t - G_r),  Q^ = q 2^(G_t - G_r),  W^ = p_hat k 2^(G_r - G_t),
+    // G_t the log-decay from the chunk start through token t (per channel) and
+    // G_r its value at token 31.  The gain's column scale 1 / (r + z) comes
+    // later from the diagonal of K^ W^T (z_t = sum of p_hat k^2).
+    float cd_p0 = 1.f;  // the carried variance, read in pass 1 (pass 2 of the
+                        // last segment rewrites the carry)
+    auto cd_pass1 = [&](int c) __attribute__((always_inline)) {
+      if constexpr (CD) {
+        const int d = sid % DK, g = sid / DK, cb = d & ~63;
+        const uint16_t* kb = sm.k[c & 1];
+        cd_p0 = sm.acarry[d];
+        float m00 = 1.f, m01 = 0.f, m10 = 0.f, m11 = 1.f, pr = 1.f;
+#pragma unroll 1
+        for (int t4 = 0; t4 < SL; t4 += 4) {
+          const int t = g * SL + t4;
+          const f32x4 kk = KL::col4(kb, t, cb, lane);
+          const f32x4 al = KL::col4(sm.w[0], t, cb, lane);
+          const f32x4 om = KL::col4(sm.w[1], t, cb, lane);
+          const f32x4 mu4 = *reinterpret_cast<const f32x4*>(&sm.galpha[c & 1][t]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float aa = al[j] * al[j];
+            const float ua = mu4[j] * kk[j] * kk[j] * aa, ue = fmaf(mu4[j] * kk[j] * kk[j], om[j], 1.f);
+            const float n00 = fmaf(aa, m00, om[j] * m10), n01 = fmaf(aa, m01, om[j] * m11);
+            const float n10 = fmaf(ua, m00, ue * m10), n11 = fmaf(ua, m01, ue * m11);
+            m00 = n00;
+            m01 = n01;
+            m10 = n10;
+            m11 = n11;
+            pr *= al[j];
+          }
+          // the map is projective: divide by its (1, 1) entry, which is >= 1
+          const float sc = __builtin_amdgcn_rcpf(m11);
+          m00 *= sc;
+          m01 *= sc;
+          m10 *= sc;
+          m11 = 1.f;
+        }
+        sm.msum[0][sid] = m00;
+        sm.msum[1][sid] = m01;
+        sm.msum[2][sid] = m10;
+        sm.msum[3][sid] = pr;
+      }
+    };
+    auto cd_pass2 = [&](int c) __attribute__((always_inline)) {
+      if constexpr (CD) {
+        const int d = sid % DK, g = sid / DK, cb = d & ~63;
+        constexpr int RS = NSEG / 2 - 1;  // the segment that ends at token 31
+        float p = cd_p0, num = 1.f, den = 1.f, gr = 1.f, gt = 1.f;
+#pragma unroll
+        for (int gg = 0; gg < NSEG; ++gg) {
+          const float pr = sm.msum[3][gg * DK + d];
+          if (gg < g) {
+            p = fmaf(sm.msum[0][gg * DK + d], p, sm.msum[1][gg * DK + d]) *
+                __builtin_amdgcn_rcpf(fmaf(sm.msum[2][gg * DK + d], p, 1.f));
+            if (gg > RS) num *= pr;
+          } else if (gg <= RS) {
+            den *= pr;
+          }
+          if (gg <= RS) gr *= pr;
+          else gt *= pr;
+        }
+        // 2^(G - G_r) before the segment's first token, and its inverse
+        float e = num * __builtin_amdgcn_rcpf(den), ei = den * __builtin_amdgcn_rcpf(num);
+        if (g == 0) {
+          sm.gref[c & 1][d] = gr;  // 2^(G_r): chunk start -> token 31
+          sm.gnr[c & 1][d] = gt;   // 2^(G_n - G_r): token 31 -> chunk end
+        }
+        uint16_t* kw = sm.k[c & 1];  // raw k, rewritten in place with W^
+        uint16_t* qh = sm.q[0];      // raw q, rewritten in place with Q^
+        uint16_t* kh = sm.q[1];      // K^
+#pragma unroll 1
+        for (int t4 = 0; t4 < SL; t4 += 4) {
+          const int t = g * SL + t4;
+          const f32x4 kk = KL::col4(kw, t, cb, lane);
+          const f32x4 qq = KL::col4(qh, t, cb, lane);
+          const f32x4 al = KL::col4(sm.w[0], t, cb, lane);
+          const f32x4 om = KL::col4(sm.w[1], t, cb, lane);
+          const f32x4 mu4 = *reinterpret_cast<const f32x4*>(&sm.galpha[c & 1][t]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float ph = fmaf(al[j] * al[j], p, om[j]);
+            const float u = mu4[j] * kk[j] * kk[j];
+            e *= al[j];
+            ei *= __builtin_amdgcn_rcpf(al[j]);
+            kh[KL::idx(t + j, d)] = f2bf(kk[j] * e);
+            qh[KL::idx(t + j, d)] = f2bf(qq[j] * e);
+            kw[KL::idx(t + j, d)] = f2bf(ph * kk[j] * ei);
+            p = ph * __builtin_amdgcn_rcpf(fmaf(u, ph, 1.f));
+          }
+        }
+        if (g == NSEG - 1) sm.acarry[d] = p;
+      }
+    };
+
+    // LDS operands of chunk c: keys, queries and write vectors (KDN: the
+    // decay-scaled K^, Q^ and W^)
+    auto opk = [&](int c) __attribute__((always_inline)) -> const uint16_t* {
+      return CD ? sm.q[1] : sm.k[c & 1];
+    };
+    auto opq = [&](int c) __attribute__((always_inline)) -> const uint16_t* {
+      return CD ? sm.q[0] : sm.q[c & 1];
+    };
+    auto opw = [&](int c) __attribute__((always_inline)) -> const uint16_t* {
+      return CD ? sm.k[c & 1] : HAS_W ? sm.w[c & 1] : sm.k[c & 1];
+    };
+
     // ---------------- producers: tile products of chunk c (raw, in registers)
     // Producer p owns the diagonal block p (L_pp in both orientations, M_pp)
     // and three of the twelve off-diagonal tiles (L or M of (bi, bj), bj < bi).
@@ -554,15 +728,16 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
     auto item_bj = [](int it) { const int pr = it >> 1; return pr < 1 ? 0 : pr < 3 ? pr - 1 : pr - 3; };
     f32x4 at = zero4(), an = zero4(), mt = zero4(), off[3] = {zero4(), zero4(), zero4()};
     auto tiles = [&](int c) __attribute__((always_inline)) {
-      const uint16_t* kb = sm.k[c & 1];
-      const uint16_t* wb = HAS_W ? sm.w[c & 1] : kb;
+      const uint16_t* kb = opk(c);
+      const uint16_t* qb = opq(c);
+      const uint16_t* wb = opw(c);
       const int p = pw;
       at = an = mt = zero4();
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const bf16x8 kp = KL::frag32(kb, fb, 16 * p, s);
-        const bf16x8 qp = KL::frag32(sm.q[c & 1], fb, 16 * p, s);
-        const bf16x8 wp = HAS_W ? KL::frag32(wb, fb, 16 * p, s) : kp;
+        const bf16x8 qp = KL::frag32(qb, fb, 16 * p, s);
+        const bf16x8 wp = HAS_W || CD ? KL::frag32(wb, fb, 16 * p, s) : kp;
         at = mfma32(wp, kp, at);  // lane: [j = 16p + 4 g4 + u][i = 16p + c16]
         mt = mfma32(wp, qp, mt);
         an = mfma32(kp, wp, an);  // lane: [i = 16p + 4 g4 + u][j = 16p + c16]
@@ -571,7 +746,7 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
       for (int k = 0; k < 3; ++k) {
         const int it = 3 * pw + k;  // wave-uniform
         const int bi = item_bi(it), bj = item_bj(it);
-        const uint16_t* xsrc = item_is_m(it) ? sm.q[c & 1] : kb;
+        const uint16_t* xsrc = item_is_m(it) ? qb : kb;
         f32x4 acc = zero4();
 #pragma unroll
         for (int s = 0; s < KS; ++s)
@@ -584,18 +759,40 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
     // the lane of each token t = 16 p + (lane % 16) that holds the diagonal
     // entry w_t . k_t of the raw product at (for KLA ||k_t||^2, exact: bf16
     // products are exact in fp32); also kap_t = 2^(E_p - G_t) c_t
+    // KDN: the column scales of the diagonal block in registers, for
+    // scale_diag in the same phase: cdi for token 16 p + c16 (the lane's row of
+    // an), cdj for tokens 16 p + 4 g4 + u (its columns of at and mt)
+    float cdi = 0.f;
+    f32x4 cdj = zero4();
     auto diag_gains = [&](int c, int n) __attribute__((always_inline)) {
+      if constexpr (CD) {
+        // the diagonal entry z_t of token t = 16 p + x sits in lane 16 (x / 4) + x,
+        // slot x % 4; the other lanes of the block fetch it with a lane shuffle
+        const float zs = c16 & 2 ? (c16 & 1 ? at[3] : at[2]) : (c16 & 1 ? at[1] : at[0]);
+        const float* rr = sm.geta[c & 1] + 16 * pw;
+        const float zi = __shfl(zs, 16 * (c16 >> 2) + c16);
+        cdi = 16 * pw + c16 < n ? __builtin_amdgcn_rcpf(rr[c16] + zi) : 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float zj = __shfl(zs, 20 * g4 + u);
+          cdj[u] = 16 * pw + 4 * g4 + u < n ? __builtin_amdgcn_rcpf(rr[4 * g4 + u] + zj) : 0.f;
+        }
+      }
       if (g4 == (c16 >> 2)) {
         const int u = c16 & 3, t = 16 * pw + c16;
         const float nk = u == 0 ? at[0] : u == 1 ? at[1] : u == 2 ? at[2] : at[3];
         // KLA step size eta / (||k||^2 + eps) (Kaczmarz Linear Attention §2.1),
         // with the hardware reciprocal; GDN: eta; stored write vectors: 1
         const float et = sm.geta[c & 1][t];
+        // KDN: nk = K^_t . W^_t = z_t, the sum of p_hat k^2 over the channels,
+        // and the gain's column scale is 1 / (r_t + z_t) (Kalman Delta
+        // Networks §2.4)
         float cv = GAIN == GAIN_KLA ? et * __builtin_amdgcn_rcpf(nk + a.g.eps)
-                 : GAIN == GAIN_GDN ? et : 1.f;
+                 : GAIN == GAIN_GDN ? et
+                 : CD ? cdi : 1.f;
         cv = t < n ? cv : 0.f;
         sm.cs[c & 1][t] = cv;
-        sm.kap[c & 1][t] = cv * exp2_hw(sm.g2[c & 1][16 * pw + 15] - sm.g2[c & 1][t]);
+        sm.kap[c & 1][t] = CD ? cv : cv * exp2_hw(sm.g2[c & 1][16 * pw + 15] - sm.g2[c & 1][t]);
       }
     };
 
@@ -611,17 +808,19 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
       const int p = pw;
       const float* g2 = sm.g2[c & 1];
       const float* cs = sm.cs[c & 1];
-      const float gd_i = g2[16 * p + c16], cd_i = cs[16 * p + c16];
-      const f32x4 gd_j = *reinterpret_cast<const f32x4*>(&g2[16 * p + 4 * g4]);
-      const f32x4 cd_j = *reinterpret_cast<const f32x4*>(&cs[16 * p + 4 * g4]);
+      // (KDN: the scales come from diag_gains' registers; the LDS copy is
+      // written in this same phase by other lanes)
+      const float gd_i = CD ? 0.f : g2[16 * p + c16], cd_i = CD ? 0.f : cs[16 * p + c16];
+      const f32x4 gd_j = CD ? zero4() : *reinterpret_cast<const f32x4*>(&g2[16 * p + 4 * g4]);
+      const f32x4 cd_j = CD ? zero4() : *reinterpret_cast<const f32x4*>(&cs[16 * p + 4 * g4]);
       // diagonal block p: at = A^T (row i = 16p + c16, columns j = 16p + 4 g4 + u),
       // an = A (transposed roles), mt = M_pp like at
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float f = exp2_hw(gd_i - gd_j[u]) * cd_j[u];
+        const float f = CD ? cdj[u] : exp2_hw(gd_i - gd_j[u]) * cd_j[u];
         at[u] = (4 * g4 + u < c16) ? at[u] * f : 0.f;
         mt[u] = (4 * g4 + u <= c16) ? mt[u] * f : 0.f;
-        an[u] = (c16 < 4 * g4 + u) ? an[u] * (exp2_hw(gd_j[u] - gd_i) * cd_i) : 0.f;
+        an[u] = (c16 < 4 * g4 + u) ? an[u] * (CD ? cdi : exp2_hw(gd_j[u] - gd_i) * cd_i) : 0.f;
       }
       *reinterpret_cast<u32x2*>(&sm.mp[(16 * p + c16) * PT + mcol(16 * p + 4 * g4)]) =
           u32x2{pack_bf2(mt[0], mt[1]), pack_bf2(mt[2], mt[3])};
@@ -634,7 +833,7 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
       for (int k = 0; k < 3; ++k) {
         const int it = 3 * pw + k;
         const float sg = item_is_m(it) ? 1.f : -1.f;
-        rho[k] = sg * exp2_hw(g2[16 * item_bi(it) + c16] - g2[16 * item_bj(it) + 15]);
+        rho[k] = CD ? sg : sg * exp2_hw(g2[16 * item_bi(it) + c16] - g2[16 * item_bj(it) + 15]);
         ko_j[k] = *reinterpret_cast<const f32x4*>(&sm.kap[c & 1][16 * item_bj(it) + 4 * g4]);
       }
 #pragma unroll
@@ -660,7 +859,8 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
     const int ud = c16 - 4 * g4;  // the slot of this lane's diagonal entry, if 0..3
     const f32x4 idm = {ud == 0 ? 1.f : 0.f, ud == 1 ? 1.f : 0.f, ud == 2 ? 1.f : 0.f, ud == 3 ? 1.f : 0.f};
     auto invert = [&](int c) __attribute__((always_inline)) {
-      if (pw == 1) sm.fs[lane] = sm.cs[c & 1][lane] * exp2_hw(sm.g2[c & 1][CH - 1] - sm.g2[c & 1][lane]);
+      if (pw == 1)
+        sm.fs[lane] = CD ? sm.cs[c & 1][lane] : sm.cs[c & 1][lane] * exp2_hw(sm.g2[c & 1][CH - 1] - sm.g2[c & 1][lane]);
       const s16x4 sat = pack16(at), san = pack16(an);
       const f32x4 A2 = mfma16(sat, san, zero4()), A2t = mfma16(san, sat, zero4());
       const s16x4 sA2 = pack16(A2), sA2t = pack16(A2t);
@@ -676,63 +876,22 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           u32x2{pack_bf2(tt_[0], tt_[1]), pack_bf2(tt_[2], tt_[3])};
     };
 
-    // ---------------- prologue: chunk 0 staged, its gains (and, REG, tiles)
-    if (nchunks > 0) {
-      // loaders: chunk 0 (REG: and the gates of chunk 1) into LDS; the loads
-      // the loop stages first (k, q, v and, PGDN, the gates of chunk 1)
-      if constexpr (LOAD) {
-        fetch_k(0);
-        fetch_q(0);
-        fetch_v(0);
-        fetch_gates(0);
-        stash_k(0, min(CH, T));
-        stash_q(0);
-        stash_v();
-        stash_gates(0, min(CH, T));
-        fetch_gates(1);
-        if constexpr (REG) stash_gates(1, ntok(1));
-        fetch_k(1);
-        fetch_q(1);
-        fetch_v(1);
-      }
-    }
-    __syncthreads();
-    if constexpr (REG) {
-      if (PROD && nchunks > 0) regains(0, min(CH, T));
-      __syncthreads();
-    }
-    if (nchunks > 0) {
-      if constexpr (REG) {
-        if constexpr (PROD) {
-          tiles(0);
-          diag_gains(0, min(CH, T));
-        }
-      } else if constexpr (!CONS) {
-        gains1(0);
-      }
-    }
-    __syncthreads();
-    if (nchunks > 0) {
-      if constexpr (REG) {
-        if constexpr (PROD) scale_diag(0);
-      } else if constexpr (!CONS) {
-        gains2(0);
-      }
-    }
-    __syncthreads();
-
-    for (int c = 0; c < nchunks; ++c) {
-      const int t0 = c * CH;
-      const int n = min(CH, T - t0);
-      const int n1 = min(CH, T - t0 - CH);  // tokens of chunk c + 1 (if any)
-      const uint16_t* kb = sm.k[c & 1];
-      const uint16_t* wb = HAS_W ? sm.w[c & 1] : kb;
-
-      // ================= P1 =================
-      f32x4 R[4], OQ[4];
-      float gn = 1.f;  // g_n of chunk c (gam is rewritten in P2 / P3)
+    // ---------------- consumers, per chunk c (bodies of the three phases)
+    f32x4 R[4], OQ[4];
+    float gn = 1.f;         // g_n of chunk c (gam is rewritten in P2 / P3)
+    bf16x8 U0, U1, F0, F1;  // U and diag(f) U, k-blocks 0 and 1 (tiles 0,1 and 2,3)
+    // P1: K S -> R = V - g K S, and (Q S)^T.  KDN: S is scaled per key channel
+    // by 2^(G_r) first (the operands carry the decay relative to token 31)
+    auto cons_p1 = [&](int c) __attribute__((always_inline)) {
       if constexpr (CONS) {
+        const uint16_t* kb = opk(c);
+        const uint16_t* qb = opq(c);
         // packed state: k-block s = tiles 2 s and 2 s + 1
+        if constexpr (CD) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            S[dt] = S[dt] * *reinterpret_cast<const f32x4*>(&sm.gref[c & 1][KL::sigma_channel(dt, g4, 0)]);
+        }
         bf16x8 Spk[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) Spk[s] = cat8(pack16(S[2 * s]), pack16(S[2 * s + 1]));
@@ -741,7 +900,7 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           kf[s] = KL::frag32(kb, fb, 0, s);
-          qf[s] = KL::frag32(sm.q[c & 1], fb, 0, s);
+          qf[s] = KL::frag32(qb, fb, 0, s);
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -750,7 +909,7 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
               kn[s] = KL::frag32(kb, fb, 16 * (rt + 1), s);
-              qn[s] = KL::frag32(sm.q[c & 1], fb, 16 * (rt + 1), s);
+              qn[s] = KL::frag32(qb, fb, 16 * (rt + 1), s);
             }
           }
           f32x4 ak = zero4(), aq = zero4();
@@ -769,37 +928,15 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           // R[t][c] = V[t][c] - g_t (K S)[t][c], rows t = 16 rt + 4 g4 + i
           const f32x4 vv = unpack16(read_tr(sm.v, PV, lane, 16 * rt, 16 * ct));
           const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.gam[c & 1][16 * rt + 4 * g4]);
-          R[rt] = vv - gt * ak;
+          R[rt] = CD ? vv - ak : vv - gt * ak;
           // (Q S)^T[c][t] scaled by g_t, token t = 16 rt + c16
-          OQ[rt] = aq * sm.gam[c & 1][16 * rt + c16];
+          OQ[rt] = CD ? aq : aq * sm.gam[c & 1][16 * rt + c16];
         }
         gn = sm.gam[c & 1][CH - 1];
-      } else if constexpr (LOAD) {
-        // k, q (PGDN: and the gates) of chunk c + 1 into LDS; the loads of k
-        // and of the gates of chunk c + 2
-        if (c + 1 < nchunks) {
-          stash_k(c + 1, n1);
-          stash_q(c + 1);
-          if constexpr (PG) stash_gates(c + 1, n1);
-        }
-        fetch_k(c + 2);
-        fetch_gates(c + 2);
-      } else {
-        if constexpr (!REG) {
-          tiles(c);
-          scale_diag(c);
-        }
-        // REG: the decay of chunk c + 1 from its staged gates
-        if constexpr (REG) {
-          if (c + 1 < nchunks) regains(c + 1, n1);
-        }
-        scale_off(c);
-        invert(c);
       }
-      __syncthreads();  // (1) L, M, (I + L_bb)^-1, f of chunk c ready
-
-      // ================= P2 =================
-      bf16x8 U0, U1, F0, F1;  // U and diag(f) U, k-blocks 0 and 1 (tiles 0,1 and 2,3)
+    };
+    // P2: solve -> U; O = g Q S + M U -> HBM
+    auto cons_p2 = [&](int c, int t0, int n) __attribute__((always_inline)) {
       if constexpr (CONS) {
         // U_b = (I + L_bb)^-1 (R_b - sum_{m<b} L_bm U_m)
         s16x4 Ub[4], Fb[4];
@@ -829,56 +966,252 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
         }
         // PGDN: v of chunk c + 1 into LDS (chunk c's was last read in P1),
         // the loads of q and v of chunk c + 2 (the loads of k go out in P3)
-      } else if constexpr (LOAD) {
-        // v of chunk c + 1 into LDS (chunk c's was last read in P1); the
-        // loads of q and v of chunk c + 2; PGDN: their share of pass 1
-        if (c + 1 < nchunks) stash_v();
-        fetch_q(c + 2);
-        fetch_v(c + 2);
-        if constexpr (PG) {
-          if (c + 1 < nchunks) gains1(c + 1);
-        }
-      } else {
-        if (c + 1 < nchunks) {
-          if constexpr (REG) {
-            tiles(c + 1);  // raw products, scaled in P3
-            diag_gains(c + 1, n1);
-          } else {
-            gains1(c + 1);  // PGDN statistic pass 1 (and the decay) of chunk c + 1
-          }
-        }
       }
-      __syncthreads();  // (2) REG: raw tiles of chunk c + 1; PGDN: its pass 1
-
-      // ================= P3 =================
+    };
+    // P3: S = g_n S + W^T diag(f) U
+    auto cons_p3 = [&](int c) __attribute__((always_inline)) {
       if constexpr (CONS) {
+        const uint16_t* wb = opw(c);
         // S_dt = g_n S_dt + W^T diag(f) U: A = W^T read transposed from the
         // [token][d_k] rows of chunk c (tokens 32 s + 4 g4 + j and + 16)
         auto update = [&](int dt) __attribute__((always_inline)) {
-          f32x4 acc = S[dt] * gn;
+          f32x4 acc = CD ? S[dt] : S[dt] * gn;
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
             const bf16x8 wa = cat8(KL::read_tr(wb, trb, 32 * s, dt >> 1, dt & 1),
                                    KL::read_tr(wb, trb, 32 * s + 16, dt >> 1, dt & 1));
             acc = mfma32(wa, s == 0 ? F0 : F1, acc);
           }
-          S[dt] = acc;
+          // KDN: S carries 2^(G_r) since P1; 2^(G_n - G_r) completes the decay
+          S[dt] = CD ? acc * *reinterpret_cast<const f32x4*>(&sm.gnr[c & 1][KL::sigma_channel(dt, g4, 0)]) : acc;
         };
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) update(dt);
-      } else if constexpr (LOAD) {
-        // REG: the gates of chunk c + 2 into LDS (their parity's last
-        // readers, regains and diag_gains of chunk c, are done); PGDN: their
-        // share of pass 2
-        if constexpr (REG) stash_gates(c + 2, ntok(c + 2));
-        else if (c + 1 < nchunks) gains2(c + 1);
-      } else {
-        if (c + 1 < nchunks) {
-          if constexpr (REG) scale_diag(c + 1);
-          else gains2(c + 1);  // PGDN pass 2: the write vectors of chunk c + 1
+      }
+    };
+
+    if constexpr (CD) {
+      // ---------------- KDN, per-channel decay: four phases per chunk c
+      //   P1  consumers: K^ S, Q^ S of c.  producers: scale_off and the
+      //       inverses of c.  loaders: k, alpha, omega, r of c + 1 into LDS,
+      //       their loads for c + 2.
+      //   P2  consumers: solve and output of c.  loaders: q, v of c + 1 into
+      //       LDS, their loads for c + 2.  producers and loaders: scan pass 1
+      //       of c + 1.
+      //   P3  consumers: state update of c.  producers and loaders: scan
+      //       pass 2 of c + 1 (writes K^, Q^, W^ of c + 1).
+      //   P4  producers: the raw tile products of c + 1, its column scales
+      //       from their diagonal, and its scaled diagonal blocks.
+      if (nchunks > 0) {
+        if constexpr (LOAD) {
+          const int n0 = ntok(0);
+          fetch_k(0);
+          fetch_q(0);
+          fetch_v(0);
+          fetch_ao(0);
+          fetch_gates(0);
+          stash_k(0, n0);
+          stash_q(0);
+          stash_v();
+          stash_ao(n0);
+          stash_gates(0, n0);
+          fetch_k(1);
+          fetch_ao(1);
+          fetch_gates(1);
+          fetch_q(1);
+          fetch_v(1);
         }
       }
-      __syncthreads();  // (3) chunk c + 1: tiles (REG) or gains (PGDN) ready; S updated
+      __syncthreads();
+      if constexpr (!CONS) {
+        if (nchunks > 0) cd_pass1(0);
+      }
+      __syncthreads();
+      if constexpr (!CONS) {
+        if (nchunks > 0) cd_pass2(0);
+      }
+      __syncthreads();
+      if constexpr (PROD) {
+        if (nchunks > 0) {
+          tiles(0);
+          diag_gains(0, ntok(0));
+          scale_diag(0);
+        }
+      }
+      __syncthreads();
+      for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * CH;
+        const int n = min(CH, T - t0);
+        const int n1 = ntok(c + 1);
+        // P1
+        if constexpr (CONS) {
+          cons_p1(c);
+        } else if constexpr (LOAD) {
+          if (c + 1 < nchunks) {
+            stash_k(c + 1, n1);
+            stash_ao(n1);
+            stash_gates(c + 1, n1);
+          }
+          fetch_k(c + 2);
+          fetch_ao(c + 2);
+          fetch_gates(c + 2);
+        } else {
+          scale_off(c);
+          invert(c);
+        }
+        __syncthreads();  // (1) L, M, (I + L_bb)^-1, f of chunk c ready
+        // P2
+        if constexpr (CONS) {
+          cons_p2(c, t0, n);
+        } else {
+          if constexpr (LOAD) {
+            if (c + 1 < nchunks) {
+              stash_q(c + 1);
+              stash_v();
+            }
+            fetch_q(c + 2);
+            fetch_v(c + 2);
+          }
+          if (c + 1 < nchunks) cd_pass1(c + 1);
+        }
+        __syncthreads();  // (2) pass 1 of chunk c + 1 done; chunk c's solve done
+        // P3
+        if constexpr (CONS) {
+          cons_p3(c);
+        } else {
+          if (c + 1 < nchunks) cd_pass2(c + 1);
+        }
+        __syncthreads();  // (3) K^, Q^, W^ of chunk c + 1 ready; S updated
+        // P4
+        if constexpr (PROD) {
+          if (c + 1 < nchunks) {
+            tiles(c + 1);
+            diag_gains(c + 1, n1);
+            scale_diag(c + 1);
+          }
+        }
+        __syncthreads();  // (4) column scales and diagonal blocks of chunk c + 1 ready
+      }
+    } else {
+      // ---------------- prologue: chunk 0 staged, its gains (and, REG, tiles)
+      if (nchunks > 0) {
+        // loaders: chunk 0 (REG: and the gates of chunk 1) into LDS; the loads
+        // the loop stages first (k, q, v and, PGDN, the gates of chunk 1)
+        if constexpr (LOAD) {
+          fetch_k(0);
+          fetch_q(0);
+          fetch_v(0);
+          fetch_gates(0);
+          stash_k(0, min(CH, T));
+          stash_q(0);
+          stash_v();
+          stash_gates(0, min(CH, T));
+          fetch_gates(1);
+          if constexpr (REG) stash_gates(1, ntok(1));
+          fetch_k(1);
+          fetch_q(1);
+          fetch_v(1);
+        }
+      }
+      __syncthreads();
+      if constexpr (REG) {
+        if (PROD && nchunks > 0) regains(0, min(CH, T));
+        __syncthreads();
+      }
+      if (nchunks > 0) {
+        if constexpr (REG) {
+          if constexpr (PROD) {
+            tiles(0);
+            diag_gains(0, min(CH, T));
+          }
+        } else if constexpr (!CONS) {
+          gains1(0);
+        }
+      }
+      __syncthreads();
+      if (nchunks > 0) {
+        if constexpr (REG) {
+          if constexpr (PROD) scale_diag(0);
+        } else if constexpr (!CONS) {
+          gains2(0);
+        }
+      }
+      __syncthreads();
+
+      for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * CH;
+        const int n = min(CH, T - t0);
+        const int n1 = min(CH, T - t0 - CH);  // tokens of chunk c + 1 (if any)
+
+        // ================= P1 =================
+        if constexpr (CONS) {
+          cons_p1(c);
+        } else if constexpr (LOAD) {
+          // k, q (PGDN: and the gates) of chunk c + 1 into LDS; the loads of k
+          // and of the gates of chunk c + 2
+          if (c + 1 < nchunks) {
+            stash_k(c + 1, n1);
+            stash_q(c + 1);
+            if constexpr (PG) stash_gates(c + 1, n1);
+          }
+          fetch_k(c + 2);
+          fetch_gates(c + 2);
+        } else {
+          if constexpr (!REG) {
+            tiles(c);
+            scale_diag(c);
+          }
+          // REG: the decay of chunk c + 1 from its staged gates
+          if constexpr (REG) {
+            if (c + 1 < nchunks) regains(c + 1, n1);
+          }
+          scale_off(c);
+          invert(c);
+        }
+        __syncthreads();  // (1) L, M, (I + L_bb)^-1, f of chunk c ready
+
+        // ================= P2 =================
+        if constexpr (CONS) {
+          cons_p2(c, t0, n);
+        } else if constexpr (LOAD) {
+          // v of chunk c + 1 into LDS (chunk c's was last read in P1); the
+          // loads of q and v of chunk c + 2; PGDN: their share of pass 1
+          if (c + 1 < nchunks) stash_v();
+          fetch_q(c + 2);
+          fetch_v(c + 2);
+          if constexpr (PG) {
+            if (c + 1 < nchunks) gains1(c + 1);
+          }
+        } else {
+          if (c + 1 < nchunks) {
+            if constexpr (REG) {
+              tiles(c + 1);  // raw products, scaled in P3
+              diag_gains(c + 1, n1);
+            } else {
+              gains1(c + 1);  // PGDN statistic pass 1 (and the decay) of chunk c + 1
+            }
+          }
+        }
+        __syncthreads();  // (2) REG: raw tiles of chunk c + 1; PGDN: its pass 1
+
+        // ================= P3 =================
+        if constexpr (CONS) {
+          cons_p3(c);
+        } else if constexpr (LOAD) {
+          // REG: the gates of chunk c + 2 into LDS (their parity's last
+          // readers, regains and diag_gains of chunk c, are done); PGDN: their
+          // share of pass 2
+          if constexpr (REG) stash_gates(c + 2, ntok(c + 2));
+          else if (c + 1 < nchunks) gains2(c + 1);
+        } else {
+          if (c + 1 < nchunks) {
+            if constexpr (REG) scale_diag(c + 1);
+            else gains2(c + 1);  // PGDN pass 2: the write vectors of chunk c + 1
+          }
+        }
+        __syncthreads();  // (3) chunk c + 1: tiles (REG) or gains (PGDN) ready; S updated
+      }
+
     }
 
     // ---------------- final state and statistic
@@ -891,7 +1224,7 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           for (int i = 0; i < 4; ++i) base[(KL::sigma_channel(dt, 0, i)) * a.dv] = S[dt][i];
       }
     } else if constexpr (PROD) {
-      if (PG && a.aux_final && slice == 0 && ptid < DK)
+      if ((PG || CD) && a.aux_final && slice == 0 && ptid < DK)
         a.aux_final[static_cast<long>(bh) * DK + ptid] = sm.acarry[ptid];
     }
   };
@@ -935,6 +1268,12 @@ hipError_t launch_chunk_fwd_bf16_scalar(const ChunkArgs& a, int gain, hipStream_
   }
   DN_WS(64)
 #undef DN_WS
+}
+
+// bf16 io, KDN with per-channel decay.
+hipError_t launch_chunk_fwd_bf16_kdn(const ChunkArgs& a, hipStream_t st) {
+  if (a.dk == 128) return launch_ws_one<128, GAIN_KDN>(a, st);
+  return launch_ws_one<64, GAIN_KDN>(a, st);
 }
 
 }  // namespace dn

@@ -77,8 +77,8 @@ def test_bf16_other_head_dims(dk, dv):
 
 
 # d_k = 64 changes the work split of the per-channel scans: the PGDN
-# statistic runs in eight 8-token segments, the KDN channel-decay scan on one
-# thread per channel; ragged lengths cover the partial last chunk
+# statistic and the KDN channel-decay variance both run in eight 8-token
+# segments per channel; ragged lengths cover the partial last chunk
 @pytest.mark.parametrize("T", [37, 200])
 @pytest.mark.parametrize("dv", [64, 128])
 @pytest.mark.parametrize("gain,decay,keys", [("gdn", "scalar", "unit"), ("pgdn", "scalar", "unit"),
