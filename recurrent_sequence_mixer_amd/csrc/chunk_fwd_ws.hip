@@ -718,15 +718,25 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
       return CD ? sm.k[c & 1] : HAS_W ? sm.w[c & 1] : sm.k[c & 1];
     };
 
-    // ---------------- producers: tile products of chunk c (raw, in registers)
-    // Producer p owns the diagonal block p (L_pp in both orientations, M_pp)
-    // and three of the twelve off-diagonal tiles (L or M of (bi, bj), bj < bi).
-    // item it: kind it % 2 (0: L, 1: M) of tile (bi, bj) = pair it / 2 of
-    // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+    // ---------------- producers and loaders: tile products of chunk c (raw,
+    // in registers).  Producer p owns the diagonal block p (L_pp in both
+    // orientations, M_pp) and, for the gains formed from the staging registers,
+    // one of the twelve off-diagonal tiles (L or M of (bi, bj), bj < bi) while
+    // loader l takes two: item it = 3 p (producer p), 3 l + 1 and 3 l + 2
+    // (loader l); otherwise producer p takes items 3 p .. 3 p + 2.  Item it is
+    // of kind it % 2 (0: L, 1: M)
+    // and covers tile (bi, bj) = pair it / 2 of (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
     auto item_is_m = [](int it) { return (it & 1) != 0; };
     auto item_bi = [](int it) { const int pr = it >> 1; return pr < 1 ? 1 : pr < 3 ? 2 : 3; };
     auto item_bj = [](int it) { const int pr = it >> 1; return pr < 1 ? 0 : pr < 3 ? pr - 1 : pr - 3; };
-    f32x4 at = zero4(), an = zero4(), mt = zero4(), off[3] = {zero4(), zero4(), zero4()};
+    // (REG; PGDN and KDN, whose loaders are busy with the scans: three items
+    // per producer, none for the loaders)
+    constexpr int NIT = REG ? (LOAD ? 2 : 1) : (LOAD ? 0 : 3);  // off-diagonal items of this wavefront
+    const int lw = wave - 8;  // loaders: wavefront index
+    auto item_of = [&](int k) { return REG ? (PROD ? 3 * pw : 3 * lw + 1 + k) : 3 * pw + k; };  // wave-uniform
+    f32x4 at = zero4(), an = zero4(), mt = zero4(), off[NIT > 0 ? NIT : 1];
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) off[k] = zero4();
     auto tiles = [&](int c) __attribute__((always_inline)) {
       const uint16_t* kb = opk(c);
       const uint16_t* qb = opq(c);
@@ -742,9 +752,14 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
         mt = mfma32(wp, qp, mt);
         an = mfma32(kp, wp, an);  // lane: [i = 16p + 4 g4 + u][j = 16p + c16]
       }
+    };
+    auto tiles_off = [&](int c) __attribute__((always_inline)) {
+      const uint16_t* kb = opk(c);
+      const uint16_t* qb = opq(c);
+      const uint16_t* wb = opw(c);
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const int it = 3 * pw + k;  // wave-uniform
+      for (int k = 0; k < NIT; ++k) {
+        const int it = item_of(k);
         const int bi = item_bi(it), bj = item_bj(it);
         const uint16_t* xsrc = item_is_m(it) ? qb : kb;
         f32x4 acc = zero4();
@@ -827,18 +842,18 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
     };
     auto scale_off = [&](int c) __attribute__((always_inline)) {
       const float* g2 = sm.g2[c & 1];
-      float rho[3];
-      f32x4 ko_j[3];
+      float rho[NIT > 0 ? NIT : 1];
+      f32x4 ko_j[NIT > 0 ? NIT : 1];
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const int it = 3 * pw + k;
+      for (int k = 0; k < NIT; ++k) {
+        const int it = item_of(k);
         const float sg = item_is_m(it) ? 1.f : -1.f;
         rho[k] = CD ? sg : sg * exp2_hw(g2[16 * item_bi(it) + c16] - g2[16 * item_bj(it) + 15]);
         ko_j[k] = *reinterpret_cast<const f32x4*>(&sm.kap[c & 1][16 * item_bj(it) + 4 * g4]);
       }
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const int it = 3 * pw + k;
+      for (int k = 0; k < NIT; ++k) {
+        const int it = item_of(k);
         const bool m = item_is_m(it);
         f32x4 val;
 #pragma unroll
@@ -895,6 +910,18 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
         bf16x8 Spk[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) Spk[s] = cat8(pack16(S[2 * s]), pack16(S[2 * s + 1]));
+        // the value tiles and decays of all four row tiles are read first: LDS
+        // reads complete in order, so a wait for one read issued after the
+        // next row tile's fragments would also wait for those fragments
+        s16x4 vt[4];
+        f32x4 gt[4];
+        float go[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          vt[rt] = read_tr(sm.v, PV, lane, 16 * rt, 16 * ct);
+          gt[rt] = *reinterpret_cast<const f32x4*>(&sm.gam[c & 1][16 * rt + 4 * g4]);
+          go[rt] = sm.gam[c & 1][16 * rt + c16];
+        }
         // K and Q fragments of row tile rt + 1 are read while rt multiplies
         bf16x8 kf[KS], qf[KS];
 #pragma unroll
@@ -926,11 +953,10 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
             }
           }
           // R[t][c] = V[t][c] - g_t (K S)[t][c], rows t = 16 rt + 4 g4 + i
-          const f32x4 vv = unpack16(read_tr(sm.v, PV, lane, 16 * rt, 16 * ct));
-          const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.gam[c & 1][16 * rt + 4 * g4]);
-          R[rt] = CD ? vv - ak : vv - gt * ak;
+          const f32x4 vv = unpack16(vt[rt]);
+          R[rt] = CD ? vv - ak : vv - gt[rt] * ak;
           // (Q S)^T[c][t] scaled by g_t, token t = 16 rt + c16
-          OQ[rt] = CD ? aq : aq * sm.gam[c & 1][16 * rt + c16];
+          OQ[rt] = CD ? aq : aq * go[rt];
         }
         gn = sm.gam[c & 1][CH - 1];
       }
@@ -938,16 +964,25 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
     // P2: solve -> U; O = g Q S + M U -> HBM
     auto cons_p2 = [&](int c, int t0, int n) __attribute__((always_inline)) {
       if constexpr (CONS) {
-        // U_b = (I + L_bb)^-1 (R_b - sum_{m<b} L_bm U_m)
-        s16x4 Ub[4], Fb[4];
+        // U_b = (I + L_bb)^-1 (R_b - sum_{m<b} L_bm U_m); every operand of the
+        // chain is read up front (in the order it is used)
+        s16x4 Ub[4], Fb[4], lt[6], tv[4];
+        f32x4 fv[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+#pragma unroll
+          for (int m = 0; m < b; ++m) lt[b * (b - 1) / 2 + m] = frag16(sm.ln + 16 * b * PT + 16 * m, PT, lane);
+          tv[b] = frag16(sm.tb + 16 * b * P16, P16, lane);
+          fv[b] = *reinterpret_cast<const f32x4*>(&sm.fs[16 * b + 4 * g4]);
+        }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           f32x4 acc = R[b];
 #pragma unroll
-          for (int m = 0; m < b; ++m) acc = mfma16(frag16(sm.ln + 16 * b * PT + 16 * m, PT, lane), Ub[m], acc);
-          const f32x4 u = mfma16(frag16(sm.tb + 16 * b * P16, P16, lane), pack16(acc), zero4());
+          for (int m = 0; m < b; ++m) acc = mfma16(lt[b * (b - 1) / 2 + m], Ub[m], acc);
+          const f32x4 u = mfma16(tv[b], pack16(acc), zero4());
           Ub[b] = pack16(u);
-          Fb[b] = pack16(u * *reinterpret_cast<const f32x4*>(&sm.fs[16 * b + 4 * g4]));
+          Fb[b] = pack16(u * fv[b]);
         }
         U0 = cat8(Ub[0], Ub[1]);
         U1 = cat8(Ub[2], Ub[3]);
@@ -1034,6 +1069,7 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
       if constexpr (PROD) {
         if (nchunks > 0) {
           tiles(0);
+          tiles_off(0);
           diag_gains(0, ntok(0));
           scale_diag(0);
         }
@@ -1086,6 +1122,7 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
         if constexpr (PROD) {
           if (c + 1 < nchunks) {
             tiles(c + 1);
+            tiles_off(c + 1);
             diag_gains(c + 1, n1);
             scale_diag(c + 1);
           }
@@ -1122,7 +1159,10 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
         if constexpr (REG) {
           if constexpr (PROD) {
             tiles(0);
+            tiles_off(0);
             diag_gains(0, min(CH, T));
+          } else if constexpr (LOAD) {
+            tiles_off(0);
           }
         } else if constexpr (!CONS) {
           gains1(0);
@@ -1156,9 +1196,12 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           }
           fetch_k(c + 2);
           fetch_gates(c + 2);
+          // REG: their off-diagonal tiles of chunk c
+          if constexpr (REG) scale_off(c);
         } else {
           if constexpr (!REG) {
             tiles(c);
+            tiles_off(c);
             scale_diag(c);
           }
           // REG: the decay of chunk c + 1 from its staged gates
@@ -1181,11 +1224,14 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           fetch_v(c + 2);
           if constexpr (PG) {
             if (c + 1 < nchunks) gains1(c + 1);
+          } else {
+            if (c + 1 < nchunks) tiles_off(c + 1);  // raw products, scaled in P1 of c + 1
           }
         } else {
           if (c + 1 < nchunks) {
             if constexpr (REG) {
-              tiles(c + 1);  // raw products, scaled in P3
+              tiles(c + 1);  // raw products, scaled in P3 (diagonal) and P1 of c + 1
+              tiles_off(c + 1);
               diag_gains(c + 1, n1);
             } else {
               gains1(c + 1);  // PGDN statistic pass 1 (and the decay) of chunk c + 1
