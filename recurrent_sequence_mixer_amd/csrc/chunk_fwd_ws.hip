@@ -98,14 +98,6 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// PGDN write scale on the hardware log2 / rcp / exp2 (Preconditioned DeltaNet
-// §2.4, Eq. 9): B(A) = exp(-ln(x) s), s = r / (1 + |r|), r = ln A - mu.
-__device__ __forceinline__ float pgdn_scale_hw(float A, float mu, float log2x) {
-  const float r = log2_hw(A) * 0.69314718055994531f - mu;
-  const float s = r * __builtin_amdgcn_rcpf(1.0f + fabsf(r));
-  return exp2_hw(-log2x * s);
-}
-
 // Raw buffer resource (stride 0, 32-bit data format) over nbytes from base:
 // loads at offsets >= nbytes return 0 and stores there are dropped, which
 // zero-fills the rows of a partial chunk and masks its output rows.
@@ -581,7 +573,13 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           At = sm.ah[d];
           for (int gg = 1; gg < g; ++gg) At = fmaf(sm.segp[gg], At, sm.ah[gg * DK + d]);
         }
-        const float mu = a.g.mu_log[h];
+        // the write scale B(A) = exp(-ln(x) s), s = r / (1 + |r|), r = ln A - mu
+        // (Preconditioned DeltaNet §2.4, Eq. 9) on the hardware log2 / rcp /
+        // exp2: B = 2^(y / (1 + |r|)) with y = -log2(x) r one fma of log2 A,
+        // and 1 + |r| = 1 + |y| / log2(x)
+        const float l2x = a.g.log2x;
+        const float cy = -l2x * 0.69314718055994531f, y0 = l2x * a.g.mu_log[h];
+        const float il2x = __builtin_amdgcn_rcpf(l2x);
         const int cb = d & ~63;
 #pragma unroll
         for (int t4 = 0; t4 < SL; t4 += 4) {
@@ -590,10 +588,20 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           const f32x4 ap4 = *reinterpret_cast<const f32x4*>(&sm.ap[t]);
           const f32x4 bp4 = *reinterpret_cast<const f32x4*>(&sm.bp[t]);
           const f32x4 et4 = *reinterpret_cast<const f32x4*>(&sm.eta[t]);
+          // two tokens per conversion; the halves go to their two rows
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            At = pgdn_stat(At, ap4[j], bp4[j], kk[j]);
-            wb[KL::idx(t + j, d)] = f2bf(et4[j] * pgdn_scale_hw(At, mu, a.g.log2x) * kk[j]);
+          for (int j = 0; j < 4; j += 2) {
+            float xw[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              At = pgdn_stat(At, ap4[j + h2], bp4[j + h2], kk[j + h2]);
+              const float y = fmaf(log2_hw(At), cy, y0);
+              const float bs = exp2_hw(y * __builtin_amdgcn_rcpf(fmaf(fabsf(y), il2x, 1.0f)));
+              xw[h2] = et4[j + h2] * bs * kk[j + h2];
+            }
+            const uint32_t pw2 = pack_bf2(xw[0], xw[1]);
+            wb[KL::idx(t + j, d)] = static_cast<uint16_t>(pw2);
+            wb[KL::idx(t + j + 1, d)] = static_cast<uint16_t>(pw2 >> 16);
           }
         }
         // the carried statistic is read again only by the next chunk's pass 1
@@ -673,8 +681,8 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           if (gg <= RS) gr *= pr;
           else gt *= pr;
         }
-        // 2^(G - G_r) before the segment's first token, and its inverse
-        float e = num * __builtin_amdgcn_rcpf(den), ei = den * __builtin_amdgcn_rcpf(num);
+        // 2^(G - G_r) before the segment's first token
+        float e = num * __builtin_amdgcn_rcpf(den);
         if (g == 0) {
           sm.gref[c & 1][d] = gr;  // 2^(G_r): chunk start -> token 31
           sm.gnr[c & 1][d] = gt;   // 2^(G_n - G_r): token 31 -> chunk end
@@ -690,16 +698,31 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           const f32x4 al = KL::col4(sm.w[0], t, cb, lane);
           const f32x4 om = KL::col4(sm.w[1], t, cb, lane);
           const f32x4 mu4 = *reinterpret_cast<const f32x4*>(&sm.galpha[c & 1][t]);
+          // two tokens per step: one conversion packs the pair, whose halves
+          // go to their two rows
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float ph = fmaf(al[j] * al[j], p, om[j]);
-            const float u = mu4[j] * kk[j] * kk[j];
-            e *= al[j];
-            ei *= __builtin_amdgcn_rcpf(al[j]);
-            kh[KL::idx(t + j, d)] = f2bf(kk[j] * e);
-            qh[KL::idx(t + j, d)] = f2bf(qq[j] * e);
-            kw[KL::idx(t + j, d)] = f2bf(ph * kk[j] * ei);
-            p = ph * __builtin_amdgcn_rcpf(fmaf(u, ph, 1.f));
+          for (int j = 0; j < 4; j += 2) {
+            float xk[2], xq[2], xw[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const int jj = j + h2;
+              const float ph = fmaf(al[jj] * al[jj], p, om[jj]);
+              const float pk = ph * kk[jj];
+              e *= al[jj];
+              xk[h2] = kk[jj] * e;
+              xq[h2] = qq[jj] * e;
+              xw[h2] = pk * __builtin_amdgcn_rcpf(e);
+              // p_hat / (1 + u p_hat) with u p_hat = (mu / r) k (p_hat k)
+              p = ph * __builtin_amdgcn_rcpf(fmaf(mu4[jj] * kk[jj], pk, 1.f));
+            }
+            const uint32_t pkh = pack_bf2(xk[0], xk[1]), pqh = pack_bf2(xq[0], xq[1]),
+                           pkw = pack_bf2(xw[0], xw[1]);
+            kh[KL::idx(t + j, d)] = static_cast<uint16_t>(pkh);
+            kh[KL::idx(t + j + 1, d)] = static_cast<uint16_t>(pkh >> 16);
+            qh[KL::idx(t + j, d)] = static_cast<uint16_t>(pqh);
+            qh[KL::idx(t + j + 1, d)] = static_cast<uint16_t>(pqh >> 16);
+            kw[KL::idx(t + j, d)] = static_cast<uint16_t>(pkw);
+            kw[KL::idx(t + j + 1, d)] = static_cast<uint16_t>(pkw >> 16);
           }
         }
         if (g == NSEG - 1) sm.acarry[d] = p;
@@ -1031,12 +1054,12 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
       //       inverses of c.  loaders: k, alpha, omega, r of c + 1 into LDS,
       //       their loads for c + 2.
       //   P2  consumers: solve and output of c.  loaders: q, v of c + 1 into
-      //       LDS, their loads for c + 2.  producers and loaders: scan pass 1
-      //       of c + 1.
+      //       LDS.  producers and loaders: scan pass 1 of c + 1.
       //   P3  consumers: state update of c.  producers and loaders: scan
       //       pass 2 of c + 1 (writes K^, Q^, W^ of c + 1).
       //   P4  producers: the raw tile products of c + 1, its column scales
-      //       from their diagonal, and its scaled diagonal blocks.
+      //       from their diagonal, and its scaled diagonal blocks.  loaders:
+      //       the loads of q, v of c + 2.
       if (nchunks > 0) {
         if constexpr (LOAD) {
           const int n0 = ntok(0);
@@ -1105,8 +1128,6 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
               stash_q(c + 1);
               stash_v();
             }
-            fetch_q(c + 2);
-            fetch_v(c + 2);
           }
           if (c + 1 < nchunks) cd_pass1(c + 1);
         }
@@ -1126,6 +1147,11 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
             diag_gains(c + 1, n1);
             scale_diag(c + 1);
           }
+        } else if constexpr (LOAD) {
+          // the loads of q and v of chunk c + 2 (staged in P2 of chunk c + 1),
+          // issued here, where the loaders have no scan work to hold back
+          fetch_q(c + 2);
+          fetch_v(c + 2);
         }
         __syncthreads();  // (4) column scales and diagonal blocks of chunk c + 1 ready
       }
