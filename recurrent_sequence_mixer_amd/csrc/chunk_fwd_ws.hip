@@ -743,20 +743,20 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
 
     // ---------------- producers and loaders: tile products of chunk c (raw,
     // in registers).  Producer p owns the diagonal block p (L_pp in both
-    // orientations, M_pp) and, for the gains formed from the staging registers,
-    // one of the twelve off-diagonal tiles (L or M of (bi, bj), bj < bi) while
-    // loader l takes two: item it = 3 p (producer p), 3 l + 1 and 3 l + 2
-    // (loader l); otherwise producer p takes items 3 p .. 3 p + 2.  Item it is
-    // of kind it % 2 (0: L, 1: M)
+    // orientations, M_pp) and items 3 p .. 3 p + NIT_P - 1 of the twelve
+    // off-diagonal tiles (L or M of (bi, bj), bj < bi), loader l items
+    // 3 l + NIT_P .. 3 l + 2: the loaders take what their other work (the
+    // statistic scans of PGDN and KDN) leaves room for.  Item it is of kind
+    // it % 2 (0: L, 1: M)
     // and covers tile (bi, bj) = pair it / 2 of (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
     auto item_is_m = [](int it) { return (it & 1) != 0; };
     auto item_bi = [](int it) { const int pr = it >> 1; return pr < 1 ? 1 : pr < 3 ? 2 : 3; };
     auto item_bj = [](int it) { const int pr = it >> 1; return pr < 1 ? 0 : pr < 3 ? pr - 1 : pr - 3; };
-    // (REG; PGDN and KDN, whose loaders are busy with the scans: three items
-    // per producer, none for the loaders)
-    constexpr int NIT = REG ? (LOAD ? 2 : 1) : (LOAD ? 0 : 3);  // off-diagonal items of this wavefront
+    // Items per producer: REG 1, PGDN 2, KDN 3; the loaders take the rest
+    constexpr int NIT_P = REG ? 1 : PG ? 2 : 3;
+    constexpr int NIT = LOAD ? 3 - NIT_P : NIT_P;  // off-diagonal items of this wavefront
     const int lw = wave - 8;  // loaders: wavefront index
-    auto item_of = [&](int k) { return REG ? (PROD ? 3 * pw : 3 * lw + 1 + k) : 3 * pw + k; };  // wave-uniform
+    auto item_of = [&](int k) { return PROD ? 3 * pw + k : 3 * lw + NIT_P + k; };  // wave-uniform
     f32x4 at = zero4(), an = zero4(), mt = zero4(), off[NIT > 0 ? NIT : 1];
 #pragma unroll
     for (int k = 0; k < NIT; ++k) off[k] = zero4();
@@ -1222,8 +1222,9 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           }
           fetch_k(c + 2);
           fetch_gates(c + 2);
-          // REG: their off-diagonal tiles of chunk c
-          if constexpr (REG) scale_off(c);
+          // their off-diagonal tiles of chunk c (PGDN: the raw products too)
+          if constexpr (PG) tiles_off(c);
+          scale_off(c);
         } else {
           if constexpr (!REG) {
             tiles(c);
