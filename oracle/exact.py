@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
 
 Tiny single-head inputs as Python lists of fractions.Fraction.  Gains whose
 arithmetic stays rational are supported: kla, gdn, kdn and explicit (pgdn
-takes log/exp and is pinned in fp64 instead).
+takes log/exp and is pinned in fp64 instead); kdn_iso as well, with
+scalar omega_t and the variance b as a one-element list.
 
 token_recurrence follows the same five steps as oracle.recurrence.forward
 (Kaczmarz Linear Attention §2.1; Kalman Delta Networks §1.1 and §2.4-2.5).
@@ -46,7 +47,7 @@ def gains(k: Mat, gain: str, alpha, eta=None, eps=F(0), omega=None, r=None,
     """Per-token write vectors w_t (and the KDN variance after each token)."""
     T, dk = len(k), len(k[0])
     ws, ps = [], []
-    p = list(p0) if p0 is not None else [F(1)] * dk
+    p = list(p0) if p0 is not None else [F(1)] * (1 if gain == "kdn_iso" else dk)
     for t in range(T):
         kt = k[t]
         a = alpha[t] if isinstance(alpha[t], list) else [alpha[t]] * dk
@@ -61,6 +62,15 @@ def gains(k: Mat, gain: str, alpha, eta=None, eps=F(0), omega=None, r=None,
             ws.append([p_hat[i] * kt[i] / (r[t] + z) for i in range(dk)])
             u = [mu_info / r[t] * kt[i] * kt[i] for i in range(dk)]
             p = [p_hat[i] / (1 + u[i] * p_hat[i]) for i in range(dk)]
+            ps.append(list(p))
+        elif gain == "kdn_iso":
+            # Kalman Delta Networks §2.7, Eq. 40 (p holds the one variance b)
+            b_hat = sum((x * x for x in a), F(0)) / dk * p[0] + omega[t]
+            n = _dot(kt, kt)
+            beta = b_hat / (r[t] + b_hat * n)
+            ws.append([beta * x for x in kt])
+            u = mu_info * n / (dk * r[t])
+            p = [b_hat / (1 + u * b_hat)]
             ps.append(list(p))
         elif gain == "explicit":
             ws.append(list(w[t]))

@@ -26,6 +26,13 @@ For every token t, per head, in this order:
                  u = (mu_info / r) k^2;  p_t = p_hat / (1 + u p_hat)
                  (Kalman Delta Networks §2.4 Eqs. 23-30, §2.5; kappa uses
                  p_hat, and p_t is formed after the write)
+       kdn_iso   a = mean over channels of alpha^2;  b_hat = a b_{t-1} + omega;
+                 n = ||k||^2;  w = beta k,  beta = b_hat / (r + b_hat n);  then
+                 u = mu_info n / (d_k r);  b_t = b_hat / (1 + u b_hat)
+                 (Kalman Delta Networks §2.7, Eq. 40: one variance b per head,
+                 predicted by the trace projection of D (b I) D + omega I and
+                 updated by the reverse-KL projection; omega and r are
+                 scalars per token)
        explicit  w = w_t given by the caller (used for the exact ATK /
                  ridge special case, Preconditioned DeltaNet §2.2)
   3. residual         e = v - S_dec^T k   (from the decayed state, raw key:
@@ -53,9 +60,10 @@ def forward(q, k, v, gain, alpha, *, eta=None, eps=0.0, alphaP=None, betaP=None,
 
     Shapes: q, k [N, T, dk]; v [N, T, dv]; alpha [N, T] (scalar decay) or
     [N, T, dk] (per-channel decay); eta, alphaP, betaP, r [N, T];
-    omega, w [N, T, dk]; mu_log [N] (the head's centre, already broadcast);
-    S0 [N, dk, dv] (None: zeros); aux0 [N, dk] (None: ones) is A_0 for pgdn
-    and p_0 for kdn.
+    omega, w [N, T, dk] (kdn_iso: omega [N, T]); mu_log [N] (the head's
+    centre, already broadcast); S0 [N, dk, dv] (None: zeros); aux0 [N, dk]
+    (None: ones) is A_0 for pgdn and p_0 for kdn, and [N] (None: ones) b_0 for
+    kdn_iso.
 
     Returns (o [N, T, dv], S_T [N, dk, dv], aux_T [N, dk] or None, trace),
     trace holding per-token w, e and the gain's auxiliary values when
@@ -69,6 +77,8 @@ def forward(q, k, v, gain, alpha, *, eta=None, eps=0.0, alphaP=None, betaP=None,
     aux = None
     if gain in ("pgdn", "kdn"):
         aux = np.ones((N, dk)) if aux0 is None else _f64(aux0).copy()
+    elif gain == "kdn_iso":
+        aux = np.ones(N) if aux0 is None else _f64(aux0).reshape(N).copy()
     eta, alphaP, betaP, mu_log = _f64(eta), _f64(alphaP), _f64(betaP), _f64(mu_log)
     omega, r, w_in = _f64(omega), _f64(r), _f64(w)
     o = np.zeros((N, T, dv))
@@ -102,6 +112,17 @@ def forward(q, k, v, gain, alpha, *, eta=None, eps=0.0, alphaP=None, betaP=None,
             aux = p_hat / (1.0 + u * p_hat)
             if record:
                 trace["p_hat"].append(p_hat)
+                trace["p"].append(aux.copy())
+        elif gain == "kdn_iso":
+            a_mean = np.mean(a * a, axis=1)
+            b_hat = a_mean * aux + omega[:, t]
+            nk = np.sum(kt * kt, axis=1)
+            beta = b_hat / (r[:, t] + b_hat * nk)
+            wt = beta[:, None] * kt
+            u = mu_info * nk / (dk * r[:, t])
+            aux = b_hat / (1.0 + u * b_hat)
+            if record:
+                trace["p_hat"].append(b_hat)
                 trace["p"].append(aux.copy())
         elif gain == "explicit":
             wt = w_in[:, t]

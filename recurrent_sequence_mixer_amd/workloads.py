@@ -8,9 +8,11 @@ bit-identical inputs.
 Conventions (shared with the C ABI):
   * q, k, v, o: [B, H, T, d] row-major, d contiguous.
   * per-token scalar gates (eta, scalar alpha, alphaP, betaP, r): fp32 [B, H, T].
-  * per-channel gates (alpha, omega of diagonal KDN): io dtype [B, H, T, dk].
+  * per-channel gates (alpha, omega of diagonal KDN): io dtype [B, H, T, dk];
+    isotropic KDN draws omega per token, fp32 [B, H, T].
   * per-head PGDN log-centre mu_log: fp32 [H].
-  * state S: fp32 [B, H, dk, dv]; auxiliary state (PGDN A, KDN p): fp32 [B, H, dk].
+  * state S: fp32 [B, H, dk, dv]; auxiliary state (PGDN A, KDN p): fp32 [B, H, dk];
+    isotropic KDN b: fp32 [B, H].
 
 Distributions follow the workloads the pages evaluate, stated per config
 below.  Values are drawn in fp64 with numpy's PCG64 generator, rounded to
@@ -27,7 +29,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-GAINS = ("kla", "gdn", "pgdn", "kdn", "explicit")
+GAINS = ("kla", "gdn", "pgdn", "kdn", "kdn_iso", "explicit")
 DECAYS = ("scalar", "channel")
 
 
@@ -164,6 +166,9 @@ def generate(wl: Workload) -> Dict[str, np.ndarray]:
         out["mu_log"] = round_f32(np.full((H,), wl.mu_log))
     if wl.gain == "kdn":
         out["omega"] = round_io(_softplus(rng.normal(-3.0, 1.0, size=shp + (dk,))), wl.io)
+        out["r"] = round_f32(_softplus(rng.standard_normal(shp)))
+    if wl.gain == "kdn_iso":
+        out["omega"] = round_f32(_softplus(rng.normal(-3.0, 1.0, size=shp)))
         out["r"] = round_f32(_softplus(rng.standard_normal(shp)))
     if wl.s0 == "zero":
         out["S0"] = np.zeros((B, H, dk, dv), np.float32)

@@ -385,6 +385,96 @@ def test_kdn_variance_matches_mobius_scan():
 
 
 # --------------------------------------------------------------------------
+# Isotropic KDN (Kalman Delta Networks §2.7, Eq. 40)
+# --------------------------------------------------------------------------
+
+def _iso(k, v, alpha, omega, r, mu_info, b0, S0=None, q=None):
+    q = k if q is None else q
+    return forward(one(q), one(k), one(v), "kdn_iso", one(alpha), omega=one(omega), r=one(r),
+                   mu_info=mu_info, aux0=np.array([b0], float),
+                   S0=None if S0 is None else one(S0), record=True)
+
+
+@pytest.mark.parametrize("channel", [False, True])
+def test_kdn_iso_one_channel_equals_diagonal(channel):
+    """§2.7: with a single key channel the isotropic and the diagonal variance
+    are the same number, so both variants give the same gains, variances,
+    outputs and state (ties the isotropic branch to the diagonal pins)."""
+    T, dv = 80, 3
+    k = RNG.standard_normal((T, 1)) * 2
+    q = RNG.standard_normal((T, 1))
+    v = RNG.standard_normal((T, dv))
+    alpha = RNG.uniform(0.5, 1.0, size=(T, 1) if channel else T)
+    omega = RNG.uniform(0.0, 0.4, size=T)
+    r = RNG.uniform(0.1, 2.0, size=T)
+    S0 = RNG.standard_normal((1, dv))
+    o_i, S_i, b, tr_i = _iso(k, v, alpha, omega, r, 1.7, 1.3, S0=S0, q=q)
+    o_d, S_d, p, tr_d = _kdn(k, v, alpha if channel else alpha[:, None], omega[:, None], r, 1.7,
+                             np.array([1.3]), S0=S0, q=q)
+    np.testing.assert_allclose(tr_i["w"], tr_d["w"], rtol=1e-13)
+    np.testing.assert_allclose(tr_i["p"], tr_d["p"][..., 0], rtol=1e-13)
+    np.testing.assert_allclose(o_i, o_d, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S_i, S_d, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(b, p[:, 0], rtol=1e-13)
+
+
+def test_kdn_iso_steps_are_kalman_steps_with_the_two_projections():
+    """§2.7: prediction projects D (b I) D^T + omega I to the isotropic matrix
+    with the same trace; the gain is the exact Kalman gain of that isotropic
+    prediction (textbook filter); the reverse-KL projection of the exact
+    posterior keeps the harmonic mean of its eigenvalues (mu = 1)."""
+    T, dk, dv = 25, 6, 2
+    k = RNG.standard_normal((T, dk)) * RNG.uniform(0.3, 3, size=(T, 1))
+    v = RNG.standard_normal((T, dv))
+    alpha = RNG.uniform(0.6, 1.0, size=(T, dk))
+    omega = RNG.uniform(0.0, 0.3, size=T)
+    r = RNG.uniform(0.2, 2.0, size=T)
+    _, _, _, tr = _iso(k, v, alpha, omega, r, 1.0, 0.8)
+    b = 0.8
+    for t in range(T):
+        P_hat = np.diag(alpha[t]) @ (b * np.eye(dk)) @ np.diag(alpha[t]) + omega[t] * np.eye(dk)
+        b_hat = np.trace(P_hat) / dk
+        assert abs(tr["p_hat"][0, t] - b_hat) <= 1e-14 * b_hat
+        _, P_post, kap = kalman.dense_kalman(k[t:t + 1], v[t:t + 1], np.eye(dk)[None],
+                                             np.zeros((1, dk, dk)), r[t:t + 1], np.zeros((dk, dv)),
+                                             b_hat * np.eye(dk))
+        np.testing.assert_allclose(tr["w"][0, t], kap[0], rtol=1e-12, atol=1e-15)
+        eig = np.linalg.eigvalsh((P_post + P_post.T) / 2)
+        b = dk / np.sum(1.0 / eig)
+        assert abs(tr["p"][0, t] - b) <= 1e-11 * b
+
+
+def test_kdn_iso_repeated_observation_exact():
+    """§2.7: with mu = d_k and a unit key the information term is 1 / r; with
+    D = 1, omega = 0, r = 1 and b_0 = 1 the variance is 1/(n+1) and the read
+    along the key is the running mean with one prior pseudo-observation at 0
+    (exact in rationals)."""
+    n, dk = 10, 4
+    key = [Fr(3, 5), Fr(4, 5), Fr(0), Fr(0)]
+    vs = [[Fr(int(x)), Fr(int(y), 7)] for x, y in RNG.integers(-9, 9, size=(n, 2))]
+    k = [key] * n
+    ws, bs = exact.gains(k, "kdn_iso", [Fr(1)] * n, omega=[Fr(0)] * n, r=[Fr(1)] * n,
+                         mu_info=Fr(dk), p0=[Fr(1)])
+    _, S = exact.token_recurrence(k, k, vs, ws, [Fr(1)] * n)
+    for i, b in enumerate(bs):
+        assert b == [Fr(1, i + 2)]
+    read = [sum((S[d][j] * key[d] for d in range(dk)), Fr(0)) for j in range(2)]
+    assert read == [sum((v[j] for v in vs), Fr(0)) / (n + 1) for j in range(2)]
+
+
+def test_kdn_iso_effective_gain_in_unit_interval():
+    """§2.7 with §2.2: beta_eff = k^T kappa = b_hat ||k||^2 / (r + b_hat ||k||^2)
+    lies in [0, 1) for any positive noise."""
+    T, dk, dv = 200, 16, 4
+    q, k, v, _, alpha, S0 = _random_head(T, dk, dv, channel=True)
+    omega = np.log1p(np.exp(RNG.normal(-3, 1, size=T)))
+    r = np.log1p(np.exp(RNG.standard_normal(T)))
+    _, _, _, tr = _iso(k, v, alpha, omega, r, 1.0, 1.0, S0=S0, q=q)
+    be = np.einsum("td,td->t", k, tr["w"][0])
+    assert np.all(be >= 0) and np.all(be < 1)
+
+
+# --------------------------------------------------------------------------
 # Chunkwise form == recurrence (Kaczmarz Linear Attention §2.5;
 # Preconditioned DeltaNet §2.6; Kalman Delta Networks §2.6)
 # --------------------------------------------------------------------------
@@ -393,7 +483,7 @@ def _rat(x, den=8):
     return Fr(int(round(x * den)), den)
 
 
-@pytest.mark.parametrize("gain", ["kla", "gdn", "kdn", "explicit"])
+@pytest.mark.parametrize("gain", ["kla", "gdn", "kdn", "kdn_iso", "explicit"])
 @pytest.mark.parametrize("channel", [False, True])
 @pytest.mark.parametrize("T,C", [(1, 1), (5, 2), (9, 4), (13, 4)])
 def test_chunk_form_equals_recurrence_exactly(gain, channel, T, C):
@@ -411,6 +501,9 @@ def test_chunk_form_equals_recurrence_exactly(gain, channel, T, C):
               omega=[[Fr(int(x), 16) for x in row] for row in RNG.integers(0, 4, size=(T, dk))],
               r=[Fr(int(x), 4) for x in RNG.integers(1, 8, size=T)], mu_info=Fr(3, 2),
               w=[[_rat(x) for x in row] for row in rnd(T, dk)], p0=[Fr(1)] * dk)
+    if gain == "kdn_iso":  # scalar process noise and one variance per head
+        kw["omega"] = [Fr(int(x), 16) for x in RNG.integers(0, 4, size=T)]
+        kw["p0"] = [Fr(5, 4)]
     ws, _ = exact.gains(k, gain, alpha, **kw)
     o_rec, S_rec = exact.token_recurrence(q, k, v, ws, alpha, S0)
     o_chk, S_chk = exact.chunkwise(q, k, v, ws, alpha, C, S0)
@@ -419,24 +512,26 @@ def test_chunk_form_equals_recurrence_exactly(gain, channel, T, C):
     f = lambda M: np.array([[float(x) for x in row] for row in M])
     fa = lambda a: np.array([[float(x) for x in row] for row in a]) if channel else \
         np.array([float(x) for x in a])
+    om = [float(x) for x in kw["omega"]] if gain == "kdn_iso" else f(kw["omega"])
     o64, S64, _, _ = forward(one(f(q)), one(f(k)), one(f(v)), gain, one(fa(alpha)),
                              eta=one([float(x) for x in kw["eta"]]), eps=0.01,
-                             omega=one(f(kw["omega"])), r=one([float(x) for x in kw["r"]]),
-                             mu_info=1.5, w=one(f(kw["w"])), S0=one(f(S0)))
+                             omega=one(om), r=one([float(x) for x in kw["r"]]),
+                             mu_info=1.5, w=one(f(kw["w"])), S0=one(f(S0)),
+                             aux0=np.array([1.25]) if gain == "kdn_iso" else None)
     np.testing.assert_allclose(o64[0], f(o_rec), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(S64[0], f(S_rec), rtol=1e-11, atol=1e-12)
 
 
-@pytest.mark.parametrize("gain", ["kla", "gdn", "pgdn", "kdn"])
+@pytest.mark.parametrize("gain", ["kla", "gdn", "pgdn", "kdn", "kdn_iso"])
 def test_chunk_form_equals_recurrence_fp64(gain):
     N, T, dk, dv, C = 3, 150, 16, 12, 64
-    channel = gain == "kdn"
-    heads = [_random_head(T, dk, dv, scaled=gain in ("kla", "kdn"), channel=channel)
+    channel = gain in ("kdn", "kdn_iso")
+    heads = [_random_head(T, dk, dv, scaled=gain in ("kla", "kdn", "kdn_iso"), channel=channel)
              for _ in range(N)]
     q, k, v, eta, alpha, S0 = (np.stack(x) for x in zip(*heads))
     kw = dict(eta=eta, eps=1e-6, alphaP=1 / (1 + np.exp(-RNG.normal(2, 1, (N, T)))),
               betaP=1 / (1 + np.exp(-RNG.normal(2, 1, (N, T)))), mu_log=np.full(N, math.log(4)),
-              x=1.5, omega=np.log1p(np.exp(RNG.normal(-3, 1, (N, T, dk)))),
+              x=1.5, omega=np.log1p(np.exp(RNG.normal(-3, 1, (N, T) if gain == "kdn_iso" else (N, T, dk)))),
               r=np.log1p(np.exp(RNG.standard_normal((N, T)))), mu_info=1.0)
     o, S, _, tr = forward(q, k, v, gain, alpha, S0=S0, record=True, **kw)
     o2, S2 = chunkwise.forward(q, k, v, tr["w"], alpha, C, S0=S0)
@@ -445,15 +540,16 @@ def test_chunk_form_equals_recurrence_fp64(gain):
     np.testing.assert_allclose(S2, S, rtol=0, atol=1e-11 * np.abs(S).max())
 
 
-@pytest.mark.parametrize("gain", ["kla", "pgdn", "kdn"])
+@pytest.mark.parametrize("gain", ["kla", "pgdn", "kdn", "kdn_iso"])
 def test_resume_equals_single_pass(gain):
     """Tokenwise and chunkwise computation share one recurrence: splitting
     the sequence and carrying (S, aux) reproduces one pass."""
     T, dk, dv, T1 = 90, 8, 6, 37
-    channel = gain == "kdn"
+    channel = gain in ("kdn", "kdn_iso")
     q, k, v, eta, alpha, S0 = _random_head(T, dk, dv, channel=channel)
     kw = dict(eta=eta, eps=1e-6, alphaP=np.full(T, 0.9), betaP=np.full(T, 0.6), x=1.5,
-              omega=np.full((T, dk), 0.05), r=np.full(T, 0.7), mu_info=2.0)
+              omega=np.full(T, 0.05) if gain == "kdn_iso" else np.full((T, dk), 0.05),
+              r=np.full(T, 0.7), mu_info=2.0)
     full = forward(one(q), one(k), one(v), gain, one(alpha), mu_log=np.array([1.0]), S0=one(S0),
                    **{n: one(a) if isinstance(a, np.ndarray) else a for n, a in kw.items()})
     cut = lambda a, s: one(a[s]) if isinstance(a, np.ndarray) else a
