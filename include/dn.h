@@ -27,6 +27,12 @@
  *                     (Kalman Delta Networks §2.4 Eqs. 23-30 and §2.5)
  *   DN_GAIN_EXPLICIT  w_t read from gates->w (e.g. the exact ATK write key of
  *                     Preconditioned DeltaNet §2.2)
+ *   DN_GAIN_KDN_ISO   one variance b per head: a = mean_i alpha_i^2 (alpha^2
+ *                     for scalar decay);  b_hat = a b_{t-1} + omega;
+ *                     n = ||k||^2;  w = b_hat / (r + b_hat n) * k;
+ *                     b_t = b_hat / (1 + u b_hat),  u = mu_info n / (dk r)
+ *                     (Kalman Delta Networks §2.7, Eq. 40; omega and r are
+ *                     scalars per token)
  *
  * q is used as given: normalising it (Kaczmarz Linear Attention §2.1 reads
  * S^T q / ||q||) is the caller's job.
@@ -39,11 +45,13 @@
  *   eta           fp32 [B, H, T]   (KLA eta, GDN/PGDN beta; unused by KDN)
  *   alphaP, betaP fp32 [B, H, T]   (PGDN statistic gates)
  *   mu_log        fp32 [H]         (PGDN per-head log-centre)
- *   omega         io   [B, H, T, dk] (KDN process noise)
- *   r             fp32 [B, H, T]   (KDN observation noise, > 0)
+ *   omega         io   [B, H, T, dk] (KDN process noise);
+ *                 KDN_ISO: fp32 [B, H, T]
+ *   r             fp32 [B, H, T]   (KDN / KDN_ISO observation noise, > 0)
  *   w             io   [B, H, T, dk] (EXPLICIT write vectors)
  *   S0, S_final   fp32 [B, H, dk, dv]
- *   aux0, aux_final fp32 [B, H, dk] (PGDN statistic A; KDN variance p)
+ *   aux0, aux_final fp32 [B, H, dk] (PGDN statistic A; KDN variance p);
+ *                 KDN_ISO: fp32 [B, H] (the variance b of each head)
  *
  * OWNERSHIP.  Every pointer except the descriptor and the gate table (host
  * structs, read before the call returns) is a device pointer owned by the
@@ -54,7 +62,8 @@
  * on a negative status nothing has been enqueued.  DN_ERR_HIP reports a
  * failed launch.  NaN/Inf in the data are not checked and propagate.
  * Preconditions on values (not checked): alpha in (0, 1]; PGDN A_0 > 0 and
- * alphaP, betaP >= 0; KDN r > 0, omega >= 0, p_0 > 0; for channel decay the
+ * alphaP, betaP >= 0; KDN and KDN_ISO r > 0, omega >= 0, p_0 and b_0 > 0;
+ * for channel decay the
  * sum of -log(alpha) over any 32 consecutive tokens of one channel stays
  * below 80 (fp32 range of the in-chunk decay factors).
  *
@@ -91,7 +100,8 @@ typedef enum dn_gain {
   DN_GAIN_GDN = 1,
   DN_GAIN_PGDN = 2,
   DN_GAIN_KDN = 3,
-  DN_GAIN_EXPLICIT = 4
+  DN_GAIN_EXPLICIT = 4,
+  DN_GAIN_KDN_ISO = 5
 } dn_gain;
 
 typedef enum dn_decay { DN_DECAY_SCALAR = 0, DN_DECAY_CHANNEL = 1 } dn_decay;
@@ -101,7 +111,8 @@ typedef enum dn_decay { DN_DECAY_SCALAR = 0, DN_DECAY_CHANNEL = 1 } dn_decay;
  *   dk, dv in {64, 128}; C = 64 (chunk length of the chunked forward);
  *   io: dn_dtype of q, k, v, o and of per-channel gates;
  *   gain: dn_gain; decay: dn_decay (KDN requires DN_DECAY_CHANNEL or SCALAR);
- *   eps >= 0 (KLA), x > 1 (PGDN bound: B in [1/x, x]), mu_info > 0 (KDN). */
+ *   eps >= 0 (KLA), x > 1 (PGDN bound: B in [1/x, x]), mu_info > 0 (KDN,
+ *   KDN_ISO). */
 typedef struct dn_desc {
   int32_t B, H, T, dk, dv, C;
   int32_t io;
@@ -119,8 +130,8 @@ typedef struct dn_gates {
   const float* alphaP; /* PGDN                                       */
   const float* betaP;  /* PGDN                                       */
   const float* mu_log; /* PGDN                                       */
-  const void* omega;   /* KDN                                        */
-  const float* r;      /* KDN                                        */
+  const void* omega;   /* KDN (io, per channel), KDN_ISO (fp32)      */
+  const float* r;      /* KDN, KDN_ISO                               */
   const void* w;       /* EXPLICIT                                   */
 } dn_gates;
 
@@ -128,10 +139,11 @@ typedef struct dn_gates {
  * §2.5 Eqs. 7-9 and Preconditioned DeltaNet §2.6 Eq. 6 give the chunk form;
  * results equal the token recurrence above up to rounding).
  *   S0        initial state, NULL = zeros.
- *   aux0      PGDN A_0 / KDN p_0, NULL = ones; ignored by other gains.
+ *   aux0      PGDN A_0 / KDN p_0 / KDN_ISO b_0, NULL = ones; ignored by
+ *             other gains.
  *   o         output [B, H, T, dv], io dtype (round to nearest even).
  *   S_final   final state, nullable.  May alias S0 exactly (in-place resume).
- *   aux_final final A_T / p_T, nullable.  Must not overlap aux0 (every value
+ *   aux_final final A_T / p_T / b_T, nullable.  Must not overlap aux0 (every value
  *             slice of a head reads aux0 while one of them writes aux_final).
  * No other buffers may overlap (DN_ERR_ALIAS is returned for the overlaps
  * the host can see from the pointer ranges).  With T = 0 the tensors q, k, v,
@@ -142,8 +154,8 @@ int dn_chunk_fwd(const dn_desc* desc, const void* q, const void* k, const void* 
 
 /* One token for N = desc->B independent sequences (desc->T must be 1), the
  * tokenwise step of Kaczmarz Linear Attention Algorithm 1 (and its PGDN/KDN
- * analogues).  S [N, H, dk, dv] and aux [N, H, dk] (PGDN, KDN; NULL
- * otherwise) are updated in place; o [N, H, dv] receives S_t^T q_t.
+ * analogues).  S [N, H, dk, dv] and aux [N, H, dk] (PGDN, KDN; [N, H] for
+ * KDN_ISO; NULL otherwise) are updated in place; o [N, H, dv] receives S_t^T q_t.
  * q, k, v, gates are laid out as for dn_chunk_fwd with T = 1. */
 int dn_decode_step(const dn_desc* desc, const void* q, const void* k, const void* v,
                    const dn_gates* gates, float* S, float* aux, void* o, void* stream);
@@ -154,8 +166,9 @@ int dn_decode_step(const dn_desc* desc, const void* q, const void* k, const void
  *             (G_t = sum of log alpha from the chunk start through t):
  *             [B, H, T] (scalar decay) or [B, H, T, dk] (channel); nullable.
  *   aux_chunk fp32 [B, H, ceil(T/C), dk]: PGDN A / KDN p entering each
- *             chunk; nullable (ignored by gains without state).
- *   aux_final fp32 [B, H, dk]: A_T / p_T; nullable.
+ *             chunk ([B, H, ceil(T/C)]: KDN_ISO b); nullable (ignored by
+ *             gains without state).
+ *   aux_final fp32 [B, H, dk]: A_T / p_T ([B, H]: KDN_ISO b_T); nullable.
  *   aux0      as for dn_chunk_fwd. */
 int dn_gain_prep(const dn_desc* desc, const void* k, const dn_gates* gates, const float* aux0,
                  float* w_out, float* g_out, float* aux_chunk, float* aux_final, void* stream);

@@ -253,7 +253,11 @@ void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
   for (int cc = 0; cc < CPT; ++cc) {
     const int d = tid + cc * NT;
-    aux[cc] = (d < DK && a.aux0) ? a.aux0[static_cast<long>(bh) * DK + d] : 1.f;
+    aux[cc] = (d < DK && a.aux0 && GAIN != GAIN_KDN_ISO) ? a.aux0[static_cast<long>(bh) * DK + d] : 1.f;
+  }
+  // isotropic KDN: the head's variance b, carried between chunks in LDS
+  if constexpr (GAIN == GAIN_KDN_ISO) {
+    if (tid == 0) sm.acarry[0] = a.aux0 ? a.aux0[bh] : 1.f;
   }
 
   if constexpr (PG2) {
@@ -305,13 +309,15 @@ void chunk_fwd_kernel(ChunkArgs a) {
     }
     if (tid < CH) {
       const long ti = static_cast<long>(bh) * T + t0 + (tid < n ? tid : 0);
-      if (GAIN != GAIN_KDN && GAIN != GAIN_EXPLICIT) p_eta = a.g.eta[ti];
+      if (GAIN != GAIN_KDN && GAIN != GAIN_EXPLICIT && GAIN != GAIN_KDN_ISO) p_eta = a.g.eta[ti];
+      // isotropic KDN: the per-token process noise omega travels in the eta slot
+      if (GAIN == GAIN_KDN_ISO) p_eta = static_cast<const float*>(a.g.omega)[ti];
       if (!CHANNEL) p_alpha = static_cast<const float*>(a.g.alpha)[ti];
       if (GAIN == GAIN_PGDN) {
         p_ap = a.g.alphaP[ti];
         p_bp = a.g.betaP[ti];
       }
-      if (GAIN == GAIN_KDN) p_r = a.g.r[ti];
+      if (GAIN == GAIN_KDN || GAIN == GAIN_KDN_ISO) p_r = a.g.r[ti];
     }
   };
 
@@ -444,12 +450,14 @@ void chunk_fwd_kernel(ChunkArgs a) {
         if (half == 1) sm.acarry[d] = At;
       }
     }
-    if constexpr (GAIN == GAIN_KLA || GAIN == GAIN_GDN) {
-      // ||k_t||^2 (KLA) with NT/64 threads per token, 16-byte LDS reads; column scale beta_t
+    if constexpr (GAIN == GAIN_KLA || GAIN == GAIN_GDN || GAIN == GAIN_KDN_ISO) {
+      // ||k_t||^2 (KLA, isotropic KDN) with NT/64 threads per token, 16-byte
+      // LDS reads; column scale beta_t (isotropic KDN: ||k_t||^2 kept for its
+      // variance scan below)
       constexpr int TPT = NT / CH;
       const int t = tid / TPT, part = tid % TPT;
       float s = 0.f;
-      if (GAIN == GAIN_KLA) {
+      if (GAIN == GAIN_KLA || GAIN == GAIN_KDN_ISO) {
         constexpr int PER = DK / TPT;
 #pragma unroll
         for (int d0 = 0; d0 < PER; d0 += VEC) {
@@ -473,8 +481,10 @@ void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
         for (int off = 1; off < TPT; off <<= 1) s += __shfl_xor(s, off, 64);
       }
-      if (part == 0)
-        sm.cs[t] = (GAIN == GAIN_KLA) ? kla_beta(sm.eta[t], s, a.g.eps) : sm.eta[t];
+      if (part == 0) {
+        if constexpr (GAIN == GAIN_KDN_ISO) sm.zp[0][t] = s;
+        else sm.cs[t] = (GAIN == GAIN_KLA) ? kla_beta(sm.eta[t], s, a.g.eps) : sm.eta[t];
+      }
     }
     if constexpr (GAIN == GAIN_PGDN || GAIN == GAIN_KDN || GAIN == GAIN_EXPLICIT) {
       if (tid < CH) sm.cs[tid] = 1.f;
@@ -657,6 +667,41 @@ void chunk_fwd_kernel(ChunkArgs a) {
           sm.red[tid] = 1.f / (sm.r[tid] + z);
         }
         }
+      }
+    }
+    if constexpr (GAIN == GAIN_KDN_ISO) {
+      // isotropic KDN (Kalman Delta Networks §2.7, Eq. 40): the mean of
+      // alpha_t^2 over the channels (channel decay: from its staged copy,
+      // NT/64 threads per token), then one thread runs the head's variance
+      // through the chunk and sets the column scales beta_t
+      constexpr int TPT = NT / CH;
+      const int t = tid / TPT, part = tid % TPT;
+      float s2 = 0.f;
+      if constexpr (CHANNEL) {
+        constexpr int PER = DK / TPT;
+        const E* s_al = sm.wt;
+#pragma unroll
+        for (int d0 = 0; d0 < PER; ++d0) {
+          const float x = EL::get(s_al[t * DK + part * PER + d0]);
+          s2 = fmaf(x, x, s2);
+        }
+#pragma unroll
+        for (int off = 1; off < TPT; off <<= 1) s2 += __shfl_xor(s2, off, 64);
+        s2 *= 1.0f / DK;
+      } else {
+        s2 = sm.alpha[t] * sm.alpha[t];
+      }
+      if (part == 0) sm.zp[1][t] = s2;
+      __syncthreads();
+      if (tid == 0) {
+        float b = sm.acarry[0];
+        for (int tt = 0; tt < CH; ++tt) {
+          const float nk = sm.zp[0][tt], rr = sm.r[tt];
+          const float bh_ = kdn_iso_predict(sm.zp[1][tt], b, sm.eta[tt]);
+          sm.cs[tt] = kdn_iso_beta(bh_, rr, nk);
+          b = kdn_iso_update(bh_, nk, a.g.mu_info / (DK * rr));
+        }
+        sm.acarry[0] = b;
       }
     }
     __syncthreads();  // (B) gains visible
@@ -1039,6 +1084,9 @@ void chunk_fwd_kernel(ChunkArgs a) {
   if constexpr (PG2) {
     if (a.aux_final && slice == 0 && tid < DK)
       a.aux_final[static_cast<long>(bh) * DK + tid] = nchunks > 0 ? sm.acarry[tid] : aux[0];
+  } else if (GAIN == GAIN_KDN_ISO) {
+    if (a.aux_final && slice == 0 && tid == 0)
+      a.aux_final[bh] = nchunks > 0 ? sm.acarry[0] : (a.aux0 ? a.aux0[bh] : 1.f);
   } else if ((GAIN == GAIN_PGDN || GAIN == GAIN_KDN) && a.aux_final && slice == 0) {
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) {
@@ -1072,6 +1120,7 @@ static hipError_t launch_gain(const ChunkArgs& a, int gain, bool channel, hipStr
       case GAIN_GDN: return launch_one<E, DK, BV, GAIN_GDN, true>(a, st);
       case GAIN_PGDN: return launch_one<E, DK, BV, GAIN_PGDN, true>(a, st);
       case GAIN_KDN: return launch_one<E, DK, BV, GAIN_KDN, true>(a, st);
+      case GAIN_KDN_ISO: return launch_one<E, DK, BV, GAIN_KDN_ISO, true>(a, st);
       default: return launch_one<E, DK, BV, GAIN_EXPLICIT, true>(a, st);
     }
   }
@@ -1080,6 +1129,7 @@ static hipError_t launch_gain(const ChunkArgs& a, int gain, bool channel, hipStr
     case GAIN_GDN: return launch_one<E, DK, BV, GAIN_GDN, false>(a, st);
     case GAIN_PGDN: return launch_one<E, DK, BV, GAIN_PGDN, false>(a, st);
     case GAIN_KDN: return launch_one<E, DK, BV, GAIN_KDN, false>(a, st);
+    case GAIN_KDN_ISO: return launch_one<E, DK, BV, GAIN_KDN_ISO, false>(a, st);
     default: return launch_one<E, DK, BV, GAIN_EXPLICIT, false>(a, st);
   }
 }
@@ -1087,7 +1137,7 @@ static hipError_t launch_gain(const ChunkArgs& a, int gain, bool channel, hipStr
 hipError_t launch_chunk_fwd(const ChunkArgs& a, int io_bf16, int gain, bool channel,
                             hipStream_t st) {
   if (io_bf16) {
-    if (!channel && gain != GAIN_KDN) return launch_chunk_fwd_bf16_scalar(a, gain, st);
+    if (!channel && gain != GAIN_KDN && gain != GAIN_KDN_ISO) return launch_chunk_fwd_bf16_scalar(a, gain, st);
     if (channel && gain == GAIN_KDN) return launch_chunk_fwd_bf16_kdn(a, st);
     if (a.dk == 128) return launch_gain<uint16_t, 128, 64>(a, gain, channel, st);
     return launch_gain<uint16_t, 64, 64>(a, gain, channel, st);

@@ -1,7 +1,7 @@
 // Batched tokenwise decode step: one token for each of N sequences x H heads
 // (the tokenwise step of Kaczmarz Linear Attention Algorithm 1; the same
-// step with the PGDN and diagonal-KDN gains of Preconditioned DeltaNet §2.4
-// and Kalman Delta Networks §2.4-2.5).
+// step with the PGDN, diagonal-KDN and isotropic-KDN gains of Preconditioned
+// DeltaNet §2.4 and Kalman Delta Networks §2.4-2.5, §2.7).
 //
 // One workgroup per (sequence, head).  The d_k x d_v fp32 state is read from
 // HBM once into registers, both readouts S^T (alpha k) and S^T (alpha q) are
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
 
   __shared__ __align__(16) float s_a[DK], s_ak[DK], s_aq[DK], s_w[DK];
   __shared__ __align__(16) float s_v[DV], s_e[DV];
-  __shared__ float s_red[DECODE_THREADS / 64][2];
+  __shared__ float s_red[DECODE_THREADS / 64][3];
   __shared__ __align__(16) f32x4 s_yk[RG][CG], s_yq[RG][CG];
 
   const int tid = threadIdx.x;
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
     s[i] = __builtin_nontemporal_load(Sp + (rg + RG * i) * CG + cg);
 
   // 2. token inputs and the write gain (threads d < DK own key channel d).
-  float red1 = 0.f, red2 = 0.f;
+  float red1 = 0.f, red2 = 0.f, red3 = 0.f;
   float kd = 0.f, qd = 0.f, ad = 0.f, pre = 0.f, aux_new = 0.f, mu_over_r = 0.f;
   if (tid < DV) s_v[tid] = L::at(a.v, nh * DV + tid);
   if (tid < DK) {
@@ -88,6 +88,10 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
       red2 = pre * qd;
       mu_over_r = a.mu_info / a.r[nh];
       aux_new = kdn_update(ph, kd, mu_over_r);
+    } else if (GAIN == GAIN_KDN_ISO) {
+      red1 = kd * kd;
+      red2 = kd * qd;
+      red3 = ad * ad;
     } else {  // explicit
       pre = L::at(a.w, nh * DK + tid);
       red2 = pre * qd;
@@ -95,16 +99,28 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
   }
   red1 = wave_sum(red1);
   red2 = wave_sum(red2);
+  if (GAIN == GAIN_KDN_ISO && CHANNEL) red3 = wave_sum(red3);
   if ((tid & 63) == 0) {
     s_red[tid >> 6][0] = red1;
     s_red[tid >> 6][1] = red2;
+    s_red[tid >> 6][2] = red3;
   }
   __syncthreads();
-  float sum1 = 0.f, sum2 = 0.f;
+  float sum1 = 0.f, sum2 = 0.f, sum3 = 0.f;
 #pragma unroll
   for (int i = 0; i < DECODE_THREADS / 64; ++i) {
     sum1 += s_red[i][0];
     sum2 += s_red[i][1];
+    sum3 += s_red[i][2];
+  }
+  // isotropic KDN: the head's predicted variance and step size (every thread)
+  float iso_beta = 0.f, iso_b = 0.f;
+  if (GAIN == GAIN_KDN_ISO) {
+    const float as = CHANNEL ? 0.f : static_cast<const float*>(a.alpha)[nh];
+    const float a2 = CHANNEL ? sum3 * (1.0f / DK) : as * as;
+    const float bh = kdn_iso_predict(a2, a.aux[nh], static_cast<const float*>(a.omega)[nh]);
+    iso_beta = kdn_iso_beta(bh, a.r[nh], sum1);
+    iso_b = kdn_iso_update(bh, sum1, a.mu_info / (DK * a.r[nh]));
   }
   float wq;  // w . q
   if (tid < DK) {
@@ -116,6 +132,8 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
       wd = a.eta[nh] * kd;
     } else if (GAIN == GAIN_KDN) {
       wd = pre / (a.r[nh] + sum1);
+    } else if (GAIN == GAIN_KDN_ISO) {
+      wd = iso_beta * kd;
     } else {
       wd = pre;
     }
@@ -128,6 +146,7 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
   if (GAIN == GAIN_KLA) wq = kla_beta(a.eta[nh], sum1, a.eps) * sum2;
   else if (GAIN == GAIN_GDN) wq = a.eta[nh] * sum2;
   else if (GAIN == GAIN_KDN) wq = sum2 / (a.r[nh] + sum1);
+  else if (GAIN == GAIN_KDN_ISO) wq = iso_beta * sum2;
   else wq = sum2;
   __syncthreads();
 
@@ -145,6 +164,9 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
   }
   s_yk[rg][cg] = pk;
   s_yq[rg][cg] = pq;
+  // isotropic KDN: every thread read the head's variance before the barrier
+  // that follows the gains, so it can be replaced now
+  if (GAIN == GAIN_KDN_ISO && tid == 0) a.aux[nh] = iso_b;
   __syncthreads();
 
   // 4. residual and output (threads c < DV own value column c).
@@ -187,6 +209,7 @@ static hipError_t launch_decode_io(const DecodeArgs& a, int gain, bool channel, 
     case GAIN_GDN: if (channel) DN_DEC(GAIN_GDN, true); else DN_DEC(GAIN_GDN, false); break;
     case GAIN_PGDN: if (channel) DN_DEC(GAIN_PGDN, true); else DN_DEC(GAIN_PGDN, false); break;
     case GAIN_KDN: if (channel) DN_DEC(GAIN_KDN, true); else DN_DEC(GAIN_KDN, false); break;
+    case GAIN_KDN_ISO: if (channel) DN_DEC(GAIN_KDN_ISO, true); else DN_DEC(GAIN_KDN_ISO, false); break;
     default: if (channel) DN_DEC(GAIN_EXPLICIT, true); else DN_DEC(GAIN_EXPLICIT, false); break;
   }
 #undef DN_DEC

@@ -39,11 +39,12 @@ int check_desc(const dn_desc* d, bool chunked) {
       (1LL << 40))
     return DN_ERR_SHAPE;
   if (d->io != DN_F32 && d->io != DN_BF16) return DN_ERR_DTYPE;
-  if (d->gain < DN_GAIN_KLA || d->gain > DN_GAIN_EXPLICIT) return DN_ERR_GAIN;
+  if (d->gain < DN_GAIN_KLA || d->gain > DN_GAIN_KDN_ISO) return DN_ERR_GAIN;
   if (d->decay != DN_DECAY_SCALAR && d->decay != DN_DECAY_CHANNEL) return DN_ERR_GAIN;
   if (d->gain == DN_GAIN_KLA && !(d->eps >= 0.f && std::isfinite(d->eps))) return DN_ERR_GAIN;
   if (d->gain == DN_GAIN_PGDN && !(d->x >= 1.f && std::isfinite(d->x))) return DN_ERR_GAIN;
-  if (d->gain == DN_GAIN_KDN && !(d->mu_info > 0.f && std::isfinite(d->mu_info)))
+  if ((d->gain == DN_GAIN_KDN || d->gain == DN_GAIN_KDN_ISO) &&
+      !(d->mu_info > 0.f && std::isfinite(d->mu_info)))
     return DN_ERR_GAIN;
   return DN_OK;
 }
@@ -59,6 +60,7 @@ int check_gates(const dn_desc* d, const dn_gates* g) {
       if (!g->eta || !g->alphaP || !g->betaP || !g->mu_log) return DN_ERR_NULL;
       break;
     case DN_GAIN_KDN:
+    case DN_GAIN_KDN_ISO:
       if (!g->omega || !g->r) return DN_ERR_NULL;
       break;
     default:
@@ -93,13 +95,19 @@ int gate_ranges(const dn_desc* d, const dn_gates* g, Range* out) {
   out[n++] = {g->alphaP, bht * 4};
   out[n++] = {g->betaP, bht * 4};
   out[n++] = {g->mu_log, static_cast<size_t>(d->H) * 4};
-  out[n++] = {g->omega, bht * d->dk * es};
+  out[n++] = {g->omega, d->gain == DN_GAIN_KDN_ISO ? bht * 4 : bht * d->dk * es};
   out[n++] = {g->r, bht * 4};
   out[n++] = {g->w, bht * d->dk * es};
   return n;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DN_OK : DN_ERR_HIP; }
+
+// Gains that carry an auxiliary state between tokens, and its size per head.
+bool has_aux_state(const dn_desc* d) {
+  return d->gain == DN_GAIN_PGDN || d->gain == DN_GAIN_KDN || d->gain == DN_GAIN_KDN_ISO;
+}
+size_t aux_per_head(const dn_desc* d) { return d->gain == DN_GAIN_KDN_ISO ? 1 : d->dk; }
 
 }  // namespace
 
@@ -133,8 +141,8 @@ DN_EXPORT int dn_chunk_fwd(const dn_desc* d, const void* q, const void* k, const
   const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
   const size_t es = io_size(d->io);
   const size_t sbytes = static_cast<size_t>(d->B) * d->H * d->dk * d->dv * 4;
-  const size_t abytes = static_cast<size_t>(d->B) * d->H * d->dk * 4;
-  const bool has_aux = d->gain == DN_GAIN_PGDN || d->gain == DN_GAIN_KDN;
+  const size_t abytes = static_cast<size_t>(d->B) * d->H * aux_per_head(d) * 4;
+  const bool has_aux = has_aux_state(d);
   Range in[16];
   const dn_gates nog{};
   int n = gate_ranges(d, g ? g : &nog, in);
@@ -181,7 +189,7 @@ DN_EXPORT int dn_decode_step(const dn_desc* d, const void* q, const void* k, con
   if (st != DN_OK) return st;
   if (d->T != 1) return DN_ERR_SHAPE;
   if ((st = check_gates(d, g)) != DN_OK) return st;
-  const bool has_aux = d->gain == DN_GAIN_PGDN || d->gain == DN_GAIN_KDN;
+  const bool has_aux = has_aux_state(d);
   if (!q || !k || !v || !o || !S || (has_aux && !aux)) return DN_ERR_NULL;
 
   const size_t bh = static_cast<size_t>(d->B) * d->H;
@@ -192,7 +200,7 @@ DN_EXPORT int dn_decode_step(const dn_desc* d, const void* q, const void* k, con
   in[n++] = {k, bh * d->dk * es};
   in[n++] = {v, bh * d->dv * es};
   const Range ro{o, bh * d->dv * es}, rs{S, bh * d->dk * d->dv * 4},
-      ra{has_aux ? aux : nullptr, bh * d->dk * 4};
+      ra{has_aux ? aux : nullptr, bh * aux_per_head(d) * 4};
   for (int i = 0; i < n; ++i)
     if (overlap(ro, in[i]) || overlap(rs, in[i]) || overlap(ra, in[i])) return DN_ERR_ALIAS;
   if (overlap(ro, rs) || overlap(ro, ra) || overlap(rs, ra)) return DN_ERR_ALIAS;
@@ -231,18 +239,19 @@ DN_EXPORT int dn_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, c
   if (st != DN_OK) return st;
   if ((st = check_gates(d, g)) != DN_OK) return st;
   if (!k || !w_out) return DN_ERR_NULL;
-  const bool has_aux = d->gain == DN_GAIN_PGDN || d->gain == DN_GAIN_KDN;
+  const bool has_aux = has_aux_state(d);
   const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
   const size_t es = io_size(d->io);
   const size_t nch = (static_cast<size_t>(d->T) + d->C - 1) / d->C;
+  const size_t aph = aux_per_head(d);
   Range in[16];
   int n = gate_ranges(d, g, in);
   in[n++] = {k, bht * d->dk * es};
-  in[n++] = {has_aux ? aux0 : nullptr, static_cast<size_t>(d->B) * d->H * d->dk * 4};
+  in[n++] = {has_aux ? aux0 : nullptr, static_cast<size_t>(d->B) * d->H * aph * 4};
   Range outs[4] = {{w_out, bht * d->dk * 4},
                    {g_out, g_out ? bht * (d->decay == DN_DECAY_CHANNEL ? d->dk : 1) * 4 : 0},
-                   {has_aux ? aux_chunk : nullptr, static_cast<size_t>(d->B) * d->H * nch * d->dk * 4},
-                   {has_aux ? aux_final : nullptr, static_cast<size_t>(d->B) * d->H * d->dk * 4}};
+                   {has_aux ? aux_chunk : nullptr, static_cast<size_t>(d->B) * d->H * nch * aph * 4},
+                   {has_aux ? aux_final : nullptr, static_cast<size_t>(d->B) * d->H * aph * 4}};
   for (int j = 0; j < 4; ++j) {
     for (int i = 0; i < n; ++i)
       if (overlap(outs[j], in[i])) return DN_ERR_ALIAS;

@@ -6,7 +6,7 @@
 
 namespace dn {
 
-enum Gain { GAIN_KLA = 0, GAIN_GDN = 1, GAIN_PGDN = 2, GAIN_KDN = 3, GAIN_EXPLICIT = 4 };
+enum Gain { GAIN_KLA = 0, GAIN_GDN = 1, GAIN_PGDN = 2, GAIN_KDN = 3, GAIN_EXPLICIT = 4, GAIN_KDN_ISO = 5 };
 
 // KLA step size eta / (||k||^2 + eps)  (Kaczmarz Linear Attention §2.1).
 __device__ __forceinline__ float kla_beta(float eta, float knorm2, float eps) {
@@ -36,6 +36,20 @@ __device__ __forceinline__ float kdn_predict(float a, float p, float om) {
 __device__ __forceinline__ float kdn_update(float p_hat, float k, float mu_over_r) {
   const float u = mu_over_r * k * k;
   return p_hat * __builtin_amdgcn_rcpf(fmaf(u, p_hat, 1.0f));
+}
+
+// Isotropic KDN, one variance b per head (Kalman Delta Networks §2.7,
+// Eq. 40): predicted b_hat = mean(alpha^2) b + omega (the trace projection of
+// D (b I) D + omega I), gain beta = b_hat / (r + b_hat n) with n = ||k||^2,
+// and the reverse-KL update b = b_hat / (1 + u b_hat), u = mu n / (d_k r).
+__device__ __forceinline__ float kdn_iso_predict(float alpha2_mean, float b, float om) {
+  return fmaf(alpha2_mean, b, om);
+}
+__device__ __forceinline__ float kdn_iso_beta(float b_hat, float r, float n) {
+  return b_hat / fmaf(b_hat, n, r);
+}
+__device__ __forceinline__ float kdn_iso_update(float b_hat, float n, float mu_over_dk_r) {
+  return b_hat / fmaf(mu_over_dk_r * n, b_hat, 1.0f);
 }
 
 }  // namespace dn

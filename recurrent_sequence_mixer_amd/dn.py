@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdn.so")
 DN_OK = 0
 STATUS = {0: "DN_OK", -1: "DN_ERR_NULL", -2: "DN_ERR_SHAPE", -3: "DN_ERR_DTYPE", -4: "DN_ERR_GAIN",
           -6: "DN_ERR_UNSUPPORTED", -7: "DN_ERR_HIP", -8: "DN_ERR_ALIAS"}
-GAIN = {"kla": 0, "gdn": 1, "pgdn": 2, "kdn": 3, "explicit": 4}
+GAIN = {"kla": 0, "gdn": 1, "pgdn": 2, "kdn": 3, "explicit": 4, "kdn_iso": 5}
 DECAY = {"scalar": 0, "channel": 1}
 IO = {torch.float32: 0, torch.bfloat16: 1}
 
@@ -124,9 +124,10 @@ def chunk_fwd(q, k, v, gates: Dict[str, torch.Tensor], *, gain="kla", decay=None
     o = out if out is not None else torch.empty((B, H, T, dv), dtype=v.dtype, device=v.device)
     if want_state and S_final is None:
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=v.device)
-    has_aux = gain in ("pgdn", "kdn")
+    has_aux = gain in ("pgdn", "kdn", "kdn_iso")
     if has_aux and want_state and aux_final is None:
-        aux_final = torch.empty((B, H, dk), dtype=torch.float32, device=v.device)
+        aux_final = torch.empty((B, H) if gain == "kdn_iso" else (B, H, dk), dtype=torch.float32,
+                                device=v.device)
     gt = make_gates(gates)
     st = lib().dn_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(gt),
                             _ptr(S0), _ptr(aux0), _ptr(o), _ptr(S_final), _ptr(aux_final),
@@ -138,7 +139,8 @@ def chunk_fwd(q, k, v, gates: Dict[str, torch.Tensor], *, gain="kla", decay=None
 def decode_step(q, k, v, gates: Dict[str, torch.Tensor], S, aux=None, *, gain="kla", decay=None,
                 eps=1e-6, x=1.5, mu_info=1.0, out=None, stream=None):
     """One token for N sequences: q, k [N, H, dk], v [N, H, dv]; S [N, H, dk, dv]
-    (and aux [N, H, dk] for pgdn/kdn) updated in place.  Returns o [N, H, dv]."""
+    (and aux [N, H, dk] for pgdn/kdn, [N, H] for kdn_iso) updated in place.
+    Returns o [N, H, dv]."""
     N, H, dk = k.shape
     dv = v.shape[-1]
     if decay is None:
@@ -163,10 +165,11 @@ def gain_prep(k, gates: Dict[str, torch.Tensor], *, gain="kla", decay=None, eps=
     w = torch.empty((B, H, T, dk), dtype=torch.float32, device=dev)
     g = torch.empty((B, H, T, dk) if decay == "channel" else (B, H, T), dtype=torch.float32,
                     device=dev)
-    has_aux = gain in ("pgdn", "kdn")
+    has_aux = gain in ("pgdn", "kdn", "kdn_iso")
     nch = (T + C - 1) // C
-    aux_chunk = torch.empty((B, H, nch, dk), dtype=torch.float32, device=dev) if has_aux else None
-    aux_final = torch.empty((B, H, dk), dtype=torch.float32, device=dev) if has_aux else None
+    per = () if gain == "kdn_iso" else (dk,)
+    aux_chunk = torch.empty((B, H, nch) + per, dtype=torch.float32, device=dev) if has_aux else None
+    aux_final = torch.empty((B, H) + per, dtype=torch.float32, device=dev) if has_aux else None
     gt = make_gates(gates)
     st = lib().dn_gain_prep(ctypes.byref(desc), _ptr(k), ctypes.byref(gt), _ptr(aux0), _ptr(w),
                             _ptr(g), _ptr(aux_chunk), _ptr(aux_final), _stream(stream))
@@ -184,7 +187,8 @@ def to_device(arrays, io_dtype: torch.dtype, device="cuda"):
     out = {}
     for name, a in arrays.items():
         t = torch.from_numpy(a)
-        io_like = name in ("q", "k", "v", "omega", "w") or (name == "alpha" and a.ndim == 4)
+        # per-channel gates are io dtype; isotropic KDN's omega is a per-token scalar
+        io_like = name in ("q", "k", "v", "w") or (name in ("alpha", "omega") and a.ndim == 4)
         out[name] = t.to(device=device, dtype=io_dtype if io_like else torch.float32).contiguous()
     return out
 

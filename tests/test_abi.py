@@ -72,6 +72,7 @@ def _desc(**kw):
     (dict(dk=96), -2), (dict(dv=32), -2), (dict(B=0), -2), (dict(H=0), -2), (dict(T=-1), -2),
     (dict(B=300, H=300), -2), (dict(io=7), -3), (dict(gain=9), -4), (dict(decay=3), -4),
     (dict(eps=-1.0), -4), (dict(gain="pgdn", x=0.5), -4), (dict(gain="kdn", mu_info=0.0), -4),
+    (dict(gain="kdn_iso", mu_info=-1.0), -4), (dict(gain=6), -4),
     (dict(io=0, dk=128), -6),
 ])
 def test_chunk_fwd_rejects_bad_descriptor(kw, status):
@@ -91,6 +92,7 @@ def test_chunk_fwd_rejects_missing_pointers():
     assert _chunk(_desc(), gates=_gates(eta=None)) == -1
     assert _chunk(_desc(gain="pgdn")) == -1  # alphaP, betaP, mu_log missing
     assert _chunk(_desc(gain="kdn")) == -1  # omega, r missing
+    assert _chunk(_desc(gain="kdn_iso")) == -1  # omega, r missing
     assert _chunk(_desc(gain="explicit")) == -1  # w missing
     assert dn.lib().dn_chunk_fwd(None, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None,
                                  None) == -1

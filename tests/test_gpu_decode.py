@@ -38,7 +38,8 @@ def test_workload0_as_decode_steps_f32():
 
 
 @pytest.mark.parametrize("gain,decay", [("kla", "scalar"), ("gdn", "scalar"), ("pgdn", "scalar"),
-                                        ("kdn", "channel"), ("kdn", "scalar"), ("kla", "channel")])
+                                        ("kdn", "channel"), ("kdn", "scalar"), ("kla", "channel"),
+                                        ("kdn_iso", "channel"), ("kdn_iso", "scalar")])
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128)])
 def test_decode_gains(gain, decay, io, dk, dv):
@@ -51,6 +52,8 @@ def test_decode_gains(gain, decay, io, dk, dv):
     t = dn.to_device(inp, dt)
     S = t["S0"].clone()
     aux = torch.ones((6, 3, dk), device="cuda") if gain in ("pgdn", "kdn") else None
+    if gain == "kdn_iso":
+        aux = torch.ones((6, 3), device="cuda")
     outs = []
     for s in range(wl.T):
         gates = {n: t[n][:, :, s].contiguous() for n in ("alpha", "eta", "alphaP", "betaP", "omega", "r")
@@ -122,7 +125,8 @@ def test_prefill_then_decode_equals_one_pass():
 
 @pytest.mark.parametrize("gain,decay,io", [("kla", "scalar", "bf16"), ("pgdn", "scalar", "bf16"),
                                            ("kdn", "channel", "bf16"), ("kdn", "channel", "f32"),
-                                           ("gdn", "channel", "f32")])
+                                           ("gdn", "channel", "f32"), ("kdn_iso", "channel", "bf16"),
+                                           ("kdn_iso", "scalar", "f32")])
 def test_gain_prep_per_token(gain, decay, io):
     """dn_gain_prep's per-token write vectors, chunk-start aux and in-chunk
     cumulative log-decay against the oracle's trace."""

@@ -43,9 +43,9 @@ def test_kla_f32_workload0():
 
 
 @pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 130, 200])
-@pytest.mark.parametrize("gain", ["kla", "gdn", "pgdn", "kdn"])
+@pytest.mark.parametrize("gain", ["kla", "gdn", "pgdn", "kdn", "kdn_iso"])
 def test_f32_gains_ragged(gain, T):
-    decay = "channel" if gain == "kdn" else "scalar"
+    decay = "channel" if gain in ("kdn", "kdn_iso") else "scalar"
     keys = "unit" if gain in ("gdn", "pgdn") else "scaled"
     wl = W.Workload(f"{gain}_f32", gain, decay, "f32", 2, 3, T, 64, 64, keys=keys, seed=10 + T)
     inp = W.generate(wl)
@@ -59,7 +59,8 @@ def test_f32_gains_ragged(gain, T):
 @pytest.mark.parametrize("gain,decay,keys", [("kla", "scalar", "scaled"), ("gdn", "scalar", "unit"),
                                              ("pgdn", "scalar", "unit"), ("kdn", "channel", "scaled"),
                                              ("kla", "channel", "scaled"), ("kdn", "scalar", "scaled"),
-                                             ("pgdn", "channel", "unit")])
+                                             ("pgdn", "channel", "unit"), ("kdn_iso", "channel", "scaled"),
+                                             ("kdn_iso", "scalar", "scaled")])
 def test_bf16_gains_ragged(gain, decay, keys, T):
     wl = W.Workload(f"{gain}_{decay}_bf16", gain, decay, "bf16", 2, 2, T, 128, 128, keys=keys,
                     seed=100 + T)
@@ -82,7 +83,7 @@ def test_bf16_other_head_dims(dk, dv):
 @pytest.mark.parametrize("T", [37, 200])
 @pytest.mark.parametrize("dv", [64, 128])
 @pytest.mark.parametrize("gain,decay,keys", [("gdn", "scalar", "unit"), ("pgdn", "scalar", "unit"),
-                                             ("kdn", "channel", "scaled")])
+                                             ("kdn", "channel", "scaled"), ("kdn_iso", "channel", "scaled")])
 def test_bf16_gains_dk64(gain, decay, keys, dv, T):
     wl = W.Workload(f"{gain}_{decay}_bf16_dk64", gain, decay, "bf16", 2, 2, T, 64, dv, keys=keys,
                     seed=300 + T + dv)
@@ -102,6 +103,33 @@ def test_full_size_sampled_heads(idx):
     heads = [0, nheads // 3, nheads - 1]
     _check(wl, inp, heads, o, S, aux)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+
+
+def test_kdn_iso_full_size_sampled_heads():
+    """Isotropic KDN (Kalman Delta Networks §2.7) at the diagonal-KDN shape
+    B4 H16 T8192 d128 with per-channel decay, sampled heads."""
+    wl = W.WORKLOADS[3].replace(name="kdn_iso_bf16_B4H16T8192d128", gain="kdn_iso")
+    inp = W.generate(wl)
+    o, S, aux = gpu_chunk(wl, inp)
+    heads = [0, 21, 63]
+    _check(wl, inp, heads, o, S, aux)
+
+
+def test_kdn_mu_dk_and_kla_key_norm_only():
+    """The pages' other gain settings on the same kernels: diagonal KDN with
+    information scaling mu = d_k (Kalman Delta Networks §2.5), and KLA's
+    key-norm-only step 1 / ||k||^2 (eta = 1, eps = 0; Kaczmarz Linear
+    Attention ablation)."""
+    wl = W.Workload("kdn_mu128", "kdn", "channel", "bf16", 2, 2, 200, 128, 128, mu_info=128.0,
+                    seed=41)
+    inp = W.generate(wl)
+    o, S, aux = gpu_chunk(wl, inp)
+    _check(wl, inp, None, o, S, aux)
+    wl = W.Workload("kla_keynorm", "kla", "scalar", "bf16", 2, 2, 200, 128, 128, eps=0.0, seed=42)
+    inp = W.generate(wl)
+    inp["eta"] = np.ones_like(inp["eta"])
+    o, S, _ = gpu_chunk(wl, inp)
+    _check(wl, inp, None, o, S)
 
 
 # ---------------------------------------------------------------- edge cases
