@@ -6,7 +6,7 @@ One step = one dn_chunk_fwd call (the fused chunked forward: gains, intra-chunk
 products, triangular solve, output and state propagation) over the KLA bf16
 workload B=8, H=16, T=4096, d_k=d_v=128, C=64, inputs resident in HBM.
 `value` is tokens/s (B*T tokens per call).  The same line also reports the
-PGDN and diagonal-KDN forwards and the batched decode step (HBM GB/s), the
+PGDN, diagonal-KDN and isotropic-KDN forwards and the batched decode step (HBM GB/s), the
 roofline of the chunked-forward kernel, and the fp64 oracle timed on a
 bounded sample on the host CPU.
 """
@@ -46,9 +46,12 @@ def chunk_bytes(wl):
         per_ht += 4  # alpha
     else:
         per_ht += es * wl.dk
-    per_ht += {"kla": 4, "gdn": 4, "pgdn": 12, "kdn": 4 + es * wl.dk, "explicit": es * wl.dk}[wl.gain]
+    per_ht += {"kla": 4, "gdn": 4, "pgdn": 12, "kdn": 4 + es * wl.dk, "kdn_iso": 8,
+               "explicit": es * wl.dk}[wl.gain]
     state = 2 * wl.B * wl.H * wl.dk * wl.dv * 4
     aux = 2 * wl.B * wl.H * wl.dk * 4 if wl.gain in ("pgdn", "kdn") else 0
+    if wl.gain == "kdn_iso":
+        aux = 2 * wl.B * wl.H * 4
     return ht * per_ht + state + aux
 
 
@@ -91,6 +94,8 @@ def time_chunk(wl, steps, warmup, settle_s=0.0):
     o = torch.empty_like(t["v"])
     S = torch.empty_like(t["S0"])
     aux = torch.empty((wl.B, wl.H, wl.dk), device="cuda") if wl.gain in ("pgdn", "kdn") else None
+    if wl.gain == "kdn_iso":
+        aux = torch.empty((wl.B, wl.H), device="cuda")
     call = lambda: dn.chunk_fwd(t["q"], t["k"], t["v"], gates, gain=wl.gain, eps=wl.eps, x=wl.x,
                                 mu_info=wl.mu_info, S0=t["S0"], out=o, S_final=S, aux_final=aux)
     settle(call, settle_s)
@@ -267,8 +272,9 @@ def main():
     log(f"[bench] {wl.name}: {ms:.3f} ms/step")
     if not args.no_extra:
         extra = {}
-        for idx in (2, 3):
-            w2 = W.WORKLOADS[idx]
+        # isotropic KDN (Kalman Delta Networks §2.7) at the diagonal-KDN shape
+        iso = W.WORKLOADS[3].replace(name="kdn_iso_bf16_B4H16T8192d128", gain="kdn_iso")
+        for w2 in (W.WORKLOADS[2], W.WORKLOADS[3], iso):
             ms2, _ = time_chunk(w2, max(5, args.steps // 2), args.warmup, args.settle_s)
             b2 = chunk_bytes(w2)
             extra[w2.gain] = {"workload": w2.name, "ms": ms2, "tokens_per_s": w2.tokens / (ms2 * 1e-3),
