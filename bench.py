@@ -274,10 +274,14 @@ def main():
         extra = {}
         # isotropic KDN (Kalman Delta Networks §2.7) at the diagonal-KDN shape
         iso = W.WORKLOADS[3].replace(name="kdn_iso_bf16_B4H16T8192d128", gain="kdn_iso")
-        for w2 in (W.WORKLOADS[2], W.WORKLOADS[3], iso):
+        # batch-1 long prefill at the pages' 131072-token length (8 heads: 16 workgroups)
+        longp = W.Workload("kla_long_B1H8T131072d128", "kla", "scalar", "bf16", 1, 8, 131072, 128,
+                           128, seed=51)
+        for w2 in (W.WORKLOADS[2], W.WORKLOADS[3], iso, longp):
             ms2, _ = time_chunk(w2, max(5, args.steps // 2), args.warmup, args.settle_s)
             b2 = chunk_bytes(w2)
-            extra[w2.gain] = {"workload": w2.name, "ms": ms2, "tokens_per_s": w2.tokens / (ms2 * 1e-3),
+            key = "long_prefill" if w2 is longp else w2.gain
+            extra[key] = {"workload": w2.name, "ms": ms2, "tokens_per_s": w2.tokens / (ms2 * 1e-3),
                               "hbm_gbs": b2 / (ms2 * 1e-3) / 1e9,
                               "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
                               "mfma_frac": chunk_flops(w2) / (ms2 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}

@@ -115,6 +115,18 @@ def test_kdn_iso_full_size_sampled_heads():
     _check(wl, inp, heads, o, S, aux)
 
 
+def test_long_prefill_batch1_sampled_head():
+    """Batch-1 long prefill (B1 H8 T131072 d128, KLA bf16; the pages' long-context
+    prefill length): one launch walks 2048 chunks per head; one head is
+    compared in full with the oracle."""
+    wl = W.Workload("kla_long_B1H8T131072d128", "kla", "scalar", "bf16", 1, 8, 131072, 128, 128,
+                    seed=51)
+    inp = W.generate(wl)
+    o, S, _ = gpu_chunk(wl, inp)
+    _check(wl, inp, [5], o, S)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+
+
 def test_kdn_mu_dk_and_kla_key_norm_only():
     """The pages' other gain settings on the same kernels: diagonal KDN with
     information scaling mu = d_k (Kalman Delta Networks §2.5), and KLA's
