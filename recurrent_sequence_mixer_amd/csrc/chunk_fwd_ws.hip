@@ -219,7 +219,8 @@ struct Smem {
   static constexpr int PT = CH + 8;   // [token][token] rows, bf16
   static constexpr int P16 = 16 + 8;  // rows of 16-wide blocks
   static constexpr bool HAS_W = GAIN == GAIN_PGDN || GAIN == GAIN_EXPLICIT;
-  static constexpr bool CD = GAIN == GAIN_KDN;  // KDN with per-channel decay
+  // KDN-family gains with per-channel decay (diagonal and isotropic KDN)
+  static constexpr bool CD = GAIN == GAIN_KDN || GAIN == GAIN_KDN_ISO;
   static constexpr bool PG = GAIN == GAIN_PGDN;
   // KDN: k holds raw k, then (in place) the scaled write vectors W^, by parity;
   // q[0] raw q, then Q^ in place; q[1] K^; w[0], w[1] the raw alpha, omega
@@ -263,7 +264,11 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
   constexpr int V_LOADS = CH * BV / (NP * VEC);
   constexpr bool HAS_W = GAIN == GAIN_PGDN || GAIN == GAIN_EXPLICIT;
   constexpr bool PG = GAIN == GAIN_PGDN;
-  constexpr bool CD = GAIN == GAIN_KDN;  // KDN, per-channel decay
+  // KDN-family gains with per-channel decay: diagonal KDN (a variance per
+  // channel) and isotropic KDN (one variance per head, Kalman Delta Networks
+  // §2.7, Eq. 40), which share the decay-scaled operands of this mode
+  constexpr bool CD = GAIN == GAIN_KDN || GAIN == GAIN_KDN_ISO;
+  constexpr bool ISO = GAIN == GAIN_KDN_ISO;
   constexpr bool HAS_ETA = GAIN != GAIN_EXPLICIT && !CD;
   // Gains straight from the staging registers (no per-channel scan): the
   // gains of chunk c + 1 are formed in P2 as it is staged, and its tiles in
@@ -347,7 +352,9 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
         for (int dt = 0; dt < NDT; ++dt) S[dt] = zero4();
       }
     } else if constexpr (PROD) {
-      if ((PG || CD) && ptid < DK) sm.acarry[ptid] = a.aux0 ? a.aux0[static_cast<long>(bh) * DK + ptid] : 1.f;
+      if ((PG || (CD && !ISO)) && ptid < DK) sm.acarry[ptid] = a.aux0 ? a.aux0[static_cast<long>(bh) * DK + ptid] : 1.f;
+      // isotropic KDN: the head's variance entering chunk x sits in acarry[x % 2]
+      if (ISO && ptid == 0) sm.acarry[0] = a.aux0 ? a.aux0[bh] : 1.f;
       // KDN: the decay lives in the operands, the token-decay arrays stay 0 / 1
       if (CD && ptid < 2 * CH) {
         sm.g2[ptid >> 6][ptid & 63] = 0.f;
@@ -360,6 +367,7 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
     u32x4 pk[KV_LOADS], pq[KV_LOADS], pwv[GAIN == GAIN_EXPLICIT ? KV_LOADS : 1], pv[V_LOADS];
     u32x4 pa[CD ? KV_LOADS : 1], po[CD ? KV_LOADS : 1];  // KDN: alpha, omega pieces
     float l_alpha = 1.f, l_eta = 0.f, l_ap = 1.f, l_bp = 0.f;  // loaders: gates of token ltid
+    float l_om = 0.f;  // loaders: isotropic KDN process noise of token ltid
     float pg_start = 0.f;  // PGDN: carried statistic read by pass 1 (segment 0)
 
     // per-lane byte offsets inside a chunk: the k / q / w pieces (row-major
@@ -412,11 +420,12 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
         const int n = ntok(c);
         const long off = qk_base + static_cast<long>(t0) * DK;
         const auto ra = rsrc(static_cast<const uint16_t*>(a.g.alpha) + off, 2 * n * DK);
-        const auto rw = rsrc(static_cast<const uint16_t*>(a.g.omega) + off, 2 * n * DK);
 #pragma unroll
-        for (int j = 0; j < KV_LOADS; ++j) {
-          pa[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, koff[j], 0, 0);
-          po[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, koff[j], 0, 0);
+        for (int j = 0; j < KV_LOADS; ++j) pa[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, koff[j], 0, 0);
+        if constexpr (!ISO) {  // isotropic KDN's omega is a per-token scalar (with the gates)
+          const auto rw = rsrc(static_cast<const uint16_t*>(a.g.omega) + off, 2 * n * DK);
+#pragma unroll
+          for (int j = 0; j < KV_LOADS; ++j) po[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, koff[j], 0, 0);
         }
       }
     };
@@ -447,7 +456,27 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           const int t = e / DK, d = e % DK;
           const u32x4 one = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
           *reinterpret_cast<u32x4*>(&sm.w[0][KL::idx(t, d)]) = t < n ? pa[j] : one;
-          *reinterpret_cast<u32x4*>(&sm.w[1][KL::idx(t, d)]) = po[j];
+          if constexpr (!ISO) *reinterpret_cast<u32x4*>(&sm.w[1][KL::idx(t, d)]) = po[j];
+          if constexpr (ISO) {
+            // isotropic KDN: ||k_t||^2 and the sum of alpha_t^2 over the
+            // channels, from the staging registers (DK / 8 consecutive lanes per
+            // token; k is 0 and alpha 1 past the end)
+            const u32x4 al4 = t < n ? pa[j] : one;
+            float sk = 0.f, sa = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float k0 = __uint_as_float(pk[j][i] << 16), k1 = __uint_as_float(pk[j][i] & 0xFFFF0000u);
+              const float a0 = __uint_as_float(al4[i] << 16), a1 = __uint_as_float(al4[i] & 0xFFFF0000u);
+              sk = fmaf(k0, k0, fmaf(k1, k1, sk));
+              sa = fmaf(a0, a0, fmaf(a1, a1, sa));
+            }
+            sk = group_sum<DK / VEC>(sk);
+            sa = group_sum<DK / VEC>(sa);
+            if (d == 0) {
+              sm.msum[4][t] = sk;
+              sm.msum[4][CH + t] = sa;
+            }
+          }
         }
       }
     };
@@ -476,8 +505,12 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
       const int n = ntok(c);
       const long tok = static_cast<long>(bh) * T + t0;
       if constexpr (CD) {
-        // KDN: the observation noise r_t (alpha is per channel, in its own tile)
+        // KDN: the observation noise r_t (alpha is per channel, in its own tile);
+        // isotropic KDN also its process noise omega_t
         l_eta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.r + tok, 4 * n), 4 * ltid, 0, 0));
+        if constexpr (ISO)
+          l_om = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rsrc(static_cast<const float*>(a.g.omega) + tok, 4 * n), 4 * ltid, 0, 0));
         return;
       }
       l_alpha = __uint_as_float(
@@ -497,7 +530,8 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           // r_t, and the information scale mu / r_t of the variance update
           // (0 past the end)
           sm.geta[c & 1][ltid] = l_eta;
-          sm.galpha[c & 1][ltid] = ltid < n ? a.g.mu_info * __builtin_amdgcn_rcpf(l_eta) : 0.f;
+          // isotropic KDN: omega_t instead (0 past the end)
+          sm.galpha[c & 1][ltid] = ISO ? l_om : ltid < n ? a.g.mu_info * __builtin_amdgcn_rcpf(l_eta) : 0.f;
         } else if constexpr (PG) {
           const bool ok = ltid < n;
           sm.eta[ltid] = l_eta;
@@ -634,8 +668,12 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll 1
         for (int t4 = 0; t4 < SL; t4 += 4) {
           const int t = g * SL + t4;
-          const f32x4 kk = KL::col4(kb, t, cb, lane);
           const f32x4 al = KL::col4(sm.w[0], t, cb, lane);
+          if constexpr (ISO) {  // isotropic KDN: the segment's decay product only
+            pr *= al[0] * al[1] * (al[2] * al[3]);
+            continue;
+          }
+          const f32x4 kk = KL::col4(kb, t, cb, lane);
           const f32x4 om = KL::col4(sm.w[1], t, cb, lane);
           const f32x4 mu4 = *reinterpret_cast<const f32x4*>(&sm.galpha[c & 1][t]);
 #pragma unroll
@@ -672,8 +710,9 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
         for (int gg = 0; gg < NSEG; ++gg) {
           const float pr = sm.msum[3][gg * DK + d];
           if (gg < g) {
-            p = fmaf(sm.msum[0][gg * DK + d], p, sm.msum[1][gg * DK + d]) *
-                __builtin_amdgcn_rcpf(fmaf(sm.msum[2][gg * DK + d], p, 1.f));
+            if constexpr (!ISO)
+              p = fmaf(sm.msum[0][gg * DK + d], p, sm.msum[1][gg * DK + d]) *
+                  __builtin_amdgcn_rcpf(fmaf(sm.msum[2][gg * DK + d], p, 1.f));
             if (gg > RS) num *= pr;
           } else if (gg <= RS) {
             den *= pr;
@@ -706,14 +745,20 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
               const int jj = j + h2;
-              const float ph = fmaf(al[jj] * al[jj], p, om[jj]);
-              const float pk = ph * kk[jj];
               e *= al[jj];
               xk[h2] = kk[jj] * e;
               xq[h2] = qq[jj] * e;
-              xw[h2] = pk * __builtin_amdgcn_rcpf(e);
-              // p_hat / (1 + u p_hat) with u p_hat = (mu / r) k (p_hat k)
-              p = ph * __builtin_amdgcn_rcpf(fmaf(mu4[jj] * kk[jj], pk, 1.f));
+              if constexpr (ISO) {
+                // isotropic KDN: W^ = k 2^(G_r - G_t); the gain beta_t is the
+                // column scale
+                xw[h2] = kk[jj] * __builtin_amdgcn_rcpf(e);
+              } else {
+                const float ph = fmaf(al[jj] * al[jj], p, om[jj]);
+                const float pk = ph * kk[jj];
+                xw[h2] = pk * __builtin_amdgcn_rcpf(e);
+                // p_hat / (1 + u p_hat) with u p_hat = (mu / r) k (p_hat k)
+                p = ph * __builtin_amdgcn_rcpf(fmaf(mu4[jj] * kk[jj], pk, 1.f));
+              }
             }
             const uint32_t pkh = pack_bf2(xk[0], xk[1]), pqh = pack_bf2(xq[0], xq[1]),
                            pkw = pack_bf2(xw[0], xw[1]);
@@ -725,7 +770,7 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
             kw[KL::idx(t + j + 1, d)] = static_cast<uint16_t>(pkw >> 16);
           }
         }
-        if (g == NSEG - 1) sm.acarry[d] = p;
+        if (!ISO && g == NSEG - 1) sm.acarry[d] = p;
       }
     };
 
@@ -803,7 +848,44 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
     float cdi = 0.f;
     f32x4 cdj = zero4();
     auto diag_gains = [&](int c, int n) __attribute__((always_inline)) {
-      if constexpr (CD) {
+      if constexpr (ISO) {
+        // isotropic KDN (Kalman Delta Networks §2.7, Eq. 40), lane = token t of
+        // the chunk: the head's variance runs through the chunk as a prefix
+        // product of the Moebius maps b -> (a b + omega) / (u a b + 1 + u omega),
+        // u = mu ||k||^2 / (d_k r), a = mean alpha^2 (padding: the identity).
+        // Every producer wavefront forms the same scan, so each has the step
+        // sizes beta_t = b_hat / (r + b_hat ||k||^2) of its block in registers.
+        const int t = lane;
+        const bool ok = t < n;
+        const float nk = sm.msum[4][t], am = sm.msum[4][CH + t] * (1.0f / DK);
+        const float om = sm.galpha[c & 1][t], rr = ok ? sm.geta[c & 1][t] : 1.f;
+        const float u = ok ? a.g.mu_info * nk / (DK * rr) : 0.f;
+        float m00 = am, m01 = om, m10 = u * am, m11 = fmaf(u, om, 1.f);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y00 = __shfl_up(m00, off), y01 = __shfl_up(m01, off);
+          const float y10 = __shfl_up(m10, off), y11 = __shfl_up(m11, off);
+          if (lane >= off) {  // (maps of tokens t - off + 1 .. t) o (maps before)
+            const float n00 = fmaf(m00, y00, m01 * y10), n01 = fmaf(m00, y01, m01 * y11);
+            const float n10 = fmaf(m10, y00, m11 * y10), n11 = fmaf(m10, y01, m11 * y11);
+            const float sc = __builtin_amdgcn_rcpf(n11);  // projective: keep (1, 1) at 1
+            m00 = n00 * sc;
+            m01 = n01 * sc;
+            m10 = n10 * sc;
+            m11 = 1.f;
+          }
+        }
+        const float b0 = sm.acarry[c & 1];
+        const float bt = fmaf(m00, b0, m01) / fmaf(m10, b0, m11);  // variance after token t
+        const float bs = __shfl_up(bt, 1);                           // (every lane takes part)
+        const float bp = lane == 0 ? b0 : bs;                         // variance before token t
+        const float bh_ = fmaf(am, bp, om);
+        const float beta = ok ? bh_ / fmaf(bh_, nk, rr) : 0.f;
+        if (pw == 0 && lane == CH - 1) sm.acarry[(c + 1) & 1] = bt;
+        cdi = __shfl(beta, 16 * pw + c16);
+#pragma unroll
+        for (int u4 = 0; u4 < 4; ++u4) cdj[u4] = __shfl(beta, 16 * pw + 4 * g4 + u4);
+      } else       if constexpr (CD) {
         // the diagonal entry z_t of token t = 16 p + x sits in lane 16 (x / 4) + x,
         // slot x % 4; the other lanes of the block fetch it with a lane shuffle
         const float zs = c16 & 2 ? (c16 & 1 ? at[3] : at[2]) : (c16 & 1 ? at[1] : at[0]);
@@ -1297,8 +1379,9 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           for (int i = 0; i < 4; ++i) base[(KL::sigma_channel(dt, 0, i)) * a.dv] = S[dt][i];
       }
     } else if constexpr (PROD) {
-      if ((PG || CD) && a.aux_final && slice == 0 && ptid < DK)
+      if ((PG || (CD && !ISO)) && a.aux_final && slice == 0 && ptid < DK)
         a.aux_final[static_cast<long>(bh) * DK + ptid] = sm.acarry[ptid];
+      if (ISO && a.aux_final && slice == 0 && ptid == 0) a.aux_final[bh] = sm.acarry[nchunks & 1];
     }
   };
   if (wave < 4) {
@@ -1343,8 +1426,10 @@ hipError_t launch_chunk_fwd_bf16_scalar(const ChunkArgs& a, int gain, hipStream_
 #undef DN_WS
 }
 
-// bf16 io, KDN with per-channel decay.
-hipError_t launch_chunk_fwd_bf16_kdn(const ChunkArgs& a, hipStream_t st) {
+// bf16 io, diagonal or isotropic KDN with per-channel decay.
+hipError_t launch_chunk_fwd_bf16_kdn(const ChunkArgs& a, int gain, hipStream_t st) {
+  if (gain == GAIN_KDN_ISO)
+    return a.dk == 128 ? launch_ws_one<128, GAIN_KDN_ISO>(a, st) : launch_ws_one<64, GAIN_KDN_ISO>(a, st);
   if (a.dk == 128) return launch_ws_one<128, GAIN_KDN>(a, st);
   return launch_ws_one<64, GAIN_KDN>(a, st);
 }

@@ -65,8 +65,8 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, int io_bf16, int gain, bool chan
                             hipStream_t st);
 // bf16 io, scalar decay, gains KLA / GDN / PGDN / explicit (chunk_fwd_bf16.hip)
 hipError_t launch_chunk_fwd_bf16_scalar(const ChunkArgs& a, int gain, hipStream_t st);
-// bf16 io, KDN with per-channel decay (chunk_fwd_ws.hip)
-hipError_t launch_chunk_fwd_bf16_kdn(const ChunkArgs& a, hipStream_t st);
+// bf16 io, diagonal or isotropic KDN with per-channel decay (chunk_fwd_ws.hip)
+hipError_t launch_chunk_fwd_bf16_kdn(const ChunkArgs& a, int gain, hipStream_t st);
 hipError_t launch_gain_prep(const GainPrepArgs& a, int io_bf16, int gain, bool channel,
                             hipStream_t st);
 
