@@ -69,7 +69,7 @@ def _desc(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dk=96), -2), (dict(dv=32), -2), (dict(B=0), -2), (dict(H=0), -2), (dict(T=-1), -2),
+    (dict(dk=96), -2), (dict(dv=32), -2), (dict(dv=96), -2), (dict(dv=4096), -2), (dict(B=0), -2), (dict(H=0), -2), (dict(T=-1), -2),
     (dict(B=300, H=300), -2), (dict(io=7), -3), (dict(gain=9), -4), (dict(decay=3), -4),
     (dict(eps=-1.0), -4), (dict(gain="pgdn", x=0.5), -4), (dict(gain="kdn", mu_info=0.0), -4),
     (dict(gain="kdn_iso", mu_info=-1.0), -4), (dict(gain=6), -4),
@@ -121,6 +121,7 @@ def test_decode_rejects_bad_arguments():
     assert f(_desc(T=1), S=None) == -1
     assert f(_desc(T=1, gain="pgdn")) == -1
     assert f(_desc(T=1, dk=48)) == -2
+    assert f(_desc(T=1, dv=256)) == -2  # wider value heads are built for the chunked forward only
 
 
 def test_gain_prep_rejects_bad_arguments():

@@ -77,6 +77,21 @@ def test_bf16_other_head_dims(dk, dv):
     _check(wl, inp, None, o, S)
 
 
+# wider value heads, d_v = v_expand d_k (2 and 4): more 64-column value slices
+# per head on the same kernels
+@pytest.mark.parametrize("gain,decay,keys,io,dk,dv", [
+    ("kla", "scalar", "scaled", "bf16", 128, 256), ("kla", "scalar", "scaled", "bf16", 128, 512),
+    ("pgdn", "scalar", "unit", "bf16", 128, 256), ("kdn", "channel", "scaled", "bf16", 128, 256),
+    ("kdn_iso", "channel", "scaled", "bf16", 128, 256), ("kla", "channel", "scaled", "bf16", 64, 256),
+    ("kla", "scalar", "scaled", "f32", 64, 256)])
+def test_value_expansion(gain, decay, keys, io, dk, dv):
+    wl = W.Workload(f"{gain}_{decay}_{io}_dv{dv}", gain, decay, io, 1, 2, 150, dk, dv, keys=keys,
+                    seed=400 + dv)
+    inp = W.generate(wl)
+    o, S, aux = gpu_chunk(wl, inp)
+    _check(wl, inp, None, o, S, aux)
+
+
 # d_k = 64 changes the work split of the per-channel scans: the PGDN
 # statistic and the KDN channel-decay variance both run in eight 8-token
 # segments per channel; ragged lengths cover the partial last chunk
