@@ -123,6 +123,41 @@ def test_prefill_then_decode_equals_one_pass():
     assert max_rel_err(flat_heads(S.cpu().numpy()), S_ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("decay", ["channel", "scalar"])
+def test_kdn_iso_prefill_decode_and_resume(decay):
+    """Isotropic KDN: dn_chunk_fwd over a prefix (ragged), a second
+    dn_chunk_fwd resuming from its (S, b), then dn_decode_step token by
+    token, against one oracle pass (the head's variance b is handed over
+    between the chunk kernel and the decode kernel)."""
+    dn = _dn()
+    wl = W.Workload("iso_pd", "kdn_iso", decay, "bf16", 2, 2, 170, 128, 128, seed=13)
+    inp = W.generate(wl)
+    t = dn.to_device(inp, torch.bfloat16)
+    P1, P2 = 70, 150
+    names = ("alpha", "omega", "r")
+    part = lambda a, b: {n: t[n][:, :, a:b].contiguous() for n in names}
+    seq = lambda n, a, b: t[n][:, :, a:b].contiguous()
+    kw = dict(gain="kdn_iso", mu_info=wl.mu_info)
+    o1, S, b = dn.chunk_fwd(seq("q", 0, P1), seq("k", 0, P1), seq("v", 0, P1), part(0, P1),
+                            S0=t["S0"], **kw)
+    b2 = torch.empty_like(b)
+    o2, _, _ = dn.chunk_fwd(seq("q", P1, P2), seq("k", P1, P2), seq("v", P1, P2), part(P1, P2),
+                            S0=S, aux0=b, S_final=S, aux_final=b2, **kw)
+    outs = [o1, o2]
+    for s in range(P2, wl.T):
+        g = {n: t[n][:, :, s].contiguous() for n in names}
+        outs.append(dn.decode_step(t["q"][:, :, s].contiguous(), t["k"][:, :, s].contiguous(),
+                                   t["v"][:, :, s].contiguous(), g, S, b2, **kw)[:, :, None])
+    torch.cuda.synchronize()
+    o = torch.cat(outs, dim=2).float().cpu().numpy()
+    o_ref, S_ref, b_ref, _ = run_workload(wl, inp)
+    eo = max_rel_err(flat_heads(o), o_ref)
+    es = max_rel_err(flat_heads(S.cpu().numpy()), S_ref)
+    eb = max_rel_err(flat_heads(b2.cpu().numpy()), b_ref)
+    print(f"iso prefill/resume/decode {decay}: o {eo:.2e} S {es:.2e} b {eb:.2e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"] and eb <= 1e-3
+
+
 @pytest.mark.parametrize("gain,decay,io", [("kla", "scalar", "bf16"), ("pgdn", "scalar", "bf16"),
                                            ("kdn", "channel", "bf16"), ("kdn", "channel", "f32"),
                                            ("gdn", "channel", "f32"), ("kdn_iso", "channel", "bf16"),
