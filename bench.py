@@ -152,10 +152,18 @@ def time_decode(dwl, steps_timed, settle_s=0.0):
 
 
 def kernel_source_hash():
+    """sha256[:16] of the chunk kernel's code: its sources with comments and
+    blank lines removed, so that an edit of the comments alone keeps the
+    counters that were taken on the same code."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

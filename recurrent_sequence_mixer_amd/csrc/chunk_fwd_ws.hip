@@ -1,5 +1,6 @@
-// Chunked forward, bf16 operands, scalar decay (KLA, GDN, PGDN, explicit
-// write vectors): producer and consumer wavefronts.
+// Chunked forward, bf16 operands: scalar decay (KLA, GDN, PGDN, explicit
+// write vectors) and per-channel decay with the KDN gains (diagonal and
+// isotropic): consumer, producer and loader wavefronts.
 //
 // Chunk form (our statement of Kaczmarz Linear Attention §2.5 Eqs. 7-9 and
 // Preconditioned DeltaNet §2.6 Eq. 6), per chunk of 64 tokens with G the
@@ -8,36 +9,42 @@
 //   L = strict_lower(K W^T) 2^(G_i - G_j) c_j,  M = lower(Q W^T) 2^(G_i - G_j) c_j,
 //   (I + L) U = V - diag(g) K S,   O = diag(g) Q S + M U,
 //   S_out = g_n S + W^T diag(f) U,   f_j = 2^(G_n - G_j) c_j.
+// With per-channel decay the operands carry the decay instead: K^, Q^ and W^
+// are scaled per channel relative to token 31 (see cd_pass2) and S enters
+// the products scaled by the decay from the chunk start to token 31.
 //
-// A workgroup owns one (batch, head) and 64 value columns and runs eight
-// wavefronts, two per SIMD:
+// A workgroup owns one (batch, head) and 64 value columns and runs twelve
+// wavefronts, three per SIMD:
 //   consumers (waves 0..3): wave ct owns value columns 16 ct .. 16 ct + 15 and
 //     keeps the whole d_k x 16 slice of S in registers.  Per chunk it forms
 //     K S and (Q S)^T, runs the blocked triangular solve, adds M U, writes the
-//     output tile and updates S; the consumers also move q and v
-//     HBM -> registers -> LDS.
-//   producers (waves 4..7): build the chunk-local operands (the L and M
-//     tiles, the inverses of the diagonal blocks of I + L, the gains) and move
-//     k (w) and the gates HBM -> registers -> LDS.
-// Per chunk c, three phases separated by workgroup barriers:
-//   P1  consumers: K S -> R = V - g K S, and (Q S)^T; q of chunk c + 1 into
-//       LDS and its loads for c + 2.
-//       producers: the decay of chunk c + 1 from its staging registers, its
-//       k into LDS and its loads for c + 2; the off-diagonal L and M tiles
-//       of c and (I + L_bb)^-1 of c.
-//   P2  consumers: solve -> U; O = g Q S + M U -> HBM; v of chunk c + 1
-//       into LDS and its loads for c + 2.
-//       producers: the raw L and M tile products of chunk c + 1, and its
-//       column scales (the key norms of KLA are the diagonal of the raw
-//       K K^T).
-//   P3  consumers: S = g_n S + W^T diag(f) U.
-//       producers: scale the diagonal L and M blocks of chunk c + 1.
+//     output tile and updates S.
+//   producers (waves 4..7): build the chunk-local operands: the gains and
+//     decays, the L and M tiles (the diagonal blocks and some of the twelve
+//     off-diagonal tiles), the inverses of the diagonal blocks of I + L.
+//   loaders (waves 8..11): issue every global load, one chunk step ahead,
+//     stage it into LDS, and take the off-diagonal tiles and the share of the
+//     statistic scans that their other work leaves room for.
+// Scalar-decay gains formed from the staging registers (KLA, GDN, explicit):
+// per chunk c, three phases separated by workgroup barriers:
+//   P1  consumers: K S -> R = V - g K S, and (Q S)^T of c.
+//       producers: the decay of c + 1; the off-diagonal L and M tiles of c
+//       scaled; (I + L_bb)^-1 of c.  loaders: k, q of c + 1 into LDS, the
+//       loads of k and the gates of c + 2; their off-diagonal tiles of c scaled.
+//   P2  consumers: solve -> U; O = g Q S + M U -> HBM.
+//       producers: the raw L and M tile products of c + 1 and its column
+//       scales (the key norms of KLA are the diagonal of the raw K K^T).
+//       loaders: v of c + 1 into LDS, the loads of q, v of c + 2; their raw
+//       off-diagonal tiles of c + 1.
+//   P3  consumers: S = g_n S + W^T diag(f) U.  producers: the diagonal L and
+//       M blocks of c + 1 scaled.  loaders: the gates of c + 2 into LDS.
 // PGDN, whose write vectors come out of a statistic scan over the LDS copy
-// of k, stages k of chunk c + 1 in P2, scans in P3 (split around the scan's
-// synchronisation) and forms its tiles in P1.  Every load has a whole chunk
-// step to arrive.  k, q, w and the gains are double buffered by chunk parity;
-// every other LDS buffer is single: it is rewritten only after its last
-// reader of the previous chunk has passed a barrier.
+// of k, forms its tiles of c in P1 and scans chunk c + 1 in P2 (pass 1) and
+// P3 (pass 2) on producers and loaders.  The KDN gains run four phases per
+// chunk (see the KDN loop).  Every load has a whole chunk step to arrive.  k,
+// q, w and the gains are double buffered by chunk parity; every other LDS
+// buffer is single: it is rewritten only after its last reader of the
+// previous chunk has passed a barrier.
 //
 // Register-resident operands.  In v_mfma_f32_16x16x32_bf16 lane l supplies
 // k = 8 (l / 16) .. +7 of its row (A) or column (B), and the accumulator holds
