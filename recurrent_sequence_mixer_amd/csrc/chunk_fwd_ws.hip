@@ -685,14 +685,14 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           const f32x4 mu4 = *reinterpret_cast<const f32x4*>(&sm.galpha[c & 1][t]);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
+            // M_t = [[1, 0], [u, 1]] [[a^2, omega], [0, 1]]: the prediction
+            // acts on the top row, the update adds u times it to the bottom row
             const float aa = al[j] * al[j];
-            const float ua = mu4[j] * kk[j] * kk[j] * aa, ue = fmaf(mu4[j] * kk[j] * kk[j], om[j], 1.f);
-            const float n00 = fmaf(aa, m00, om[j] * m10), n01 = fmaf(aa, m01, om[j] * m11);
-            const float n10 = fmaf(ua, m00, ue * m10), n11 = fmaf(ua, m01, ue * m11);
-            m00 = n00;
-            m01 = n01;
-            m10 = n10;
-            m11 = n11;
+            const float u = mu4[j] * kk[j] * kk[j];
+            m00 = fmaf(aa, m00, om[j] * m10);
+            m01 = fmaf(aa, m01, om[j] * m11);
+            m10 = fmaf(u, m00, m10);
+            m11 = fmaf(u, m01, m11);
             pr *= al[j];
           }
           // the map is projective: divide by its (1, 1) entry, which is >= 1
