@@ -744,6 +744,17 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           const f32x4 al = KL::col4(sm.w[0], t, cb, lane);
           const f32x4 om = KL::col4(sm.w[1], t, cb, lane);
           const f32x4 mu4 = *reinterpret_cast<const f32x4*>(&sm.galpha[c & 1][t]);
+          // the decay 2^(G_t - G_r) at the four tokens, and its inverse: one
+          // reciprocal at the last token, then back through the alphas
+          f32x4 et, ie;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            e *= al[j];
+            et[j] = e;
+          }
+          ie[3] = __builtin_amdgcn_rcpf(e);
+#pragma unroll
+          for (int j = 3; j > 0; --j) ie[j - 1] = ie[j] * al[j];
           // two tokens per step: one conversion packs the pair, whose halves
           // go to their two rows
 #pragma unroll
@@ -752,17 +763,16 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
               const int jj = j + h2;
-              e *= al[jj];
-              xk[h2] = kk[jj] * e;
-              xq[h2] = qq[jj] * e;
+              xk[h2] = kk[jj] * et[jj];
+              xq[h2] = qq[jj] * et[jj];
               if constexpr (ISO) {
                 // isotropic KDN: W^ = k 2^(G_r - G_t); the gain beta_t is the
                 // column scale
-                xw[h2] = kk[jj] * __builtin_amdgcn_rcpf(e);
+                xw[h2] = kk[jj] * ie[jj];
               } else {
                 const float ph = fmaf(al[jj] * al[jj], p, om[jj]);
                 const float pk = ph * kk[jj];
-                xw[h2] = pk * __builtin_amdgcn_rcpf(e);
+                xw[h2] = pk * ie[jj];
                 // p_hat / (1 + u p_hat) with u p_hat = (mu / r) k (p_hat k)
                 p = ph * __builtin_amdgcn_rcpf(fmaf(mu4[jj] * kk[jj], pk, 1.f));
               }
