@@ -82,6 +82,30 @@ def settle(call, seconds):
         torch.cuda.synchronize()
 
 
+def time_chunk_long(wl, nseg, steps, warmup, settle_s=0.0):
+    """dn_chunk_fwd_long (segments in parallel) on a workload; ms per call."""
+    import torch
+    from recurrent_sequence_mixer_amd import dn
+    from recurrent_sequence_mixer_amd import workloads as W
+    inp = W.generate(wl)
+    t = dn.to_device(inp, torch.bfloat16)
+    o = torch.empty_like(t["v"])
+    S = torch.empty_like(t["S0"])
+    call = lambda: dn.chunk_fwd_long(t["q"], t["k"], t["v"], {"alpha": t["alpha"], "eta": t["eta"]},
+                                     nseg, gain=wl.gain, eps=wl.eps, S0=t["S0"], out=o, S_final=S)
+    settle(call, settle_s)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        call()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
 def time_chunk(wl, steps, warmup, settle_s=0.0):
     import torch
     from recurrent_sequence_mixer_amd import dn
@@ -294,6 +318,12 @@ def main():
                               "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
                               "mfma_frac": chunk_flops(w2) / (ms2 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
             log(f"[bench] {w2.name}: {ms2:.3f} ms/step")
+        # the same long prefill by 16 segments of 8192 tokens in parallel (dn_chunk_fwd_long)
+        ms3 = time_chunk_long(longp, 16, max(5, args.steps // 2), args.warmup, args.settle_s)
+        extra["long_prefill_segments"] = {"workload": longp.name, "nseg": 16, "ms": ms3,
+                                          "tokens_per_s": longp.tokens / (ms3 * 1e-3),
+                                          "hbm_frac": chunk_bytes(longp) / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"[bench] {longp.name} by 16 segments: {ms3:.3f} ms/step")
         dwl = W.WORKLOADS[4]
         dms = time_decode(dwl, args.decode_steps, args.settle_s)
         gbs = decode_bytes(dwl) / (dms * 1e-3) / 1e9

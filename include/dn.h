@@ -88,6 +88,7 @@ typedef enum dn_status {
   DN_ERR_SHAPE = -2,       /* B, H, T, dk, dv or C outside the supported set  */
   DN_ERR_DTYPE = -3,       /* unknown io dtype                                 */
   DN_ERR_GAIN = -4,        /* unknown gain / decay, or invalid gain parameter  */
+  DN_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required       */
   DN_ERR_UNSUPPORTED = -6, /* valid but not built (e.g. fp32 io with dk = 128) */
   DN_ERR_HIP = -7,         /* a kernel launch failed                           */
   DN_ERR_ALIAS = -8        /* forbidden overlap between buffers                */
@@ -153,6 +154,31 @@ typedef struct dn_gates {
 int dn_chunk_fwd(const dn_desc* desc, const void* q, const void* k, const void* v,
                  const dn_gates* gates, const float* S0, const float* aux0, void* o,
                  float* S_final, float* aux_final, void* stream);
+
+/* Chunked forward of long sequences by segments, for shapes with few heads
+ * (e.g. batch-1 prefill): each head's T tokens are cut into nseg segments
+ * of T / nseg tokens, which run in parallel.  Over a segment the recurrence
+ * is affine in its entering state, S_out = A S_in + B (the affine memory
+ * scan of Kalman Delta Networks §2.6, Eq. 39, taken per segment), so the
+ * call (1) forms every segment's end state B from S_in = 0 and its transfer
+ * matrix A from S_in = I with v = 0, (2) chains S_in(s + 1) = A_s S_in(s) + B_s
+ * from S0, and (3) reruns every segment from its S_in, writing o.  Results
+ * equal dn_chunk_fwd's up to rounding.
+ *   Built for io = DN_BF16, decay = DN_DECAY_SCALAR and the gains KLA, GDN
+ *   and EXPLICIT (DN_ERR_UNSUPPORTED otherwise).  nseg >= 1 must divide T
+ *   into segments of a multiple of C = 64 tokens, and B H nseg <= 65535
+ *   (DN_ERR_SHAPE).
+ *   q, k, v, gates, S0 (nullable: zeros), o and S_final (nullable) are laid
+ *   out as for dn_chunk_fwd; S_final is A_{nseg-1} S_in(nseg-1) + B_{nseg-1}.
+ *   workspace: device memory of at least dn_chunk_fwd_long_workspace(desc,
+ *   nseg) bytes (fp32 A [B, H nseg, dk, dk], then B and S_in
+ *   [B, H nseg, dk, dv] each), owned by the caller; it may not overlap any
+ *   other buffer (DN_ERR_WORKSPACE when too small, DN_ERR_ALIAS on overlap).
+ *   Four launches on `stream`; nothing is allocated. */
+size_t dn_chunk_fwd_long_workspace(const dn_desc* desc, int nseg);
+int dn_chunk_fwd_long(const dn_desc* desc, int nseg, const void* q, const void* k, const void* v,
+                      const dn_gates* gates, const float* S0, void* o, float* S_final,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* One token for N = desc->B independent sequences (desc->T must be 1), the
  * tokenwise step of Kaczmarz Linear Attention Algorithm 1 (and its PGDN/KDN

@@ -348,7 +348,14 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
     f32x4 S[CONS ? NDT : 1];
     const long s_lane = (static_cast<long>(bh) * DK + 8 * g4) * a.dv + col0 + 16 * ct + c16;
     if constexpr (CONS) {
-      if (a.S0) {
+      if (a.s0_identity) {
+        // S0 = I (d_v = d_k): the state after a segment is then its transfer matrix
+        const int col = col0 + 16 * ct + c16;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[dt][i] = KL::sigma_channel(dt, g4, i) == col ? 1.f : 0.f;
+      } else if (a.S0) {
         const float* base = a.S0 + s_lane;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -439,7 +446,9 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
     auto fetch_v = [&](int c) __attribute__((always_inline)) {
       const int t0 = c * CH;
       const int n = ntok(c);
-      const auto rv = rsrc(static_cast<const uint16_t*>(a.v) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv);
+      // v == NULL: an empty resource, every load returns 0
+      const auto rv = a.v ? rsrc(static_cast<const uint16_t*>(a.v) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv)
+                          : rsrc(a.k, 0);
 #pragma unroll
       for (int j = 0; j < V_LOADS; ++j) pv[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[j], 0, 0);
     };
@@ -1112,7 +1121,9 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
         F1 = cat8(Fb[2], Fb[3]);
         // O^T = g (Q S)^T + (M U)^T: lane holds value columns 16 ct + 4 g4 .. +3
         // of token 16 rt + c16; rows past the end fall outside the resource
-        const auto ro = rsrc(static_cast<uint16_t*>(a.o) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv);
+        // o == NULL: an empty resource, every store is dropped
+        const auto ro = a.o ? rsrc(static_cast<uint16_t*>(a.o) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv)
+                            : rsrc(a.k, 0);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           const uint16_t* mrow = sm.mp + (16 * rt + c16) * PT + 8 * g4;

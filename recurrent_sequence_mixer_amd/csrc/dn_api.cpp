@@ -125,6 +125,7 @@ DN_EXPORT const char* dn_status_string(int s) {
     case DN_ERR_GAIN: return "unknown gain or decay, or invalid gain parameter";
     case DN_ERR_UNSUPPORTED: return "combination not built (fp32 io chunked forward needs dk = 64)";
     case DN_ERR_HIP: return "kernel launch failed";
+    case DN_ERR_WORKSPACE: return "workspace missing or smaller than required";
     case DN_ERR_ALIAS: return "forbidden overlap between buffers";
     default: return "unknown status";
   }
@@ -181,9 +182,105 @@ DN_EXPORT int dn_chunk_fwd(const dn_desc* d, const void* q, const void* k, const
   a.o = o;
   a.S_final = S_final;
   a.aux_final = has_aux ? aux_final : nullptr;
+  a.s0_identity = 0;
   return hip_status(dn::launch_chunk_fwd(a, d->io == DN_BF16, d->gain,
                                          d->decay == DN_DECAY_CHANNEL,
                                          static_cast<hipStream_t>(stream)));
+}
+
+// Workspace of dn_chunk_fwd_long: A [B, H nseg, dk, dk], then B and S_in
+// [B, H nseg, dk, dv], fp32.
+static size_t long_ws_bytes(const dn_desc* d, int nseg) {
+  const size_t heads = static_cast<size_t>(d->B) * d->H * nseg;
+  return heads * d->dk * (static_cast<size_t>(d->dk) + 2 * static_cast<size_t>(d->dv)) * sizeof(float);
+}
+
+DN_EXPORT size_t dn_chunk_fwd_long_workspace(const dn_desc* d, int nseg) {
+  if (check_desc(d, true) != DN_OK || nseg < 1) return 0;
+  return long_ws_bytes(d, nseg);
+}
+
+DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const void* k,
+                                const void* v, const dn_gates* g, const float* S0, void* o,
+                                float* S_final, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_desc(d, true);
+  if (st != DN_OK) return st;
+  if (d->io != DN_BF16 || d->decay != DN_DECAY_SCALAR ||
+      !(d->gain == DN_GAIN_KLA || d->gain == DN_GAIN_GDN || d->gain == DN_GAIN_EXPLICIT))
+    return DN_ERR_UNSUPPORTED;
+  if (nseg < 1 || d->T % nseg != 0 || (d->T / nseg) % d->C != 0) return DN_ERR_SHAPE;
+  if (static_cast<long long>(d->B) * d->H * nseg > 65535) return DN_ERR_SHAPE;
+  if ((st = check_gates(d, g)) != DN_OK) return st;
+  if (!q || !k || !v || !o) return DN_ERR_NULL;
+  const size_t need = long_ws_bytes(d, nseg);
+  if (!ws || ws_bytes < need) return DN_ERR_WORKSPACE;
+
+  const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
+  const size_t sbytes = static_cast<size_t>(d->B) * d->H * d->dk * d->dv * 4;
+  Range in[16];
+  int n = gate_ranges(d, g, in);
+  in[n++] = {q, bht * d->dk * 2};
+  in[n++] = {k, bht * d->dk * 2};
+  in[n++] = {v, bht * d->dv * 2};
+  in[n++] = {S0, S0 ? sbytes : 0};
+  const Range ro{o, bht * d->dv * 2}, rs{S_final, S_final ? sbytes : 0}, rw{ws, need};
+  for (int i = 0; i < n; ++i)
+    if (overlap(ro, in[i]) || overlap(rs, in[i]) || overlap(rw, in[i])) return DN_ERR_ALIAS;
+  if (overlap(ro, rs) || overlap(ro, rw) || overlap(rs, rw)) return DN_ERR_ALIAS;
+
+  // the [B, H, T, d] tensors read as [B, H nseg, T / nseg, d]: segment s of
+  // head h is head h nseg + s of the view (and likewise the per-token gates)
+  const int Hs = d->H * nseg, Ts = d->T / nseg;
+  const size_t heads = static_cast<size_t>(d->B) * Hs;
+  float* wA = static_cast<float*>(ws);
+  float* wB = wA + heads * d->dk * d->dk;
+  float* wS = wB + heads * d->dk * d->dv;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  dn::ChunkArgs a;
+  a.B = d->B;
+  a.H = Hs;
+  a.T = Ts;
+  a.dk = d->dk;
+  a.dv = d->dv;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = gate_args(d, g);
+  a.S0 = nullptr;
+  a.aux0 = nullptr;
+  a.o = nullptr;
+  a.S_final = wB;
+  a.aux_final = nullptr;
+  a.s0_identity = 0;
+  // (1) end states B_s from S_in = 0, transfer matrices A_s from S_in = I, v = 0
+  hipError_t e = dn::launch_chunk_fwd_bf16_scalar(a, d->gain, s);
+  if (e != hipSuccess) return DN_ERR_HIP;
+  dn::ChunkArgs t = a;
+  t.dv = d->dk;
+  t.v = nullptr;
+  t.s0_identity = 1;
+  t.S_final = wA;
+  e = dn::launch_chunk_fwd_bf16_scalar(t, d->gain, s);
+  if (e != hipSuccess) return DN_ERR_HIP;
+  // (2) the entering state of every segment, and the final state
+  dn::CombineArgs c;
+  c.B = d->B;
+  c.H = d->H;
+  c.nseg = nseg;
+  c.dk = d->dk;
+  c.dv = d->dv;
+  c.A = wA;
+  c.Bs = wB;
+  c.S0 = S0;
+  c.S_in = wS;
+  c.S_final = S_final;
+  e = dn::launch_segment_combine(c, s);
+  if (e != hipSuccess) return DN_ERR_HIP;
+  // (3) every segment from its entering state, writing o
+  a.S0 = wS;
+  a.o = o;
+  a.S_final = nullptr;
+  return hip_status(dn::launch_chunk_fwd_bf16_scalar(a, d->gain, s));
 }
 
 DN_EXPORT int dn_decode_step(const dn_desc* d, const void* q, const void* k, const void* v,

@@ -40,14 +40,28 @@ struct DecodeArgs {
 
 struct ChunkArgs {
   int B, H, T, dk, dv;
-  const void *q, *k, *v;
+  const void *q, *k, *v;  // v nullable (bf16 scalar-decay kernel only): v = 0
   GateArgs g;
   const float* S0;    // nullable
   const float* aux0;  // nullable
-  void* o;
+  void* o;            // nullable (bf16 scalar-decay kernel only): no output
   float* S_final;    // nullable
   float* aux_final;  // nullable
+  int s0_identity;   // S0 = I (dv = dk; bf16 scalar-decay kernel only): a segment's transfer matrix
 };
+
+// Long-sequence forward by segments (segment_combine.hip): per head, the
+// entering state of every segment from the segments' transfer matrices A_s
+// [B, H nseg, dk, dk] and local end states B_s [B, H nseg, dk, dv].
+struct CombineArgs {
+  int B, H, nseg, dk, dv;
+  const float* A;   // [B, H nseg, dk, dk]
+  const float* Bs;  // [B, H nseg, dk, dv]
+  const float* S0;  // [B, H, dk, dv], nullable (zeros)
+  float* S_in;      // [B, H nseg, dk, dv]
+  float* S_final;   // [B, H, dk, dv], nullable
+};
+hipError_t launch_segment_combine(const CombineArgs& a, hipStream_t st);
 
 struct GainPrepArgs {
   int B, H, T, dk;

@@ -16,13 +16,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdn.so")
 
 DN_OK = 0
 STATUS = {0: "DN_OK", -1: "DN_ERR_NULL", -2: "DN_ERR_SHAPE", -3: "DN_ERR_DTYPE", -4: "DN_ERR_GAIN",
-          -6: "DN_ERR_UNSUPPORTED", -7: "DN_ERR_HIP", -8: "DN_ERR_ALIAS"}
+          -5: "DN_ERR_WORKSPACE", -6: "DN_ERR_UNSUPPORTED", -7: "DN_ERR_HIP", -8: "DN_ERR_ALIAS"}
 GAIN = {"kla": 0, "gdn": 1, "pgdn": 2, "kdn": 3, "explicit": 4, "kdn_iso": 5}
 DECAY = {"scalar": 0, "channel": 1}
 IO = {torch.float32: 0, torch.bfloat16: 1}
 
 # Symbols declared in include/dn.h.
-EXPORTS = ("dn_chunk_fwd", "dn_decode_step", "dn_gain_prep", "dn_status_string", "dn_version")
+EXPORTS = ("dn_chunk_fwd", "dn_chunk_fwd_long", "dn_chunk_fwd_long_workspace", "dn_decode_step",
+           "dn_gain_prep", "dn_status_string", "dn_version")
 
 
 class DnDesc(ctypes.Structure):
@@ -58,6 +59,11 @@ def lib() -> ctypes.CDLL:
         L.dn_chunk_fwd.argtypes = [ctypes.POINTER(DnDesc), vp, vp, vp, ctypes.POINTER(DnGates),
                                    vp, vp, vp, vp, vp, vp]
         L.dn_chunk_fwd.restype = ip
+        L.dn_chunk_fwd_long.argtypes = [ctypes.POINTER(DnDesc), ip, vp, vp, vp, ctypes.POINTER(DnGates),
+                                        vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.dn_chunk_fwd_long.restype = ip
+        L.dn_chunk_fwd_long_workspace.argtypes = [ctypes.POINTER(DnDesc), ip]
+        L.dn_chunk_fwd_long_workspace.restype = ctypes.c_size_t
         L.dn_decode_step.argtypes = [ctypes.POINTER(DnDesc), vp, vp, vp, ctypes.POINTER(DnGates),
                                      vp, vp, vp, vp]
         L.dn_decode_step.restype = ip
@@ -134,6 +140,27 @@ def chunk_fwd(q, k, v, gates: Dict[str, torch.Tensor], *, gain="kla", decay=None
                             _stream(stream))
     _check(st, "dn_chunk_fwd")
     return o, S_final, aux_final
+
+
+def chunk_fwd_long(q, k, v, gates: Dict[str, torch.Tensor], nseg: int, *, gain="kla", eps=1e-6,
+                   S0=None, out=None, S_final=None, want_state=True, stream=None):
+    """Chunked forward by nseg parallel segments per head (bf16, scalar decay;
+    KLA, GDN, explicit): returns (o, S_final).  The workspace is allocated
+    here with torch and passed to the library."""
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    desc = make_desc(B, H, T, dk, dv, q.dtype, gain, "scalar", eps)
+    o = out if out is not None else torch.empty((B, H, T, dv), dtype=v.dtype, device=v.device)
+    if want_state and S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=v.device)
+    nbytes = lib().dn_chunk_fwd_long_workspace(ctypes.byref(desc), nseg)
+    ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=v.device)
+    gt = make_gates(gates)
+    st = lib().dn_chunk_fwd_long(ctypes.byref(desc), nseg, _ptr(q), _ptr(k), _ptr(v),
+                                 ctypes.byref(gt), _ptr(S0), _ptr(o), _ptr(S_final), _ptr(ws),
+                                 nbytes, _stream(stream))
+    _check(st, "dn_chunk_fwd_long")
+    return o, S_final
 
 
 def decode_step(q, k, v, gates: Dict[str, torch.Tensor], S, aux=None, *, gain="kla", decay=None,

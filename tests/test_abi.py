@@ -135,3 +135,29 @@ def test_gain_prep_rejects_bad_arguments():
     # w_out overlapping k
     assert L.dn_gain_prep(ctypes.byref(d), FAKE + (3 << 30), ctypes.byref(g), None, FAKE + (3 << 30),
                           None, None, None, None) == -8
+
+
+def test_chunk_fwd_long_rejects_bad_arguments():
+    L = dn.lib()
+    g = _gates()
+    q, k, v, o = FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30), FAKE + (5 << 30)
+    ws = FAKE + (20 << 30)
+
+    def f(desc, nseg=4, ws=ws, nbytes=None, o=o):
+        if nbytes is None:
+            nbytes = L.dn_chunk_fwd_long_workspace(ctypes.byref(desc), nseg)
+        return L.dn_chunk_fwd_long(ctypes.byref(desc), nseg, q, k, v, ctypes.byref(g), None, o, None,
+                                   ws, nbytes, None)
+    d = _desc(B=1, H=2, T=1024)
+    # fp32 A [B H nseg, dk, dk], then B and S_in [B H nseg, dk, dv]
+    assert L.dn_chunk_fwd_long_workspace(ctypes.byref(d), 4) == 8 * 128 * (128 + 2 * 128) * 4
+    assert L.dn_chunk_fwd_long_workspace(ctypes.byref(d), 0) == 0
+    assert f(_desc(B=1, H=2, T=1024, io=0, dk=64, dv=64)) == -6  # fp32: not built
+    assert f(_desc(B=1, H=2, T=1024, gain="pgdn")) == -6
+    assert f(_desc(B=1, H=2, T=1024, decay="channel")) == -6
+    assert f(d, nseg=0) == -2
+    assert f(d, nseg=3) == -2  # does not divide T
+    assert f(d, nseg=32) == -2  # segments of 32 tokens: not whole chunks
+    assert f(d, ws=None) == -5
+    assert f(d, nbytes=1024) == -5
+    assert f(d, ws=o) == -8  # workspace overlapping the output

@@ -142,6 +142,64 @@ def test_long_prefill_batch1_sampled_head():
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
 
 
+@pytest.mark.parametrize("gain,keys,nseg", [("kla", "scaled", 1), ("kla", "scaled", 4), ("kla", "scaled", 8),
+                                            ("gdn", "unit", 4)])
+def test_chunk_fwd_long_segments(gain, keys, nseg):
+    """dn_chunk_fwd_long: segments in parallel, chained by their transfer
+    matrices (S_out = A S_in + B per segment), against the oracle over every
+    head, from a nonzero S0."""
+    from recurrent_sequence_mixer_amd import dn
+    wl = W.Workload(f"{gain}_long_small", gain, "scalar", "bf16", 1, 2, 2048, 128, 128, keys=keys,
+                    seed=60 + nseg)
+    inp = W.generate(wl)
+    t = dn.to_device(inp, torch.bfloat16)
+    gates = {n: t[n] for n in ("alpha", "eta")}
+    o, S = dn.chunk_fwd_long(t["q"], t["k"], t["v"], gates, nseg, gain=gain, eps=wl.eps, S0=t["S0"])
+    torch.cuda.synchronize()
+    _check(wl, inp, None, o.float().cpu().numpy(), S.cpu().numpy())
+
+
+def test_chunk_fwd_long_segments_carry_state():
+    """No decay and a small step (alpha = 1, eta = 0.1, unit keys): a segment
+    keeps much of its entering state, so the transfer matrices carry it; the
+    norm of A_s is checked to be far from 0 through the state it hands on."""
+    from oracle.recurrence import run_workload
+    from recurrent_sequence_mixer_amd import dn
+    wl = W.Workload("gdn_long_carry", "gdn", "scalar", "bf16", 1, 2, 2048, 128, 128, keys="unit",
+                    seed=71)
+    inp = W.generate(wl)
+    inp["alpha"] = np.ones_like(inp["alpha"])
+    inp["eta"] = np.full_like(inp["eta"], np.float32(0.1))
+    t = dn.to_device(inp, torch.bfloat16)
+    o, S = dn.chunk_fwd_long(t["q"], t["k"], t["v"], {"alpha": t["alpha"], "eta": t["eta"]}, 4,
+                             gain="gdn", S0=t["S0"])
+    torch.cuda.synchronize()
+    _check(wl, inp, None, o.float().cpu().numpy(), S.cpu().numpy())
+    # the state entering the last segment still matters: rerunning that segment
+    # from zero instead changes its outputs by a sizeable fraction
+    last = slice(1536, 2048)
+    part = {n: (a[:, :, last] if n not in ("S0",) else np.zeros_like(a)) for n, a in inp.items()}
+    o_zero, _, _, _ = run_workload(wl.replace(T=512), part)
+    o_ref, _, _, _ = run_workload(wl, inp)
+    diff = np.abs(o_zero - o_ref[:, 1536:]).max() / np.abs(o_ref[:, 1536:]).max()
+    print(f"carried state: last segment from zero differs by {diff:.2f}")
+    assert diff > 0.1
+
+
+def test_chunk_fwd_long_full_size_sampled_head():
+    """Batch-1 long prefill B1 H8 T131072 d128 by 16 segments of 8192 tokens
+    (256 workgroups per pass instead of 16); one head against the oracle."""
+    from recurrent_sequence_mixer_amd import dn
+    wl = W.Workload("kla_long_B1H8T131072d128", "kla", "scalar", "bf16", 1, 8, 131072, 128, 128,
+                    seed=51)
+    inp = W.generate(wl)
+    t = dn.to_device(inp, torch.bfloat16)
+    o, S = dn.chunk_fwd_long(t["q"], t["k"], t["v"], {"alpha": t["alpha"], "eta": t["eta"]}, 16,
+                             gain="kla", eps=wl.eps, S0=t["S0"])
+    torch.cuda.synchronize()
+    _check(wl, inp, [5], o.float().cpu().numpy(), S.cpu().numpy())
+
+
 def test_kdn_mu_dk_and_kla_key_norm_only():
     """The pages' other gain settings on the same kernels: diagonal KDN with
     information scaling mu = d_k (Kalman Delta Networks §2.5), and KLA's
