@@ -160,8 +160,8 @@ int dn_chunk_fwd(const dn_desc* desc, const void* q, const void* k, const void* 
  * of T / nseg tokens, which run in parallel.  Over a segment the recurrence
  * is affine in its entering state, S_out = A S_in + B (the affine memory
  * scan of Kalman Delta Networks §2.6, Eq. 39, taken per segment), so the
- * call (1) forms every segment's end state B from S_in = 0 and its transfer
- * matrix A from S_in = I with v = 0, (2) chains S_in(s + 1) = A_s S_in(s) + B_s
+ * call (1) forms every segment's end state B from S_in = 0 and, in the same
+ * launch, its transfer matrix A from S_in = I with v = 0, (2) chains S_in(s + 1) = A_s S_in(s) + B_s
  * from S0, and (3) reruns every segment from its S_in, writing o.  Results
  * equal dn_chunk_fwd's up to rounding.
  *   Built for io = DN_BF16, decay = DN_DECAY_SCALAR and the gains KLA, GDN
@@ -174,7 +174,7 @@ int dn_chunk_fwd(const dn_desc* desc, const void* q, const void* k, const void* 
  *   nseg) bytes (fp32 A [B, H nseg, dk, dk], then B and S_in
  *   [B, H nseg, dk, dv] each), owned by the caller; it may not overlap any
  *   other buffer (DN_ERR_WORKSPACE when too small, DN_ERR_ALIAS on overlap).
- *   Four launches on `stream`; nothing is allocated. */
+ *   Three launches on `stream`; nothing is allocated. */
 size_t dn_chunk_fwd_long_workspace(const dn_desc* desc, int nseg);
 int dn_chunk_fwd_long(const dn_desc* desc, int nseg, const void* q, const void* k, const void* v,
                       const dn_gates* gates, const float* S0, void* o, float* S_final,

@@ -299,7 +299,7 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
   // XCD-aware mapping of the 1-D grid: consecutive workgroups are dealt to the
   // 8 XCDs in turn, so the value slices of one head get ids that are equal
   // modulo 8 and share that XCD's L2 (k and q come from HBM once).
-  const int ns = a.dv / BV;
+  const int ns = (a.dv + a.xcols) / BV;  // value slices (and transfer slices)
   const int nwg = ns * a.B * a.H;
   int bh, slice;
   {
@@ -315,6 +315,8 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
   }
   const int h = bh % a.H;
   const int col0 = slice * BV;
+  // a transfer slice: columns col0 - dv of S0 = I, v = 0, no output
+  const bool xfer = col0 >= a.dv;
   const int T = a.T;
   const int nchunks = (T + CH - 1) / CH;
   const long qk_base = static_cast<long>(bh) * T * DK;
@@ -346,11 +348,12 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
     // ---------------- consumer state: element i of tile dt = key channel
     // sigma_channel(dt, g4, i), value column c16 of the wave's 16
     f32x4 S[CONS ? NDT : 1];
-    const long s_lane = (static_cast<long>(bh) * DK + 8 * g4) * a.dv + col0 + 16 * ct + c16;
+    const int sstride = xfer ? a.xcols : a.dv, scol0 = xfer ? col0 - a.dv : col0;
+    const long s_lane = (static_cast<long>(bh) * DK + 8 * g4) * sstride + scol0 + 16 * ct + c16;
     if constexpr (CONS) {
-      if (a.s0_identity) {
-        // S0 = I (d_v = d_k): the state after a segment is then its transfer matrix
-        const int col = col0 + 16 * ct + c16;
+      if (xfer) {
+        // S0 = I: the state after a segment is then its transfer matrix
+        const int col = scol0 + 16 * ct + c16;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -447,7 +450,8 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
       const int t0 = c * CH;
       const int n = ntok(c);
       // v == NULL: an empty resource, every load returns 0
-      const auto rv = a.v ? rsrc(static_cast<const uint16_t*>(a.v) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv)
+      const auto rv = a.v && !xfer
+                          ? rsrc(static_cast<const uint16_t*>(a.v) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv)
                           : rsrc(a.k, 0);
 #pragma unroll
       for (int j = 0; j < V_LOADS; ++j) pv[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[j], 0, 0);
@@ -1122,7 +1126,8 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
         // O^T = g (Q S)^T + (M U)^T: lane holds value columns 16 ct + 4 g4 .. +3
         // of token 16 rt + c16; rows past the end fall outside the resource
         // o == NULL: an empty resource, every store is dropped
-        const auto ro = a.o ? rsrc(static_cast<uint16_t*>(a.o) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv)
+        const auto ro = a.o && !xfer
+                            ? rsrc(static_cast<uint16_t*>(a.o) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv)
                             : rsrc(a.k, 0);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -1399,12 +1404,13 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
 
     // ---------------- final state and statistic
     if constexpr (CONS) {
-      if (a.S_final) {
-        float* base = a.S_final + s_lane;
+      float* fin = xfer ? a.S_final_x : a.S_final;
+      if (fin) {
+        float* base = fin + s_lane;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) base[(KL::sigma_channel(dt, 0, i)) * a.dv] = S[dt][i];
+          for (int i = 0; i < 4; ++i) base[(KL::sigma_channel(dt, 0, i)) * sstride] = S[dt][i];
       }
     } else if constexpr (PROD) {
       if ((PG || (CD && !ISO)) && a.aux_final && slice == 0 && ptid < DK)
@@ -1432,7 +1438,7 @@ static hipError_t launch_ws_one(const ChunkArgs& a, hipStream_t st) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(sizeof(Sm)));
   if (err != hipSuccess) return err;
-  dim3 grid(static_cast<unsigned>((a.dv / ws::BV) * a.B * a.H));
+  dim3 grid(static_cast<unsigned>(((a.dv + a.xcols) / ws::BV) * a.B * a.H));
   hipLaunchKernelGGL(kern, grid, dim3(ws::WS_THREADS), sizeof(Sm), st, a);
   return hipGetLastError();
 }

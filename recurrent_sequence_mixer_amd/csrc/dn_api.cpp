@@ -182,7 +182,8 @@ DN_EXPORT int dn_chunk_fwd(const dn_desc* d, const void* q, const void* k, const
   a.o = o;
   a.S_final = S_final;
   a.aux_final = has_aux ? aux_final : nullptr;
-  a.s0_identity = 0;
+  a.xcols = 0;
+  a.S_final_x = nullptr;
   return hip_status(dn::launch_chunk_fwd(a, d->io == DN_BF16, d->gain,
                                          d->decay == DN_DECAY_CHANNEL,
                                          static_cast<hipStream_t>(stream)));
@@ -251,17 +252,14 @@ DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const
   a.o = nullptr;
   a.S_final = wB;
   a.aux_final = nullptr;
-  a.s0_identity = 0;
-  // (1) end states B_s from S_in = 0, transfer matrices A_s from S_in = I, v = 0
+  // (1) in one launch: the end states B_s from S_in = 0 (the value slices) and
+  // the transfer matrices A_s from S_in = I with v = 0 (d_k more slices)
+  a.xcols = d->dk;
+  a.S_final_x = wA;
   hipError_t e = dn::launch_chunk_fwd_bf16_scalar(a, d->gain, s);
   if (e != hipSuccess) return DN_ERR_HIP;
-  dn::ChunkArgs t = a;
-  t.dv = d->dk;
-  t.v = nullptr;
-  t.s0_identity = 1;
-  t.S_final = wA;
-  e = dn::launch_chunk_fwd_bf16_scalar(t, d->gain, s);
-  if (e != hipSuccess) return DN_ERR_HIP;
+  a.xcols = 0;
+  a.S_final_x = nullptr;
   // (2) the entering state of every segment, and the final state
   dn::CombineArgs c;
   c.B = d->B;
@@ -278,6 +276,7 @@ DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const
   if (e != hipSuccess) return DN_ERR_HIP;
   // (3) every segment from its entering state, writing o
   a.S0 = wS;
+  a.S_final = nullptr;
   a.o = o;
   a.S_final = nullptr;
   return hip_status(dn::launch_chunk_fwd_bf16_scalar(a, d->gain, s));

@@ -47,7 +47,11 @@ struct ChunkArgs {
   void* o;            // nullable (bf16 scalar-decay kernel only): no output
   float* S_final;    // nullable
   float* aux_final;  // nullable
-  int s0_identity;   // S0 = I (dv = dk; bf16 scalar-decay kernel only): a segment's transfer matrix
+  // bf16 scalar-decay kernel only: xcols (0 or dk) more value slices that run
+  // from S0 = I with v = 0 and no output, their final state going to
+  // S_final_x [B, H, dk, xcols] (the transfer matrices of segments)
+  int xcols;
+  float* S_final_x;
 };
 
 // Long-sequence forward by segments (segment_combine.hip): per head, the
