@@ -174,6 +174,8 @@ int dn_chunk_fwd(const dn_desc* desc, const void* q, const void* k, const void* 
  *   nseg) bytes (fp32 A [B, H nseg, dk, dk], then B and S_in
  *   [B, H nseg, dk, dv] each), owned by the caller; it may not overlap any
  *   other buffer (DN_ERR_WORKSPACE when too small, DN_ERR_ALIAS on overlap).
+ *   dn_chunk_fwd_long_workspace returns that size in bytes, or 0 for an
+ *   invalid descriptor or nseg < 1.
  *   Three launches on `stream`; nothing is allocated. */
 size_t dn_chunk_fwd_long_workspace(const dn_desc* desc, int nseg);
 int dn_chunk_fwd_long(const dn_desc* desc, int nseg, const void* q, const void* k, const void* v,

@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -161,3 +162,11 @@ def test_chunk_fwd_long_rejects_bad_arguments():
     assert f(d, ws=None) == -5
     assert f(d, nbytes=1024) == -5
     assert f(d, ws=o) == -8  # workspace overlapping the output
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU; --gpus N > 1 exits with a message before any GPU work."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
