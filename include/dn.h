@@ -169,7 +169,9 @@ int dn_chunk_fwd(const dn_desc* desc, const void* q, const void* k, const void* 
  *   into segments of a multiple of C = 64 tokens, and B H nseg <= 65535
  *   (DN_ERR_SHAPE).
  *   q, k, v, gates, S0 (nullable: zeros), o and S_final (nullable) are laid
- *   out as for dn_chunk_fwd; S_final is A_{nseg-1} S_in(nseg-1) + B_{nseg-1}.
+ *   out as for dn_chunk_fwd; S_final is A_{nseg-1} S_in(nseg-1) + B_{nseg-1}
+ *   and may be S0 exactly (in-place resume).  q, k, v and o are required
+ *   also when T = 0.
  *   workspace: device memory of at least dn_chunk_fwd_long_workspace(desc,
  *   nseg) bytes (fp32 A [B, H nseg, dk, dk], then B and S_in
  *   [B, H nseg, dk, dv] each), owned by the caller; it may not overlap any

@@ -225,8 +225,13 @@ DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const
   in[n++] = {v, bht * d->dv * 2};
   in[n++] = {S0, S0 ? sbytes : 0};
   const Range ro{o, bht * d->dv * 2}, rs{S_final, S_final ? sbytes : 0}, rw{ws, need};
-  for (int i = 0; i < n; ++i)
-    if (overlap(ro, in[i]) || overlap(rs, in[i]) || overlap(rw, in[i])) return DN_ERR_ALIAS;
+  for (int i = 0; i < n; ++i) {
+    // S_final may be S0 exactly (in-place resume): the combine kernel reads
+    // and writes each element of the state from the same thread
+    const bool s_in_place = in[i].p == S0 && S_final == S0;
+    if (overlap(ro, in[i]) || (!s_in_place && overlap(rs, in[i])) || overlap(rw, in[i]))
+      return DN_ERR_ALIAS;
+  }
   if (overlap(ro, rs) || overlap(ro, rw) || overlap(rs, rw)) return DN_ERR_ALIAS;
 
   // the [B, H, T, d] tensors read as [B, H nseg, T / nseg, d]: segment s of

@@ -154,7 +154,10 @@ def test_chunk_fwd_long_segments(gain, keys, nseg):
     inp = W.generate(wl)
     t = dn.to_device(inp, torch.bfloat16)
     gates = {n: t[n] for n in ("alpha", "eta")}
-    o, S = dn.chunk_fwd_long(t["q"], t["k"], t["v"], gates, nseg, gain=gain, eps=wl.eps, S0=t["S0"])
+    # the state in place (S_final is S0)
+    S = t["S0"].clone()
+    o, _ = dn.chunk_fwd_long(t["q"], t["k"], t["v"], gates, nseg, gain=gain, eps=wl.eps, S0=S,
+                             S_final=S)
     torch.cuda.synchronize()
     _check(wl, inp, None, o.float().cpu().numpy(), S.cpu().numpy())
 
