@@ -90,8 +90,14 @@ def time_chunk_long(wl, nseg, steps, warmup, settle_s=0.0):
     t = dn.to_device(inp, torch.bfloat16)
     o = torch.empty_like(t["v"])
     S = torch.empty_like(t["S0"])
-    call = lambda: dn.chunk_fwd_long(t["q"], t["k"], t["v"], {"alpha": t["alpha"], "eta": t["eta"]},
-                                     nseg, gain=wl.gain, eps=wl.eps, S0=t["S0"], out=o, S_final=S)
+    gates = {n: t[n] for n in ("alpha", "eta", "alphaP", "betaP", "mu_log", "omega", "r", "w")
+             if n in t}
+    aux = torch.empty((wl.B, wl.H, wl.dk), device="cuda") if wl.gain in ("pgdn", "kdn") else None
+    if wl.gain == "kdn_iso":
+        aux = torch.empty((wl.B, wl.H), device="cuda")
+    call = lambda: dn.chunk_fwd_long(t["q"], t["k"], t["v"], gates, nseg, gain=wl.gain, eps=wl.eps,
+                                     x=wl.x, mu_info=wl.mu_info, S0=t["S0"], aux0=t.get("aux0"),
+                                     out=o, S_final=S, aux_final=aux)
     settle(call, settle_s)
     for _ in range(warmup):
         call()
@@ -336,6 +342,16 @@ def main():
                                           "tokens_per_s": longp.tokens / (ms3 * 1e-3),
                                           "hbm_frac": chunk_bytes(longp) / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS}
         log(f"[bench] {longp.name} by 16 segments: {ms3:.3f} ms/step")
+        # PGDN batch-1 prefill (Preconditioned DeltaNet Fig. 4: batch 1, 8 heads,
+        # head dim 128): one pass (16 workgroups) and 16 segments of 2048 tokens
+        longpg = W.Workload("pgdn_long_B1H8T32768d128", "pgdn", "scalar", "bf16", 1, 8, 32768, 128,
+                            128, keys="unit", seed=52)
+        ms4, _ = time_chunk(longpg, max(5, args.steps // 2), args.warmup, args.settle_s)
+        ms5 = time_chunk_long(longpg, 16, max(5, args.steps // 2), args.warmup, args.settle_s)
+        extra["long_prefill_pgdn"] = {"workload": longpg.name, "ms_one_pass": ms4, "nseg": 16,
+                                      "ms_segments": ms5,
+                                      "tokens_per_s_segments": longpg.tokens / (ms5 * 1e-3)}
+        log(f"[bench] {longpg.name}: one pass {ms4:.3f} ms, by 16 segments {ms5:.3f} ms")
         dwl = W.WORKLOADS[4]
         dms = time_decode(dwl, args.decode_steps, args.settle_s)
         gbs = decode_bytes(dwl) / (dms * 1e-3) / 1e9

@@ -161,28 +161,38 @@ int dn_chunk_fwd(const dn_desc* desc, const void* q, const void* k, const void* 
  * is affine in its entering state, S_out = A S_in + B (the affine memory
  * scan of Kalman Delta Networks §2.6, Eq. 39, taken per segment), so the
  * call (1) forms every segment's end state B from S_in = 0 and, in the same
- * launch, its transfer matrix A from S_in = I with v = 0, (2) chains S_in(s + 1) = A_s S_in(s) + B_s
- * from S0, and (3) reruns every segment from its S_in, writing o.  Results
- * equal dn_chunk_fwd's up to rounding.
- *   Built for io = DN_BF16, decay = DN_DECAY_SCALAR and the gains KLA, GDN
- *   and EXPLICIT (DN_ERR_UNSUPPORTED otherwise).  nseg >= 1 must divide T
- *   into segments of a multiple of C = 64 tokens, and B H nseg <= 65535
+ * launch, its transfer matrix A from S_in = I with v = 0, (2) chains
+ * S_in(s + 1) = A_s S_in(s) + B_s from S0, and (3) reruns every segment from
+ * its S_in, writing o.  For PGDN and KDN the gain statistic (A_t, p_t, b_t)
+ * does not depend on S: a first step (0) composes its per-token maps (affine
+ * for PGDN, Moebius for KDN, the associative gain scan of §2.6) over pieces
+ * of each segment in parallel and chains them from aux0, giving the
+ * statistic entering every segment and aux_final.  Results equal
+ * dn_chunk_fwd's up to rounding.
+ *   Built for io = DN_BF16 with decay = DN_DECAY_SCALAR and the gains KLA,
+ *   GDN, PGDN and EXPLICIT, or decay = DN_DECAY_CHANNEL and the gains KDN and
+ *   KDN_ISO (DN_ERR_UNSUPPORTED otherwise).  nseg >= 1 must divide T into
+ *   segments of a multiple of C = 64 tokens, and B H nseg <= 65535
  *   (DN_ERR_SHAPE).
- *   q, k, v, gates, S0 (nullable: zeros), o and S_final (nullable) are laid
- *   out as for dn_chunk_fwd; S_final is A_{nseg-1} S_in(nseg-1) + B_{nseg-1}
- *   and may be S0 exactly (in-place resume).  q, k, v and o are required
- *   also when T = 0.
+ *   q, k, v, gates, S0 (nullable: zeros), aux0 (nullable: ones), o, S_final
+ *   (nullable) and aux_final (nullable) are laid out as for dn_chunk_fwd;
+ *   aux0 and aux_final are ignored for the gains without a statistic.
+ *   S_final may be S0 exactly, and aux_final aux0 exactly (in-place resume).
+ *   q, k, v and o are required also when T = 0.
  *   workspace: device memory of at least dn_chunk_fwd_long_workspace(desc,
- *   nseg) bytes (fp32 A [B, H nseg, dk, dk], then B and S_in
- *   [B, H nseg, dk, dv] each), owned by the caller; it may not overlap any
+ *   nseg) bytes, owned by the caller: fp32 A [B, H nseg, dk, dk], then B and
+ *   S_in [B, H nseg, dk, dv] each, and for PGDN and KDN the segments'
+ *   entering statistics and the piece summaries.  It may not overlap any
  *   other buffer (DN_ERR_WORKSPACE when too small, DN_ERR_ALIAS on overlap).
  *   dn_chunk_fwd_long_workspace returns that size in bytes, or 0 for an
- *   invalid descriptor or nseg < 1.
- *   Three launches on `stream`; nothing is allocated. */
+ *   invalid descriptor, nseg < 1, or segments that are not whole chunks.
+ *   Three launches on `stream` (five with a statistic); nothing is
+ *   allocated. */
 size_t dn_chunk_fwd_long_workspace(const dn_desc* desc, int nseg);
 int dn_chunk_fwd_long(const dn_desc* desc, int nseg, const void* q, const void* k, const void* v,
-                      const dn_gates* gates, const float* S0, void* o, float* S_final,
-                      void* workspace, size_t workspace_bytes, void* stream);
+                      const dn_gates* gates, const float* S0, const float* aux0, void* o,
+                      float* S_final, float* aux_final, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* One token for N = desc->B independent sequences (desc->T must be 1), the
  * tokenwise step of Kaczmarz Linear Attention Algorithm 1 (and its PGDN/KDN

@@ -189,58 +189,98 @@ DN_EXPORT int dn_chunk_fwd(const dn_desc* d, const void* q, const void* k, const
                                          static_cast<hipStream_t>(stream)));
 }
 
-// Workspace of dn_chunk_fwd_long: A [B, H nseg, dk, dk], then B and S_in
-// [B, H nseg, dk, dv], fp32.
-static size_t long_ws_bytes(const dn_desc* d, int nseg) {
+// Workspace of dn_chunk_fwd_long, fp32: A [B, H nseg, dk, dk], then B and S_in
+// [B, H nseg, dk, dv]; for the gains with a statistic (PGDN, KDN) then
+// aux_in [B, H nseg, aph], mu_seg [H nseg] and the piece summaries
+// [B, H, T / lsub, 3, aph], each of these starting on a 256-byte boundary.
+struct LongLayout {
+  size_t a, b, s, aux_in, mu_seg, summ, total;
+  int lsub;
+};
+
+static size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+static LongLayout long_layout(const dn_desc* d, int nseg) {
+  LongLayout L{};
   const size_t heads = static_cast<size_t>(d->B) * d->H * nseg;
-  return heads * d->dk * (static_cast<size_t>(d->dk) + 2 * static_cast<size_t>(d->dv)) * sizeof(float);
+  const int ts = d->T / nseg;
+  L.lsub = ts % 256 == 0 ? 256 : ts % 128 == 0 ? 128 : 64;
+  L.a = 0;
+  L.b = heads * d->dk * d->dk * sizeof(float);
+  L.s = L.b + heads * d->dk * d->dv * sizeof(float);
+  L.total = L.s + heads * d->dk * d->dv * sizeof(float);
+  if (has_aux_state(d)) {
+    const size_t aph = aux_per_head(d);
+    L.aux_in = round256(L.total);
+    L.mu_seg = round256(L.aux_in + heads * aph * sizeof(float));
+    L.summ = round256(L.mu_seg + static_cast<size_t>(d->H) * nseg * sizeof(float));
+    L.total = L.summ + static_cast<size_t>(d->B) * d->H * (d->T / L.lsub) * 3 * aph * sizeof(float);
+  }
+  return L;
+}
+
+static bool long_shape_ok(const dn_desc* d, int nseg) {
+  return nseg >= 1 && d->T % nseg == 0 && (d->T / nseg) % d->C == 0;
 }
 
 DN_EXPORT size_t dn_chunk_fwd_long_workspace(const dn_desc* d, int nseg) {
-  if (check_desc(d, true) != DN_OK || nseg < 1) return 0;
-  return long_ws_bytes(d, nseg);
+  if (check_desc(d, true) != DN_OK || !long_shape_ok(d, nseg)) return 0;
+  return long_layout(d, nseg).total;
 }
 
 DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const void* k,
-                                const void* v, const dn_gates* g, const float* S0, void* o,
-                                float* S_final, void* ws, size_t ws_bytes, void* stream) {
+                                const void* v, const dn_gates* g, const float* S0,
+                                const float* aux0, void* o, float* S_final, float* aux_final,
+                                void* ws, size_t ws_bytes, void* stream) {
   int st = check_desc(d, true);
   if (st != DN_OK) return st;
-  if (d->io != DN_BF16 || d->decay != DN_DECAY_SCALAR ||
-      !(d->gain == DN_GAIN_KLA || d->gain == DN_GAIN_GDN || d->gain == DN_GAIN_EXPLICIT))
-    return DN_ERR_UNSUPPORTED;
-  if (nseg < 1 || d->T % nseg != 0 || (d->T / nseg) % d->C != 0) return DN_ERR_SHAPE;
+  // the combinations that run on the producer/consumer kernel
+  const bool scalar_ok = d->decay == DN_DECAY_SCALAR &&
+                         (d->gain == DN_GAIN_KLA || d->gain == DN_GAIN_GDN ||
+                          d->gain == DN_GAIN_EXPLICIT || d->gain == DN_GAIN_PGDN);
+  const bool channel_ok = d->decay == DN_DECAY_CHANNEL &&
+                          (d->gain == DN_GAIN_KDN || d->gain == DN_GAIN_KDN_ISO);
+  if (d->io != DN_BF16 || !(scalar_ok || channel_ok)) return DN_ERR_UNSUPPORTED;
+  if (!long_shape_ok(d, nseg)) return DN_ERR_SHAPE;
   if (static_cast<long long>(d->B) * d->H * nseg > 65535) return DN_ERR_SHAPE;
   if ((st = check_gates(d, g)) != DN_OK) return st;
   if (!q || !k || !v || !o) return DN_ERR_NULL;
-  const size_t need = long_ws_bytes(d, nseg);
-  if (!ws || ws_bytes < need) return DN_ERR_WORKSPACE;
+  const LongLayout lay = long_layout(d, nseg);
+  if (!ws || ws_bytes < lay.total) return DN_ERR_WORKSPACE;
 
+  const bool has_aux = has_aux_state(d);
   const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
   const size_t sbytes = static_cast<size_t>(d->B) * d->H * d->dk * d->dv * 4;
+  const size_t abytes = static_cast<size_t>(d->B) * d->H * aux_per_head(d) * 4;
   Range in[16];
   int n = gate_ranges(d, g, in);
   in[n++] = {q, bht * d->dk * 2};
   in[n++] = {k, bht * d->dk * 2};
   in[n++] = {v, bht * d->dv * 2};
   in[n++] = {S0, S0 ? sbytes : 0};
-  const Range ro{o, bht * d->dv * 2}, rs{S_final, S_final ? sbytes : 0}, rw{ws, need};
+  in[n++] = {has_aux ? aux0 : nullptr, abytes};
+  const Range ro{o, bht * d->dv * 2}, rs{S_final, S_final ? sbytes : 0},
+      ra{has_aux ? aux_final : nullptr, abytes}, rw{ws, lay.total};
   for (int i = 0; i < n; ++i) {
-    // S_final may be S0 exactly (in-place resume): the combine kernel reads
-    // and writes each element of the state from the same thread
+    // S_final may be S0 exactly and aux_final aux0 (in-place resume): the
+    // combine and chain kernels read and write each element from one thread
     const bool s_in_place = in[i].p == S0 && S_final == S0;
-    if (overlap(ro, in[i]) || (!s_in_place && overlap(rs, in[i])) || overlap(rw, in[i]))
+    const bool a_in_place = has_aux && in[i].p == aux0 && aux_final == aux0;
+    if (overlap(ro, in[i]) || (!s_in_place && overlap(rs, in[i])) ||
+        (!a_in_place && overlap(ra, in[i])) || overlap(rw, in[i]))
       return DN_ERR_ALIAS;
   }
-  if (overlap(ro, rs) || overlap(ro, rw) || overlap(rs, rw)) return DN_ERR_ALIAS;
+  if (overlap(ro, rs) || overlap(ro, ra) || overlap(rs, ra) || overlap(ro, rw) ||
+      overlap(rs, rw) || overlap(ra, rw))
+    return DN_ERR_ALIAS;
 
   // the [B, H, T, d] tensors read as [B, H nseg, T / nseg, d]: segment s of
   // head h is head h nseg + s of the view (and likewise the per-token gates)
   const int Hs = d->H * nseg, Ts = d->T / nseg;
-  const size_t heads = static_cast<size_t>(d->B) * Hs;
-  float* wA = static_cast<float*>(ws);
-  float* wB = wA + heads * d->dk * d->dk;
-  float* wS = wB + heads * d->dk * d->dv;
+  char* wbase = static_cast<char*>(ws);
+  float* wA = reinterpret_cast<float*>(wbase + lay.a);
+  float* wB = reinterpret_cast<float*>(wbase + lay.b);
+  float* wS = reinterpret_cast<float*>(wbase + lay.s);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   dn::ChunkArgs a;
   a.B = d->B;
@@ -257,12 +297,37 @@ DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const
   a.o = nullptr;
   a.S_final = wB;
   a.aux_final = nullptr;
+  hipError_t e;
+  if (has_aux) {
+    // (0) the gain statistic entering every segment (and after the last)
+    dn::StatArgs sa;
+    sa.B = d->B;
+    sa.H = d->H;
+    sa.T = d->T;
+    sa.dk = d->dk;
+    sa.nseg = nseg;
+    sa.lsub = lay.lsub;
+    sa.gain = d->gain;
+    sa.k = k;
+    sa.g = a.g;
+    sa.aux0 = aux0;
+    sa.summ = reinterpret_cast<float*>(wbase + lay.summ);
+    sa.aux_in = reinterpret_cast<float*>(wbase + lay.aux_in);
+    sa.aux_final = aux_final;
+    sa.mu_seg = reinterpret_cast<float*>(wbase + lay.mu_seg);
+    if ((e = dn::launch_segment_stats(sa, s)) != hipSuccess) return DN_ERR_HIP;
+    a.aux0 = sa.aux_in;
+    if (d->gain == DN_GAIN_PGDN) a.g.mu_log = sa.mu_seg;
+  }
+  const auto launch = [&]() {
+    return d->decay == DN_DECAY_CHANNEL ? dn::launch_chunk_fwd_bf16_kdn(a, d->gain, s)
+                                        : dn::launch_chunk_fwd_bf16_scalar(a, d->gain, s);
+  };
   // (1) in one launch: the end states B_s from S_in = 0 (the value slices) and
   // the transfer matrices A_s from S_in = I with v = 0 (d_k more slices)
   a.xcols = d->dk;
   a.S_final_x = wA;
-  hipError_t e = dn::launch_chunk_fwd_bf16_scalar(a, d->gain, s);
-  if (e != hipSuccess) return DN_ERR_HIP;
+  if ((e = launch()) != hipSuccess) return DN_ERR_HIP;
   a.xcols = 0;
   a.S_final_x = nullptr;
   // (2) the entering state of every segment, and the final state
@@ -277,14 +342,12 @@ DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const
   c.S0 = S0;
   c.S_in = wS;
   c.S_final = S_final;
-  e = dn::launch_segment_combine(c, s);
-  if (e != hipSuccess) return DN_ERR_HIP;
+  if ((e = dn::launch_segment_combine(c, s)) != hipSuccess) return DN_ERR_HIP;
   // (3) every segment from its entering state, writing o
   a.S0 = wS;
   a.S_final = nullptr;
   a.o = o;
-  a.S_final = nullptr;
-  return hip_status(dn::launch_chunk_fwd_bf16_scalar(a, d->gain, s));
+  return hip_status(launch());
 }
 
 DN_EXPORT int dn_decode_step(const dn_desc* d, const void* q, const void* k, const void* v,

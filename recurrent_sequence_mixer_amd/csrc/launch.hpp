@@ -67,6 +67,24 @@ struct CombineArgs {
 };
 hipError_t launch_segment_combine(const CombineArgs& a, hipStream_t st);
 
+// Long-sequence forward, PGDN and KDN gains (segment_stats.hip): the gain
+// statistic entering every segment.  Per head of [B, H] and channel (one per
+// head for isotropic KDN), pieces of lsub tokens (lsub divides T / nseg) are
+// summarised into summ [B, H, T / lsub, 3, aph], then applied in order from
+// aux0 (nullable: ones) into aux_in [B, H nseg, aph] and aux_final (nullable)
+// [B, H, aph].  PGDN also repeats mu_log [H] into mu_seg [H nseg].
+struct StatArgs {
+  int B, H, T, dk, nseg, lsub, gain;
+  const void* k;
+  GateArgs g;
+  const float* aux0;
+  float* summ;
+  float* aux_in;
+  float* aux_final;
+  float* mu_seg;
+};
+hipError_t launch_segment_stats(const StatArgs& a, hipStream_t st);
+
 struct GainPrepArgs {
   int B, H, T, dk;
   const void* k;

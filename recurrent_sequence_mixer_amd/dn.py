@@ -60,7 +60,7 @@ def lib() -> ctypes.CDLL:
                                    vp, vp, vp, vp, vp, vp]
         L.dn_chunk_fwd.restype = ip
         L.dn_chunk_fwd_long.argtypes = [ctypes.POINTER(DnDesc), ip, vp, vp, vp, ctypes.POINTER(DnGates),
-                                        vp, vp, vp, vp, ctypes.c_size_t, vp]
+                                        vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.dn_chunk_fwd_long.restype = ip
         L.dn_chunk_fwd_long_workspace.argtypes = [ctypes.POINTER(DnDesc), ip]
         L.dn_chunk_fwd_long_workspace.restype = ctypes.c_size_t
@@ -142,25 +142,33 @@ def chunk_fwd(q, k, v, gates: Dict[str, torch.Tensor], *, gain="kla", decay=None
     return o, S_final, aux_final
 
 
-def chunk_fwd_long(q, k, v, gates: Dict[str, torch.Tensor], nseg: int, *, gain="kla", eps=1e-6,
-                   S0=None, out=None, S_final=None, want_state=True, stream=None):
-    """Chunked forward by nseg parallel segments per head (bf16, scalar decay;
-    KLA, GDN, explicit): returns (o, S_final).  The workspace is allocated
-    here with torch and passed to the library."""
+def chunk_fwd_long(q, k, v, gates: Dict[str, torch.Tensor], nseg: int, *, gain="kla", decay=None,
+                   eps=1e-6, x=1.5, mu_info=1.0, S0=None, aux0=None, out=None, S_final=None,
+                   aux_final=None, want_state=True, stream=None):
+    """Chunked forward by nseg parallel segments per head (bf16; KLA, GDN, PGDN,
+    explicit with scalar decay, KDN and isotropic KDN with per-channel decay):
+    returns (o, S_final, aux_final).  The workspace is allocated here with
+    torch and passed to the library."""
     B, H, T, dk = k.shape
     dv = v.shape[-1]
-    desc = make_desc(B, H, T, dk, dv, q.dtype, gain, "scalar", eps)
+    if decay is None:
+        decay = "channel" if gates["alpha"].dim() == 4 else "scalar"
+    desc = make_desc(B, H, T, dk, dv, q.dtype, gain, decay, eps, x, mu_info)
     o = out if out is not None else torch.empty((B, H, T, dv), dtype=v.dtype, device=v.device)
     if want_state and S_final is None:
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=v.device)
+    has_aux = gain in ("pgdn", "kdn", "kdn_iso")
+    if has_aux and want_state and aux_final is None:
+        aux_final = torch.empty((B, H) if gain == "kdn_iso" else (B, H, dk), dtype=torch.float32,
+                                device=v.device)
     nbytes = lib().dn_chunk_fwd_long_workspace(ctypes.byref(desc), nseg)
     ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=v.device)
     gt = make_gates(gates)
     st = lib().dn_chunk_fwd_long(ctypes.byref(desc), nseg, _ptr(q), _ptr(k), _ptr(v),
-                                 ctypes.byref(gt), _ptr(S0), _ptr(o), _ptr(S_final), _ptr(ws),
-                                 nbytes, _stream(stream))
+                                 ctypes.byref(gt), _ptr(S0), _ptr(aux0), _ptr(o), _ptr(S_final),
+                                 _ptr(aux_final), _ptr(ws), nbytes, _stream(stream))
     _check(st, "dn_chunk_fwd_long")
-    return o, S_final
+    return o, S_final, aux_final
 
 
 def decode_step(q, k, v, gates: Dict[str, torch.Tensor], S, aux=None, *, gain="kla", decay=None,

@@ -49,3 +49,19 @@ def oracle_chunk(wl, inp, heads=None):
     o, S, aux, _ = run_workload(wl, inp, heads=heads, aux0=None if "aux0" not in inp
                                 else flat_heads(inp["aux0"], heads))
     return o, S, aux
+
+
+def gpu_chunk_long(wl, inp, nseg, in_place=True):
+    """Run dn_chunk_fwd_long on a workload's bf16 inputs; returns numpy
+    (o, S_T, aux_T).  With in_place, S_T and aux_T overwrite S0 and aux0."""
+    from recurrent_sequence_mixer_amd import dn
+    t = dn.to_device(inp, torch.bfloat16)
+    gates = {n: t[n] for n in ("alpha", "eta", "alphaP", "betaP", "mu_log", "omega", "r", "w")
+             if n in t}
+    S0, aux0 = t.get("S0"), t.get("aux0")
+    kw = dict(S_final=S0, aux_final=aux0) if in_place else {}
+    o, S, aux = dn.chunk_fwd_long(t["q"], t["k"], t["v"], gates, nseg, gain=wl.gain, eps=wl.eps,
+                                  x=wl.x, mu_info=wl.mu_info, S0=S0, aux0=aux0, **kw)
+    torch.cuda.synchronize()
+    to_np = lambda x: None if x is None else x.float().cpu().numpy()
+    return to_np(o), to_np(S), to_np(aux)

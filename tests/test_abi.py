@@ -147,15 +147,22 @@ def test_chunk_fwd_long_rejects_bad_arguments():
     def f(desc, nseg=4, ws=ws, nbytes=None, o=o):
         if nbytes is None:
             nbytes = L.dn_chunk_fwd_long_workspace(ctypes.byref(desc), nseg)
-        return L.dn_chunk_fwd_long(ctypes.byref(desc), nseg, q, k, v, ctypes.byref(g), None, o, None,
-                                   ws, nbytes, None)
+        return L.dn_chunk_fwd_long(ctypes.byref(desc), nseg, q, k, v, ctypes.byref(g), None, None, o,
+                                   None, None, ws, nbytes, None)
     d = _desc(B=1, H=2, T=1024)
     # fp32 A [B H nseg, dk, dk], then B and S_in [B H nseg, dk, dv]
     assert L.dn_chunk_fwd_long_workspace(ctypes.byref(d), 4) == 8 * 128 * (128 + 2 * 128) * 4
     assert L.dn_chunk_fwd_long_workspace(ctypes.byref(d), 0) == 0
     assert f(_desc(B=1, H=2, T=1024, io=0, dk=64, dv=64)) == -6  # fp32: not built
-    assert f(_desc(B=1, H=2, T=1024, gain="pgdn")) == -6
-    assert f(_desc(B=1, H=2, T=1024, decay="channel")) == -6
+    assert f(_desc(B=1, H=2, T=1024, decay="channel")) == -6  # KLA with channel decay
+    assert f(_desc(B=1, H=2, T=1024, gain="kdn")) == -6  # KDN with scalar decay
+    assert f(_desc(B=1, H=2, T=1024, gain="pgdn", decay="channel")) == -6
+    # the statistic's part: aux_in [B H nseg, dk] and mu_seg [H nseg] on
+    # 256-byte boundaries, then 3 floats per channel for each 256-token piece
+    dp = _desc(B=1, H=2, T=1024, gain="pgdn")
+    base = 8 * 128 * (128 + 2 * 128) * 4
+    assert L.dn_chunk_fwd_long_workspace(ctypes.byref(dp), 4) == base + 4096 + 256 + 2 * 4 * 3 * 128 * 4
+    assert L.dn_chunk_fwd_long_workspace(ctypes.byref(d), 3) == 0  # does not divide T
     assert f(d, nseg=0) == -2
     assert f(d, nseg=3) == -2  # does not divide T
     assert f(d, nseg=32) == -2  # segments of 32 tokens: not whole chunks

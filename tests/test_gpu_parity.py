@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from parity import TOL, flat_heads, gpu_chunk, max_rel_err, oracle_chunk
+from parity import TOL, flat_heads, gpu_chunk, gpu_chunk_long, max_rel_err, oracle_chunk
 from recurrent_sequence_mixer_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -156,7 +156,7 @@ def test_chunk_fwd_long_segments(gain, keys, nseg):
     gates = {n: t[n] for n in ("alpha", "eta")}
     # the state in place (S_final is S0)
     S = t["S0"].clone()
-    o, _ = dn.chunk_fwd_long(t["q"], t["k"], t["v"], gates, nseg, gain=gain, eps=wl.eps, S0=S,
+    o, _, _ = dn.chunk_fwd_long(t["q"], t["k"], t["v"], gates, nseg, gain=gain, eps=wl.eps, S0=S,
                              S_final=S)
     torch.cuda.synchronize()
     _check(wl, inp, None, o.float().cpu().numpy(), S.cpu().numpy())
@@ -174,7 +174,7 @@ def test_chunk_fwd_long_segments_carry_state():
     inp["alpha"] = np.ones_like(inp["alpha"])
     inp["eta"] = np.full_like(inp["eta"], np.float32(0.1))
     t = dn.to_device(inp, torch.bfloat16)
-    o, S = dn.chunk_fwd_long(t["q"], t["k"], t["v"], {"alpha": t["alpha"], "eta": t["eta"]}, 4,
+    o, S, _ = dn.chunk_fwd_long(t["q"], t["k"], t["v"], {"alpha": t["alpha"], "eta": t["eta"]}, 4,
                              gain="gdn", S0=t["S0"])
     torch.cuda.synchronize()
     _check(wl, inp, None, o.float().cpu().numpy(), S.cpu().numpy())
@@ -197,10 +197,44 @@ def test_chunk_fwd_long_full_size_sampled_head():
                     seed=51)
     inp = W.generate(wl)
     t = dn.to_device(inp, torch.bfloat16)
-    o, S = dn.chunk_fwd_long(t["q"], t["k"], t["v"], {"alpha": t["alpha"], "eta": t["eta"]}, 16,
+    o, S, _ = dn.chunk_fwd_long(t["q"], t["k"], t["v"], {"alpha": t["alpha"], "eta": t["eta"]}, 16,
                              gain="kla", eps=wl.eps, S0=t["S0"])
     torch.cuda.synchronize()
     _check(wl, inp, [5], o.float().cpu().numpy(), S.cpu().numpy())
+
+
+@pytest.mark.parametrize("gain,decay,keys,T,nseg,d", [
+    ("pgdn", "scalar", "unit", 2048, 4, 128),      # 512-token segments: two 256-token pieces
+    ("pgdn", "scalar", "unit", 1536, 8, 128),      # 192-token segments: three 64-token pieces
+    ("kdn", "channel", "scaled", 2048, 8, 128),    # one 256-token piece per segment
+    ("kdn", "channel", "scaled", 1536, 8, 128),
+    ("kdn", "channel", "scaled", 1024, 2, 64),
+    ("kdn_iso", "channel", "scaled", 2048, 4, 128),
+    ("kdn_iso", "channel", "scaled", 1280, 10, 64),  # 128-token segments
+])
+def test_chunk_fwd_long_statistic_gains(gain, decay, keys, T, nseg, d):
+    """dn_chunk_fwd_long with a gain statistic (PGDN's A_t, KDN's p_t and b_t):
+    the statistic entering every segment comes from the composed per-token
+    maps; o, S_T and aux_T (both in place) against one oracle pass, from a
+    nonzero S0 and a non-default aux0."""
+    wl = W.Workload(f"{gain}_long_small", gain, decay, "bf16", 1, 2, T, d, d, keys=keys,
+                    seed=80 + nseg)
+    inp = W.generate(wl)
+    rng = np.random.default_rng(wl.seed)
+    shape = (1, 2) if gain == "kdn_iso" else (1, 2, d)
+    inp["aux0"] = rng.uniform(0.5, 2.0, size=shape).astype(np.float32)
+    o, S, aux = gpu_chunk_long(wl, inp, nseg)
+    _check(wl, inp, None, o, S, aux)
+
+
+def test_chunk_fwd_long_pgdn_full_size_sampled_head():
+    """PGDN batch-1 prefill B1 H8 T32768 d128 by 16 segments of 2048 tokens,
+    one head against the oracle."""
+    wl = W.Workload("pgdn_long_B1H8T32768d128", "pgdn", "scalar", "bf16", 1, 8, 32768, 128, 128,
+                    keys="unit", seed=52)
+    inp = W.generate(wl)
+    o, S, aux = gpu_chunk_long(wl, inp, 16, in_place=False)
+    _check(wl, inp, [3], o, S, aux)
 
 
 def test_kdn_mu_dk_and_kla_key_norm_only():
