@@ -38,8 +38,21 @@ __global__ __launch_bounds__(SC_THREADS) void segment_combine_kernel(CombineArgs
   const int tid = threadIdx.x;
   const int cg = tid % CG, r = tid / CG;
   const int nsl = a.dv / COLS;
-  const long bh = blockIdx.x / nsl;
-  const int col0 = (blockIdx.x % nsl) * COLS + 4 * cg;
+  // XCD-aware mapping: consecutive workgroups are dealt to the 8 XCDs in turn;
+  // every column slice of a head gets an id of the same residue modulo 8, so
+  // that A_s comes into one XCD's L2 and is read there by all of them
+  const int nwg = a.B * a.H * nsl;
+  long bh;
+  int slice;
+  if (nwg % 8 == 0 && (nwg / 8) % nsl == 0) {
+    const int xcd = blockIdx.x % 8, rr = blockIdx.x / 8;
+    slice = rr % nsl;
+    bh = static_cast<long>(xcd) * (nwg / 8 / nsl) + rr / nsl;
+  } else {
+    slice = blockIdx.x % nsl;
+    bh = blockIdx.x / nsl;
+  }
+  const int col0 = slice * COLS + 4 * cg;
 
   f32x4 an[NA];
   auto load_a = [&](long seg) {
@@ -67,16 +80,20 @@ __global__ __launch_bounds__(SC_THREADS) void segment_combine_kernel(CombineArgs
       bn = *reinterpret_cast<const f32x4*>(&a.Bs[((seg + 1) * DK + r) * a.dv + col0]);
     }
     __syncthreads();  // A_s and the entering state visible
-    // x <- A_s x + B_s: four k per step, A read as 16-byte pieces of row r
-#pragma unroll 4
-    for (int kk = 0; kk < DK; kk += 4) {
-      const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sA[r][kk]);
+    // x <- A_s x + B_s: eight k per step, A read as 16-byte pieces of row r;
+    // every read of a step is issued before its arithmetic, so that the LDS
+    // latency is paid once per eight k rather than once per k
+#pragma unroll 2
+    for (int kk = 0; kk < DK; kk += 8) {
+      f32x4 a8[2], xv[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 xv = *reinterpret_cast<const f32x4*>(&sX[kk + q][4 * cg]);
+      for (int h = 0; h < 2; ++h) a8[h] = *reinterpret_cast<const f32x4*>(&sA[r][kk + 4 * h]);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) x[jj] = fmaf(a4[q], xv[jj], x[jj]);
-      }
+      for (int q = 0; q < 8; ++q) xv[q] = *reinterpret_cast<const f32x4*>(&sX[kk + q][4 * cg]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) x[jj] = fmaf(a8[q / 4][q % 4], xv[q][jj], x[jj]);
     }
     __syncthreads();  // every read of sA and sX done
     *reinterpret_cast<f32x4*>(&sX[r][4 * cg]) = x;

@@ -41,8 +41,11 @@ __device__ __forceinline__ void mobius_step(float& m00, float& m01, float& m10, 
 }
 
 // PGDN and diagonal KDN: one thread per key channel, one workgroup per piece.
+// The loads of U tokens are issued before their arithmetic (the composition
+// is a serial chain per channel; its inputs are not).
 template <int DK, int GAIN>
 __global__ __launch_bounds__(DK) void segment_summary_kernel(StatArgs a) {
+  constexpr int U = 16;  // lsub is a multiple of 64
   const int c = threadIdx.x;
   const int nsub = a.T / a.lsub;
   const long bh = blockIdx.x / nsub;
@@ -51,22 +54,40 @@ __global__ __launch_bounds__(DK) void segment_summary_kernel(StatArgs a) {
   float s0, s1, s2;
   if constexpr (GAIN == GAIN_PGDN) {
     float m = 1.f, cc = 0.f;
-    for (int i = 0; i < a.lsub; ++i) {
-      const float kk = bf2f(kp[static_cast<long>(i) * DK]);
-      const float ap = a.g.alphaP[t0 + i], bp = a.g.betaP[t0 + i];
-      m *= ap;
-      cc = fmaf(ap, cc, bp * kk * kk);
+    for (int i0 = 0; i0 < a.lsub; i0 += U) {
+      float kk[U], ap[U], bp[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        kk[j] = bf2f(kp[static_cast<long>(i0 + j) * DK]);
+        ap[j] = a.g.alphaP[t0 + i0 + j];
+        bp[j] = a.g.betaP[t0 + i0 + j];
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        m *= ap[j];
+        cc = fmaf(ap[j], cc, bp[j] * kk[j] * kk[j]);
+      }
     }
     s0 = m, s1 = cc, s2 = 0.f;
   } else {
     const uint16_t* al = static_cast<const uint16_t*>(a.g.alpha) + t0 * DK + c;
     const uint16_t* om = static_cast<const uint16_t*>(a.g.omega) + t0 * DK + c;
     float m00 = 1.f, m01 = 0.f, m10 = 0.f;
-    for (int i = 0; i < a.lsub; ++i) {
-      const long o = static_cast<long>(i) * DK;
-      const float kk = bf2f(kp[o]), al1 = bf2f(al[o]);
-      const float u = a.g.mu_info * kk * kk / a.g.r[t0 + i];
-      mobius_step(m00, m01, m10, al1 * al1, bf2f(om[o]), u);
+    for (int i0 = 0; i0 < a.lsub; i0 += U) {
+      float kk[U], aa[U], ww[U], rr[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const long o = static_cast<long>(i0 + j) * DK;
+        kk[j] = bf2f(kp[o]);
+        aa[j] = bf2f(al[o]);
+        ww[j] = bf2f(om[o]);
+        rr[j] = a.g.r[t0 + i0 + j];
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const float u = a.g.mu_info * kk[j] * kk[j] / rr[j];
+        mobius_step(m00, m01, m10, aa[j] * aa[j], ww[j], u);
+      }
     }
     s0 = m00, s1 = m01, s2 = m10;
   }
@@ -76,11 +97,12 @@ __global__ __launch_bounds__(DK) void segment_summary_kernel(StatArgs a) {
   out[2 * DK] = s2;
 }
 
-// Isotropic KDN: thread i forms token i's map from its channel sums, thread 0
-// composes the piece's maps in token order.
+// Isotropic KDN: thread i forms token i's map from its channel sums; the
+// piece's maps are then composed pairwise in a tree (later map on the left),
+// every product renormalised to a (1, 1) entry of 1.  lsub is a power of two.
 template <int DK>
 __global__ __launch_bounds__(256) void segment_summary_iso_kernel(StatArgs a) {
-  __shared__ float fa[256], fo[256], fu[256];
+  __shared__ float f00[256], f01[256], f10[256];
   const int i = threadIdx.x;
   const int nsub = a.T / a.lsub;
   const long bh = blockIdx.x / nsub;
@@ -102,23 +124,37 @@ __global__ __launch_bounds__(256) void segment_summary_iso_kernel(StatArgs a) {
       }
     }
     const float r = a.g.r[t0 + i];
-    fa[i] = sa * (1.f / DK);
-    fo[i] = static_cast<const float*>(a.g.omega)[t0 + i];
-    fu[i] = a.g.mu_info * nk / (DK * r);
+    const float am = sa * (1.f / DK), om = static_cast<const float*>(a.g.omega)[t0 + i];
+    const float u = a.g.mu_info * nk / (DK * r);
+    // the token's map [[am, om], [u am, 1 + u om]] / (1 + u om)
+    const float inv = 1.f / fmaf(u, om, 1.f);
+    f00[i] = am * inv;
+    f01[i] = om * inv;
+    f10[i] = u * am * inv;
   }
-  __syncthreads();
+  for (int w = 1; w < a.lsub; w *= 2) {
+    __syncthreads();
+    if (i % (2 * w) == 0 && i + w < a.lsub) {
+      const float l00 = f00[i + w], l01 = f01[i + w], l10 = f10[i + w];
+      const float r00 = f00[i], r01 = f01[i], r10 = f10[i];
+      const float inv = 1.f / fmaf(l10, r01, 1.f);
+      f00[i] = fmaf(l00, r00, l01 * r10) * inv;
+      f01[i] = fmaf(l00, r01, l01) * inv;
+      f10[i] = fmaf(l10, r00, r10) * inv;
+    }
+  }
   if (i == 0) {
-    float m00 = 1.f, m01 = 0.f, m10 = 0.f;
-    for (int j = 0; j < a.lsub; ++j) mobius_step(m00, m01, m10, fa[j], fo[j], fu[j]);
     float* out = a.summ + static_cast<long>(blockIdx.x) * 3;
-    out[0] = m00;
-    out[1] = m01;
-    out[2] = m10;
+    out[0] = f00[0];
+    out[1] = f01[0];
+    out[2] = f10[0];
   }
 }
 
-// One thread per (head, channel): the pieces applied in order.
-__global__ __launch_bounds__(256) void segment_chain_kernel(StatArgs a) {
+// One thread per (head, channel): the pieces applied in order, their
+// summaries loaded U at a time ahead of the serial arithmetic.
+__global__ __launch_bounds__(64) void segment_chain_kernel(StatArgs a) {
+  constexpr int U = 8;
   const int aph = a.gain == GAIN_KDN_ISO ? 1 : a.dk;
   const long item = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
   const long nitems = static_cast<long>(a.B) * a.H * aph;
@@ -130,12 +166,24 @@ __global__ __launch_bounds__(256) void segment_chain_kernel(StatArgs a) {
     const float* sm = a.summ + bh * nsub * 3 * aph + c;
     for (int s = 0; s < a.nseg; ++s) {
       a.aux_in[(bh * a.nseg + s) * aph + c] = x;
-      for (int j = s * per; j < (s + 1) * per; ++j) {
-        const float* p = sm + static_cast<long>(j) * 3 * aph;
-        if (a.gain == GAIN_PGDN) {
-          x = fmaf(p[0], x, p[aph]);
-        } else {
-          x = fmaf(p[0], x, p[aph]) / fmaf(p[2 * aph], x, 1.f);
+      for (int j0 = s * per; j0 < (s + 1) * per; j0 += U) {
+        float p0[U], p1[U], p2[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          // pieces past the segment's end read as the identity map
+          const bool in = j0 + j < (s + 1) * per;
+          const float* p = sm + static_cast<long>(in ? j0 + j : j0) * 3 * aph;
+          p0[j] = in ? p[0] : 1.f;
+          p1[j] = in ? p[aph] : 0.f;
+          p2[j] = in ? p[2 * aph] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          if (a.gain == GAIN_PGDN) {
+            x = fmaf(p0[j], x, p1[j]);
+          } else {
+            x = fmaf(p0[j], x, p1[j]) / fmaf(p2[j], x, 1.f);
+          }
         }
       }
     }
@@ -164,7 +212,7 @@ hipError_t launch_segment_stats(const StatArgs& a, hipStream_t st) {
   }
   const long items = static_cast<long>(a.B) * a.H * (a.gain == GAIN_KDN_ISO ? 1 : a.dk);
   const long cover = items > static_cast<long>(a.H) * a.nseg ? items : static_cast<long>(a.H) * a.nseg;
-  hipLaunchKernelGGL(segment_chain_kernel, dim3(static_cast<unsigned>((cover + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(segment_chain_kernel, dim3(static_cast<unsigned>((cover + 63) / 64)), dim3(64), 0,
                      st, a);
   return hipGetLastError();
 }
