@@ -13,13 +13,14 @@
 // Networks §2.6), so the statistic at every segment start comes from
 // (1) segment_summary_kernel: the composed map of every piece of `lsub`
 //     tokens, all pieces in parallel;
-// (2) segment_chain_kernel: per head and channel, the pieces applied in order
-//     from aux0, the value at each segment start written for the segment's
-//     head of the [B, H nseg] view, and the value after the last token as
-//     aux_final.
-// A summary holds three floats per channel: PGDN (m, c, -) with
-// A -> m A + c; KDN (m00, m01, m10) with p -> (m00 p + m01) / (m10 p + 1), the
-// map's matrix kept normalised to a (1, 1) entry of 1 after every token.
+// (2) segment_chain_kernel: per head and channel, one wavefront scans the
+//     pieces' maps 64 at a time (an inclusive scan across the lanes) and
+//     applies the prefixes to the carried value: the value at each segment
+//     start is written for the segment's head of the [B, H nseg] view, the
+//     value after the last token as aux_final.
+// A summary is the map p -> (m00 p + m01) / (m10 p + 1) as three floats
+// (m00, m01, m10), its matrix normalised to a (1, 1) entry of 1; PGDN's affine
+// map A -> m A + c is the case (m, c, 0).  Layout [B, H, aph, T / lsub, 3].
 #include "common.hpp"
 #include "gains.hpp"
 #include "launch.hpp"
@@ -44,7 +45,7 @@ __device__ __forceinline__ void mobius_step(float& m00, float& m01, float& m10, 
 // The loads of U tokens are issued before their arithmetic (the composition
 // is a serial chain per channel; its inputs are not).
 template <int DK, int GAIN>
-__global__ __launch_bounds__(DK) void segment_summary_kernel(StatArgs a) {
+__global__ __launch_bounds__(DK) __attribute__((amdgpu_waves_per_eu(1, 4))) void segment_summary_kernel(StatArgs a) {
   constexpr int U = 16;  // lsub is a multiple of 64
   const int c = threadIdx.x;
   const int nsub = a.T / a.lsub;
@@ -91,10 +92,10 @@ __global__ __launch_bounds__(DK) void segment_summary_kernel(StatArgs a) {
     }
     s0 = m00, s1 = m01, s2 = m10;
   }
-  float* out = a.summ + static_cast<long>(blockIdx.x) * 3 * DK + c;
+  float* out = a.summ + ((bh * DK + c) * nsub + blockIdx.x % nsub) * 3;
   out[0] = s0;
-  out[DK] = s1;
-  out[2 * DK] = s2;
+  out[1] = s1;
+  out[2] = s2;
 }
 
 // Isotropic KDN: thread i forms token i's map from its channel sums; the
@@ -151,47 +152,66 @@ __global__ __launch_bounds__(256) void segment_summary_iso_kernel(StatArgs a) {
   }
 }
 
-// One thread per (head, channel): the pieces applied in order, their
-// summaries loaded U at a time ahead of the serial arithmetic.
+// The composition L R of two normalised maps (L after R), renormalised.
+__device__ __forceinline__ void mobius_compose(float& l00, float& l01, float& l10, float r00, float r01,
+                                               float r10) {
+  const float inv = 1.f / fmaf(l10, r01, 1.f);
+  const float n00 = fmaf(l00, r00, l01 * r10);
+  const float n01 = fmaf(l00, r01, l01);
+  const float n10 = fmaf(l10, r00, r10);
+  l00 = n00 * inv;
+  l01 = n01 * inv;
+  l10 = n10 * inv;
+}
+
+// One wavefront per (head, channel).  Round by round, lane l takes piece
+// j0 + l (the identity past the last piece), the lanes' maps are scanned so
+// that lane l holds pieces j0 .. j0 + l composed, and every lane applies its
+// prefix to the value carried into the round.  The next round's summaries are
+// loaded before the current round's scan.
 __global__ __launch_bounds__(64) void segment_chain_kernel(StatArgs a) {
-  constexpr int U = 8;
   const int aph = a.gain == GAIN_KDN_ISO ? 1 : a.dk;
-  const long item = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const long nitems = static_cast<long>(a.B) * a.H * aph;
-  if (item < nitems) {
-    const long bh = item / aph;
-    const int c = static_cast<int>(item % aph);
-    const int nsub = a.T / a.lsub, per = nsub / a.nseg;
-    float x = a.aux0 ? a.aux0[item] : 1.f;
-    const float* sm = a.summ + bh * nsub * 3 * aph + c;
-    for (int s = 0; s < a.nseg; ++s) {
-      a.aux_in[(bh * a.nseg + s) * aph + c] = x;
-      for (int j0 = s * per; j0 < (s + 1) * per; j0 += U) {
-        float p0[U], p1[U], p2[U];
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-          // pieces past the segment's end read as the identity map
-          const bool in = j0 + j < (s + 1) * per;
-          const float* p = sm + static_cast<long>(in ? j0 + j : j0) * 3 * aph;
-          p0[j] = in ? p[0] : 1.f;
-          p1[j] = in ? p[aph] : 0.f;
-          p2[j] = in ? p[2 * aph] : 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-          if (a.gain == GAIN_PGDN) {
-            x = fmaf(p0[j], x, p1[j]);
-          } else {
-            x = fmaf(p0[j], x, p1[j]) / fmaf(p2[j], x, 1.f);
-          }
-        }
-      }
-    }
-    if (a.aux_final) a.aux_final[item] = x;
-  }
+  const int lane = threadIdx.x;
+  const long item = blockIdx.x;  // head bh, channel c: item = bh aph + c
   // the per-head PGDN centre, repeated for the nseg segment heads of the view
-  if (a.gain == GAIN_PGDN && item < static_cast<long>(a.H) * a.nseg)
-    a.mu_seg[item] = a.g.mu_log[item / a.nseg];
+  if (a.gain == GAIN_PGDN && item == 0)
+    for (int e = lane; e < a.H * a.nseg; e += 64) a.mu_seg[e] = a.g.mu_log[e / a.nseg];
+  if (item >= static_cast<long>(a.B) * a.H * aph) return;
+  const long bh = item / aph;
+  const int c = static_cast<int>(item % aph);
+  const int nsub = a.T / a.lsub, per = nsub > 0 ? nsub / a.nseg : 1;
+  float x = a.aux0 ? a.aux0[item] : 1.f;
+  if (nsub == 0) {  // T = 0: every segment is empty
+    for (int s = lane; s < a.nseg; s += 64) a.aux_in[(bh * a.nseg + s) * aph + c] = x;
+    if (lane == 0 && a.aux_final) a.aux_final[item] = x;
+    return;
+  }
+  if (lane == 0) a.aux_in[bh * a.nseg * aph + c] = x;
+  const float* sm = a.summ + item * nsub * 3;
+  float n0, n1, n2;
+  auto load = [&](int j) {
+    const float* p = sm + static_cast<long>(j < nsub ? j : nsub - 1) * 3;
+    const float q0 = p[0], q1 = p[1], q2 = p[2];
+    n0 = j < nsub ? q0 : 1.f;
+    n1 = j < nsub ? q1 : 0.f;
+    n2 = j < nsub ? q2 : 0.f;
+  };
+  load(lane);
+  for (int j0 = 0; j0 < nsub; j0 += 64) {
+    float m00 = n0, m01 = n1, m10 = n2;
+    load(j0 + 64 + lane);
+    for (int d = 1; d < 64; d *= 2) {
+      const float e00 = __shfl_up(m00, d), e01 = __shfl_up(m01, d), e10 = __shfl_up(m10, d);
+      if (lane >= d) mobius_compose(m00, m01, m10, e00, e01, e10);
+    }
+    const float y = fmaf(m00, x, m01) / fmaf(m10, x, 1.f);
+    const int j = j0 + lane;
+    // the value after the last piece of segment s - 1 enters segment s
+    if (j < nsub && (j + 1) % per == 0 && (j + 1) / per < a.nseg)
+      a.aux_in[(bh * a.nseg + (j + 1) / per) * aph + c] = y;
+    x = __shfl(y, 63);
+  }
+  if (lane == 0 && a.aux_final) a.aux_final[item] = x;
 }
 
 hipError_t launch_segment_stats(const StatArgs& a, hipStream_t st) {
@@ -211,9 +231,7 @@ hipError_t launch_segment_stats(const StatArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   const long items = static_cast<long>(a.B) * a.H * (a.gain == GAIN_KDN_ISO ? 1 : a.dk);
-  const long cover = items > static_cast<long>(a.H) * a.nseg ? items : static_cast<long>(a.H) * a.nseg;
-  hipLaunchKernelGGL(segment_chain_kernel, dim3(static_cast<unsigned>((cover + 63) / 64)), dim3(64), 0,
-                     st, a);
+  hipLaunchKernelGGL(segment_chain_kernel, dim3(static_cast<unsigned>(items)), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -211,6 +211,8 @@ def test_chunk_fwd_long_full_size_sampled_head():
     ("kdn", "channel", "scaled", 1024, 2, 64),
     ("kdn_iso", "channel", "scaled", 2048, 4, 128),
     ("kdn_iso", "channel", "scaled", 1280, 10, 64),  # 128-token segments
+    ("kdn_iso", "channel", "scaled", 8320, 2, 128),  # 130 pieces of 64 tokens: three scan rounds
+    ("pgdn", "scalar", "unit", 8320, 5, 128),        # 65 pieces of 128 tokens
 ])
 def test_chunk_fwd_long_statistic_gains(gain, decay, keys, T, nseg, d):
     """dn_chunk_fwd_long with a gain statistic (PGDN's A_t, KDN's p_t and b_t):
