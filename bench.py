@@ -352,6 +352,15 @@ def main():
                                       "ms_segments": ms5,
                                       "tokens_per_s_segments": longpg.tokens / (ms5 * 1e-3)}
         log(f"[bench] {longpg.name}: one pass {ms4:.3f} ms, by 16 segments {ms5:.3f} ms")
+        # diagonal KDN with per-channel decay at the same batch-1 shape
+        longkd = W.Workload("kdn_long_B1H8T32768d128", "kdn", "channel", "bf16", 1, 8, 32768, 128,
+                            128, seed=53)
+        ms6, _ = time_chunk(longkd, max(5, args.steps // 4), args.warmup, args.settle_s)
+        ms7 = time_chunk_long(longkd, 16, max(5, args.steps // 2), args.warmup, args.settle_s)
+        extra["long_prefill_kdn"] = {"workload": longkd.name, "ms_one_pass": ms6, "nseg": 16,
+                                     "ms_segments": ms7,
+                                     "tokens_per_s_segments": longkd.tokens / (ms7 * 1e-3)}
+        log(f"[bench] {longkd.name}: one pass {ms6:.3f} ms, by 16 segments {ms7:.3f} ms")
         dwl = W.WORKLOADS[4]
         dms = time_decode(dwl, args.decode_steps, args.settle_s)
         gbs = decode_bytes(dwl) / (dms * 1e-3) / 1e9
