@@ -213,6 +213,7 @@ def test_chunk_fwd_long_full_size_sampled_head():
     ("kdn_iso", "channel", "scaled", 1280, 10, 64),  # 128-token segments
     ("kdn_iso", "channel", "scaled", 8320, 2, 128),  # 130 pieces of 64 tokens: three scan rounds
     ("pgdn", "scalar", "unit", 8320, 5, 128),        # 65 pieces of 128 tokens
+    ("pgdn", "scalar", "unit", 1024, 4, 64),
 ])
 def test_chunk_fwd_long_statistic_gains(gain, decay, keys, T, nseg, d):
     """dn_chunk_fwd_long with a gain statistic (PGDN's A_t, KDN's p_t and b_t):
@@ -227,6 +228,44 @@ def test_chunk_fwd_long_statistic_gains(gain, decay, keys, T, nseg, d):
     inp["aux0"] = rng.uniform(0.5, 2.0, size=shape).astype(np.float32)
     o, S, aux = gpu_chunk_long(wl, inp, nseg)
     _check(wl, inp, None, o, S, aux)
+
+
+@pytest.mark.parametrize("gain", ["kla", "pgdn", "kdn_iso"])
+def test_chunk_fwd_long_empty_sequence(gain):
+    """T = 0 through dn_chunk_fwd_long: S_final is S0 and aux_final is aux0
+    (q, k, v, o point at one-token buffers; no token is read or written)."""
+    import ctypes
+    from recurrent_sequence_mixer_amd import dn
+    decay = "channel" if gain == "kdn_iso" else "scalar"
+    desc = dn.make_desc(1, 2, 0, 128, 128, torch.bfloat16, gain, decay, 1e-6, 1.5, 1.0)
+    dev = "cuda"
+    q, k, v, o = (torch.ones((1, 2, 1, 128), dtype=torch.bfloat16, device=dev) for _ in range(4))
+    alpha = torch.ones((1, 2, 1, 128) if decay == "channel" else (1, 2, 1), device=dev,
+                       dtype=torch.bfloat16 if decay == "channel" else torch.float32)
+    one = torch.ones((1, 2, 1), device=dev)
+    gates = {"alpha": alpha, "eta": one}
+    if gain == "pgdn":
+        gates |= {"alphaP": one, "betaP": one, "mu_log": torch.zeros(2, device=dev)}
+    if gain == "kdn_iso":
+        gates |= {"omega": one, "r": one}
+    g = torch.Generator(device="cpu").manual_seed(9)
+    S0 = torch.randn((1, 2, 128, 128), generator=g).to(dev)
+    aux0 = (torch.rand((1, 2) if gain == "kdn_iso" else (1, 2, 128), generator=g) + 0.5).to(dev)
+    S = torch.full_like(S0, float("nan"))
+    aux = torch.full_like(aux0, float("nan"))
+    nbytes = dn.lib().dn_chunk_fwd_long_workspace(ctypes.byref(desc), 4)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    gt = dn.make_gates(gates)
+    st = dn.lib().dn_chunk_fwd_long(ctypes.byref(desc), 4, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    ctypes.byref(gt), S0.data_ptr(), aux0.data_ptr(), o.data_ptr(),
+                                    S.data_ptr(), aux.data_ptr(), ws.data_ptr(), nbytes,
+                                    torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.equal(S, S0)
+    if gain != "kla":
+        assert torch.equal(aux, aux0)
+    assert torch.equal(o, torch.ones_like(o))
 
 
 def test_chunk_fwd_long_pgdn_full_size_sampled_head():
