@@ -35,7 +35,7 @@ __device__ __forceinline__ void mobius_step(float& m00, float& m01, float& m10, 
   const float n00 = fmaf(a, m00, om * m10);
   const float n01 = fmaf(a, m01, om);
   const float n10 = fmaf(u, n00, m10);
-  const float inv = 1.f / fmaf(u, n01, 1.f);
+  const float inv = __builtin_amdgcn_rcpf(fmaf(u, n01, 1.f));
   m00 = n00 * inv;
   m01 = n01 * inv;
   m10 = n10 * inv;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(DK) __attribute__((amdgpu_waves_per_eu(1, 4))) void
       }
 #pragma unroll
       for (int j = 0; j < U; ++j) {
-        const float u = a.g.mu_info * kk[j] * kk[j] / rr[j];
+        const float u = a.g.mu_info * kk[j] * kk[j] * __builtin_amdgcn_rcpf(rr[j]);
         mobius_step(m00, m01, m10, aa[j] * aa[j], ww[j], u);
       }
     }
