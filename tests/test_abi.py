@@ -170,6 +170,19 @@ def test_chunk_fwd_long_rejects_bad_arguments():
     assert f(d, nbytes=1024) == -5
     assert f(d, ws=o) == -8  # workspace overlapping the output
 
+    # PGDN: aux0 / aux_final [B, H, dk] fp32 join the alias checks
+    def fa(aux0, aux_final, S0=None, S_final=None):
+        nbytes = L.dn_chunk_fwd_long_workspace(ctypes.byref(dp), 4)
+        gp = _gates(alphaP=FAKE + (6 << 30), betaP=FAKE + (7 << 30), mu_log=FAKE + (8 << 30))
+        return L.dn_chunk_fwd_long(ctypes.byref(dp), 4, q, k, v, ctypes.byref(gp), S0, aux0, o,
+                                   S_final, aux_final, ws, nbytes, None)
+    aux = FAKE + (9 << 30)
+    assert fa(aux, aux + 256) == -8      # aux_final overlapping aux0 other than exactly
+    assert fa(aux, o) == -8              # aux_final overlapping the output
+    assert fa(aux, ws + 64) == -8        # aux_final inside the workspace
+    assert fa(ws + 64, None) == -8       # aux0 inside the workspace
+    assert fa(aux, FAKE + (10 << 30), S_final=FAKE + (10 << 30) + 512) == -8  # aux_final in S_final
+
 
 def test_bench_refuses_more_than_one_gpu():
     """bench.py runs on one GPU; --gpus N > 1 exits with a message before any GPU work."""
