@@ -260,7 +260,9 @@ struct Smem {
   alignas(16) float gnr[CD ? 2 : 1][CD ? DK : 4];
 };
 
-template <int DK, int GAIN>
+// OUT = false: an instance for launches without an output (a.o == NULL), whose
+// consumers leave out Q S and M U.
+template <int DK, int GAIN, bool OUT>
 __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
   constexpr int NT = WS_THREADS;        // threads
   constexpr int NP = 256;               // producer threads
@@ -1058,40 +1060,40 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
           go[rt] = sm.gam[c & 1][16 * rt + c16];
         }
         // K and Q fragments of row tile rt + 1 are read while rt multiplies
-        bf16x8 kf[KS], qf[KS];
+        bf16x8 kf[KS], qf[OUT ? KS : 1];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           kf[s] = KL::frag32(kb, fb, 0, s);
-          qf[s] = KL::frag32(qb, fb, 0, s);
+          if constexpr (OUT) qf[s] = KL::frag32(qb, fb, 0, s);
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          bf16x8 kn[KS], qn[KS];
+          bf16x8 kn[KS], qn[OUT ? KS : 1];
           if (rt < 3) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
               kn[s] = KL::frag32(kb, fb, 16 * (rt + 1), s);
-              qn[s] = KL::frag32(qb, fb, 16 * (rt + 1), s);
+              if constexpr (OUT) qn[s] = KL::frag32(qb, fb, 16 * (rt + 1), s);
             }
           }
           f32x4 ak = zero4(), aq = zero4();
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
             ak = mfma32(kf[s], Spk[s], ak);
-            aq = mfma32(Spk[s], qf[s], aq);
+            if constexpr (OUT) aq = mfma32(Spk[s], qf[s], aq);
           }
           if (rt < 3) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
               kf[s] = kn[s];
-              qf[s] = qn[s];
+              if constexpr (OUT) qf[s] = qn[s];
             }
           }
           // R[t][c] = V[t][c] - g_t (K S)[t][c], rows t = 16 rt + 4 g4 + i
           const f32x4 vv = unpack16(vt[rt]);
           R[rt] = CD ? vv - ak : vv - gt[rt] * ak;
           // (Q S)^T[c][t] scaled by g_t, token t = 16 rt + c16
-          OQ[rt] = CD ? aq : aq * go[rt];
+          if constexpr (OUT) OQ[rt] = CD ? aq : aq * go[rt];
         }
         gn = sm.gam[c & 1][CH - 1];
       }
@@ -1123,19 +1125,21 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
         U1 = cat8(Ub[2], Ub[3]);
         F0 = cat8(Fb[0], Fb[1]);
         F1 = cat8(Fb[2], Fb[3]);
-        // O^T = g (Q S)^T + (M U)^T: lane holds value columns 16 ct + 4 g4 .. +3
-        // of token 16 rt + c16; rows past the end fall outside the resource
-        // o == NULL: an empty resource, every store is dropped
-        const auto ro = a.o && !xfer
-                            ? rsrc(static_cast<uint16_t*>(a.o) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv)
-                            : rsrc(a.k, 0);
+        if constexpr (OUT) {
+          // O^T = g (Q S)^T + (M U)^T: lane holds value columns 16 ct + 4 g4 .. +3
+          // of token 16 rt + c16; rows past the end fall outside the resource
+          // a transfer slice: an empty resource, every store is dropped
+          const auto ro = a.o && !xfer
+                              ? rsrc(static_cast<uint16_t*>(a.o) + v_base + static_cast<long>(t0) * a.dv, 2 * n * a.dv)
+                              : rsrc(a.k, 0);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const uint16_t* mrow = sm.mp + (16 * rt + c16) * PT + 8 * g4;
-          f32x4 o = mfma32(U0, __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(mrow)), OQ[rt]);
-          if (rt >= 2) o = mfma32(U1, __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(mrow + 32)), o);
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])}, ro,
-                                                ooff[rt], 0, 0);
+          for (int rt = 0; rt < 4; ++rt) {
+            const uint16_t* mrow = sm.mp + (16 * rt + c16) * PT + 8 * g4;
+            f32x4 o = mfma32(U0, __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(mrow)), OQ[rt]);
+            if (rt >= 2) o = mfma32(U1, __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(mrow + 32)), o);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])}, ro,
+                                                  ooff[rt], 0, 0);
+          }
         }
         // PGDN: v of chunk c + 1 into LDS (chunk c's was last read in P1),
         // the loads of q and v of chunk c + 2 (the loads of k go out in P3)
@@ -1429,11 +1433,11 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
 
 }  // namespace ws
 
-template <int DK, int GAIN>
-static hipError_t launch_ws_one(const ChunkArgs& a, hipStream_t st) {
+template <int DK, int GAIN, bool OUT>
+static hipError_t launch_ws_inst(const ChunkArgs& a, hipStream_t st) {
   using Sm = ws::Smem<DK, GAIN>;
   static_assert(sizeof(Sm) <= 160 * 1024, "LDS budget");
-  auto kern = ws::chunk_fwd_ws_kernel<DK, GAIN>;
+  auto kern = ws::chunk_fwd_ws_kernel<DK, GAIN, OUT>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(sizeof(Sm)));
@@ -1441,6 +1445,13 @@ static hipError_t launch_ws_one(const ChunkArgs& a, hipStream_t st) {
   dim3 grid(static_cast<unsigned>(((a.dv + a.xcols) / ws::BV) * a.B * a.H));
   hipLaunchKernelGGL(kern, grid, dim3(ws::WS_THREADS), sizeof(Sm), st, a);
   return hipGetLastError();
+}
+
+// launches without an output (a.o == NULL) take the instance that leaves out
+// Q S and M U
+template <int DK, int GAIN>
+static hipError_t launch_ws_one(const ChunkArgs& a, hipStream_t st) {
+  return a.o ? launch_ws_inst<DK, GAIN, true>(a, st) : launch_ws_inst<DK, GAIN, false>(a, st);
 }
 
 // bf16 io, scalar decay, gains KLA / GDN / PGDN / explicit.
