@@ -260,8 +260,9 @@ struct Smem {
   alignas(16) float gnr[CD ? 2 : 1][CD ? DK : 4];
 };
 
-// OUT = false: an instance for launches without an output (a.o == NULL), whose
-// consumers leave out Q S and M U.
+// OUT = false: an instance for launches without an output (a.o == NULL): the
+// consumers leave out Q S and M U, the producers and loaders the M tiles, and
+// q is not read.
 template <int DK, int GAIN, bool OUT>
 __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
   constexpr int NT = WS_THREADS;        // threads
@@ -428,7 +429,9 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
     auto fetch_q = [&](int c) __attribute__((always_inline)) {
       const int t0 = c * CH;
       const int n = ntok(c);
-      const auto rq = rsrc(static_cast<const uint16_t*>(a.q) + qk_base + static_cast<long>(t0) * DK, 2 * n * DK);
+      // without an output q is not needed: an empty resource, every load returns 0
+      const auto rq = OUT ? rsrc(static_cast<const uint16_t*>(a.q) + qk_base + static_cast<long>(t0) * DK, 2 * n * DK)
+                          : rsrc(a.k, 0);
 #pragma unroll
       for (int j = 0; j < KV_LOADS; ++j) pq[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, koff[j], 0, 0);
     };
@@ -846,10 +849,11 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const bf16x8 kp = KL::frag32(kb, fb, 16 * p, s);
-        const bf16x8 qp = KL::frag32(qb, fb, 16 * p, s);
+        bf16x8 qp;
+        if constexpr (OUT) qp = KL::frag32(qb, fb, 16 * p, s);  // M only with an output
         const bf16x8 wp = HAS_W || CD ? KL::frag32(wb, fb, 16 * p, s) : kp;
         at = mfma32(wp, kp, at);  // lane: [j = 16p + 4 g4 + u][i = 16p + c16]
-        mt = mfma32(wp, qp, mt);
+        if constexpr (OUT) mt = mfma32(wp, qp, mt);
         an = mfma32(kp, wp, an);  // lane: [i = 16p + 4 g4 + u][j = 16p + c16]
       }
     };
@@ -860,6 +864,7 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
 #pragma unroll
       for (int k = 0; k < NIT; ++k) {
         const int it = item_of(k);
+        if (!OUT && item_is_m(it)) continue;  // M tiles only with an output
         const int bi = item_bi(it), bj = item_bj(it);
         const uint16_t* xsrc = item_is_m(it) ? qb : kb;
         f32x4 acc = zero4();
@@ -974,8 +979,9 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
         mt[u] = (4 * g4 + u <= c16) ? mt[u] * f : 0.f;
         an[u] = (c16 < 4 * g4 + u) ? an[u] * (CD ? cdi : exp2_hw(gd_j[u] - gd_i) * cd_i) : 0.f;
       }
-      *reinterpret_cast<u32x2*>(&sm.mp[(16 * p + c16) * PT + mcol(16 * p + 4 * g4)]) =
-          u32x2{pack_bf2(mt[0], mt[1]), pack_bf2(mt[2], mt[3])};
+      if constexpr (OUT)
+        *reinterpret_cast<u32x2*>(&sm.mp[(16 * p + c16) * PT + mcol(16 * p + 4 * g4)]) =
+            u32x2{pack_bf2(mt[0], mt[1]), pack_bf2(mt[2], mt[3])};
     };
     auto scale_off = [&](int c) __attribute__((always_inline)) {
       const float* g2 = sm.g2[c & 1];
@@ -992,6 +998,7 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
       for (int k = 0; k < NIT; ++k) {
         const int it = item_of(k);
         const bool m = item_is_m(it);
+        if (!OUT && m) continue;
         f32x4 val;
 #pragma unroll
         for (int u = 0; u < 4; ++u) val[u] = off[k][u] * (rho[k] * ko_j[k][u]);
