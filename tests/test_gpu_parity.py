@@ -230,6 +230,21 @@ def test_chunk_fwd_long_statistic_gains(gain, decay, keys, T, nseg, d):
     _check(wl, inp, None, o, S, aux)
 
 
+@pytest.mark.parametrize("gain,decay,keys", [("kla", "scalar", "scaled"), ("pgdn", "scalar", "unit"),
+                                             ("kdn", "channel", "scaled")])
+def test_chunk_fwd_long_batch_of_two(gain, decay, keys):
+    """B = 2, H = 3 through dn_chunk_fwd_long: the [B, H nseg] segment view
+    across batches, and the combine's workgroup mapping when the slices of
+    the heads do not divide evenly over the XCDs."""
+    wl = W.Workload(f"{gain}_long_b2", gain, decay, "bf16", 2, 3, 1024, 128, 128, keys=keys, seed=90)
+    inp = W.generate(wl)
+    if gain != "kla":
+        rng = np.random.default_rng(91)
+        inp["aux0"] = rng.uniform(0.5, 2.0, size=(2, 3, 128)).astype(np.float32)
+    o, S, aux = gpu_chunk_long(wl, inp, 4)
+    _check(wl, inp, None, o, S, aux)
+
+
 @pytest.mark.parametrize("gain", ["kla", "pgdn", "kdn_iso"])
 def test_chunk_fwd_long_empty_sequence(gain):
     """T = 0 through dn_chunk_fwd_long: S_final is S0 and aux_final is aux0
