@@ -98,9 +98,10 @@ __global__ __launch_bounds__(DK) __attribute__((amdgpu_waves_per_eu(1, 4))) void
   out[2] = s2;
 }
 
-// Isotropic KDN: thread i forms token i's map from its channel sums; the
-// piece's maps are then composed pairwise in a tree (later map on the left),
-// every product renormalised to a (1, 1) entry of 1.  lsub is a power of two.
+// Isotropic KDN: each token's map from its channel sums (a group of lanes per
+// token row); the piece's maps are then composed pairwise in a tree (later
+// map on the left), every product renormalised to a (1, 1) entry of 1.  lsub
+// is a power of two.
 template <int DK>
 __global__ __launch_bounds__(256) void segment_summary_iso_kernel(StatArgs a) {
   __shared__ float f00[256], f01[256], f10[256];
@@ -108,30 +109,39 @@ __global__ __launch_bounds__(256) void segment_summary_iso_kernel(StatArgs a) {
   const int nsub = a.T / a.lsub;
   const long bh = blockIdx.x / nsub;
   const long t0 = bh * a.T + static_cast<long>(blockIdx.x % nsub) * a.lsub;
-  if (i < a.lsub) {
-    const uint4* kr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + (t0 + i) * DK);
-    const uint4* ar = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.g.alpha) + (t0 + i) * DK);
+  // channel sums of token t: the DK / 8 lanes of a row group read its
+  // 16-byte pieces of k and alpha (whole rows per load instruction) and sum
+  // them across the group with lane exchanges
+  constexpr int LPR = DK / 8;            // lanes per row
+  constexpr int RPI = 256 / LPR;         // rows per iteration of the block
+  const int piece = i % LPR;
+  for (int t = i / LPR; t < a.lsub; t += RPI) {
+    const uint4 kv = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + (t0 + t) * DK)[piece];
+    const uint4 av = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.g.alpha) + (t0 + t) * DK)[piece];
+    const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, aw[4] = {av.x, av.y, av.z, av.w};
     float nk = 0.f, sa = 0.f;
-#pragma unroll 4
-    for (int j = 0; j < DK / 8; ++j) {
-      const uint4 kv = kr[j], av = ar[j];
-      const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, aw[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float k0 = __uint_as_float(kw[e] << 16), k1 = __uint_as_float(kw[e] & 0xffff0000u);
-        const float a0 = __uint_as_float(aw[e] << 16), a1 = __uint_as_float(aw[e] & 0xffff0000u);
-        nk = fmaf(k0, k0, fmaf(k1, k1, nk));
-        sa = fmaf(a0, a0, fmaf(a1, a1, sa));
-      }
+    for (int e = 0; e < 4; ++e) {
+      const float k0 = __uint_as_float(kw[e] << 16), k1 = __uint_as_float(kw[e] & 0xffff0000u);
+      const float a0 = __uint_as_float(aw[e] << 16), a1 = __uint_as_float(aw[e] & 0xffff0000u);
+      nk = fmaf(k0, k0, fmaf(k1, k1, nk));
+      sa = fmaf(a0, a0, fmaf(a1, a1, sa));
     }
-    const float r = a.g.r[t0 + i];
-    const float am = sa * (1.f / DK), om = static_cast<const float*>(a.g.omega)[t0 + i];
-    const float u = a.g.mu_info * nk / (DK * r);
-    // the token's map [[am, om], [u am, 1 + u om]] / (1 + u om)
-    const float inv = 1.f / fmaf(u, om, 1.f);
-    f00[i] = am * inv;
-    f01[i] = om * inv;
-    f10[i] = u * am * inv;
+#pragma unroll
+    for (int m = 1; m < LPR; m *= 2) {
+      nk += __shfl_xor(nk, m);
+      sa += __shfl_xor(sa, m);
+    }
+    if (piece == 0) {
+      const float r = a.g.r[t0 + t];
+      const float am = sa * (1.f / DK), om = static_cast<const float*>(a.g.omega)[t0 + t];
+      const float u = a.g.mu_info * nk / (DK * r);
+      // the token's map [[am, om], [u am, 1 + u om]] / (1 + u om)
+      const float inv = 1.f / fmaf(u, om, 1.f);
+      f00[t] = am * inv;
+      f01[t] = om * inv;
+      f10[t] = u * am * inv;
+    }
   }
   for (int w = 1; w < a.lsub; w *= 2) {
     __syncthreads();
