@@ -187,7 +187,11 @@ int dn_chunk_fwd(const dn_desc* desc, const void* q, const void* k, const void* 
  *   dn_chunk_fwd_long_workspace returns that size in bytes, or 0 for an
  *   invalid descriptor, nseg < 1, or segments that are not whole chunks.
  *   Three launches on `stream` (five with a statistic); nothing is
- *   allocated. */
+ *   allocated.  Choosing nseg: the last launch runs B H nseg d_v / 64
+ *   workgroups of one chunk step at a time each; filling the device's
+ *   compute units once (256 on MI355X) is best, e.g. nseg = 16 for B1 H8
+ *   d128 (measured at T = 32768 and 131072: 32 and 64 segments are slower,
+ *   the combine's serial chain growing with nseg). */
 size_t dn_chunk_fwd_long_workspace(const dn_desc* desc, int nseg);
 int dn_chunk_fwd_long(const dn_desc* desc, int nseg, const void* q, const void* k, const void* v,
                       const dn_gates* gates, const float* S0, const float* aux0, void* o,

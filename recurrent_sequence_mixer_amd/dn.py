@@ -148,7 +148,8 @@ def chunk_fwd_long(q, k, v, gates: Dict[str, torch.Tensor], nseg: int, *, gain="
     """Chunked forward by nseg parallel segments per head (bf16; KLA, GDN, PGDN,
     explicit with scalar decay, KDN and isotropic KDN with per-channel decay):
     returns (o, S_final, aux_final).  The workspace is allocated here with
-    torch and passed to the library."""
+    torch and passed to the library.  nseg: B H nseg d_v / 64 near the number
+    of compute units works best (16 for B1 H8 d128)."""
     B, H, T, dk = k.shape
     dv = v.shape[-1]
     if decay is None:
