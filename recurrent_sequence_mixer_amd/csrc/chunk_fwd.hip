@@ -211,7 +211,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
   // XCD-aware mapping of the 1-D grid: consecutive workgroups are dealt to
   // the 8 XCDs in turn, so the value slices of one head get ids that are
   // equal modulo 8 and share that XCD's L2 (k and q are read once from HBM).
-  const int ns = a.dv / BV;
+  const int ns = (a.dv + a.xcols) / BV;  // value slices (and transfer slices)
   const int nwg = ns * a.B * a.H;
   int bh, slice;
   {
@@ -227,6 +227,9 @@ void chunk_fwd_kernel(ChunkArgs a) {
   }
   const int h = bh % a.H;
   const int col0 = slice * BV;  // first value column of this slice
+  // a transfer slice: columns col0 - dv of S0 = I, v = 0, no output
+  const bool xfer = col0 >= a.dv;
+  const bool has_out = a.o && !xfer;
   const int T = a.T;
   const int nchunks = (T + CH - 1) / CH;
   const long qk_base = static_cast<long>(bh) * T * DK;
@@ -234,7 +237,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
   const E* gk = static_cast<const E*>(a.k) + qk_base;
   const E* gq = static_cast<const E*>(a.q) + qk_base;
   const E* gv = static_cast<const E*>(a.v) + v_base;
-  E* go = static_cast<E*>(a.o) + v_base;
+  E* go = a.o ? static_cast<E*>(a.o) + v_base : nullptr;
 
   // ---- state slice in registers: tile dt holds rows 16 dt + 4 g4 + i, column c16
   f32x4 S[DK / 16];
@@ -245,7 +248,8 @@ void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * dt + 4 * g4 + i;
-        S[dt][i] = a.S0 ? a.S0[(static_cast<long>(bh) * DK + row) * a.dv + col] : 0.f;
+        const float s0 = a.S0 && !xfer ? a.S0[(static_cast<long>(bh) * DK + row) * a.dv + col] : 0.f;
+        S[dt][i] = xfer ? (row == col - a.dv ? 1.f : 0.f) : s0;
       }
   }
   // ---- per-channel gain state (PGDN statistic A, KDN variance p)
@@ -304,8 +308,11 @@ void chunk_fwd_kernel(ChunkArgs a) {
       const int e = (tid + j * NT) * VEC;
       const int t = e / BV, cc = e % BV;
       const bool ok = e < CH * BV && t < n;
-      pv[j] = *reinterpret_cast<const u32x4*>(gv + static_cast<long>(t0 + (ok ? t : 0)) * a.dv +
-                                              col0 + (ok ? cc : 0));
+      // transfer slices read v = 0 (their columns lie past d_v: the load
+      // takes column 0 and is discarded)
+      const u32x4 ld = *reinterpret_cast<const u32x4*>(gv + static_cast<long>(t0 + (ok ? t : 0)) * a.dv +
+                                                       (xfer ? 0 : col0) + (ok ? cc : 0));
+      pv[j] = xfer ? u32x4{0u, 0u, 0u, 0u} : ld;
     }
     if (tid < CH) {
       const long ti = static_cast<long>(bh) * T + t0 + (tid < n ? tid : 0);
@@ -360,6 +367,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
 
   // output tile of a chunk (in sm.o) -> HBM, 16-byte rows
   auto store_out = [&](int ts, int nn) __attribute__((always_inline)) {
+    if (!has_out) return;  // a transfer slice, or o == NULL
     for (int e = tid * VEC; e < CH * BV; e += NT * VEC) {
       const int t = e / BV, cc = e % BV;
       if (t < nn)
@@ -1071,14 +1079,17 @@ void chunk_fwd_kernel(ChunkArgs a) {
   DN_PHASE_FLUSH
 
   // ---- final state and auxiliary state
-  if (a.S_final) {
-    const int col = col0 + 16 * wave + c16;
+  float* const fin = xfer ? a.S_final_x : a.S_final;
+  if (fin) {
+    // transfer slices: their columns of S_final_x [B, H, dk, xcols]
+    const int sstride = xfer ? a.xcols : a.dv;
+    const int col = col0 + 16 * wave + c16 - (xfer ? a.dv : 0);
 #pragma unroll
     for (int dt = 0; dt < DK / 16; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * dt + 4 * g4 + i;
-        a.S_final[(static_cast<long>(bh) * DK + row) * a.dv + col] = S[dt][i];
+        fin[(static_cast<long>(bh) * DK + row) * sstride + col] = S[dt][i];
       }
   }
   if constexpr (PG2) {
@@ -1107,7 +1118,7 @@ static hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(smem));
   if (err != hipSuccess) return err;
-  dim3 grid(static_cast<unsigned>((a.dv / BV) * a.B * a.H));
+  dim3 grid(static_cast<unsigned>(((a.dv + a.xcols) / BV) * a.B * a.H));
   hipLaunchKernelGGL(kern, grid, dim3(BV * 4), smem, st, a);
   return hipGetLastError();
 }

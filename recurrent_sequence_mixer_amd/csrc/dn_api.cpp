@@ -234,13 +234,11 @@ DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const
                                 void* ws, size_t ws_bytes, void* stream) {
   int st = check_desc(d, true);
   if (st != DN_OK) return st;
-  // the combinations that run on the producer/consumer kernel
-  const bool scalar_ok = d->decay == DN_DECAY_SCALAR &&
-                         (d->gain == DN_GAIN_KLA || d->gain == DN_GAIN_GDN ||
-                          d->gain == DN_GAIN_EXPLICIT || d->gain == DN_GAIN_PGDN);
-  const bool channel_ok = d->decay == DN_DECAY_CHANNEL &&
-                          (d->gain == DN_GAIN_KDN || d->gain == DN_GAIN_KDN_ISO);
-  if (d->io != DN_BF16 || !(scalar_ok || channel_ok)) return DN_ERR_UNSUPPORTED;
+  // bf16; KDN's statistic with scalar decay is not built (its summaries read
+  // a per-channel alpha)
+  const bool kdn_scalar = (d->gain == DN_GAIN_KDN || d->gain == DN_GAIN_KDN_ISO) &&
+                          d->decay == DN_DECAY_SCALAR;
+  if (d->io != DN_BF16 || kdn_scalar) return DN_ERR_UNSUPPORTED;
   if (!long_shape_ok(d, nseg)) return DN_ERR_SHAPE;
   if (static_cast<long long>(d->B) * d->H * nseg > 65535) return DN_ERR_SHAPE;
   if ((st = check_gates(d, g)) != DN_OK) return st;
@@ -320,8 +318,7 @@ DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const
     if (d->gain == DN_GAIN_PGDN) a.g.mu_log = sa.mu_seg;
   }
   const auto launch = [&]() {
-    return d->decay == DN_DECAY_CHANNEL ? dn::launch_chunk_fwd_bf16_kdn(a, d->gain, s)
-                                        : dn::launch_chunk_fwd_bf16_scalar(a, d->gain, s);
+    return dn::launch_chunk_fwd(a, 1, d->gain, d->decay == DN_DECAY_CHANNEL, s);
   };
   // (1) in one launch: the end states B_s from S_in = 0 (the value slices) and
   // the transfer matrices A_s from S_in = I with v = 0 (d_k more slices)

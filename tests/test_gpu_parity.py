@@ -214,6 +214,10 @@ def test_chunk_fwd_long_full_size_sampled_head():
     ("kdn_iso", "channel", "scaled", 8320, 2, 128),  # 130 pieces of 64 tokens: three scan rounds
     ("pgdn", "scalar", "unit", 8320, 5, 128),        # 65 pieces of 128 tokens
     ("pgdn", "scalar", "unit", 1024, 4, 64),
+    # per-channel decay on the generic chunk kernel: PKDA (PGDN), KLA, GDN
+    ("pgdn", "channel", "unit", 1024, 4, 128),
+    ("kla", "channel", "scaled", 1024, 4, 128),
+    ("gdn", "channel", "unit", 1024, 2, 64),
 ])
 def test_chunk_fwd_long_statistic_gains(gain, decay, keys, T, nseg, d):
     """dn_chunk_fwd_long with a gain statistic (PGDN's A_t, KDN's p_t and b_t):
@@ -225,7 +229,8 @@ def test_chunk_fwd_long_statistic_gains(gain, decay, keys, T, nseg, d):
     inp = W.generate(wl)
     rng = np.random.default_rng(wl.seed)
     shape = (1, 2) if gain == "kdn_iso" else (1, 2, d)
-    inp["aux0"] = rng.uniform(0.5, 2.0, size=shape).astype(np.float32)
+    if gain in ("pgdn", "kdn", "kdn_iso"):
+        inp["aux0"] = rng.uniform(0.5, 2.0, size=shape).astype(np.float32)
     o, S, aux = gpu_chunk_long(wl, inp, nseg)
     _check(wl, inp, None, o, S, aux)
 
