@@ -169,8 +169,8 @@ int dn_chunk_fwd(const dn_desc* desc, const void* q, const void* k, const void* 
  * of each segment in parallel and chains them from aux0, giving the
  * statistic entering every segment and aux_final.  Results equal
  * dn_chunk_fwd's up to rounding.
- *   Built for io = DN_BF16 with every gain and decay except KDN and KDN_ISO
- *   with decay = DN_DECAY_SCALAR (DN_ERR_UNSUPPORTED for those and for fp32).  nseg >= 1 must divide T into
+ *   Built for io = DN_BF16 with every gain and decay (DN_ERR_UNSUPPORTED for
+ *   fp32).  nseg >= 1 must divide T into
  *   segments of a multiple of C = 64 tokens, and B H nseg <= 65535
  *   (DN_ERR_SHAPE).
  *   q, k, v, gates, S0 (nullable: zeros), aux0 (nullable: ones), o, S_final

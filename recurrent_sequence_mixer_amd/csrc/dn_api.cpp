@@ -234,11 +234,7 @@ DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const
                                 void* ws, size_t ws_bytes, void* stream) {
   int st = check_desc(d, true);
   if (st != DN_OK) return st;
-  // bf16; KDN's statistic with scalar decay is not built (its summaries read
-  // a per-channel alpha)
-  const bool kdn_scalar = (d->gain == DN_GAIN_KDN || d->gain == DN_GAIN_KDN_ISO) &&
-                          d->decay == DN_DECAY_SCALAR;
-  if (d->io != DN_BF16 || kdn_scalar) return DN_ERR_UNSUPPORTED;
+  if (d->io != DN_BF16) return DN_ERR_UNSUPPORTED;
   if (!long_shape_ok(d, nseg)) return DN_ERR_SHAPE;
   if (static_cast<long long>(d->B) * d->H * nseg > 65535) return DN_ERR_SHAPE;
   if ((st = check_gates(d, g)) != DN_OK) return st;
@@ -306,6 +302,7 @@ DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const
     sa.nseg = nseg;
     sa.lsub = lay.lsub;
     sa.gain = d->gain;
+    sa.channel = d->decay == DN_DECAY_CHANNEL;
     sa.k = k;
     sa.g = a.g;
     sa.aux0 = aux0;

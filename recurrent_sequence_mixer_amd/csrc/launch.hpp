@@ -75,6 +75,7 @@ hipError_t launch_segment_combine(const CombineArgs& a, hipStream_t st);
 // [B, H, aph].  PGDN also repeats mu_log [H] into mu_seg [H nseg].
 struct StatArgs {
   int B, H, T, dk, nseg, lsub, gain;
+  int channel;  // per-channel decay (alpha bf16 per channel), else fp32 per token
   const void* k;
   GateArgs g;
   const float* aux0;

@@ -44,7 +44,9 @@ __device__ __forceinline__ void mobius_step(float& m00, float& m01, float& m10, 
 // PGDN and diagonal KDN: one thread per key channel, one workgroup per piece.
 // The loads of U tokens are issued before their arithmetic (the composition
 // is a serial chain per channel; its inputs are not).
-template <int DK, int GAIN>
+// CHN: per-channel decay (alpha bf16 [B, H, T, dk]), else one fp32 alpha per
+// token [B, H, T].
+template <int DK, int GAIN, bool CHN>
 __global__ __launch_bounds__(DK) __attribute__((amdgpu_waves_per_eu(1, 4))) void segment_summary_kernel(StatArgs a) {
   constexpr int U = 16;  // lsub is a multiple of 64
   const int c = threadIdx.x;
@@ -71,7 +73,8 @@ __global__ __launch_bounds__(DK) __attribute__((amdgpu_waves_per_eu(1, 4))) void
     }
     s0 = m, s1 = cc, s2 = 0.f;
   } else {
-    const uint16_t* al = static_cast<const uint16_t*>(a.g.alpha) + t0 * DK + c;
+    const uint16_t* al = static_cast<const uint16_t*>(a.g.alpha) + (CHN ? t0 * DK + c : 0);
+    const float* als = static_cast<const float*>(a.g.alpha) + t0;
     const uint16_t* om = static_cast<const uint16_t*>(a.g.omega) + t0 * DK + c;
     float m00 = 1.f, m01 = 0.f, m10 = 0.f;
     for (int i0 = 0; i0 < a.lsub; i0 += U) {
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(DK) __attribute__((amdgpu_waves_per_eu(1, 4))) void
       for (int j = 0; j < U; ++j) {
         const long o = static_cast<long>(i0 + j) * DK;
         kk[j] = bf2f(kp[o]);
-        aa[j] = bf2f(al[o]);
+        aa[j] = CHN ? bf2f(al[o]) : als[i0 + j];
         ww[j] = bf2f(om[o]);
         rr[j] = a.g.r[t0 + i0 + j];
       }
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(DK) __attribute__((amdgpu_waves_per_eu(1, 4))) void
 // token row); the piece's maps are then composed pairwise in a tree (later
 // map on the left), every product renormalised to a (1, 1) entry of 1.  lsub
 // is a power of two.
-template <int DK>
+template <int DK, bool CHN>
 __global__ __launch_bounds__(256) void segment_summary_iso_kernel(StatArgs a) {
   __shared__ float f00[256], f01[256], f10[256];
   const int i = threadIdx.x;
@@ -117,7 +120,8 @@ __global__ __launch_bounds__(256) void segment_summary_iso_kernel(StatArgs a) {
   const int piece = i % LPR;
   for (int t = i / LPR; t < a.lsub; t += RPI) {
     const uint4 kv = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + (t0 + t) * DK)[piece];
-    const uint4 av = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.g.alpha) + (t0 + t) * DK)[piece];
+    const uint4 av = CHN ? reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.g.alpha) + (t0 + t) * DK)[piece]
+                         : uint4{0u, 0u, 0u, 0u};
     const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, aw[4] = {av.x, av.y, av.z, av.w};
     float nk = 0.f, sa = 0.f;
 #pragma unroll
@@ -134,7 +138,9 @@ __global__ __launch_bounds__(256) void segment_summary_iso_kernel(StatArgs a) {
     }
     if (piece == 0) {
       const float r = a.g.r[t0 + t];
-      const float am = sa * (1.f / DK), om = static_cast<const float*>(a.g.omega)[t0 + t];
+      // scalar decay: the mean of alpha^2 over the channels is alpha^2
+      const float al = CHN ? 0.f : static_cast<const float*>(a.g.alpha)[t0 + t];
+      const float am = CHN ? sa * (1.f / DK) : al * al, om = static_cast<const float*>(a.g.omega)[t0 + t];
       const float u = a.g.mu_info * nk / (DK * r);
       // the token's map [[am, om], [u am, 1 + u om]] / (1 + u om)
       const float inv = 1.f / fmaf(u, om, 1.f);
@@ -227,16 +233,19 @@ __global__ __launch_bounds__(64) void segment_chain_kernel(StatArgs a) {
 hipError_t launch_segment_stats(const StatArgs& a, hipStream_t st) {
   if (a.T > 0) {
     const unsigned nblk = static_cast<unsigned>(static_cast<long>(a.B) * a.H * (a.T / a.lsub));
-    if (a.gain == GAIN_KDN_ISO) {
-      if (a.dk == 128) hipLaunchKernelGGL(segment_summary_iso_kernel<128>, dim3(nblk), dim3(256), 0, st, a);
-      else hipLaunchKernelGGL(segment_summary_iso_kernel<64>, dim3(nblk), dim3(256), 0, st, a);
-    } else if (a.gain == GAIN_PGDN) {
-      if (a.dk == 128) hipLaunchKernelGGL((segment_summary_kernel<128, GAIN_PGDN>), dim3(nblk), dim3(128), 0, st, a);
-      else hipLaunchKernelGGL((segment_summary_kernel<64, GAIN_PGDN>), dim3(nblk), dim3(64), 0, st, a);
+#define DN_SUMMARY(DKV, CH)                                                                              \
+  if (a.gain == GAIN_KDN_ISO)                                                                            \
+    hipLaunchKernelGGL((segment_summary_iso_kernel<DKV, CH>), dim3(nblk), dim3(256), 0, st, a);         \
+  else if (a.gain == GAIN_PGDN)                                                                          \
+    hipLaunchKernelGGL((segment_summary_kernel<DKV, GAIN_PGDN, CH>), dim3(nblk), dim3(DKV), 0, st, a); \
+  else                                                                                                   \
+    hipLaunchKernelGGL((segment_summary_kernel<DKV, GAIN_KDN, CH>), dim3(nblk), dim3(DKV), 0, st, a);
+    if (a.dk == 128) {
+      if (a.channel) { DN_SUMMARY(128, true) } else { DN_SUMMARY(128, false) }
     } else {
-      if (a.dk == 128) hipLaunchKernelGGL((segment_summary_kernel<128, GAIN_KDN>), dim3(nblk), dim3(128), 0, st, a);
-      else hipLaunchKernelGGL((segment_summary_kernel<64, GAIN_KDN>), dim3(nblk), dim3(64), 0, st, a);
+      if (a.channel) { DN_SUMMARY(64, true) } else { DN_SUMMARY(64, false) }
     }
+#undef DN_SUMMARY
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -146,7 +146,7 @@ def chunk_fwd_long(q, k, v, gates: Dict[str, torch.Tensor], nseg: int, *, gain="
                    eps=1e-6, x=1.5, mu_info=1.0, S0=None, aux0=None, out=None, S_final=None,
                    aux_final=None, want_state=True, stream=None):
     """Chunked forward by nseg parallel segments per head (bf16; every gain and
-    decay but KDN and isotropic KDN with scalar decay):
+    decay):
     returns (o, S_final, aux_final).  The workspace is allocated here with
     torch and passed to the library.  nseg: B H nseg d_v / 64 near the number
     of compute units works best (16 for B1 H8 d128)."""

@@ -154,8 +154,6 @@ def test_chunk_fwd_long_rejects_bad_arguments():
     assert L.dn_chunk_fwd_long_workspace(ctypes.byref(d), 4) == 8 * 128 * (128 + 2 * 128) * 4
     assert L.dn_chunk_fwd_long_workspace(ctypes.byref(d), 0) == 0
     assert f(_desc(B=1, H=2, T=1024, io=0, dk=64, dv=64)) == -6  # fp32: not built
-    assert f(_desc(B=1, H=2, T=1024, gain="kdn")) == -6  # KDN with scalar decay
-    assert f(_desc(B=1, H=2, T=1024, gain="kdn_iso")) == -6
     # the statistic's part: aux_in [B H nseg, dk] and mu_seg [H nseg] on
     # 256-byte boundaries, then 3 floats per channel for each 256-token piece
     dp = _desc(B=1, H=2, T=1024, gain="pgdn")

@@ -218,6 +218,9 @@ def test_chunk_fwd_long_full_size_sampled_head():
     ("pgdn", "channel", "unit", 1024, 4, 128),
     ("kla", "channel", "scaled", 1024, 4, 128),
     ("gdn", "channel", "unit", 1024, 2, 64),
+    # KDN and isotropic KDN with scalar decay (generic kernel; alpha per token)
+    ("kdn", "scalar", "scaled", 1024, 4, 128),
+    ("kdn_iso", "scalar", "scaled", 1024, 4, 64),
 ])
 def test_chunk_fwd_long_statistic_gains(gain, decay, keys, T, nseg, d):
     """dn_chunk_fwd_long with a gain statistic (PGDN's A_t, KDN's p_t and b_t):
