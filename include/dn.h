@@ -170,9 +170,10 @@ int dn_chunk_fwd(const dn_desc* desc, const void* q, const void* k, const void* 
  * statistic entering every segment and aux_final.  Results equal
  * dn_chunk_fwd's up to rounding.
  *   Built for io = DN_BF16 with every gain and decay (DN_ERR_UNSUPPORTED for
- *   fp32).  nseg >= 1 must divide T into
- *   segments of a multiple of C = 64 tokens, and B H nseg <= 65535
- *   (DN_ERR_SHAPE).
+ *   fp32).  nseg >= 1 must divide T into segments of a multiple of C = 64
+ *   tokens, and B H nseg <= 65535 (DN_ERR_SHAPE).  Any other T: run the
+ *   longest such prefix here and the remaining tokens with dn_chunk_fwd,
+ *   its S0 and aux0 being this call's S_final and aux_final.
  *   q, k, v, gates, S0 (nullable: zeros), aux0 (nullable: ones), o, S_final
  *   (nullable) and aux_final (nullable) are laid out as for dn_chunk_fwd;
  *   aux0 and aux_final are ignored for the gains without a statistic.

@@ -253,6 +253,32 @@ def test_chunk_fwd_long_batch_of_two(gain, decay, keys):
     _check(wl, inp, None, o, S, aux)
 
 
+@pytest.mark.parametrize("gain,decay,keys", [("kla", "scalar", "scaled"), ("pgdn", "scalar", "unit"),
+                                             ("kdn", "channel", "scaled")])
+def test_chunk_fwd_long_then_resume(gain, decay, keys):
+    """T not a multiple of nseg C: the first 1024 tokens by 4 segments, the
+    last 101 with dn_chunk_fwd from the segmented call's S_final and
+    aux_final, against one oracle pass over all 1125 tokens."""
+    from recurrent_sequence_mixer_amd import dn
+    wl = W.Workload(f"{gain}_long_resume", gain, decay, "bf16", 1, 2, 1125, 128, 128, keys=keys,
+                    seed=95)
+    inp = W.generate(wl)
+    t = dn.to_device(inp, torch.bfloat16)
+    names = ("alpha", "eta", "alphaP", "betaP", "omega", "r")
+    part = lambda x, sl: x[:, :, sl].contiguous()
+    gates = lambda sl: {n: part(t[n], sl) for n in names if n in t} | (
+        {"mu_log": t["mu_log"]} if "mu_log" in t else {})
+    kw = dict(gain=gain, eps=wl.eps, x=wl.x, mu_info=wl.mu_info)
+    head, tail = slice(0, 1024), slice(1024, None)
+    o1, S, aux = dn.chunk_fwd_long(part(t["q"], head), part(t["k"], head), part(t["v"], head),
+                                   gates(head), 4, S0=t["S0"], **kw)
+    o2, S, aux = dn.chunk_fwd(part(t["q"], tail), part(t["k"], tail), part(t["v"], tail), gates(tail),
+                              S0=S, aux0=aux, **kw)
+    torch.cuda.synchronize()
+    o = torch.cat([o1, o2], dim=2).float().cpu().numpy()
+    _check(wl, inp, None, o, S.cpu().numpy(), None if aux is None else aux.cpu().numpy())
+
+
 @pytest.mark.parametrize("gain", ["kla", "pgdn", "kdn_iso"])
 def test_chunk_fwd_long_empty_sequence(gain):
     """T = 0 through dn_chunk_fwd_long: S_final is S0 and aux_final is aux0
