@@ -160,6 +160,12 @@ def test_chunk_fwd_long_rejects_bad_arguments():
     base = 8 * 128 * (128 + 2 * 128) * 4
     assert L.dn_chunk_fwd_long_workspace(ctypes.byref(dp), 4) == base + 4096 + 256 + 2 * 4 * 3 * 128 * 4
     assert L.dn_chunk_fwd_long_workspace(ctypes.byref(d), 3) == 0  # does not divide T
+    # isotropic KDN: one statistic per head (aux_in 8 floats, mu_seg 8 floats, 2 x 4 pieces x 3)
+    di = _desc(B=1, H=2, T=1024, gain="kdn_iso", decay="channel")
+    assert L.dn_chunk_fwd_long_workspace(ctypes.byref(di), 4) == base + 256 + 256 + 2 * 4 * 3 * 4
+    # 192-token segments: 64-token pieces, 3 per segment
+    assert L.dn_chunk_fwd_long_workspace(ctypes.byref(_desc(B=1, H=2, T=1536, gain="pgdn")), 8) == \
+        16 * 128 * (128 + 2 * 128) * 4 + 16 * 128 * 4 + 256 + 2 * 24 * 3 * 128 * 4
     assert f(d, nseg=0) == -2
     assert f(d, nseg=3) == -2  # does not divide T
     assert f(d, nseg=32) == -2  # segments of 32 tokens: not whole chunks
