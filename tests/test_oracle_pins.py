@@ -170,6 +170,36 @@ def test_pgdn_scale_worked_example():
     np.testing.assert_allclose(tr["w"][0, 0], B)  # w = eta B * k with k = 1
 
 
+def test_pgdn_scale_uses_current_statistic():
+    """§2.4, Eq. 9 and the three changes listed after it: the write scale B_t
+    is formed from the current statistic A_t, which already holds k_t * k_t.
+    Two tokens chosen so that A_1 = (16, 1) is the teaching example's
+    statistic (B_1 printed on the page) and A_2 = (4, 4) sits at the centre
+    mu = log 4 (B_2 = 1 exactly); a scale formed from A_{t-1} differs in
+    both tokens."""
+    g = load_golden("pgdn_current_statistic_example.json")
+    su = g["setup"]
+    toks = su["tokens"]
+    k = np.sqrt(np.array([t["k_squared"] for t in toks], float))
+    T = len(toks)
+    _, _, A, tr = forward(one(k), one(k), one(np.zeros((T, 2))), "pgdn", one(np.ones(T)),
+                          eta=one(np.full(T, su["eta"])),
+                          alphaP=one([t["alphaP"] for t in toks]),
+                          betaP=one([t["betaP"] for t in toks]), mu_log=np.array([math.log(4.0)]),
+                          x=su["x"], aux0=one(su["A0"]), record=True)
+    np.testing.assert_allclose(tr["A"][0], g["A"], rtol=1e-14)
+    np.testing.assert_allclose(A[0], g["A"][-1], rtol=1e-14)
+    B = tr["B"][0]
+    half_ulp = 0.5 * 10 ** -g["printed_decimals"]
+    np.testing.assert_allclose(B, g["B_printed"], atol=half_ulp)
+    np.testing.assert_allclose(B[1], [1.0, 1.0], rtol=0, atol=1e-15)
+    # the scale from the previous statistic is far from what the oracle forms
+    stale = np.asarray(g["B_from_previous_statistic"], float)
+    assert np.abs(B - stale).max(axis=1).min() > 0.1
+    # w_t = eta B_t * k_t (Eq. 9 with the raw key scaled per channel)
+    np.testing.assert_allclose(tr["w"][0], su["eta"] * B * k, rtol=1e-14)
+
+
 def test_pgdn_scale_bounds():
     """§2.4: B in [1/x, x] for every A > 0; for unit k, k^T k~ in [1/x, x] (§2.7)."""
     dk, x = 64, 1.5
