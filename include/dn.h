@@ -108,13 +108,15 @@ typedef enum dn_gain {
 typedef enum dn_decay { DN_DECAY_SCALAR = 0, DN_DECAY_CHANNEL = 1 } dn_decay;
 
 /* Problem descriptor (host struct).
- *   B, H >= 1; T >= 0 (T = 0: S_final = S0, aux_final = aux0, o untouched);
+ *   B, H >= 1, B H <= 65535; T >= 0 (T = 0: S_final = S0, aux_final = aux0,
+ *   o untouched);
  *   dk in {64, 128}; dv in {64, 128} for dn_decode_step, and for the chunked
  *   calls any multiple of 64 up to 2048 (d_v = v_expand d_k); C = 64 (chunk
  *   length of the chunked forward);
  *   io: dn_dtype of q, k, v, o and of per-channel gates;
  *   gain: dn_gain; decay: dn_decay (KDN requires DN_DECAY_CHANNEL or SCALAR);
- *   eps >= 0 (KLA), x > 1 (PGDN bound: B in [1/x, x]), mu_info > 0 (KDN,
+ *   eps >= 0 (KLA), x >= 1 (PGDN bound: B in [1/x, x];
+ *   x = 1 is the GDN write), mu_info > 0 (KDN,
  *   KDN_ISO). */
 typedef struct dn_desc {
   int32_t B, H, T, dk, dv, C;
@@ -138,6 +140,22 @@ typedef struct dn_gates {
   const void* w;       /* EXPLICIT                                   */
 } dn_gates;
 
+/* Device workspace, in bytes, that dn_chunk_fwd and dn_gain_prep need for
+ * this descriptor: the larger of the two needs, 0 when neither call needs
+ * any, and 0 for an invalid descriptor.  It depends on the descriptor only
+ * (not on pointers or data), so one query serves every call of that shape.
+ *   dn_chunk_fwd: shapes with too few (batch, head, 64-column value slice)
+ *     workgroups to fill the device's compute units and a long sequence
+ *     (bf16 io, T a multiple of C) run by segments of each head, as
+ *     dn_chunk_fwd_long does, on dn_chunk_fwd_long's workspace layout for
+ *     the chosen segment count (e.g. B1 H8 T131072 d128: 16 segments, about
+ *     26 MB); every other shape needs none.
+ *   dn_gain_prep: the gains with a statistic (PGDN, KDN, KDN_ISO), bf16 io
+ *     and T a multiple of C (at least two chunks) scan every chunk in
+ *     parallel; the workspace holds the chunks' piece summaries, the
+ *     statistic entering every chunk and PGDN's centre repeated per chunk. */
+size_t dn_workspace_bytes(const dn_desc* desc);
+
 /* Chunked forward over a whole sequence batch (Kaczmarz Linear Attention
  * §2.5 Eqs. 7-9 and Preconditioned DeltaNet §2.6 Eq. 6 give the chunk form;
  * results equal the token recurrence above up to rounding).
@@ -148,12 +166,17 @@ typedef struct dn_gates {
  *   S_final   final state, nullable.  May alias S0 exactly (in-place resume).
  *   aux_final final A_T / p_T / b_T, nullable.  Must not overlap aux0 (every value
  *             slice of a head reads aux0 while one of them writes aux_final).
+ *   ws        device workspace of ws_bytes >= dn_workspace_bytes(desc) bytes,
+ *             owned by the caller; may be NULL when that size is 0.  It holds
+ *             nothing between calls and may not overlap any other buffer.
+ *             DN_ERR_WORKSPACE when it is missing or too small.
  * No other buffers may overlap (DN_ERR_ALIAS is returned for the overlaps
  * the host can see from the pointer ranges).  With T = 0 the tensors q, k, v,
- * o and the gate table may be NULL. */
+ * o and the gate table may be NULL.  One launch on `stream` (a
+ * segmented schedule: three, five with a statistic); nothing is allocated. */
 int dn_chunk_fwd(const dn_desc* desc, const void* q, const void* k, const void* v,
                  const dn_gates* gates, const float* S0, const float* aux0, void* o,
-                 float* S_final, float* aux_final, void* stream);
+                 float* S_final, float* aux_final, void* ws, size_t ws_bytes, void* stream);
 
 /* Chunked forward of long sequences by segments, for shapes with few heads
  * (e.g. batch-1 prefill): each head's T tokens are cut into nseg segments
@@ -206,7 +229,18 @@ int dn_chunk_fwd_long(const dn_desc* desc, int nseg, const void* q, const void* 
 int dn_decode_step(const dn_desc* desc, const void* q, const void* k, const void* v,
                    const dn_gates* gates, float* S, float* aux, void* o, void* stream);
 
-/* The write-gain scans alone, for inspection and testing.
+/* The write-gain scans alone, for inspection and testing: the write vector
+ * w_t of every token as the chunked forward applies it (KLA / GDN:
+ * Kaczmarz Linear Attention §2.1 and §1.1; PGDN: Preconditioned DeltaNet
+ * §2.4, Eq. 9; KDN: Kalman Delta Networks §2.4, Eqs. 23-30, with the
+ * information scaling of §2.5; KDN_ISO: §2.7, Eq. 40; EXPLICIT: w copied),
+ * the in-chunk cumulative log-decay and the statistic entering each chunk.
+ * Whole chunks (T a multiple of C, at least two) are scanned in parallel:
+ * for the gains with a statistic (bf16 io) the statistic entering every
+ * chunk comes first from chunk summaries of the per-token maps and a carry
+ * across chunks (the gain scan of Kalman Delta Networks §6 and Appendix D:
+ * summaries, carry, replay; the chunked statistic recursion of
+ * Preconditioned DeltaNet §2.6), then every chunk replays its tokens.
  *   w_out     fp32 [B, H, T, dk]: write vectors w_t (required).
  *   g_out     fp32 cumulative log-decay within each chunk of C tokens
  *             (G_t = sum of log alpha from the chunk start through t):
@@ -215,9 +249,15 @@ int dn_decode_step(const dn_desc* desc, const void* q, const void* k, const void
  *             chunk ([B, H, ceil(T/C)]: KDN_ISO b); nullable (ignored by
  *             gains without state).
  *   aux_final fp32 [B, H, dk]: A_T / p_T ([B, H]: KDN_ISO b_T); nullable.
- *   aux0      as for dn_chunk_fwd. */
+ *   aux0      as for dn_chunk_fwd.
+ *   ws        device workspace of ws_bytes >= dn_workspace_bytes(desc)
+ *             bytes (may be NULL when that is 0); DN_ERR_WORKSPACE when
+ *             missing or too small.
+ * Outputs may not overlap inputs, each other or the workspace
+ * (DN_ERR_ALIAS).  One to three launches on `stream`. */
 int dn_gain_prep(const dn_desc* desc, const void* k, const dn_gates* gates, const float* aux0,
-                 float* w_out, float* g_out, float* aux_chunk, float* aux_final, void* stream);
+                 float* w_out, float* g_out, float* aux_chunk, float* aux_final, void* ws,
+                 size_t ws_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* dn_status_string(int status);

@@ -51,30 +51,6 @@ namespace dn {
 
 constexpr int CH = 64;  // chunk length
 
-// Phase-timing hook: a no-op unless the library is built with
-// -DDN_PHASE_TIMING, in which case every wavefront accumulates shader-clock
-// cycles per phase of the chunk loop into dn_phase_cycles[wave][phase].
-#ifdef DN_PHASE_TIMING
-constexpr int DN_NPHASE = 8;
-__device__ unsigned long long dn_phase_cycles[4][DN_NPHASE];
-#define DN_PHASE_DECL unsigned long long ph_acc[DN_NPHASE] = {}, ph_last = __builtin_readcyclecounter();
-#define DN_PHASE(i)                                              \
-  do {                                                           \
-    const unsigned long long now = __builtin_readcyclecounter(); \
-    ph_acc[i] += now - ph_last;                                  \
-    ph_last = now;                                               \
-  } while (0)
-#define DN_PHASE_FLUSH \
-  if (lane == 0)       \
-    for (int i = 0; i < DN_NPHASE; ++i) atomicAdd(&dn_phase_cycles[wave][i], ph_acc[i]);
-#else
-#define DN_PHASE_DECL
-#define DN_PHASE(i) \
-  do {              \
-  } while (0)
-#define DN_PHASE_FLUSH
-#endif
-
 // Synchronisation of LDS traffic between lanes of one wavefront: LDS
 // instructions of a wavefront complete in order; the fences keep the
 // compiler from moving LDS accesses across this point.
@@ -381,7 +357,6 @@ void chunk_fwd_kernel(ChunkArgs a) {
     fetch(0, 1);
     fetch(0, 2);
   }
-  DN_PHASE_DECL
 
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * CH;
@@ -393,15 +368,12 @@ void chunk_fwd_kernel(ChunkArgs a) {
     for (int j = 0; j < (CHANNEL ? KV_LOADS : 0); ++j) cal[j] = pal[j];
 #pragma unroll
     for (int j = 0; j < (GAIN == GAIN_KDN ? KV_LOADS : 0); ++j) com[j] = pom[j];
-    DN_PHASE(0);
     __syncthreads();  // (A) chunk inputs visible
-    DN_PHASE(6);
     // the next chunk's inputs travel from HBM while this chunk is processed;
     // the previous chunk's output tile leaves after them, so that waiting for
     // these loads at the next stash never waits on the stores
     if (c + 1 < nchunks) fetch(c + 1, 0);
     if (c > 0) store_out(t0 - CH, CH);
-    DN_PHASE(7);
 
     // ================= 2. gains =================
     if constexpr (!CHANNEL) {
@@ -714,7 +686,6 @@ void chunk_fwd_kernel(ChunkArgs a) {
     }
     __syncthreads();  // (B) gains visible
     if (c + 1 < nchunks) fetch(c + 1, 1);
-    DN_PHASE(1);
 
     // ================= 3. write-vector operands =================
     if constexpr (!CHANNEL) {
@@ -846,7 +817,6 @@ void chunk_fwd_kernel(ChunkArgs a) {
     }
     __syncthreads();  // (C) operands of the intra-chunk products ready
     if (c + 1 < nchunks) fetch(c + 1, 2);
-    DN_PHASE(2);
 
     // ================= 4. L and M, lower-triangular 16x16 tile pairs =================
     {
@@ -909,7 +879,6 @@ void chunk_fwd_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();  // (D) L, M ready
-    DN_PHASE(3);
 
     // ================= 5. diagonal-block inverses and Khat S, Qhat S =================
     // wavefront w inverts diagonal block(s) w, w + NW, ...: lane c < 16
@@ -992,7 +961,6 @@ void chunk_fwd_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();  // (E) block inverses ready
-    DN_PHASE(4);
 
     // ================= 6. solve, output, state update (per wavefront) =================
     if constexpr (BF16) {
@@ -1068,7 +1036,6 @@ void chunk_fwd_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();  // (F) output tile complete; chunk operands free
-    DN_PHASE(5);
 
   }
   // the last chunk's output tile
@@ -1076,7 +1043,6 @@ void chunk_fwd_kernel(ChunkArgs a) {
     const int cl = nchunks - 1;
     store_out(cl * CH, min(CH, T - cl * CH));
   }
-  DN_PHASE_FLUSH
 
   // ---- final state and auxiliary state
   float* const fin = xfer ? a.S_final_x : a.S_final;

@@ -131,64 +131,6 @@ DN_EXPORT const char* dn_status_string(int s) {
   }
 }
 
-DN_EXPORT int dn_chunk_fwd(const dn_desc* d, const void* q, const void* k, const void* v,
-                           const dn_gates* g, const float* S0, const float* aux0, void* o,
-                           float* S_final, float* aux_final, void* stream) {
-  int st = check_desc(d, true);
-  if (st != DN_OK) return st;
-  if (d->T > 0) {
-    if ((st = check_gates(d, g)) != DN_OK) return st;
-    if (!q || !k || !v || !o) return DN_ERR_NULL;
-  }
-  if (d->io == DN_F32 && d->dk != 64) return DN_ERR_UNSUPPORTED;
-
-  const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
-  const size_t es = io_size(d->io);
-  const size_t sbytes = static_cast<size_t>(d->B) * d->H * d->dk * d->dv * 4;
-  const size_t abytes = static_cast<size_t>(d->B) * d->H * aux_per_head(d) * 4;
-  const bool has_aux = has_aux_state(d);
-  Range in[16];
-  const dn_gates nog{};
-  int n = gate_ranges(d, g ? g : &nog, in);
-  in[n++] = {q, bht * d->dk * es};
-  in[n++] = {k, bht * d->dk * es};
-  in[n++] = {v, bht * d->dv * es};
-  in[n++] = {S0, S0 ? sbytes : 0};
-  in[n++] = {has_aux ? aux0 : nullptr, abytes};
-  const Range ro{o, bht * d->dv * es}, rs{S_final, S_final ? sbytes : 0},
-      ra{has_aux ? aux_final : nullptr, abytes};
-  for (int i = 0; i < n; ++i) {
-    if (overlap(ro, in[i])) return DN_ERR_ALIAS;
-    // S may be updated in place: each workgroup reads and writes only its own
-    // value columns.  aux may not: every value slice of a head reads aux0.
-    const bool s_in_place = in[i].p == S0 && S_final == S0;
-    if (!s_in_place && overlap(rs, in[i])) return DN_ERR_ALIAS;
-    if (overlap(ra, in[i])) return DN_ERR_ALIAS;
-  }
-  if (overlap(ro, rs) || overlap(ro, ra) || overlap(rs, ra)) return DN_ERR_ALIAS;
-
-  dn::ChunkArgs a;
-  a.B = d->B;
-  a.H = d->H;
-  a.T = d->T;
-  a.dk = d->dk;
-  a.dv = d->dv;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.g = gate_args(d, g ? g : &nog);
-  a.S0 = S0;
-  a.aux0 = has_aux ? aux0 : nullptr;
-  a.o = o;
-  a.S_final = S_final;
-  a.aux_final = has_aux ? aux_final : nullptr;
-  a.xcols = 0;
-  a.S_final_x = nullptr;
-  return hip_status(dn::launch_chunk_fwd(a, d->io == DN_BF16, d->gain,
-                                         d->decay == DN_DECAY_CHANNEL,
-                                         static_cast<hipStream_t>(stream)));
-}
-
 // Workspace of dn_chunk_fwd_long, fp32: A [B, H nseg, dk, dk], then B and S_in
 // [B, H nseg, dk, dv]; for the gains with a statistic (PGDN, KDN) then
 // aux_in [B, H nseg, aph], mu_seg [H nseg] and the piece summaries
@@ -223,25 +165,10 @@ static bool long_shape_ok(const dn_desc* d, int nseg) {
   return nseg >= 1 && d->T % nseg == 0 && (d->T / nseg) % d->C == 0;
 }
 
-DN_EXPORT size_t dn_chunk_fwd_long_workspace(const dn_desc* d, int nseg) {
-  if (check_desc(d, true) != DN_OK || !long_shape_ok(d, nseg)) return 0;
-  return long_layout(d, nseg).total;
-}
-
-DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const void* k,
-                                const void* v, const dn_gates* g, const float* S0,
-                                const float* aux0, void* o, float* S_final, float* aux_final,
-                                void* ws, size_t ws_bytes, void* stream) {
-  int st = check_desc(d, true);
-  if (st != DN_OK) return st;
-  if (d->io != DN_BF16) return DN_ERR_UNSUPPORTED;
-  if (!long_shape_ok(d, nseg)) return DN_ERR_SHAPE;
-  if (static_cast<long long>(d->B) * d->H * nseg > 65535) return DN_ERR_SHAPE;
-  if ((st = check_gates(d, g)) != DN_OK) return st;
-  if (!q || !k || !v || !o) return DN_ERR_NULL;
-  const LongLayout lay = long_layout(d, nseg);
-  if (!ws || ws_bytes < lay.total) return DN_ERR_WORKSPACE;
-
+// Aliasing checks of a segmented run against its workspace range.
+static int check_long_aliases(const dn_desc* d, const dn_gates* g, const void* q, const void* k,
+                              const void* v, const float* S0, const float* aux0, void* o,
+                              float* S_final, float* aux_final, const void* ws, size_t ws_used) {
   const bool has_aux = has_aux_state(d);
   const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
   const size_t sbytes = static_cast<size_t>(d->B) * d->H * d->dk * d->dv * 4;
@@ -254,7 +181,7 @@ DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const
   in[n++] = {S0, S0 ? sbytes : 0};
   in[n++] = {has_aux ? aux0 : nullptr, abytes};
   const Range ro{o, bht * d->dv * 2}, rs{S_final, S_final ? sbytes : 0},
-      ra{has_aux ? aux_final : nullptr, abytes}, rw{ws, lay.total};
+      ra{has_aux ? aux_final : nullptr, abytes}, rw{ws, ws_used};
   for (int i = 0; i < n; ++i) {
     // S_final may be S0 exactly and aux_final aux0 (in-place resume): the
     // combine and chain kernels read and write each element from one thread
@@ -267,7 +194,15 @@ DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const
   if (overlap(ro, rs) || overlap(ro, ra) || overlap(rs, ra) || overlap(ro, rw) ||
       overlap(rs, rw) || overlap(ra, rw))
     return DN_ERR_ALIAS;
+  return DN_OK;
+}
 
+// The segmented forward (already validated): steps (0) to (3) of
+// dn_chunk_fwd_long on `ws`, laid out by long_layout(d, nseg).
+static int run_long(const dn_desc* d, int nseg, const void* q, const void* k, const void* v,
+                    const dn_gates* g, const float* S0, const float* aux0, void* o, float* S_final,
+                    float* aux_final, void* ws, const LongLayout& lay, hipStream_t s) {
+  const bool has_aux = has_aux_state(d);
   // the [B, H, T, d] tensors read as [B, H nseg, T / nseg, d]: segment s of
   // head h is head h nseg + s of the view (and likewise the per-token gates)
   const int Hs = d->H * nseg, Ts = d->T / nseg;
@@ -275,7 +210,6 @@ DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const
   float* wA = reinterpret_cast<float*>(wbase + lay.a);
   float* wB = reinterpret_cast<float*>(wbase + lay.b);
   float* wS = reinterpret_cast<float*>(wbase + lay.s);
-  const hipStream_t s = static_cast<hipStream_t>(stream);
   dn::ChunkArgs a;
   a.B = d->B;
   a.H = Hs;
@@ -344,6 +278,175 @@ DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const
   return hip_status(launch());
 }
 
+// Schedule of dn_chunk_fwd: one pass (nseg = 1), or nseg segments per head
+// run as by dn_chunk_fwd_long when the shape has too few workgroups to fill
+// the device.  A pass of the chunk kernel costs one chunk step per round of
+// CU_COUNT workgroups; by segments, the first launch runs the value and the
+// d_k / 64 transfer slices of every segment, the last one the value slices,
+// each over T / nseg tokens, and the combine chains nseg steps of about 1.2
+// chunk steps each.  The cheapest nseg (a power of two that cuts T into whole
+// chunks) is taken when it saves at least a fifth of the single pass; the
+// extra launches count as a few chunk steps.
+constexpr int CU_COUNT = 256;        // compute units of an MI355X
+constexpr double SEG_LAUNCHES = 6.;  // the segmented schedule's extra launches, in chunk steps
+
+static double rounds(long long wgs) { return static_cast<double>((wgs + CU_COUNT - 1) / CU_COUNT); }
+
+static int auto_nseg(const dn_desc* d) {
+  if (d->io != DN_BF16 || d->T <= 0 || d->T % d->C != 0) return 1;
+  const long long wg = static_cast<long long>(d->B) * d->H * (d->dv / 64);
+  const long long nch = d->T / d->C;
+  const double one = rounds(wg) * static_cast<double>(nch);
+  double best = one;
+  int pick = 1;
+  for (int nseg = 2; nseg <= nch && static_cast<long long>(d->B) * d->H * nseg <= 65535; nseg *= 2) {
+    if (nch % nseg != 0) break;
+    const double cost = (rounds(wg * nseg * (d->dv + d->dk) / d->dv) + rounds(wg * nseg)) *
+                            static_cast<double>(nch / nseg) +
+                        1.2 * nseg + SEG_LAUNCHES;
+    if (cost < best) {
+      best = cost;
+      pick = nseg;
+    }
+  }
+  return best <= 0.8 * one ? pick : 1;
+}
+
+// Workspace of dn_gain_prep: for the gains with a statistic, bf16 io and T a
+// multiple of C (at least two chunks), the chunk-parallel scan's piece summaries
+// [B, H, aph, T / C, 3], the statistic entering every chunk [B, H, T / C, aph]
+// (used when the caller passes no aux_chunk) and PGDN's centre repeated per
+// chunk [H T / C], each on a 256-byte boundary.
+struct PrepLayout {
+  size_t summ, aux_in, mu_seg, total;
+};
+
+// chunks scanned in parallel: whole chunks, at least two; with a statistic
+// only for bf16 io (the summary kernels read bf16 k and gates)
+static bool prep_by_chunks(const dn_desc* d) {
+  return d->T >= 2 * d->C && d->T % d->C == 0 && (!has_aux_state(d) || d->io == DN_BF16);
+}
+static bool prep_parallel(const dn_desc* d) { return has_aux_state(d) && prep_by_chunks(d); }
+
+static PrepLayout prep_layout(const dn_desc* d) {
+  PrepLayout L{};
+  if (!prep_parallel(d)) return L;
+  const size_t nch = d->T / d->C, aph = aux_per_head(d), bh = static_cast<size_t>(d->B) * d->H;
+  L.summ = 0;
+  L.aux_in = round256(bh * aph * nch * 3 * sizeof(float));
+  L.mu_seg = round256(L.aux_in + bh * nch * aph * sizeof(float));
+  L.total = L.mu_seg + static_cast<size_t>(d->H) * nch * sizeof(float);
+  return L;
+}
+
+static size_t chunk_ws_bytes(const dn_desc* d) {
+  const int nseg = auto_nseg(d);
+  return nseg > 1 ? long_layout(d, nseg).total : 0;
+}
+
+DN_EXPORT size_t dn_workspace_bytes(const dn_desc* d) {
+  if (check_desc(d, true) != DN_OK) return 0;
+  const size_t a = chunk_ws_bytes(d), b = prep_layout(d).total;
+  return a > b ? a : b;
+}
+
+DN_EXPORT size_t dn_chunk_fwd_long_workspace(const dn_desc* d, int nseg) {
+  if (check_desc(d, true) != DN_OK || !long_shape_ok(d, nseg)) return 0;
+  return long_layout(d, nseg).total;
+}
+
+DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const void* k,
+                                const void* v, const dn_gates* g, const float* S0,
+                                const float* aux0, void* o, float* S_final, float* aux_final,
+                                void* ws, size_t ws_bytes, void* stream) {
+  int st = check_desc(d, true);
+  if (st != DN_OK) return st;
+  if (d->io != DN_BF16) return DN_ERR_UNSUPPORTED;
+  if (!long_shape_ok(d, nseg)) return DN_ERR_SHAPE;
+  if (static_cast<long long>(d->B) * d->H * nseg > 65535) return DN_ERR_SHAPE;
+  if ((st = check_gates(d, g)) != DN_OK) return st;
+  if (!q || !k || !v || !o) return DN_ERR_NULL;
+  const LongLayout lay = long_layout(d, nseg);
+  if (!ws || ws_bytes < lay.total) return DN_ERR_WORKSPACE;
+  if ((st = check_long_aliases(d, g, q, k, v, S0, aux0, o, S_final, aux_final, ws, lay.total)) !=
+      DN_OK)
+    return st;
+  return run_long(d, nseg, q, k, v, g, S0, aux0, o, S_final, aux_final, ws, lay,
+                  static_cast<hipStream_t>(stream));
+}
+
+DN_EXPORT int dn_chunk_fwd(const dn_desc* d, const void* q, const void* k, const void* v,
+                           const dn_gates* g, const float* S0, const float* aux0, void* o,
+                           float* S_final, float* aux_final, void* ws, size_t ws_bytes,
+                           void* stream) {
+  int st = check_desc(d, true);
+  if (st != DN_OK) return st;
+  if (d->T > 0) {
+    if ((st = check_gates(d, g)) != DN_OK) return st;
+    if (!q || !k || !v || !o) return DN_ERR_NULL;
+  }
+  if (d->io == DN_F32 && d->dk != 64) return DN_ERR_UNSUPPORTED;
+  const size_t need = chunk_ws_bytes(d);
+  if (need > 0 && (!ws || ws_bytes < need)) return DN_ERR_WORKSPACE;
+
+  const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
+  const size_t es = io_size(d->io);
+  const size_t sbytes = static_cast<size_t>(d->B) * d->H * d->dk * d->dv * 4;
+  const size_t abytes = static_cast<size_t>(d->B) * d->H * aux_per_head(d) * 4;
+  const bool has_aux = has_aux_state(d);
+  Range in[16];
+  const dn_gates nog{};
+  int n = gate_ranges(d, g ? g : &nog, in);
+  in[n++] = {q, bht * d->dk * es};
+  in[n++] = {k, bht * d->dk * es};
+  in[n++] = {v, bht * d->dv * es};
+  in[n++] = {S0, S0 ? sbytes : 0};
+  in[n++] = {has_aux ? aux0 : nullptr, abytes};
+  const Range ro{o, bht * d->dv * es}, rs{S_final, S_final ? sbytes : 0},
+      ra{has_aux ? aux_final : nullptr, abytes};
+  for (int i = 0; i < n; ++i) {
+    if (overlap(ro, in[i])) return DN_ERR_ALIAS;
+    // S may be updated in place: each workgroup reads and writes only its own
+    // value columns.  aux may not: every value slice of a head reads aux0.
+    const bool s_in_place = in[i].p == S0 && S_final == S0;
+    if (!s_in_place && overlap(rs, in[i])) return DN_ERR_ALIAS;
+    if (overlap(ra, in[i])) return DN_ERR_ALIAS;
+  }
+  if (overlap(ro, rs) || overlap(ro, ra) || overlap(rs, ra)) return DN_ERR_ALIAS;
+
+  // few heads: the same forward by segments, on the workspace
+  const int nseg = auto_nseg(d);
+  if (nseg > 1) {
+    const LongLayout lay = long_layout(d, nseg);
+    if ((st = check_long_aliases(d, g, q, k, v, S0, aux0, o, S_final, aux_final, ws, lay.total)) !=
+        DN_OK)
+      return st;
+    return run_long(d, nseg, q, k, v, g, S0, aux0, o, S_final, aux_final, ws, lay,
+                    static_cast<hipStream_t>(stream));
+  }
+
+  dn::ChunkArgs a;
+  a.B = d->B;
+  a.H = d->H;
+  a.T = d->T;
+  a.dk = d->dk;
+  a.dv = d->dv;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = gate_args(d, g ? g : &nog);
+  a.S0 = S0;
+  a.aux0 = has_aux ? aux0 : nullptr;
+  a.o = o;
+  a.S_final = S_final;
+  a.aux_final = has_aux ? aux_final : nullptr;
+  a.xcols = 0;
+  a.S_final_x = nullptr;
+  return hip_status(dn::launch_chunk_fwd(a, d->io == DN_BF16, d->gain,
+                                         d->decay == DN_DECAY_CHANNEL,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 DN_EXPORT int dn_decode_step(const dn_desc* d, const void* q, const void* k, const void* v,
                              const dn_gates* g, float* S, float* aux, void* o, void* stream) {
   int st = check_desc(d, false);
@@ -394,12 +497,14 @@ DN_EXPORT int dn_decode_step(const dn_desc* d, const void* q, const void* k, con
 }
 
 DN_EXPORT int dn_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, const float* aux0,
-                           float* w_out, float* g_out, float* aux_chunk, float* aux_final,
-                           void* stream) {
+                           float* w_out, float* g_out, float* aux_chunk, float* aux_final, void* ws,
+                           size_t ws_bytes, void* stream) {
   int st = check_desc(d, true);
   if (st != DN_OK) return st;
   if ((st = check_gates(d, g)) != DN_OK) return st;
   if (!k || !w_out) return DN_ERR_NULL;
+  const PrepLayout lay = prep_layout(d);
+  if (lay.total > 0 && (!ws || ws_bytes < lay.total)) return DN_ERR_WORKSPACE;
   const bool has_aux = has_aux_state(d);
   const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
   const size_t es = io_size(d->io);
@@ -409,16 +514,18 @@ DN_EXPORT int dn_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, c
   int n = gate_ranges(d, g, in);
   in[n++] = {k, bht * d->dk * es};
   in[n++] = {has_aux ? aux0 : nullptr, static_cast<size_t>(d->B) * d->H * aph * 4};
-  Range outs[4] = {{w_out, bht * d->dk * 4},
+  Range outs[5] = {{w_out, bht * d->dk * 4},
                    {g_out, g_out ? bht * (d->decay == DN_DECAY_CHANNEL ? d->dk : 1) * 4 : 0},
                    {has_aux ? aux_chunk : nullptr, static_cast<size_t>(d->B) * d->H * nch * aph * 4},
-                   {has_aux ? aux_final : nullptr, static_cast<size_t>(d->B) * d->H * aph * 4}};
-  for (int j = 0; j < 4; ++j) {
+                   {has_aux ? aux_final : nullptr, static_cast<size_t>(d->B) * d->H * aph * 4},
+                   {lay.total > 0 ? ws : nullptr, lay.total}};
+  for (int j = 0; j < 5; ++j) {
     for (int i = 0; i < n; ++i)
       if (overlap(outs[j], in[i])) return DN_ERR_ALIAS;
-    for (int i = j + 1; i < 4; ++i)
+    for (int i = j + 1; i < 5; ++i)
       if (overlap(outs[j], outs[i])) return DN_ERR_ALIAS;
   }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   dn::GainPrepArgs a;
   a.B = d->B;
   a.H = d->H;
@@ -431,7 +538,40 @@ DN_EXPORT int dn_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, c
   a.g_out = g_out;
   a.aux_chunk = has_aux ? aux_chunk : nullptr;
   a.aux_final = has_aux ? aux_final : nullptr;
+  // Whole chunks: every chunk is scanned by its own workgroup, as a head of
+  // the [B, H nch, C] view of the [B, H, T] tensors.  The gains with a
+  // statistic first get the statistic entering every chunk from the
+  // composed per-token maps of the chunks (the associative gain scan of
+  // Kalman Delta Networks §2.6; the chunked statistic recursion of
+  // Preconditioned DeltaNet §2.6), written where aux_chunk goes.
+  if (prep_by_chunks(d)) {
+    if (has_aux) {
+      char* wbase = static_cast<char*>(ws);
+      dn::StatArgs sa;
+      sa.B = d->B;
+      sa.H = d->H;
+      sa.T = d->T;
+      sa.dk = d->dk;
+      sa.nseg = static_cast<int>(nch);
+      sa.lsub = d->C;
+      sa.gain = d->gain;
+      sa.channel = d->decay == DN_DECAY_CHANNEL;
+      sa.k = k;
+      sa.g = a.g;
+      sa.aux0 = aux0;
+      sa.summ = reinterpret_cast<float*>(wbase + lay.summ);
+      sa.aux_in = aux_chunk ? aux_chunk : reinterpret_cast<float*>(wbase + lay.aux_in);
+      sa.aux_final = aux_final;
+      sa.mu_seg = reinterpret_cast<float*>(wbase + lay.mu_seg);
+      if (dn::launch_segment_stats(sa, s) != hipSuccess) return DN_ERR_HIP;
+      a.aux0 = sa.aux_in;
+      if (d->gain == DN_GAIN_PGDN) a.g.mu_log = sa.mu_seg;
+    }
+    a.H = static_cast<int>(d->H * nch);
+    a.T = d->C;
+    a.aux_chunk = nullptr;
+    a.aux_final = nullptr;
+  }
   return hip_status(dn::launch_gain_prep(a, d->io == DN_BF16, d->gain,
-                                         d->decay == DN_DECAY_CHANNEL,
-                                         static_cast<hipStream_t>(stream)));
+                                         d->decay == DN_DECAY_CHANNEL, s));
 }

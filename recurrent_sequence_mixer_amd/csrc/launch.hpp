@@ -40,16 +40,16 @@ struct DecodeArgs {
 
 struct ChunkArgs {
   int B, H, T, dk, dv;
-  const void *q, *k, *v;  // v nullable (bf16 scalar-decay kernel only): v = 0
+  const void *q, *k, *v;  // required (transfer slices read no v)
   GateArgs g;
   const float* S0;    // nullable
   const float* aux0;  // nullable
-  void* o;            // nullable (bf16 scalar-decay kernel only): no output
+  void* o;            // nullable: no output
   float* S_final;    // nullable
   float* aux_final;  // nullable
-  // bf16 scalar-decay kernel only: xcols (0 or dk) more value slices that run
-  // from S0 = I with v = 0 and no output, their final state going to
-  // S_final_x [B, H, dk, xcols] (the transfer matrices of segments)
+  // xcols (0 or dk) more value slices that run from S0 = I with v = 0 and no
+  // output, their final state going to S_final_x [B, H, dk, xcols] (the
+  // transfer matrices of segments)
   int xcols;
   float* S_final_x;
 };
@@ -100,7 +100,7 @@ struct GainPrepArgs {
 hipError_t launch_decode(const DecodeArgs& a, int io_bf16, int gain, bool channel, hipStream_t st);
 hipError_t launch_chunk_fwd(const ChunkArgs& a, int io_bf16, int gain, bool channel,
                             hipStream_t st);
-// bf16 io, scalar decay, gains KLA / GDN / PGDN / explicit (chunk_fwd_bf16.hip)
+// bf16 io, scalar decay, gains KLA / GDN / PGDN / explicit (chunk_fwd_ws.hip)
 hipError_t launch_chunk_fwd_bf16_scalar(const ChunkArgs& a, int gain, hipStream_t st);
 // bf16 io, diagonal or isotropic KDN with per-channel decay (chunk_fwd_ws.hip)
 hipError_t launch_chunk_fwd_bf16_kdn(const ChunkArgs& a, int gain, hipStream_t st);

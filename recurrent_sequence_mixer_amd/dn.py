@@ -23,7 +23,7 @@ IO = {torch.float32: 0, torch.bfloat16: 1}
 
 # Symbols declared in include/dn.h.
 EXPORTS = ("dn_chunk_fwd", "dn_chunk_fwd_long", "dn_chunk_fwd_long_workspace", "dn_decode_step",
-           "dn_gain_prep", "dn_status_string", "dn_version")
+           "dn_gain_prep", "dn_status_string", "dn_version", "dn_workspace_bytes")
 
 
 class DnDesc(ctypes.Structure):
@@ -56,8 +56,10 @@ def lib() -> ctypes.CDLL:
                                "`python -m recurrent_sequence_mixer_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         vp, ip = ctypes.c_void_p, ctypes.c_int
+        L.dn_workspace_bytes.argtypes = [ctypes.POINTER(DnDesc)]
+        L.dn_workspace_bytes.restype = ctypes.c_size_t
         L.dn_chunk_fwd.argtypes = [ctypes.POINTER(DnDesc), vp, vp, vp, ctypes.POINTER(DnGates),
-                                   vp, vp, vp, vp, vp, vp]
+                                   vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.dn_chunk_fwd.restype = ip
         L.dn_chunk_fwd_long.argtypes = [ctypes.POINTER(DnDesc), ip, vp, vp, vp, ctypes.POINTER(DnGates),
                                         vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -68,7 +70,7 @@ def lib() -> ctypes.CDLL:
                                      vp, vp, vp, vp]
         L.dn_decode_step.restype = ip
         L.dn_gain_prep.argtypes = [ctypes.POINTER(DnDesc), vp, ctypes.POINTER(DnGates), vp,
-                                   vp, vp, vp, vp, vp]
+                                   vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.dn_gain_prep.restype = ip
         L.dn_status_string.argtypes = [ip]
         L.dn_status_string.restype = ctypes.c_char_p
@@ -113,14 +115,34 @@ def _check(status: int, what: str):
         raise DnError(status, what)
 
 
+def workspace_bytes(desc: DnDesc) -> int:
+    """dn_workspace_bytes: device workspace a chunked forward or gain scan of
+    this shape needs (0: none)."""
+    return lib().dn_workspace_bytes(ctypes.byref(desc))
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    """(pointer, size) of the caller's workspace tensor, or of a fresh one."""
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace of {workspace.numel() * workspace.element_size()} bytes, "
+                         f"{nbytes} needed")
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
 def chunk_fwd(q, k, v, gates: Dict[str, torch.Tensor], *, gain="kla", decay=None, eps=1e-6,
               x=1.5, mu_info=1.0, S0=None, aux0=None, out=None, S_final=None, aux_final=None,
-              want_state=True, stream=None):
+              want_state=True, workspace=None, stream=None):
     """Chunked forward: returns (o, S_final, aux_final).
 
     q, k [B, H, T, dk], v [B, H, T, dv] (fp32 or bf16, same dtype); gates as
     in include/dn.h.  Output buffers may be passed in (S_final may be S0 for
-    an in-place resume).
+    an in-place resume).  `workspace`: a device tensor of at least
+    workspace_bytes(desc) bytes, allocated here with torch when not given
+    and the shape needs one.
     """
     B, H, T, dk = k.shape
     dv = v.shape[-1]
@@ -134,10 +156,11 @@ def chunk_fwd(q, k, v, gates: Dict[str, torch.Tensor], *, gain="kla", decay=None
     if has_aux and want_state and aux_final is None:
         aux_final = torch.empty((B, H) if gain == "kdn_iso" else (B, H, dk), dtype=torch.float32,
                                 device=v.device)
+    ws, nbytes = _workspace(workspace_bytes(desc), v.device, workspace)
     gt = make_gates(gates)
     st = lib().dn_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(gt),
                             _ptr(S0), _ptr(aux0), _ptr(o), _ptr(S_final), _ptr(aux_final),
-                            _stream(stream))
+                            ws, nbytes, _stream(stream))
     _check(st, "dn_chunk_fwd")
     return o, S_final, aux_final
 
@@ -191,7 +214,7 @@ def decode_step(q, k, v, gates: Dict[str, torch.Tensor], S, aux=None, *, gain="k
 
 
 def gain_prep(k, gates: Dict[str, torch.Tensor], *, gain="kla", decay=None, eps=1e-6, x=1.5,
-              mu_info=1.0, aux0=None, C=64, stream=None):
+              mu_info=1.0, aux0=None, C=64, workspace=None, stream=None):
     """Write-gain scans: returns (w, g, aux_chunk, aux_final)."""
     B, H, T, dk = k.shape
     if decay is None:
@@ -206,9 +229,11 @@ def gain_prep(k, gates: Dict[str, torch.Tensor], *, gain="kla", decay=None, eps=
     per = () if gain == "kdn_iso" else (dk,)
     aux_chunk = torch.empty((B, H, nch) + per, dtype=torch.float32, device=dev) if has_aux else None
     aux_final = torch.empty((B, H) + per, dtype=torch.float32, device=dev) if has_aux else None
+    ws, nbytes = _workspace(workspace_bytes(desc), dev, workspace)
     gt = make_gates(gates)
     st = lib().dn_gain_prep(ctypes.byref(desc), _ptr(k), ctypes.byref(gt), _ptr(aux0), _ptr(w),
-                            _ptr(g), _ptr(aux_chunk), _ptr(aux_final), _stream(stream))
+                            _ptr(g), _ptr(aux_chunk), _ptr(aux_final), ws, nbytes,
+                            _stream(stream))
     _check(st, "dn_gain_prep")
     return w, g, aux_chunk, aux_final
 

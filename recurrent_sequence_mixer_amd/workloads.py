@@ -49,7 +49,10 @@ class Workload:
     C: int = 64
     eps: float = 1e-6  # KLA stabiliser
     x: float = 1.5  # PGDN bound of the write scale, B in [1/x, x]
-    mu_log: float = math.log(4.0)  # PGDN per-head log-centre (same for all heads)
+    mu_log: float = math.log(4.0)  # PGDN per-head log-centre
+    # PGDN: head h gets mu_log + mu_spread (2 h / (H - 1) - 1), so that the
+    # per-head indexing of the centre is exercised (0: the same for all heads)
+    mu_spread: float = 0.0
     mu_info: float = 1.0  # KDN information scaling (1 = strict reverse-KL update)
     keys: str = "scaled"  # "scaled": N(0,1) rows times U[0.25, 4]; "unit": L2-normalised
     s0: str = "normal"  # "zero" or "normal" (N(0, 0.01), i.e. std 0.1)
@@ -163,7 +166,8 @@ def generate(wl: Workload) -> Dict[str, np.ndarray]:
     if wl.gain == "pgdn":
         out["alphaP"] = round_f32(_sigmoid(rng.normal(2.0, 1.0, size=shp)))
         out["betaP"] = round_f32(_sigmoid(rng.normal(2.0, 1.0, size=shp)))
-        out["mu_log"] = round_f32(np.full((H,), wl.mu_log))
+        spread = np.linspace(-1.0, 1.0, H) if H > 1 else np.zeros(1)
+        out["mu_log"] = round_f32(wl.mu_log + wl.mu_spread * spread)
     if wl.gain == "kdn":
         out["omega"] = round_io(_softplus(rng.normal(-3.0, 1.0, size=shp + (dk,))), wl.io)
         out["r"] = round_f32(_softplus(rng.standard_normal(shp)))

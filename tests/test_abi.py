@@ -57,10 +57,11 @@ def _gates(**kw):
 
 
 def _chunk(desc, gates=None, q=FAKE + (2 << 30), k=FAKE + (3 << 30), v=FAKE + (4 << 30),
-           o=FAKE + (5 << 30), S0=None, aux0=None, S_final=None, aux_final=None):
+           o=FAKE + (5 << 30), S0=None, aux0=None, S_final=None, aux_final=None, ws=None,
+           nbytes=0):
     gates = gates or _gates()
     return dn.lib().dn_chunk_fwd(ctypes.byref(desc), q, k, v, ctypes.byref(gates), S0, aux0, o,
-                                 S_final, aux_final, None)
+                                 S_final, aux_final, ws, nbytes, None)
 
 
 def _desc(**kw):
@@ -96,7 +97,7 @@ def test_chunk_fwd_rejects_missing_pointers():
     assert _chunk(_desc(gain="kdn_iso")) == -1  # omega, r missing
     assert _chunk(_desc(gain="explicit")) == -1  # w missing
     assert dn.lib().dn_chunk_fwd(None, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None,
-                                 None) == -1
+                                 None, 0, None) == -1
 
 
 def test_chunk_fwd_rejects_overlaps():
@@ -129,13 +130,60 @@ def test_gain_prep_rejects_bad_arguments():
     L = dn.lib()
     g = _gates()
     d = _desc()
-    assert L.dn_gain_prep(ctypes.byref(d), FAKE, ctypes.byref(g), None, None, None, None, None,
-                          None) == -1
-    assert L.dn_gain_prep(ctypes.byref(_desc(dk=80)), FAKE, ctypes.byref(g), None, FAKE + (7 << 30),
-                          None, None, None, None) == -2
+    gp = lambda desc, k, w, ws=None, nbytes=0, gates=g: L.dn_gain_prep(
+        ctypes.byref(desc), k, ctypes.byref(gates), None, w, None, None, None, ws, nbytes, None)
+    assert gp(d, FAKE, None) == -1
+    assert gp(_desc(dk=80), FAKE, FAKE + (7 << 30)) == -2
     # w_out overlapping k
-    assert L.dn_gain_prep(ctypes.byref(d), FAKE + (3 << 30), ctypes.byref(g), None, FAKE + (3 << 30),
-                          None, None, None, None) == -8
+    assert gp(d, FAKE + (3 << 30), FAKE + (3 << 30)) == -8
+    # PGDN over whole chunks scans them in parallel and needs its workspace
+    dp = _desc(B=2, H=3, T=1024, gain="pgdn")
+    gpg = _gates(alphaP=FAKE + (6 << 30), betaP=FAKE + (7 << 30), mu_log=FAKE + (8 << 30))
+    need = L.dn_workspace_bytes(ctypes.byref(dp))
+    assert need > 0
+    assert gp(dp, FAKE + (3 << 30), FAKE + (12 << 30), gates=gpg) == -5
+    assert gp(dp, FAKE + (3 << 30), FAKE + (12 << 30), FAKE + (20 << 30), need - 1, gates=gpg) == -5
+    # workspace overlapping w_out
+    assert gp(dp, FAKE + (3 << 30), FAKE + (12 << 30), FAKE + (12 << 30) + 64, need, gates=gpg) == -8
+
+
+def test_workspace_bytes_layouts():
+    """dn_workspace_bytes follows the layouts the header states."""
+    L = dn.lib()
+    ws = lambda **kw: L.dn_workspace_bytes(ctypes.byref(_desc(**kw)))
+    # many heads: one pass, nothing; gains without a statistic scan by chunks with none
+    assert ws(B=8, H=16, T=4096) == 0
+    assert ws(B=2, H=3, T=1024) == 0  # few heads but a short sequence: one pass is cheaper
+    assert ws(B=8, H=16, T=4096, io=0, dk=64, dv=64, gain="pgdn") == 0  # fp32: serial scan
+    assert ws(B=8, H=16, T=100, gain="pgdn") == 0  # not whole chunks: serial scan
+    # the chunk-parallel gain scan: summaries [B, H, dk, T / C, 3], the
+    # statistic entering every chunk [B, H, T / C, dk] and PGDN's centre per
+    # chunk [H T / C], each on a 256-byte boundary
+    summ, aux_in, mu = 6 * 128 * 16 * 3 * 4, 6 * 16 * 128 * 4, 3 * 16 * 4
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert ws(B=2, H=3, T=1024, gain="pgdn") == r256(r256(summ) + aux_in) + mu
+    assert ws(B=2, H=3, T=1024, gain="kdn_iso", decay="channel") == r256(r256(6 * 16 * 3 * 4) + 6 * 16 * 4) + mu
+    # a batch-1 long prefill: 16 segments of 8192 tokens, dn_chunk_fwd_long's layout
+    d = _desc(B=1, H=8, T=131072)
+    assert ws(B=1, H=8, T=131072) == L.dn_chunk_fwd_long_workspace(ctypes.byref(d), 16) == \
+        128 * 128 * (128 + 2 * 128) * 4
+    dp = _desc(B=1, H=8, T=32768, gain="pgdn")
+    long16 = L.dn_chunk_fwd_long_workspace(ctypes.byref(dp), 16)
+    prep = r256(r256(8 * 128 * 512 * 3 * 4) + 8 * 512 * 128 * 4) + 8 * 512 * 4
+    assert ws(B=1, H=8, T=32768, gain="pgdn") == max(long16, prep)
+    assert ws(B=0, H=8, T=32768) == 0  # invalid descriptor
+
+
+def test_chunk_fwd_rejects_missing_workspace():
+    """A shape that runs by segments needs its workspace (DN_ERR_WORKSPACE),
+    which may not overlap another buffer (DN_ERR_ALIAS)."""
+    L = dn.lib()
+    d = _desc(B=1, H=8, T=131072)
+    need = L.dn_workspace_bytes(ctypes.byref(d))
+    assert _chunk(d) == -5
+    assert _chunk(d, ws=FAKE + (20 << 30), nbytes=need - 256) == -5
+    assert _chunk(d, ws=FAKE + (5 << 30), nbytes=need) == -8  # the output's range
+    assert _chunk(d, ws=FAKE + (2 << 30) + 4096, nbytes=need) == -8  # inside q
 
 
 def test_chunk_fwd_long_rejects_bad_arguments():

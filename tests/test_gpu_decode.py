@@ -75,27 +75,60 @@ def test_decode_gains(gain, decay, io, dk, dv):
 
 
 def test_decode_full_size_sampled():
-    """Workload 4 at its full size (512 sequences x 16 heads), 8 steps, sampled heads."""
+    """Workload 4 at its full size (512 sequences x 16 heads) over all 256
+    steps, every step on the whole batch; sampled heads against the oracle,
+    o over all 256 steps and the final state."""
     dn = _dn()
     wl = W.WORKLOADS[4]
     S0 = W.generate_decode_state(wl)
     S = torch.from_numpy(S0).cuda()
-    steps = [W.generate_decode_step(wl, s) for s in range(8)]
-    outs = []
-    for st in steps:
-        t = dn.to_device(st, torch.bfloat16)
-        outs.append(dn.decode_step(t["q"], t["k"], t["v"], {"alpha": t["alpha"], "eta": t["eta"]}, S,
-                                   gain="kla", eps=wl.eps))
-    torch.cuda.synchronize()
     heads = [0, 4097, 8191]
     sel = lambda a: a.reshape((wl.N * wl.H,) + a.shape[2:])[heads]
-    stack = lambda name: np.stack([sel(st[name]) for st in steps], axis=1)
+    picked = {n: [] for n in ("q", "k", "v", "eta", "alpha")}
+    outs = []
+    for s in range(wl.steps):
+        st = W.generate_decode_step(wl, s)
+        for n in picked:
+            picked[n].append(sel(st[n]))
+        t = dn.to_device(st, torch.bfloat16)
+        o = dn.decode_step(t["q"], t["k"], t["v"], {"alpha": t["alpha"], "eta": t["eta"]}, S,
+                           gain="kla", eps=wl.eps)
+        outs.append(o.reshape(wl.N * wl.H, wl.dv)[heads].float())
+        if s % 64 == 63:
+            print(f"decode full size: {s + 1} of {wl.steps} steps", flush=True)
+    torch.cuda.synchronize()
+    stack = lambda name: np.stack(picked[name], axis=1)
     o_ref, S_ref, _, _ = forward(stack("q"), stack("k"), stack("v"), "kla", stack("alpha"),
                                  eta=stack("eta"), eps=wl.eps, S0=sel(S0))
-    o = np.stack([sel(x.float().cpu().numpy()) for x in outs], axis=1)
+    o = torch.stack(outs, dim=1).cpu().numpy()
     eo, es = max_rel_err(o, o_ref), max_rel_err(sel(S.cpu().numpy()), S_ref)
-    print(f"decode full size: o {eo:.2e} S {es:.2e}")
+    print(f"decode full size, {wl.steps} steps: o {eo:.2e} S {es:.2e}")
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("decay", ["scalar", "channel"])
+def test_decode_pgdn_distinct_centre_per_head(decay):
+    """PGDN decode with a different centre mu_h per head (N = 4, H = 3)."""
+    dn = _dn()
+    wl = W.Workload("dec_pgdn_mu", "pgdn", decay, "bf16", 4, 3, 10, 128, 128, keys="unit",
+                    mu_spread=1.5, seed=540)
+    inp = W.generate(wl)
+    t = dn.to_device(inp, torch.bfloat16)
+    S = t["S0"].clone()
+    aux = torch.ones((4, 3, 128), device="cuda")
+    outs = []
+    for s in range(wl.T):
+        gates = {n: t[n][:, :, s].contiguous() for n in ("alpha", "eta", "alphaP", "betaP")}
+        gates["mu_log"] = t["mu_log"]
+        outs.append(dn.decode_step(t["q"][:, :, s].contiguous(), t["k"][:, :, s].contiguous(),
+                                   t["v"][:, :, s].contiguous(), gates, S, aux, gain="pgdn", x=wl.x))
+    torch.cuda.synchronize()
+    o = torch.stack(outs, dim=2).float().cpu().numpy()
+    o_ref, S_ref, aux_ref, _ = run_workload(wl, inp)
+    eo, es = max_rel_err(flat_heads(o), o_ref), max_rel_err(flat_heads(S.cpu().numpy()), S_ref)
+    ea = max_rel_err(flat_heads(aux.cpu().numpy()), aux_ref)
+    print(f"decode pgdn per-head mu ({decay}): o {eo:.2e} S {es:.2e} aux {ea:.2e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"] and ea <= 1e-5
 
 
 def test_prefill_then_decode_equals_one_pass():
@@ -158,24 +191,34 @@ def test_kdn_iso_prefill_decode_and_resume(decay):
     assert eo <= TOL["bf16"] and es <= TOL["bf16"] and eb <= 1e-3
 
 
+@pytest.mark.parametrize("T", [150, 320])
 @pytest.mark.parametrize("gain,decay,io", [("kla", "scalar", "bf16"), ("pgdn", "scalar", "bf16"),
                                            ("kdn", "channel", "bf16"), ("kdn", "channel", "f32"),
                                            ("gdn", "channel", "f32"), ("kdn_iso", "channel", "bf16"),
-                                           ("kdn_iso", "scalar", "f32")])
-def test_gain_prep_per_token(gain, decay, io):
+                                           ("kdn_iso", "scalar", "f32"), ("kdn", "scalar", "bf16"),
+                                           ("pgdn", "channel", "bf16"), ("kdn_iso", "scalar", "bf16")])
+def test_gain_prep_per_token(gain, decay, io, T):
     """dn_gain_prep's per-token write vectors, chunk-start aux and in-chunk
-    cumulative log-decay against the oracle's trace."""
+    cumulative log-decay against the oracle's trace.  T = 320 (whole chunks)
+    scans every chunk in parallel (for the gains with a statistic from the
+    chunk summaries and carry, bf16), T = 150 one head at a time; a
+    non-default aux0 and, for PGDN, a different centre per head."""
     dn = _dn()
     keys = "unit" if gain in ("gdn", "pgdn") else "scaled"
-    wl = W.Workload("gp", gain, decay, io, 2, 3, 150, 128 if io == "bf16" else 64,
-                    128 if io == "bf16" else 64, keys=keys, seed=31)
+    wl = W.Workload("gp", gain, decay, io, 2, 3, T, 128 if io == "bf16" else 64,
+                    128 if io == "bf16" else 64, keys=keys, mu_spread=1.0, seed=31)
     inp = W.generate(wl)
+    rng = np.random.default_rng(32)
+    if gain in ("pgdn", "kdn", "kdn_iso"):
+        shape = (2, 3) if gain == "kdn_iso" else (2, 3, wl.dk)
+        inp["aux0"] = rng.uniform(0.5, 2.0, size=shape).astype(np.float32)
     t = dn.to_device(inp, torch.float32 if io == "f32" else torch.bfloat16)
     gates = {n: t[n] for n in ("alpha", "eta", "alphaP", "betaP", "mu_log", "omega", "r") if n in t}
     w, g, aux_chunk, aux_final = dn.gain_prep(t["k"], gates, gain=gain, eps=wl.eps, x=wl.x,
-                                              mu_info=wl.mu_info)
+                                              mu_info=wl.mu_info, aux0=t.get("aux0"))
     torch.cuda.synchronize()
-    _, _, aux_ref, tr = run_workload(wl, inp, record=True)
+    _, _, aux_ref, tr = run_workload(wl, inp, record=True, aux0=None if "aux0" not in inp
+                                     else flat_heads(inp["aux0"]))
     ew = max_rel_err(flat_heads(w.cpu().numpy()), tr["w"])
     print(f"gain_prep {gain}: w {ew:.2e}")
     assert ew <= 1e-5
@@ -189,5 +232,6 @@ def test_gain_prep_per_token(gain, decay, io):
         assert max_rel_err(flat_heads(aux_final.cpu().numpy()), aux_ref) <= 1e-5
         key = "A" if gain == "pgdn" else "p"
         ac = flat_heads(aux_chunk.cpu().numpy())
+        np.testing.assert_array_equal(ac[:, 0], flat_heads(inp["aux0"]))
         for ci, c0 in enumerate(range(64, T, 64)):
             assert max_rel_err(ac[:, ci + 1], tr[key][:, c0 - 1]) <= 1e-5

@@ -130,12 +130,17 @@ def test_kdn_iso_full_size_sampled_heads():
     _check(wl, inp, heads, o, S, aux)
 
 
-def test_long_prefill_batch1_sampled_head():
-    """Batch-1 long prefill (B1 H8 T131072 d128, KLA bf16; the pages' long-context
-    prefill length): one launch walks 2048 chunks per head; one head is
+@pytest.mark.parametrize("T", [131072, 131071])
+def test_long_prefill_batch1_sampled_head(T):
+    """Batch-1 long prefill (B1 H8 d128, KLA bf16; the pages' long-context
+    prefill length) through dn_chunk_fwd: at T = 131072 the call picks 16
+    segments per head on its workspace; T = 131071 is not whole chunks, so
+    one launch walks 2048 chunks per head and a ragged tail.  One head is
     compared in full with the oracle."""
-    wl = W.Workload("kla_long_B1H8T131072d128", "kla", "scalar", "bf16", 1, 8, 131072, 128, 128,
-                    seed=51)
+    from recurrent_sequence_mixer_amd import dn
+    wl = W.Workload("kla_long_B1H8d128", "kla", "scalar", "bf16", 1, 8, T, 128, 128, seed=51)
+    desc = dn.make_desc(1, 8, T, 128, 128, torch.bfloat16, "kla")
+    assert (dn.workspace_bytes(desc) > 0) == (T % 64 == 0)
     inp = W.generate(wl)
     o, S, _ = gpu_chunk(wl, inp)
     _check(wl, inp, [5], o, S)
@@ -325,6 +330,54 @@ def test_chunk_fwd_long_pgdn_full_size_sampled_head():
     inp = W.generate(wl)
     o, S, aux = gpu_chunk_long(wl, inp, 16, in_place=False)
     _check(wl, inp, [3], o, S, aux)
+
+
+@pytest.mark.parametrize("decay,dk,T", [("scalar", 128, 333), ("scalar", 64, 200), ("channel", 128, 150)])
+def test_pgdn_distinct_centre_per_head(decay, dk, T):
+    """PGDN with a different centre mu_h for every head (Preconditioned
+    DeltaNet §2.4: mu is per head): B2 H3, so heads of both batch rows use
+    their own entry of mu_log.  Scalar decay runs the producer / consumer
+    kernel, channel decay (PKDA) the generic one."""
+    wl = W.Workload("pgdn_mu_heads", "pgdn", decay, "bf16", 2, 3, T, dk, dk, keys="unit",
+                    mu_spread=1.5, seed=500 + T)
+    inp = W.generate(wl)
+    assert len(set(inp["mu_log"].tolist())) == 3
+    o, S, aux = gpu_chunk(wl, inp)
+    _check(wl, inp, None, o, S, aux)
+
+
+@pytest.mark.parametrize("decay,nseg", [("scalar", 4), ("channel", 2)])
+def test_chunk_fwd_long_pgdn_distinct_centre_per_head(decay, nseg):
+    """dn_chunk_fwd_long, PGDN with a different mu_h per head (B2 H3): the
+    centre is repeated into the [H nseg] segment view, head by head."""
+    wl = W.Workload("pgdn_long_mu_heads", "pgdn", decay, "bf16", 2, 3, 1024, 128, 128, keys="unit",
+                    mu_spread=1.5, seed=520 + nseg)
+    inp = W.generate(wl)
+    rng = np.random.default_rng(wl.seed)
+    inp["aux0"] = rng.uniform(0.5, 2.0, size=(2, 3, 128)).astype(np.float32)
+    o, S, aux = gpu_chunk_long(wl, inp, nseg)
+    _check(wl, inp, None, o, S, aux)
+
+
+def test_kla_zero_key_rows():
+    """KLA with some all-zero keys (Kaczmarz Linear Attention §2.4: with
+    eps > 0 a zero key writes nothing): the column scale eta / eps (about
+    1e6) multiplies a zero key in the chunk kernel; o and S must still match."""
+    wl = W.Workload("kla_zero_keys", "kla", "scalar", "bf16", 2, 2, 200, 128, 128, seed=530)
+    inp = W.generate(wl)
+    rng = np.random.default_rng(531)
+    zero = rng.random((2, 2, 200)) < 0.15
+    zero[:, :, 63] = zero[:, :, 64] = zero[:, :, 0] = True  # chunk edges and the first token
+    inp["k"][zero] = 0.0
+    o, S, _ = gpu_chunk(wl, inp)
+    _check(wl, inp, None, o, S)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    # f32 io (the generic kernel) as well
+    wl = wl.replace(io="f32", dk=64, dv=64)
+    inp = W.generate(wl)
+    inp["k"][zero] = 0.0
+    o, S, _ = gpu_chunk(wl, inp)
+    _check(wl, inp, None, o, S)
 
 
 def test_kdn_mu_dk_and_kla_key_norm_only():

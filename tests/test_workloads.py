@@ -48,3 +48,17 @@ def test_decode_steps_independent_streams():
     s2 = W.generate_decode_step(small, 2)
     assert W.sha256(s1) == W.sha256(s1b) and W.sha256(s1) != W.sha256(s2)
     assert wl.N == 512 and wl.steps == 256
+
+
+def test_pgdn_centre_spread_per_head():
+    """mu_spread gives every head its own PGDN centre, symmetric about mu_log;
+    without it all heads share mu_log (the draws are unchanged either way)."""
+    base = W.WORKLOADS[2].replace(B=1, H=4, T=8)
+    a = W.generate(base)
+    b = W.generate(base.replace(mu_spread=0.75))
+    np.testing.assert_array_equal(a["mu_log"], np.float32(np.log(4.0)))
+    assert len(set(b["mu_log"].tolist())) == 4
+    np.testing.assert_allclose(b["mu_log"].mean(), np.log(4.0), rtol=1e-6)
+    np.testing.assert_allclose(b["mu_log"].max() - b["mu_log"].min(), 1.5, rtol=1e-6)
+    for name in ("q", "k", "v", "eta", "alpha", "alphaP", "betaP", "S0"):
+        np.testing.assert_array_equal(a[name], b[name])
