@@ -178,6 +178,24 @@ int dn_chunk_fwd(const dn_desc* desc, const void* q, const void* k, const void* 
                  const dn_gates* gates, const float* S0, const float* aux0, void* o,
                  float* S_final, float* aux_final, void* ws, size_t ws_bytes, void* stream);
 
+/* dn_chunk_fwd for callers that cannot allocate device memory (code under
+ * stream capture into a graph, tight serving loops, harnesses that forbid
+ * allocation): the same computation, with the workspace taken from a
+ * device array inside the library instead of an argument.
+ *   The array holds DN_NOALLOC_SCRATCH_BYTES (48 MiB) on every device the
+ *   library runs on, from the first call on that device until the process
+ *   ends.  A descriptor whose dn_workspace_bytes exceeds it returns
+ *   DN_ERR_WORKSPACE before anything is launched.  The call itself allocates
+ *   nothing (no hipMalloc, no allocating library routine).
+ *   Every call on one device shares that device's array: calls that overlap
+ *   in time on one device (other streams, other host threads) race on it and
+ *   must be serialised by the caller.  Nothing is kept between calls.
+ * Arguments, errors and results as for dn_chunk_fwd. */
+#define DN_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+int dn_chunk_fwd_noalloc(const dn_desc* desc, const void* q, const void* k, const void* v,
+                         const dn_gates* gates, const float* S0, const float* aux0, void* o,
+                         float* S_final, float* aux_final, void* stream);
+
 /* Chunked forward of long sequences by segments, for shapes with few heads
  * (e.g. batch-1 prefill): each head's T tokens are cut into nseg segments
  * of T / nseg tokens, which run in parallel.  Over a segment the recurrence

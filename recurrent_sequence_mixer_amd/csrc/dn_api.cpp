@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "dn.h"
 #include "launch.hpp"
@@ -574,4 +575,46 @@ DN_EXPORT int dn_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, c
   }
   return hip_status(dn::launch_gain_prep(a, d->io == DN_BF16, d->gain,
                                          d->decay == DN_DECAY_CHANNEL, s));
+}
+
+// ---------------------------------------------------------------------------
+// dn_chunk_fwd_noalloc: dn_chunk_fwd with the workspace in a file-scope
+// device array, for callers that cannot allocate.  Every device the library
+// runs on holds its own copy of the array until the process ends.  The host
+// name `scratch` is not a device address: its device address is looked up
+// once per device (hipGetSymbolAddress, with that device current) and only
+// that address is passed on.  No segmented step accumulates into the
+// workspace (every region is written before it is read), so nothing needs
+// clearing between calls.
+static __device__ __align__(256) unsigned char scratch[DN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES];  // device address of `scratch` per device, once looked up
+
+// The current device's address of `scratch`, or nullptr on a HIP error.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+}  // namespace
+
+DN_EXPORT int dn_chunk_fwd_noalloc(const dn_desc* d, const void* q, const void* k, const void* v,
+                                   const dn_gates* g, const float* S0, const float* aux0, void* o,
+                                   float* S_final, float* aux_final, void* stream) {
+  const int st = check_desc(d, true);
+  if (st != DN_OK) return st;
+  const size_t need = chunk_ws_bytes(d);
+  if (need > DN_NOALLOC_SCRATCH_BYTES) return DN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && !(ws = scratch_address())) return DN_ERR_HIP;
+  return dn_chunk_fwd(d, q, k, v, g, S0, aux0, o, S_final, aux_final, ws, need, stream);
 }

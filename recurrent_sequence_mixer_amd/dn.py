@@ -23,7 +23,8 @@ IO = {torch.float32: 0, torch.bfloat16: 1}
 
 # Symbols declared in include/dn.h.
 EXPORTS = ("dn_chunk_fwd", "dn_chunk_fwd_long", "dn_chunk_fwd_long_workspace", "dn_decode_step",
-           "dn_gain_prep", "dn_status_string", "dn_version", "dn_workspace_bytes")
+           "dn_gain_prep", "dn_status_string", "dn_version", "dn_workspace_bytes",
+           "dn_chunk_fwd_noalloc")
 
 
 class DnDesc(ctypes.Structure):
@@ -61,6 +62,9 @@ def lib() -> ctypes.CDLL:
         L.dn_chunk_fwd.argtypes = [ctypes.POINTER(DnDesc), vp, vp, vp, ctypes.POINTER(DnGates),
                                    vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.dn_chunk_fwd.restype = ip
+        L.dn_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(DnDesc), vp, vp, vp,
+                                           ctypes.POINTER(DnGates), vp, vp, vp, vp, vp, vp]
+        L.dn_chunk_fwd_noalloc.restype = ip
         L.dn_chunk_fwd_long.argtypes = [ctypes.POINTER(DnDesc), ip, vp, vp, vp, ctypes.POINTER(DnGates),
                                         vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.dn_chunk_fwd_long.restype = ip

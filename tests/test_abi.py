@@ -235,6 +235,21 @@ def test_chunk_fwd_long_rejects_bad_arguments():
     assert fa(aux, FAKE + (10 << 30), S_final=FAKE + (10 << 30) + 512) == -8  # aux_final in S_final
 
 
+def test_noalloc_rejects_workspace_beyond_scratch():
+    """dn_chunk_fwd_noalloc: a shape whose workspace exceeds the library's
+    scratch array (48 MiB) returns DN_ERR_WORKSPACE before any HIP call; an
+    invalid descriptor is reported as by dn_chunk_fwd."""
+    L = dn.lib()
+    d = _desc(B=1, H=1, T=1 << 22, gain="pgdn")
+    assert L.dn_workspace_bytes(ctypes.byref(d)) > (48 << 20)
+    gp = _gates(alphaP=FAKE + (6 << 30), betaP=FAKE + (7 << 30), mu_log=FAKE + (8 << 30))
+    call = lambda desc: L.dn_chunk_fwd_noalloc(ctypes.byref(desc), FAKE + (2 << 30), FAKE + (3 << 30),
+                                               FAKE + (4 << 30), ctypes.byref(gp), None, None,
+                                               FAKE + (5 << 30), None, None, None)
+    assert call(d) == -5
+    assert call(_desc(dk=96)) == -2
+
+
 def test_bench_refuses_more_than_one_gpu():
     """bench.py runs on one GPU; --gpus N > 1 exits with a message before any GPU work."""
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
