@@ -6,14 +6,20 @@ One step = one dn_chunk_fwd call (the fused chunked forward: gains, intra-chunk
 products, triangular solve, output and state propagation) over the KLA bf16
 workload B=8, H=16, T=4096, d_k=d_v=128, C=64, inputs resident in HBM.
 `value` is tokens/s (B*T tokens per call).  The same line also reports the
-PGDN, diagonal-KDN and isotropic-KDN forwards and the batched decode step (HBM GB/s), the
-roofline of the chunked-forward kernel, and the fp64 oracle timed on a
-bounded sample on the host CPU.
+PGDN, diagonal-KDN and isotropic-KDN forwards, batch-1 long prefills and the
+batched decode step (HBM GB/s), the roofline of the chunked-forward kernel,
+the parity of sampled heads of the timed run against the fp64 oracle, and the
+oracle timed on the host CPU over the same inputs.
+
+Every timed loop is bracketed by two one-element fill launches, so that the
+dispatches between such a pair in a `rocprofv3 --kernel-trace` of this script
+are exactly the timed launches (no settle or warm-up launches).
 """
 import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -29,10 +35,32 @@ KERNEL_SOURCES = ("recurrent_sequence_mixer_amd/csrc/chunk_fwd_ws.hip",
                   "recurrent_sequence_mixer_amd/csrc/common.hpp",
                   "recurrent_sequence_mixer_amd/csrc/gains.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_kla_B8H16T4096d128_traffic.txt")
+GATES = ("alpha", "eta", "alphaP", "betaP", "mu_log", "omega", "r", "w")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+class Region:
+    """Delimiters of the timed loops in a kernel trace: a one-element fill
+    launch right before and right after each timed loop (on the same stream),
+    so that the dispatches between a pair of fills in a `rocprofv3
+    --kernel-trace` of this script are exactly the timed launches (no settle
+    or warm-up launches)."""
+
+    def __init__(self):
+        import torch
+        self.flag = torch.zeros(1, device="cuda")
+
+    def resume(self):
+        self.flag.fill_(1.0)
+
+    def pause(self):
+        self.flag.fill_(0.0)
+
+
+REGION = None
 
 
 def chunk_bytes(wl):
@@ -81,37 +109,9 @@ def settle(call, seconds):
         torch.cuda.synchronize()
 
 
-def time_chunk_long(wl, nseg, steps, warmup, settle_s=0.0):
-    """dn_chunk_fwd_long (segments in parallel) on a workload; ms per call."""
-    import torch
-    from recurrent_sequence_mixer_amd import dn
-    from recurrent_sequence_mixer_amd import workloads as W
-    inp = W.generate(wl)
-    t = dn.to_device(inp, torch.bfloat16)
-    o = torch.empty_like(t["v"])
-    S = torch.empty_like(t["S0"])
-    gates = {n: t[n] for n in ("alpha", "eta", "alphaP", "betaP", "mu_log", "omega", "r", "w")
-             if n in t}
-    aux = torch.empty((wl.B, wl.H, wl.dk), device="cuda") if wl.gain in ("pgdn", "kdn") else None
-    if wl.gain == "kdn_iso":
-        aux = torch.empty((wl.B, wl.H), device="cuda")
-    call = lambda: dn.chunk_fwd_long(t["q"], t["k"], t["v"], gates, nseg, gain=wl.gain, eps=wl.eps,
-                                     x=wl.x, mu_info=wl.mu_info, S0=t["S0"], aux0=t.get("aux0"),
-                                     out=o, S_final=S, aux_final=aux)
-    settle(call, settle_s)
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(steps):
-        call()
-    ev1.record()
-    torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / steps
-
-
-def time_chunk(wl, steps, warmup, settle_s=0.0):
+def prepare_chunk(wl):
+    """Inputs on the device, output buffers and the workspace of a chunked
+    forward; returns (inputs numpy, tensors, call)."""
     import torch
     from recurrent_sequence_mixer_amd import dn
     from recurrent_sequence_mixer_amd import workloads as W
@@ -119,36 +119,61 @@ def time_chunk(wl, steps, warmup, settle_s=0.0):
     inp = W.generate(wl)
     t = dn.to_device(inp, torch.bfloat16 if wl.io == "bf16" else torch.float32)
     log(f"[bench] {wl.name}: inputs ready in {time.time() - t0:.1f}s")
-    gates = {n: t[n] for n in ("alpha", "eta", "alphaP", "betaP", "mu_log", "omega", "r") if n in t}
+    gates = {n: t[n] for n in GATES if n in t}
     o = torch.empty_like(t["v"])
     S = torch.empty_like(t["S0"])
     aux = torch.empty((wl.B, wl.H, wl.dk), device="cuda") if wl.gain in ("pgdn", "kdn") else None
     if wl.gain == "kdn_iso":
         aux = torch.empty((wl.B, wl.H), device="cuda")
+    desc = dn.make_desc(wl.B, wl.H, wl.T, wl.dk, wl.dv, t["q"].dtype, wl.gain, wl.decay, wl.eps,
+                        wl.x, wl.mu_info)
+    nbytes = dn.workspace_bytes(desc)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda") if nbytes else None
     call = lambda: dn.chunk_fwd(t["q"], t["k"], t["v"], gates, gain=wl.gain, eps=wl.eps, x=wl.x,
-                                mu_info=wl.mu_info, S0=t["S0"], out=o, S_final=S, aux_final=aux)
+                                mu_info=wl.mu_info, S0=t["S0"], out=o, S_final=S, aux_final=aux,
+                                workspace=ws)
+    return inp, {"o": o, "S": S, "aux": aux, "ws_bytes": nbytes}, call
+
+
+def time_calls(call, steps, warmup, settle_s, per_step=False):
+    """Settle, warm up, then time `steps` calls between HIP events on torch's
+    current stream (the stream the library launches on).  Returns (ms per
+    call, sorted per-call ms or None)."""
+    import torch
     settle(call, settle_s)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    # dn launches on torch's current stream, so these events bracket exactly its kernels
+    each = None
+    if per_step:
+        per = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            per.append((a, b))
+        torch.cuda.synchronize()
+        each = sorted(x.elapsed_time(y) for x, y in per)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    per = []
-    for _ in range(steps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        call()
-        b.record()
-        per.append((a, b))
-    torch.cuda.synchronize()
+    REGION.resume()
     ev0.record()
     for _ in range(steps):
         call()
     ev1.record()
     torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
-    each = sorted(x.elapsed_time(y) for x, y in per)
-    return total_ms / steps, each
+    REGION.pause()
+    return ev0.elapsed_time(ev1) / steps, each
+
+
+def parity_sample(wl, inp, out, heads):
+    """Max relative error (per head, worst of the sampled heads) of o and S_T
+    of the timed run against the fp64 oracle on the same inputs."""
+    from oracle.recurrence import run_workload
+    o_ref, S_ref, _, _ = run_workload(wl, inp, heads=heads)
+    flat = lambda x: x.reshape((wl.B * wl.H,) + tuple(x.shape[2:]))[heads].float().cpu().numpy()
+    rel = lambda g, r: float(max(np.abs(g[i] - r[i]).max() / np.abs(r[i]).max() for i in range(len(heads))))
+    return {"heads": list(heads), "o": rel(flat(out["o"]), o_ref), "S": rel(flat(out["S"]), S_ref)}
 
 
 def time_decode(dwl, steps_timed, settle_s=0.0):
@@ -171,12 +196,14 @@ def time_decode(dwl, steps_timed, settle_s=0.0):
         dn.decode_step(q, k, v, g, S.clone(), gain="kla", eps=dwl.eps, out=o)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    REGION.resume()
     ev0.record()
     for s in range(steps_timed):
         q, k, v, g = ins[s % dwl.steps]
         dn.decode_step(q, k, v, g, S, gain="kla", eps=dwl.eps, out=o)
     ev1.record()
     torch.cuda.synchronize()
+    REGION.pause()
     return ev0.elapsed_time(ev1) / steps_timed
 
 
@@ -228,6 +255,22 @@ def calib_copy(mib):
     log(f"[bench] calibration copy: {mib} MiB read + {mib} MiB written, 3 launches")
 
 
+def host_info():
+    import torch
+    cpu = platform.processor()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": cpu, "host_cores": len(os.sched_getaffinity(0)), "numpy": np.__version__,
+            "torch": torch.__version__, "hip": torch.version.hip,
+            "gpu": torch.cuda.get_device_name(0), "python": platform.python_version()}
+
+
 _ORACLE_JOB = {}
 
 
@@ -239,14 +282,15 @@ def _oracle_heads(heads):
     return float(o[..., 0].sum())
 
 
-def cpu_baseline(wl, heads=2, T=1024):
-    """The fp64 oracle, as it is, on a bounded sample (`heads` heads x `T`
-    tokens), its heads spread over a process pool of the host's cores."""
+def cpu_baseline(wl, inp, heads, T):
+    """The fp64 oracle, as it is, on a bounded sample of the timed workload's
+    own inputs (`heads` heads x the first `T` tokens), its heads spread over a
+    process pool of the host's cores."""
     import multiprocessing as mp
-    from recurrent_sequence_mixer_amd import workloads as W
-    sample = wl.replace(B=1, H=heads, T=T)
-    _ORACLE_JOB["wl"] = sample
-    _ORACLE_JOB["inp"] = W.generate(sample)  # shared with the forked workers
+    T = min(T, wl.T)
+    heads = min(heads, wl.B * wl.H)
+    _ORACLE_JOB["wl"] = wl.replace(T=T)
+    _ORACLE_JOB["inp"] = inp  # shared with the forked workers
     nproc = max(1, min(len(os.sched_getaffinity(0)), heads))
     shares = [list(range(i, heads, nproc)) for i in range(nproc)]
     t0 = time.time()
@@ -259,12 +303,25 @@ def cpu_baseline(wl, heads=2, T=1024):
         "unit": "tokens/s",
         "cores": nproc,
         "kind": "oracle",
-        "sample": f"{wl.name}: {heads} heads x {T} tokens (of {wl.B * wl.H} x {wl.T}) over {nproc} "
-                  f"processes, {wall:.1f}s wall; value scaled to workload tokens/s ({wl.H} heads per token)",
+        "sample": f"{wl.name}: the timed inputs' first {heads} heads (of {wl.B * wl.H}) x {T} tokens "
+                  f"(of {wl.T}) over {nproc} processes, {wall:.1f}s wall; value scaled to workload "
+                  f"tokens/s ({wl.H} heads per token)",
     }
 
 
+def extra_chunk(wl, steps, warmup, settle_s):
+    _, out, call = prepare_chunk(wl)
+    ms, _ = time_calls(call, steps, warmup, settle_s)
+    b = chunk_bytes(wl)
+    log(f"[bench] {wl.name}: {ms:.3f} ms/step")
+    return {"workload": wl.name, "ms": ms, "tokens_per_s": wl.tokens / (ms * 1e-3),
+            "hbm_gbs": b / (ms * 1e-3) / 1e9, "hbm_frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_frac": chunk_flops(wl) / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "workspace_bytes": out["ws_bytes"]}
+
+
 def main():
+    global REGION
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -278,6 +335,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample: tokens per head")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a device copy of this size (byte-counter calibration)")
+    ap.add_argument("--only", default=None,
+                    help="time only these extras (comma list of pgdn, kdn, kdn_iso, long, decode) "
+                         "after the headline")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the forward engine shards "
@@ -288,12 +348,18 @@ def main():
     import torch
     from recurrent_sequence_mixer_amd import workloads as W
     torch.cuda.set_device(0)
+    REGION = Region()
 
     wl = W.WORKLOADS[1]
-    ms, each = time_chunk(wl, args.steps, args.warmup, args.settle_s)
+    inp, out1, call = prepare_chunk(wl)
+    ms, each = time_calls(call, args.steps, args.warmup, args.settle_s, per_step=True)
     bytes_ = chunk_bytes(wl)
     flops = chunk_flops(wl)
     achieved = bytes_ / (ms * 1e-3) / 1e9
+    log(f"[bench] {wl.name}: {ms:.3f} ms/step")
+    nh = wl.B * wl.H
+    parity = parity_sample(wl, inp, out1, [0, nh // 2 + 3, nh - 1])
+    log(f"[bench] parity of the timed run (sampled heads): {parity}")
     out = {
         "metric": METRIC,
         "value": wl.tokens / (ms * 1e-3),
@@ -318,59 +384,45 @@ def main():
                  "counted_flops_per_launch": flops},
         "step_ms_p10_p50_p90": [each[len(each) // 10], each[len(each) // 2], each[9 * len(each) // 10]],
         "settle_s": args.settle_s,
+        "parity": parity,
+        "inputs_sha256": W.sha256(inp),
+        "host": host_info(),
     }
-    log(f"[bench] {wl.name}: {ms:.3f} ms/step")
     if not args.no_extra:
         extra = {}
+        only = None if args.only is None else set(args.only.split(","))
+        want = lambda key: only is None or key in only
+        half = max(5, args.steps // 2)
         # isotropic KDN (Kalman Delta Networks §2.7) at the diagonal-KDN shape
         iso = W.WORKLOADS[3].replace(name="kdn_iso_bf16_B4H16T8192d128", gain="kdn_iso")
-        # batch-1 long prefill at the pages' 131072-token length (8 heads: 16 workgroups)
-        longp = W.Workload("kla_long_B1H8T131072d128", "kla", "scalar", "bf16", 1, 8, 131072, 128,
-                           128, seed=51)
-        for w2 in (W.WORKLOADS[2], W.WORKLOADS[3], iso, longp):
-            ms2, _ = time_chunk(w2, max(5, args.steps // 2), args.warmup, args.settle_s)
-            b2 = chunk_bytes(w2)
-            key = "long_prefill" if w2 is longp else w2.gain
-            extra[key] = {"workload": w2.name, "ms": ms2, "tokens_per_s": w2.tokens / (ms2 * 1e-3),
-                              "hbm_gbs": b2 / (ms2 * 1e-3) / 1e9,
-                              "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                              "mfma_frac": chunk_flops(w2) / (ms2 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
-            log(f"[bench] {w2.name}: {ms2:.3f} ms/step")
-        # the same long prefill by 16 segments of 8192 tokens in parallel (dn_chunk_fwd_long)
-        ms3 = time_chunk_long(longp, 16, max(5, args.steps // 2), args.warmup, args.settle_s)
-        extra["long_prefill_segments"] = {"workload": longp.name, "nseg": 16, "ms": ms3,
-                                          "tokens_per_s": longp.tokens / (ms3 * 1e-3),
-                                          "hbm_frac": chunk_bytes(longp) / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        log(f"[bench] {longp.name} by 16 segments: {ms3:.3f} ms/step")
-        # PGDN batch-1 prefill (Preconditioned DeltaNet Fig. 4: batch 1, 8 heads,
-        # head dim 128): one pass (16 workgroups) and 16 segments of 2048 tokens
-        longpg = W.Workload("pgdn_long_B1H8T32768d128", "pgdn", "scalar", "bf16", 1, 8, 32768, 128,
-                            128, keys="unit", seed=52)
-        ms4, _ = time_chunk(longpg, max(5, args.steps // 2), args.warmup, args.settle_s)
-        ms5 = time_chunk_long(longpg, 16, max(5, args.steps // 2), args.warmup, args.settle_s)
-        extra["long_prefill_pgdn"] = {"workload": longpg.name, "ms_one_pass": ms4, "nseg": 16,
-                                      "ms_segments": ms5,
-                                      "tokens_per_s_segments": longpg.tokens / (ms5 * 1e-3)}
-        log(f"[bench] {longpg.name}: one pass {ms4:.3f} ms, by 16 segments {ms5:.3f} ms")
-        # diagonal KDN with per-channel decay at the same batch-1 shape
-        longkd = W.Workload("kdn_long_B1H8T32768d128", "kdn", "channel", "bf16", 1, 8, 32768, 128,
-                            128, seed=53)
-        ms6, _ = time_chunk(longkd, max(5, args.steps // 4), args.warmup, args.settle_s)
-        ms7 = time_chunk_long(longkd, 16, max(5, args.steps // 2), args.warmup, args.settle_s)
-        extra["long_prefill_kdn"] = {"workload": longkd.name, "ms_one_pass": ms6, "nseg": 16,
-                                     "ms_segments": ms7,
-                                     "tokens_per_s_segments": longkd.tokens / (ms7 * 1e-3)}
-        log(f"[bench] {longkd.name}: one pass {ms6:.3f} ms, by 16 segments {ms7:.3f} ms")
-        dwl = W.WORKLOADS[4]
-        dms = time_decode(dwl, args.decode_steps, args.settle_s)
-        gbs = decode_bytes(dwl) / (dms * 1e-3) / 1e9
-        extra["decode"] = {"workload": dwl.name, "ms_per_step": dms,
-                           "seq_tokens_per_s": dwl.N / (dms * 1e-3), "hbm_gbs": gbs,
-                           "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_step": decode_bytes(dwl)}
-        log(f"[bench] decode: {dms:.3f} ms/step, {gbs:.0f} GB/s")
+        for key, w2 in (("pgdn", W.WORKLOADS[2]), ("kdn", W.WORKLOADS[3]), ("kdn_iso", iso)):
+            if want(key):
+                extra[key] = extra_chunk(w2, half, args.warmup, args.settle_s)
+        if want("long"):
+            # batch-1 long prefills (dn_chunk_fwd picks 16 segments per head for
+            # these shapes): KLA at the pages' 131072-token length, PGDN and
+            # diagonal KDN at B1 H8 T32768 (Preconditioned DeltaNet Fig. 4:
+            # batch 1, 8 heads, head dim 128)
+            longs = (("long_prefill", W.Workload("kla_long_B1H8T131072d128", "kla", "scalar", "bf16", 1,
+                                                 8, 131072, 128, 128, seed=51)),
+                     ("long_prefill_pgdn", W.Workload("pgdn_long_B1H8T32768d128", "pgdn", "scalar",
+                                                      "bf16", 1, 8, 32768, 128, 128, keys="unit",
+                                                      seed=52)),
+                     ("long_prefill_kdn", W.Workload("kdn_long_B1H8T32768d128", "kdn", "channel", "bf16",
+                                                     1, 8, 32768, 128, 128, seed=53)))
+            for key, w2 in longs:
+                extra[key] = extra_chunk(w2, half, args.warmup, args.settle_s)
+        if want("decode"):
+            dwl = W.WORKLOADS[4]
+            dms = time_decode(dwl, args.decode_steps, args.settle_s)
+            gbs = decode_bytes(dwl) / (dms * 1e-3) / 1e9
+            extra["decode"] = {"workload": dwl.name, "ms_per_step": dms,
+                               "seq_tokens_per_s": dwl.N / (dms * 1e-3), "hbm_gbs": gbs,
+                               "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_step": decode_bytes(dwl)}
+            log(f"[bench] decode: {dms:.3f} ms/step, {gbs:.0f} GB/s")
         out["extra"] = extra
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_heads, args.cpu_tokens)
         log(f"[bench] cpu baseline: {out['cpu_baseline']}")
     if args.calib_copy_mib:
         calib_copy(args.calib_copy_mib)
