@@ -62,10 +62,14 @@
  * on a negative status nothing has been enqueued.  DN_ERR_HIP reports a
  * failed launch.  NaN/Inf in the data are not checked and propagate.
  * Preconditions on values (not checked): alpha in (0, 1]; PGDN A_0 > 0 and
- * alphaP, betaP >= 0; KDN and KDN_ISO r > 0, omega >= 0, p_0 and b_0 > 0;
- * for channel decay the
- * sum of -log(alpha) over any 32 consecutive tokens of one channel stays
- * below 80 (fp32 range of the in-chunk decay factors).
+ * alphaP, betaP >= 0; KDN and KDN_ISO r > 0, omega >= 0, p_0 and b_0 > 0.
+ * RANGE OF CHANNEL DECAY (checked on the device).  The chunked calls refer
+ * the decay factors of each key channel to the middle of its chunk of 64
+ * tokens (token 31), so each half chunk's decay of a channel must be at least
+ * 2^-96 (a geometric-mean alpha of at least 1/8 over its 32 tokens).  A chunk
+ * that goes beyond turns the head's state, and every output of the head from
+ * that chunk on, into NaN: no finite wrong value is returned.  dn_decode_step
+ * has no such bound; scalar decay has none in any call. 
  *
  * Thread safety: all entry points are reentrant; there is no mutable global
  * state.

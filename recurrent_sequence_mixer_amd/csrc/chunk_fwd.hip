@@ -64,6 +64,17 @@ __device__ __forceinline__ void wave_lds_sync() {
 // sums and their differences (finite, and exp2 of very negative values
 // underflowing to 0 is the right limit).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Channel decay: the scale 2^Gmid of the state rows, Gmid the log2-decay from
+// the chunk start to its midpoint (token 31) and Gn to its end.  Referred to
+// the midpoint, every operand factor stays within 2^96 and the scaled state
+// stays normal while both half-chunk decays are at least 2^-96; beyond that
+// the chunk form cannot be evaluated this way, and a NaN scale turns the
+// head's state and every later output into NaN rather than into wrong
+// finite values.
+__device__ __forceinline__ float midpoint_scale(float gm, float gn) {
+  return gm >= -96.f && gn - gm >= -96.f ? fast_exp2(gm) : __builtin_nanf("");
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // PGDN write scale B(A) = exp(-ln(x) s), s = r / (1 + |r|), r = ln A - mu
@@ -742,7 +753,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
         // and 63 from the scan's boundary values
         const float gm = seg == 0 ? gs[HT - 1] : sm.g31[dch], gl = sm.g63[dch];
         if (seg == 0) {
-          sm.gmid[dch] = fast_exp2(gm);
+          sm.gmid[dch] = midpoint_scale(gm, gl);
           sm.gn[dch] = fast_exp2(gl);
         }
         const float fl = fast_exp2(gl - gm);  // 2^(Gn - Gmid)
@@ -769,7 +780,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
         if (tid < DK) {
           const int d = tid, cb = 64 * wave;
           const float gm = gch[0][CH / 2 - 1], gl = gch[0][CH - 1];
-          sm.gmid[d] = fast_exp2(gm);
+          sm.gmid[d] = midpoint_scale(gm, gl);
           sm.gn[d] = fast_exp2(gl);
           const float fl = fast_exp2(gl - gm);  // 2^(Gn - Gmid)
 #pragma unroll
@@ -797,7 +808,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
         const int d = tid + cc * NT;
         if (d < DK) {
           const float gm = gch[cc][CH / 2 - 1], gl = gch[cc][CH - 1];
-          sm.gmid[d] = fast_exp2(gm);
+          sm.gmid[d] = midpoint_scale(gm, gl);
           sm.gn[d] = fast_exp2(gl);
 #pragma unroll
           for (int t = 0; t < CH; ++t) {

@@ -748,8 +748,14 @@ __global__ __launch_bounds__(WS_THREADS) void chunk_fwd_ws_kernel(ChunkArgs a) {
         // 2^(G - G_r) before the segment's first token
         float e = num * __builtin_amdgcn_rcpf(den);
         if (g == 0) {
-          sm.gref[c & 1][d] = gr;  // 2^(G_r): chunk start -> token 31
-          sm.gnr[c & 1][d] = gt;   // 2^(G_n - G_r): token 31 -> chunk end
+          // 2^(G_r): chunk start -> token 31; 2^(G_n - G_r): token 31 -> chunk
+          // end.  Referred to token 31, every factor stays within 2^96 and S
+          // 2^(G_r) stays normal while both half-chunk decays are at least
+          // 2^-96; beyond that the chunk form cannot be evaluated this way, and
+          // a NaN reference turns the head's state and every later output
+          // into NaN rather than into wrong finite values
+          sm.gref[c & 1][d] = gr >= 0x1p-96f && gt >= 0x1p-96f ? gr : __builtin_nanf("");
+          sm.gnr[c & 1][d] = gt;
         }
         uint16_t* kw = sm.k[c & 1];  // raw k, rewritten in place with W^
         uint16_t* qh = sm.q[0];      // raw q, rewritten in place with Q^

@@ -54,6 +54,7 @@ class Workload:
     # per-head indexing of the centre is exercised (0: the same for all heads)
     mu_spread: float = 0.0
     mu_info: float = 1.0  # KDN information scaling (1 = strict reverse-KL update)
+    alpha_mean: float = 3.0  # decay alpha = sigmoid(N(alpha_mean, 1)); lower is stronger decay
     keys: str = "scaled"  # "scaled": N(0,1) rows times U[0.25, 4]; "unit": L2-normalised
     s0: str = "normal"  # "zero" or "normal" (N(0, 0.01), i.e. std 0.1)
     seed: int = 0
@@ -153,9 +154,9 @@ def generate(wl: Workload) -> Dict[str, np.ndarray]:
     v = rng.standard_normal(shp + (dv,))
     eta = _sigmoid(rng.standard_normal(shp))
     if wl.decay == "scalar":
-        alpha = round_f32(_sigmoid(rng.normal(3.0, 1.0, size=shp)))
+        alpha = round_f32(_sigmoid(rng.normal(wl.alpha_mean, 1.0, size=shp)))
     else:
-        alpha = round_io(_sigmoid(rng.normal(3.0, 1.0, size=shp + (dk,))), wl.io)
+        alpha = round_io(_sigmoid(rng.normal(wl.alpha_mean, 1.0, size=shp + (dk,))), wl.io)
     out = {
         "q": round_io(q, wl.io),
         "k": round_io(k, wl.io),

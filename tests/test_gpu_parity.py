@@ -380,6 +380,54 @@ def test_kla_zero_key_rows():
     _check(wl, inp, None, o, S)
 
 
+@pytest.mark.parametrize("gain,keys,io,dk", [("kdn", "scaled", "bf16", 128), ("kdn_iso", "scaled", "bf16", 128),
+                                           ("kdn", "scaled", "bf16", 64), ("pgdn", "unit", "bf16", 128),
+                                           ("kla", "scaled", "bf16", 128), ("gdn", "unit", "f32", 64)])
+def test_strong_channel_decay_in_range(gain, keys, io, dk):
+    """Per-channel decay alpha = sigmoid(N(-1, 1)) (about 2 bits of decay per
+    token; within a chunk the state decays by 2^-128 or more): every factor
+    of the chunk form stays in range, o and S match the oracle.  KDN and
+    isotropic KDN run the producer / consumer kernel, PKDA (PGDN), KLA and
+    fp32 GDN the generic one."""
+    wl = W.Workload(f"{gain}_strong_decay", gain, "channel", io, 2, 2, 333, dk, dk, keys=keys,
+                    alpha_mean=-1.0, seed=550 + dk)
+    inp = W.generate(wl)
+    o, S, aux = gpu_chunk(wl, inp)
+    _check(wl, inp, None, o, S, aux)
+
+
+def test_strong_channel_decay_long_segments():
+    """The same strong decay through dn_chunk_fwd_long (4 segments)."""
+    wl = W.Workload("kdn_strong_decay_long", "kdn", "channel", "bf16", 1, 2, 1024, 128, 128,
+                    alpha_mean=-1.0, seed=560)
+    inp = W.generate(wl)
+    o, S, aux = gpu_chunk_long(wl, inp, 4)
+    _check(wl, inp, None, o, S, aux)
+
+
+@pytest.mark.parametrize("gain,keys", [("kdn", "scaled"), ("kdn_iso", "scaled"), ("pgdn", "unit")])
+def test_channel_decay_beyond_range_is_nan(gain, keys):
+    """One channel of head 0 decays by 2^-320 over the first half of chunk 5
+    (alpha = 2^-10 for 32 tokens): referred to the chunk midpoint its factors
+    would leave fp32 range, so the kernels turn the head's state into NaN from
+    that chunk on.  Before it, head 0 matches the oracle; head 1 matches it
+    everywhere; no output of head 0 is a finite wrong value."""
+    wl = W.Workload(f"{gain}_decay_nan", gain, "channel", "bf16", 1, 2, 448, 128, 128, keys=keys,
+                    seed=570)
+    inp = W.generate(wl)
+    inp["alpha"][0, 0, 320:352, 3] = np.float32(2.0 ** -10)
+    o, S, aux = gpu_chunk(wl, inp)
+    o_ref, S_ref, _ = oracle_chunk(wl, inp)
+    assert np.all(np.isfinite(o_ref)) and np.all(np.isfinite(S_ref))
+    o = flat_heads(o)
+    S = flat_heads(S)
+    assert np.all(np.isnan(o[0, 320:])) and np.all(np.isnan(S[0]))
+    e_before = max_rel_err(o[:1, :320], o_ref[:1, :320])
+    e_other = max(max_rel_err(o[1:], o_ref[1:]), max_rel_err(S[1:], S_ref[1:]))
+    print(f"{gain}: head 0 before chunk 5 {e_before:.2e}, head 1 {e_other:.2e}")
+    assert e_before <= TOL["bf16"] and e_other <= TOL["bf16"]
+
+
 def test_kdn_mu_dk_and_kla_key_norm_only():
     """The pages' other gain settings on the same kernels: diagonal KDN with
     information scaling mu = d_k (Kalman Delta Networks §2.5), and KLA's

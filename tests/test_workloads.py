@@ -62,3 +62,13 @@ def test_pgdn_centre_spread_per_head():
     np.testing.assert_allclose(b["mu_log"].max() - b["mu_log"].min(), 1.5, rtol=1e-6)
     for name in ("q", "k", "v", "eta", "alpha", "alphaP", "betaP", "S0"):
         np.testing.assert_array_equal(a[name], b[name])
+
+
+def test_alpha_mean_sets_decay_strength():
+    """alpha_mean moves the decay distribution; the other draws are unchanged."""
+    base = W.WORKLOADS[3].replace(B=1, H=2, T=64)
+    a = W.generate(base)
+    b = W.generate(base.replace(alpha_mean=-1.0))
+    assert np.median(np.log2(b["alpha"].astype(np.float64))) < -1.5 < np.median(np.log2(a["alpha"].astype(np.float64)))
+    for name in ("q", "k", "v", "omega", "r", "S0"):
+        np.testing.assert_array_equal(a[name], b[name])
