@@ -114,9 +114,8 @@ typedef enum dn_decay { DN_DECAY_SCALAR = 0, DN_DECAY_CHANNEL = 1 } dn_decay;
 /* Problem descriptor (host struct).
  *   B, H >= 1, B H <= 65535; T >= 0 (T = 0: S_final = S0, aux_final = aux0,
  *   o untouched);
- *   dk in {64, 128}; dv in {64, 128} for dn_decode_step, and for the chunked
- *   calls any multiple of 64 up to 2048 (d_v = v_expand d_k); C = 64 (chunk
- *   length of the chunked forward);
+ *   dk in {64, 128}; dv any multiple of 64 up to 2048 (d_v = v_expand d_k);
+ *   C = 64 (chunk length of the chunked forward);
  *   io: dn_dtype of q, k, v, o and of per-channel gates;
  *   gain: dn_gain; decay: dn_decay (KDN requires DN_DECAY_CHANNEL or SCALAR);
  *   eps >= 0 (KLA), x >= 1 (PGDN bound: B in [1/x, x];

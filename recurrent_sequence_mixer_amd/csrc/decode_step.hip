@@ -38,7 +38,13 @@ template <> struct IoLoad<float> {
 
 constexpr int DECODE_THREADS = 256;
 
-template <typename IO, int DK, int DV, int GAIN, bool CHANNEL>
+// DV is the width of the value slice one pass of the workgroup handles (64
+// or 128 columns).  WIDE: a head of d_v = a.dv columns (v_expand d_k, a
+// multiple of DV) is walked slice by slice by the same workgroup, whose
+// write gain is formed once; one workgroup per head keeps the in-place update
+// of the gain's statistic (aux) free of races between value slices.  Without
+// WIDE, d_v = DV and every stride is a compile-time constant.
+template <typename IO, int DK, int DV, int GAIN, bool CHANNEL, bool WIDE>
 __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs a) {
   constexpr int CG = DV / 4;                   // float4 column groups
   constexpr int RG = DECODE_THREADS / CG;      // row groups
@@ -55,18 +61,20 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
   const long nh = blockIdx.x;  // n * H + h
   const int h = static_cast<int>(nh % a.H);
   const int cg = tid % CG, rg = tid / CG;
-  f32x4* Sp = reinterpret_cast<f32x4*>(a.S + nh * DK * DV);
+  const int dv = WIDE ? a.dv : DV, ncg = dv / 4, nsl = dv / DV;
+  f32x4* Sp = reinterpret_cast<f32x4*>(a.S + nh * DK * dv);
 
-  // 1. issue the state loads first: they are the bulk of the traffic.
+  // 1. issue the state loads of the first slice first: they are the bulk of
+  // the traffic.
   f32x4 s[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
-    s[i] = __builtin_nontemporal_load(Sp + (rg + RG * i) * CG + cg);
+    s[i] = __builtin_nontemporal_load(Sp + (rg + RG * i) * ncg + cg);
 
   // 2. token inputs and the write gain (threads d < DK own key channel d).
   float red1 = 0.f, red2 = 0.f, red3 = 0.f;
   float kd = 0.f, qd = 0.f, ad = 0.f, pre = 0.f, aux_new = 0.f, mu_over_r = 0.f;
-  if (tid < DV) s_v[tid] = L::at(a.v, nh * DV + tid);
+  if (tid < DV) s_v[tid] = L::at(a.v, nh * dv + tid);
   if (tid < DK) {
     kd = L::at(a.k, nh * DK + tid);
     qd = L::at(a.q, nh * DK + tid);
@@ -148,62 +156,72 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
   else if (GAIN == GAIN_KDN) wq = sum2 / (a.r[nh] + sum1);
   else if (GAIN == GAIN_KDN_ISO) wq = iso_beta * sum2;
   else wq = sum2;
-  __syncthreads();
-
-  // 3. partial readouts of the decayed state over this thread's rows.
-  f32x4 pk = zero4(), pq = zero4();
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = rg + RG * i;
-    const float ak = s_ak[r], aq = s_aq[r];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pk[j] = fmaf(ak, s[i][j], pk[j]);
-      pq[j] = fmaf(aq, s[i][j], pq[j]);
-    }
-  }
-  s_yk[rg][cg] = pk;
-  s_yq[rg][cg] = pq;
-  // isotropic KDN: every thread read the head's variance before the barrier
-  // that follows the gains, so it can be replaced now
-  if (GAIN == GAIN_KDN_ISO && tid == 0) a.aux[nh] = iso_b;
-  __syncthreads();
-
-  // 4. residual and output (threads c < DV own value column c).
-  if (tid < DV) {
-    const int g = tid / 4, j = tid % 4;
-    float yk = 0.f, yq = 0.f;
-#pragma unroll
-    for (int i = 0; i < RG; ++i) {
-      yk += reinterpret_cast<const float*>(&s_yk[i][g])[j];
-      yq += reinterpret_cast<const float*>(&s_yq[i][g])[j];
-    }
-    const float e = s_v[tid] - yk;
-    s_e[tid] = e;
-    L::store(a.o, nh * DV + tid, fmaf(wq, e, yq));
-  }
-  __syncthreads();
-
-  // 5. rank-1 write of the decayed state, one HBM write.
   const float a_scalar = CHANNEL ? 0.f : static_cast<const float*>(a.alpha)[nh];
-  const f32x4 e4 = reinterpret_cast<const f32x4*>(s_e)[cg];
+
+  for (int sl = 0; sl < nsl; ++sl) {
+    const int c0 = sl * DV;  // first value column of the slice
+    if (sl > 0) {
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = rg + RG * i;
-    const float dec = CHANNEL ? s_a[r] : a_scalar;
-    const float wr = s_w[r];
-    f32x4 o4;
+      for (int i = 0; i < RPT; ++i)
+        s[i] = __builtin_nontemporal_load(Sp + (rg + RG * i) * ncg + c0 / 4 + cg);
+      if (tid < DV) s_v[tid] = L::at(a.v, nh * dv + c0 + tid);
+    }
+    __syncthreads();  // gains, slice inputs visible; the previous slice's LDS reads done
+    // isotropic KDN: every thread read the head's variance before the barrier
+    // above, so it can be replaced now
+    if (GAIN == GAIN_KDN_ISO && tid == 0 && sl == 0) a.aux[nh] = iso_b;
+
+    // 3. partial readouts of the decayed state over this thread's rows.
+    f32x4 pk = zero4(), pq = zero4();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o4[j] = fmaf(dec, s[i][j], wr * e4[j]);
-    __builtin_nontemporal_store(o4, Sp + r * CG + cg);
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rg + RG * i;
+      const float ak = s_ak[r], aq = s_aq[r];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pk[j] = fmaf(ak, s[i][j], pk[j]);
+        pq[j] = fmaf(aq, s[i][j], pq[j]);
+      }
+    }
+    s_yk[rg][cg] = pk;
+    s_yq[rg][cg] = pq;
+    __syncthreads();
+
+    // 4. residual and output (threads c < DV own value column c0 + c).
+    if (tid < DV) {
+      const int g = tid / 4, j = tid % 4;
+      float yk = 0.f, yq = 0.f;
+#pragma unroll
+      for (int i = 0; i < RG; ++i) {
+        yk += reinterpret_cast<const float*>(&s_yk[i][g])[j];
+        yq += reinterpret_cast<const float*>(&s_yq[i][g])[j];
+      }
+      const float e = s_v[tid] - yk;
+      s_e[tid] = e;
+      L::store(a.o, nh * dv + c0 + tid, fmaf(wq, e, yq));
+    }
+    __syncthreads();
+
+    // 5. rank-1 write of the decayed state, one HBM write.
+    const f32x4 e4 = reinterpret_cast<const f32x4*>(s_e)[cg];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rg + RG * i;
+      const float dec = CHANNEL ? s_a[r] : a_scalar;
+      const float wr = s_w[r];
+      f32x4 o4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o4[j] = fmaf(dec, s[i][j], wr * e4[j]);
+      __builtin_nontemporal_store(o4, Sp + r * ncg + c0 / 4 + cg);
+    }
   }
 }
 
-template <typename IO, int DK, int DV>
-static hipError_t launch_decode_io(const DecodeArgs& a, int gain, bool channel, hipStream_t st) {
+template <typename IO, int DK, int DV, bool WIDE>
+static hipError_t launch_decode_w(const DecodeArgs& a, int gain, bool channel, hipStream_t st) {
   dim3 grid(static_cast<unsigned>(a.N * a.H)), block(DECODE_THREADS);
 #define DN_DEC(G, CH) \
-  hipLaunchKernelGGL((decode_step_kernel<IO, DK, DV, G, CH>), grid, block, 0, st, a)
+  hipLaunchKernelGGL((decode_step_kernel<IO, DK, DV, G, CH, WIDE>), grid, block, 0, st, a)
   switch (gain) {
     case GAIN_KLA: if (channel) DN_DEC(GAIN_KLA, true); else DN_DEC(GAIN_KLA, false); break;
     case GAIN_GDN: if (channel) DN_DEC(GAIN_GDN, true); else DN_DEC(GAIN_GDN, false); break;
@@ -216,13 +234,21 @@ static hipError_t launch_decode_io(const DecodeArgs& a, int gain, bool channel, 
   return hipGetLastError();
 }
 
+template <typename IO, int DK, int DV>
+static hipError_t launch_decode_io(const DecodeArgs& a, int gain, bool channel, hipStream_t st) {
+  return a.dv == DV ? launch_decode_w<IO, DK, DV, false>(a, gain, channel, st)
+                    : launch_decode_w<IO, DK, DV, true>(a, gain, channel, st);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int io_bf16, int gain, bool channel, hipStream_t st) {
   if (a.N * a.H == 0) return hipSuccess;
+  // value slices of 128 columns where d_v allows, else of 64
+  const bool w128 = a.dv % 128 == 0;
 #define DN_SHAPE(IO)                                                                  \
-  if (a.dk == 128 && a.dv == 128) return launch_decode_io<IO, 128, 128>(a, gain, channel, st); \
-  if (a.dk == 128 && a.dv == 64) return launch_decode_io<IO, 128, 64>(a, gain, channel, st);   \
-  if (a.dk == 64 && a.dv == 128) return launch_decode_io<IO, 64, 128>(a, gain, channel, st);   \
-  if (a.dk == 64 && a.dv == 64) return launch_decode_io<IO, 64, 64>(a, gain, channel, st);
+  if (a.dk == 128 && w128) return launch_decode_io<IO, 128, 128>(a, gain, channel, st); \
+  if (a.dk == 128) return launch_decode_io<IO, 128, 64>(a, gain, channel, st);          \
+  if (a.dk == 64 && w128) return launch_decode_io<IO, 64, 128>(a, gain, channel, st);   \
+  if (a.dk == 64) return launch_decode_io<IO, 64, 64>(a, gain, channel, st);
   if (io_bf16) {
     DN_SHAPE(uint16_t)
   } else {

@@ -15,9 +15,9 @@
 namespace {
 
 bool valid_dim(int d) { return d == 64 || d == 128; }
-// value width of the chunked forward: d_v = v_expand d_k, any multiple of 64
-// up to 2048 (the kernels walk 64-column value slices)
-bool valid_chunk_dv(int d) { return d >= 64 && d <= 2048 && d % 64 == 0; }
+// value width: d_v = v_expand d_k, any multiple of 64 up to 2048 (the kernels
+// walk 64- or 128-column value slices)
+bool valid_dv(int d) { return d >= 64 && d <= 2048 && d % 64 == 0; }
 
 size_t io_size(int io) { return io == DN_BF16 ? 2 : 4; }
 
@@ -36,7 +36,7 @@ bool overlap(Range a, Range b) {
 int check_desc(const dn_desc* d, bool chunked) {
   if (!d) return DN_ERR_NULL;
   if (d->B < 1 || d->H < 1 || d->T < 0) return DN_ERR_SHAPE;
-  if (!valid_dim(d->dk) || !(chunked ? valid_chunk_dv(d->dv) : valid_dim(d->dv))) return DN_ERR_SHAPE;
+  if (!valid_dim(d->dk) || !valid_dv(d->dv)) return DN_ERR_SHAPE;
   if (chunked && d->C != 64) return DN_ERR_SHAPE;
   if (static_cast<long long>(d->B) * d->H > 65535) return DN_ERR_SHAPE;
   if (static_cast<long long>(d->B) * d->H * d->T * (d->dk > d->dv ? d->dk : d->dv) >

@@ -123,7 +123,8 @@ def test_decode_rejects_bad_arguments():
     assert f(_desc(T=1), S=None) == -1
     assert f(_desc(T=1, gain="pgdn")) == -1
     assert f(_desc(T=1, dk=48)) == -2
-    assert f(_desc(T=1, dv=256)) == -2  # wider value heads are built for the chunked forward only
+    assert f(_desc(T=1, dv=96)) == -2  # value heads are multiples of 64 columns
+    assert f(_desc(T=1, dv=4096)) == -2
 
 
 def test_gain_prep_rejects_bad_arguments():

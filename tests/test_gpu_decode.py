@@ -74,6 +74,42 @@ def test_decode_gains(gain, decay, io, dk, dv):
         assert max_rel_err(flat_heads(aux.cpu().numpy()), aux_ref) <= 1e-5
 
 
+@pytest.mark.parametrize("gain,decay,keys,dk,dv", [("kla", "scalar", "scaled", 128, 256),
+                                                  ("kdn", "channel", "scaled", 128, 512),
+                                                  ("pgdn", "scalar", "unit", 64, 192),
+                                                  ("kdn_iso", "channel", "scaled", 128, 384),
+                                                  ("gdn", "scalar", "unit", 64, 2048)])
+def test_decode_value_expansion(gain, decay, keys, dk, dv):
+    """Wider value heads d_v = v_expand d_k (Kalman Delta Networks: value
+    expansion up to 16): one workgroup walks the head's value slices, its
+    gain (and statistic update) formed once; 10 steps over 3 x 2 heads."""
+    dn = _dn()
+    wl = W.Workload("dec_vexp", gain, decay, "bf16", 3, 2, 10, dk, dv, keys=keys, seed=580 + dv)
+    inp = W.generate(wl)
+    t = dn.to_device(inp, torch.bfloat16)
+    S = t["S0"].clone()
+    aux = torch.ones((3, 2, dk), device="cuda") if gain in ("pgdn", "kdn") else None
+    if gain == "kdn_iso":
+        aux = torch.ones((3, 2), device="cuda")
+    outs = []
+    for s in range(wl.T):
+        gates = {n: t[n][:, :, s].contiguous() for n in ("alpha", "eta", "alphaP", "betaP", "omega", "r")
+                 if n in t}
+        if "mu_log" in t:
+            gates["mu_log"] = t["mu_log"]
+        outs.append(dn.decode_step(t["q"][:, :, s].contiguous(), t["k"][:, :, s].contiguous(),
+                                   t["v"][:, :, s].contiguous(), gates, S, aux, gain=gain, eps=wl.eps,
+                                   x=wl.x, mu_info=wl.mu_info))
+    torch.cuda.synchronize()
+    o = torch.stack(outs, dim=2).float().cpu().numpy()
+    o_ref, S_ref, aux_ref, _ = run_workload(wl, inp)
+    eo, es = max_rel_err(flat_heads(o), o_ref), max_rel_err(flat_heads(S.cpu().numpy()), S_ref)
+    print(f"decode {gain} {dk}x{dv}: o {eo:.2e} S {es:.2e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    if aux is not None:
+        assert max_rel_err(flat_heads(aux.cpu().numpy()), aux_ref) <= 1e-5
+
+
 def test_decode_full_size_sampled():
     """Workload 4 at its full size (512 sequences x 16 heads) over all 256
     steps, every step on the whole batch; sampled heads against the oracle,
