@@ -24,6 +24,8 @@ Modules:
   chunkwise   the chunkwise (triangular-system) form in fp64, to pin the
               chunk equations against the recurrence
   kalman      textbook dense Kalman filter and ridge regression (pins)
+  backward    gradients of the recurrence by a reverse sweep (training's
+              backpropagation through the same recurrence)
 
 Every function here has a pin in tests/ (worked examples printed on the
 pages, closed forms, invariants, library special cases); none is
