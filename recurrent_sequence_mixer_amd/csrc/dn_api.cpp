@@ -618,3 +618,185 @@ DN_EXPORT int dn_chunk_fwd_noalloc(const dn_desc* d, const void* q, const void* 
   if (need > 0 && !(ws = scratch_address())) return DN_ERR_HIP;
   return dn_chunk_fwd(d, q, k, v, g, S0, aux0, o, S_final, aux_final, ws, need, stream);
 }
+
+// ---------------------------------------------------------------------------
+// Chunked backward.  Workspace, fp32, each part on a 256-byte boundary: w
+// [B, H, T, dk], S_ck [B, H, nch, dk, dv], E [B, H, T, dv], dw_acc
+// [B, H, T, dk], dG [B, H, T], then for PGDN aux_chunk [B, H, nch, dk].
+struct BwdLayout {
+  size_t w, sck, e, dw, dg, aux, total;
+};
+
+static BwdLayout bwd_layout(const dn_desc* d) {
+  BwdLayout L{};
+  const size_t bh = static_cast<size_t>(d->B) * d->H, bht = bh * d->T;
+  const size_t nch = (static_cast<size_t>(d->T) + d->C - 1) / d->C;
+  L.w = 0;
+  L.sck = round256(L.w + bht * d->dk * 4);
+  L.e = round256(L.sck + bh * nch * d->dk * d->dv * 4);
+  L.dw = round256(L.e + bht * d->dv * 4);
+  L.dg = round256(L.dw + bht * d->dk * 4);
+  L.aux = round256(L.dg + bht * 4);
+  L.total = L.aux + (d->gain == DN_GAIN_PGDN ? bh * nch * d->dk * 4 : 0);
+  return L;
+}
+
+static int bwd_supported(const dn_desc* d) {
+  if (d->decay != DN_DECAY_SCALAR) return DN_ERR_UNSUPPORTED;
+  if (d->gain != DN_GAIN_KLA && d->gain != DN_GAIN_GDN && d->gain != DN_GAIN_PGDN &&
+      d->gain != DN_GAIN_EXPLICIT)
+    return DN_ERR_UNSUPPORTED;
+  if (d->io == DN_F32 && d->dk != 64) return DN_ERR_UNSUPPORTED;
+  return DN_OK;
+}
+
+DN_EXPORT size_t dn_chunk_bwd_workspace(const dn_desc* d) {
+  if (check_desc(d, true) != DN_OK || bwd_supported(d) != DN_OK) return 0;
+  return bwd_layout(d).total;
+}
+
+DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const void* v,
+                           const dn_gates* g, const float* S0, const float* aux0, const void* dO,
+                           const float* dS_T, const float* daux_T, const dn_grads* gr, void* ws,
+                           size_t ws_bytes, void* stream) {
+  int st = check_desc(d, true);
+  if (st != DN_OK) return st;
+  if ((st = bwd_supported(d)) != DN_OK) return st;
+  if (!gr) return DN_ERR_NULL;
+  const bool pg = d->gain == DN_GAIN_PGDN;
+  if (d->T > 0) {
+    if ((st = check_gates(d, g)) != DN_OK) return st;
+    if (!q || !k || !v || !dO || !gr->dq || !gr->dk || !gr->dv || !gr->dalpha) return DN_ERR_NULL;
+    if (d->gain != DN_GAIN_EXPLICIT && !gr->deta) return DN_ERR_NULL;
+    if (pg && (!gr->dalphaP || !gr->dbetaP || !gr->dmu_log)) return DN_ERR_NULL;
+    if (d->gain == DN_GAIN_EXPLICIT && !gr->dw) return DN_ERR_NULL;
+  }
+  const BwdLayout lay = bwd_layout(d);
+  if (d->T > 0 && (!ws || ws_bytes < lay.total)) return DN_ERR_WORKSPACE;
+
+  const size_t bh = static_cast<size_t>(d->B) * d->H, bht = bh * d->T;
+  const size_t es = io_size(d->io);
+  const size_t sbytes = bh * d->dk * d->dv * 4;
+  Range in[20];
+  const dn_gates nog{};
+  int n = gate_ranges(d, g ? g : &nog, in);
+  in[n++] = {q, bht * d->dk * es};
+  in[n++] = {k, bht * d->dk * es};
+  in[n++] = {v, bht * d->dv * es};
+  in[n++] = {dO, bht * d->dv * es};
+  in[n++] = {S0, S0 ? sbytes : 0};
+  in[n++] = {pg ? aux0 : nullptr, bh * d->dk * 4};
+  in[n++] = {dS_T, dS_T ? sbytes : 0};
+  in[n++] = {pg ? daux_T : nullptr, bh * d->dk * 4};
+  const Range outs[12] = {{gr->dq, bht * d->dk * 4},
+                          {gr->dk, bht * d->dk * 4},
+                          {gr->dv, bht * d->dv * 4},
+                          {gr->dalpha, bht * 4},
+                          {d->gain != DN_GAIN_EXPLICIT ? gr->deta : nullptr, bht * 4},
+                          {pg ? gr->dalphaP : nullptr, bht * 4},
+                          {pg ? gr->dbetaP : nullptr, bht * 4},
+                          {pg ? gr->dmu_log : nullptr, static_cast<size_t>(d->H) * 4},
+                          {d->gain == DN_GAIN_EXPLICIT ? gr->dw : nullptr, bht * d->dk * 4},
+                          {gr->dS0, gr->dS0 ? sbytes : 0},
+                          {pg ? gr->daux0 : nullptr, bh * d->dk * 4},
+                          {d->T > 0 ? ws : nullptr, lay.total}};
+  for (int j = 0; j < 12; ++j) {
+    for (int i = 0; i < n; ++i)
+      if (overlap(outs[j], in[i])) return DN_ERR_ALIAS;
+    for (int i = j + 1; i < 12; ++i)
+      if (overlap(outs[j], outs[i])) return DN_ERR_ALIAS;
+  }
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->T == 0) {
+    // no token: dS0 = dS_T, dA_0 = daux_T
+    if (gr->dS0) {
+      if (dS_T) {
+        if (hipMemcpyAsync(gr->dS0, dS_T, sbytes, hipMemcpyDeviceToDevice, s) != hipSuccess) return DN_ERR_HIP;
+      } else if (dn::launch_zero(gr->dS0, sbytes / 4, s) != hipSuccess) {
+        return DN_ERR_HIP;
+      }
+    }
+    if (pg && gr->daux0) {
+      if (daux_T) {
+        if (hipMemcpyAsync(gr->daux0, daux_T, bh * d->dk * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+          return DN_ERR_HIP;
+      } else if (dn::launch_zero(gr->daux0, bh * d->dk, s) != hipSuccess) {
+        return DN_ERR_HIP;
+      }
+    }
+    if (pg && gr->dmu_log && dn::launch_zero(gr->dmu_log, d->H, s) != hipSuccess) return DN_ERR_HIP;
+    return DN_OK;
+  }
+  char* wb = static_cast<char*>(ws);
+  float* w_ws = reinterpret_cast<float*>(wb + lay.w);
+  float* dw_acc = reinterpret_cast<float*>(wb + lay.dw);
+  float* dG = reinterpret_cast<float*>(wb + lay.dg);
+  float* aux_chunk = pg ? reinterpret_cast<float*>(wb + lay.aux) : nullptr;
+  // the accumulated gradients start at zero
+  if (dn::launch_zero(gr->dq, bht * d->dk, s) != hipSuccess ||
+      dn::launch_zero(gr->dk, bht * d->dk, s) != hipSuccess ||
+      dn::launch_zero(dw_acc, bht * d->dk, s) != hipSuccess || dn::launch_zero(dG, bht, s) != hipSuccess ||
+      (pg && dn::launch_zero(gr->dmu_log, d->H, s) != hipSuccess))
+    return DN_ERR_HIP;
+  const dn::GateArgs ga = gate_args(d, g);
+  // the write vectors (and PGDN's statistic entering every chunk)
+  dn::GainPrepArgs gp;
+  gp.B = d->B;
+  gp.H = d->H;
+  gp.T = d->T;
+  gp.dk = d->dk;
+  gp.k = k;
+  gp.g = ga;
+  gp.aux0 = pg ? aux0 : nullptr;
+  gp.w_out = w_ws;
+  gp.g_out = nullptr;
+  gp.aux_chunk = aux_chunk;
+  gp.aux_final = nullptr;
+  if (dn::launch_gain_prep(gp, d->io == DN_BF16, d->gain, false, s) != hipSuccess) return DN_ERR_HIP;
+  // the memory recurrence backwards, chunk by chunk
+  dn::BwdArgs b;
+  b.B = d->B;
+  b.H = d->H;
+  b.T = d->T;
+  b.dk = d->dk;
+  b.dv = d->dv;
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.g = ga;
+  b.w = w_ws;
+  b.S0 = S0;
+  b.dO = dO;
+  b.dS_T = dS_T;
+  b.S_ck = reinterpret_cast<float*>(wb + lay.sck);
+  b.E = reinterpret_cast<float*>(wb + lay.e);
+  b.dq_out = gr->dq;
+  b.dk_out = gr->dk;
+  b.dv_out = gr->dv;
+  b.dw_acc = dw_acc;
+  b.dG = dG;
+  b.dS0 = gr->dS0;
+  if (dn::launch_chunk_bwd_state(b, d->io == DN_BF16, s) != hipSuccess) return DN_ERR_HIP;
+  // the write gains and the decay backwards
+  dn::GainBwdArgs gb;
+  gb.B = d->B;
+  gb.H = d->H;
+  gb.T = d->T;
+  gb.dk = d->dk;
+  gb.k = k;
+  gb.g = ga;
+  gb.aux_chunk = aux_chunk;
+  gb.daux_T = pg ? daux_T : nullptr;
+  gb.dw_acc = dw_acc;
+  gb.dG = dG;
+  gb.dk_out = gr->dk;
+  gb.dalpha = gr->dalpha;
+  gb.deta = d->gain != DN_GAIN_EXPLICIT ? gr->deta : nullptr;
+  gb.dalphaP = pg ? gr->dalphaP : nullptr;
+  gb.dbetaP = pg ? gr->dbetaP : nullptr;
+  gb.dmu_log = pg ? gr->dmu_log : nullptr;
+  gb.dw_out = d->gain == DN_GAIN_EXPLICIT ? gr->dw : nullptr;
+  gb.daux0 = pg ? gr->daux0 : nullptr;
+  return hip_status(dn::launch_gain_bwd(gb, d->io == DN_BF16, d->gain, s));
+}

@@ -97,6 +97,55 @@ struct GainPrepArgs {
   float* aux_final;  // nullable
 };
 
+// Chunked backward (chunk_bwd.hip), scalar decay.  Inputs as ChunkArgs, the
+// write vectors w [B, H, T, dk] fp32 from the gain scan, and the cotangents
+// dO [B, H, T, dv] (io dtype), dS_T [B, H, dk, dv] and daux_T (nullable).
+// Gradients are fp32: dq, dk, dw_acc [B, H, T, dk] and dG [B, H, T] are
+// accumulated over value slices and must start at zero; dv [B, H, T, dv] and
+// dS0 (nullable) are written.  Workspace: the state entering every chunk
+// S_ck [B, H, nch, dk, dv] and the residuals E [B, H, T, dv].
+struct BwdArgs {
+  int B, H, T, dk, dv;
+  const void *q, *k, *v;
+  GateArgs g;
+  const float* w;  // [B, H, T, dk] fp32
+  const float* S0;
+  const void* dO;
+  const float* dS_T;
+  float* S_ck;
+  float* E;
+  float* dq_out;
+  float* dk_out;
+  float* dv_out;
+  float* dw_acc;
+  float* dG;
+  float* dS0;
+};
+hipError_t launch_chunk_bwd_state(const BwdArgs& a, int io_bf16, hipStream_t st);
+
+// Back through the gains (chunk_bwd.hip), one workgroup per (b, h): adds the
+// gain's part to dk and forms the gates' gradients from dw_acc and dG.
+struct GainBwdArgs {
+  int B, H, T, dk;
+  const void* k;
+  GateArgs g;
+  const float* aux_chunk;  // PGDN: A entering every chunk [B, H, nch, dk]
+  const float* daux_T;     // nullable
+  const float* dw_acc;
+  const float* dG;
+  float* dk_out;           // holds the state part on entry
+  float* dalpha;
+  float* deta;
+  float* dalphaP;
+  float* dbetaP;
+  float* dmu_log;          // [H], accumulated over batch rows (starts at zero)
+  float* dw_out;           // explicit w
+  float* daux0;            // nullable
+};
+hipError_t launch_gain_bwd(const GainBwdArgs& a, int io_bf16, int gain, hipStream_t st);
+// Zero n floats (a plain fill kernel, so that callers may capture it).
+hipError_t launch_zero(float* p, size_t n, hipStream_t st);
+
 hipError_t launch_decode(const DecodeArgs& a, int io_bf16, int gain, bool channel, hipStream_t st);
 hipError_t launch_chunk_fwd(const ChunkArgs& a, int io_bf16, int gain, bool channel,
                             hipStream_t st);

@@ -24,7 +24,7 @@ IO = {torch.float32: 0, torch.bfloat16: 1}
 # Symbols declared in include/dn.h.
 EXPORTS = ("dn_chunk_fwd", "dn_chunk_fwd_long", "dn_chunk_fwd_long_workspace", "dn_decode_step",
            "dn_gain_prep", "dn_status_string", "dn_version", "dn_workspace_bytes",
-           "dn_chunk_fwd_noalloc")
+           "dn_chunk_fwd_noalloc", "dn_chunk_bwd", "dn_chunk_bwd_workspace")
 
 
 class DnDesc(ctypes.Structure):
@@ -37,6 +37,12 @@ class DnDesc(ctypes.Structure):
 class DnGates(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("alpha", "eta", "alphaP", "betaP", "mu_log", "omega", "r", "w")]
+
+
+class DnGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dq", "dk", "dv", "dalpha", "deta", "dalphaP", "dbetaP", "dmu_log", "dw", "dS0",
+                 "daux0")]
 
 
 class DnError(RuntimeError):
@@ -76,6 +82,11 @@ def lib() -> ctypes.CDLL:
         L.dn_gain_prep.argtypes = [ctypes.POINTER(DnDesc), vp, ctypes.POINTER(DnGates), vp,
                                    vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.dn_gain_prep.restype = ip
+        L.dn_chunk_bwd_workspace.argtypes = [ctypes.POINTER(DnDesc)]
+        L.dn_chunk_bwd_workspace.restype = ctypes.c_size_t
+        L.dn_chunk_bwd.argtypes = [ctypes.POINTER(DnDesc), vp, vp, vp, ctypes.POINTER(DnGates), vp, vp,
+                                   vp, vp, vp, ctypes.POINTER(DnGrads), vp, ctypes.c_size_t, vp]
+        L.dn_chunk_bwd.restype = ip
         L.dn_status_string.argtypes = [ip]
         L.dn_status_string.restype = ctypes.c_char_p
         L.dn_version.argtypes = []
@@ -240,6 +251,41 @@ def gain_prep(k, gates: Dict[str, torch.Tensor], *, gain="kla", decay=None, eps=
                             _stream(stream))
     _check(st, "dn_gain_prep")
     return w, g, aux_chunk, aux_final
+
+
+def chunk_bwd(q, k, v, gates: Dict[str, torch.Tensor], dO, *, gain="kla", decay=None, eps=1e-6,
+              x=1.5, mu_info=1.0, S0=None, aux0=None, dS_T=None, daux_T=None, workspace=None,
+              stream=None) -> Dict[str, Optional[torch.Tensor]]:
+    """Chunked backward (dn_chunk_bwd): the gradients of
+    sum <dO, o> + <dS_T, S_T> + <daux_T, aux_T> with respect to the inputs of
+    chunk_fwd, as fp32 tensors in a dict (q, k, v, alpha, S0 and the gain's
+    gates; aux0 for PGDN)."""
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    if decay is None:
+        decay = "channel" if gates["alpha"].dim() == 4 else "scalar"
+    desc = make_desc(B, H, T, dk, dv, q.dtype, gain, decay, eps, x, mu_info)
+    dev = v.device
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    g = {"q": f32(B, H, T, dk), "k": f32(B, H, T, dk), "v": f32(B, H, T, dv),
+         "alpha": f32(*gates["alpha"].shape), "S0": f32(B, H, dk, dv)}
+    if gain in ("kla", "gdn", "pgdn"):
+        g["eta"] = f32(B, H, T)
+    if gain == "pgdn":
+        g |= {"alphaP": f32(B, H, T), "betaP": f32(B, H, T), "mu_log": f32(H), "aux0": f32(B, H, dk)}
+    if gain == "explicit":
+        g["w"] = f32(B, H, T, dk)
+    grads = DnGrads(_ptr(g["q"]), _ptr(g["k"]), _ptr(g["v"]), _ptr(g["alpha"]), _ptr(g.get("eta")),
+                    _ptr(g.get("alphaP")), _ptr(g.get("betaP")), _ptr(g.get("mu_log")), _ptr(g.get("w")),
+                    _ptr(g["S0"]), _ptr(g.get("aux0")))
+    nbytes = lib().dn_chunk_bwd_workspace(ctypes.byref(desc))
+    ws, nbytes = _workspace(nbytes, dev, workspace)
+    gt = make_gates(gates)
+    st = lib().dn_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(gt), _ptr(S0),
+                            _ptr(aux0), _ptr(dO), _ptr(dS_T), _ptr(daux_T), ctypes.byref(grads), ws,
+                            nbytes, _stream(stream))
+    _check(st, "dn_chunk_bwd")
+    return g
 
 
 def to_device(arrays, io_dtype: torch.dtype, device="cuda"):

@@ -251,6 +251,41 @@ def test_noalloc_rejects_workspace_beyond_scratch():
     assert call(_desc(dk=96)) == -2
 
 
+def test_chunk_bwd_rejects_bad_arguments():
+    """dn_chunk_bwd: unsupported combinations, missing pointers and
+    gradients, the workspace, and overlaps are refused before any launch."""
+    L = dn.lib()
+    q, k, v, dO = FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30), FAKE + (5 << 30)
+    outs = [FAKE + ((10 + i) << 30) for i in range(11)]
+    ws = FAKE + (30 << 30)
+
+    def call(desc, gates=None, grads=None, ws_=ws, nbytes=None):
+        gates = gates or _gates()
+        grads = grads or dn.DnGrads(*outs)
+        if nbytes is None:
+            nbytes = L.dn_chunk_bwd_workspace(ctypes.byref(desc))
+        return L.dn_chunk_bwd(ctypes.byref(desc), q, k, v, ctypes.byref(gates), None, None, dO, None, None,
+                              ctypes.byref(grads), ws_, nbytes, None)
+    d = _desc(B=2, H=3, T=100)
+    assert call(_desc(decay="channel")) == -6
+    assert call(_desc(gain="kdn")) == -6
+    assert call(_desc(io=0, dk=128)) == -6
+    assert L.dn_chunk_bwd_workspace(ctypes.byref(_desc(gain="kdn"))) == 0
+    assert call(d, grads=dn.DnGrads(None, *outs[1:])) == -1  # dq missing
+    assert call(_desc(gain="pgdn")) == -1  # PGDN gates missing
+    assert call(d, ws_=None) == -5
+    assert call(d, nbytes=1024) == -5
+    assert call(d, grads=dn.DnGrads(q, *outs[1:])) == -8  # dq on top of q
+    assert call(d, ws_=outs[0]) == -8  # workspace on top of dq
+    # the workspace: w, S_ck, E, dw, dG (each on a 256-byte boundary)
+    r256 = lambda x: (x + 255) // 256 * 256
+    bht, nch = 2 * 3 * 100, 2
+    size = r256(r256(r256(r256(bht * 128 * 4) + 6 * nch * 128 * 128 * 4) + bht * 128 * 4) + bht * 128 * 4) + bht * 4
+    assert L.dn_chunk_bwd_workspace(ctypes.byref(d)) == r256(size)
+    dp = _desc(B=2, H=3, T=100, gain="pgdn")
+    assert L.dn_chunk_bwd_workspace(ctypes.byref(dp)) == r256(size) + 6 * nch * 128 * 4
+
+
 def test_bench_refuses_more_than_one_gpu():
     """bench.py runs on one GPU; --gpus N > 1 exits with a message before any GPU work."""
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
