@@ -289,14 +289,17 @@ typedef struct dn_grads {
   float* dq;      /* [B, H, T, dk]                                  */
   float* dk;      /* [B, H, T, dk] (through the residual and the gain) */
   float* dv;      /* [B, H, T, dv]                                  */
-  float* dalpha;  /* [B, H, T] (scalar decay)                       */
+  float* dalpha;  /* [B, H, T] (scalar decay), [B, H, T, dk] (channel) */
   float* deta;    /* KLA, GDN, PGDN: [B, H, T]                      */
   float* dalphaP; /* PGDN: [B, H, T]                                */
   float* dbetaP;  /* PGDN: [B, H, T]                                */
   float* dmu_log; /* PGDN: [H], summed over the batch rows          */
   float* dw;      /* EXPLICIT: [B, H, T, dk]                        */
   float* dS0;     /* [B, H, dk, dv], nullable                       */
-  float* daux0;   /* PGDN: dL/dA_0 [B, H, dk], nullable             */
+  float* daux0;   /* PGDN dL/dA_0, KDN dL/dp_0 [B, H, dk]; KDN_ISO dL/db_0
+                     [B, H]; nullable                               */
+  float* domega;  /* KDN: [B, H, T, dk]; KDN_ISO: [B, H, T]         */
+  float* dr;      /* KDN, KDN_ISO: [B, H, T]                        */
 } dn_grads;
 
 /* Chunked backward.  Per chunk of C tokens it evaluates the derivative of
@@ -305,28 +308,35 @@ typedef struct dn_grads {
  * S_in + M E and S_out = g_n S_in + W~^T E, the chunk takes dO and dS_out
  * and gives dE = M^T dO + W~ dS_out, dR from (I + L)^T dR = dE, dV = dR,
  * dS_in = g_n dS_out + (gQ)^T dO - (gK)^T dR, dL = -dR E^T, dM = dO E^T, and
- * from them the gradients of k, q, w and the decay; the chunks are walked
- * from the last, after a forward sweep that keeps the state entering each
- * chunk.  The write gain is then differentiated token by token backwards
- * (KLA, GDN: Kaczmarz Linear Attention §2.1; PGDN: Preconditioned DeltaNet
- * §2.4, Eq. 9, through the statistic A_t, its centre mu and its gates).
- *   Built for scalar decay (DN_DECAY_SCALAR) and the gains KLA, GDN, PGDN and
- *   EXPLICIT, io bf16 (dk 64 or 128) or fp32 (dk 64); other combinations
- *   return DN_ERR_UNSUPPORTED.  Results equal the gradients of the token
- *   recurrence up to rounding (fp32 arithmetic; k, q and w enter the
- *   products in the io dtype).
- *   q, k, v, gates, S0 (nullable: zeros), aux0 (PGDN A_0, nullable: ones):
- *   as for dn_chunk_fwd.  dO [B, H, T, dv] io dtype; dS_T [B, H, dk, dv] and
- *   daux_T [B, H, dk] fp32, nullable (zero).
+ * from them the gradients of k, q, w and the decay (per key channel for
+ * channel decay, the decay then applied inside the products); the chunks are
+ * walked from the last, after a forward sweep that keeps the state entering
+ * each chunk.  The write gain is then differentiated token by token
+ * backwards (KLA, GDN: Kaczmarz Linear Attention §2.1; PGDN: Preconditioned
+ * DeltaNet §2.4, Eq. 9, through the statistic A_t, its centre mu and its
+ * gates; KDN: Kalman Delta Networks §2.4, Eqs. 23-30 and §2.5, through the
+ * variance p_t, omega and r; KDN_ISO: §2.7, Eq. 40 - the gain scan of
+ * Appendix D run backwards).
+ *   Every gain and both decays; io bf16 (dk 64 or 128) or fp32 (dk 64);
+ *   other shapes return DN_ERR_UNSUPPORTED.  Results equal the gradients of
+ *   the token recurrence up to rounding (fp32 arithmetic; k, q and w enter
+ *   the products in the io dtype, with channel decay scaled by their decay
+ *   relative to the chunk's token 31 first).  Channel decay has the range of
+ *   the chunked forward (RANGE OF CHANNEL DECAY): beyond it the gradients
+ *   of the head are NaN.
+ *   q, k, v, gates, S0 (nullable: zeros), aux0 (nullable: ones): as for
+ *   dn_chunk_fwd.  dO [B, H, T, dv] io dtype; dS_T [B, H, dk, dv] and
+ *   daux_T (PGDN / KDN [B, H, dk], KDN_ISO [B, H]) fp32, nullable (zero).
  *   ws: device workspace of at least dn_chunk_bwd_workspace(desc) bytes
  *   (fp32: the write vectors [B, H, T, dk], the state entering every chunk
  *   [B, H, ceil(T/C), dk, dv], the residuals [B, H, T, dv], the write vectors'
- *   gradient [B, H, T, dk], the decay's per token [B, H, T] and for PGDN the
- *   statistic entering every chunk [B, H, ceil(T/C), dk]; 1.3 GB at
- *   B8 H16 T4096 d128).  No gradient buffer may overlap an input, another
- *   gradient or the workspace (DN_ERR_ALIAS).  dmu_log is summed over the
- *   batch rows with atomic additions: its last bits may vary from run to
- *   run, as may those of dq, dk and dw (summed over value-column slices). */
+ *   gradient [B, H, T, dk], the decay's per token ([B, H, T], channel decay
+ *   [B, H, T, dk]) and for the gains with a statistic the statistic entering
+ *   every chunk; 1.3 GB at B8 H16 T4096 d128, scalar decay).  No gradient
+ *   buffer may overlap an input, another gradient or the workspace
+ *   (DN_ERR_ALIAS).  dmu_log is summed over the batch rows with atomic
+ *   additions: its last bits may vary from run to run, as may those of dq,
+ *   dk, dw and dalpha (summed over value-column slices). */
 size_t dn_chunk_bwd_workspace(const dn_desc* desc);
 int dn_chunk_bwd(const dn_desc* desc, const void* q, const void* k, const void* v,
                  const dn_gates* gates, const float* S0, const float* aux0, const void* dO,

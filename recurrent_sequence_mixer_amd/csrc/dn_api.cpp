@@ -622,7 +622,9 @@ DN_EXPORT int dn_chunk_fwd_noalloc(const dn_desc* d, const void* q, const void* 
 // ---------------------------------------------------------------------------
 // Chunked backward.  Workspace, fp32, each part on a 256-byte boundary: w
 // [B, H, T, dk], S_ck [B, H, nch, dk, dv], E [B, H, T, dv], dw_acc
-// [B, H, T, dk], dG [B, H, T], then for PGDN aux_chunk [B, H, nch, dk].
+// [B, H, T, dk], dG ([B, H, T]; channel decay [B, H, T, dk]), then for the
+// gains with a statistic the statistic entering every chunk ([B, H, nch, dk];
+// KDN_ISO [B, H, nch]).
 struct BwdLayout {
   size_t w, sck, e, dw, dg, aux, total;
 };
@@ -631,22 +633,22 @@ static BwdLayout bwd_layout(const dn_desc* d) {
   BwdLayout L{};
   const size_t bh = static_cast<size_t>(d->B) * d->H, bht = bh * d->T;
   const size_t nch = (static_cast<size_t>(d->T) + d->C - 1) / d->C;
+  const size_t gdim = d->decay == DN_DECAY_CHANNEL ? d->dk : 1;
   L.w = 0;
   L.sck = round256(L.w + bht * d->dk * 4);
   L.e = round256(L.sck + bh * nch * d->dk * d->dv * 4);
   L.dw = round256(L.e + bht * d->dv * 4);
   L.dg = round256(L.dw + bht * d->dk * 4);
-  L.aux = round256(L.dg + bht * 4);
-  L.total = L.aux + (d->gain == DN_GAIN_PGDN ? bh * nch * d->dk * 4 : 0);
+  L.aux = round256(L.dg + bht * gdim * 4);
+  L.total = L.aux + (has_aux_state(d) ? bh * nch * aux_per_head(d) * 4 : 0);
   return L;
 }
 
+// every gain and decay; io bf16 with dk 64 or 128, fp32 with dk 64; dv a
+// multiple of the value slice (16 columns with channel decay, 32 with scalar)
 static int bwd_supported(const dn_desc* d) {
-  if (d->decay != DN_DECAY_SCALAR) return DN_ERR_UNSUPPORTED;
-  if (d->gain != DN_GAIN_KLA && d->gain != DN_GAIN_GDN && d->gain != DN_GAIN_PGDN &&
-      d->gain != DN_GAIN_EXPLICIT)
-    return DN_ERR_UNSUPPORTED;
   if (d->io == DN_F32 && d->dk != 64) return DN_ERR_UNSUPPORTED;
+  if (d->dv % (d->decay == DN_DECAY_CHANNEL ? 16 : 32) != 0) return DN_ERR_UNSUPPORTED;
   return DN_OK;
 }
 
@@ -664,11 +666,16 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
   if ((st = bwd_supported(d)) != DN_OK) return st;
   if (!gr) return DN_ERR_NULL;
   const bool pg = d->gain == DN_GAIN_PGDN;
+  const bool kd = d->gain == DN_GAIN_KDN || d->gain == DN_GAIN_KDN_ISO;
+  const bool has_aux = has_aux_state(d);
+  const bool has_eta = d->gain == DN_GAIN_KLA || d->gain == DN_GAIN_GDN || pg;
+  const bool chan = d->decay == DN_DECAY_CHANNEL;
   if (d->T > 0) {
     if ((st = check_gates(d, g)) != DN_OK) return st;
     if (!q || !k || !v || !dO || !gr->dq || !gr->dk || !gr->dv || !gr->dalpha) return DN_ERR_NULL;
-    if (d->gain != DN_GAIN_EXPLICIT && !gr->deta) return DN_ERR_NULL;
+    if (has_eta && !gr->deta) return DN_ERR_NULL;
     if (pg && (!gr->dalphaP || !gr->dbetaP || !gr->dmu_log)) return DN_ERR_NULL;
+    if (kd && (!gr->domega || !gr->dr)) return DN_ERR_NULL;
     if (d->gain == DN_GAIN_EXPLICIT && !gr->dw) return DN_ERR_NULL;
   }
   const BwdLayout lay = bwd_layout(d);
@@ -677,6 +684,7 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
   const size_t bh = static_cast<size_t>(d->B) * d->H, bht = bh * d->T;
   const size_t es = io_size(d->io);
   const size_t sbytes = bh * d->dk * d->dv * 4;
+  const size_t abytes = has_aux ? bh * aux_per_head(d) * 4 : 0;
   Range in[20];
   const dn_gates nog{};
   int n = gate_ranges(d, g ? g : &nog, in);
@@ -685,25 +693,29 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
   in[n++] = {v, bht * d->dv * es};
   in[n++] = {dO, bht * d->dv * es};
   in[n++] = {S0, S0 ? sbytes : 0};
-  in[n++] = {pg ? aux0 : nullptr, bh * d->dk * 4};
+  in[n++] = {has_aux ? aux0 : nullptr, abytes};
   in[n++] = {dS_T, dS_T ? sbytes : 0};
-  in[n++] = {pg ? daux_T : nullptr, bh * d->dk * 4};
-  const Range outs[12] = {{gr->dq, bht * d->dk * 4},
-                          {gr->dk, bht * d->dk * 4},
-                          {gr->dv, bht * d->dv * 4},
-                          {gr->dalpha, bht * 4},
-                          {d->gain != DN_GAIN_EXPLICIT ? gr->deta : nullptr, bht * 4},
-                          {pg ? gr->dalphaP : nullptr, bht * 4},
-                          {pg ? gr->dbetaP : nullptr, bht * 4},
-                          {pg ? gr->dmu_log : nullptr, static_cast<size_t>(d->H) * 4},
-                          {d->gain == DN_GAIN_EXPLICIT ? gr->dw : nullptr, bht * d->dk * 4},
-                          {gr->dS0, gr->dS0 ? sbytes : 0},
-                          {pg ? gr->daux0 : nullptr, bh * d->dk * 4},
-                          {d->T > 0 ? ws : nullptr, lay.total}};
-  for (int j = 0; j < 12; ++j) {
+  in[n++] = {has_aux ? daux_T : nullptr, abytes};
+  const size_t omega_bytes = d->gain == DN_GAIN_KDN_ISO ? bht * 4 : bht * d->dk * 4;
+  constexpr int NOUT = 14;
+  const Range outs[NOUT] = {{gr->dq, bht * d->dk * 4},
+                            {gr->dk, bht * d->dk * 4},
+                            {gr->dv, bht * d->dv * 4},
+                            {gr->dalpha, bht * (chan ? d->dk : 1) * 4},
+                            {has_eta ? gr->deta : nullptr, bht * 4},
+                            {pg ? gr->dalphaP : nullptr, bht * 4},
+                            {pg ? gr->dbetaP : nullptr, bht * 4},
+                            {pg ? gr->dmu_log : nullptr, static_cast<size_t>(d->H) * 4},
+                            {d->gain == DN_GAIN_EXPLICIT ? gr->dw : nullptr, bht * d->dk * 4},
+                            {gr->dS0, gr->dS0 ? sbytes : 0},
+                            {has_aux ? gr->daux0 : nullptr, abytes},
+                            {kd ? gr->domega : nullptr, omega_bytes},
+                            {kd ? gr->dr : nullptr, bht * 4},
+                            {d->T > 0 ? ws : nullptr, lay.total}};
+  for (int j = 0; j < NOUT; ++j) {
     for (int i = 0; i < n; ++i)
       if (overlap(outs[j], in[i])) return DN_ERR_ALIAS;
-    for (int i = j + 1; i < 12; ++i)
+    for (int i = j + 1; i < NOUT; ++i)
       if (overlap(outs[j], outs[i])) return DN_ERR_ALIAS;
   }
 
@@ -717,11 +729,11 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
         return DN_ERR_HIP;
       }
     }
-    if (pg && gr->daux0) {
+    if (has_aux && gr->daux0) {
       if (daux_T) {
-        if (hipMemcpyAsync(gr->daux0, daux_T, bh * d->dk * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        if (hipMemcpyAsync(gr->daux0, daux_T, abytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
           return DN_ERR_HIP;
-      } else if (dn::launch_zero(gr->daux0, bh * d->dk, s) != hipSuccess) {
+      } else if (dn::launch_zero(gr->daux0, abytes / 4, s) != hipSuccess) {
         return DN_ERR_HIP;
       }
     }
@@ -732,11 +744,12 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
   float* w_ws = reinterpret_cast<float*>(wb + lay.w);
   float* dw_acc = reinterpret_cast<float*>(wb + lay.dw);
   float* dG = reinterpret_cast<float*>(wb + lay.dg);
-  float* aux_chunk = pg ? reinterpret_cast<float*>(wb + lay.aux) : nullptr;
+  float* aux_chunk = has_aux ? reinterpret_cast<float*>(wb + lay.aux) : nullptr;
   // the accumulated gradients start at zero
   if (dn::launch_zero(gr->dq, bht * d->dk, s) != hipSuccess ||
       dn::launch_zero(gr->dk, bht * d->dk, s) != hipSuccess ||
-      dn::launch_zero(dw_acc, bht * d->dk, s) != hipSuccess || dn::launch_zero(dG, bht, s) != hipSuccess ||
+      dn::launch_zero(dw_acc, bht * d->dk, s) != hipSuccess ||
+      dn::launch_zero(dG, bht * (chan ? d->dk : 1), s) != hipSuccess ||
       (pg && dn::launch_zero(gr->dmu_log, d->H, s) != hipSuccess))
     return DN_ERR_HIP;
   const dn::GateArgs ga = gate_args(d, g);
@@ -748,12 +761,12 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
   gp.dk = d->dk;
   gp.k = k;
   gp.g = ga;
-  gp.aux0 = pg ? aux0 : nullptr;
+  gp.aux0 = has_aux ? aux0 : nullptr;
   gp.w_out = w_ws;
   gp.g_out = nullptr;
   gp.aux_chunk = aux_chunk;
   gp.aux_final = nullptr;
-  if (dn::launch_gain_prep(gp, d->io == DN_BF16, d->gain, false, s) != hipSuccess) return DN_ERR_HIP;
+  if (dn::launch_gain_prep(gp, d->io == DN_BF16, d->gain, chan, s) != hipSuccess) return DN_ERR_HIP;
   // the memory recurrence backwards, chunk by chunk
   dn::BwdArgs b;
   b.B = d->B;
@@ -777,7 +790,7 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
   b.dw_acc = dw_acc;
   b.dG = dG;
   b.dS0 = gr->dS0;
-  if (dn::launch_chunk_bwd_state(b, d->io == DN_BF16, s) != hipSuccess) return DN_ERR_HIP;
+  if (dn::launch_chunk_bwd_state(b, d->io == DN_BF16, chan, s) != hipSuccess) return DN_ERR_HIP;
   // the write gains and the decay backwards
   dn::GainBwdArgs gb;
   gb.B = d->B;
@@ -787,16 +800,18 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
   gb.k = k;
   gb.g = ga;
   gb.aux_chunk = aux_chunk;
-  gb.daux_T = pg ? daux_T : nullptr;
+  gb.daux_T = has_aux ? daux_T : nullptr;
   gb.dw_acc = dw_acc;
   gb.dG = dG;
   gb.dk_out = gr->dk;
   gb.dalpha = gr->dalpha;
-  gb.deta = d->gain != DN_GAIN_EXPLICIT ? gr->deta : nullptr;
+  gb.deta = has_eta ? gr->deta : nullptr;
   gb.dalphaP = pg ? gr->dalphaP : nullptr;
   gb.dbetaP = pg ? gr->dbetaP : nullptr;
   gb.dmu_log = pg ? gr->dmu_log : nullptr;
   gb.dw_out = d->gain == DN_GAIN_EXPLICIT ? gr->dw : nullptr;
-  gb.daux0 = pg ? gr->daux0 : nullptr;
-  return hip_status(dn::launch_gain_bwd(gb, d->io == DN_BF16, d->gain, s));
+  gb.domega = kd ? gr->domega : nullptr;
+  gb.dr = kd ? gr->dr : nullptr;
+  gb.daux0 = has_aux ? gr->daux0 : nullptr;
+  return hip_status(dn::launch_gain_bwd(gb, d->io == DN_BF16, d->gain, chan, s));
 }

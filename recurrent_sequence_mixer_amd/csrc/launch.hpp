@@ -97,12 +97,12 @@ struct GainPrepArgs {
   float* aux_final;  // nullable
 };
 
-// Chunked backward (chunk_bwd.hip), scalar decay.  Inputs as ChunkArgs, the
-// write vectors w [B, H, T, dk] fp32 from the gain scan, and the cotangents
-// dO [B, H, T, dv] (io dtype), dS_T [B, H, dk, dv] and daux_T (nullable).
-// Gradients are fp32: dq, dk, dw_acc [B, H, T, dk] and dG [B, H, T] are
-// accumulated over value slices and must start at zero; dv [B, H, T, dv] and
-// dS0 (nullable) are written.  Workspace: the state entering every chunk
+// Chunked backward (chunk_bwd.hip).  Inputs as ChunkArgs, the write vectors
+// w [B, H, T, dk] fp32 from the gain scan, and the cotangents dO [B, H, T, dv]
+// (io dtype), dS_T [B, H, dk, dv] and daux_T (nullable).  Gradients are fp32:
+// dq, dk, dw_acc [B, H, T, dk] and dG ([B, H, T], per channel [B, H, T, dk])
+// are accumulated over value slices and must start at zero; dv [B, H, T, dv]
+// and dS0 (nullable) are written.  Workspace: the state entering every chunk
 // S_ck [B, H, nch, dk, dv] and the residuals E [B, H, T, dv].
 struct BwdArgs {
   int B, H, T, dk, dv;
@@ -121,7 +121,7 @@ struct BwdArgs {
   float* dG;
   float* dS0;
 };
-hipError_t launch_chunk_bwd_state(const BwdArgs& a, int io_bf16, hipStream_t st);
+hipError_t launch_chunk_bwd_state(const BwdArgs& a, int io_bf16, bool channel, hipStream_t st);
 
 // Back through the gains (chunk_bwd.hip), one workgroup per (b, h): adds the
 // gain's part to dk and forms the gates' gradients from dw_acc and dG.
@@ -129,7 +129,8 @@ struct GainBwdArgs {
   int B, H, T, dk;
   const void* k;
   GateArgs g;
-  const float* aux_chunk;  // PGDN: A entering every chunk [B, H, nch, dk]
+  const float* aux_chunk;  // the statistic entering every chunk: PGDN A, KDN p
+                           // [B, H, nch, dk]; KDN_ISO b [B, H, nch]
   const float* daux_T;     // nullable
   const float* dw_acc;
   const float* dG;
@@ -140,9 +141,12 @@ struct GainBwdArgs {
   float* dbetaP;
   float* dmu_log;          // [H], accumulated over batch rows (starts at zero)
   float* dw_out;           // explicit w
+  float* domega;           // KDN [B, H, T, dk], KDN_ISO [B, H, T]
+  float* dr;               // KDN, KDN_ISO [B, H, T]
   float* daux0;            // nullable
 };
-hipError_t launch_gain_bwd(const GainBwdArgs& a, int io_bf16, int gain, hipStream_t st);
+hipError_t launch_gain_bwd(const GainBwdArgs& a, int io_bf16, int gain, bool channel,
+                           hipStream_t st);
 // Zero n floats (a plain fill kernel, so that callers may capture it).
 hipError_t launch_zero(float* p, size_t n, hipStream_t st);
 

@@ -42,7 +42,7 @@ class DnGates(ctypes.Structure):
 class DnGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("dq", "dk", "dv", "dalpha", "deta", "dalphaP", "dbetaP", "dmu_log", "dw", "dS0",
-                 "daux0")]
+                 "daux0", "domega", "dr")]
 
 
 class DnError(RuntimeError):
@@ -259,7 +259,7 @@ def chunk_bwd(q, k, v, gates: Dict[str, torch.Tensor], dO, *, gain="kla", decay=
     """Chunked backward (dn_chunk_bwd): the gradients of
     sum <dO, o> + <dS_T, S_T> + <daux_T, aux_T> with respect to the inputs of
     chunk_fwd, as fp32 tensors in a dict (q, k, v, alpha, S0 and the gain's
-    gates; aux0 for PGDN)."""
+    gates; aux0 for the gains with a statistic)."""
     B, H, T, dk = k.shape
     dv = v.shape[-1]
     if decay is None:
@@ -273,11 +273,15 @@ def chunk_bwd(q, k, v, gates: Dict[str, torch.Tensor], dO, *, gain="kla", decay=
         g["eta"] = f32(B, H, T)
     if gain == "pgdn":
         g |= {"alphaP": f32(B, H, T), "betaP": f32(B, H, T), "mu_log": f32(H), "aux0": f32(B, H, dk)}
+    if gain == "kdn":
+        g |= {"omega": f32(B, H, T, dk), "r": f32(B, H, T), "aux0": f32(B, H, dk)}
+    if gain == "kdn_iso":
+        g |= {"omega": f32(B, H, T), "r": f32(B, H, T), "aux0": f32(B, H)}
     if gain == "explicit":
         g["w"] = f32(B, H, T, dk)
     grads = DnGrads(_ptr(g["q"]), _ptr(g["k"]), _ptr(g["v"]), _ptr(g["alpha"]), _ptr(g.get("eta")),
                     _ptr(g.get("alphaP")), _ptr(g.get("betaP")), _ptr(g.get("mu_log")), _ptr(g.get("w")),
-                    _ptr(g["S0"]), _ptr(g.get("aux0")))
+                    _ptr(g["S0"]), _ptr(g.get("aux0")), _ptr(g.get("omega")), _ptr(g.get("r")))
     nbytes = lib().dn_chunk_bwd_workspace(ctypes.byref(desc))
     ws, nbytes = _workspace(nbytes, dev, workspace)
     gt = make_gates(gates)

@@ -256,7 +256,7 @@ def test_chunk_bwd_rejects_bad_arguments():
     gradients, the workspace, and overlaps are refused before any launch."""
     L = dn.lib()
     q, k, v, dO = FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30), FAKE + (5 << 30)
-    outs = [FAKE + ((10 + i) << 30) for i in range(11)]
+    outs = [FAKE + ((10 + i) << 30) for i in range(13)]
     ws = FAKE + (30 << 30)
 
     def call(desc, gates=None, grads=None, ws_=ws, nbytes=None):
@@ -267,12 +267,14 @@ def test_chunk_bwd_rejects_bad_arguments():
         return L.dn_chunk_bwd(ctypes.byref(desc), q, k, v, ctypes.byref(gates), None, None, dO, None, None,
                               ctypes.byref(grads), ws_, nbytes, None)
     d = _desc(B=2, H=3, T=100)
-    assert call(_desc(decay="channel")) == -6
-    assert call(_desc(gain="kdn")) == -6
     assert call(_desc(io=0, dk=128)) == -6
-    assert L.dn_chunk_bwd_workspace(ctypes.byref(_desc(gain="kdn"))) == 0
+    assert L.dn_chunk_bwd_workspace(ctypes.byref(_desc(io=0, dk=128))) == 0
     assert call(d, grads=dn.DnGrads(None, *outs[1:])) == -1  # dq missing
     assert call(_desc(gain="pgdn")) == -1  # PGDN gates missing
+    gk = _gates(omega=FAKE + (6 << 30), r=FAKE + (7 << 30))
+    assert call(_desc(gain="kdn", decay="channel"), gates=gk,
+                grads=dn.DnGrads(*outs[:11], None, outs[12])) == -1  # KDN domega missing
+    assert call(_desc(gain="kdn_iso"), gates=gk, grads=dn.DnGrads(*outs[:12], None)) == -1  # dr missing
     assert call(d, ws_=None) == -5
     assert call(d, nbytes=1024) == -5
     assert call(d, grads=dn.DnGrads(q, *outs[1:])) == -8  # dq on top of q
@@ -284,6 +286,14 @@ def test_chunk_bwd_rejects_bad_arguments():
     assert L.dn_chunk_bwd_workspace(ctypes.byref(d)) == r256(size)
     dp = _desc(B=2, H=3, T=100, gain="pgdn")
     assert L.dn_chunk_bwd_workspace(ctypes.byref(dp)) == r256(size) + 6 * nch * 128 * 4
+    # channel decay: dG per (token, channel); KDN / KDN_ISO: the statistic per chunk
+    sizec = r256(r256(r256(r256(bht * 128 * 4) + 6 * nch * 128 * 128 * 4) + bht * 128 * 4) + bht * 128 * 4) + bht * 128 * 4
+    dc = _desc(B=2, H=3, T=100, decay="channel")
+    assert L.dn_chunk_bwd_workspace(ctypes.byref(dc)) == sizec
+    dk_ = _desc(B=2, H=3, T=100, decay="channel", gain="kdn")
+    assert L.dn_chunk_bwd_workspace(ctypes.byref(dk_)) == r256(sizec) + 6 * nch * 128 * 4
+    di = _desc(B=2, H=3, T=100, gain="kdn_iso")
+    assert L.dn_chunk_bwd_workspace(ctypes.byref(di)) == r256(size) + 6 * nch * 4
 
 
 def test_bench_refuses_more_than_one_gpu():

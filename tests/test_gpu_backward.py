@@ -22,18 +22,20 @@ def _run(wl, seed, with_dS=True, with_daux=True):
     rng = np.random.default_rng(seed)
     dO = W.round_io(rng.standard_normal((wl.B, wl.H, wl.T, wl.dv)), wl.io)
     dS_T = rng.standard_normal((wl.B, wl.H, wl.dk, wl.dv)).astype(np.float32) if with_dS else None
-    daux_T = (rng.standard_normal((wl.B, wl.H, wl.dk)).astype(np.float32)
-              if with_daux and wl.gain == "pgdn" else None)
-    if wl.gain == "pgdn":
-        inp["aux0"] = rng.uniform(0.5, 2.0, size=(wl.B, wl.H, wl.dk)).astype(np.float32)
+    aux_shape = {"pgdn": (wl.B, wl.H, wl.dk), "kdn": (wl.B, wl.H, wl.dk), "kdn_iso": (wl.B, wl.H)}
+    daux_T = (rng.standard_normal(aux_shape[wl.gain]).astype(np.float32)
+              if with_daux and wl.gain in aux_shape else None)
+    if wl.gain in aux_shape:
+        inp["aux0"] = rng.uniform(0.5, 2.0, size=aux_shape[wl.gain]).astype(np.float32)
     if wl.gain == "explicit":
         inp["w"] = W.round_io(rng.standard_normal((wl.B, wl.H, wl.T, wl.dk)) * 0.05, wl.io)
     io = torch.float32 if wl.io == "f32" else torch.bfloat16
     t = dn.to_device(inp, io)
-    gates = {n: t[n] for n in ("alpha", "eta", "alphaP", "betaP", "mu_log", "w") if n in t}
+    gates = {n: t[n] for n in ("alpha", "eta", "alphaP", "betaP", "mu_log", "omega", "r", "w") if n in t}
     cuda = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    g = dn.chunk_bwd(t["q"], t["k"], t["v"], gates, cuda(dO).to(io), gain=wl.gain, eps=wl.eps, x=wl.x,
-                     S0=t["S0"], aux0=t.get("aux0"), dS_T=cuda(dS_T), daux_T=cuda(daux_T))
+    g = dn.chunk_bwd(t["q"], t["k"], t["v"], gates, cuda(dO).to(io), gain=wl.gain, decay=wl.decay,
+                     eps=wl.eps, x=wl.x, mu_info=wl.mu_info, S0=t["S0"], aux0=t.get("aux0"),
+                     dS_T=cuda(dS_T), daux_T=cuda(daux_T))
     torch.cuda.synchronize()
     got = {n: a.cpu().numpy() for n, a in g.items()}
     # the oracle on the same values
@@ -42,7 +44,8 @@ def _run(wl, seed, with_dS=True, with_daux=True):
     mu = None if "mu_log" not in inp else np.asarray(inp["mu_log"], np.float64)[np.arange(wl.B * H) % H]
     ref = backward(fh(inp["q"]), fh(inp["k"]), fh(inp["v"]), wl.gain, fh(inp["alpha"]), fh(dO),
                    eta=fh(inp.get("eta")), eps=wl.eps, alphaP=fh(inp.get("alphaP")),
-                   betaP=fh(inp.get("betaP")), mu_log=mu, x=wl.x, w=fh(inp.get("w")),
+                   betaP=fh(inp.get("betaP")), mu_log=mu, x=wl.x, omega=fh(inp.get("omega")),
+                   r=fh(inp.get("r")), mu_info=wl.mu_info, w=fh(inp.get("w")),
                    S0=fh(inp["S0"]), aux0=fh(inp.get("aux0")), dS_T=fh(dS_T), daux_T=fh(daux_T))
     return got, ref
 
@@ -68,6 +71,37 @@ def test_chunk_bwd_against_oracle(gain, keys, io, dk, dv, T):
     wl = W.Workload(f"bwd_{gain}_{io}_dk{dk}", gain, "scalar", io, 2, 2, T, dk, dv, keys=keys,
                     mu_spread=0.5, seed=600 + T + dk + dv)
     got, ref = _run(wl, wl.seed + 1)
-    names = ["q", "k", "v", "alpha", "S0"] + {"kla": ["eta"], "gdn": ["eta"], "explicit": ["w"],
-                                            "pgdn": ["eta", "alphaP", "betaP", "mu_log", "aux0"]}[gain]
-    _compare(wl, got, ref, names)
+    _compare(wl, got, ref, _names(gain))
+
+
+def _names(gain):
+    return ["q", "k", "v", "alpha", "S0"] + {
+        "kla": ["eta"], "gdn": ["eta"], "explicit": ["w"],
+        "pgdn": ["eta", "alphaP", "betaP", "mu_log", "aux0"],
+        "kdn": ["omega", "r", "aux0"], "kdn_iso": ["omega", "r", "aux0"]}[gain]
+
+
+# Per-channel decay (every gain; PGDN with it is PKDA) and the KDN gains with
+# either decay: the decay applied inside the products, the variance scans
+# differentiated backwards.
+@pytest.mark.parametrize("T", [64, 150])
+@pytest.mark.parametrize("gain,decay,keys,io,dk,dv", [
+    ("kla", "channel", "scaled", "bf16", 128, 128), ("gdn", "channel", "unit", "bf16", 64, 64),
+    ("pgdn", "channel", "unit", "bf16", 128, 128), ("explicit", "channel", "unit", "f32", 64, 64),
+    ("kdn", "channel", "scaled", "bf16", 128, 128), ("kdn", "channel", "scaled", "f32", 64, 64),
+    ("kdn", "scalar", "scaled", "bf16", 64, 128), ("kdn_iso", "channel", "scaled", "bf16", 128, 64),
+    ("kdn_iso", "scalar", "scaled", "bf16", 64, 64), ("kdn_iso", "channel", "scaled", "f32", 64, 64)])
+def test_chunk_bwd_channel_and_kdn(gain, decay, keys, io, dk, dv, T):
+    wl = W.Workload(f"bwd_{gain}_{decay}_{io}_dk{dk}", gain, decay, io, 2, 2, T, dk, dv, keys=keys,
+                    mu_spread=0.5, seed=700 + T + dk + dv)
+    got, ref = _run(wl, wl.seed + 1)
+    _compare(wl, got, ref, _names(gain))
+
+
+def test_chunk_bwd_kdn_information_scaling_and_strong_decay():
+    """KDN with mu = d_k and a stronger per-channel decay (alpha = sigmoid(N(0, 1)),
+    still inside the chunked forward's range)."""
+    wl = W.Workload("bwd_kdn_mu_dk_strong", "kdn", "channel", "bf16", 1, 3, 200, 128, 128,
+                    mu_info=128.0, alpha_mean=0.0, seed=771)
+    got, ref = _run(wl, wl.seed + 1)
+    _compare(wl, got, ref, _names("kdn"))
