@@ -16,6 +16,7 @@ dispatches between such a pair in a `rocprofv3 --kernel-trace` of this script
 are exactly the timed launches (no settle or warm-up launches).
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -320,6 +321,42 @@ def extra_chunk(wl, steps, warmup, settle_s):
             "workspace_bytes": out["ws_bytes"]}
 
 
+def bwd_bytes(wl):
+    """Least HBM bytes of one chunked backward: q, k, v, dO and the gates read
+    once, every gradient (fp32) written once, S0 / dS_T read and dS0 written."""
+    es = 2 if wl.io == "bf16" else 4
+    nht = wl.B * wl.H * wl.T
+    per_ht = 2 * wl.dk * es + 2 * wl.dv * es + 8  # q, k, v, dO; eta, alpha
+    per_ht += 2 * wl.dk * 4 + wl.dv * 4 + 8       # dq, dk, dv; deta, dalpha
+    return nht * per_ht + 3 * wl.B * wl.H * wl.dk * wl.dv * 4
+
+
+def extra_bwd(wl, steps, warmup, settle_s):
+    """The chunked backward (dn_chunk_bwd) of a KLA workload."""
+    import numpy as np
+    import torch
+    from recurrent_sequence_mixer_amd import dn
+    from recurrent_sequence_mixer_amd import workloads as W
+    inp = W.generate(wl)
+    io = torch.bfloat16 if wl.io == "bf16" else torch.float32
+    t = dn.to_device(inp, io)
+    gates = {n: t[n] for n in GATES if n in t}
+    rng = np.random.default_rng(wl.seed + 1)
+    dO = torch.from_numpy(W.round_io(rng.standard_normal((wl.B, wl.H, wl.T, wl.dv)), wl.io)).cuda().to(io)
+    dS_T = torch.from_numpy(rng.standard_normal((wl.B, wl.H, wl.dk, wl.dv)).astype(np.float32)).cuda()
+    desc = dn.make_desc(wl.B, wl.H, wl.T, wl.dk, wl.dv, io, wl.gain, wl.decay, wl.eps, wl.x, wl.mu_info)
+    nbytes = dn.lib().dn_chunk_bwd_workspace(ctypes.byref(desc))
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
+    call = lambda: dn.chunk_bwd(t["q"], t["k"], t["v"], gates, dO, gain=wl.gain, eps=wl.eps, S0=t["S0"],
+                                dS_T=dS_T, workspace=ws)
+    ms, _ = time_calls(call, steps, warmup, settle_s)
+    b = bwd_bytes(wl)
+    log(f"[bench] backward {wl.name}: {ms:.3f} ms/step")
+    return {"workload": wl.name, "ms": ms, "tokens_per_s": wl.tokens / (ms * 1e-3),
+            "hbm_gbs": b / (ms * 1e-3) / 1e9, "hbm_frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "workspace_bytes": nbytes}
+
+
 def main():
     global REGION
     ap = argparse.ArgumentParser()
@@ -336,7 +373,7 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a device copy of this size (byte-counter calibration)")
     ap.add_argument("--only", default=None,
-                    help="time only these extras (comma list of pgdn, kdn, kdn_iso, long, decode) "
+                    help="time only these extras (comma list of pgdn, kdn, kdn_iso, long, bwd, decode) "
                          "after the headline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -412,6 +449,13 @@ def main():
                                                      1, 8, 32768, 128, 128, seed=53)))
             for key, w2 in longs:
                 extra[key] = extra_chunk(w2, half, args.warmup, args.settle_s)
+        if want("bwd"):
+            # the chunked backward at the headline shape and at the pages' operator
+            # shape (Preconditioned DeltaNet Fig. 4: batch 1, 8 heads, head dim 128)
+            for key, w2 in (("bwd_kla", W.WORKLOADS[1]),
+                            ("bwd_kla_B1H8", W.Workload("kla_bwd_B1H8T4096d128", "kla", "scalar", "bf16",
+                                                        1, 8, 4096, 128, 128, seed=54))):
+                extra[key] = extra_bwd(w2, 3, 1, 0.0)
         if want("decode"):
             dwl = W.WORKLOADS[4]
             dms = time_decode(dwl, args.decode_steps, args.settle_s)

@@ -55,7 +55,8 @@
  *
  * OWNERSHIP.  Every pointer except the descriptor and the gate table (host
  * structs, read before the call returns) is a device pointer owned by the
- * caller.  The library allocates no device memory, never synchronises, and
+ * caller, 16-byte aligned (as hipMalloc and tensor allocators return them:
+ * the kernels move rows in 16-byte vectors).  The library allocates no device memory, never synchronises, and
  * enqueues all work on `stream` (a hipStream_t; NULL = the null stream).
  *
  * ERRORS.  Arguments are validated on the host before anything is launched;

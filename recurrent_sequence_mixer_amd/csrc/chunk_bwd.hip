@@ -63,8 +63,10 @@ namespace dn {
 namespace bwd {
 
 constexpr int CH = 64;      // chunk length
-constexpr int NT = 256;     // threads of the state kernel
+constexpr int NT = 512;     // threads of the state kernel
+constexpr int NW = NT / 64; // its wavefronts
 constexpr int PC = CH + 1;  // row pitch of [CH][CH] fp32 arrays
+constexpr int PT = 17;      // row pitch of the 16x16 diagonal-block inverses
 constexpr int RT = 31;      // reference token of the per-channel decay factors
 
 template <typename E, int DK, bool CHAN>
@@ -81,6 +83,7 @@ struct Smem {
   float y[CH * PS];   // reverse: dE, then dR in place
   float lm[CH * PC];  // L, then (D o) dL
   float mm[CH * PC];  // M, then (D o) dM
+  float tb[4 * 16 * PT];  // (I + L_bb)^-1 of the four diagonal 16x16 blocks
   // channel decay: G per (token, channel), exp(G_r), exp(G_n - G_r), and
   // dL/dG of the chunk's last token per channel
   float Gc[CHAN ? CH * PG : 1];
@@ -94,61 +97,173 @@ __device__ __forceinline__ float ld(const void* p, long i) {
   return Elem<E>::get(static_cast<const E*>(p)[i]);
 }
 
+// N consecutive elements from element offset `off` of `base` as fp32, in
+// 16-byte (or 8- / 4-byte) loads; zeros when !ok.
+template <typename E, int N>
+__device__ __forceinline__ void load_vec(const void* base, long off, bool ok, float (&v)[N]) {
+  if constexpr (sizeof(E) == 2) {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + off;
+    uint32_t u[N / 2];
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 8; ++i) {
+        const u32x4 x = ok ? reinterpret_cast<const u32x4*>(p)[i] : u32x4{0u, 0u, 0u, 0u};
+        u[4 * i] = x[0], u[4 * i + 1] = x[1], u[4 * i + 2] = x[2], u[4 * i + 3] = x[3];
+      }
+    } else if constexpr (N == 4) {
+      const u32x2 x = ok ? *reinterpret_cast<const u32x2*>(p) : u32x2{0u, 0u};
+      u[0] = x[0], u[1] = x[1];
+    } else {
+      static_assert(N == 2, "bf16 vector length");
+      u[0] = ok ? *reinterpret_cast<const uint32_t*>(p) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float* p = static_cast<const float*>(base) + off;
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 4; ++i) {
+        const f32x4 x = ok ? reinterpret_cast<const f32x4*>(p)[i] : zero4();
+        v[4 * i] = x[0], v[4 * i + 1] = x[1], v[4 * i + 2] = x[2], v[4 * i + 3] = x[3];
+      }
+    } else {
+      static_assert(N == 2, "fp32 vector length");
+      typedef float f32x2_ __attribute__((ext_vector_type(2)));
+      const f32x2_ x = ok ? *reinterpret_cast<const f32x2_*>(p) : f32x2_{0.f, 0.f};
+      v[0] = x[0], v[1] = x[1];
+    }
+  }
+}
+
+// LDS accesses of one wavefront complete in order; the fences keep the
+// compiler from moving them across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Sums over the 16 lanes of a row group (lanes 16 g .. 16 g + 15) and over
+// the four row groups (lanes with the same l % 16).
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float col4_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// One 16x16 output tile of a product on v_mfma_f32_16x16x4_f32:
+// acc += sum over k in [k0, k1) of A[r][k] B[k][c], k0 and k1 multiples of 4,
+// fa(r, k) = A[r][k], fb(k, c) = B[k][c] (tile-local r, c).  Lane l supplies
+// A row l % 16 and B column l % 16 at k = k0 + 4 s + l / 16; on return lane l
+// holds rows 4 (l / 16) + i, i = 0..3, of column l % 16.
+template <typename FA, typename FB>
+__device__ __forceinline__ f32x4 mm(f32x4 acc, int k0, int k1, FA fa, FB fb, int lane) {
+  const int r = lane & 15, kq = lane >> 4;
+#pragma unroll 4
+  for (int k = k0; k < k1; k += 4) acc = mfma4(fa(r, k + kq), fb(k + kq, r), acc);
+  return acc;
+}
+
 template <typename E, int DK, bool CHAN>
 __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
   using Sm = Smem<E, DK, CHAN>;
   constexpr int PK = Sm::PK, PS = Sm::PS, PG = Sm::PG, DVS = Sm::DVS;
-  constexpr int TPC = NT / DVS;  // threads per value column in the substitutions
+  constexpr int NC = DVS / 16;      // 16-column tiles of the value slice
+  constexpr int ND = DK / 16;       // 16-row tiles of the key dimension
+  constexpr int TPW = 4 * ND / NW;  // [token][key] tiles per wavefront
+  static_assert(TPW * NW == 4 * ND, "key tiles per wavefront");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;  // tile column / row group of this lane
   const int nsl = a.dv / DVS;
   const long bh = blockIdx.x / nsl;
   const int col0 = (blockIdx.x % nsl) * DVS;
   const int T = a.T, dv = a.dv;
   const int nch = (T + CH - 1) / CH;
   const long tok0 = bh * T;
+  auto kf = [&](int t, int d) { return Elem<E>::get(sm.k[t * PK + d]); };
+  auto qf = [&](int t, int d) { return Elem<E>::get(sm.q[t * PK + d]); };
+  auto wf = [&](int t, int d) { return Elem<E>::get(sm.w[t * PK + d]); };
 
-  // chunk c into LDS: k, w (and q), the decay; x holds v (forward) or dO
-  // (reverse); rows past the end are zero
-  auto stage = [&](int c, bool with_q, const void* xsrc) {
+  // chunk c into LDS: k, w, the decay, x = v (forward); reverse also q,
+  // x = dO, the residuals e and the state entering the chunk.  Rows past the
+  // end are zero.  Every thread first issues all its global loads (16-byte
+  // vectors of consecutive elements), then converts and stores.
+  constexpr int KV = CH * DK / NT, XV = CH * DVS / NT, SV = DK * DVS / NT;
+  auto stage = [&](int c, bool rev) {
     const int t0 = c * CH, n = min(CH, T - t0);
+    const int kt = tid * KV / DK, kd = tid * KV % DK;
+    const int xt = tid * XV / DVS, xc = tid * XV % DVS;
+    const int sd = tid * SV / DVS, sc = tid * SV % DVS;
+    const long krow = (tok0 + t0 + kt) * DK + kd, xrow = (tok0 + t0 + xt) * dv + col0 + xc;
+    const bool kok = kt < n, xok = xt < n;
+    float kv[KV], qv[KV], wv[KV], xv[XV], ev[XV], sv[SV], av[CHAN ? KV : 1];
+    load_vec<E, KV>(a.k, krow, kok, kv);
+    load_vec<float, KV>(a.w, krow, kok, wv);
+    load_vec<E, XV>(rev ? a.dO : a.v, xrow, xok, xv);
+    if (rev) {
+      load_vec<E, KV>(a.q, krow, kok, qv);
+      load_vec<float, XV>(a.E, xrow, xok, ev);
+      load_vec<float, SV>(a.S_ck, ((bh * nch + c) * DK + sd) * dv + col0 + sc, true, sv);
+    }
     if constexpr (CHAN) {
+      load_vec<E, KV>(a.g.alpha, krow, kok, av);
       // per channel: G_t = sum of log alpha through t (padding: alpha = 1)
+#pragma unroll
+      for (int j = 0; j < KV; ++j) sm.Gc[kt * PG + kd + j] = kok ? logf(av[j]) : 0.f;
+      __syncthreads();
       if (tid < DK) {
         const int d = tid;
-        float G = 0.f;
+        float G = 0.f, Gr = 0.f;
+#pragma unroll 16
         for (int t = 0; t < CH; ++t) {
-          if (t < n) G += logf(ld<E>(a.g.alpha, (tok0 + t0 + t) * DK + d));
+          G += sm.Gc[t * PG + d];
           sm.Gc[t * PG + d] = G;
+          if (t == RT) Gr = G;
         }
-        const float gr = expf(sm.Gc[RT * PG + d]), gt = expf(G - sm.Gc[RT * PG + d]);
+        const float gr = expf(Gr), gt = expf(G - Gr);
         sm.gref[d] = gr >= 0x1p-96f && gt >= 0x1p-96f ? gr : __builtin_nanf("");
         sm.gnr[d] = gt;
         sm.endc[d] = 0.f;
       }
       __syncthreads();
     }
-    for (int idx = tid; idx < CH * DK; idx += NT) {
-      const int t = idx / DK, d = idx % DK;
-      const bool ok = t < n;
-      const long gi = (tok0 + t0 + t) * DK + d;
-      float kv = ok ? ld<E>(a.k, gi) : 0.f, wv = ok ? a.w[gi] : 0.f;
-      float qv = with_q && ok ? ld<E>(a.q, gi) : 0.f;
+#pragma unroll
+    for (int j = 0; j < KV; ++j) {
+      const int d = kd + j;
+      float k_ = kv[j], q_ = rev ? qv[j] : 0.f, w_ = wv[j];
       if constexpr (CHAN) {
-        const float gd = sm.Gc[t * PG + d] - sm.Gc[RT * PG + d];
+        const float gd = sm.Gc[kt * PG + d] - sm.Gc[RT * PG + d];
         const float ek = expf(gd);
-        kv *= ek;
-        qv *= ek;
-        wv *= expf(-gd);
+        k_ *= ek;
+        q_ *= ek;
+        w_ *= expf(-gd);
       }
-      sm.k[t * PK + d] = Elem<E>::put(kv);
-      sm.w[t * PK + d] = Elem<E>::put(wv);
-      if (with_q) sm.q[t * PK + d] = Elem<E>::put(qv);
+      sm.k[kt * PK + d] = Elem<E>::put(k_);
+      sm.w[kt * PK + d] = Elem<E>::put(w_);
+      if (rev) sm.q[kt * PK + d] = Elem<E>::put(q_);
     }
-    for (int idx = tid; idx < CH * DVS; idx += NT) {
-      const int t = idx / DVS, cc = idx % DVS;
-      sm.x[t * PS + cc] = t < n ? ld<E>(xsrc, (tok0 + t0 + t) * dv + col0 + cc) : 0.f;
+#pragma unroll
+    for (int j = 0; j < XV; ++j) {
+      sm.x[xt * PS + xc + j] = xv[j];
+      if (rev) sm.e[xt * PS + xc + j] = ev[j];
+    }
+    if (rev) {
+#pragma unroll
+      for (int j = 0; j < SV; ++j) sm.S[sd * PS + sc + j] = sv[j];
     }
     if constexpr (!CHAN) {
       if (tid < 64) {
@@ -165,22 +280,81 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
       }
     }
   };
-  auto dotkw = [&](const E* rows, int j, int i) {  // rows_j . w_i over DK
-    float s = 0.f;
-#pragma unroll 8
-    for (int d = 0; d < DK; ++d) s = fmaf(Elem<E>::get(rows[j * PK + d]), Elem<E>::get(sm.w[i * PK + d]), s);
-    return s;
-  };
   // the decay between token i and token j (scalar decay; with channel decay
   // the staged operands carry it)
   auto dec = [&](int j, int i) { return CHAN ? 1.f : expf(sm.G[j] - sm.G[i]); };
   // exp(G_t - G_r) of channel d
   auto eref = [&](int t, int d) { return expf(sm.Gc[t * PG + d] - sm.Gc[RT * PG + d]); };
-  // the sum of s over the TPC threads of one value column
-  auto column_sum = [&](float s) {
+  // L = strict_lower(D o K W^T) (and, with_m, M = lower(D o Q W^T)) of the
+  // chunk's n tokens into lm (mm); tiles above the diagonal are zero
+  auto form_lm = [&](int n, bool with_m) {
+    for (int tile = wave; tile < 16; tile += NW) {
+      const int tr = tile >> 2, tc = tile & 3;
+      f32x4 al = zero4(), am = zero4();
+      if (tr >= tc) {
+        auto fw = [&](int k_, int c) { return wf(16 * tc + c, k_); };
+        al = mm(al, 0, DK, [&](int r, int k_) { return kf(16 * tr + r, k_); }, fw, lane);
+        if (with_m) am = mm(am, 0, DK, [&](int r, int k_) { return qf(16 * tr + r, k_); }, fw, lane);
+      }
+      const int i = 16 * tc + lr;
 #pragma unroll
-    for (int o = 1; o < TPC; o <<= 1) s += __shfl_xor(s, o);
-    return s;
+      for (int ii = 0; ii < 4; ++ii) {
+        const int j = 16 * tr + 4 * lg + ii;
+        const float dm = j < n && i <= j ? dec(j, i) : 0.f;
+        sm.lm[j * PC + i] = i < j ? dm * al[ii] : 0.f;
+        if (with_m) sm.mm[j * PC + i] = dm * am[ii];
+      }
+    }
+  };
+  // (I + L_bb)^-1 of the diagonal blocks, by forward substitution (waves 0..3,
+  // lane c holds column c)
+  auto invert_blocks = [&]() {
+    if (wave < 4 && lane < 16) {
+      const int b = wave, c = lane;
+      float t[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s = r == c ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < r; ++m) s = fmaf(-sm.lm[(16 * b + r) * PC + 16 * b + m], t[m], s);
+        t[r] = s;
+        sm.tb[(16 * b + r) * PT + c] = s;
+      }
+    }
+  };
+  // block b of a solve, in place in the 16-column tile cb of X:
+  // X_b <- T_b (X_b - acc) (or T_b^T when `tr`).  The product's k index runs
+  // over the rows this lane holds, 4 (lane / 16) + s, matched in T_b.
+  auto apply_block = [&](float* X, int b, int cb, f32x4 acc, bool tr) {
+    f32x4 z, u = zero4();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[i] = X[(16 * b + 4 * lg + i) * PS + 16 * cb + lr] - acc[i];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float tv = tr ? sm.tb[(16 * b + 4 * lg + s) * PT + lr] : sm.tb[(16 * b + lr) * PT + 4 * lg + s];
+      u = mfma4(tv, z[s], u);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) X[(16 * b + 4 * lg + i) * PS + 16 * cb + lr] = u[i];
+    wave_lds_sync();
+  };
+  // (I + L) Z = X: Z_b = T_b (X_b - sum_{m<b} L_bm Z_m), one wave per column tile
+  auto solve_lower = [&](float* X) {
+    for (int cb = wave; cb < NC; cb += NW)
+      for (int b = 0; b < 4; ++b) {
+        const f32x4 acc = mm(zero4(), 0, 16 * b, [&](int r, int k_) { return sm.lm[(16 * b + r) * PC + k_]; },
+                             [&](int k_, int c) { return X[k_ * PS + 16 * cb + c]; }, lane);
+        apply_block(X, b, cb, acc, false);
+      }
+  };
+  // (I + L)^T Z = X: Z_b = T_b^T (X_b - sum_{m>b} L_mb^T Z_m)
+  auto solve_upper = [&](float* X) {
+    for (int cb = wave; cb < NC; cb += NW)
+      for (int b = 3; b >= 0; --b) {
+        const f32x4 acc = mm(zero4(), 16 * (b + 1), CH, [&](int r, int k_) { return sm.lm[k_ * PC + 16 * b + r]; },
+                             [&](int k_, int c) { return X[k_ * PS + 16 * cb + c]; }, lane);
+        apply_block(X, b, cb, acc, true);
+      }
   };
 
   // ---------------- forward sweep: S_in of every chunk and E
@@ -191,55 +365,47 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
   for (int c = 0; c < nch; ++c) {
     const int t0 = c * CH, n = min(CH, T - t0);
     __syncthreads();  // the previous chunk's readers of k, w, x, S are done
-    stage(c, false, a.v);
+    stage(c, false);
     __syncthreads();
     // S_in to the checkpoint; L; R = V - g K S_in
     for (int idx = tid; idx < DK * DVS; idx += NT) {
       const int d = idx / DVS, cc = idx % DVS;
       a.S_ck[((bh * nch + c) * DK + d) * dv + col0 + cc] = sm.S[d * PS + cc];
     }
-    for (int idx = tid; idx < CH * CH; idx += NT) {
-      const int j = idx / CH, i = idx % CH;
-      sm.lm[j * PC + i] = i < j && j < n ? dec(j, i) * dotkw(sm.k, j, i) : 0.f;
-    }
-    for (int idx = tid; idx < CH * DVS; idx += NT) {
-      const int t = idx / DVS, cc = idx % DVS;
-      float s = 0.f;
-      for (int d = 0; d < DK; ++d) {
-        const float kv = Elem<E>::get(sm.k[t * PK + d]);
-        s = fmaf(CHAN ? kv * sm.gref[d] : kv, sm.S[d * PS + cc], s);
+    form_lm(n, false);
+    for (int tile = wave; tile < 4 * NC; tile += NW) {
+      const int tb_ = tile / NC, cb = tile % NC;
+      const f32x4 acc =
+          mm(zero4(), 0, DK, [&](int r, int k_) { return CHAN ? kf(16 * tb_ + r, k_) * sm.gref[k_] : kf(16 * tb_ + r, k_); },
+             [&](int k_, int cc) { return sm.S[k_ * PS + 16 * cb + cc]; }, lane);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int t = 16 * tb_ + 4 * lg + ii;
+        sm.x[t * PS + 16 * cb + lr] -= CHAN ? acc[ii] : sm.gam[t] * acc[ii];
       }
-      sm.x[t * PS + cc] -= CHAN ? s : sm.gam[t] * s;
     }
     __syncthreads();
-    // (I + L) E = R by forward substitution, in place
-    {
-      const int cc = tid / TPC, part = tid % TPC;
-      for (int j = 1; j < n; ++j) {
-        float s = 0.f;
-        for (int i = part; i < j; i += TPC) s = fmaf(sm.lm[j * PC + i], sm.x[i * PS + cc], s);
-        s = column_sum(s);
-        if (part == 0) sm.x[j * PS + cc] -= s;
-        __syncthreads();
-      }
-    }
+    invert_blocks();
+    __syncthreads();
+    solve_lower(sm.x);  // E
+    __syncthreads();
     for (int idx = tid; idx < CH * DVS; idx += NT) {
       const int t = idx / DVS, cc = idx % DVS;
       if (t < n) a.E[(tok0 + t0 + t) * dv + col0 + cc] = sm.x[t * PS + cc];
     }
     // S_out = g_n S_in + sum_t (g_n / g_t) w_t E_t^T
     const float gn = CHAN ? 1.f : sm.gam[CH - 1];
-    for (int idx = tid; idx < DK * DVS; idx += NT) {
-      const int d = idx / DVS, cc = idx % DVS;
-      float s = 0.f;
-      for (int t = 0; t < n; ++t) {
-        const float wv = Elem<E>::get(sm.w[t * PK + d]);
-        s = fmaf(CHAN ? wv : gn / sm.gam[t] * wv, sm.x[t * PS + cc], s);
+    for (int tile = wave; tile < ND * NC; tile += NW) {
+      const int db = tile / NC, cb = tile % NC;
+      const f32x4 acc =
+          mm(zero4(), 0, CH, [&](int r, int k_) { return CHAN ? wf(k_, 16 * db + r) : gn / sm.gam[k_] * wf(k_, 16 * db + r); },
+             [&](int k_, int cc) { return sm.x[k_ * PS + 16 * cb + cc]; }, lane);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int d = 16 * db + 4 * lg + ii;
+        float& s = sm.S[d * PS + 16 * cb + lr];
+        s = CHAN ? sm.gnr[d] * fmaf(sm.gref[d], s, acc[ii]) : fmaf(gn, s, acc[ii]);
       }
-      if constexpr (CHAN)
-        sm.S[d * PS + cc] = sm.gnr[d] * fmaf(sm.gref[d], sm.S[d * PS + cc], s);
-      else
-        sm.S[d * PS + cc] = fmaf(gn, sm.S[d * PS + cc], s);
     }
   }
 
@@ -252,37 +418,25 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
   for (int c = nch - 1; c >= 0; --c) {
     const int t0 = c * CH, n = min(CH, T - t0);
     __syncthreads();
-    stage(c, true, a.dO);
-    for (int idx = tid; idx < DK * DVS; idx += NT) {
-      const int d = idx / DVS, cc = idx % DVS;
-      sm.S[d * PS + cc] = a.S_ck[((bh * nch + c) * DK + d) * dv + col0 + cc];
-    }
-    for (int idx = tid; idx < CH * DVS; idx += NT) {
-      const int t = idx / DVS, cc = idx % DVS;
-      sm.e[t * PS + cc] = t < n ? a.E[(tok0 + t0 + t) * dv + col0 + cc] : 0.f;
-    }
+    stage(c, true);
     __syncthreads();
     const float gn = CHAN ? 1.f : sm.gam[CH - 1];
-    // L and M
-    for (int idx = tid; idx < CH * CH; idx += NT) {
-      const int j = idx / CH, i = idx % CH;
-      const bool in = j < n;
-      const float dm = dec(j, i);
-      sm.lm[j * PC + i] = in && i < j ? dm * dotkw(sm.k, j, i) : 0.f;
-      sm.mm[j * PC + i] = in && i <= j ? dm * dotkw(sm.q, j, i) : 0.f;
-    }
+    form_lm(n, true);
     __syncthreads();
+    invert_blocks();
     // dE = M^T dO + W~ dS_out
-    for (int idx = tid; idx < CH * DVS; idx += NT) {
-      const int i = idx / DVS, cc = idx % DVS;
-      float s = 0.f;
-      for (int j = i; j < n; ++j) s = fmaf(sm.mm[j * PC + i], sm.x[j * PS + cc], s);
-      float s2 = 0.f;
-      for (int d = 0; d < DK; ++d) {
-        const float wv = Elem<E>::get(sm.w[i * PK + d]);
-        s2 = fmaf(CHAN ? wv * sm.gnr[d] : wv, sm.dS[d * PS + cc], s2);
+    for (int tile = wave; tile < 4 * NC; tile += NW) {
+      const int ib = tile / NC, cb = tile % NC;
+      const f32x4 a1 = mm(zero4(), 16 * ib, CH, [&](int r, int k_) { return sm.mm[k_ * PC + 16 * ib + r]; },
+                          [&](int k_, int cc) { return sm.x[k_ * PS + 16 * cb + cc]; }, lane);
+      const f32x4 a2 =
+          mm(zero4(), 0, DK, [&](int r, int k_) { return CHAN ? wf(16 * ib + r, k_) * sm.gnr[k_] : wf(16 * ib + r, k_); },
+             [&](int k_, int cc) { return sm.dS[k_ * PS + 16 * cb + cc]; }, lane);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 16 * ib + 4 * lg + ii;
+        sm.y[i * PS + 16 * cb + lr] = i < n ? fmaf(CHAN ? 1.f : gn / sm.gam[i], a2[ii], a1[ii]) : 0.f;
       }
-      sm.y[i * PS + cc] = i < n ? fmaf(CHAN ? 1.f : gn / sm.gam[i], s2, s) : 0.f;
     }
     // dL/dG of the chunk end: g_n <S_in, dS_out> (per channel: row d)
     if constexpr (CHAN) {
@@ -302,57 +456,119 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
       if (lane == 0) atomicAdd(&sm.sg[CH - 1], gn * s);
     }
     __syncthreads();
-    // (I + L)^T dR = dE by back substitution, in place
-    {
-      const int cc = tid / TPC, part = tid % TPC;
-      for (int j = n - 2; j >= 0; --j) {
-        float s = 0.f;
-        for (int i = j + 1 + part; i < n; i += TPC) s = fmaf(sm.lm[i * PC + j], sm.y[i * PS + cc], s);
-        s = column_sum(s);
-        if (part == 0) sm.y[j * PS + cc] -= s;
-        __syncthreads();
-      }
-    }
+    solve_upper(sm.y);  // dR
+    __syncthreads();
     // dV = dR
     for (int idx = tid; idx < CH * DVS; idx += NT) {
       const int t = idx / DVS, cc = idx % DVS;
       if (t < n) a.dv_out[(tok0 + t0 + t) * dv + col0 + cc] = sm.y[t * PS + cc];
     }
-    // per (token, key channel), the parts through S_in and dS_out:
-    //   dk += g_t (-S_in dR_t),  dq += g_t (S_in dO_t),  dw += (g_n / g_t) dS_out E_t;
-    // their decay terms go to dL/dG
-    for (int idx = tid; idx < CH * DK; idx += NT) {
-      const int t = idx / DK, d = idx % DK;
-      float kh = 0.f, qh = 0.f, tw = 0.f;
-      for (int cc = 0; cc < DVS; ++cc) {
-        const float sv = sm.S[d * PS + cc];
-        kh = fmaf(-sm.y[t * PS + cc], sv, kh);
-        qh = fmaf(sm.x[t * PS + cc], sv, qh);
-        tw = fmaf(sm.e[t * PS + cc], sm.dS[d * PS + cc], tw);
+    // dL = -dR E^T, dM = dO E^T.  Scalar decay: their decay terms (L o dL,
+    // M o dM: + to the row token, - to the column token), then L <- D o dL,
+    // M <- D o dM.  Channel decay: L <- dL, M <- dM (the decay terms follow
+    // per channel below)
+    for (int tile = wave; tile < 16; tile += NW) {
+      const int tr = tile >> 2, tc = tile & 3;
+      if (tr < tc) continue;
+      auto fe = [&](int k_, int ii_) { return sm.e[(16 * tc + ii_) * PS + k_]; };
+      const f32x4 al = mm(zero4(), 0, DVS, [&](int r, int k_) { return sm.y[(16 * tr + r) * PS + k_]; }, fe, lane);
+      const f32x4 am = mm(zero4(), 0, DVS, [&](int r, int k_) { return sm.x[(16 * tr + r) * PS + k_]; }, fe, lane);
+      const int i = 16 * tc + lr;
+      float col = 0.f;  // scalar decay: - (L o dL + M o dM) summed over this lane's rows
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int j = 16 * tr + 4 * lg + ii;
+        const bool ok = j < n && i <= j;
+        const float dl = -al[ii], dmv = am[ii];
+        if constexpr (CHAN) {
+          if (ok) {
+            sm.lm[j * PC + i] = i < j ? dl : 0.f;
+            sm.mm[j * PC + i] = dmv;
+          }
+        } else {
+          float tlm = 0.f;
+          if (ok) {
+            const float dm = expf(sm.G[j] - sm.G[i]);
+            tlm = (i < j ? sm.lm[j * PC + i] * dl : 0.f) + sm.mm[j * PC + i] * dmv;
+            if (i == j) tlm = 0.f;  // the diagonal adds and subtracts the same term
+            sm.lm[j * PC + i] = i < j ? dm * dl : 0.f;
+            sm.mm[j * PC + i] = dm * dmv;
+          }
+          col -= tlm;
+          const float row = row16_sum(tlm);  // + to the row token j
+          if (lr == 0 && j < n) atomicAdd(&sm.sg[j], row);
+        }
       }
-      if (t < n) {
+      if constexpr (!CHAN) {
+        col = col4_sum(col);  // - to the column token i
+        if (lg == 0) atomicAdd(&sm.sg[i], col);
+      }
+    }
+    __syncthreads();
+    // per (token, key channel) tile, with one addition per gradient element
+    // and value slice:
+    //   through S_in and dS_out: dk += g_t (-S_in dR_t), dq += g_t (S_in dO_t),
+    //     dw += (g_n / g_t) dS_out E_t, and their decay terms;
+    //   through L and M: dk += sum_{i<t} (D o dL)_ti w_i,
+    //     dq += sum_{i<=t} (D o dM)_ti w_i,
+    //     dw_t += sum_{j>t} (D o dL)_jt k_j + sum_{j>=t} (D o dM)_jt q_j
+    float wend = 0.f;  // scalar decay: the chunk end's part of the W~ terms
+#pragma unroll 1
+    for (int tile = wave; tile < 4 * ND; tile += NW) {
+      const int tb_ = tile / ND, db = tile % ND;
+      auto fS = [&](int k_, int dd) { return sm.S[(16 * db + dd) * PS + k_]; };
+      const f32x4 akh = mm(zero4(), 0, DVS, [&](int r, int k_) { return sm.y[(16 * tb_ + r) * PS + k_]; }, fS, lane);
+      const f32x4 aqh = mm(zero4(), 0, DVS, [&](int r, int k_) { return sm.x[(16 * tb_ + r) * PS + k_]; }, fS, lane);
+      const f32x4 atw = mm(zero4(), 0, DVS, [&](int r, int k_) { return sm.e[(16 * tb_ + r) * PS + k_]; },
+                           [&](int k_, int dd) { return sm.dS[(16 * db + dd) * PS + k_]; }, lane);
+      auto fw = [&](int k_, int dd) { return wf(k_, 16 * db + dd); };
+      const f32x4 ask = mm(zero4(), 0, 16 * (tb_ + 1), [&](int r, int k_) { return sm.lm[(16 * tb_ + r) * PC + k_]; }, fw, lane);
+      const f32x4 asq = mm(zero4(), 0, 16 * (tb_ + 1), [&](int r, int k_) { return sm.mm[(16 * tb_ + r) * PC + k_]; }, fw, lane);
+      f32x4 asw = mm(zero4(), 16 * tb_, CH, [&](int r, int k_) { return sm.lm[k_ * PC + 16 * tb_ + r]; },
+                     [&](int k_, int dd) { return kf(k_, 16 * db + dd); }, lane);
+      asw = mm(asw, 16 * tb_, CH, [&](int r, int k_) { return sm.mm[k_ * PC + 16 * tb_ + r]; },
+               [&](int k_, int dd) { return qf(k_, 16 * db + dd); }, lane);
+      float ce = 0.f;  // channel decay: this lane's part of the chunk end's dL/dG
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int t = 16 * tb_ + 4 * lg + ii, d = 16 * db + lr;
+        const bool ok = t < n;
         const long gi = (tok0 + t0 + t) * DK + d;
-        const float kv = Elem<E>::get(sm.k[t * PK + d]), qv = Elem<E>::get(sm.q[t * PK + d]);
-        const float wv = Elem<E>::get(sm.w[t * PK + d]);
+        const float kh = -akh[ii], qh = aqh[ii], tw = atw[ii];
+        const float sk = ask[ii], sq = asq[ii], sw = asw[ii];
+        const float kv = kf(t, d), qv = qf(t, d), wv = wf(t, d);
         if constexpr (CHAN) {
           // g_t = exp(G_r) exp(G_t - G_r); g_n / g_t = exp(G_n - G_r) exp(G_r - G_t)
           const float er = eref(t, d), gr = sm.gref[d], gt = sm.gnr[d];
-          atomicAdd(&a.dk_out[gi], gr * er * kh);
-          atomicAdd(&a.dq_out[gi], gr * er * qh);
-          atomicAdd(&a.dw_acc[gi], gt / er * tw);
           const float wtw = gt * wv * tw;
-          atomicAdd(&a.dG[gi], gr * (kv * kh + qv * qh) - wtw);
-          atomicAdd(&sm.endc[d], wtw);
+          if (ok) {
+            atomicAdd(&a.dk_out[gi], er * fmaf(gr, kh, sk));
+            atomicAdd(&a.dq_out[gi], er * fmaf(gr, qh, sq));
+            atomicAdd(&a.dw_acc[gi], fmaf(gt, tw, sw) / er);
+            atomicAdd(&a.dG[gi], gr * (kv * kh + qv * qh) - wtw + kv * sk + qv * sq - wv * sw);
+            ce += wtw;
+          }
         } else {
           const float g = sm.gam[t], f = gn / g;
-          atomicAdd(&a.dk_out[gi], g * kh);
-          atomicAdd(&a.dq_out[gi], g * qh);
-          atomicAdd(&a.dw_acc[gi], f * tw);
           const float wtw = f * wv * tw;
-          atomicAdd(&sm.sg[t], g * (kv * kh + qv * qh) - wtw);
-          atomicAdd(&sm.sg[CH - 1], wtw);
+          if (ok) {
+            atomicAdd(&a.dk_out[gi], fmaf(g, kh, sk));
+            atomicAdd(&a.dq_out[gi], fmaf(g, qh, sq));
+            atomicAdd(&a.dw_acc[gi], fmaf(f, tw, sw));
+            wend += wtw;
+          }
+          const float row = row16_sum(ok ? g * (kv * kh + qv * qh) - wtw : 0.f);
+          if (lr == 0 && ok) atomicAdd(&sm.sg[t], row);
         }
       }
+      if constexpr (CHAN) {
+        ce = col4_sum(ce);
+        if (lg == 0) atomicAdd(&sm.endc[16 * db + lr], ce);
+      }
+    }
+    if constexpr (!CHAN) {
+      wend = wave_sum(wend);
+      if (lane == 0) atomicAdd(&sm.sg[CH - 1], wend);
     }
     __syncthreads();
     // the chunk end's dL/dG per channel is complete
@@ -360,73 +576,17 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
       if (tid < DK) atomicAdd(&a.dG[(tok0 + t0 + n - 1) * DK + tid], sm.endc[tid]);
     }
     // dS_in = g_n dS_out + sum_t g_t (q_t dO_t^T - k_t dR_t^T)
-    for (int idx = tid; idx < DK * DVS; idx += NT) {
-      const int d = idx / DVS, cc = idx % DVS;
-      float s = 0.f;
-      for (int t = 0; t < n; ++t)
-        s = fmaf(CHAN ? 1.f : sm.gam[t],
-                 Elem<E>::get(sm.q[t * PK + d]) * sm.x[t * PS + cc] -
-                     Elem<E>::get(sm.k[t * PK + d]) * sm.y[t * PS + cc],
-                 s);
-      if constexpr (CHAN)
-        sm.dS[d * PS + cc] = sm.gref[d] * fmaf(sm.gnr[d], sm.dS[d * PS + cc], s);
-      else
-        sm.dS[d * PS + cc] = fmaf(gn, sm.dS[d * PS + cc], s);
-    }
-    // dL = -dR E^T, dM = dO E^T.  Scalar decay: their decay terms (L o dL,
-    // M o dM: + to the row token, - to the column token), then L <- D o dL,
-    // M <- D o dM.  Channel decay: L <- dL, M <- dM (the decay terms follow
-    // per channel below)
-    for (int idx = tid; idx < CH * CH; idx += NT) {
-      const int j = idx / CH, i = idx % CH;
-      if (j >= n || i > j) continue;
-      float dl = 0.f, dmv = 0.f;
-      for (int cc = 0; cc < DVS; ++cc) {
-        const float ev = sm.e[i * PS + cc];
-        dl = fmaf(-sm.y[j * PS + cc], ev, dl);
-        dmv = fmaf(sm.x[j * PS + cc], ev, dmv);
-      }
-      if constexpr (CHAN) {
-        sm.lm[j * PC + i] = i < j ? dl : 0.f;
-        sm.mm[j * PC + i] = dmv;
-      } else {
-        const float dm = expf(sm.G[j] - sm.G[i]);
-        const float tl = i < j ? sm.lm[j * PC + i] * dl : 0.f, tm = sm.mm[j * PC + i] * dmv;
-        if (i < j) {
-          atomicAdd(&sm.sg[j], tl + tm);
-          atomicAdd(&sm.sg[i], -(tl + tm));
-        }
-        sm.lm[j * PC + i] = i < j ? dm * dl : 0.f;
-        sm.mm[j * PC + i] = dm * dmv;
-      }
-    }
-    __syncthreads();
-    // dk += sum_{i<t} (D o dL)_ti w_i,  dq += sum_{i<=t} (D o dM)_ti w_i,
-    // dw_i += sum_{j>i} (D o dL)_ji k_j + sum_{j>=i} (D o dM)_ji q_j
-    for (int idx = tid; idx < CH * DK; idx += NT) {
-      const int t = idx / DK, d = idx % DK;
-      if (t >= n) continue;
-      float sk = 0.f, sq = 0.f, sw = 0.f;
-      for (int i = 0; i <= t; ++i) {
-        const float wv = Elem<E>::get(sm.w[i * PK + d]);
-        sk = fmaf(sm.lm[t * PC + i], wv, sk);
-        sq = fmaf(sm.mm[t * PC + i], wv, sq);
-      }
-      for (int j = t; j < n; ++j)
-        sw = fmaf(sm.lm[j * PC + t], Elem<E>::get(sm.k[j * PK + d]),
-                  fmaf(sm.mm[j * PC + t], Elem<E>::get(sm.q[j * PK + d]), sw));
-      const long gi = (tok0 + t0 + t) * DK + d;
-      if constexpr (CHAN) {
-        const float er = eref(t, d);
-        atomicAdd(&a.dk_out[gi], er * sk);
-        atomicAdd(&a.dq_out[gi], er * sq);
-        atomicAdd(&a.dw_acc[gi], sw / er);
-        atomicAdd(&a.dG[gi], Elem<E>::get(sm.k[t * PK + d]) * sk + Elem<E>::get(sm.q[t * PK + d]) * sq -
-                                 Elem<E>::get(sm.w[t * PK + d]) * sw);
-      } else {
-        atomicAdd(&a.dk_out[gi], sk);
-        atomicAdd(&a.dq_out[gi], sq);
-        atomicAdd(&a.dw_acc[gi], sw);
+    for (int tile = wave; tile < ND * NC; tile += NW) {
+      const int db = tile / NC, cb = tile % NC;
+      f32x4 acc = mm(zero4(), 0, CH, [&](int r, int k_) { return CHAN ? qf(k_, 16 * db + r) : sm.gam[k_] * qf(k_, 16 * db + r); },
+                     [&](int k_, int cc) { return sm.x[k_ * PS + 16 * cb + cc]; }, lane);
+      acc = mm(acc, 0, CH, [&](int r, int k_) { return CHAN ? -kf(k_, 16 * db + r) : -sm.gam[k_] * kf(k_, 16 * db + r); },
+               [&](int k_, int cc) { return sm.y[k_ * PS + 16 * cb + cc]; }, lane);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int d = 16 * db + 4 * lg + ii;
+        float& s = sm.dS[d * PS + 16 * cb + lr];
+        s = CHAN ? sm.gref[d] * fmaf(sm.gnr[d], s, acc[ii]) : fmaf(gn, s, acc[ii]);
       }
     }
     // scalar decay: dL/dG of the chunk to HBM; the padding tokens of a

@@ -497,36 +497,14 @@ DN_EXPORT int dn_decode_step(const dn_desc* d, const void* q, const void* k, con
                                       static_cast<hipStream_t>(stream)));
 }
 
-DN_EXPORT int dn_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, const float* aux0,
-                           float* w_out, float* g_out, float* aux_chunk, float* aux_final, void* ws,
-                           size_t ws_bytes, void* stream) {
-  int st = check_desc(d, true);
-  if (st != DN_OK) return st;
-  if ((st = check_gates(d, g)) != DN_OK) return st;
-  if (!k || !w_out) return DN_ERR_NULL;
-  const PrepLayout lay = prep_layout(d);
-  if (lay.total > 0 && (!ws || ws_bytes < lay.total)) return DN_ERR_WORKSPACE;
+// The gain scans of dn_gain_prep on validated arguments; ws holds at least
+// prep_layout(d).total bytes when that is not zero.
+static int run_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, const float* aux0,
+                         float* w_out, float* g_out, float* aux_chunk, float* aux_final, void* ws,
+                         hipStream_t s) {
   const bool has_aux = has_aux_state(d);
-  const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
-  const size_t es = io_size(d->io);
   const size_t nch = (static_cast<size_t>(d->T) + d->C - 1) / d->C;
-  const size_t aph = aux_per_head(d);
-  Range in[16];
-  int n = gate_ranges(d, g, in);
-  in[n++] = {k, bht * d->dk * es};
-  in[n++] = {has_aux ? aux0 : nullptr, static_cast<size_t>(d->B) * d->H * aph * 4};
-  Range outs[5] = {{w_out, bht * d->dk * 4},
-                   {g_out, g_out ? bht * (d->decay == DN_DECAY_CHANNEL ? d->dk : 1) * 4 : 0},
-                   {has_aux ? aux_chunk : nullptr, static_cast<size_t>(d->B) * d->H * nch * aph * 4},
-                   {has_aux ? aux_final : nullptr, static_cast<size_t>(d->B) * d->H * aph * 4},
-                   {lay.total > 0 ? ws : nullptr, lay.total}};
-  for (int j = 0; j < 5; ++j) {
-    for (int i = 0; i < n; ++i)
-      if (overlap(outs[j], in[i])) return DN_ERR_ALIAS;
-    for (int i = j + 1; i < 5; ++i)
-      if (overlap(outs[j], outs[i])) return DN_ERR_ALIAS;
-  }
-  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const PrepLayout lay = prep_layout(d);
   dn::GainPrepArgs a;
   a.B = d->B;
   a.H = d->H;
@@ -577,6 +555,39 @@ DN_EXPORT int dn_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, c
                                          d->decay == DN_DECAY_CHANNEL, s));
 }
 
+DN_EXPORT int dn_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, const float* aux0,
+                           float* w_out, float* g_out, float* aux_chunk, float* aux_final, void* ws,
+                           size_t ws_bytes, void* stream) {
+  int st = check_desc(d, true);
+  if (st != DN_OK) return st;
+  if ((st = check_gates(d, g)) != DN_OK) return st;
+  if (!k || !w_out) return DN_ERR_NULL;
+  const PrepLayout lay = prep_layout(d);
+  if (lay.total > 0 && (!ws || ws_bytes < lay.total)) return DN_ERR_WORKSPACE;
+  const bool has_aux = has_aux_state(d);
+  const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
+  const size_t es = io_size(d->io);
+  const size_t nch = (static_cast<size_t>(d->T) + d->C - 1) / d->C;
+  const size_t aph = aux_per_head(d);
+  Range in[16];
+  int n = gate_ranges(d, g, in);
+  in[n++] = {k, bht * d->dk * es};
+  in[n++] = {has_aux ? aux0 : nullptr, static_cast<size_t>(d->B) * d->H * aph * 4};
+  Range outs[5] = {{w_out, bht * d->dk * 4},
+                   {g_out, g_out ? bht * (d->decay == DN_DECAY_CHANNEL ? d->dk : 1) * 4 : 0},
+                   {has_aux ? aux_chunk : nullptr, static_cast<size_t>(d->B) * d->H * nch * aph * 4},
+                   {has_aux ? aux_final : nullptr, static_cast<size_t>(d->B) * d->H * aph * 4},
+                   {lay.total > 0 ? ws : nullptr, lay.total}};
+  for (int j = 0; j < 5; ++j) {
+    for (int i = 0; i < n; ++i)
+      if (overlap(outs[j], in[i])) return DN_ERR_ALIAS;
+    for (int i = j + 1; i < 5; ++i)
+      if (overlap(outs[j], outs[i])) return DN_ERR_ALIAS;
+  }
+  return run_gain_prep(d, k, g, aux0, w_out, g_out, aux_chunk, aux_final, ws,
+                       static_cast<hipStream_t>(stream));
+}
+
 // ---------------------------------------------------------------------------
 // dn_chunk_fwd_noalloc: dn_chunk_fwd with the workspace in a file-scope
 // device array, for callers that cannot allocate.  Every device the library
@@ -624,9 +635,10 @@ DN_EXPORT int dn_chunk_fwd_noalloc(const dn_desc* d, const void* q, const void* 
 // [B, H, T, dk], S_ck [B, H, nch, dk, dv], E [B, H, T, dv], dw_acc
 // [B, H, T, dk], dG ([B, H, T]; channel decay [B, H, T, dk]), then for the
 // gains with a statistic the statistic entering every chunk ([B, H, nch, dk];
-// KDN_ISO [B, H, nch]).
+// KDN_ISO [B, H, nch]), and the workspace of the gain scans (as for
+// dn_gain_prep).
 struct BwdLayout {
-  size_t w, sck, e, dw, dg, aux, total;
+  size_t w, sck, e, dw, dg, aux, prep, total;
 };
 
 static BwdLayout bwd_layout(const dn_desc* d) {
@@ -640,7 +652,8 @@ static BwdLayout bwd_layout(const dn_desc* d) {
   L.dw = round256(L.e + bht * d->dv * 4);
   L.dg = round256(L.dw + bht * d->dk * 4);
   L.aux = round256(L.dg + bht * gdim * 4);
-  L.total = L.aux + (has_aux_state(d) ? bh * nch * aux_per_head(d) * 4 : 0);
+  L.prep = round256(L.aux + (has_aux_state(d) ? bh * nch * aux_per_head(d) * 4 : 0));
+  L.total = L.prep + prep_layout(d).total;
   return L;
 }
 
@@ -753,20 +766,11 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
       (pg && dn::launch_zero(gr->dmu_log, d->H, s) != hipSuccess))
     return DN_ERR_HIP;
   const dn::GateArgs ga = gate_args(d, g);
-  // the write vectors (and PGDN's statistic entering every chunk)
-  dn::GainPrepArgs gp;
-  gp.B = d->B;
-  gp.H = d->H;
-  gp.T = d->T;
-  gp.dk = d->dk;
-  gp.k = k;
-  gp.g = ga;
-  gp.aux0 = has_aux ? aux0 : nullptr;
-  gp.w_out = w_ws;
-  gp.g_out = nullptr;
-  gp.aux_chunk = aux_chunk;
-  gp.aux_final = nullptr;
-  if (dn::launch_gain_prep(gp, d->io == DN_BF16, d->gain, chan, s) != hipSuccess) return DN_ERR_HIP;
+  // the write vectors (and the statistic entering every chunk), chunks in
+  // parallel where T is whole chunks
+  if ((st = run_gain_prep(d, k, g, has_aux ? aux0 : nullptr, w_ws, nullptr, aux_chunk, nullptr,
+                          wb + lay.prep, s)) != DN_OK)
+    return st;
   // the memory recurrence backwards, chunk by chunk
   dn::BwdArgs b;
   b.B = d->B;
@@ -813,5 +817,11 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
   gb.domega = kd ? gr->domega : nullptr;
   gb.dr = kd ? gr->dr : nullptr;
   gb.daux0 = has_aux ? gr->daux0 : nullptr;
+  if (!has_aux && d->T % d->C == 0) {
+    // no statistic carried between chunks: every chunk is independent (a head
+    // of the [B, H nch, C] view)
+    gb.H = static_cast<int>(d->H * (d->T / d->C));
+    gb.T = d->C;
+  }
   return hip_status(dn::launch_gain_bwd(gb, d->io == DN_BF16, d->gain, chan, s));
 }

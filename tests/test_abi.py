@@ -293,7 +293,7 @@ def test_chunk_bwd_rejects_bad_arguments():
     dk_ = _desc(B=2, H=3, T=100, decay="channel", gain="kdn")
     assert L.dn_chunk_bwd_workspace(ctypes.byref(dk_)) == r256(sizec) + 6 * nch * 128 * 4
     di = _desc(B=2, H=3, T=100, gain="kdn_iso")
-    assert L.dn_chunk_bwd_workspace(ctypes.byref(di)) == r256(size) + 6 * nch * 4
+    assert L.dn_chunk_bwd_workspace(ctypes.byref(di)) == r256(r256(size) + 6 * nch * 4)
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -105,3 +105,16 @@ def test_chunk_bwd_kdn_information_scaling_and_strong_decay():
                     mu_info=128.0, alpha_mean=0.0, seed=771)
     got, ref = _run(wl, wl.seed + 1)
     _compare(wl, got, ref, _names("kdn"))
+
+
+# Whole chunks (T a multiple of 64, at least two): the gain scans run chunk
+# by chunk in parallel, and so does the gain backward of the gains without a
+# statistic.
+@pytest.mark.parametrize("gain,decay,keys", [("kla", "scalar", "scaled"), ("gdn", "channel", "unit"),
+                                             ("pgdn", "scalar", "unit"), ("kdn", "channel", "scaled"),
+                                             ("kdn_iso", "channel", "scaled"), ("explicit", "scalar", "unit")])
+def test_chunk_bwd_whole_chunks(gain, decay, keys):
+    wl = W.Workload(f"bwd_{gain}_{decay}_whole", gain, decay, "bf16", 2, 2, 256, 128, 128, keys=keys,
+                    mu_spread=0.5, seed=800)
+    got, ref = _run(wl, wl.seed + 1)
+    _compare(wl, got, ref, _names(gain))
