@@ -292,9 +292,18 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
       const int tr = tile >> 2, tc = tile & 3;
       f32x4 al = zero4(), am = zero4();
       if (tr >= tc) {
-        auto fw = [&](int k_, int c) { return wf(16 * tc + c, k_); };
-        al = mm(al, 0, DK, [&](int r, int k_) { return kf(16 * tr + r, k_); }, fw, lane);
-        if (with_m) am = mm(am, 0, DK, [&](int r, int k_) { return qf(16 * tr + r, k_); }, fw, lane);
+        if (with_m) {
+#pragma unroll 4
+          for (int k0 = 0; k0 < DK; k0 += 4) {
+            const int k_ = k0 + lg;
+            const float wv = wf(16 * tc + lr, k_);
+            al = mfma4(kf(16 * tr + lr, k_), wv, al);
+            am = mfma4(qf(16 * tr + lr, k_), wv, am);
+          }
+        } else {
+          al = mm(al, 0, DK, [&](int r, int k_) { return kf(16 * tr + r, k_); },
+                  [&](int k_, int c) { return wf(16 * tc + c, k_); }, lane);
+        }
       }
       const int i = 16 * tc + lr;
 #pragma unroll
@@ -470,9 +479,14 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
     for (int tile = wave; tile < 16; tile += NW) {
       const int tr = tile >> 2, tc = tile & 3;
       if (tr < tc) continue;
-      auto fe = [&](int k_, int ii_) { return sm.e[(16 * tc + ii_) * PS + k_]; };
-      const f32x4 al = mm(zero4(), 0, DVS, [&](int r, int k_) { return sm.y[(16 * tr + r) * PS + k_]; }, fe, lane);
-      const f32x4 am = mm(zero4(), 0, DVS, [&](int r, int k_) { return sm.x[(16 * tr + r) * PS + k_]; }, fe, lane);
+      f32x4 al = zero4(), am = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < DVS; k0 += 4) {
+        const int k_ = k0 + lg;
+        const float ev = sm.e[(16 * tc + lr) * PS + k_];
+        al = mfma4(sm.y[(16 * tr + lr) * PS + k_], ev, al);
+        am = mfma4(sm.x[(16 * tr + lr) * PS + k_], ev, am);
+      }
       const int i = 16 * tc + lr;
       float col = 0.f;  // scalar decay: - (L o dL + M o dM) summed over this lane's rows
 #pragma unroll
@@ -516,18 +530,32 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
 #pragma unroll 1
     for (int tile = wave; tile < 4 * ND; tile += NW) {
       const int tb_ = tile / ND, db = tile % ND;
-      auto fS = [&](int k_, int dd) { return sm.S[(16 * db + dd) * PS + k_]; };
-      const f32x4 akh = mm(zero4(), 0, DVS, [&](int r, int k_) { return sm.y[(16 * tb_ + r) * PS + k_]; }, fS, lane);
-      const f32x4 aqh = mm(zero4(), 0, DVS, [&](int r, int k_) { return sm.x[(16 * tb_ + r) * PS + k_]; }, fS, lane);
-      const f32x4 atw = mm(zero4(), 0, DVS, [&](int r, int k_) { return sm.e[(16 * tb_ + r) * PS + k_]; },
-                           [&](int k_, int dd) { return sm.dS[(16 * db + dd) * PS + k_]; }, lane);
-      auto fw = [&](int k_, int dd) { return wf(k_, 16 * db + dd); };
-      const f32x4 ask = mm(zero4(), 0, 16 * (tb_ + 1), [&](int r, int k_) { return sm.lm[(16 * tb_ + r) * PC + k_]; }, fw, lane);
-      const f32x4 asq = mm(zero4(), 0, 16 * (tb_ + 1), [&](int r, int k_) { return sm.mm[(16 * tb_ + r) * PC + k_]; }, fw, lane);
-      f32x4 asw = mm(zero4(), 16 * tb_, CH, [&](int r, int k_) { return sm.lm[k_ * PC + 16 * tb_ + r]; },
-                     [&](int k_, int dd) { return kf(k_, 16 * db + dd); }, lane);
-      asw = mm(asw, 16 * tb_, CH, [&](int r, int k_) { return sm.mm[k_ * PC + 16 * tb_ + r]; },
-               [&](int k_, int dd) { return qf(k_, 16 * db + dd); }, lane);
+      // the tile's products, independent chains interleaved (operands as
+      // for mm: A row lr, B column lr, k = 4 s + lg)
+      f32x4 akh = zero4(), aqh = zero4(), atw = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < DVS; k0 += 4) {
+        const int k_ = k0 + lg;
+        const float sv = sm.S[(16 * db + lr) * PS + k_];
+        akh = mfma4(sm.y[(16 * tb_ + lr) * PS + k_], sv, akh);
+        aqh = mfma4(sm.x[(16 * tb_ + lr) * PS + k_], sv, aqh);
+        atw = mfma4(sm.e[(16 * tb_ + lr) * PS + k_], sm.dS[(16 * db + lr) * PS + k_], atw);
+      }
+      f32x4 ask = zero4(), asq = zero4(), asw = zero4(), asw2 = zero4();
+#pragma unroll 4
+      for (int k0 = 0; k0 < 16 * (tb_ + 1); k0 += 4) {
+        const int k_ = k0 + lg;
+        const float wv = wf(k_, 16 * db + lr);
+        ask = mfma4(sm.lm[(16 * tb_ + lr) * PC + k_], wv, ask);
+        asq = mfma4(sm.mm[(16 * tb_ + lr) * PC + k_], wv, asq);
+      }
+#pragma unroll 4
+      for (int k0 = 16 * tb_; k0 < CH; k0 += 4) {
+        const int k_ = k0 + lg;
+        asw = mfma4(sm.lm[k_ * PC + 16 * tb_ + lr], kf(k_, 16 * db + lr), asw);
+        asw2 = mfma4(sm.mm[k_ * PC + 16 * tb_ + lr], qf(k_, 16 * db + lr), asw2);
+      }
+      asw += asw2;
       float ce = 0.f;  // channel decay: this lane's part of the chunk end's dL/dG
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
@@ -578,10 +606,15 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
     // dS_in = g_n dS_out + sum_t g_t (q_t dO_t^T - k_t dR_t^T)
     for (int tile = wave; tile < ND * NC; tile += NW) {
       const int db = tile / NC, cb = tile % NC;
-      f32x4 acc = mm(zero4(), 0, CH, [&](int r, int k_) { return CHAN ? qf(k_, 16 * db + r) : sm.gam[k_] * qf(k_, 16 * db + r); },
-                     [&](int k_, int cc) { return sm.x[k_ * PS + 16 * cb + cc]; }, lane);
-      acc = mm(acc, 0, CH, [&](int r, int k_) { return CHAN ? -kf(k_, 16 * db + r) : -sm.gam[k_] * kf(k_, 16 * db + r); },
-               [&](int k_, int cc) { return sm.y[k_ * PS + 16 * cb + cc]; }, lane);
+      f32x4 acc = zero4(), acc2 = zero4();
+#pragma unroll 4
+      for (int k0 = 0; k0 < CH; k0 += 4) {
+        const int k_ = k0 + lg;
+        const float gk = CHAN ? 1.f : sm.gam[k_];
+        acc = mfma4(gk * qf(k_, 16 * db + lr), sm.x[k_ * PS + 16 * cb + lr], acc);
+        acc2 = mfma4(gk * kf(k_, 16 * db + lr), sm.y[k_ * PS + 16 * cb + lr], acc2);
+      }
+      acc -= acc2;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int d = 16 * db + 4 * lg + ii;
