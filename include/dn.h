@@ -115,8 +115,20 @@ typedef enum dn_decay { DN_DECAY_SCALAR = 0, DN_DECAY_CHANNEL = 1 } dn_decay;
 /* Problem descriptor (host struct).
  *   B, H >= 1, B H <= 65535; T >= 0 (T = 0: S_final = S0, aux_final = aux0,
  *   o untouched);
- *   dk in {64, 128}; dv any multiple of 64 up to 2048 (d_v = v_expand d_k);
- *   C = 64 (chunk length of the chunked forward);
+ *   dk a multiple of 8 up to 128; dv a multiple of 8 up to 128, or any
+ *   multiple of 64 up to 2048 (d_v = v_expand d_k).  The kernels are built
+ *   for dk in {64, 128} and dv a multiple of 64; other widths (the 120-wide
+ *   heads of Preconditioned DeltaNet §3.1, for example) run on them: the
+ *   chunked calls on zero-padded copies in the workspace (key channels with
+ *   k = q = w = 0 and decay 1, value columns with v = 0, the outputs cropped
+ *   back; isotropic KDN's mu rescaled so that mu ||k||^2 / (d_k r) keeps its
+ *   value), the decode step masked in place.  Isotropic KDN with channel
+ *   decay at such a d_k (the mean of alpha^2 over the channels has no padded
+ *   form), fp32 io with dk > 64, the backward and the segmented call at such
+ *   widths return DN_ERR_UNSUPPORTED;
+ *   C = 64, the chunk length of the chunked forward and backward; dn_gain_prep
+ *   also takes C = 32 (its per-chunk outputs and parallel scan pieces: the
+ *   memory chunk of 32 or 64 tokens of Kalman Delta Networks Appendix D);
  *   io: dn_dtype of q, k, v, o and of per-channel gates;
  *   gain: dn_gain; decay: dn_decay (KDN requires DN_DECAY_CHANNEL or SCALAR);
  *   eps >= 0 (KLA), x >= 1 (PGDN bound: B in [1/x, x];
@@ -157,7 +169,11 @@ typedef struct dn_gates {
  *   dn_gain_prep: the gains with a statistic (PGDN, KDN, KDN_ISO), bf16 io
  *     and T a multiple of C (at least two chunks) scan every chunk in
  *     parallel; the workspace holds the chunks' piece summaries, the
- *     statistic entering every chunk and PGDN's centre repeated per chunk. */
+ *     statistic entering every chunk and PGDN's centre repeated per chunk.
+ *   Head widths no kernel is built for: the padded call's own workspace,
+ *   then the padded copies of the inputs and outputs (each on a 256-byte
+ *   boundary).
+ *   C = 32 is valid for dn_gain_prep only: the size is then its need. */
 size_t dn_workspace_bytes(const dn_desc* desc);
 
 /* Chunked forward over a whole sequence batch (Kaczmarz Linear Attention

@@ -42,9 +42,12 @@ constexpr int DECODE_THREADS = 256;
 // or 128 columns).  WIDE: a head of d_v = a.dv columns (v_expand d_k, a
 // multiple of DV) is walked slice by slice by the same workgroup, whose
 // write gain is formed once; one workgroup per head keeps the in-place update
-// of the gain's statistic (aux) free of races between value slices.  Without
-// WIDE, d_v = DV and every stride is a compile-time constant.
-template <typename IO, int DK, int DV, int GAIN, bool CHANNEL, bool WIDE>
+// of the gain's statistic (aux) free of races between value slices.  PAD: a
+// head narrower than the instance (d_k = a.dk <= DK, d_v = a.dv <= DV, both
+// multiples of 8): the missing key channels and value columns are neither
+// read nor written and count as zero.  Otherwise d_k = DK, d_v = DV and
+// every stride is a compile-time constant.
+template <typename IO, int DK, int DV, int GAIN, bool CHANNEL, bool WIDE, bool PAD>
 __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs a) {
   constexpr int CG = DV / 4;                   // float4 column groups
   constexpr int RG = DECODE_THREADS / CG;      // row groups
@@ -61,36 +64,40 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
   const long nh = blockIdx.x;  // n * H + h
   const int h = static_cast<int>(nh % a.H);
   const int cg = tid % CG, rg = tid / CG;
-  const int dv = WIDE ? a.dv : DV, ncg = dv / 4, nsl = dv / DV;
-  f32x4* Sp = reinterpret_cast<f32x4*>(a.S + nh * DK * dv);
+  const int dk = PAD ? a.dk : DK;
+  const int dv = WIDE || PAD ? a.dv : DV, ncg = dv / 4, nsl = PAD ? 1 : dv / DV;
+  f32x4* Sp = reinterpret_cast<f32x4*>(a.S + nh * dk * dv);
+  // PAD: this thread's state columns, and whether state row r exists
+  const bool col_in = !PAD || cg < ncg;
+  auto row_in = [&](int r) { return !PAD || (r < dk && col_in); };
 
   // 1. issue the state loads of the first slice first: they are the bulk of
   // the traffic.
   f32x4 s[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
-    s[i] = __builtin_nontemporal_load(Sp + (rg + RG * i) * ncg + cg);
+    s[i] = row_in(rg + RG * i) ? __builtin_nontemporal_load(Sp + (rg + RG * i) * ncg + cg) : zero4();
 
-  // 2. token inputs and the write gain (threads d < DK own key channel d).
+  // 2. token inputs and the write gain (threads d < d_k own key channel d).
   float red1 = 0.f, red2 = 0.f, red3 = 0.f;
   float kd = 0.f, qd = 0.f, ad = 0.f, pre = 0.f, aux_new = 0.f, mu_over_r = 0.f;
-  if (tid < DV) s_v[tid] = L::at(a.v, nh * dv + tid);
-  if (tid < DK) {
-    kd = L::at(a.k, nh * DK + tid);
-    qd = L::at(a.q, nh * DK + tid);
-    ad = CHANNEL ? L::at(a.alpha, nh * DK + tid) : static_cast<const float*>(a.alpha)[nh];
+  if (tid < DV) s_v[tid] = !PAD || tid < dv ? L::at(a.v, nh * dv + tid) : 0.f;
+  if (tid < dk) {
+    kd = L::at(a.k, nh * dk + tid);
+    qd = L::at(a.q, nh * dk + tid);
+    ad = CHANNEL ? L::at(a.alpha, nh * dk + tid) : static_cast<const float*>(a.alpha)[nh];
     if (GAIN == GAIN_KLA) {
       red1 = kd * kd;
       red2 = kd * qd;
     } else if (GAIN == GAIN_GDN) {
       red2 = kd * qd;
     } else if (GAIN == GAIN_PGDN) {
-      const float A = pgdn_stat(a.aux[nh * DK + tid], a.alphaP[nh], a.betaP[nh], kd);
+      const float A = pgdn_stat(a.aux[nh * dk + tid], a.alphaP[nh], a.betaP[nh], kd);
       aux_new = A;
       pre = a.eta[nh] * pgdn_scale(A, a.mu_log[h], a.log2x) * kd;
       red2 = pre * qd;
     } else if (GAIN == GAIN_KDN) {
-      const float ph = kdn_predict(ad, a.aux[nh * DK + tid], L::at(a.omega, nh * DK + tid));
+      const float ph = kdn_predict(ad, a.aux[nh * dk + tid], L::at(a.omega, nh * dk + tid));
       pre = ph * kd;
       red1 = pre * kd;
       red2 = pre * qd;
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
       red2 = kd * qd;
       red3 = ad * ad;
     } else {  // explicit
-      pre = L::at(a.w, nh * DK + tid);
+      pre = L::at(a.w, nh * dk + tid);
       red2 = pre * qd;
     }
   }
@@ -125,13 +132,13 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
   float iso_beta = 0.f, iso_b = 0.f;
   if (GAIN == GAIN_KDN_ISO) {
     const float as = CHANNEL ? 0.f : static_cast<const float*>(a.alpha)[nh];
-    const float a2 = CHANNEL ? sum3 * (1.0f / DK) : as * as;
+    const float a2 = CHANNEL ? sum3 / static_cast<float>(dk) : as * as;
     const float bh = kdn_iso_predict(a2, a.aux[nh], static_cast<const float*>(a.omega)[nh]);
     iso_beta = kdn_iso_beta(bh, a.r[nh], sum1);
-    iso_b = kdn_iso_update(bh, sum1, a.mu_info / (DK * a.r[nh]));
+    iso_b = kdn_iso_update(bh, sum1, a.mu_info / (dk * a.r[nh]));
   }
   float wq;  // w . q
-  if (tid < DK) {
+  if (tid < dk) {
     float wd;
     if (GAIN == GAIN_KLA) {
       const float beta = kla_beta(a.eta[nh], sum1, a.eps);
@@ -149,7 +156,13 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
     s_a[tid] = ad;
     s_ak[tid] = ad * kd;
     s_aq[tid] = ad * qd;
-    if (GAIN == GAIN_PGDN || GAIN == GAIN_KDN) a.aux[nh * DK + tid] = aux_new;
+    if (GAIN == GAIN_PGDN || GAIN == GAIN_KDN) a.aux[nh * dk + tid] = aux_new;
+  } else if (PAD && tid < DK) {
+    // missing key channels: no write, no decay term, no readout
+    s_w[tid] = 0.f;
+    s_a[tid] = 0.f;
+    s_ak[tid] = 0.f;
+    s_aq[tid] = 0.f;
   }
   if (GAIN == GAIN_KLA) wq = kla_beta(a.eta[nh], sum1, a.eps) * sum2;
   else if (GAIN == GAIN_GDN) wq = a.eta[nh] * sum2;
@@ -198,7 +211,7 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
       }
       const float e = s_v[tid] - yk;
       s_e[tid] = e;
-      L::store(a.o, nh * dv + c0 + tid, fmaf(wq, e, yq));
+      if (!PAD || tid < dv) L::store(a.o, nh * dv + c0 + tid, fmaf(wq, e, yq));
     }
     __syncthreads();
 
@@ -212,16 +225,16 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
       f32x4 o4;
 #pragma unroll
       for (int j = 0; j < 4; ++j) o4[j] = fmaf(dec, s[i][j], wr * e4[j]);
-      __builtin_nontemporal_store(o4, Sp + r * ncg + c0 / 4 + cg);
+      if (row_in(r)) __builtin_nontemporal_store(o4, Sp + r * ncg + c0 / 4 + cg);
     }
   }
 }
 
-template <typename IO, int DK, int DV, bool WIDE>
+template <typename IO, int DK, int DV, bool WIDE, bool PAD = false>
 static hipError_t launch_decode_w(const DecodeArgs& a, int gain, bool channel, hipStream_t st) {
   dim3 grid(static_cast<unsigned>(a.N * a.H)), block(DECODE_THREADS);
 #define DN_DEC(G, CH) \
-  hipLaunchKernelGGL((decode_step_kernel<IO, DK, DV, G, CH, WIDE>), grid, block, 0, st, a)
+  hipLaunchKernelGGL((decode_step_kernel<IO, DK, DV, G, CH, WIDE, PAD>), grid, block, 0, st, a)
   switch (gain) {
     case GAIN_KLA: if (channel) DN_DEC(GAIN_KLA, true); else DN_DEC(GAIN_KLA, false); break;
     case GAIN_GDN: if (channel) DN_DEC(GAIN_GDN, true); else DN_DEC(GAIN_GDN, false); break;
@@ -240,8 +253,23 @@ static hipError_t launch_decode_io(const DecodeArgs& a, int gain, bool channel, 
                     : launch_decode_w<IO, DK, DV, true>(a, gain, channel, st);
 }
 
+// heads narrower than the instances (d_k, d_v multiples of 8 up to 128, not
+// 64 / 128-wide): the instance of the next widths, with masking
+template <typename IO>
+static hipError_t launch_decode_pad(const DecodeArgs& a, int gain, bool channel, hipStream_t st) {
+  if (a.dk <= 64 && a.dv <= 64) return launch_decode_w<IO, 64, 64, false, true>(a, gain, channel, st);
+  if (a.dk <= 64) return launch_decode_w<IO, 64, 128, false, true>(a, gain, channel, st);
+  if (a.dv <= 64) return launch_decode_w<IO, 128, 64, false, true>(a, gain, channel, st);
+  return launch_decode_w<IO, 128, 128, false, true>(a, gain, channel, st);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int io_bf16, int gain, bool channel, hipStream_t st) {
   if (a.N * a.H == 0) return hipSuccess;
+  if (!((a.dk == 64 || a.dk == 128) && a.dv % 64 == 0)) {
+    if (a.dk > 128 || a.dv > 128 || a.dk % 8 != 0 || a.dv % 8 != 0) return hipErrorInvalidValue;
+    return io_bf16 ? launch_decode_pad<uint16_t>(a, gain, channel, st)
+                   : launch_decode_pad<float>(a, gain, channel, st);
+  }
   // value slices of 128 columns where d_v allows, else of 64
   const bool w128 = a.dv % 128 == 0;
 #define DN_SHAPE(IO)                                                                  \

@@ -14,10 +14,29 @@
 
 namespace {
 
-bool valid_dim(int d) { return d == 64 || d == 128; }
-// value width: d_v = v_expand d_k, any multiple of 64 up to 2048 (the kernels
-// walk 64- or 128-column value slices)
-bool valid_dv(int d) { return d >= 64 && d <= 2048 && d % 64 == 0; }
+// key width: a multiple of 8 up to 128 (the kernels are built for 64 and
+// 128; other widths run on them zero-padded, see pad.hip)
+bool valid_dim(int d) { return d >= 8 && d <= 128 && d % 8 == 0; }
+// value width: a multiple of 8 up to 128, or d_v = v_expand d_k, a multiple of
+// 64 up to 2048 (the kernels walk 64- or 128-column value slices)
+bool valid_dv(int d) { return d >= 8 && d <= 2048 && d % 8 == 0 && (d <= 128 || d % 64 == 0); }
+// the widths the kernels are built for
+bool kernel_dims(const dn_desc* d) { return (d->dk == 64 || d->dk == 128) && d->dv % 64 == 0; }
+// the kernel widths a head of other widths runs at.  Isotropic KDN divides
+// by d_k (u = mu ||k||^2 / (d_k r)): mu is scaled so that the padded call
+// computes the same u.
+dn_desc padded_desc(const dn_desc* d) {
+  dn_desc p = *d;
+  p.dk = d->dk <= 64 ? 64 : 128;
+  p.dv = (d->dv + 63) / 64 * 64;
+  if (d->gain == DN_GAIN_KDN_ISO) p.mu_info = d->mu_info * static_cast<float>(p.dk) / d->dk;
+  return p;
+}
+// Padding keeps every gain except isotropic KDN with channel decay, whose
+// mean of alpha^2 over the channels no padded decay value preserves.
+bool paddable(const dn_desc* d) {
+  return kernel_dims(d) || !(d->gain == DN_GAIN_KDN_ISO && d->decay == DN_DECAY_CHANNEL);
+}
 
 size_t io_size(int io) { return io == DN_BF16 ? 2 : 4; }
 
@@ -163,10 +182,11 @@ static LongLayout long_layout(const dn_desc* d, int nseg) {
 }
 
 static bool long_shape_ok(const dn_desc* d, int nseg) {
-  return nseg >= 1 && d->T % nseg == 0 && (d->T / nseg) % d->C == 0;
+  return kernel_dims(d) && nseg >= 1 && d->T % nseg == 0 && (d->T / nseg) % d->C == 0;
 }
 
-// Aliasing checks of a segmented run against its workspace range.
+// Aliasing checks of a run that works on copies in the workspace (by
+// segments, or padded) against its workspace range.
 static int check_long_aliases(const dn_desc* d, const dn_gates* g, const void* q, const void* k,
                               const void* v, const float* S0, const float* aux0, void* o,
                               float* S_final, float* aux_final, const void* ws, size_t ws_used) {
@@ -174,14 +194,15 @@ static int check_long_aliases(const dn_desc* d, const dn_gates* g, const void* q
   const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
   const size_t sbytes = static_cast<size_t>(d->B) * d->H * d->dk * d->dv * 4;
   const size_t abytes = static_cast<size_t>(d->B) * d->H * aux_per_head(d) * 4;
+  const size_t es = io_size(d->io);
   Range in[16];
   int n = gate_ranges(d, g, in);
-  in[n++] = {q, bht * d->dk * 2};
-  in[n++] = {k, bht * d->dk * 2};
-  in[n++] = {v, bht * d->dv * 2};
+  in[n++] = {q, bht * d->dk * es};
+  in[n++] = {k, bht * d->dk * es};
+  in[n++] = {v, bht * d->dv * es};
   in[n++] = {S0, S0 ? sbytes : 0};
   in[n++] = {has_aux ? aux0 : nullptr, abytes};
-  const Range ro{o, bht * d->dv * 2}, rs{S_final, S_final ? sbytes : 0},
+  const Range ro{o, bht * d->dv * es}, rs{S_final, S_final ? sbytes : 0},
       ra{has_aux ? aux_final : nullptr, abytes}, rw{ws, ws_used};
   for (int i = 0; i < n; ++i) {
     // S_final may be S0 exactly and aux_final aux0 (in-place resume): the
@@ -340,14 +361,69 @@ static PrepLayout prep_layout(const dn_desc* d) {
   return L;
 }
 
+// Heads of widths no kernel is built for (padded_desc): the call runs at the
+// padded widths on copies in the workspace.  After the padded call's own
+// workspace come the padded inputs and outputs, each on a 256-byte boundary
+// (a region of 0 bytes where the gain or decay has no such tensor).
+struct PadLayout {
+  size_t inner;                     // the padded call's workspace, at offset 0
+  size_t q, k, v, o, al, om, w;     // io tensors [B, H, T, d]
+  size_t s0, sf;                    // S0, S_final [B, H, dk, dv]
+  size_t a0, af;                    // per-channel aux0 / aux_final [B, H, dk]
+  size_t wo, go, ac;                // dn_gain_prep: w_out, g_out, aux_chunk
+  size_t total;
+};
+
+static bool per_channel_aux(const dn_desc* d) { return d->gain == DN_GAIN_PGDN || d->gain == DN_GAIN_KDN; }
+
+static size_t chunk_ws_bytes(const dn_desc* d);
+
+// prep: the layout of dn_gain_prep, else of dn_chunk_fwd
+static PadLayout pad_layout(const dn_desc* d, bool prep) {
+  const dn_desc p = padded_desc(d);
+  const size_t bh = static_cast<size_t>(d->B) * d->H, bht = bh * d->T, es = io_size(d->io);
+  const size_t nch = (static_cast<size_t>(d->T) + d->C - 1) / d->C;
+  const bool chan = d->decay == DN_DECAY_CHANNEL, pca = per_channel_aux(d);
+  PadLayout L{};
+  L.inner = prep ? prep_layout(&p).total : chunk_ws_bytes(&p);
+  size_t off = round256(L.inner);
+  auto take = [&](bool on, size_t bytes) {
+    const size_t at = off;
+    if (on) off = round256(off + bytes);
+    return at;
+  };
+  L.q = take(!prep, bht * p.dk * es);
+  L.k = take(true, bht * p.dk * es);
+  L.v = take(!prep, bht * p.dv * es);
+  L.o = take(!prep, bht * p.dv * es);
+  L.al = take(chan, bht * p.dk * es);
+  L.om = take(d->gain == DN_GAIN_KDN, bht * p.dk * es);
+  L.w = take(d->gain == DN_GAIN_EXPLICIT, bht * p.dk * es);
+  L.s0 = take(!prep, bh * p.dk * p.dv * 4);
+  L.sf = take(!prep, bh * p.dk * p.dv * 4);
+  L.a0 = take(pca, bh * p.dk * 4);
+  L.af = take(pca, bh * p.dk * 4);
+  L.wo = take(prep, bht * p.dk * 4);
+  L.go = take(prep && chan, bht * p.dk * 4);
+  L.ac = take(prep && pca, bh * nch * p.dk * 4);
+  L.total = off;
+  return L;
+}
+
 static size_t chunk_ws_bytes(const dn_desc* d) {
+  if (!kernel_dims(d)) return pad_layout(d, false).total;
   const int nseg = auto_nseg(d);
   return nseg > 1 ? long_layout(d, nseg).total : 0;
 }
 
+static size_t prep_ws_bytes(const dn_desc* d) {
+  return kernel_dims(d) ? prep_layout(d).total : pad_layout(d, true).total;
+}
+
 DN_EXPORT size_t dn_workspace_bytes(const dn_desc* d) {
-  if (check_desc(d, true) != DN_OK) return 0;
-  const size_t a = chunk_ws_bytes(d), b = prep_layout(d).total;
+  if (check_desc(d, false) != DN_OK || (d->C != 64 && d->C != 32) || !paddable(d)) return 0;
+  // dn_chunk_fwd needs C = 64; dn_gain_prep takes either chunk length
+  const size_t a = d->C == 64 ? chunk_ws_bytes(d) : 0, b = prep_ws_bytes(d);
   return a > b ? a : b;
 }
 
@@ -376,6 +452,73 @@ DN_EXPORT int dn_chunk_fwd_long(const dn_desc* d, int nseg, const void* q, const
                   static_cast<hipStream_t>(stream));
 }
 
+// Copies [outer][rs][cs] -> [outer][rd][cd] (padding with `fill`, or
+// cropping); false once a launch failed.
+struct Reshaper {
+  hipStream_t s;
+  bool ok = true;
+  void operator()(const void* src, void* dst, long outer, int rs, int cs, int rd, int cd, int esize,
+                  uint32_t fill = 0) {
+    ok = ok && dn::launch_reshape3(src, dst, outer, rs, cs, rd, cd, esize, fill, s) == hipSuccess;
+  }
+};
+
+constexpr uint32_t ONE_F32 = 0x3F800000u, ONE_BF16 = 0x3F80u;
+
+// dn_chunk_fwd of a head whose widths no kernel is built for, on validated
+// arguments: the inputs padded into the workspace (key channels with k = q =
+// w = 0, decay 1, omega 0, statistic 1; value columns with v = 0), the call
+// at the padded widths, the outputs cropped back.
+static int run_padded_fwd(const dn_desc* d, const PadLayout& L, const void* q, const void* k,
+                          const void* v, const dn_gates* g, const float* S0, const float* aux0,
+                          void* o, float* S_final, float* aux_final, void* ws, hipStream_t s) {
+  const dn_desc p = padded_desc(d);
+  char* wb = static_cast<char*>(ws);
+  const long bh = static_cast<long>(d->B) * d->H, bht = bh * d->T;
+  const int es = static_cast<int>(io_size(d->io));
+  const uint32_t one_io = d->io == DN_BF16 ? ONE_BF16 : ONE_F32;
+  const bool pca = per_channel_aux(d);
+  Reshaper copy{s};
+  dn_gates gp = g ? *g : dn_gates{};
+  if (d->T > 0) {
+    copy(q, wb + L.q, bht, 1, d->dk, 1, p.dk, es);
+    copy(k, wb + L.k, bht, 1, d->dk, 1, p.dk, es);
+    copy(v, wb + L.v, bht, 1, d->dv, 1, p.dv, es);
+    if (d->decay == DN_DECAY_CHANNEL) {
+      copy(g->alpha, wb + L.al, bht, 1, d->dk, 1, p.dk, es, one_io);
+      gp.alpha = reinterpret_cast<const float*>(wb + L.al);
+    }
+    if (d->gain == DN_GAIN_KDN) {
+      copy(g->omega, wb + L.om, bht, 1, d->dk, 1, p.dk, es);
+      gp.omega = wb + L.om;
+    }
+    if (d->gain == DN_GAIN_EXPLICIT) {
+      copy(g->w, wb + L.w, bht, 1, d->dk, 1, p.dk, es);
+      gp.w = wb + L.w;
+    }
+  }
+  float* S0p = nullptr;
+  if (S0) {
+    S0p = reinterpret_cast<float*>(wb + L.s0);
+    copy(S0, S0p, bh, d->dk, d->dv, p.dk, p.dv, 4);
+  }
+  const float* aux0p = aux0;
+  if (pca && aux0) {
+    aux0p = reinterpret_cast<const float*>(wb + L.a0);
+    copy(aux0, wb + L.a0, bh, 1, d->dk, 1, p.dk, 4, ONE_F32);
+  }
+  float* Sfp = S_final ? reinterpret_cast<float*>(wb + L.sf) : nullptr;
+  float* afp = pca ? (aux_final ? reinterpret_cast<float*>(wb + L.af) : nullptr) : aux_final;
+  if (!copy.ok) return DN_ERR_HIP;
+  const int st = dn_chunk_fwd(&p, wb + L.q, wb + L.k, wb + L.v, &gp, S0p, aux0p, wb + L.o, Sfp, afp,
+                              ws, L.inner, s);
+  if (st != DN_OK) return st;
+  if (d->T > 0) copy(wb + L.o, o, bht, 1, p.dv, 1, d->dv, es);
+  if (S_final) copy(Sfp, S_final, bh, p.dk, p.dv, d->dk, d->dv, 4);
+  if (pca && aux_final) copy(afp, aux_final, bh, 1, p.dk, 1, d->dk, 4);
+  return copy.ok ? DN_OK : DN_ERR_HIP;
+}
+
 DN_EXPORT int dn_chunk_fwd(const dn_desc* d, const void* q, const void* k, const void* v,
                            const dn_gates* g, const float* S0, const float* aux0, void* o,
                            float* S_final, float* aux_final, void* ws, size_t ws_bytes,
@@ -386,7 +529,8 @@ DN_EXPORT int dn_chunk_fwd(const dn_desc* d, const void* q, const void* k, const
     if ((st = check_gates(d, g)) != DN_OK) return st;
     if (!q || !k || !v || !o) return DN_ERR_NULL;
   }
-  if (d->io == DN_F32 && d->dk != 64) return DN_ERR_UNSUPPORTED;
+  if (d->io == DN_F32 && d->dk > 64) return DN_ERR_UNSUPPORTED;
+  if (!paddable(d)) return DN_ERR_UNSUPPORTED;
   const size_t need = chunk_ws_bytes(d);
   if (need > 0 && (!ws || ws_bytes < need)) return DN_ERR_WORKSPACE;
 
@@ -414,6 +558,16 @@ DN_EXPORT int dn_chunk_fwd(const dn_desc* d, const void* q, const void* k, const
     if (overlap(ra, in[i])) return DN_ERR_ALIAS;
   }
   if (overlap(ro, rs) || overlap(ro, ra) || overlap(rs, ra)) return DN_ERR_ALIAS;
+
+  // widths no kernel is built for: padded copies in the workspace
+  if (!kernel_dims(d)) {
+    const PadLayout L = pad_layout(d, false);
+    if ((st = check_long_aliases(d, g, q, k, v, S0, aux0, o, S_final, aux_final, ws, L.total)) !=
+        DN_OK)
+      return st;
+    return run_padded_fwd(d, L, q, k, v, g, S0, aux0, o, S_final, aux_final, ws,
+                          static_cast<hipStream_t>(stream));
+  }
 
   // few heads: the same forward by segments, on the workspace
   const int nseg = auto_nseg(d);
@@ -517,6 +671,7 @@ static int run_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, con
   a.g_out = g_out;
   a.aux_chunk = has_aux ? aux_chunk : nullptr;
   a.aux_final = has_aux ? aux_final : nullptr;
+  a.C = d->C;
   // Whole chunks: every chunk is scanned by its own workgroup, as a head of
   // the [B, H nch, C] view of the [B, H, T] tensors.  The gains with a
   // statistic first get the statistic entering every chunk from the
@@ -555,15 +710,65 @@ static int run_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, con
                                          d->decay == DN_DECAY_CHANNEL, s));
 }
 
+// dn_gain_prep of a head whose key width no kernel is built for, on validated
+// arguments: the inputs padded into the workspace as for run_padded_fwd, the
+// scans at the padded width, the outputs cropped back.
+static int run_padded_prep(const dn_desc* d, const PadLayout& L, const void* k, const dn_gates* g,
+                           const float* aux0, float* w_out, float* g_out, float* aux_chunk,
+                           float* aux_final, void* ws, hipStream_t s) {
+  const dn_desc p = padded_desc(d);
+  char* wb = static_cast<char*>(ws);
+  const long bh = static_cast<long>(d->B) * d->H, bht = bh * d->T;
+  const long nch = (d->T + d->C - 1) / d->C;
+  const int es = static_cast<int>(io_size(d->io));
+  const uint32_t one_io = d->io == DN_BF16 ? ONE_BF16 : ONE_F32;
+  const bool pca = per_channel_aux(d), chan = d->decay == DN_DECAY_CHANNEL;
+  Reshaper copy{s};
+  dn_gates gp = *g;
+  copy(k, wb + L.k, bht, 1, d->dk, 1, p.dk, es);
+  if (chan) {
+    copy(g->alpha, wb + L.al, bht, 1, d->dk, 1, p.dk, es, one_io);
+    gp.alpha = reinterpret_cast<const float*>(wb + L.al);
+  }
+  if (d->gain == DN_GAIN_KDN) {
+    copy(g->omega, wb + L.om, bht, 1, d->dk, 1, p.dk, es);
+    gp.omega = wb + L.om;
+  }
+  if (d->gain == DN_GAIN_EXPLICIT) {
+    copy(g->w, wb + L.w, bht, 1, d->dk, 1, p.dk, es);
+    gp.w = wb + L.w;
+  }
+  const float* aux0p = aux0;
+  if (pca && aux0) {
+    aux0p = reinterpret_cast<const float*>(wb + L.a0);
+    copy(aux0, wb + L.a0, bh, 1, d->dk, 1, p.dk, 4, ONE_F32);
+  }
+  float* wop = reinterpret_cast<float*>(wb + L.wo);
+  float* gop = chan ? (g_out ? reinterpret_cast<float*>(wb + L.go) : nullptr) : g_out;
+  float* acp = pca ? (aux_chunk ? reinterpret_cast<float*>(wb + L.ac) : nullptr) : aux_chunk;
+  float* afp = pca ? (aux_final ? reinterpret_cast<float*>(wb + L.af) : nullptr) : aux_final;
+  if (!copy.ok) return DN_ERR_HIP;
+  const int st = run_gain_prep(&p, wb + L.k, &gp, aux0p, wop, gop, acp, afp, ws, s);
+  if (st != DN_OK) return st;
+  copy(wop, w_out, bht, 1, p.dk, 1, d->dk, 4);
+  if (chan && g_out) copy(gop, g_out, bht, 1, p.dk, 1, d->dk, 4);
+  if (pca && aux_chunk) copy(acp, aux_chunk, bh * nch, 1, p.dk, 1, d->dk, 4);
+  if (pca && aux_final) copy(afp, aux_final, bh, 1, p.dk, 1, d->dk, 4);
+  return copy.ok ? DN_OK : DN_ERR_HIP;
+}
+
 DN_EXPORT int dn_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, const float* aux0,
                            float* w_out, float* g_out, float* aux_chunk, float* aux_final, void* ws,
                            size_t ws_bytes, void* stream) {
-  int st = check_desc(d, true);
+  int st = check_desc(d, false);
   if (st != DN_OK) return st;
+  if (d->C != 64 && d->C != 32) return DN_ERR_SHAPE;
+  if (d->io == DN_F32 && d->dk > 64) return DN_ERR_UNSUPPORTED;
+  if (!paddable(d)) return DN_ERR_UNSUPPORTED;
   if ((st = check_gates(d, g)) != DN_OK) return st;
   if (!k || !w_out) return DN_ERR_NULL;
-  const PrepLayout lay = prep_layout(d);
-  if (lay.total > 0 && (!ws || ws_bytes < lay.total)) return DN_ERR_WORKSPACE;
+  const size_t need = prep_ws_bytes(d);
+  if (need > 0 && (!ws || ws_bytes < need)) return DN_ERR_WORKSPACE;
   const bool has_aux = has_aux_state(d);
   const size_t bht = static_cast<size_t>(d->B) * d->H * d->T;
   const size_t es = io_size(d->io);
@@ -577,13 +782,16 @@ DN_EXPORT int dn_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, c
                    {g_out, g_out ? bht * (d->decay == DN_DECAY_CHANNEL ? d->dk : 1) * 4 : 0},
                    {has_aux ? aux_chunk : nullptr, static_cast<size_t>(d->B) * d->H * nch * aph * 4},
                    {has_aux ? aux_final : nullptr, static_cast<size_t>(d->B) * d->H * aph * 4},
-                   {lay.total > 0 ? ws : nullptr, lay.total}};
+                   {need > 0 ? ws : nullptr, need}};
   for (int j = 0; j < 5; ++j) {
     for (int i = 0; i < n; ++i)
       if (overlap(outs[j], in[i])) return DN_ERR_ALIAS;
     for (int i = j + 1; i < 5; ++i)
       if (overlap(outs[j], outs[i])) return DN_ERR_ALIAS;
   }
+  if (!kernel_dims(d))
+    return run_padded_prep(d, pad_layout(d, true), k, g, aux0, w_out, g_out, aux_chunk, aux_final, ws,
+                           static_cast<hipStream_t>(stream));
   return run_gain_prep(d, k, g, aux0, w_out, g_out, aux_chunk, aux_final, ws,
                        static_cast<hipStream_t>(stream));
 }
@@ -660,6 +868,7 @@ static BwdLayout bwd_layout(const dn_desc* d) {
 // every gain and decay; io bf16 with dk 64 or 128, fp32 with dk 64; dv a
 // multiple of the value slice (16 columns with channel decay, 32 with scalar)
 static int bwd_supported(const dn_desc* d) {
+  if (!kernel_dims(d)) return DN_ERR_UNSUPPORTED;
   if (d->io == DN_F32 && d->dk != 64) return DN_ERR_UNSUPPORTED;
   if (d->dv % (d->decay == DN_DECAY_CHANNEL ? 16 : 32) != 0) return DN_ERR_UNSUPPORTED;
   return DN_OK;

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(DK) void gain_prep_kernel(GainPrepArgs a) {
   const long bh = blockIdx.x;
   const int h = static_cast<int>(bh % a.H);
   const int T = a.T;
-  constexpr int C = 64;
+  const int C = a.C;
   float st = a.aux0 ? a.aux0[ISO ? bh : bh * DK + d] : 1.f;
   float G = 0.f;
   const float mu = GAIN == GAIN_PGDN ? a.g.mu_log[h] : 0.f;

@@ -88,6 +88,7 @@ hipError_t launch_segment_stats(const StatArgs& a, hipStream_t st);
 
 struct GainPrepArgs {
   int B, H, T, dk;
+  int C;  // chunk length of the per-chunk outputs (g_out, aux_chunk): 32 or 64
   const void* k;
   GateArgs g;
   const float* aux0;  // nullable
@@ -147,6 +148,10 @@ struct GainBwdArgs {
 };
 hipError_t launch_gain_bwd(const GainBwdArgs& a, int io_bf16, int gain, bool channel,
                            hipStream_t st);
+// [outer][rs][cs] -> [outer][rd][cd] (pad.hip): copy where r < rs and
+// c < cs, `fill_bits` (the element's bit pattern) elsewhere; esize 2 or 4.
+hipError_t launch_reshape3(const void* src, void* dst, long outer, int rs, int cs, int rd, int cd,
+                           int esize, uint32_t fill_bits, hipStream_t st);
 // Zero n floats (a plain fill kernel, so that callers may capture it).
 hipError_t launch_zero(float* p, size_t n, hipStream_t st);
 

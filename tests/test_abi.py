@@ -71,7 +71,7 @@ def _desc(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dk=96), -2), (dict(dv=32), -2), (dict(dv=96), -2), (dict(dv=4096), -2), (dict(B=0), -2), (dict(H=0), -2), (dict(T=-1), -2),
+    (dict(dk=100), -2), (dict(dk=136), -2), (dict(dk=0), -2), (dict(dv=36), -2), (dict(dv=200), -2), (dict(dv=4096), -2), (dict(B=0), -2), (dict(H=0), -2), (dict(T=-1), -2),
     (dict(B=300, H=300), -2), (dict(io=7), -3), (dict(gain=9), -4), (dict(decay=3), -4),
     (dict(eps=-1.0), -4), (dict(gain="pgdn", x=0.5), -4), (dict(gain="kdn", mu_info=0.0), -4),
     (dict(gain="kdn_iso", mu_info=-1.0), -4), (dict(gain=6), -4),
@@ -122,8 +122,9 @@ def test_decode_rejects_bad_arguments():
     assert f(_desc(T=2)) == -2
     assert f(_desc(T=1), S=None) == -1
     assert f(_desc(T=1, gain="pgdn")) == -1
-    assert f(_desc(T=1, dk=48)) == -2
-    assert f(_desc(T=1, dv=96)) == -2  # value heads are multiples of 64 columns
+    assert f(_desc(T=1, dk=50)) == -2  # head widths are multiples of 8
+    assert f(_desc(T=1, dv=100)) == -2
+    assert f(_desc(T=1, dv=200)) == -2  # wide value heads are multiples of 64 columns
     assert f(_desc(T=1, dv=4096)) == -2
 
 
@@ -134,7 +135,7 @@ def test_gain_prep_rejects_bad_arguments():
     gp = lambda desc, k, w, ws=None, nbytes=0, gates=g: L.dn_gain_prep(
         ctypes.byref(desc), k, ctypes.byref(gates), None, w, None, None, None, ws, nbytes, None)
     assert gp(d, FAKE, None) == -1
-    assert gp(_desc(dk=80), FAKE, FAKE + (7 << 30)) == -2
+    assert gp(_desc(dk=81), FAKE, FAKE + (7 << 30)) == -2
     # w_out overlapping k
     assert gp(d, FAKE + (3 << 30), FAKE + (3 << 30)) == -8
     # PGDN over whole chunks scans them in parallel and needs its workspace
@@ -248,7 +249,7 @@ def test_noalloc_rejects_workspace_beyond_scratch():
                                                FAKE + (4 << 30), ctypes.byref(gp), None, None,
                                                FAKE + (5 << 30), None, None, None)
     assert call(d) == -5
-    assert call(_desc(dk=96)) == -2
+    assert call(_desc(dk=100)) == -2
 
 
 def test_chunk_bwd_rejects_bad_arguments():
@@ -302,3 +303,33 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_narrow_heads_workspace_and_limits():
+    """Head widths no kernel is built for (multiples of 8 up to 128) run on
+    padded copies in the workspace: dn_workspace_bytes sizes them, the
+    unpaddable combination (isotropic KDN with channel decay) and fp32 keys
+    wider than 64 are refused, the backward and the segmented call refuse
+    them, and dn_gain_prep takes C = 32."""
+    L = dn.lib()
+    r256 = lambda x: (x + 255) // 256 * 256
+    d = _desc(B=2, H=3, T=100, dk=120, dv=120)
+    bht, bh = 2 * 3 * 100, 6
+    # q, k, v, o padded (bf16), S0 and S_final padded (fp32); KLA has no other tensor
+    want = 4 * r256(bht * 128 * 2) + 2 * r256(bh * 128 * 128 * 4)
+    assert L.dn_workspace_bytes(ctypes.byref(d)) == want
+    assert L.dn_workspace_bytes(ctypes.byref(_desc(dk=120, dv=120, gain="kdn_iso", decay="channel"))) == 0
+    gk = _gates(omega=FAKE + (6 << 30), r=FAKE + (7 << 30))
+    assert _chunk(_desc(dk=120, dv=120, gain="kdn_iso", decay="channel"), gates=gk) == -6
+    assert _chunk(_desc(io=0, dk=120, dv=64)) == -6
+    assert L.dn_chunk_bwd_workspace(ctypes.byref(d)) == 0
+    assert L.dn_chunk_fwd_long_workspace(ctypes.byref(_desc(B=1, H=1, T=4096, dk=120, dv=120)), 4) == 0
+    # workspace missing or short for the padded copies
+    assert _chunk(d) == -5
+    assert _chunk(d, ws=FAKE + (30 << 30), nbytes=want - 256) == -5
+    # C = 32: the gain scans only
+    d32 = _desc(B=2, H=3, T=128, C=32, gain="pgdn")
+    assert L.dn_workspace_bytes(ctypes.byref(d32)) > 0
+    gp = _gates(alphaP=FAKE + (6 << 30), betaP=FAKE + (7 << 30), mu_log=FAKE + (8 << 30))
+    assert _chunk(d32, gates=gp) == -2
+    assert _desc(C=16).C == 16 and L.dn_workspace_bytes(ctypes.byref(_desc(C=16))) == 0

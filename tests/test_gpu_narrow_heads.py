@@ -1,0 +1,146 @@
+"""GPU parity of head widths no kernel is built for (multiples of 8 up to
+128, e.g. the 120-wide heads of Preconditioned DeltaNet §3.1's 1B
+architecture) and of the gain scans' 32-token chunks (Kalman Delta Networks
+Appendix D: memory chunks of 32 or 64), against the fp64 oracle.
+
+dn_chunk_fwd and dn_gain_prep run such heads on zero-padded copies at the
+next kernel width; dn_decode_step masks the missing channels and columns in
+place.  Bars as for the other parity tests: 1e-4 (fp32 io) and 2e-2 (bf16)
+on o and S_T, 1e-5 / 1e-3 on the gain statistics.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle.recurrence import run_workload
+from parity import TOL, flat_heads, gpu_chunk, max_rel_err, oracle_chunk
+from recurrent_sequence_mixer_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(wl, inp, o, S, aux):
+    o_ref, S_ref, aux_ref = oracle_chunk(wl, inp)
+    eo, es = max_rel_err(flat_heads(o), o_ref), max_rel_err(flat_heads(S), S_ref)
+    print(f"{wl.name} {wl.dk}x{wl.dv} T={wl.T}: o {eo:.2e} S {es:.2e}", flush=True)
+    assert eo <= TOL[wl.io] and es <= TOL[wl.io]
+    if aux_ref is not None:
+        ea = max_rel_err(flat_heads(aux), aux_ref)
+        print(f"   aux {ea:.2e}", flush=True)
+        assert ea <= (1e-5 if wl.io == "f32" else 1e-3)
+
+
+@pytest.mark.parametrize("T", [150, 256])
+@pytest.mark.parametrize("gain,decay,keys,io,dk,dv", [
+    ("kla", "scalar", "scaled", "bf16", 120, 120), ("gdn", "channel", "unit", "bf16", 120, 120),
+    ("kdn", "channel", "scaled", "bf16", 120, 120), ("pgdn", "scalar", "unit", "bf16", 120, 120),
+    ("kdn_iso", "scalar", "scaled", "bf16", 120, 120), ("kla", "scalar", "scaled", "bf16", 128, 120),
+    ("pgdn", "channel", "unit", "bf16", 120, 64), ("kla", "scalar", "scaled", "f32", 40, 48),
+    ("kdn", "channel", "scaled", "f32", 56, 24)])
+def test_narrow_heads_chunk_fwd(gain, decay, keys, io, dk, dv, T):
+    wl = W.Workload(f"narrow_{gain}_{decay}_{io}", gain, decay, io, 2, 3, T, dk, dv, keys=keys,
+                    mu_spread=0.5, seed=900 + dk + dv + T)
+    inp = W.generate(wl)
+    if gain in ("pgdn", "kdn"):
+        inp["aux0"] = np.random.default_rng(5).uniform(0.5, 2.0, (2, 3, dk)).astype(np.float32)
+    o, S, aux = gpu_chunk(wl, inp)
+    _check(wl, inp, o, S, aux)
+
+
+def test_narrow_heads_in_place_resume():
+    """S_final = S0 (in-place resume; aux_final goes to a second buffer, as
+    dn_chunk_fwd requires) at d = 120: two calls over the halves of the
+    sequence equal one call over all of it."""
+    from recurrent_sequence_mixer_amd import dn
+    wl = W.Workload("narrow_resume", "kdn", "channel", "bf16", 2, 2, 256, 120, 120, seed=950)
+    inp = W.generate(wl)
+    t = dn.to_device(inp, torch.bfloat16)
+    S = t["S0"].clone()
+    aux = torch.ones((2, 2, 120), device="cuda")
+    aux2 = torch.empty_like(aux)
+    outs = []
+    for h0 in (0, 128):
+        part = lambda n: t[n][:, :, h0:h0 + 128].contiguous()
+        gates = {"alpha": part("alpha"), "omega": part("omega"), "r": part("r")}
+        o, _, _ = dn.chunk_fwd(part("q"), part("k"), part("v"), gates, gain="kdn", mu_info=wl.mu_info,
+                               S0=S, aux0=aux, S_final=S, aux_final=aux2)
+        aux, aux2 = aux2, aux
+        outs.append(o)
+    torch.cuda.synchronize()
+    o = torch.cat(outs, dim=2).float().cpu().numpy()
+    _check(wl, inp, o, S.cpu().numpy(), aux.cpu().numpy())
+
+
+@pytest.mark.parametrize("gain,decay,io,dk,dv", [
+    ("kla", "scalar", "bf16", 120, 120), ("kdn", "channel", "bf16", 120, 120),
+    ("kdn_iso", "channel", "bf16", 120, 120), ("pgdn", "scalar", "bf16", 120, 64),
+    ("gdn", "channel", "f32", 40, 120)])
+def test_narrow_heads_decode(gain, decay, io, dk, dv):
+    """12 decode steps over 5 sequences x 3 heads of narrow widths (masked in
+    the decode kernel, no copies): o, S and the statistic against the oracle."""
+    from recurrent_sequence_mixer_amd import dn
+    keys = "unit" if gain in ("gdn", "pgdn") else "scaled"
+    wl = W.Workload("dec_narrow", gain, decay, io, 5, 3, 12, dk, dv, keys=keys, mu_spread=0.5, seed=960)
+    inp = W.generate(wl)
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    t = dn.to_device(inp, dt)
+    S = t["S0"].clone()
+    aux = torch.ones((5, 3, dk), device="cuda") if gain in ("pgdn", "kdn") else None
+    if gain == "kdn_iso":
+        aux = torch.ones((5, 3), device="cuda")
+    outs = []
+    for s in range(wl.T):
+        gates = {n: t[n][:, :, s].contiguous() for n in ("alpha", "eta", "alphaP", "betaP", "omega", "r")
+                 if n in t}
+        if "mu_log" in t:
+            gates["mu_log"] = t["mu_log"]
+        outs.append(dn.decode_step(t["q"][:, :, s].contiguous(), t["k"][:, :, s].contiguous(),
+                                   t["v"][:, :, s].contiguous(), gates, S, aux, gain=gain, eps=wl.eps,
+                                   x=wl.x, mu_info=wl.mu_info))
+    torch.cuda.synchronize()
+    o = torch.stack(outs, dim=2).float().cpu().numpy()
+    o_ref, S_ref, aux_ref, _ = run_workload(wl, inp)
+    eo, es = max_rel_err(flat_heads(o), o_ref), max_rel_err(flat_heads(S.cpu().numpy()), S_ref)
+    print(f"decode narrow {gain}/{decay}/{io} {dk}x{dv}: o {eo:.2e} S {es:.2e}", flush=True)
+    assert eo <= TOL[io] and es <= TOL[io]
+    if aux is not None:
+        assert max_rel_err(flat_heads(aux.cpu().numpy()), aux_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("C,T", [(32, 128), (32, 100), (64, 256)])
+@pytest.mark.parametrize("gain,decay,dk", [("pgdn", "scalar", 128), ("kdn", "channel", 128),
+                                           ("kdn_iso", "channel", 128), ("kdn", "channel", 120),
+                                           ("pgdn", "scalar", 120)])
+def test_gain_prep_chunk_length_and_narrow(gain, decay, dk, C, T):
+    """dn_gain_prep with chunks of C tokens (32: the short memory chunk of the
+    chunked gain scan; T = 128 scans the 32-token chunks in parallel, T = 100
+    one head at a time) and with 120-wide keys: per-token write vectors,
+    the statistic entering every chunk and the in-chunk log-decay."""
+    from recurrent_sequence_mixer_amd import dn
+    keys = "unit" if gain == "pgdn" else "scaled"
+    wl = W.Workload("gp_c", gain, decay, "bf16", 2, 3, T, dk, dk, keys=keys, mu_spread=1.0, seed=970)
+    inp = W.generate(wl)
+    rng = np.random.default_rng(971)
+    shape = (2, 3) if gain == "kdn_iso" else (2, 3, dk)
+    inp["aux0"] = rng.uniform(0.5, 2.0, size=shape).astype(np.float32)
+    t = dn.to_device(inp, torch.bfloat16)
+    gates = {n: t[n] for n in ("alpha", "eta", "alphaP", "betaP", "mu_log", "omega", "r") if n in t}
+    w, g, aux_chunk, aux_final = dn.gain_prep(t["k"], gates, gain=gain, eps=wl.eps, x=wl.x,
+                                              mu_info=wl.mu_info, aux0=t["aux0"], C=C)
+    torch.cuda.synchronize()
+    _, _, aux_ref, tr = run_workload(wl, inp, record=True, aux0=flat_heads(inp["aux0"]))
+    ew = max_rel_err(flat_heads(w.cpu().numpy()), tr["w"])
+    print(f"gain_prep {gain} dk {dk} C {C} T {T}: w {ew:.2e}", flush=True)
+    assert ew <= 1e-5
+    alpha = flat_heads(inp["alpha"]).astype(np.float64)
+    G = np.zeros_like(alpha)
+    for c0 in range(0, T, C):
+        G[:, c0:c0 + C] = np.cumsum(np.log(alpha[:, c0:c0 + C]), axis=1)
+    np.testing.assert_allclose(flat_heads(g.cpu().numpy()), G, rtol=1e-5, atol=1e-5)
+    assert max_rel_err(flat_heads(aux_final.cpu().numpy()), aux_ref) <= 1e-5
+    key = "A" if gain == "pgdn" else "p"
+    ac = flat_heads(aux_chunk.cpu().numpy())
+    assert ac.shape[1] == (T + C - 1) // C
+    np.testing.assert_array_equal(ac[:, 0], flat_heads(inp["aux0"]))
+    for ci, c0 in enumerate(range(C, T, C)):
+        assert max_rel_err(ac[:, ci + 1], tr[key][:, c0 - 1]) <= 1e-5
