@@ -118,3 +118,33 @@ def test_chunk_bwd_whole_chunks(gain, decay, keys):
                     mu_spread=0.5, seed=800)
     got, ref = _run(wl, wl.seed + 1)
     _compare(wl, got, ref, _names(gain))
+
+
+@pytest.mark.parametrize("B,H", [(8, 16), (1, 8)])
+def test_chunk_bwd_full_size_sampled_heads(B, H):
+    """The backward at the sizes bench.py times (KLA bf16, T 4096, d 128: the
+    headline workload's B8 H16 and the pages' operator shape B1 H8), every
+    head on the GPU in one call; two sampled heads' gradients against the
+    oracle run on those heads alone."""
+    from recurrent_sequence_mixer_amd import dn
+    wl = W.WORKLOADS[1] if (B, H) == (8, 16) else W.Workload("kla_bwd_B1H8T4096d128", "kla", "scalar",
+                                                            "bf16", 1, 8, 4096, 128, 128, seed=54)
+    inp = W.generate(wl)
+    rng = np.random.default_rng(wl.seed + 1)
+    dO = W.round_io(rng.standard_normal((wl.B, wl.H, wl.T, wl.dv)), wl.io)
+    dS_T = rng.standard_normal((wl.B, wl.H, wl.dk, wl.dv)).astype(np.float32)
+    t = dn.to_device(inp, torch.bfloat16)
+    gates = {n: t[n] for n in ("alpha", "eta")}
+    g = dn.chunk_bwd(t["q"], t["k"], t["v"], gates, torch.from_numpy(dO).cuda().to(torch.bfloat16),
+                     gain="kla", eps=wl.eps, S0=t["S0"], dS_T=torch.from_numpy(dS_T).cuda())
+    torch.cuda.synchronize()
+    heads = [1, wl.B * wl.H - 2]
+    got = {n: flat_heads(a.cpu().numpy())[heads] for n, a in g.items()}
+    fh = lambda a: flat_heads(a)[heads]
+    ref = backward(fh(inp["q"]), fh(inp["k"]), fh(inp["v"]), "kla", fh(inp["alpha"]), fh(dO),
+                   eta=fh(inp["eta"]), eps=wl.eps, S0=fh(inp["S0"]), dS_T=fh(dS_T))
+    worst = {n: max_rel_err(got[n], ref[n]) for n in ("q", "k", "v", "alpha", "S0", "eta")}
+    print(f"backward {wl.name} heads {heads}: " + " ".join(f"d{n} {e:.1e}" for n, e in worst.items()),
+          flush=True)
+    for n, e in worst.items():
+        assert e <= TOL["bf16"], (n, e)
