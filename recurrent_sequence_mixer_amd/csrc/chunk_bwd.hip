@@ -185,6 +185,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
   constexpr int TPW = 4 * ND / NW;  // [token][key] tiles per wavefront
   static_assert(TPW * NW == 4 * ND, "key tiles per wavefront");
   extern __shared__ __align__(16) unsigned char smem_raw[];
+  DN_LDS_POISON(smem_raw, sizeof(Sm));
   Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;  // tile column / row group of this lane
@@ -654,6 +655,9 @@ __global__ __launch_bounds__(DK) void gain_bwd_kernel(GainBwdArgs a) {
   __shared__ float red[4][NW];
   __shared__ float As[ST ? CH : 1][ST ? DK : 1];    // PGDN: A_t; KDN: p before token t
   __shared__ float iso[ISO ? 3 : 1][ISO ? CH : 1];  // KDN_ISO: b before token t, a_t, ||k_t||^2
+  DN_LDS_POISON(red, sizeof(red));
+  DN_LDS_POISON(As, sizeof(As));
+  DN_LDS_POISON(iso, sizeof(iso));
   const int d = threadIdx.x, wave = d >> 6, lane = d & 63;
   const long bh = blockIdx.x;
   const int h = static_cast<int>(bh % a.H);

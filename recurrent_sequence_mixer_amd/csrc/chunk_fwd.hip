@@ -188,6 +188,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
   using Frag = typename MM::Frag;
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
+  DN_LDS_POISON(smem_raw, sizeof(Sm));
   Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
   E* const sL = sm.lm;            // -L
   E* const sM = sm.lm + CH * PT;  // M

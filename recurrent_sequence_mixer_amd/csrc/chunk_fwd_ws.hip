@@ -293,6 +293,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
                 "statistic scan layout");
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
+  DN_LDS_POISON(smem_raw, sizeof(Sm));
   Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
 
   const int tid = threadIdx.x;

@@ -99,6 +99,24 @@ template <> struct Mma<float> {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Debug builds (-DDN_DEBUG): every byte of a kernel's LDS is set to all ones
+// (NaN as fp32 and as bf16) before the kernel's first LDS access, so that a
+// result depending on LDS that no thread wrote turns into NaN in the parity
+// tests.  Release builds compile DN_LDS_POISON to nothing.
+#ifdef DN_DEBUG
+#define DN_LDS_POISON(p, bytes)                                                              \
+  do {                                                                                       \
+    uint32_t* w_ = reinterpret_cast<uint32_t*>(p);                                           \
+    for (unsigned i_ = threadIdx.x; i_ < static_cast<unsigned>((bytes) / 4); i_ += blockDim.x) \
+      w_[i_] = 0xFFFFFFFFu;                                                                  \
+    __syncthreads();                                                                         \
+  } while (0)
+#else
+#define DN_LDS_POISON(p, bytes) \
+  do {                          \
+  } while (0)
+#endif
+
 // Sum over the 64 lanes of a wavefront.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

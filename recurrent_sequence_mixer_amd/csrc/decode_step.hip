@@ -59,6 +59,15 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_step_kernel(DecodeArgs 
   __shared__ __align__(16) float s_v[DV], s_e[DV];
   __shared__ float s_red[DECODE_THREADS / 64][3];
   __shared__ __align__(16) f32x4 s_yk[RG][CG], s_yq[RG][CG];
+  DN_LDS_POISON(s_a, sizeof(s_a));
+  DN_LDS_POISON(s_ak, sizeof(s_ak));
+  DN_LDS_POISON(s_aq, sizeof(s_aq));
+  DN_LDS_POISON(s_w, sizeof(s_w));
+  DN_LDS_POISON(s_v, sizeof(s_v));
+  DN_LDS_POISON(s_e, sizeof(s_e));
+  DN_LDS_POISON(s_red, sizeof(s_red));
+  DN_LDS_POISON(s_yk, sizeof(s_yk));
+  DN_LDS_POISON(s_yq, sizeof(s_yq));
 
   const int tid = threadIdx.x;
   const long nh = blockIdx.x;  // n * H + h

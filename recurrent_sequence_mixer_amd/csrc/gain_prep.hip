@@ -28,6 +28,7 @@ __global__ __launch_bounds__(DK) void gain_prep_kernel(GainPrepArgs a) {
   constexpr bool ISO = GAIN == GAIN_KDN_ISO;
   constexpr bool AUX = GAIN == GAIN_PGDN || GAIN == GAIN_KDN || ISO;
   __shared__ float s_part[2][2][NW];
+  DN_LDS_POISON(s_part, sizeof(s_part));
   const int d = threadIdx.x, wave = d >> 6, lane = d & 63;
   const long bh = blockIdx.x;
   const int h = static_cast<int>(bh % a.H);

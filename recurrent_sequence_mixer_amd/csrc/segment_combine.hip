@@ -33,6 +33,7 @@ __global__ __launch_bounds__(SC_THREADS) void segment_combine_kernel(CombineArgs
   // dynamic LDS: A_s [DK][DK + 4] (the pitch spreads the rows of a wavefront
   // over the banks), then the state [DK][4]
   extern __shared__ __align__(16) float sc_smem[];
+  DN_LDS_POISON(sc_smem, (DK * (DK + 4) + DK * SC_COLS) * sizeof(float));
   float (*sA)[DK + 4] = reinterpret_cast<float (*)[DK + 4]>(sc_smem);
   f32x4* sX = reinterpret_cast<f32x4*>(sc_smem + DK * (DK + 4));
 

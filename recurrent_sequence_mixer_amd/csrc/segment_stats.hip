@@ -108,6 +108,9 @@ __global__ __launch_bounds__(DK) __attribute__((amdgpu_waves_per_eu(1, 4))) void
 template <int DK, bool CHN>
 __global__ __launch_bounds__(256) void segment_summary_iso_kernel(StatArgs a) {
   __shared__ float f00[256], f01[256], f10[256];
+  DN_LDS_POISON(f00, sizeof(f00));
+  DN_LDS_POISON(f01, sizeof(f01));
+  DN_LDS_POISON(f10, sizeof(f10));
   const int i = threadIdx.x;
   const int nsub = a.T / a.lsub;
   const long bh = blockIdx.x / nsub;

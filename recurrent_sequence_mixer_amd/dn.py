@@ -12,7 +12,13 @@ from typing import Dict, Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdn.so")
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# The library; DN_LIBRARY names another build of it (the checking builds next
+# to it: libdn_debug.so with LDS poisoning, libdn_hostasan.so with the host
+# code under AddressSanitizer).
+LIB_PATH = os.environ.get("DN_LIBRARY") or os.path.join(_HERE, "libdn.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libdn_debug.so")
+HOSTASAN_LIB_PATH = os.path.join(_HERE, "libdn_hostasan.so")
 
 DN_OK = 0
 STATUS = {0: "DN_OK", -1: "DN_ERR_NULL", -2: "DN_ERR_SHAPE", -3: "DN_ERR_DTYPE", -4: "DN_ERR_GAIN",
@@ -52,6 +58,13 @@ class DnError(RuntimeError):
 
 
 _lib = None
+
+
+def use_library(path: str) -> None:
+    """Load another build of the library (same ABI) for the calls that follow."""
+    global _lib, LIB_PATH
+    LIB_PATH = path
+    _lib = None
 
 
 def lib() -> ctypes.CDLL:
