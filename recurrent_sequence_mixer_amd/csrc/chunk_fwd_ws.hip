@@ -1445,15 +1445,15 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
   }
 }
 
-// Two entry points over the same body.  The one for the gains formed from
-// the staging registers, with an output (KLA, GDN, explicit w), states that
-// three wavefronts per SIMD is its occupancy (768 threads per workgroup allow
-// no more): the compiler's scheduler then keeps the LDS reads of the
-// consumers' products ahead of their MFMAs instead of waiting on each in
-// turn (measured: the consumers' K S, Q S phase from 1.99 K to 1.56 K cycles
-// per chunk, the chunk step 3% shorter).  The other instances keep the
-// default: the statistic scans of PGDN and KDN measured slower with it, and
-// the no-output instance would spill.
+// Two entry points over the same body.  The one for the scalar-decay gains
+// with an output (KLA, GDN, explicit w, PGDN) states that three wavefronts
+// per SIMD is its occupancy (768 threads per workgroup allow no more): the
+// compiler's scheduler then keeps the LDS reads of the consumers' products
+// ahead of their MFMAs instead of waiting on each in turn (measured: the
+// consumers' K S, Q S phase from 1.99 K to 1.56 K cycles per chunk, the KLA
+// chunk step 3% shorter, PGDN 2.6%).  The other instances keep the default:
+// the KDN modes compile to the same registers either way, and the
+// no-output instances would spill.
 template <int DK, int GAIN, bool OUT>
 __global__ __launch_bounds__(WS_THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void
 chunk_fwd_ws_kernel(ChunkArgs a) {
@@ -1472,7 +1472,7 @@ static hipError_t launch_ws_inst(const ChunkArgs& a, hipStream_t st) {
   static_assert(sizeof(Sm) <= 160 * 1024, "LDS budget");
   constexpr bool REG = GAIN == GAIN_KLA || GAIN == GAIN_GDN || GAIN == GAIN_EXPLICIT;
   auto kern = [] {
-    if constexpr (REG && OUT) return ws::chunk_fwd_ws_kernel<DK, GAIN, OUT>;
+    if constexpr ((REG || GAIN == GAIN_PGDN) && OUT) return ws::chunk_fwd_ws_kernel<DK, GAIN, OUT>;
     else return ws::chunk_fwd_ws_scan_kernel<DK, GAIN, OUT>;
   }();
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
