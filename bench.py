@@ -373,7 +373,8 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a device copy of this size (byte-counter calibration)")
     ap.add_argument("--only", default=None,
-                    help="time only these extras (comma list of pgdn, kdn, kdn_iso, long, bwd, decode) "
+                    help="time only these extras (comma list of pgdn, kdn, kdn_iso, kda, kla_channel, long, bwd, "
+                         "decode) "
                          "after the headline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -432,7 +433,13 @@ def main():
         half = max(5, args.steps // 2)
         # isotropic KDN (Kalman Delta Networks §2.7) at the diagonal-KDN shape
         iso = W.WORKLOADS[3].replace(name="kdn_iso_bf16_B4H16T8192d128", gain="kdn_iso")
-        for key, w2 in (("pgdn", W.WORKLOADS[2]), ("kdn", W.WORKLOADS[3]), ("kdn_iso", iso)):
+        # GDN with per-channel decay (KDA) and KLA with per-channel decay at the
+        # KLA shape B8 H16 T4096 d128
+        kda = W.WORKLOADS[1].replace(name="kda_bf16_B8H16T4096d128", gain="gdn", decay="channel",
+                                     keys="unit")
+        kla_ch = W.WORKLOADS[1].replace(name="kla_channel_bf16_B8H16T4096d128", decay="channel")
+        for key, w2 in (("pgdn", W.WORKLOADS[2]), ("kdn", W.WORKLOADS[3]), ("kdn_iso", iso),
+                        ("kda", kda), ("kla_channel", kla_ch)):
             if want(key):
                 extra[key] = extra_chunk(w2, half, args.warmup, args.settle_s)
         if want("long"):

@@ -1127,7 +1127,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, int io_bf16, int gain, bool chan
                             hipStream_t st) {
   if (io_bf16) {
     if (!channel && gain != GAIN_KDN && gain != GAIN_KDN_ISO) return launch_chunk_fwd_bf16_scalar(a, gain, st);
-    if (channel && (gain == GAIN_KDN || gain == GAIN_KDN_ISO)) return launch_chunk_fwd_bf16_kdn(a, gain, st);
+    if (channel && gain != GAIN_PGDN) return launch_chunk_fwd_bf16_channel(a, gain, st);
     if (a.dk == 128) return launch_gain<uint16_t, 128, 64>(a, gain, channel, st);
     return launch_gain<uint16_t, 64, 64>(a, gain, channel, st);
   }

@@ -226,8 +226,9 @@ struct Smem {
   static constexpr int PT = CH + 8;   // [token][token] rows, bf16
   static constexpr int P16 = 16 + 8;  // rows of 16-wide blocks
   static constexpr bool HAS_W = GAIN == GAIN_PGDN || GAIN == GAIN_EXPLICIT;
-  // KDN-family gains with per-channel decay (diagonal and isotropic KDN)
-  static constexpr bool CD = GAIN == GAIN_KDN || GAIN == GAIN_KDN_ISO;
+  // per-channel decay: diagonal and isotropic KDN, and KLA / GDN / explicit w
+  // (GAIN_*_CD)
+  static constexpr bool CD = GAIN == GAIN_KDN || GAIN == GAIN_KDN_ISO || GAIN >= GAIN_CD;
   static constexpr bool PG = GAIN == GAIN_PGDN;
   // KDN: k holds raw k, then (in place) the scaled write vectors W^, by parity;
   // q[0] raw q, then Q^ in place; q[1] K^; w[0], w[1] the raw alpha, omega
@@ -274,11 +275,17 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
   constexpr int V_LOADS = CH * BV / (NP * VEC);
   constexpr bool HAS_W = GAIN == GAIN_PGDN || GAIN == GAIN_EXPLICIT;
   constexpr bool PG = GAIN == GAIN_PGDN;
-  // KDN-family gains with per-channel decay: diagonal KDN (a variance per
-  // channel) and isotropic KDN (one variance per head, Kalman Delta Networks
-  // §2.7, Eq. 40), which share the decay-scaled operands of this mode
-  constexpr bool CD = GAIN == GAIN_KDN || GAIN == GAIN_KDN_ISO;
+  // Per-channel decay (CD): diagonal KDN (a variance per channel), isotropic
+  // KDN (one variance per head, Kalman Delta Networks §2.7, Eq. 40), and KLA,
+  // GDN (KDA) and explicit w (CDX), which have no variance: their write
+  // vectors are the keys (or w) scaled like isotropic KDN's, their column
+  // scales the gain's.  All share the decay-scaled operands of this mode.
+  constexpr bool CDX = GAIN >= GAIN_CD;
+  constexpr int BG = CDX ? GAIN - GAIN_CD : GAIN;  // the write gain of a CDX instance
+  constexpr bool CD = GAIN == GAIN_KDN || GAIN == GAIN_KDN_ISO || CDX;
   constexpr bool ISO = GAIN == GAIN_KDN_ISO;
+  constexpr bool KD = GAIN == GAIN_KDN;    // a variance per key channel
+  constexpr bool NOVAR = ISO || CDX;       // no per-channel variance scan
   constexpr bool HAS_ETA = GAIN != GAIN_EXPLICIT && !CD;
   // Gains straight from the staging registers (no per-channel scan): the
   // gains of chunk c + 1 are formed in P2 as it is staged, and its tiles in
@@ -373,7 +380,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
         for (int dt = 0; dt < NDT; ++dt) S[dt] = zero4();
       }
     } else if constexpr (PROD) {
-      if ((PG || (CD && !ISO)) && ptid < DK) sm.acarry[ptid] = a.aux0 ? a.aux0[static_cast<long>(bh) * DK + ptid] : 1.f;
+      if ((PG || KD) && ptid < DK) sm.acarry[ptid] = a.aux0 ? a.aux0[static_cast<long>(bh) * DK + ptid] : 1.f;
       // isotropic KDN: the head's variance entering chunk x sits in acarry[x % 2]
       if (ISO && ptid == 0) sm.acarry[0] = a.aux0 ? a.aux0[bh] : 1.f;
       // KDN: the decay lives in the operands, the token-decay arrays stay 0 / 1
@@ -445,8 +452,10 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
         const auto ra = rsrc(static_cast<const uint16_t*>(a.g.alpha) + off, 2 * n * DK);
 #pragma unroll
         for (int j = 0; j < KV_LOADS; ++j) pa[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, koff[j], 0, 0);
-        if constexpr (!ISO) {  // isotropic KDN's omega is a per-token scalar (with the gates)
-          const auto rw = rsrc(static_cast<const uint16_t*>(a.g.omega) + off, 2 * n * DK);
+        // diagonal KDN: omega; explicit w: w (isotropic KDN's omega is a
+        // per-token scalar, with the gates)
+        if constexpr (KD || (CDX && BG == GAIN_EXPLICIT)) {
+          const auto rw = rsrc(static_cast<const uint16_t*>(KD ? a.g.omega : a.g.w) + off, 2 * n * DK);
 #pragma unroll
           for (int j = 0; j < KV_LOADS; ++j) po[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, koff[j], 0, 0);
         }
@@ -482,8 +491,9 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           const int t = e / DK, d = e % DK;
           const u32x4 one = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
           *reinterpret_cast<u32x4*>(&sm.w[0][KL::idx(t, d)]) = t < n ? pa[j] : one;
-          if constexpr (!ISO) *reinterpret_cast<u32x4*>(&sm.w[1][KL::idx(t, d)]) = po[j];
-          if constexpr (ISO) {
+          if constexpr (KD || (CDX && BG == GAIN_EXPLICIT))
+            *reinterpret_cast<u32x4*>(&sm.w[1][KL::idx(t, d)]) = po[j];
+          if constexpr (ISO || (CDX && BG == GAIN_KLA)) {
             // isotropic KDN: ||k_t||^2 and the sum of alpha_t^2 over the
             // channels, from the staging registers (DK / 8 consecutive lanes per
             // token; k is 0 and alpha 1 past the end)
@@ -530,7 +540,12 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
       const int t0 = c * CH;
       const int n = ntok(c);
       const long tok = static_cast<long>(bh) * T + t0;
-      if constexpr (CD) {
+      if constexpr (CDX) {
+        // KLA / GDN: eta_t (alpha is per channel, in its own tile)
+        if constexpr (BG != GAIN_EXPLICIT)
+          l_eta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.eta + tok, 4 * n), 4 * ltid, 0, 0));
+        return;
+      } else if constexpr (CD) {
         // KDN: the observation noise r_t (alpha is per channel, in its own tile);
         // isotropic KDN also its process noise omega_t
         l_eta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.g.r + tok, 4 * n), 4 * ltid, 0, 0));
@@ -556,8 +571,9 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           // r_t, and the information scale mu / r_t of the variance update
           // (0 past the end)
           sm.geta[c & 1][ltid] = l_eta;
-          // isotropic KDN: omega_t instead (0 past the end)
-          sm.galpha[c & 1][ltid] = ISO ? l_om : ltid < n ? a.g.mu_info * __builtin_amdgcn_rcpf(l_eta) : 0.f;
+          // isotropic KDN: omega_t instead (0 past the end); KLA / GDN: eta_t
+          // in geta, nothing here
+          sm.galpha[c & 1][ltid] = ISO ? l_om : KD && ltid < n ? a.g.mu_info * __builtin_amdgcn_rcpf(l_eta) : 0.f;
         } else if constexpr (PG) {
           const bool ok = ltid < n;
           sm.eta[ltid] = l_eta;
@@ -689,13 +705,13 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
       if constexpr (CD) {
         const int d = sid % DK, g = sid / DK, cb = d & ~63;
         const uint16_t* kb = sm.k[c & 1];
-        cd_p0 = sm.acarry[d];
+        if constexpr (KD) cd_p0 = sm.acarry[d];
         float m00 = 1.f, m01 = 0.f, m10 = 0.f, m11 = 1.f, pr = 1.f;
 #pragma unroll 1
         for (int t4 = 0; t4 < SL; t4 += 4) {
           const int t = g * SL + t4;
           const f32x4 al = KL::col4(sm.w[0], t, cb, lane);
-          if constexpr (ISO) {  // isotropic KDN: the segment's decay product only
+          if constexpr (NOVAR) {  // no variance per channel: the segment's decay product only
             pr *= al[0] * al[1] * (al[2] * al[3]);
             continue;
           }
@@ -736,7 +752,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
         for (int gg = 0; gg < NSEG; ++gg) {
           const float pr = sm.msum[3][gg * DK + d];
           if (gg < g) {
-            if constexpr (!ISO)
+            if constexpr (KD)
               p = fmaf(sm.msum[0][gg * DK + d], p, sm.msum[1][gg * DK + d]) *
                   __builtin_amdgcn_rcpf(fmaf(sm.msum[2][gg * DK + d], p, 1.f));
             if (gg > RS) num *= pr;
@@ -767,8 +783,9 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           const f32x4 kk = KL::col4(kw, t, cb, lane);
           const f32x4 qq = KL::col4(qh, t, cb, lane);
           const f32x4 al = KL::col4(sm.w[0], t, cb, lane);
-          const f32x4 om = KL::col4(sm.w[1], t, cb, lane);
-          const f32x4 mu4 = *reinterpret_cast<const f32x4*>(&sm.galpha[c & 1][t]);
+          // diagonal KDN: omega; explicit w: w
+          const f32x4 om = KD || BG == GAIN_EXPLICIT ? KL::col4(sm.w[1], t, cb, lane) : zero4();
+          const f32x4 mu4 = KD ? *reinterpret_cast<const f32x4*>(&sm.galpha[c & 1][t]) : zero4();
           // the decay 2^(G_t - G_r) at the four tokens, and its inverse: one
           // reciprocal at the last token, then back through the alphas
           f32x4 et, ie;
@@ -790,10 +807,11 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
               const int jj = j + h2;
               xk[h2] = kk[jj] * et[jj];
               xq[h2] = qq[jj] * et[jj];
-              if constexpr (ISO) {
-                // isotropic KDN: W^ = k 2^(G_r - G_t); the gain beta_t is the
-                // column scale
-                xw[h2] = kk[jj] * ie[jj];
+              if constexpr (NOVAR) {
+                // isotropic KDN, KLA, GDN: W^ = k 2^(G_r - G_t) (explicit: w in
+                // place of k); the gain (beta_t, eta_t / (||k_t||^2 + eps),
+                // eta_t, 1) is the column scale
+                xw[h2] = (BG == GAIN_EXPLICIT ? om[jj] : kk[jj]) * ie[jj];
               } else {
                 const float ph = fmaf(al[jj] * al[jj], p, om[jj]);
                 const float pk = ph * kk[jj];
@@ -812,7 +830,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
             kw[KL::idx(t + j + 1, d)] = static_cast<uint16_t>(pkw >> 16);
           }
         }
-        if (!ISO && g == NSEG - 1) sm.acarry[d] = p;
+        if (KD && g == NSEG - 1) sm.acarry[d] = p;
       }
     };
 
@@ -929,7 +947,20 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
         cdi = __shfl(beta, 16 * pw + c16);
 #pragma unroll
         for (int u4 = 0; u4 < 4; ++u4) cdj[u4] = __shfl(beta, 16 * pw + 4 * g4 + u4);
-      } else       if constexpr (CD) {
+      } else if constexpr (CDX) {
+        // KLA, GDN, explicit w: the column scale of token t is the gain's,
+        // eta_t / (||k_t||^2 + eps) with the raw keys' norm (Kaczmarz Linear
+        // Attention §2.1), eta_t, or 1; 0 past the end
+        auto colscale = [&](int t) __attribute__((always_inline)) {
+          const float g = BG == GAIN_KLA   ? sm.geta[c & 1][t] * __builtin_amdgcn_rcpf(sm.msum[4][t] + a.g.eps)
+                        : BG == GAIN_GDN   ? sm.geta[c & 1][t]
+                                           : 1.f;
+          return t < n ? g : 0.f;
+        };
+        cdi = colscale(16 * pw + c16);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cdj[u] = colscale(16 * pw + 4 * g4 + u);
+      } else if constexpr (KD) {
         // the diagonal entry z_t of token t = 16 p + x sits in lane 16 (x / 4) + x,
         // slot x % 4; the other lanes of the block fetch it with a lane shuffle
         const float zs = c16 & 2 ? (c16 & 1 ? at[3] : at[2]) : (c16 & 1 ? at[1] : at[0]);
@@ -1431,7 +1462,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           for (int i = 0; i < 4; ++i) base[(KL::sigma_channel(dt, 0, i)) * sstride] = S[dt][i];
       }
     } else if constexpr (PROD) {
-      if ((PG || (CD && !ISO)) && a.aux_final && slice == 0 && ptid < DK)
+      if ((PG || KD) && a.aux_final && slice == 0 && ptid < DK)
         a.aux_final[static_cast<long>(bh) * DK + ptid] = sm.acarry[ptid];
       if (ISO && a.aux_final && slice == 0 && ptid == 0) a.aux_final[bh] = sm.acarry[nchunks & 1];
     }
@@ -1508,12 +1539,21 @@ hipError_t launch_chunk_fwd_bf16_scalar(const ChunkArgs& a, int gain, hipStream_
 #undef DN_WS
 }
 
-// bf16 io, diagonal or isotropic KDN with per-channel decay.
-hipError_t launch_chunk_fwd_bf16_kdn(const ChunkArgs& a, int gain, hipStream_t st) {
-  if (gain == GAIN_KDN_ISO)
-    return a.dk == 128 ? launch_ws_one<128, GAIN_KDN_ISO>(a, st) : launch_ws_one<64, GAIN_KDN_ISO>(a, st);
-  if (a.dk == 128) return launch_ws_one<128, GAIN_KDN>(a, st);
-  return launch_ws_one<64, GAIN_KDN>(a, st);
+// bf16 io, per-channel decay: diagonal or isotropic KDN, KLA, GDN (KDA),
+// explicit w.  (PGDN with per-channel decay, PKDA, takes the generic kernel.)
+template <int DK>
+static hipError_t launch_ws_channel(const ChunkArgs& a, int gain, hipStream_t st) {
+  switch (gain) {
+    case GAIN_KDN: return launch_ws_one<DK, GAIN_KDN>(a, st);
+    case GAIN_KDN_ISO: return launch_ws_one<DK, GAIN_KDN_ISO>(a, st);
+    case GAIN_KLA: return launch_ws_one<DK, GAIN_KLA_CD>(a, st);
+    case GAIN_GDN: return launch_ws_one<DK, GAIN_GDN_CD>(a, st);
+    case GAIN_EXPLICIT: return launch_ws_one<DK, GAIN_EXPLICIT_CD>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+hipError_t launch_chunk_fwd_bf16_channel(const ChunkArgs& a, int gain, hipStream_t st) {
+  return a.dk == 128 ? launch_ws_channel<128>(a, gain, st) : launch_ws_channel<64>(a, gain, st);
 }
 
 }  // namespace dn

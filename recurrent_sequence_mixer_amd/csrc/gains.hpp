@@ -7,6 +7,12 @@
 namespace dn {
 
 enum Gain { GAIN_KLA = 0, GAIN_GDN = 1, GAIN_PGDN = 2, GAIN_KDN = 3, GAIN_EXPLICIT = 4, GAIN_KDN_ISO = 5 };
+// Internal codes (not ABI values): the chunk kernel's per-channel-decay mode
+// for the gains without a statistic (KLA, GDN - KDA -, explicit w): the gain
+// code + GAIN_CD.
+constexpr int GAIN_CD = 16;
+enum GainCd { GAIN_KLA_CD = GAIN_KLA + GAIN_CD, GAIN_GDN_CD = GAIN_GDN + GAIN_CD,
+              GAIN_EXPLICIT_CD = GAIN_EXPLICIT + GAIN_CD };
 
 // KLA step size eta / (||k||^2 + eps)  (Kaczmarz Linear Attention §2.1).
 __device__ __forceinline__ float kla_beta(float eta, float knorm2, float eps) {

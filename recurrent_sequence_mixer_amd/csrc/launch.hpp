@@ -160,8 +160,8 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, int io_bf16, int gain, bool chan
                             hipStream_t st);
 // bf16 io, scalar decay, gains KLA / GDN / PGDN / explicit (chunk_fwd_ws.hip)
 hipError_t launch_chunk_fwd_bf16_scalar(const ChunkArgs& a, int gain, hipStream_t st);
-// bf16 io, diagonal or isotropic KDN with per-channel decay (chunk_fwd_ws.hip)
-hipError_t launch_chunk_fwd_bf16_kdn(const ChunkArgs& a, int gain, hipStream_t st);
+// bf16 io, per-channel decay, every gain but PGDN (chunk_fwd_ws.hip)
+hipError_t launch_chunk_fwd_bf16_channel(const ChunkArgs& a, int gain, hipStream_t st);
 hipError_t launch_gain_prep(const GainPrepArgs& a, int io_bf16, int gain, bool channel,
                             hipStream_t st);
 

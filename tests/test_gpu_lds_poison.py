@@ -45,7 +45,8 @@ def _check_fwd(wl, inp, o, S, aux):
     ("explicit", "scalar", "unit", "bf16", 64, 64), ("kdn", "channel", "scaled", "bf16", 128, 128),
     ("kdn_iso", "channel", "scaled", "bf16", 128, 64), ("gdn", "channel", "unit", "bf16", 128, 128),
     ("kdn", "scalar", "scaled", "bf16", 64, 128), ("kla", "scalar", "scaled", "f32", 64, 64),
-    ("kla", "scalar", "scaled", "bf16", 120, 120)])
+    ("kla", "scalar", "scaled", "bf16", 120, 120), ("kla", "channel", "scaled", "bf16", 128, 128),
+    ("explicit", "channel", "unit", "bf16", 64, 128)])
 def test_poisoned_chunk_fwd(debug_library, gain, decay, keys, io, dk, dv):
     wl = W.Workload(f"poison_{gain}_{decay}", gain, decay, io, 2, 2, 150, dk, dv, keys=keys, seed=990)
     inp = W.generate(wl)

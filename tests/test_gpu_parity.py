@@ -107,6 +107,23 @@ def test_bf16_gains_dk64(gain, decay, keys, dv, T):
     _check(wl, inp, None, o, S, aux)
 
 
+# KLA, GDN (KDA) and explicit write vectors with per-channel decay: the fused
+# kernel's decay-scaled mode without a variance, both head widths, ragged
+# lengths, a nonzero S0 (the workload's)
+@pytest.mark.parametrize("T", [1, 63, 65, 200, 333])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128)])
+@pytest.mark.parametrize("gain,keys", [("kla", "scaled"), ("gdn", "unit"), ("explicit", "unit")])
+def test_bf16_channel_decay_gains(gain, keys, dk, dv, T):
+    wl = W.Workload(f"{gain}_channel_bf16", gain, "channel", "bf16", 2, 2, T, dk, dv, keys=keys,
+                    seed=700 + T + dk)
+    inp = W.generate(wl)
+    if gain == "explicit":
+        inp["w"] = W.round_io(np.random.default_rng(wl.seed + 1).standard_normal((2, 2, T, dk)) * 0.05,
+                              "bf16")
+    o, S, aux = gpu_chunk(wl, inp)
+    _check(wl, inp, None, o, S, aux)
+
+
 # ---------------------------------------------------------------- full size workloads
 
 @pytest.mark.parametrize("idx", [1, 2, 3])
@@ -219,7 +236,7 @@ def test_chunk_fwd_long_full_size_sampled_head():
     ("kdn_iso", "channel", "scaled", 8320, 2, 128),  # 130 pieces of 64 tokens: three scan rounds
     ("pgdn", "scalar", "unit", 8320, 5, 128),        # 65 pieces of 128 tokens
     ("pgdn", "scalar", "unit", 1024, 4, 64),
-    # per-channel decay on the generic chunk kernel: PKDA (PGDN), KLA, GDN
+    # per-channel decay: PKDA (PGDN, generic chunk kernel), KLA, GDN
     ("pgdn", "channel", "unit", 1024, 4, 128),
     ("kla", "channel", "scaled", 1024, 4, 128),
     ("gdn", "channel", "unit", 1024, 2, 64),
@@ -405,7 +422,8 @@ def test_strong_channel_decay_long_segments():
     _check(wl, inp, None, o, S, aux)
 
 
-@pytest.mark.parametrize("gain,keys", [("kdn", "scaled"), ("kdn_iso", "scaled"), ("pgdn", "unit")])
+@pytest.mark.parametrize("gain,keys", [("kdn", "scaled"), ("kdn_iso", "scaled"), ("pgdn", "unit"),
+                                       ("gdn", "unit"), ("kla", "scaled")])
 def test_channel_decay_beyond_range_is_nan(gain, keys):
     """One channel of head 0 decays by 2^-320 over the first half of chunk 5
     (alpha = 2^-10 for 32 tokens): referred to the chunk midpoint its factors
