@@ -494,23 +494,25 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           if constexpr (KD || (CDX && BG == GAIN_EXPLICIT))
             *reinterpret_cast<u32x4*>(&sm.w[1][KL::idx(t, d)]) = po[j];
           if constexpr (ISO || (CDX && BG == GAIN_KLA)) {
-            // isotropic KDN: ||k_t||^2 and the sum of alpha_t^2 over the
-            // channels, from the staging registers (DK / 8 consecutive lanes per
-            // token; k is 0 and alpha 1 past the end)
+            // ||k_t||^2 (isotropic KDN, KLA) and the sum of alpha_t^2 over the
+            // channels (isotropic KDN), from the staging registers (DK / 8
+            // consecutive lanes per token; k is 0 and alpha 1 past the end)
             const u32x4 al4 = t < n ? pa[j] : one;
             float sk = 0.f, sa = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const float k0 = __uint_as_float(pk[j][i] << 16), k1 = __uint_as_float(pk[j][i] & 0xFFFF0000u);
-              const float a0 = __uint_as_float(al4[i] << 16), a1 = __uint_as_float(al4[i] & 0xFFFF0000u);
               sk = fmaf(k0, k0, fmaf(k1, k1, sk));
-              sa = fmaf(a0, a0, fmaf(a1, a1, sa));
+              if constexpr (ISO) {
+                const float a0 = __uint_as_float(al4[i] << 16), a1 = __uint_as_float(al4[i] & 0xFFFF0000u);
+                sa = fmaf(a0, a0, fmaf(a1, a1, sa));
+              }
             }
             sk = group_sum<DK / VEC>(sk);
-            sa = group_sum<DK / VEC>(sa);
+            if constexpr (ISO) sa = group_sum<DK / VEC>(sa);
             if (d == 0) {
               sm.msum[4][t] = sk;
-              sm.msum[4][CH + t] = sa;
+              if constexpr (ISO) sm.msum[4][CH + t] = sa;
             }
           }
         }
@@ -850,15 +852,17 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
     // in registers).  Producer p owns the diagonal block p (L_pp in both
     // orientations, M_pp) and items 3 p .. 3 p + NIT_P - 1 of the twelve
     // off-diagonal tiles (L or M of (bi, bj), bj < bi), loader l items
-    // 3 l + NIT_P .. 3 l + 2: the loaders take what their other work (the
-    // statistic scans of PGDN and KDN) leaves room for.  Item it is of kind
+    // 3 l + NIT_P .. 3 l + 2: the loaders take what their other work (PGDN's
+    // statistic scan) leaves room for.  Item it is of kind
     // it % 2 (0: L, 1: M)
     // and covers tile (bi, bj) = pair it / 2 of (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
     auto item_is_m = [](int it) { return (it & 1) != 0; };
     auto item_bi = [](int it) { const int pr = it >> 1; return pr < 1 ? 1 : pr < 3 ? 2 : 3; };
     auto item_bj = [](int it) { const int pr = it >> 1; return pr < 1 ? 0 : pr < 3 ? pr - 1 : pr - 3; };
-    // Items per producer: REG 1, PGDN 2, KDN 3; the loaders take the rest
-    constexpr int NIT_P = REG ? 1 : PG ? 2 : 3;
+    // Items per producer: REG, GDN and explicit w with per-channel decay 1,
+    // PGDN 2, the KDN modes and KLA with per-channel decay 3; the loaders take
+    // the rest (those with key norms or a variance scan to form take none)
+    constexpr int NIT_P = PG ? 2 : KD || ISO || (CDX && BG == GAIN_KLA) ? 3 : 1;
     constexpr int NIT = LOAD ? 3 - NIT_P : NIT_P;  // off-diagonal items of this wavefront
     const int lw = wave - 8;  // loaders: wavefront index
     auto item_of = [&](int k) { return PROD ? 3 * pw + k : 3 * lw + NIT_P + k; };  // wave-uniform
@@ -923,26 +927,37 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
         const float om = sm.galpha[c & 1][t], rr = ok ? sm.geta[c & 1][t] : 1.f;
         const float u = ok ? a.g.mu_info * nk / (DK * rr) : 0.f;
         float m00 = am, m01 = om, m10 = u * am, m11 = fmaf(u, om, 1.f);
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float y00 = __shfl_up(m00, off), y01 = __shfl_up(m01, off);
-          const float y10 = __shfl_up(m10, off), y11 = __shfl_up(m11, off);
-          if (lane >= off) {  // (maps of tokens t - off + 1 .. t) o (maps before)
-            const float n00 = fmaf(m00, y00, m01 * y10), n01 = fmaf(m00, y01, m01 * y11);
-            const float n10 = fmaf(m10, y00, m11 * y10), n11 = fmaf(m10, y01, m11 * y11);
-            const float sc = __builtin_amdgcn_rcpf(n11);  // projective: keep (1, 1) at 1
-            m00 = n00 * sc;
-            m01 = n01 * sc;
-            m10 = n10 * sc;
-            m11 = 1.f;
-          }
-        }
+        // inclusive scan by DPP lane moves: shifts by 1, 2, 4, 8 within rows
+        // of 16 lanes, then row 0's and row 2's last lane into rows 1 and 3,
+        // and lane 31 into rows 2 and 3.  A lane with no source receives the
+        // identity map, so every lane composes at every step:
+        // (maps of its own span) o (maps before)
+        auto compose = [&](float y00, float y01, float y10, float y11) __attribute__((always_inline)) {
+          const float n00 = fmaf(m00, y00, m01 * y10), n01 = fmaf(m00, y01, m01 * y11);
+          const float n10 = fmaf(m10, y00, m11 * y10), n11 = fmaf(m10, y01, m11 * y11);
+          const float sc = __builtin_amdgcn_rcpf(n11);  // projective: keep (1, 1) at 1
+          m00 = n00 * sc;
+          m01 = n01 * sc;
+          m10 = n10 * sc;
+          m11 = 1.f;
+        };
+#define DN_ISO_STEP(CTRL, RM)                                                                  \
+  compose(dpp<CTRL, RM>(m00, 1.f), dpp<CTRL, RM>(m01, 0.f), dpp<CTRL, RM>(m10, 0.f),          \
+          dpp<CTRL, RM>(m11, 1.f))
+        DN_ISO_STEP(0x111, 0xF);
+        DN_ISO_STEP(0x112, 0xF);
+        DN_ISO_STEP(0x114, 0xF);
+        DN_ISO_STEP(0x118, 0xF);
+        DN_ISO_STEP(0x142, 0xA);
+        DN_ISO_STEP(0x143, 0xC);
+#undef DN_ISO_STEP
         const float b0 = sm.acarry[c & 1];
-        const float bt = fmaf(m00, b0, m01) / fmaf(m10, b0, m11);  // variance after token t
-        const float bs = __shfl_up(bt, 1);                           // (every lane takes part)
-        const float bp = lane == 0 ? b0 : bs;                         // variance before token t
+        // variance after token t (hardware reciprocals, as in the other gains)
+        const float bt = fmaf(m00, b0, m01) * __builtin_amdgcn_rcpf(fmaf(m10, b0, m11));
+        // the variance before token t: lane t - 1's, b0 in lane 0 (DPP wave_shr:1)
+        const float bp = dpp<0x138>(bt, b0);
         const float bh_ = fmaf(am, bp, om);
-        const float beta = ok ? bh_ / fmaf(bh_, nk, rr) : 0.f;
+        const float beta = ok ? bh_ * __builtin_amdgcn_rcpf(fmaf(bh_, nk, rr)) : 0.f;
         if (pw == 0 && lane == CH - 1) sm.acarry[(c + 1) & 1] = bt;
         cdi = __shfl(beta, 16 * pw + c16);
 #pragma unroll
@@ -1260,6 +1275,8 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           diag_gains(0, ntok(0));
           scale_diag(0);
         }
+      } else if constexpr (LOAD) {
+        if (nchunks > 0) tiles_off(0);
       }
       __syncthreads();
       for (int c = 0; c < nchunks; ++c) {
@@ -1278,6 +1295,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           fetch_k(c + 2);
           fetch_ao(c + 2);
           fetch_gates(c + 2);
+          scale_off(c);  // their off-diagonal tiles of chunk c
         } else {
           scale_off(c);
           invert(c);
@@ -1313,9 +1331,11 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           }
         } else if constexpr (LOAD) {
           // the loads of q and v of chunk c + 2 (staged in P2 of chunk c + 1),
-          // issued here, where the loaders have no scan work to hold back
+          // issued here, where the loaders have no scan work to hold back;
+          // the raw products of their off-diagonal tiles of chunk c + 1
           fetch_q(c + 2);
           fetch_v(c + 2);
+          if (c + 1 < nchunks) tiles_off(c + 1);
         }
         __syncthreads();  // (4) column scales and diagonal blocks of chunk c + 1 ready
       }
