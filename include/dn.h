@@ -64,13 +64,17 @@
  * failed launch.  NaN/Inf in the data are not checked and propagate.
  * Preconditions on values (not checked): alpha in (0, 1]; PGDN A_0 > 0 and
  * alphaP, betaP >= 0; KDN and KDN_ISO r > 0, omega >= 0, p_0 and b_0 > 0.
- * RANGE OF CHANNEL DECAY (checked on the device).  The chunked calls refer
+ * RANGE OF CHANNEL DECAY (checked on the device).  The chunked forward refers
  * the decay factors of each key channel to the middle of its chunk of 64
- * tokens (token 31), so each half chunk's decay of a channel must be at least
- * 2^-96 (a geometric-mean alpha of at least 1/8 over its 32 tokens).  A chunk
- * that goes beyond turns the head's state, and every output of the head from
- * that chunk on, into NaN: no finite wrong value is returned.  dn_decode_step
- * has no such bound; scalar decay has none in any call. 
+ * tokens (token 31), which stays within fp32 range while each half chunk's
+ * decay of a channel is at least 2^-96 (a geometric-mean alpha of at least
+ * 1/8 over its 32 tokens).  A head whose decay goes beyond in some chunk is
+ * flagged on the device and recomputed by a tokenwise pass over its whole
+ * sequence, which has no such bound: dn_chunk_fwd and dn_chunk_fwd_long
+ * return the token recurrence's results for any alpha in (0, 1], at the cost
+ * of that head's sequential pass (about a microsecond per token) when it
+ * happens.  dn_chunk_bwd keeps the bound (the gradients of such a head are
+ * NaN).  dn_decode_step has no bound; scalar decay has none in any call.
  *
  * Thread safety: all entry points are reentrant; there is no mutable global
  * state.
@@ -165,7 +169,8 @@ typedef struct dn_gates {
  *     (bf16 io, T a multiple of C) run by segments of each head, as
  *     dn_chunk_fwd_long does, on dn_chunk_fwd_long's workspace layout for
  *     the chosen segment count (e.g. B1 H8 T131072 d128: 16 segments, about
- *     26 MB); every other shape needs none.
+ *     26 MB); other shapes with per-channel decay need an int per head (the
+ *     flags of RANGE OF CHANNEL DECAY); every other shape needs none.
  *   dn_gain_prep: the gains with a statistic (PGDN, KDN, KDN_ISO), bf16 io
  *     and T a multiple of C (at least two chunks) scan every chunk in
  *     parallel; the workspace holds the chunks' piece summaries, the
@@ -193,7 +198,9 @@ size_t dn_workspace_bytes(const dn_desc* desc);
  * No other buffers may overlap (DN_ERR_ALIAS is returned for the overlaps
  * the host can see from the pointer ranges).  With T = 0 the tensors q, k, v,
  * o and the gate table may be NULL.  One launch on `stream` (a
- * segmented schedule: three, five with a statistic); nothing is allocated. */
+ * segmented schedule: three, five with a statistic; per-channel decay adds
+ * the tokenwise pass, which returns at once for heads in range); nothing is
+ * allocated. */
 int dn_chunk_fwd(const dn_desc* desc, const void* q, const void* k, const void* v,
                  const dn_gates* gates, const float* S0, const float* aux0, void* o,
                  float* S_final, float* aux_final, void* ws, size_t ws_bytes, void* stream);
@@ -242,13 +249,14 @@ int dn_chunk_fwd_noalloc(const dn_desc* desc, const void* q, const void* k, cons
  *   q, k, v and o are required also when T = 0.
  *   workspace: device memory of at least dn_chunk_fwd_long_workspace(desc,
  *   nseg) bytes, owned by the caller: fp32 A [B, H nseg, dk, dk], then B and
- *   S_in [B, H nseg, dk, dv] each, and for PGDN and KDN the segments'
- *   entering statistics and the piece summaries.  It may not overlap any
- *   other buffer (DN_ERR_WORKSPACE when too small, DN_ERR_ALIAS on overlap).
+ *   S_in [B, H nseg, dk, dv] each, for PGDN and KDN the segments' entering
+ *   statistics and the piece summaries, and with per-channel decay an int
+ *   per segment (RANGE OF CHANNEL DECAY).  It may not overlap any other
+ *   buffer (DN_ERR_WORKSPACE when too small, DN_ERR_ALIAS on overlap).
  *   dn_chunk_fwd_long_workspace returns that size in bytes, or 0 for an
  *   invalid descriptor, nseg < 1, or segments that are not whole chunks.
- *   Three launches on `stream` (five with a statistic); nothing is
- *   allocated.  Choosing nseg: the last launch runs B H nseg d_v / 64
+ *   Three launches on `stream` (five with a statistic; one more with
+ *   per-channel decay); nothing is allocated.  Choosing nseg: the last launch runs B H nseg d_v / 64
  *   workgroups of one chunk step at a time each; filling the device's
  *   compute units once (256 on MI355X) is best, e.g. nseg = 16 for B1 H8
  *   d128 (measured at T = 32768 and 131072: 32 and 64 segments are slower,

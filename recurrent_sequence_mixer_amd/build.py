@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libdn.so")
 ARCH = "gfx950"
 
 SOURCES = ["dn_api.cpp", "decode_step.hip", "gain_prep.hip", "chunk_fwd.hip", "chunk_fwd_ws.hip",
-           "segment_combine.hip", "segment_stats.hip", "chunk_bwd.hip", "pad.hip"]
+           "segment_combine.hip", "segment_stats.hip", "chunk_bwd.hip", "pad.hip", "token_fwd.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",

@@ -69,11 +69,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // the chunk start to its midpoint (token 31) and Gn to its end.  Referred to
 // the midpoint, every operand factor stays within 2^96 and the scaled state
 // stays normal while both half-chunk decays are at least 2^-96; beyond that
-// the chunk form cannot be evaluated this way, and a NaN scale turns the
-// head's state and every later output into NaN rather than into wrong
-// finite values.
-__device__ __forceinline__ float midpoint_scale(float gm, float gn) {
-  return gm >= -96.f && gn - gm >= -96.f ? fast_exp2(gm) : __builtin_nanf("");
+// the chunk form cannot be evaluated this way: a NaN scale turns the head's
+// state and later outputs into NaN, and the head is flagged (*oor) for the
+// tokenwise pass, which recomputes it.
+__device__ __forceinline__ float midpoint_scale(float gm, float gn, int* oor) {
+  const bool ok = gm >= -96.f && gn - gm >= -96.f;
+  if (!ok) *oor = 1;
+  return ok ? fast_exp2(gm) : __builtin_nanf("");
 }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -152,6 +154,7 @@ struct ChunkSmem {
   float pmid[DK], g31[DK];               // KDN, two segments: variance and log-decay after token 31
   float pcar[DK], g63[DK];               //   and after token 63 (the carry)
   float red[CH];                         // KDN: 1 / (r_t + z_t)
+  int oor;                               // channel decay: a chunk beyond the chunk form's range
 };
 
 template <typename E, int DK, int BV, int GAIN, bool CHANNEL>
@@ -251,6 +254,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
   if constexpr (GAIN == GAIN_KDN_ISO) {
     if (tid == 0) sm.acarry[0] = a.aux0 ? a.aux0[bh] : 1.f;
   }
+  if (tid == 0) sm.oor = 0;
 
   if constexpr (PG2) {
     if (tid < DK) sm.acarry[tid] = aux[0];
@@ -754,7 +758,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
         // and 63 from the scan's boundary values
         const float gm = seg == 0 ? gs[HT - 1] : sm.g31[dch], gl = sm.g63[dch];
         if (seg == 0) {
-          sm.gmid[dch] = midpoint_scale(gm, gl);
+          sm.gmid[dch] = midpoint_scale(gm, gl, &sm.oor);
           sm.gn[dch] = fast_exp2(gl);
         }
         const float fl = fast_exp2(gl - gm);  // 2^(Gn - Gmid)
@@ -781,7 +785,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
         if (tid < DK) {
           const int d = tid, cb = 64 * wave;
           const float gm = gch[0][CH / 2 - 1], gl = gch[0][CH - 1];
-          sm.gmid[d] = midpoint_scale(gm, gl);
+          sm.gmid[d] = midpoint_scale(gm, gl, &sm.oor);
           sm.gn[d] = fast_exp2(gl);
           const float fl = fast_exp2(gl - gm);  // 2^(Gn - Gmid)
 #pragma unroll
@@ -809,7 +813,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
         const int d = tid + cc * NT;
         if (d < DK) {
           const float gm = gch[cc][CH / 2 - 1], gl = gch[cc][CH - 1];
-          sm.gmid[d] = midpoint_scale(gm, gl);
+          sm.gmid[d] = midpoint_scale(gm, gl, &sm.oor);
           sm.gn[d] = fast_exp2(gl);
 #pragma unroll
           for (int t = 0; t < CH; ++t) {
@@ -1056,9 +1060,12 @@ void chunk_fwd_kernel(ChunkArgs a) {
     store_out(cl * CH, min(CH, T - cl * CH));
   }
 
-  // ---- final state and auxiliary state
+  // ---- final state and auxiliary state (neither for a head flagged out of
+  // range: the tokenwise pass writes them from S0 and aux0 as they are)
+  const bool oor = CHANNEL && sm.oor;
+  if (CHANNEL && a.oor && slice == 0 && tid == 0) a.oor[bh] = oor ? 1 : 0;
   float* const fin = xfer ? a.S_final_x : a.S_final;
-  if (fin) {
+  if (fin && !oor) {
     // transfer slices: their columns of S_final_x [B, H, dk, xcols]
     const int sstride = xfer ? a.xcols : a.dv;
     const int col = col0 + 16 * wave + c16 - (xfer ? a.dv : 0);
@@ -1070,6 +1077,7 @@ void chunk_fwd_kernel(ChunkArgs a) {
         fin[(static_cast<long>(bh) * DK + row) * sstride + col] = S[dt][i];
       }
   }
+  if (oor) return;
   if constexpr (PG2) {
     if (a.aux_final && slice == 0 && tid < DK)
       a.aux_final[static_cast<long>(bh) * DK + tid] = nchunks > 0 ? sm.acarry[tid] : aux[0];

@@ -259,6 +259,7 @@ struct Smem {
   alignas(16) float msum[CD ? 5 : 1][CD ? 512 : 4];
   alignas(16) float gref[CD ? 2 : 1][CD ? DK : 4];
   alignas(16) float gnr[CD ? 2 : 1][CD ? DK : 4];
+  int oor;  // per-channel decay: some chunk was beyond the range of the chunk form
 };
 
 // OUT = false: an instance for launches without an output (a.o == NULL): the
@@ -383,6 +384,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
       if ((PG || KD) && ptid < DK) sm.acarry[ptid] = a.aux0 ? a.aux0[static_cast<long>(bh) * DK + ptid] : 1.f;
       // isotropic KDN: the head's variance entering chunk x sits in acarry[x % 2]
       if (ISO && ptid == 0) sm.acarry[0] = a.aux0 ? a.aux0[bh] : 1.f;
+      if (CD && ptid == 0) sm.oor = 0;
       // KDN: the decay lives in the operands, the token-decay arrays stay 0 / 1
       if (CD && ptid < 2 * CH) {
         sm.g2[ptid >> 6][ptid & 63] = 0.f;
@@ -773,8 +775,10 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           // 2^-96; beyond that the chunk form cannot be evaluated this way, and
           // a NaN reference turns the head's state and every later output
           // into NaN rather than into wrong finite values
-          sm.gref[c & 1][d] = gr >= 0x1p-96f && gt >= 0x1p-96f ? gr : __builtin_nanf("");
+          const bool in_range = gr >= 0x1p-96f && gt >= 0x1p-96f;
+          sm.gref[c & 1][d] = in_range ? gr : __builtin_nanf("");
           sm.gnr[c & 1][d] = gt;
+          if (!in_range) sm.oor = 1;  // the head is recomputed token by token
         }
         uint16_t* kw = sm.k[c & 1];  // raw k, rewritten in place with W^
         uint16_t* qh = sm.q[0];      // raw q, rewritten in place with Q^
@@ -1471,10 +1475,13 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
 
     }
 
-    // ---------------- final state and statistic
+    // ---------------- final state and statistic (neither for a head whose
+    // decay left the range of the chunk form: the tokenwise pass that follows
+    // writes them, from S0 and aux0 as they are)
+    const bool oor = CD && sm.oor;
     if constexpr (CONS) {
       float* fin = xfer ? a.S_final_x : a.S_final;
-      if (fin) {
+      if (fin && !oor) {
         float* base = fin + s_lane;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -1482,9 +1489,10 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           for (int i = 0; i < 4; ++i) base[(KL::sigma_channel(dt, 0, i)) * sstride] = S[dt][i];
       }
     } else if constexpr (PROD) {
-      if ((PG || KD) && a.aux_final && slice == 0 && ptid < DK)
+      if ((PG || KD) && !oor && a.aux_final && slice == 0 && ptid < DK)
         a.aux_final[static_cast<long>(bh) * DK + ptid] = sm.acarry[ptid];
-      if (ISO && a.aux_final && slice == 0 && ptid == 0) a.aux_final[bh] = sm.acarry[nchunks & 1];
+      if (ISO && !oor && a.aux_final && slice == 0 && ptid == 0) a.aux_final[bh] = sm.acarry[nchunks & 1];
+      if (CD && a.oor && slice == 0 && ptid == 0) a.oor[bh] = oor ? 1 : 0;
     }
   };
   if (wave < 4) {

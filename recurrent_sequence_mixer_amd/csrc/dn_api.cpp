@@ -154,13 +154,20 @@ DN_EXPORT const char* dn_status_string(int s) {
 // Workspace of dn_chunk_fwd_long, fp32: A [B, H nseg, dk, dk], then B and S_in
 // [B, H nseg, dk, dv]; for the gains with a statistic (PGDN, KDN) then
 // aux_in [B, H nseg, aph], mu_seg [H nseg] and the piece summaries
-// [B, H, T / lsub, 3, aph], each of these starting on a 256-byte boundary.
+// [B, H, T / lsub, 3, aph]; with per-channel decay then the out-of-range
+// flags [B, H nseg] (int), each of these starting on a 256-byte boundary.
 struct LongLayout {
-  size_t a, b, s, aux_in, mu_seg, summ, total;
+  size_t a, b, s, aux_in, mu_seg, summ, oor, total;
   int lsub;
 };
 
 static size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Per-channel decay: one int per head (of the [B, H nseg] view) that the
+// chunked kernels set when the head's decay leaves the range of the chunk form
+static size_t oor_bytes(const dn_desc* d, int nseg) {
+  return d->decay == DN_DECAY_CHANNEL ? static_cast<size_t>(d->B) * d->H * nseg * sizeof(int) : 0;
+}
 
 static LongLayout long_layout(const dn_desc* d, int nseg) {
   LongLayout L{};
@@ -178,7 +185,41 @@ static LongLayout long_layout(const dn_desc* d, int nseg) {
     L.summ = round256(L.mu_seg + static_cast<size_t>(d->H) * nseg * sizeof(float));
     L.total = L.summ + static_cast<size_t>(d->B) * d->H * (d->T / L.lsub) * 3 * aph * sizeof(float);
   }
+  if (oor_bytes(d, nseg) > 0) {
+    L.oor = round256(L.total);
+    L.total = L.oor + oor_bytes(d, nseg);
+  }
   return L;
+}
+
+// The tokenwise pass over the heads whose per-channel decay the chunked
+// kernels flagged (oor: nflag ints per head); aux0 is the statistic entering
+// the sequence, aux_seg the head stride of its array in units of one head's
+// statistic.  A head not flagged costs a read of its flags.
+static int run_token_pass(const dn_desc* d, const void* q, const void* k, const void* v,
+                          const dn_gates* g, const float* S0, const float* aux0, int aux_seg,
+                          void* o, float* S_final, float* aux_final, const int* oor, int nflag,
+                          hipStream_t s) {
+  const bool has_aux = has_aux_state(d);
+  dn::TokenArgs t;
+  t.B = d->B;
+  t.H = d->H;
+  t.T = d->T;
+  t.dk = d->dk;
+  t.dv = d->dv;
+  t.q = q;
+  t.k = k;
+  t.v = v;
+  t.g = gate_args(d, g);
+  t.S0 = S0;
+  t.aux0 = has_aux ? aux0 : nullptr;
+  t.aux_seg = aux_seg;
+  t.o = o;
+  t.S_final = S_final;
+  t.aux_final = has_aux ? aux_final : nullptr;
+  t.flags = oor;
+  t.nflag = nflag;
+  return hip_status(dn::launch_token_fwd(t, d->io == DN_BF16, d->gain, s));
 }
 
 static bool long_shape_ok(const dn_desc* d, int nseg) {
@@ -273,13 +314,17 @@ static int run_long(const dn_desc* d, int nseg, const void* q, const void* k, co
   const auto launch = [&]() {
     return dn::launch_chunk_fwd(a, 1, d->gain, d->decay == DN_DECAY_CHANNEL, s);
   };
+  // per-channel decay: the segments whose decay leaves the chunk form's range
+  int* const oor = lay.oor ? reinterpret_cast<int*>(wbase + lay.oor) : nullptr;
   // (1) in one launch: the end states B_s from S_in = 0 (the value slices) and
   // the transfer matrices A_s from S_in = I with v = 0 (d_k more slices)
   a.xcols = d->dk;
   a.S_final_x = wA;
+  a.oor = oor;
   if ((e = launch()) != hipSuccess) return DN_ERR_HIP;
   a.xcols = 0;
   a.S_final_x = nullptr;
+  a.oor = nullptr;
   // (2) the entering state of every segment, and the final state
   dn::CombineArgs c;
   c.B = d->B;
@@ -292,12 +337,18 @@ static int run_long(const dn_desc* d, int nseg, const void* q, const void* k, co
   c.S0 = S0;
   c.S_in = wS;
   c.S_final = S_final;
+  c.oor = oor;
   if ((e = dn::launch_segment_combine(c, s)) != hipSuccess) return DN_ERR_HIP;
   // (3) every segment from its entering state, writing o
   a.S0 = wS;
   a.S_final = nullptr;
   a.o = o;
-  return hip_status(launch());
+  if ((e = launch()) != hipSuccess) return DN_ERR_HIP;
+  // (4) per-channel decay: the flagged heads token by token, from S0 and the
+  // statistic entering segment 0
+  if (!oor) return DN_OK;
+  return run_token_pass(d, q, k, v, g, S0, has_aux ? a.aux0 : nullptr, nseg, o, S_final, aux_final,
+                        oor, nseg, s);
 }
 
 // Schedule of dn_chunk_fwd: one pass (nseg = 1), or nseg segments per head
@@ -413,7 +464,7 @@ static PadLayout pad_layout(const dn_desc* d, bool prep) {
 static size_t chunk_ws_bytes(const dn_desc* d) {
   if (!kernel_dims(d)) return pad_layout(d, false).total;
   const int nseg = auto_nseg(d);
-  return nseg > 1 ? long_layout(d, nseg).total : 0;
+  return nseg > 1 ? long_layout(d, nseg).total : oor_bytes(d, 1);
 }
 
 static size_t prep_ws_bytes(const dn_desc* d) {
@@ -580,6 +631,11 @@ DN_EXPORT int dn_chunk_fwd(const dn_desc* d, const void* q, const void* k, const
                     static_cast<hipStream_t>(stream));
   }
 
+  // per-channel decay: the out-of-range flags in the workspace
+  int* const oor = need > 0 ? static_cast<int*>(ws) : nullptr;
+  if (oor && (st = check_long_aliases(d, g ? g : &nog, q, k, v, S0, aux0, o, S_final, aux_final, ws,
+                                      need)) != DN_OK)
+    return st;
   dn::ChunkArgs a;
   a.B = d->B;
   a.H = d->H;
@@ -597,9 +653,14 @@ DN_EXPORT int dn_chunk_fwd(const dn_desc* d, const void* q, const void* k, const
   a.aux_final = has_aux ? aux_final : nullptr;
   a.xcols = 0;
   a.S_final_x = nullptr;
-  return hip_status(dn::launch_chunk_fwd(a, d->io == DN_BF16, d->gain,
-                                         d->decay == DN_DECAY_CHANNEL,
-                                         static_cast<hipStream_t>(stream)));
+  a.oor = oor;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dn::launch_chunk_fwd(a, d->io == DN_BF16, d->gain, d->decay == DN_DECAY_CHANNEL, s) !=
+      hipSuccess)
+    return DN_ERR_HIP;
+  // heads whose decay left the range of the chunk form, token by token
+  if (!oor || d->T == 0) return DN_OK;
+  return run_token_pass(d, q, k, v, g, S0, aux0, 1, o, S_final, aux_final, oor, 1, s);
 }
 
 DN_EXPORT int dn_decode_step(const dn_desc* d, const void* q, const void* k, const void* v,

@@ -52,7 +52,32 @@ struct ChunkArgs {
   // transfer matrices of segments)
   int xcols;
   float* S_final_x;
+  // per-channel decay, nullable: oor[b H + h] = 1 for a head whose decay left
+  // the range of the chunk form in some chunk (its S_final and aux_final are
+  // then not written, its outputs are NaN), else 0
+  int* oor = nullptr;
 };
+
+// Tokenwise forward of the heads flagged by the chunked kernels
+// (token_fwd.hip): per-channel decay, kernel widths (dk 64 / 128, dv a
+// multiple of 64).  A head of [B, H] runs when any of its nflag entries of
+// flags [B, H, nflag] is nonzero, from S0 (nullable: zeros) and the
+// statistic aux0[(b H + h) aux_seg] (nullable: ones), writing o, S_final and
+// aux_final (each nullable).
+struct TokenArgs {
+  int B, H, T, dk, dv;
+  const void *q, *k, *v;
+  GateArgs g;
+  const float* S0;
+  const float* aux0;
+  int aux_seg;
+  void* o;
+  float* S_final;
+  float* aux_final;
+  const int* flags;
+  int nflag;
+};
+hipError_t launch_token_fwd(const TokenArgs& a, int io_bf16, int gain, hipStream_t st);
 
 // Long-sequence forward by segments (segment_combine.hip): per head, the
 // entering state of every segment from the segments' transfer matrices A_s
@@ -64,6 +89,9 @@ struct CombineArgs {
   const float* S0;  // [B, H, dk, dv], nullable (zeros)
   float* S_in;      // [B, H nseg, dk, dv]
   float* S_final;   // [B, H, dk, dv], nullable
+  // nullable: S_final is not written for a head with any of its nseg entries
+  // of oor [B, H nseg] set
+  const int* oor = nullptr;
 };
 hipError_t launch_segment_combine(const CombineArgs& a, hipStream_t st);
 

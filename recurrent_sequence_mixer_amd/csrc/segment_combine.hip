@@ -108,7 +108,12 @@ __global__ __launch_bounds__(SC_THREADS) void segment_combine_kernel(CombineArgs
     __syncthreads();  // every read of sA and sX done
     if (lead) sX[r] = x;
   }
-  if (a.S_final && lead) *reinterpret_cast<f32x4*>(&a.S_final[(bh * DK + r) * a.dv + col0]) = x;
+  // a head the chunk form could not evaluate keeps S0 (S_final may be S0):
+  // the tokenwise pass writes its final state
+  bool oor = false;
+  if (a.oor)
+    for (int s = 0; s < a.nseg; ++s) oor |= a.oor[bh * a.nseg + s] != 0;
+  if (a.S_final && lead && !oor) *reinterpret_cast<f32x4*>(&a.S_final[(bh * DK + r) * a.dv + col0]) = x;
 }
 
 template <int DK>

@@ -158,6 +158,10 @@ def test_workspace_bytes_layouts():
     assert ws(B=2, H=3, T=1024) == 0  # few heads but a short sequence: one pass is cheaper
     assert ws(B=8, H=16, T=4096, io=0, dk=64, dv=64, gain="pgdn") == 0  # fp32: serial scan
     assert ws(B=8, H=16, T=100, gain="pgdn") == 0  # not whole chunks: serial scan
+    # per-channel decay, one pass: an int per head, the out-of-range flags of
+    # the tokenwise pass
+    assert ws(B=8, H=16, T=4096, decay="channel") == 8 * 16 * 4
+    assert ws(B=8, H=16, T=4096, gain="gdn", decay="channel", io=0, dk=64, dv=64) == 8 * 16 * 4
     # the chunk-parallel gain scan: summaries [B, H, dk, T / C, 3], the
     # statistic entering every chunk [B, H, T / C, dk] and PGDN's centre per
     # chunk [H T / C], each on a 256-byte boundary
@@ -211,8 +215,9 @@ def test_chunk_fwd_long_rejects_bad_arguments():
     assert L.dn_chunk_fwd_long_workspace(ctypes.byref(dp), 4) == base + 4096 + 256 + 2 * 4 * 3 * 128 * 4
     assert L.dn_chunk_fwd_long_workspace(ctypes.byref(d), 3) == 0  # does not divide T
     # isotropic KDN: one statistic per head (aux_in 8 floats, mu_seg 8 floats, 2 x 4 pieces x 3)
+    # then (per-channel decay) the out-of-range flags, an int per segment
     di = _desc(B=1, H=2, T=1024, gain="kdn_iso", decay="channel")
-    assert L.dn_chunk_fwd_long_workspace(ctypes.byref(di), 4) == base + 256 + 256 + 2 * 4 * 3 * 4
+    assert L.dn_chunk_fwd_long_workspace(ctypes.byref(di), 4) == base + 256 + 256 + 256 + 2 * 4 * 4
     # 192-token segments: 64-token pieces, 3 per segment
     assert L.dn_chunk_fwd_long_workspace(ctypes.byref(_desc(B=1, H=2, T=1536, gain="pgdn")), 8) == \
         16 * 128 * (128 + 2 * 128) * 4 + 16 * 128 * 4 + 256 + 2 * 24 * 3 * 128 * 4

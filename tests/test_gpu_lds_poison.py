@@ -56,6 +56,19 @@ def test_poisoned_chunk_fwd(debug_library, gain, decay, keys, io, dk, dv):
     _check_fwd(wl, inp, o, S, aux)
 
 
+@pytest.mark.parametrize("gain,io", [("kdn", "bf16"), ("gdn", "f32")])
+def test_poisoned_token_pass(debug_library, gain, io):
+    """Head 0's decay leaves the chunk form's range in chunk 0 (2^-220 over
+    tokens 10..31): the tokenwise pass recomputes it."""
+    d = 128 if io == "bf16" else 64
+    wl = W.Workload(f"poison_oor_{gain}", gain, "channel", io, 1, 2, 200, d, d,
+                    keys="scaled" if gain == "kdn" else "unit", seed=993)
+    inp = W.generate(wl)
+    inp["alpha"][0, 0, 10:32, 4] = np.float32(2.0 ** -10)
+    o, S, aux = gpu_chunk(wl, inp)
+    _check_fwd(wl, inp, o, S, aux)
+
+
 @pytest.mark.parametrize("gain,decay,keys", [("kla", "scalar", "scaled"), ("pgdn", "scalar", "unit"),
                                              ("kdn_iso", "channel", "scaled")])
 def test_poisoned_segmented(debug_library, gain, decay, keys):
