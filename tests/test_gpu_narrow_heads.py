@@ -47,6 +47,20 @@ def test_narrow_heads_chunk_fwd(gain, decay, keys, io, dk, dv, T):
     _check(wl, inp, o, S, aux)
 
 
+@pytest.mark.parametrize("gain,keys,io,dk,dv", [("kdn", "scaled", "bf16", 120, 120),
+                                               ("gdn", "unit", "f32", 40, 48)])
+def test_narrow_heads_decay_beyond_range(gain, keys, io, dk, dv):
+    """A channel whose decay leaves the chunk form's range (2^-320 over the
+    first half of chunk 2) in a padded head: the padded call's tokenwise pass
+    recomputes the head before the outputs are cropped."""
+    wl = W.Workload(f"narrow_oor_{gain}_{io}", gain, "channel", io, 1, 2, 200, dk, dv, keys=keys,
+                    seed=960 + dk)
+    inp = W.generate(wl)
+    inp["alpha"][0, 1, 128:160, dk - 3] = np.float32(2.0 ** -10)
+    o, S, aux = gpu_chunk(wl, inp)
+    _check(wl, inp, o, S, aux)
+
+
 def test_narrow_heads_in_place_resume():
     """S_final = S0 (in-place resume; aux_final goes to a second buffer, as
     dn_chunk_fwd requires) at d = 120: two calls over the halves of the
