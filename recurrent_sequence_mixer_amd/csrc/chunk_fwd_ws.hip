@@ -1362,6 +1362,10 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           fetch_k(1);
           fetch_q(1);
           fetch_v(1);
+          // REG: q is staged two chunks ahead (in P3), so chunk 1's now
+          if constexpr (REG) {
+            if (nchunks > 1) stash_q(1);
+          }
         }
       }
       __syncthreads();
@@ -1401,15 +1405,17 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
         if constexpr (CONS) {
           cons_p1(c);
         } else if constexpr (LOAD) {
-          // k, q (PGDN: and the gates) of chunk c + 1 into LDS; the loads of k
-          // and of the gates of chunk c + 2
+          // k, q (PGDN: and the gates) of chunk c + 1 into LDS (REG: q goes in
+          // P3, away from the consumers' fragment reads of this phase); the
+          // loads of k and of the gates of chunk c + 2 (REG: and of q)
           if (c + 1 < nchunks) {
             stash_k(c + 1, n1);
-            stash_q(c + 1);
+            if constexpr (!REG) stash_q(c + 1);
             if constexpr (PG) stash_gates(c + 1, n1);
           }
           fetch_k(c + 2);
           fetch_gates(c + 2);
+          if constexpr (REG) fetch_q(c + 2);
           // their off-diagonal tiles of chunk c (PGDN: the raw products too)
           if constexpr (PG) tiles_off(c);
           scale_off(c);
@@ -1435,7 +1441,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           // v of chunk c + 1 into LDS (chunk c's was last read in P1); the
           // loads of q and v of chunk c + 2; PGDN: their share of pass 1
           if (c + 1 < nchunks) stash_v();
-          fetch_q(c + 2);
+          if constexpr (!REG) fetch_q(c + 2);
           fetch_v(c + 2);
           if constexpr (PG) {
             if (c + 1 < nchunks) gains1(c + 1);
@@ -1459,11 +1465,15 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
         if constexpr (CONS) {
           cons_p3(c);
         } else if constexpr (LOAD) {
-          // REG: the gates of chunk c + 2 into LDS (their parity's last
-          // readers, regains and diag_gains of chunk c, are done); PGDN: their
-          // share of pass 2
-          if constexpr (REG) stash_gates(c + 2, ntok(c + 2));
-          else if (c + 1 < nchunks) gains2(c + 1);
+          // REG: the gates and q of chunk c + 2 into LDS (their parity's last
+          // readers - regains and diag_gains of chunk c, its Q S - are done);
+          // PGDN: their share of pass 2
+          if constexpr (REG) {
+            stash_gates(c + 2, ntok(c + 2));
+            if (c + 2 < nchunks) stash_q(c + 2);
+          } else if (c + 1 < nchunks) {
+            gains2(c + 1);
+          }
         } else {
           if (c + 1 < nchunks) {
             if constexpr (REG) scale_diag(c + 1);
