@@ -787,7 +787,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
         for (int t4 = 0; t4 < SL; t4 += 4) {
           const int t = g * SL + t4;
           const f32x4 kk = KL::col4(kw, t, cb, lane);
-          const f32x4 qq = KL::col4(qh, t, cb, lane);
+          const f32x4 qq = OUT ? KL::col4(qh, t, cb, lane) : zero4();
           const f32x4 al = KL::col4(sm.w[0], t, cb, lane);
           // diagonal KDN: omega; explicit w: w
           const f32x4 om = KD || BG == GAIN_EXPLICIT ? KL::col4(sm.w[1], t, cb, lane) : zero4();
@@ -830,8 +830,10 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
                            pkw = pack_bf2(xw[0], xw[1]);
             kh[KL::idx(t + j, d)] = static_cast<uint16_t>(pkh);
             kh[KL::idx(t + j + 1, d)] = static_cast<uint16_t>(pkh >> 16);
-            qh[KL::idx(t + j, d)] = static_cast<uint16_t>(pqh);
-            qh[KL::idx(t + j + 1, d)] = static_cast<uint16_t>(pqh >> 16);
+            if constexpr (OUT) {
+              qh[KL::idx(t + j, d)] = static_cast<uint16_t>(pqh);
+              qh[KL::idx(t + j + 1, d)] = static_cast<uint16_t>(pqh >> 16);
+            }
             kw[KL::idx(t + j, d)] = static_cast<uint16_t>(pkw);
             kw[KL::idx(t + j + 1, d)] = static_cast<uint16_t>(pkw >> 16);
           }
@@ -1245,21 +1247,22 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
       //       the loads of q, v of c + 2.
       if (nchunks > 0) {
         if constexpr (LOAD) {
+          // (without an output nothing reads q or Q^: neither is formed)
           const int n0 = ntok(0);
           fetch_k(0);
-          fetch_q(0);
+          if constexpr (OUT) fetch_q(0);
           fetch_v(0);
           fetch_ao(0);
           fetch_gates(0);
           stash_k(0, n0);
-          stash_q(0);
+          if constexpr (OUT) stash_q(0);
           stash_v();
           stash_ao(n0);
           stash_gates(0, n0);
           fetch_k(1);
           fetch_ao(1);
           fetch_gates(1);
-          fetch_q(1);
+          if constexpr (OUT) fetch_q(1);
           fetch_v(1);
         }
       }
@@ -1311,7 +1314,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
         } else {
           if constexpr (LOAD) {
             if (c + 1 < nchunks) {
-              stash_q(c + 1);
+              if constexpr (OUT) stash_q(c + 1);
               stash_v();
             }
           }
@@ -1337,7 +1340,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           // the loads of q and v of chunk c + 2 (staged in P2 of chunk c + 1),
           // issued here, where the loaders have no scan work to hold back;
           // the raw products of their off-diagonal tiles of chunk c + 1
-          fetch_q(c + 2);
+          if constexpr (OUT) fetch_q(c + 2);
           fetch_v(c + 2);
           if (c + 1 < nchunks) tiles_off(c + 1);
         }
@@ -1348,22 +1351,23 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
       if (nchunks > 0) {
         // loaders: chunk 0 (REG: and the gates of chunk 1) into LDS; the loads
         // the loop stages first (k, q, v and, PGDN, the gates of chunk 1)
+        // (without an output nothing reads q: it is neither loaded nor staged)
         if constexpr (LOAD) {
           fetch_k(0);
-          fetch_q(0);
+          if constexpr (OUT) fetch_q(0);
           fetch_v(0);
           fetch_gates(0);
           stash_k(0, min(CH, T));
-          stash_q(0);
+          if constexpr (OUT) stash_q(0);
           stash_v();
           stash_gates(0, min(CH, T));
           fetch_gates(1);
           if constexpr (REG) stash_gates(1, ntok(1));
           fetch_k(1);
-          fetch_q(1);
+          if constexpr (OUT) fetch_q(1);
           fetch_v(1);
           // REG: q is staged two chunks ahead (in P3), so chunk 1's now
-          if constexpr (REG) {
+          if constexpr (REG && OUT) {
             if (nchunks > 1) stash_q(1);
           }
         }
@@ -1410,12 +1414,12 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           // loads of k and of the gates of chunk c + 2 (REG: and of q)
           if (c + 1 < nchunks) {
             stash_k(c + 1, n1);
-            if constexpr (!REG) stash_q(c + 1);
+            if constexpr (!REG && OUT) stash_q(c + 1);
             if constexpr (PG) stash_gates(c + 1, n1);
           }
           fetch_k(c + 2);
           fetch_gates(c + 2);
-          if constexpr (REG) fetch_q(c + 2);
+          if constexpr (REG && OUT) fetch_q(c + 2);
           // their off-diagonal tiles of chunk c (PGDN: the raw products too)
           if constexpr (PG) tiles_off(c);
           scale_off(c);
@@ -1441,7 +1445,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           // v of chunk c + 1 into LDS (chunk c's was last read in P1); the
           // loads of q and v of chunk c + 2; PGDN: their share of pass 1
           if (c + 1 < nchunks) stash_v();
-          if constexpr (!REG) fetch_q(c + 2);
+          if constexpr (!REG && OUT) fetch_q(c + 2);
           fetch_v(c + 2);
           if constexpr (PG) {
             if (c + 1 < nchunks) gains1(c + 1);
@@ -1470,7 +1474,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           // PGDN: their share of pass 2
           if constexpr (REG) {
             stash_gates(c + 2, ntok(c + 2));
-            if (c + 2 < nchunks) stash_q(c + 2);
+            if (OUT && c + 2 < nchunks) stash_q(c + 2);
           } else if (c + 1 < nchunks) {
             gains2(c + 1);
           }
