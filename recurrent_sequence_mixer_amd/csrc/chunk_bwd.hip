@@ -37,8 +37,8 @@
 // factors stay finite while each half-chunk decay of a channel is at least
 // 2^-96, the range of the chunked forward; beyond it the reference is NaN.
 //
-// chunk_bwd_state_kernel: one workgroup per (batch, head, DVS value
-// columns).  The value columns of dS evolve independently, so each
+// chunk_bwd_state_kernel: one workgroup per (batch, head, DVS = 16 or 32
+// value columns).  The value columns of dS evolve independently, so each
 // workgroup carries its slice of dS; the per-token key-side gradients (dq,
 // dk, dw, dG) are sums over value columns and are accumulated over the
 // slices with fp32 atomics.  A forward sweep first stores the state entering
@@ -69,9 +69,10 @@ constexpr int PC = CH + 1;  // row pitch of [CH][CH] fp32 arrays
 constexpr int PT = 17;      // row pitch of the 16x16 diagonal-block inverses
 constexpr int RT = 31;      // reference token of the per-channel decay factors
 
-template <typename E, int DK, bool CHAN>
+// DVS_: value columns per workgroup, 16 or 32 (channel decay: 16)
+template <typename E, int DK, bool CHAN, int DVS_>
 struct Smem {
-  static constexpr int DVS = CHAN ? 16 : 32;  // value columns per workgroup
+  static constexpr int DVS = DVS_;            // value columns per workgroup
   static constexpr int PS = DVS + 1;          // row pitch of [x][DVS] fp32 arrays
   static constexpr int PK = DK + 2;           // row pitch of the [CH][DK] operand rows
   static constexpr int PG = DK + 1;           // row pitch of the per-channel decay
@@ -176,9 +177,9 @@ __device__ __forceinline__ f32x4 mm(f32x4 acc, int k0, int k1, FA fa, FB fb, int
   return acc;
 }
 
-template <typename E, int DK, bool CHAN>
+template <typename E, int DK, bool CHAN, int DVS_>
 __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
-  using Sm = Smem<E, DK, CHAN>;
+  using Sm = Smem<E, DK, CHAN, DVS_>;
   constexpr int PK = Sm::PK, PS = Sm::PS, PG = Sm::PG, DVS = Sm::DVS;
   constexpr int NC = DVS / 16;      // 16-column tiles of the value slice
   constexpr int ND = DK / 16;       // 16-row tiles of the key dimension
@@ -864,12 +865,12 @@ __global__ void zero_kernel(float* p, size_t n) {
 
 }  // namespace bwd
 
-template <typename E, int DK, bool CHAN>
-static hipError_t launch_bwd_state_t(const BwdArgs& a, hipStream_t st) {
-  using Sm = bwd::Smem<E, DK, CHAN>;
+template <typename E, int DK, bool CHAN, int DVS>
+static hipError_t launch_bwd_state_w(const BwdArgs& a, hipStream_t st) {
+  using Sm = bwd::Smem<E, DK, CHAN, DVS>;
   static_assert(sizeof(Sm) <= 160 * 1024, "LDS budget");
   if (a.dv % Sm::DVS != 0) return hipErrorInvalidValue;
-  auto kern = bwd::chunk_bwd_state_kernel<E, DK, CHAN>;
+  auto kern = bwd::chunk_bwd_state_kernel<E, DK, CHAN, DVS>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(sizeof(Sm)));
@@ -877,6 +878,22 @@ static hipError_t launch_bwd_state_t(const BwdArgs& a, hipStream_t st) {
   const unsigned grid = static_cast<unsigned>(static_cast<long>(a.B) * a.H * (a.dv / Sm::DVS));
   hipLaunchKernelGGL(kern, dim3(grid), dim3(bwd::NT), sizeof(Sm), st, a);
   return hipGetLastError();
+}
+
+// Value slices of 32 columns, or of 16 (channel decay; and scalar decay when
+// 32-column slices would leave most compute units idle: a workgroup's time
+// is a serial walk over the chunks, so more, narrower slices finish sooner
+// as long as they fit on the device at once)
+constexpr long BWD_CU_COUNT = 256;  // compute units of an MI355X
+template <typename E, int DK, bool CHAN>
+static hipError_t launch_bwd_state_t(const BwdArgs& a, hipStream_t st) {
+  if constexpr (CHAN) {
+    return launch_bwd_state_w<E, DK, CHAN, 16>(a, st);
+  } else {
+    const long wide = static_cast<long>(a.B) * a.H * (a.dv / 32);
+    if (2 * wide <= BWD_CU_COUNT) return launch_bwd_state_w<E, DK, CHAN, 16>(a, st);
+    return launch_bwd_state_w<E, DK, CHAN, 32>(a, st);
+  }
 }
 
 template <bool CHAN>
