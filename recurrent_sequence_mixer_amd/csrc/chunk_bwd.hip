@@ -163,6 +163,38 @@ __device__ __forceinline__ float col4_sum(float v) {
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// v_mfma_f32_16x16x16_bf16: lane l supplies A row l % 16 and B column l % 16
+// at k = 4 (l / 16) .. +3; the result has the layout of mfma4's
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+// An fp32 value as a pair of bf16, hi = bf16(v) and lo = bf16(v - hi), in one
+// word (hi in the low half): hi + lo equals v to about 2^-17 of |v|, so a
+// product of such a value with a bf16 value takes two bf16 matrix
+// instructions at nearly fp32 accuracy.  The fp32 zero is the pair (0, 0).
+__device__ __forceinline__ uint32_t split_bf(float v) {
+  const uint16_t hi = f2bf(v);
+  return static_cast<uint32_t>(hi) | (static_cast<uint32_t>(f2bf(v - bf2f(hi))) << 16);
+}
+// the hi and lo halves of four split words as two bf16x4 operands
+__device__ __forceinline__ void split4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, s16x4& hi,
+                                       s16x4& lo) {
+  hi = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(x1, x0, 0x05040100u),
+                                       __builtin_amdgcn_perm(x3, x2, 0x05040100u)});
+  lo = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(x1, x0, 0x07060302u),
+                                       __builtin_amdgcn_perm(x3, x2, 0x07060302u)});
+}
+// four bf16 at stride `ld` (a column of a row-major array) as one operand
+__device__ __forceinline__ s16x4 bf4_col(const uint16_t* p, int ld) {
+  return __builtin_bit_cast(s16x4, u32x2{static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[ld]) << 16),
+                                         static_cast<uint32_t>(p[2 * ld]) | (static_cast<uint32_t>(p[3 * ld]) << 16)});
+}
+// four consecutive bf16 of a row from k (a multiple of 4; rows at a pitch of
+// an even number of elements, so both halves are 4-byte aligned)
+__device__ __forceinline__ s16x4 bf4(const uint16_t* row, int k) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(row + k);
+  return __builtin_bit_cast(s16x4, u32x2{p[0], p[1]});
+}
 
 // One 16x16 output tile of a product on v_mfma_f32_16x16x4_f32:
 // acc += sum over k in [k0, k1) of A[r][k] B[k][c], k0 and k1 multiples of 4,
@@ -293,7 +325,20 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
     for (int tile = wave; tile < 16; tile += NW) {
       const int tr = tile >> 2, tc = tile & 3;
       f32x4 al = zero4(), am = zero4();
-      if (tr >= tc) {
+      if (tr >= tc && sizeof(E) == 2) {
+        // bf16 operands: products of bf16 values are exact, so the bf16 matrix
+        // instruction (16 k per step) gives the fp32 instruction's sums
+        const uint16_t* kr = reinterpret_cast<const uint16_t*>(sm.k) + (16 * tr + lr) * PK;
+        const uint16_t* qr = reinterpret_cast<const uint16_t*>(sm.q) + (16 * tr + lr) * PK;
+        const uint16_t* wr = reinterpret_cast<const uint16_t*>(sm.w) + (16 * tc + lr) * PK;
+#pragma unroll 4
+        for (int k0 = 0; k0 < DK; k0 += 16) {
+          const int k_ = k0 + 4 * lg;
+          const s16x4 wv = bf4(wr, k_);
+          al = mfma16(bf4(kr, k_), wv, al);
+          if (with_m) am = mfma16(bf4(qr, k_), wv, am);
+        }
+      } else if (tr >= tc) {
         if (with_m) {
 #pragma unroll 4
           for (int k0 = 0; k0 < DK; k0 += 4) {
@@ -477,7 +522,18 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
     // dL = -dR E^T, dM = dO E^T.  Scalar decay: their decay terms (L o dL,
     // M o dM: + to the row token, - to the column token), then L <- D o dL,
     // M <- D o dM.  Channel decay: L <- dL, M <- dM (the decay terms follow
-    // per channel below)
+    // per channel below).  bf16 io: stored as split pairs (split_bf) for the
+    // products with the bf16 operands below; the entries not written are 0
+    // in either form
+    auto put_lm = [&](int at, float l, float m) __attribute__((always_inline)) {
+      if constexpr (sizeof(E) == 2) {
+        reinterpret_cast<uint32_t*>(sm.lm)[at] = split_bf(l);
+        reinterpret_cast<uint32_t*>(sm.mm)[at] = split_bf(m);
+      } else {
+        sm.lm[at] = l;
+        sm.mm[at] = m;
+      }
+    };
     for (int tile = wave; tile < 16; tile += NW) {
       const int tr = tile >> 2, tc = tile & 3;
       if (tr < tc) continue;
@@ -498,8 +554,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
         const float dl = -al[ii], dmv = am[ii];
         if constexpr (CHAN) {
           if (ok) {
-            sm.lm[j * PC + i] = i < j ? dl : 0.f;
-            sm.mm[j * PC + i] = dmv;
+            put_lm(j * PC + i, i < j ? dl : 0.f, dmv);
           }
         } else {
           float tlm = 0.f;
@@ -507,8 +562,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
             const float dm = expf(sm.G[j] - sm.G[i]);
             tlm = (i < j ? sm.lm[j * PC + i] * dl : 0.f) + sm.mm[j * PC + i] * dmv;
             if (i == j) tlm = 0.f;  // the diagonal adds and subtracts the same term
-            sm.lm[j * PC + i] = i < j ? dm * dl : 0.f;
-            sm.mm[j * PC + i] = dm * dmv;
+            put_lm(j * PC + i, i < j ? dm * dl : 0.f, dm * dmv);
           }
           col -= tlm;
           const float row = row16_sum(tlm);  // + to the row token j
@@ -544,18 +598,53 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
         atw = mfma4(sm.e[(16 * tb_ + lr) * PS + k_], sm.dS[(16 * db + lr) * PS + k_], atw);
       }
       f32x4 ask = zero4(), asq = zero4(), asw = zero4(), asw2 = zero4();
+      if constexpr (sizeof(E) == 2) {
+        // (D o dL), (D o dM) as split pairs times the bf16 w, k, q: two bf16
+        // matrix instructions per 16 k
+        const uint32_t* lmu = reinterpret_cast<const uint32_t*>(sm.lm);
+        const uint32_t* mmu = reinterpret_cast<const uint32_t*>(sm.mm);
+        const uint16_t* wb = reinterpret_cast<const uint16_t*>(sm.w) + 16 * db + lr;
+        const uint16_t* kb = reinterpret_cast<const uint16_t*>(sm.k) + 16 * db + lr;
+        const uint16_t* qb = reinterpret_cast<const uint16_t*>(sm.q) + 16 * db + lr;
+#pragma unroll 2
+        for (int k0 = 0; k0 < 16 * (tb_ + 1); k0 += 16) {
+          const int k_ = k0 + 4 * lg;
+          const s16x4 wv = bf4_col(wb + k_ * PK, PK);
+          const uint32_t* lr_ = lmu + (16 * tb_ + lr) * PC + k_;
+          const uint32_t* mr_ = mmu + (16 * tb_ + lr) * PC + k_;
+          s16x4 h, l;
+          split4(lr_[0], lr_[1], lr_[2], lr_[3], h, l);
+          ask = mfma16(l, wv, mfma16(h, wv, ask));
+          split4(mr_[0], mr_[1], mr_[2], mr_[3], h, l);
+          asq = mfma16(l, wv, mfma16(h, wv, asq));
+        }
+#pragma unroll 2
+        for (int k0 = 16 * tb_; k0 < CH; k0 += 16) {
+          const int k_ = k0 + 4 * lg;
+          const uint32_t* lc = lmu + k_ * PC + 16 * tb_ + lr;
+          const uint32_t* mc = mmu + k_ * PC + 16 * tb_ + lr;
+          s16x4 h, l;
+          split4(lc[0], lc[PC], lc[2 * PC], lc[3 * PC], h, l);
+          const s16x4 kv = bf4_col(kb + k_ * PK, PK);
+          asw = mfma16(l, kv, mfma16(h, kv, asw));
+          split4(mc[0], mc[PC], mc[2 * PC], mc[3 * PC], h, l);
+          const s16x4 qv = bf4_col(qb + k_ * PK, PK);
+          asw2 = mfma16(l, qv, mfma16(h, qv, asw2));
+        }
+      } else {
 #pragma unroll 4
-      for (int k0 = 0; k0 < 16 * (tb_ + 1); k0 += 4) {
-        const int k_ = k0 + lg;
-        const float wv = wf(k_, 16 * db + lr);
-        ask = mfma4(sm.lm[(16 * tb_ + lr) * PC + k_], wv, ask);
-        asq = mfma4(sm.mm[(16 * tb_ + lr) * PC + k_], wv, asq);
-      }
+        for (int k0 = 0; k0 < 16 * (tb_ + 1); k0 += 4) {
+          const int k_ = k0 + lg;
+          const float wv = wf(k_, 16 * db + lr);
+          ask = mfma4(sm.lm[(16 * tb_ + lr) * PC + k_], wv, ask);
+          asq = mfma4(sm.mm[(16 * tb_ + lr) * PC + k_], wv, asq);
+        }
 #pragma unroll 4
-      for (int k0 = 16 * tb_; k0 < CH; k0 += 4) {
-        const int k_ = k0 + lg;
-        asw = mfma4(sm.lm[k_ * PC + 16 * tb_ + lr], kf(k_, 16 * db + lr), asw);
-        asw2 = mfma4(sm.mm[k_ * PC + 16 * tb_ + lr], qf(k_, 16 * db + lr), asw2);
+        for (int k0 = 16 * tb_; k0 < CH; k0 += 4) {
+          const int k_ = k0 + lg;
+          asw = mfma4(sm.lm[k_ * PC + 16 * tb_ + lr], kf(k_, 16 * db + lr), asw);
+          asw2 = mfma4(sm.mm[k_ * PC + 16 * tb_ + lr], qf(k_, 16 * db + lr), asw2);
+        }
       }
       asw += asw2;
       float ce = 0.f;  // channel decay: this lane's part of the chunk end's dL/dG
