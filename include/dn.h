@@ -98,7 +98,7 @@ typedef enum dn_status {
   DN_ERR_DTYPE = -3,       /* unknown io dtype                                 */
   DN_ERR_GAIN = -4,        /* unknown gain / decay, or invalid gain parameter  */
   DN_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required       */
-  DN_ERR_UNSUPPORTED = -6, /* valid but not built (e.g. fp32 io with dk = 128) */
+  DN_ERR_UNSUPPORTED = -6, /* valid but not built (e.g. the backward in fp32 io with dk = 128) */
   DN_ERR_HIP = -7,         /* a kernel launch failed                           */
   DN_ERR_ALIAS = -8        /* forbidden overlap between buffers                */
 } dn_status;
@@ -128,8 +128,12 @@ typedef enum dn_decay { DN_DECAY_SCALAR = 0, DN_DECAY_CHANNEL = 1 } dn_decay;
  *   back; isotropic KDN's mu rescaled so that mu ||k||^2 / (d_k r) keeps its
  *   value), the decode step masked in place.  Isotropic KDN with channel
  *   decay at such a d_k (the mean of alpha^2 over the channels has no padded
- *   form), fp32 io with dk > 64, the backward and the segmented call at such
- *   widths return DN_ERR_UNSUPPORTED;
+ *   form), the backward and the segmented call at such widths return
+ *   DN_ERR_UNSUPPORTED.  fp32 io with dk > 64: dn_chunk_fwd evaluates the
+ *   token recurrence per head (exact; a sequential pass over T, about a
+ *   microsecond per token) and needs no workspace for it; dn_gain_prep and
+ *   dn_decode_step run their usual kernels; dn_chunk_bwd returns
+ *   DN_ERR_UNSUPPORTED;
  *   C = 64, the chunk length of the chunked forward and backward; dn_gain_prep
  *   also takes C = 32 (its per-chunk outputs and parallel scan pieces: the
  *   memory chunk of 32 or 64 tokens of Kalman Delta Networks Appendix D);

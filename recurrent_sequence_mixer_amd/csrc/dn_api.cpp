@@ -219,7 +219,7 @@ static int run_token_pass(const dn_desc* d, const void* q, const void* k, const 
   t.aux_final = has_aux ? aux_final : nullptr;
   t.flags = oor;
   t.nflag = nflag;
-  return hip_status(dn::launch_token_fwd(t, d->io == DN_BF16, d->gain, s));
+  return hip_status(dn::launch_token_fwd(t, d->io == DN_BF16, d->gain, d->decay == DN_DECAY_CHANNEL, s));
 }
 
 static bool long_shape_ok(const dn_desc* d, int nseg) {
@@ -463,6 +463,7 @@ static PadLayout pad_layout(const dn_desc* d, bool prep) {
 
 static size_t chunk_ws_bytes(const dn_desc* d) {
   if (!kernel_dims(d)) return pad_layout(d, false).total;
+  if (d->io == DN_F32 && d->dk == 128) return 0;  // the tokenwise kernel: no workspace
   const int nseg = auto_nseg(d);
   return nseg > 1 ? long_layout(d, nseg).total : oor_bytes(d, 1);
 }
@@ -580,7 +581,6 @@ DN_EXPORT int dn_chunk_fwd(const dn_desc* d, const void* q, const void* k, const
     if ((st = check_gates(d, g)) != DN_OK) return st;
     if (!q || !k || !v || !o) return DN_ERR_NULL;
   }
-  if (d->io == DN_F32 && d->dk > 64) return DN_ERR_UNSUPPORTED;
   if (!paddable(d)) return DN_ERR_UNSUPPORTED;
   const size_t need = chunk_ws_bytes(d);
   if (need > 0 && (!ws || ws_bytes < need)) return DN_ERR_WORKSPACE;
@@ -631,6 +631,11 @@ DN_EXPORT int dn_chunk_fwd(const dn_desc* d, const void* q, const void* k, const
                     static_cast<hipStream_t>(stream));
   }
 
+  // fp32 io at d_k = 128: no chunk kernel is built for it (its fp32 operand
+  // tiles would exceed the LDS); the tokenwise kernel runs every head
+  if (d->io == DN_F32 && d->dk == 128)
+    return run_token_pass(d, q, k, v, g ? g : &nog, S0, aux0, 1, o, S_final, aux_final, nullptr, 0,
+                          static_cast<hipStream_t>(stream));
   // per-channel decay: the out-of-range flags in the workspace
   int* const oor = need > 0 ? static_cast<int*>(ws) : nullptr;
   if (oor && (st = check_long_aliases(d, g ? g : &nog, q, k, v, S0, aux0, o, S_final, aux_final, ws,
@@ -824,7 +829,6 @@ DN_EXPORT int dn_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, c
   int st = check_desc(d, false);
   if (st != DN_OK) return st;
   if (d->C != 64 && d->C != 32) return DN_ERR_SHAPE;
-  if (d->io == DN_F32 && d->dk > 64) return DN_ERR_UNSUPPORTED;
   if (!paddable(d)) return DN_ERR_UNSUPPORTED;
   if ((st = check_gates(d, g)) != DN_OK) return st;
   if (!k || !w_out) return DN_ERR_NULL;

@@ -58,10 +58,10 @@ struct ChunkArgs {
   int* oor = nullptr;
 };
 
-// Tokenwise forward of the heads flagged by the chunked kernels
-// (token_fwd.hip): per-channel decay, kernel widths (dk 64 / 128, dv a
-// multiple of 64).  A head of [B, H] runs when any of its nflag entries of
-// flags [B, H, nflag] is nonzero, from S0 (nullable: zeros) and the
+// Tokenwise forward of the heads flagged by the chunked kernels, and of
+// every head for fp32 io at dk = 128 (token_fwd.hip): kernel widths (dk 64 /
+// 128, dv a multiple of 64).  A head of [B, H] runs when any of its nflag entries of
+// flags [B, H, nflag] is nonzero (flags NULL: every head), from S0 (nullable: zeros) and the
 // statistic aux0[(b H + h) aux_seg] (nullable: ones), writing o, S_final and
 // aux_final (each nullable).
 struct TokenArgs {
@@ -77,7 +77,7 @@ struct TokenArgs {
   const int* flags;
   int nflag;
 };
-hipError_t launch_token_fwd(const TokenArgs& a, int io_bf16, int gain, hipStream_t st);
+hipError_t launch_token_fwd(const TokenArgs& a, int io_bf16, int gain, bool channel, hipStream_t st);
 
 // Long-sequence forward by segments (segment_combine.hip): per head, the
 // entering state of every segment from the segments' transfer matrices A_s

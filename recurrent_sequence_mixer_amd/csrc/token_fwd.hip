@@ -14,7 +14,9 @@
 // One workgroup per (batch, head, 64-column value slice) keeps its d_k x 64
 // slice of S in registers for the whole sequence; a head that is not flagged
 // returns at once, so the launch costs a few microseconds when no head needs
-// it.  The gain (and its statistic) is formed per token by every slice of the
+// it.  Without flags every head runs: the chunked forward's path for fp32
+// io at d_k = 128, which no chunk kernel is built for (its fp32 operand tiles
+// would exceed the LDS).  The gain (and its statistic) is formed per token by every slice of the
 // head, identically; slice 0 writes the final statistic.  Per token: one
 // reduction over the key channels, then the two readouts over the state rows,
 // then the residual, the output and the rank-1 update (four barriers); the
@@ -55,7 +57,8 @@ struct TokIn {
 
 }  // namespace
 
-template <typename IO, int DK, int GAIN>
+// CHAN: per-channel decay, alpha io [B, H, T, dk]; else alpha fp32 [B, H, T]
+template <typename IO, int DK, int GAIN, bool CHAN>
 __global__ __launch_bounds__(TW_THREADS) void token_fwd_kernel(TokenArgs a) {
   constexpr int CG = TW_BV / 4;           // float4 column groups
   constexpr int RG = TW_THREADS / CG;     // row groups
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(TW_THREADS) void token_fwd_kernel(TokenArgs a) {
   const long bh = blockIdx.x / nsl;
   const int sl = static_cast<int>(blockIdx.x % nsl);
   const int c0 = sl * TW_BV;
-  {
+  if (a.flags) {
     int any = 0;
     for (int i = 0; i < a.nflag; ++i) any |= a.flags[bh * a.nflag + i];
     if (!any) return;  // uniform over the workgroup
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(TW_THREADS) void token_fwd_kernel(TokenArgs a) {
     if (tid < DK) {
       x.k = ld<IO>(a.k, tt * DK + tid);
       x.q = ld<IO>(a.q, tt * DK + tid);
-      x.a = ld<IO>(a.g.alpha, tt * DK + tid);
+      x.a = CHAN ? ld<IO>(a.g.alpha, tt * DK + tid) : static_cast<const float*>(a.g.alpha)[tt];
       if constexpr (GAIN == GAIN_KDN) x.om = ld<IO>(a.g.omega, tt * DK + tid);
       if constexpr (GAIN == GAIN_EXPLICIT) x.w = ld<IO>(a.g.w, tt * DK + tid);
     }
@@ -128,7 +131,8 @@ __global__ __launch_bounds__(TW_THREADS) void token_fwd_kernel(TokenArgs a) {
     return x;
   };
 
-  TokIn cur = load(0);
+  TokIn cur{};
+  if (T > 0) cur = load(0);
   for (long t = 0; t < T; ++t) {
     const TokIn nx = load(t + 1 < T ? t + 1 : t);  // the next token's inputs, in flight
 
@@ -260,11 +264,11 @@ __global__ __launch_bounds__(TW_THREADS) void token_fwd_kernel(TokenArgs a) {
   }
 }
 
-template <typename IO, int DK>
+template <typename IO, int DK, bool CHAN>
 static hipError_t launch_token_dk(const TokenArgs& a, int gain, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(static_cast<long>(a.B) * a.H * (a.dv / TW_BV))),
       block(TW_THREADS);
-#define DN_TW(G) hipLaunchKernelGGL((token_fwd_kernel<IO, DK, G>), grid, block, 0, st, a)
+#define DN_TW(G) hipLaunchKernelGGL((token_fwd_kernel<IO, DK, G, CHAN>), grid, block, 0, st, a)
   switch (gain) {
     case GAIN_KLA: DN_TW(GAIN_KLA); break;
     case GAIN_GDN: DN_TW(GAIN_GDN); break;
@@ -278,16 +282,22 @@ static hipError_t launch_token_dk(const TokenArgs& a, int gain, hipStream_t st) 
   return hipGetLastError();
 }
 
-hipError_t launch_token_fwd(const TokenArgs& a, int io_bf16, int gain, hipStream_t st) {
-  if (a.T <= 0 || a.B * a.H <= 0) return hipSuccess;
-  if (a.dv % TW_BV != 0) return hipErrorInvalidValue;
+template <bool CHAN>
+static hipError_t launch_token_c(const TokenArgs& a, int io_bf16, int gain, hipStream_t st) {
   if (io_bf16) {
-    if (a.dk == 128) return launch_token_dk<uint16_t, 128>(a, gain, st);
-    if (a.dk == 64) return launch_token_dk<uint16_t, 64>(a, gain, st);
+    if (a.dk == 128) return launch_token_dk<uint16_t, 128, CHAN>(a, gain, st);
+    if (a.dk == 64) return launch_token_dk<uint16_t, 64, CHAN>(a, gain, st);
     return hipErrorInvalidValue;
   }
-  if (a.dk == 64) return launch_token_dk<float, 64>(a, gain, st);
+  if (a.dk == 128) return launch_token_dk<float, 128, CHAN>(a, gain, st);
+  if (a.dk == 64) return launch_token_dk<float, 64, CHAN>(a, gain, st);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_token_fwd(const TokenArgs& a, int io_bf16, int gain, bool channel, hipStream_t st) {
+  if (a.B * a.H <= 0) return hipSuccess;
+  if (a.dv % TW_BV != 0) return hipErrorInvalidValue;
+  return channel ? launch_token_c<true>(a, io_bf16, gain, st) : launch_token_c<false>(a, io_bf16, gain, st);
 }
 
 }  // namespace dn

@@ -75,7 +75,6 @@ def _desc(**kw):
     (dict(B=300, H=300), -2), (dict(io=7), -3), (dict(gain=9), -4), (dict(decay=3), -4),
     (dict(eps=-1.0), -4), (dict(gain="pgdn", x=0.5), -4), (dict(gain="kdn", mu_info=0.0), -4),
     (dict(gain="kdn_iso", mu_info=-1.0), -4), (dict(gain=6), -4),
-    (dict(io=0, dk=128), -6),
 ])
 def test_chunk_fwd_rejects_bad_descriptor(kw, status):
     assert _chunk(_desc(**kw)) == status
@@ -326,7 +325,13 @@ def test_narrow_heads_workspace_and_limits():
     assert L.dn_workspace_bytes(ctypes.byref(_desc(dk=120, dv=120, gain="kdn_iso", decay="channel"))) == 0
     gk = _gates(omega=FAKE + (6 << 30), r=FAKE + (7 << 30))
     assert _chunk(_desc(dk=120, dv=120, gain="kdn_iso", decay="channel"), gates=gk) == -6
-    assert _chunk(_desc(io=0, dk=120, dv=64)) == -6
+    # fp32 io wider than 64 key channels: the tokenwise kernel, no workspace
+    # beyond the padded copies (nothing is launched here)
+    assert L.dn_workspace_bytes(ctypes.byref(_desc(io=0, dk=128, dv=64))) == 0
+    assert L.dn_workspace_bytes(ctypes.byref(_desc(io=0, dk=128, dv=64, decay="channel"))) == 0
+    # (padded q, k; v, o; S0, S_final)
+    assert L.dn_workspace_bytes(ctypes.byref(_desc(io=0, dk=120, dv=64))) == \
+        2 * r256(bht * 128 * 4) + 2 * r256(bht * 64 * 4) + 2 * r256(bh * 128 * 64 * 4)
     assert L.dn_chunk_bwd_workspace(ctypes.byref(d)) == 0
     assert L.dn_chunk_fwd_long_workspace(ctypes.byref(_desc(B=1, H=1, T=4096, dk=120, dv=120)), 4) == 0
     # workspace missing or short for the padded copies

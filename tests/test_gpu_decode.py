@@ -232,7 +232,8 @@ def test_kdn_iso_prefill_decode_and_resume(decay):
                                            ("kdn", "channel", "bf16"), ("kdn", "channel", "f32"),
                                            ("gdn", "channel", "f32"), ("kdn_iso", "channel", "bf16"),
                                            ("kdn_iso", "scalar", "f32"), ("kdn", "scalar", "bf16"),
-                                           ("pgdn", "channel", "bf16"), ("kdn_iso", "scalar", "bf16")])
+                                           ("pgdn", "channel", "bf16"), ("kdn_iso", "scalar", "bf16"),
+                                           ("kdn", "channel", "f32_128"), ("pgdn", "scalar", "f32_128")])
 def test_gain_prep_per_token(gain, decay, io, T):
     """dn_gain_prep's per-token write vectors, chunk-start aux and in-chunk
     cumulative log-decay against the oracle's trace.  T = 320 (whole chunks)
@@ -241,8 +242,9 @@ def test_gain_prep_per_token(gain, decay, io, T):
     non-default aux0 and, for PGDN, a different centre per head."""
     dn = _dn()
     keys = "unit" if gain in ("gdn", "pgdn") else "scaled"
-    wl = W.Workload("gp", gain, decay, io, 2, 3, T, 128 if io == "bf16" else 64,
-                    128 if io == "bf16" else 64, keys=keys, mu_spread=1.0, seed=31)
+    d = 64 if io == "f32" else 128  # f32_128: fp32 io at d_k = 128
+    io = "f32" if io == "f32_128" else io
+    wl = W.Workload("gp", gain, decay, io, 2, 3, T, d, d, keys=keys, mu_spread=1.0, seed=31)
     inp = W.generate(wl)
     rng = np.random.default_rng(32)
     if gain in ("pgdn", "kdn", "kdn_iso"):

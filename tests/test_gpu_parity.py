@@ -53,6 +53,39 @@ def test_f32_gains_ragged(gain, T):
     _check(wl, inp, None, o, S, aux)
 
 
+# fp32 io at d_k = 128: dn_chunk_fwd runs the tokenwise kernel over every
+# head (no chunk kernel is built for fp32 operand tiles of that width);
+# d_v = 64 / 128 / 256, ragged lengths
+@pytest.mark.parametrize("T", [1, 150])
+@pytest.mark.parametrize("gain,decay,keys,dv", [("kla", "scalar", "scaled", 128), ("pgdn", "scalar", "unit", 64),
+                                                ("kdn", "channel", "scaled", 128),
+                                                ("kdn_iso", "channel", "scaled", 256),
+                                                ("gdn", "channel", "unit", 128), ("explicit", "scalar", "unit", 64)])
+def test_f32_dk128(gain, decay, keys, dv, T):
+    wl = W.Workload(f"{gain}_{decay}_f32_dk128", gain, decay, "f32", 2, 2, T, 128, dv, keys=keys,
+                    seed=800 + T + dv)
+    inp = W.generate(wl)
+    if gain == "explicit":
+        inp["w"] = np.random.default_rng(801).standard_normal((2, 2, T, 128)).astype(np.float32) * 0.05
+    if gain in ("pgdn", "kdn"):
+        inp["aux0"] = np.random.default_rng(802).uniform(0.5, 2.0, (2, 2, 128)).astype(np.float32)
+    o, S, aux = gpu_chunk(wl, inp)
+    _check(wl, inp, None, o, S, aux)
+
+
+def test_f32_dk128_empty_sequence():
+    """T = 0 on the tokenwise path: S_final = S0, aux_final = aux0."""
+    from recurrent_sequence_mixer_amd import dn
+    B, H, d = 1, 2, 128
+    S0 = torch.randn(B, H, d, d, device="cuda")
+    aux0 = torch.rand(B, H, d, device="cuda") + 0.5
+    z = torch.empty(B, H, 0, d, device="cuda")
+    gates = {"alpha": torch.empty(B, H, 0, d, device="cuda"), "omega": z, "r": torch.empty(B, H, 0, device="cuda")}
+    o, S, aux = dn.chunk_fwd(z, z, z, gates, gain="kdn", S0=S0, aux0=aux0)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S0) and torch.equal(aux, aux0)
+
+
 # ---------------------------------------------------------------- bf16, small
 
 @pytest.mark.parametrize("T", [1, 63, 65, 200, 333])
