@@ -170,6 +170,19 @@ def test_full_size_sampled_heads(idx):
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
 
 
+@pytest.mark.parametrize("gain,keys", [("gdn", "unit"), ("kla", "scaled")])
+def test_channel_decay_full_size_sampled_heads(gain, keys):
+    """KDA (GDN with per-channel decay) and KLA with per-channel decay at the
+    KLA workload's shape B8 H16 T4096 d128 (the bench's kda and kla_channel
+    lines), sampled heads."""
+    wl = W.WORKLOADS[1].replace(name=f"{gain}_channel_full", gain=gain, decay="channel", keys=keys)
+    inp = W.generate(wl)
+    o, S, aux = gpu_chunk(wl, inp)
+    nheads = wl.B * wl.H
+    _check(wl, inp, [0, nheads // 2, nheads - 1], o, S, aux)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+
+
 def test_kdn_iso_full_size_sampled_heads():
     """Isotropic KDN (Kalman Delta Networks §2.7) at the diagonal-KDN shape
     B4 H16 T8192 d128 with per-channel decay, sampled heads."""
