@@ -47,13 +47,15 @@
 // io dtype, w rounded to it), one product element per thread and step from
 // LDS.
 //
-// gain_bwd_kernel: one workgroup per (batch, head), one thread per key
-// channel, walking the tokens backwards: the write gain's derivative
-// (KLA / GDN: Kaczmarz Linear Attention §2.1; PGDN: Preconditioned DeltaNet
-// §2.4, Eq. 9; KDN: Kalman Delta Networks §2.4, Eqs. 23-30 with the
-// information scaling of §2.5; isotropic KDN: §2.7, Eq. 40 - the gain scan
-// differentiated backwards, Appendix D), the statistic recomputed per chunk
-// from its value at the chunk start, and the decay's gradient from dG.
+// gain_bwd_kernel (the gains with a statistic): one workgroup per (batch,
+// head), one thread per key channel, walking the tokens backwards: the write
+// gain's derivative (PGDN: Preconditioned DeltaNet §2.4, Eq. 9; KDN: Kalman
+// Delta Networks §2.4, Eqs. 23-30 with the information scaling of §2.5;
+// isotropic KDN: §2.7, Eq. 40 - the gain scan differentiated backwards,
+// Appendix D), the statistic recomputed per chunk from its value at the
+// chunk start, and the decay's gradient from dG.  gain_bwd_tok_kernel (KLA /
+// GDN: Kaczmarz Linear Attention §2.1; explicit w): one workgroup per chunk,
+// token-parallel.
 #include "common.hpp"
 #include "gains.hpp"
 #include "launch.hpp"
@@ -736,7 +738,8 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Back through the write gains and the decay.  Thread d owns key channel d.
+// Back through the write gains with a statistic and the decay.  Thread d owns
+// key channel d.
 template <typename E, int DK, int GAIN, bool CHAN>
 __global__ __launch_bounds__(DK) void gain_bwd_kernel(GainBwdArgs a) {
   constexpr int NW = DK / 64;
@@ -832,22 +835,7 @@ __global__ __launch_bounds__(DK) void gain_bwd_kernel(GainBwdArgs a) {
       float dkv = a.dk_out[ti * DK + d];
       float dag = 0.f;  // the decay's gradient through the gain (this channel's,
                         // or summed over channels for scalar decay)
-      if constexpr (GAIN == GAIN_KLA) {
-        // w = beta k, beta = eta / (n + eps), n = ||k||^2
-        float n2 = kk * kk, db = dw * kk, z0 = 0.f, z1 = 0.f;
-        reduce4(n2, db, z0, z1);
-        const float et = a.g.eta[ti], den = n2 + a.g.eps;
-        const float beta = et / den;
-        dkv = fmaf(beta, dw, fmaf(2.f * kk, db * (-et / (den * den)), dkv));
-        if (d == 0) a.deta[ti] = db / den;
-      } else if constexpr (GAIN == GAIN_GDN) {
-        float db = dw * kk, z0 = 0.f, z1 = 0.f, z2 = 0.f;
-        reduce4(db, z0, z1, z2);
-        dkv = fmaf(a.g.eta[ti], dw, dkv);
-        if (d == 0) a.deta[ti] = db;
-      } else if constexpr (GAIN == GAIN_EXPLICIT) {
-        a.dw_out[ti * DK + d] = dw;
-      } else if constexpr (PG) {
+      if constexpr (PG) {
         // A_t = alphaP A_{t-1} + betaP k^2;  r = log A_t - mu;  s = r / (1 + |r|);
         // B = exp(-log(x) s);  w = eta B k
         const float A = As[j][d];
@@ -946,6 +934,109 @@ __global__ __launch_bounds__(DK) void gain_bwd_kernel(GainBwdArgs a) {
   }
 }
 
+// N consecutive fp32 or io elements from element offset `off` (16-byte
+// accesses; off and N multiples of 8)
+template <typename E, int N>
+__device__ __forceinline__ void load_row(const void* base, long off, float (&v)[N]) {
+  load_vec<E, N>(base, off, true, v);
+}
+template <int N>
+__device__ __forceinline__ void store_row(float* base, long off, const float (&v)[N]) {
+  f32x4* p = reinterpret_cast<f32x4*>(base + off);
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) p[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+}
+
+// Back through the gains without a statistic (KLA, GDN, explicit w),
+// token-parallel: one workgroup per chunk of 64 tokens, four threads per
+// token with a quarter of the key channels each; the sums over a token's
+// channels are sums over its four lanes.  The decay's gradient is the suffix
+// sum of dL/dG over the chunk's tokens: one wavefront's for scalar decay, per
+// channel through LDS for per-channel decay.  Same derivatives as
+// gain_bwd_kernel, summed in another order.
+template <typename E, int DK, int GAIN, bool CHAN>
+__global__ __launch_bounds__(4 * CH) void gain_bwd_tok_kernel(GainBwdArgs a) {
+  constexpr int DQ = DK / 4;
+  __shared__ float s_dg[CHAN ? CH * DK : 1];
+  __shared__ float s_al[CHAN ? CH * DK : 1];
+  DN_LDS_POISON(s_dg, sizeof(s_dg));
+  DN_LDS_POISON(s_al, sizeof(s_al));
+  const int T = a.T, nch = (T + CH - 1) / CH;
+  const long bh = blockIdx.x / nch;
+  const int c = static_cast<int>(blockIdx.x % nch);
+  const int t0 = c * CH, n = min(CH, T - t0);
+  const int tid = threadIdx.x, tl = tid >> 2, q = tid & 3, d0 = q * DQ;
+  const bool ok = tl < n;
+  const long ti = bh * T + t0 + tl;
+  if (ok) {
+    float dw[DQ];
+    load_row<float, DQ>(a.dw_acc, ti * DK + d0, dw);
+    if constexpr (GAIN == GAIN_EXPLICIT) {
+      store_row<DQ>(a.dw_out, ti * DK + d0, dw);
+    } else {
+      float kv[DQ], dk[DQ];
+      load_row<E, DQ>(a.k, ti * DK + d0, kv);
+      load_row<float, DQ>(a.dk_out, ti * DK + d0, dk);
+      // (the four lanes of a token share `ok`, so its lane sums stay inside it)
+      float db = 0.f, n2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) {
+        db = fmaf(dw[i], kv[i], db);
+        n2 = fmaf(kv[i], kv[i], n2);
+      }
+      db += __shfl_xor(db, 1);
+      db += __shfl_xor(db, 2);
+      const float et = a.g.eta[ti];
+      if constexpr (GAIN == GAIN_KLA) {
+        // w = beta k, beta = eta / (n + eps), n = ||k||^2
+        n2 += __shfl_xor(n2, 1);
+        n2 += __shfl_xor(n2, 2);
+        const float den = n2 + a.g.eps, beta = et / den, g2 = db * (-et / (den * den));
+#pragma unroll
+        for (int i = 0; i < DQ; ++i) dk[i] = fmaf(beta, dw[i], fmaf(2.f * kv[i], g2, dk[i]));
+        if (q == 0) a.deta[ti] = db / den;
+      } else {
+#pragma unroll
+        for (int i = 0; i < DQ; ++i) dk[i] = fmaf(et, dw[i], dk[i]);
+        if (q == 0) a.deta[ti] = db;
+      }
+      store_row<DQ>(a.dk_out, ti * DK + d0, dk);
+    }
+  }
+  // dL/dalpha_t = (sum of dL/dG_j over j >= t in the chunk) / alpha_t
+  if constexpr (CHAN) {
+    if (ok) {
+      float g[DQ], al[DQ];
+      load_row<float, DQ>(a.dG, ti * DK + d0, g);
+      load_row<E, DQ>(a.g.alpha, ti * DK + d0, al);
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) {
+        s_dg[tl * DK + d0 + i] = g[i];
+        s_al[tl * DK + d0 + i] = al[i];
+      }
+    }
+    __syncthreads();
+    if (tid < DK) {
+      float sfx = 0.f;
+      for (int t = n - 1; t >= 0; --t) {
+        sfx += s_dg[t * DK + tid];
+        a.dalpha[(bh * T + t0 + t) * DK + tid] = sfx / s_al[t * DK + tid];
+      }
+    }
+  } else if (tid < 64) {
+    // lane l: token n - 1 - l, so that a prefix sum over the lanes is the
+    // suffix sum over the tokens
+    const int t = n - 1 - tid;
+    float sfx = t >= 0 ? a.dG[bh * T + t0 + t] : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(sfx, off);
+      if (tid >= off) sfx += y;
+    }
+    if (t >= 0) a.dalpha[bh * T + t0 + t] = sfx / static_cast<const float*>(a.g.alpha)[bh * T + t0 + t];
+  }
+}
+
 __global__ void zero_kernel(float* p, size_t n) {
   for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += static_cast<size_t>(gridDim.x) * blockDim.x)
@@ -1001,17 +1092,27 @@ hipError_t launch_chunk_bwd_state(const BwdArgs& a, int io_bf16, bool channel, h
 
 template <typename E, int DK, bool CHAN>
 static hipError_t launch_gain_bwd_t(const GainBwdArgs& a, int gain, hipStream_t st) {
+  if (gain == GAIN_KLA || gain == GAIN_GDN || gain == GAIN_EXPLICIT) {
+    // token-parallel, one workgroup per chunk of 64 tokens
+    const long nch = (a.T + bwd::CH - 1) / bwd::CH;
+    if (nch == 0) return hipSuccess;
+    const dim3 tg(static_cast<unsigned>(static_cast<long>(a.B) * a.H * nch)), tb(4 * bwd::CH);
+    if (gain == GAIN_KLA)
+      hipLaunchKernelGGL((bwd::gain_bwd_tok_kernel<E, DK, GAIN_KLA, CHAN>), tg, tb, 0, st, a);
+    else if (gain == GAIN_GDN)
+      hipLaunchKernelGGL((bwd::gain_bwd_tok_kernel<E, DK, GAIN_GDN, CHAN>), tg, tb, 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd::gain_bwd_tok_kernel<E, DK, GAIN_EXPLICIT, CHAN>), tg, tb, 0, st, a);
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>(a.B * a.H)), block(DK);
   switch (gain) {
 #define DN_GAIN_BWD_CASE(G)                                                               \
   case G:                                                                                 \
     hipLaunchKernelGGL((bwd::gain_bwd_kernel<E, DK, G, CHAN>), grid, block, 0, st, a); \
     break;
-    DN_GAIN_BWD_CASE(GAIN_KLA)
-    DN_GAIN_BWD_CASE(GAIN_GDN)
     DN_GAIN_BWD_CASE(GAIN_PGDN)
     DN_GAIN_BWD_CASE(GAIN_KDN)
-    DN_GAIN_BWD_CASE(GAIN_EXPLICIT)
     DN_GAIN_BWD_CASE(GAIN_KDN_ISO)
 #undef DN_GAIN_BWD_CASE
     default: return hipErrorInvalidValue;
