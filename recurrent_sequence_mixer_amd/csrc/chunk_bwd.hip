@@ -91,8 +91,9 @@ struct Smem {
   // dL/dG of the chunk's last token per channel
   float Gc[CHAN ? CH * PG : 1];
   float gref[CHAN ? DK : 1], gnr[CHAN ? DK : 1], endc[CHAN ? DK : 1];
-  // scalar decay: G, exp(G) and this slice's part of dL/dG per token
-  float G[CH], gam[CH], sg[CH];
+  // scalar decay: G, exp(G), exp(G_n - G) and this slice's part of dL/dG
+  // per token
+  float G[CH], gam[CH], fn[CH], sg[CH];
 };
 
 template <typename E>
@@ -151,11 +152,22 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // Sums over the 16 lanes of a row group (lanes 16 g .. 16 g + 15) and over
-// the four row groups (lanes with the same l % 16).
+// the four row groups (lanes with the same l % 16).  The row sum moves data
+// by DPP (quad permutes, then the half-row and row mirrors), not through the
+// LDS crossbar; every lane of the wavefront must be active.
 __device__ __forceinline__ float row16_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+  v += dpp_move<0xB1>(v);   // quad_perm(1,0,3,2)
+  v += dpp_move<0x4E>(v);   // quad_perm(2,3,0,1)
+  v += dpp_move<0x141>(v);  // row_half_mirror: the other quad of the 8
+  v += dpp_move<0x140>(v);  // row_mirror: the other 8 of the 16
   return v;
+}
+// the sum over the wavefront, in every lane: row sums, then the four row
+// totals read back through scalar registers (every lane active)
+__device__ __forceinline__ float wave_total(float v) {
+  v = row16_sum(v);
+  auto rl = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  return (rl(0) + rl(16)) + (rl(32) + rl(48));
 }
 __device__ __forceinline__ float col4_sum(float v) {
   v += __shfl_xor(v, 16, 64);
@@ -312,6 +324,9 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
         }
         sm.G[tid] = l;
         sm.gam[tid] = expf(l);
+        // g_n / g_t from the difference of the logs: no quotient of two
+        // exponentials that may both underflow
+        sm.fn[tid] = expf(__shfl(l, CH - 1) - l);
         sm.sg[tid] = 0.f;
       }
     }
@@ -456,7 +471,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
     for (int tile = wave; tile < ND * NC; tile += NW) {
       const int db = tile / NC, cb = tile % NC;
       const f32x4 acc =
-          mm(zero4(), 0, CH, [&](int r, int k_) { return CHAN ? wf(k_, 16 * db + r) : gn / sm.gam[k_] * wf(k_, 16 * db + r); },
+          mm(zero4(), 0, CH, [&](int r, int k_) { return CHAN ? wf(k_, 16 * db + r) : sm.fn[k_] * wf(k_, 16 * db + r); },
              [&](int k_, int cc) { return sm.x[k_ * PS + 16 * cb + cc]; }, lane);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
@@ -493,7 +508,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int i = 16 * ib + 4 * lg + ii;
-        sm.y[i * PS + 16 * cb + lr] = i < n ? fmaf(CHAN ? 1.f : gn / sm.gam[i], a2[ii], a1[ii]) : 0.f;
+        sm.y[i * PS + 16 * cb + lr] = i < n ? fmaf(CHAN ? 1.f : sm.fn[i], a2[ii], a1[ii]) : 0.f;
       }
     }
     // dL/dG of the chunk end: g_n <S_in, dS_out> (per channel: row d)
@@ -510,7 +525,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
         const int d = idx / DVS, cc = idx % DVS;
         s = fmaf(sm.S[d * PS + cc], sm.dS[d * PS + cc], s);
       }
-      s = wave_sum(s);
+      s = wave_total(s);
       if (lane == 0) atomicAdd(&sm.sg[CH - 1], gn * s);
     }
     __syncthreads();
@@ -670,7 +685,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
             ce += wtw;
           }
         } else {
-          const float g = sm.gam[t], f = gn / g;
+          const float g = sm.gam[t], f = sm.fn[t];
           const float wtw = f * wv * tw;
           if (ok) {
             atomicAdd(&a.dk_out[gi], fmaf(g, kh, sk));
@@ -688,7 +703,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
       }
     }
     if constexpr (!CHAN) {
-      wend = wave_sum(wend);
+      wend = wave_total(wend);
       if (lane == 0) atomicAdd(&sm.sg[CH - 1], wend);
     }
     __syncthreads();

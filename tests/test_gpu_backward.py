@@ -107,6 +107,18 @@ def test_chunk_bwd_kdn_information_scaling_and_strong_decay():
     _compare(wl, got, ref, _names("kdn"))
 
 
+@pytest.mark.parametrize("gain,keys,io,dk", [("kla", "scaled", "bf16", 128), ("pgdn", "unit", "bf16", 64),
+                                          ("kla", "scaled", "f32", 64)])
+def test_chunk_bwd_strong_scalar_decay(gain, keys, io, dk):
+    """Scalar decay alpha = sigmoid(N(-3, 1)): exp(G) underflows to zero within
+    a chunk, so every decay ratio must come from a difference of the logs (a
+    quotient of two underflowed exponentials is 0/0)."""
+    wl = W.Workload(f"bwd_{gain}_strong_scalar_{io}", gain, "scalar", io, 1, 2, 150, dk, dk, keys=keys,
+                    alpha_mean=-3.0, mu_spread=0.5, seed=880 + dk)
+    got, ref = _run(wl, wl.seed + 1)
+    _compare(wl, got, ref, _names(gain))
+
+
 # Whole chunks (T a multiple of 64, at least two): the gain scans run chunk
 # by chunk in parallel, and so does the gain backward of the gains without a
 # statistic.
