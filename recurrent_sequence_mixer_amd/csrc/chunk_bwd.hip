@@ -43,9 +43,10 @@
 // dk, dw, dG) are sums over value columns and are accumulated over the
 // slices with fp32 atomics.  A forward sweep first stores the state entering
 // every chunk and the residuals E; the reverse sweep then walks the chunks
-// from the last.  All arithmetic is fp32 (the operands k, q, w staged in the
-// io dtype, w rounded to it), one product element per thread and step from
-// LDS.
+// from the last.  Operands are staged in LDS (k, q, w in the io dtype, w
+// rounded to it).  With fp32 io every product runs on fp32 matrix
+// instructions; with bf16 io on bf16 ones, each fp32 operand as a pair of
+// bf16 (hi, lo) so that the products keep nearly fp32 accuracy (mm_bf).
 //
 // gain_bwd_kernel (the gains with a statistic): one workgroup per (batch,
 // head), one thread per key channel, walking the tokens backwards: the write
@@ -223,6 +224,42 @@ __device__ __forceinline__ f32x4 mm(f32x4 acc, int k0, int k1, FA fa, FB fb, int
   return acc;
 }
 
+// Four fp32 values as bf16 pairs: hi4 keeps the upper half of each value
+// (truncation), lo4 = bf16(v - hi) (v - hi is exact in fp32); hi + lo is
+// within 2^-16 of |v|.  For values that are bf16 numbers lo is zero.
+__device__ __forceinline__ s16x4 hi4(const float (&v)[4]) {
+  return __builtin_bit_cast(
+      s16x4, u32x2{__builtin_amdgcn_perm(__float_as_uint(v[1]), __float_as_uint(v[0]), 0x07060302u),
+                   __builtin_amdgcn_perm(__float_as_uint(v[3]), __float_as_uint(v[2]), 0x07060302u)});
+}
+__device__ __forceinline__ s16x4 lo4(const float (&v)[4]) {
+  auto r = [&](int j) { return v[j] - __uint_as_float(__float_as_uint(v[j]) & 0xffff0000u); };
+  return __builtin_bit_cast(s16x4, u32x2{pack_bf2(r(0), r(1)), pack_bf2(r(2), r(3))});
+}
+// mm on v_mfma_f32_16x16x16_bf16 with the fp32 operands as bf16 pairs:
+// lo A hi B + hi A lo B + hi A hi B (the lo lo term, below 2^-32 of the
+// product, is dropped).  AX / BX: the operand's values are bf16 numbers
+// (k, q, w and dO with bf16 io), so its lo term is zero and skipped.  k0 and
+// k1 multiples of 16; lane l supplies k = k0 + 16 s + 4 (l / 16) .. +3.
+template <bool AX, bool BX, typename FA, typename FB>
+__device__ __forceinline__ f32x4 mm_bf(f32x4 acc, int k0, int k1, FA fa, FB fb, int lane) {
+  const int r = lane & 15, kq = lane >> 4;
+#pragma unroll 1
+  for (int k = k0; k < k1; k += 16) {
+    float av[4], bv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      av[j] = fa(r, k + 4 * kq + j);
+      bv[j] = fb(k + 4 * kq + j, r);
+    }
+    const s16x4 ah = hi4(av), bh = hi4(bv);
+    if constexpr (!AX) acc = mfma16(lo4(av), bh, acc);
+    if constexpr (!BX) acc = mfma16(ah, lo4(bv), acc);
+    acc = mfma16(ah, bh, acc);
+  }
+  return acc;
+}
+
 template <typename E, int DK, bool CHAN, int DVS_>
 __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
   using Sm = Smem<E, DK, CHAN, DVS_>;
@@ -245,6 +282,16 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
   auto kf = [&](int t, int d) { return Elem<E>::get(sm.k[t * PK + d]); };
   auto qf = [&](int t, int d) { return Elem<E>::get(sm.q[t * PK + d]); };
   auto wf = [&](int t, int d) { return Elem<E>::get(sm.w[t * PK + d]); };
+  // A B over k0 .. k1: bf16 io on bf16 instructions with split fp32 operands
+  // (AX / BX as for mm_bf), fp32 io on fp32 instructions
+  auto mmx = [&](auto ax, auto bx, f32x4 acc, int k0, int k1, auto fa, auto fb) __attribute__((always_inline)) {
+    if constexpr (sizeof(E) == 2)
+      return mm_bf<decltype(ax)::value, decltype(bx)::value>(acc, k0, k1, fa, fb, lane);
+    else
+      return mm(acc, k0, k1, fa, fb, lane);
+  };
+  constexpr std::true_type EXACT{};
+  constexpr std::false_type SPLIT{};
 
   // chunk c into LDS: k, w, the decay, x = v (forward); reverse also q,
   // x = dO, the residuals e and the state entering the chunk.  Rows past the
@@ -415,8 +462,8 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
   auto solve_lower = [&](float* X) {
     for (int cb = wave; cb < NC; cb += NW)
       for (int b = 0; b < 4; ++b) {
-        const f32x4 acc = mm(zero4(), 0, 16 * b, [&](int r, int k_) { return sm.lm[(16 * b + r) * PC + k_]; },
-                             [&](int k_, int c) { return X[k_ * PS + 16 * cb + c]; }, lane);
+        const f32x4 acc = mmx(SPLIT, SPLIT, zero4(), 0, 16 * b, [&](int r, int k_) { return sm.lm[(16 * b + r) * PC + k_]; },
+                              [&](int k_, int c) { return X[k_ * PS + 16 * cb + c]; });
         apply_block(X, b, cb, acc, false);
       }
   };
@@ -424,8 +471,8 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
   auto solve_upper = [&](float* X) {
     for (int cb = wave; cb < NC; cb += NW)
       for (int b = 3; b >= 0; --b) {
-        const f32x4 acc = mm(zero4(), 16 * (b + 1), CH, [&](int r, int k_) { return sm.lm[k_ * PC + 16 * b + r]; },
-                             [&](int k_, int c) { return X[k_ * PS + 16 * cb + c]; }, lane);
+        const f32x4 acc = mmx(SPLIT, SPLIT, zero4(), 16 * (b + 1), CH, [&](int r, int k_) { return sm.lm[k_ * PC + 16 * b + r]; },
+                              [&](int k_, int c) { return X[k_ * PS + 16 * cb + c]; });
         apply_block(X, b, cb, acc, true);
       }
   };
@@ -449,8 +496,8 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
     for (int tile = wave; tile < 4 * NC; tile += NW) {
       const int tb_ = tile / NC, cb = tile % NC;
       const f32x4 acc =
-          mm(zero4(), 0, DK, [&](int r, int k_) { return CHAN ? kf(16 * tb_ + r, k_) * sm.gref[k_] : kf(16 * tb_ + r, k_); },
-             [&](int k_, int cc) { return sm.S[k_ * PS + 16 * cb + cc]; }, lane);
+          mmx(EXACT, SPLIT, zero4(), 0, DK, [&](int r, int k_) { return kf(16 * tb_ + r, k_); },
+              [&](int k_, int cc) { return CHAN ? sm.gref[k_] * sm.S[k_ * PS + 16 * cb + cc] : sm.S[k_ * PS + 16 * cb + cc]; });
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int t = 16 * tb_ + 4 * lg + ii;
@@ -471,8 +518,8 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
     for (int tile = wave; tile < ND * NC; tile += NW) {
       const int db = tile / NC, cb = tile % NC;
       const f32x4 acc =
-          mm(zero4(), 0, CH, [&](int r, int k_) { return CHAN ? wf(k_, 16 * db + r) : sm.fn[k_] * wf(k_, 16 * db + r); },
-             [&](int k_, int cc) { return sm.x[k_ * PS + 16 * cb + cc]; }, lane);
+          mmx(EXACT, SPLIT, zero4(), 0, CH, [&](int r, int k_) { return wf(k_, 16 * db + r); },
+              [&](int k_, int cc) { return CHAN ? sm.x[k_ * PS + 16 * cb + cc] : sm.fn[k_] * sm.x[k_ * PS + 16 * cb + cc]; });
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int d = 16 * db + 4 * lg + ii;
@@ -500,11 +547,11 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
     // dE = M^T dO + W~ dS_out
     for (int tile = wave; tile < 4 * NC; tile += NW) {
       const int ib = tile / NC, cb = tile % NC;
-      const f32x4 a1 = mm(zero4(), 16 * ib, CH, [&](int r, int k_) { return sm.mm[k_ * PC + 16 * ib + r]; },
-                          [&](int k_, int cc) { return sm.x[k_ * PS + 16 * cb + cc]; }, lane);
+      const f32x4 a1 = mmx(SPLIT, EXACT, zero4(), 16 * ib, CH, [&](int r, int k_) { return sm.mm[k_ * PC + 16 * ib + r]; },
+                           [&](int k_, int cc) { return sm.x[k_ * PS + 16 * cb + cc]; });
       const f32x4 a2 =
-          mm(zero4(), 0, DK, [&](int r, int k_) { return CHAN ? wf(16 * ib + r, k_) * sm.gnr[k_] : wf(16 * ib + r, k_); },
-             [&](int k_, int cc) { return sm.dS[k_ * PS + 16 * cb + cc]; }, lane);
+          mmx(EXACT, SPLIT, zero4(), 0, DK, [&](int r, int k_) { return wf(16 * ib + r, k_); },
+              [&](int k_, int cc) { return CHAN ? sm.gnr[k_] * sm.dS[k_ * PS + 16 * cb + cc] : sm.dS[k_ * PS + 16 * cb + cc]; });
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int i = 16 * ib + 4 * lg + ii;
@@ -714,14 +761,11 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
     // dS_in = g_n dS_out + sum_t g_t (q_t dO_t^T - k_t dR_t^T)
     for (int tile = wave; tile < ND * NC; tile += NW) {
       const int db = tile / NC, cb = tile % NC;
-      f32x4 acc = zero4(), acc2 = zero4();
-#pragma unroll 4
-      for (int k0 = 0; k0 < CH; k0 += 4) {
-        const int k_ = k0 + lg;
-        const float gk = CHAN ? 1.f : sm.gam[k_];
-        acc = mfma4(gk * qf(k_, 16 * db + lr), sm.x[k_ * PS + 16 * cb + lr], acc);
-        acc2 = mfma4(gk * kf(k_, 16 * db + lr), sm.y[k_ * PS + 16 * cb + lr], acc2);
-      }
+      auto gk = [&](int k_) { return CHAN ? 1.f : sm.gam[k_]; };
+      f32x4 acc = mmx(EXACT, SPLIT, zero4(), 0, CH, [&](int r, int k_) { return qf(k_, 16 * db + r); },
+                      [&](int k_, int cc) { return gk(k_) * sm.x[k_ * PS + 16 * cb + cc]; });
+      const f32x4 acc2 = mmx(EXACT, SPLIT, zero4(), 0, CH, [&](int r, int k_) { return kf(k_, 16 * db + r); },
+                             [&](int k_, int cc) { return gk(k_) * sm.y[k_ * PS + 16 * cb + cc]; });
       acc -= acc2;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
