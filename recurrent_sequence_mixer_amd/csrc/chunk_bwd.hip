@@ -602,12 +602,30 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
       const int tr = tile >> 2, tc = tile & 3;
       if (tr < tc) continue;
       f32x4 al = zero4(), am = zero4();
+      if constexpr (sizeof(E) == 2) {
+        // as mm_bf, E split once for both products (dO is a bf16 number)
 #pragma unroll
-      for (int k0 = 0; k0 < DVS; k0 += 4) {
-        const int k_ = k0 + lg;
-        const float ev = sm.e[(16 * tc + lr) * PS + k_];
-        al = mfma4(sm.y[(16 * tr + lr) * PS + k_], ev, al);
-        am = mfma4(sm.x[(16 * tr + lr) * PS + k_], ev, am);
+        for (int k0 = 0; k0 < DVS; k0 += 16) {
+          const int k_ = k0 + 4 * lg;
+          float ev[4], yv[4], xv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            ev[j] = sm.e[(16 * tc + lr) * PS + k_ + j];
+            yv[j] = sm.y[(16 * tr + lr) * PS + k_ + j];
+            xv[j] = sm.x[(16 * tr + lr) * PS + k_ + j];
+          }
+          const s16x4 eh = hi4(ev), el = lo4(ev), yh = hi4(yv), xh = hi4(xv);
+          al = mfma16(yh, eh, mfma16(yh, el, mfma16(lo4(yv), eh, al)));
+          am = mfma16(xh, eh, mfma16(xh, el, am));
+        }
+      } else {
+#pragma unroll
+        for (int k0 = 0; k0 < DVS; k0 += 4) {
+          const int k_ = k0 + lg;
+          const float ev = sm.e[(16 * tc + lr) * PS + k_];
+          al = mfma4(sm.y[(16 * tr + lr) * PS + k_], ev, al);
+          am = mfma4(sm.x[(16 * tr + lr) * PS + k_], ev, am);
+        }
       }
       const int i = 16 * tc + lr;
       float col = 0.f;  // scalar decay: - (L o dL + M o dM) summed over this lane's rows
@@ -653,13 +671,34 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
       // the tile's products, independent chains interleaved (operands as
       // for mm: A row lr, B column lr, k = 4 s + lg)
       f32x4 akh = zero4(), aqh = zero4(), atw = zero4();
+      if constexpr (sizeof(E) == 2) {
+        // as mm_bf, S split once for both of its products (dO is a bf16 number)
 #pragma unroll
-      for (int k0 = 0; k0 < DVS; k0 += 4) {
-        const int k_ = k0 + lg;
-        const float sv = sm.S[(16 * db + lr) * PS + k_];
-        akh = mfma4(sm.y[(16 * tb_ + lr) * PS + k_], sv, akh);
-        aqh = mfma4(sm.x[(16 * tb_ + lr) * PS + k_], sv, aqh);
-        atw = mfma4(sm.e[(16 * tb_ + lr) * PS + k_], sm.dS[(16 * db + lr) * PS + k_], atw);
+        for (int k0 = 0; k0 < DVS; k0 += 16) {
+          const int k_ = k0 + 4 * lg;
+          float sv[4], dsv[4], yv[4], xv[4], ev[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            sv[j] = sm.S[(16 * db + lr) * PS + k_ + j];
+            dsv[j] = sm.dS[(16 * db + lr) * PS + k_ + j];
+            yv[j] = sm.y[(16 * tb_ + lr) * PS + k_ + j];
+            xv[j] = sm.x[(16 * tb_ + lr) * PS + k_ + j];
+            ev[j] = sm.e[(16 * tb_ + lr) * PS + k_ + j];
+          }
+          const s16x4 sh = hi4(sv), sl = lo4(sv), dh = hi4(dsv), yh = hi4(yv), xh = hi4(xv), eh = hi4(ev);
+          akh = mfma16(yh, sh, mfma16(yh, sl, mfma16(lo4(yv), sh, akh)));
+          aqh = mfma16(xh, sh, mfma16(xh, sl, aqh));
+          atw = mfma16(eh, dh, mfma16(eh, lo4(dsv), mfma16(lo4(ev), dh, atw)));
+        }
+      } else {
+#pragma unroll
+        for (int k0 = 0; k0 < DVS; k0 += 4) {
+          const int k_ = k0 + lg;
+          const float sv = sm.S[(16 * db + lr) * PS + k_];
+          akh = mfma4(sm.y[(16 * tb_ + lr) * PS + k_], sv, akh);
+          aqh = mfma4(sm.x[(16 * tb_ + lr) * PS + k_], sv, aqh);
+          atw = mfma4(sm.e[(16 * tb_ + lr) * PS + k_], sm.dS[(16 * db + lr) * PS + k_], atw);
+        }
       }
       f32x4 ask = zero4(), asq = zero4(), asw = zero4(), asw2 = zero4();
       if constexpr (sizeof(E) == 2) {
