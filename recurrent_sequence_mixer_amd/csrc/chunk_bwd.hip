@@ -307,7 +307,12 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
     const bool kok = kt < n, xok = xt < n;
     float kv[KV], qv[KV], wv[KV], xv[XV], ev[XV], sv[SV], av[CHAN ? KV : 1];
     load_vec<E, KV>(a.k, krow, kok, kv);
-    load_vec<float, KV>(a.w, krow, kok, wv);
+    // bf16 write vectors with bf16 io and scalar decay (already rounded as
+    // they are stored below), fp32 otherwise
+    if constexpr (sizeof(E) == 2 && !CHAN)
+      load_vec<E, KV>(a.w, krow, kok, wv);
+    else
+      load_vec<float, KV>(a.w, krow, kok, wv);
     load_vec<E, XV>(rev ? a.dO : a.v, xrow, xok, xv);
     if (rev) {
       load_vec<E, KV>(a.q, krow, kok, qv);

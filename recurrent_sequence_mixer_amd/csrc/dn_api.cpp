@@ -718,10 +718,11 @@ DN_EXPORT int dn_decode_step(const dn_desc* d, const void* q, const void* k, con
 }
 
 // The gain scans of dn_gain_prep on validated arguments; ws holds at least
-// prep_layout(d).total bytes when that is not zero.
+// prep_layout(d).total bytes when that is not zero.  w_bf16: w_out receives
+// the write vectors in bf16 (RNE) instead of fp32.
 static int run_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, const float* aux0,
                          float* w_out, float* g_out, float* aux_chunk, float* aux_final, void* ws,
-                         hipStream_t s) {
+                         hipStream_t s, bool w_bf16 = false) {
   const bool has_aux = has_aux_state(d);
   const size_t nch = (static_cast<size_t>(d->T) + d->C - 1) / d->C;
   const PrepLayout lay = prep_layout(d);
@@ -734,6 +735,7 @@ static int run_gain_prep(const dn_desc* d, const void* k, const dn_gates* g, con
   a.g = gate_args(d, g);
   a.aux0 = has_aux ? aux0 : nullptr;
   a.w_out = w_out;
+  a.w_bf16 = w_bf16 ? reinterpret_cast<uint16_t*>(w_out) : nullptr;
   a.g_out = g_out;
   a.aux_chunk = has_aux ? aux_chunk : nullptr;
   a.aux_final = has_aux ? aux_final : nullptr;
@@ -1041,9 +1043,11 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
     return DN_ERR_HIP;
   const dn::GateArgs ga = gate_args(d, g);
   // the write vectors (and the statistic entering every chunk), chunks in
-  // parallel where T is whole chunks
+  // parallel where T is whole chunks; bf16 with bf16 io and scalar decay (the
+  // state kernel rounds them to bf16 as it stages them; with per-channel
+  // decay it first scales them by the decay, so they stay fp32)
   if ((st = run_gain_prep(d, k, g, has_aux ? aux0 : nullptr, w_ws, nullptr, aux_chunk, nullptr,
-                          wb + lay.prep, s)) != DN_OK)
+                          wb + lay.prep, s, d->io == DN_BF16 && !chan)) != DN_OK)
     return st;
   // the memory recurrence backwards, chunk by chunk
   dn::BwdArgs b;

@@ -93,7 +93,10 @@ __global__ __launch_bounds__(DK) void gain_prep_kernel(GainPrepArgs a) {
         wv = pre / (a.g.r[ti] + tot);
       }
     }
-    a.w_out[ti * DK + d] = wv;
+    if (a.w_bf16)
+      a.w_bf16[ti * DK + d] = f2bf(wv);
+    else
+      a.w_out[ti * DK + d] = wv;
   }
   if (a.aux_final && AUX && (!ISO || d == 0)) a.aux_final[ISO ? bh : bh * DK + d] = st;
 }
@@ -163,9 +166,17 @@ __global__ __launch_bounds__(256) void gain_prep_tok_kernel(GainPrepArgs a) {
     } else {
       load_row<IO, DQ>(a.g.w, ti * DK + d0, w);
     }
-    f32x4* wo = reinterpret_cast<f32x4*>(a.w_out + ti * DK + d0);
+    if (a.w_bf16) {
+      u32x4* wo = reinterpret_cast<u32x4*>(a.w_bf16 + ti * DK + d0);
 #pragma unroll
-    for (int i = 0; i < DQ / 4; ++i) wo[i] = f32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+      for (int i = 0; i < DQ / 8; ++i)
+        wo[i] = u32x4{pack_bf2(w[8 * i], w[8 * i + 1]), pack_bf2(w[8 * i + 2], w[8 * i + 3]),
+                      pack_bf2(w[8 * i + 4], w[8 * i + 5]), pack_bf2(w[8 * i + 6], w[8 * i + 7])};
+    } else {
+      f32x4* wo = reinterpret_cast<f32x4*>(a.w_out + ti * DK + d0);
+#pragma unroll
+      for (int i = 0; i < DQ / 4; ++i) wo[i] = f32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+    }
   }
   // (the four lanes of a token share `ok`, so its lane sums stay inside it)
   if (!a.g_out) return;  // uniform

@@ -121,13 +121,15 @@ struct GainPrepArgs {
   GateArgs g;
   const float* aux0;  // nullable
   float* w_out;
+  uint16_t* w_bf16 = nullptr;  // nullable: w written here in bf16 (RNE) instead of w_out
   float* g_out;      // nullable
   float* aux_chunk;  // nullable
   float* aux_final;  // nullable
 };
 
 // Chunked backward (chunk_bwd.hip).  Inputs as ChunkArgs, the write vectors
-// w [B, H, T, dk] fp32 from the gain scan, and the cotangents dO [B, H, T, dv]
+// w [B, H, T, dk] from the gain scan (bf16 with bf16 io and scalar decay,
+// otherwise fp32), and the cotangents dO [B, H, T, dv]
 // (io dtype), dS_T [B, H, dk, dv] and daux_T (nullable).  Gradients are fp32:
 // dq, dk, dw_acc [B, H, T, dk] and dG ([B, H, T], per channel [B, H, T, dk])
 // are accumulated over value slices and must start at zero; dv [B, H, T, dv]
@@ -137,7 +139,7 @@ struct BwdArgs {
   int B, H, T, dk, dv;
   const void *q, *k, *v;
   GateArgs g;
-  const float* w;  // [B, H, T, dk] fp32
+  const void* w;  // [B, H, T, dk]: bf16 with bf16 io and scalar decay, else fp32
   const float* S0;
   const void* dO;
   const float* dS_T;
