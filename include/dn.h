@@ -340,7 +340,9 @@ typedef struct dn_grads {
  * from them the gradients of k, q, w and the decay (per key channel for
  * channel decay, the decay then applied inside the products); the chunks are
  * walked from the last, after a forward sweep that keeps the state entering
- * each chunk.  The write gain is then differentiated token by token
+ * each chunk and the residuals E (with bf16 io and scalar decay, for KLA, GDN,
+ * PGDN and explicit w with dv a multiple of 64, the chunked forward's kernel
+ * runs that sweep without output).  The write gain is then differentiated token by token
  * backwards (KLA, GDN: Kaczmarz Linear Attention §2.1; PGDN: Preconditioned
  * DeltaNet §2.4, Eq. 9, through the statistic A_t, its centre mu and its
  * gates; KDN: Kalman Delta Networks §2.4, Eqs. 23-30 and §2.5, through the
@@ -348,16 +350,20 @@ typedef struct dn_grads {
  * Appendix D run backwards).
  *   Every gain and both decays; io bf16 (dk 64 or 128) or fp32 (dk 64);
  *   other shapes return DN_ERR_UNSUPPORTED.  Results equal the gradients of
- *   the token recurrence up to rounding (fp32 arithmetic; k, q and w enter
+ *   the token recurrence up to rounding (fp32 accumulation; k, q and w enter
  *   the products in the io dtype, with channel decay scaled by their decay
- *   relative to the chunk's token 31 first).  Channel decay has the range of
+ *   relative to the chunk's token 31 first; with bf16 io the fp32 operands
+ *   enter as pairs of bf16, within 2^-16, and where the chunked forward's
+ *   kernel writes the checkpoints they carry its rounding, as its o and
+ *   S_final do).  Channel decay has the range of
  *   the chunked forward (RANGE OF CHANNEL DECAY): beyond it the gradients
  *   of the head are NaN.
  *   q, k, v, gates, S0 (nullable: zeros), aux0 (nullable: ones): as for
  *   dn_chunk_fwd.  dO [B, H, T, dv] io dtype; dS_T [B, H, dk, dv] and
  *   daux_T (PGDN / KDN [B, H, dk], KDN_ISO [B, H]) fp32, nullable (zero).
  *   ws: device workspace of at least dn_chunk_bwd_workspace(desc) bytes
- *   (fp32: the write vectors [B, H, T, dk], the state entering every chunk
+ *   (the write vectors [B, H, T, dk], fp32 or, with bf16 io and scalar
+ *   decay, bf16; fp32: the state entering every chunk
  *   [B, H, ceil(T/C), dk, dv], the residuals [B, H, T, dv], the write vectors'
  *   gradient [B, H, T, dk], the decay's per token ([B, H, T], channel decay
  *   [B, H, T, dk]) and for the gains with a statistic the statistic entering

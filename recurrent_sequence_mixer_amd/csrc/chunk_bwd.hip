@@ -42,7 +42,8 @@
 // workgroup carries its slice of dS; the per-token key-side gradients (dq,
 // dk, dw, dG) are sums over value columns and are accumulated over the
 // slices with fp32 atomics.  A forward sweep first stores the state entering
-// every chunk and the residuals E; the reverse sweep then walks the chunks
+// every chunk and the residuals E (or, with BwdArgs::ck_given, the chunked
+// forward's kernel has stored them); the reverse sweep then walks the chunks
 // from the last.  Operands are staged in LDS (k, q, w in the io dtype, w
 // rounded to it).  With fp32 io every product runs on fp32 matrix
 // instructions; with bf16 io on bf16 ones, each fp32 operand as a pair of
@@ -483,53 +484,56 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
   };
 
   // ---------------- forward sweep: S_in of every chunk and E
-  for (int idx = tid; idx < DK * DVS; idx += NT) {
-    const int d = idx / DVS, cc = idx % DVS;
-    sm.S[d * PS + cc] = a.S0 ? a.S0[(bh * DK + d) * dv + col0 + cc] : 0.f;
-  }
-  for (int c = 0; c < nch; ++c) {
-    const int t0 = c * CH, n = min(CH, T - t0);
-    __syncthreads();  // the previous chunk's readers of k, w, x, S are done
-    stage(c, false);
-    __syncthreads();
-    // S_in to the checkpoint; L; R = V - g K S_in
+  // (skipped when the forward chunk kernel wrote the checkpoints)
+  if (!a.ck_given) {
     for (int idx = tid; idx < DK * DVS; idx += NT) {
       const int d = idx / DVS, cc = idx % DVS;
-      a.S_ck[((bh * nch + c) * DK + d) * dv + col0 + cc] = sm.S[d * PS + cc];
+      sm.S[d * PS + cc] = a.S0 ? a.S0[(bh * DK + d) * dv + col0 + cc] : 0.f;
     }
-    form_lm(n, false);
-    for (int tile = wave; tile < 4 * NC; tile += NW) {
-      const int tb_ = tile / NC, cb = tile % NC;
-      const f32x4 acc =
-          mmx(EXACT, SPLIT, zero4(), 0, DK, [&](int r, int k_) { return kf(16 * tb_ + r, k_); },
-              [&](int k_, int cc) { return CHAN ? sm.gref[k_] * sm.S[k_ * PS + 16 * cb + cc] : sm.S[k_ * PS + 16 * cb + cc]; });
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int t = 16 * tb_ + 4 * lg + ii;
-        sm.x[t * PS + 16 * cb + lr] -= CHAN ? acc[ii] : sm.gam[t] * acc[ii];
+    for (int c = 0; c < nch; ++c) {
+      const int t0 = c * CH, n = min(CH, T - t0);
+      __syncthreads();  // the previous chunk's readers of k, w, x, S are done
+      stage(c, false);
+      __syncthreads();
+      // S_in to the checkpoint; L; R = V - g K S_in
+      for (int idx = tid; idx < DK * DVS; idx += NT) {
+        const int d = idx / DVS, cc = idx % DVS;
+        a.S_ck[((bh * nch + c) * DK + d) * dv + col0 + cc] = sm.S[d * PS + cc];
       }
-    }
-    __syncthreads();
-    invert_blocks();
-    __syncthreads();
-    solve_lower(sm.x);  // E
-    __syncthreads();
-    for (int idx = tid; idx < CH * DVS; idx += NT) {
-      const int t = idx / DVS, cc = idx % DVS;
-      if (t < n) a.E[(tok0 + t0 + t) * dv + col0 + cc] = sm.x[t * PS + cc];
-    }
-    // S_out = g_n S_in + sum_t (g_n / g_t) w_t E_t^T
-    const float gn = CHAN ? 1.f : sm.gam[CH - 1];
-    for (int tile = wave; tile < ND * NC; tile += NW) {
-      const int db = tile / NC, cb = tile % NC;
-      const f32x4 acc =
-          mmx(EXACT, SPLIT, zero4(), 0, CH, [&](int r, int k_) { return wf(k_, 16 * db + r); },
-              [&](int k_, int cc) { return CHAN ? sm.x[k_ * PS + 16 * cb + cc] : sm.fn[k_] * sm.x[k_ * PS + 16 * cb + cc]; });
+      form_lm(n, false);
+      for (int tile = wave; tile < 4 * NC; tile += NW) {
+        const int tb_ = tile / NC, cb = tile % NC;
+        const f32x4 acc =
+            mmx(EXACT, SPLIT, zero4(), 0, DK, [&](int r, int k_) { return kf(16 * tb_ + r, k_); },
+                [&](int k_, int cc) { return CHAN ? sm.gref[k_] * sm.S[k_ * PS + 16 * cb + cc] : sm.S[k_ * PS + 16 * cb + cc]; });
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int d = 16 * db + 4 * lg + ii;
-        float& s = sm.S[d * PS + 16 * cb + lr];
-        s = CHAN ? sm.gnr[d] * fmaf(sm.gref[d], s, acc[ii]) : fmaf(gn, s, acc[ii]);
+        for (int ii = 0; ii < 4; ++ii) {
+          const int t = 16 * tb_ + 4 * lg + ii;
+          sm.x[t * PS + 16 * cb + lr] -= CHAN ? acc[ii] : sm.gam[t] * acc[ii];
+        }
+      }
+      __syncthreads();
+      invert_blocks();
+      __syncthreads();
+      solve_lower(sm.x);  // E
+      __syncthreads();
+      for (int idx = tid; idx < CH * DVS; idx += NT) {
+        const int t = idx / DVS, cc = idx % DVS;
+        if (t < n) a.E[(tok0 + t0 + t) * dv + col0 + cc] = sm.x[t * PS + cc];
+      }
+      // S_out = g_n S_in + sum_t (g_n / g_t) w_t E_t^T
+      const float gn = CHAN ? 1.f : sm.gam[CH - 1];
+      for (int tile = wave; tile < ND * NC; tile += NW) {
+        const int db = tile / NC, cb = tile % NC;
+        const f32x4 acc =
+            mmx(EXACT, SPLIT, zero4(), 0, CH, [&](int r, int k_) { return wf(k_, 16 * db + r); },
+                [&](int k_, int cc) { return CHAN ? sm.x[k_ * PS + 16 * cb + cc] : sm.fn[k_] * sm.x[k_ * PS + 16 * cb + cc]; });
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int d = 16 * db + 4 * lg + ii;
+          float& s = sm.S[d * PS + 16 * cb + lr];
+          s = CHAN ? sm.gnr[d] * fmaf(sm.gref[d], s, acc[ii]) : fmaf(gn, s, acc[ii]);
+        }
       }
     }
   }

@@ -1186,6 +1186,17 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           const f32x4 u = mfma16(tv[b], pack16(acc), zero4());
           Ub[b] = pack16(u);
           Fb[b] = pack16(u * fv[b]);
+          if constexpr (!OUT && !CD) {
+            // the backward's residuals: E rows 16 b + 4 g4 + i of value column
+            // col0 + 16 ct + c16 (rows past the end fall outside the resource)
+            if (a.E_ck) {
+              const auto re = rsrc(a.E_ck + v_base + static_cast<long>(t0) * a.dv, 4 * n * a.dv);
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(u[i]), re,
+                                                      4 * ((16 * b + 4 * g4 + i) * a.dv + col0 + 16 * ct + c16), 0, 0);
+            }
+          }
         }
         U0 = cat8(Ub[0], Ub[1]);
         U1 = cat8(Ub[2], Ub[3]);
@@ -1407,6 +1418,16 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
 
         // ================= P1 =================
         if constexpr (CONS) {
+          if constexpr (!OUT) {
+            // the backward's checkpoint: the state entering chunk c
+            if (a.S_ck) {
+              float* base = a.S_ck + ((static_cast<long>(bh) * nchunks + c) * DK + 8 * g4) * a.dv + col0 + 16 * ct + c16;
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) base[KL::sigma_channel(dt, 0, i) * a.dv] = S[dt][i];
+            }
+          }
           cons_p1(c);
         } else if constexpr (LOAD) {
           // k, q (PGDN: and the gates) of chunk c + 1 into LDS (REG: q goes in

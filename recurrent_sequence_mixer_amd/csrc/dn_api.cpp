@@ -1072,6 +1072,30 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
   b.dw_acc = dw_acc;
   b.dG = dG;
   b.dS0 = gr->dS0;
+  // bf16 io, scalar decay, gains the forward chunk kernel runs with a write
+  // vector per token (KLA, GDN, PGDN, explicit w), dv in 64-column slices: that
+  // kernel writes the checkpoints (the state entering every chunk and the
+  // residuals E) in a pass without output, and the state kernel runs only its
+  // reverse sweep
+  const bool fwd_ck = d->io == DN_BF16 && !chan && !kd && d->dv % 64 == 0;
+  if (fwd_ck) {
+    dn::ChunkArgs ca{};
+    ca.B = d->B;
+    ca.H = d->H;
+    ca.T = d->T;
+    ca.dk = d->dk;
+    ca.dv = d->dv;
+    ca.q = q;
+    ca.k = k;
+    ca.v = v;
+    ca.g = ga;
+    ca.S0 = S0;
+    ca.aux0 = pg ? aux0 : nullptr;
+    ca.S_ck = b.S_ck;
+    ca.E_ck = b.E;
+    if (dn::launch_chunk_fwd_bf16_scalar(ca, d->gain, s) != hipSuccess) return DN_ERR_HIP;
+    b.ck_given = 1;
+  }
   if (dn::launch_chunk_bwd_state(b, d->io == DN_BF16, chan, s) != hipSuccess) return DN_ERR_HIP;
   // the write gains and the decay backwards
   dn::GainBwdArgs gb;

@@ -56,6 +56,11 @@ struct ChunkArgs {
   // the range of the chunk form in some chunk (its S_final and aux_final are
   // then not written, its outputs are NaN), else 0
   int* oor = nullptr;
+  // the backward's checkpoints, nullable (bf16 io, scalar decay, no output
+  // o): the state entering every chunk S_ck [B, H, nch, dk, dv] and the
+  // residuals E [B, H, T, dv] of the chunk form, fp32
+  float* S_ck = nullptr;
+  float* E_ck = nullptr;
 };
 
 // Tokenwise forward of the heads flagged by the chunked kernels, and of
@@ -137,6 +142,9 @@ struct GainPrepArgs {
 // S_ck [B, H, nch, dk, dv] and the residuals E [B, H, T, dv].
 struct BwdArgs {
   int B, H, T, dk, dv;
+  // S_ck and E already hold the forward's checkpoints (written by the
+  // forward chunk kernel): the state kernel runs only its reverse sweep
+  int ck_given = 0;
   const void *q, *k, *v;
   GateArgs g;
   const void* w;  // [B, H, T, dk]: bf16 with bf16 io and scalar decay, else fp32
