@@ -1098,6 +1098,23 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
     f32x4 R[4], OQ[4];
     float gn = 1.f;         // g_n of chunk c (gam is rewritten in P2 / P3)
     bf16x8 U0, U1, F0, F1;  // U and diag(f) U, k-blocks 0 and 1 (tiles 0,1 and 2,3)
+    // the backward's checkpoints (no-output instances with S_ck / E_ck): one
+    // byte offset per lane, the row or key channel in the resource base or the
+    // scalar offset, so that no address register is rewritten between stores
+    const int ek_voff = 4 * (4 * g4 * a.dv + col0 + 16 * ct + c16);  // E: row 4 g4 of the resource
+    const int ck_voff = 4 * (8 * g4 * a.dv + col0 + 16 * ct + c16);  // S_ck: channel 8 g4 + sigma(dt, 0, i)
+    // S, the state entering chunk cidx, to S_ck
+    auto store_ck = [&](int cidx) __attribute__((always_inline)) {
+      if constexpr (CONS && !OUT && !CD) {
+        const auto rs = rsrc(a.S_ck + (static_cast<long>(bh) * nchunks + cidx) * DK * a.dv, 4 * DK * a.dv);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[dt][i]), rs, ck_voff,
+                                                  4 * KL::sigma_channel(dt, 0, i) * a.dv, 0);
+      }
+    };
     // P1: K S -> R = V - g K S, and (Q S)^T.  KDN: S is scaled per key channel
     // by 2^(G_r) first (the operands carry the decay relative to token 31)
     auto cons_p1 = [&](int c) __attribute__((always_inline)) {
@@ -1171,6 +1188,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
         // chain is read up front (in the order it is used)
         s16x4 Ub[4], Fb[4], lt[6], tv[4];
         f32x4 fv[4];
+        f32x4 Ek[!OUT && !CD ? 4 : 1];  // the residuals, kept for the checkpoint stores
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
 #pragma unroll
@@ -1186,16 +1204,21 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
           const f32x4 u = mfma16(tv[b], pack16(acc), zero4());
           Ub[b] = pack16(u);
           Fb[b] = pack16(u * fv[b]);
-          if constexpr (!OUT && !CD) {
-            // the backward's residuals: E rows 16 b + 4 g4 + i of value column
-            // col0 + 16 ct + c16 (rows past the end fall outside the resource)
-            if (a.E_ck) {
-              const auto re = rsrc(a.E_ck + v_base + static_cast<long>(t0) * a.dv, 4 * n * a.dv);
+          if constexpr (!OUT && !CD) Ek[b] = u;
+        }
+        if constexpr (!OUT && !CD) {
+          // the backward's residuals: E rows 16 b + 4 g4 + i of value column
+          // col0 + 16 ct + c16, one lane offset for all (row 16 b + i in the
+          // resource's base, rows past the end outside its range)
+          if (a.E_ck) {
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(u[i]), re,
-                                                      4 * ((16 * b + 4 * g4 + i) * a.dv + col0 + 16 * ct + c16), 0, 0);
-            }
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int row = 16 * b + i;
+                const auto re = rsrc(a.E_ck + v_base + static_cast<long>(t0 + row) * a.dv, 4 * max(0, n - row) * a.dv);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Ek[b][i]), re, ek_voff, 0, 0);
+              }
           }
         }
         U0 = cat8(Ub[0], Ub[1]);
@@ -1418,16 +1441,7 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
 
         // ================= P1 =================
         if constexpr (CONS) {
-          if constexpr (!OUT) {
-            // the backward's checkpoint: the state entering chunk c
-            if (a.S_ck) {
-              float* base = a.S_ck + ((static_cast<long>(bh) * nchunks + c) * DK + 8 * g4) * a.dv + col0 + 16 * ct + c16;
-#pragma unroll
-              for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) base[KL::sigma_channel(dt, 0, i) * a.dv] = S[dt][i];
-            }
-          }
+          if (!OUT && a.S_ck && c == 0) store_ck(0);
           cons_p1(c);
         } else if constexpr (LOAD) {
           // k, q (PGDN: and the gates) of chunk c + 1 into LDS (REG: q goes in
@@ -1489,6 +1503,9 @@ __device__ __forceinline__ void chunk_fwd_ws_body(const ChunkArgs& a) {
         // ================= P3 =================
         if constexpr (CONS) {
           cons_p3(c);
+          // the state entering chunk c + 1: the stores have the next two
+          // phases to drain before the next update rewrites S
+          if (!OUT && a.S_ck && c + 1 < nchunks) store_ck(c + 1);
         } else if constexpr (LOAD) {
           // REG: the gates and q of chunk c + 2 into LDS (their parity's last
           // readers - regains and diag_gains of chunk c, its Q S - are done);
