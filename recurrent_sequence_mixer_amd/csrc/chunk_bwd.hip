@@ -69,7 +69,9 @@ namespace bwd {
 constexpr int CH = 64;      // chunk length
 constexpr int NT = 512;     // threads of the state kernel
 constexpr int NW = NT / 64; // its wavefronts
-constexpr int PC = CH + 1;  // row pitch of [CH][CH] fp32 arrays
+// row pitch of [CH][CH] fp32 arrays: a multiple of 4, so that four consecutive
+// entries are one aligned 16-byte read, and rows four apart are 16 banks apart
+constexpr int PC = CH + 4;
 constexpr int PT = 17;      // row pitch of the 16x16 diagonal-block inverses
 constexpr int RT = 31;      // reference token of the per-channel decay factors
 
@@ -77,7 +79,7 @@ constexpr int RT = 31;      // reference token of the per-channel decay factors
 template <typename E, int DK, bool CHAN, int DVS_>
 struct Smem {
   static constexpr int DVS = DVS_;            // value columns per workgroup
-  static constexpr int PS = DVS + 1;          // row pitch of [x][DVS] fp32 arrays
+  static constexpr int PS = DVS + 4;          // row pitch of [x][DVS] fp32 arrays (as PC)
   static constexpr int PK = DK + 2;           // row pitch of the [CH][DK] operand rows
   static constexpr int PG = DK + 1;           // row pitch of the per-channel decay
   E k[CH * PK], q[CH * PK], w[CH * PK];  // channel decay: k^, q^, w^
@@ -225,6 +227,11 @@ __device__ __forceinline__ f32x4 mm(f32x4 acc, int k0, int k1, FA fa, FB fb, int
   return acc;
 }
 
+// four consecutive fp32 values from a 16-byte aligned LDS address, as one read
+__device__ __forceinline__ void ld4(float (&v)[4], const float* p) {
+  const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+  v[0] = x[0], v[1] = x[1], v[2] = x[2], v[3] = x[3];
+}
 // Four fp32 values as bf16 pairs: hi4 keeps the upper half of each value
 // (truncation), lo4 = bf16(v - hi) (v - hi is exact in fp32); hi + lo is
 // within 2^-16 of |v|.  For values that are bf16 numbers lo is zero.
@@ -265,6 +272,11 @@ template <typename E, int DK, bool CHAN, int DVS_>
 __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
   using Sm = Smem<E, DK, CHAN, DVS_>;
   constexpr int PK = Sm::PK, PS = Sm::PS, PG = Sm::PG, DVS = Sm::DVS;
+  // the fp32 arrays read as 16-byte pieces start on 16-byte boundaries
+  static_assert(offsetof(Sm, S) % 16 == 0 && offsetof(Sm, dS) % 16 == 0 && offsetof(Sm, e) % 16 == 0 &&
+                    offsetof(Sm, x) % 16 == 0 && offsetof(Sm, y) % 16 == 0 && offsetof(Sm, lm) % 16 == 0 &&
+                    offsetof(Sm, mm) % 16 == 0 && PS % 4 == 0 && PC % 4 == 0,
+                "16-byte LDS rows");
   constexpr int NC = DVS / 16;      // 16-column tiles of the value slice
   constexpr int ND = DK / 16;       // 16-row tiles of the key dimension
   constexpr int TPW = 4 * ND / NW;  // [token][key] tiles per wavefront
@@ -617,12 +629,9 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
         for (int k0 = 0; k0 < DVS; k0 += 16) {
           const int k_ = k0 + 4 * lg;
           float ev[4], yv[4], xv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            ev[j] = sm.e[(16 * tc + lr) * PS + k_ + j];
-            yv[j] = sm.y[(16 * tr + lr) * PS + k_ + j];
-            xv[j] = sm.x[(16 * tr + lr) * PS + k_ + j];
-          }
+          ld4(ev, &sm.e[(16 * tc + lr) * PS + k_]);
+          ld4(yv, &sm.y[(16 * tr + lr) * PS + k_]);
+          ld4(xv, &sm.x[(16 * tr + lr) * PS + k_]);
           const s16x4 eh = hi4(ev), el = lo4(ev), yh = hi4(yv), xh = hi4(xv);
           al = mfma16(yh, eh, mfma16(yh, el, mfma16(lo4(yv), eh, al)));
           am = mfma16(xh, eh, mfma16(xh, el, am));
@@ -686,14 +695,11 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
         for (int k0 = 0; k0 < DVS; k0 += 16) {
           const int k_ = k0 + 4 * lg;
           float sv[4], dsv[4], yv[4], xv[4], ev[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            sv[j] = sm.S[(16 * db + lr) * PS + k_ + j];
-            dsv[j] = sm.dS[(16 * db + lr) * PS + k_ + j];
-            yv[j] = sm.y[(16 * tb_ + lr) * PS + k_ + j];
-            xv[j] = sm.x[(16 * tb_ + lr) * PS + k_ + j];
-            ev[j] = sm.e[(16 * tb_ + lr) * PS + k_ + j];
-          }
+          ld4(sv, &sm.S[(16 * db + lr) * PS + k_]);
+          ld4(dsv, &sm.dS[(16 * db + lr) * PS + k_]);
+          ld4(yv, &sm.y[(16 * tb_ + lr) * PS + k_]);
+          ld4(xv, &sm.x[(16 * tb_ + lr) * PS + k_]);
+          ld4(ev, &sm.e[(16 * tb_ + lr) * PS + k_]);
           const s16x4 sh = hi4(sv), sl = lo4(sv), dh = hi4(dsv), yh = hi4(yv), xh = hi4(xv), eh = hi4(ev);
           akh = mfma16(yh, sh, mfma16(yh, sl, mfma16(lo4(yv), sh, akh)));
           aqh = mfma16(xh, sh, mfma16(xh, sl, aqh));
@@ -722,12 +728,12 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
         for (int k0 = 0; k0 < 16 * (tb_ + 1); k0 += 16) {
           const int k_ = k0 + 4 * lg;
           const s16x4 wv = bf4_col(wb + k_ * PK, PK);
-          const uint32_t* lr_ = lmu + (16 * tb_ + lr) * PC + k_;
-          const uint32_t* mr_ = mmu + (16 * tb_ + lr) * PC + k_;
+          const u32x4 lw = *reinterpret_cast<const u32x4*>(lmu + (16 * tb_ + lr) * PC + k_);
+          const u32x4 mw = *reinterpret_cast<const u32x4*>(mmu + (16 * tb_ + lr) * PC + k_);
           s16x4 h, l;
-          split4(lr_[0], lr_[1], lr_[2], lr_[3], h, l);
+          split4(lw[0], lw[1], lw[2], lw[3], h, l);
           ask = mfma16(l, wv, mfma16(h, wv, ask));
-          split4(mr_[0], mr_[1], mr_[2], mr_[3], h, l);
+          split4(mw[0], mw[1], mw[2], mw[3], h, l);
           asq = mfma16(l, wv, mfma16(h, wv, asq));
         }
 #pragma unroll 2
