@@ -851,6 +851,454 @@ __global__ __launch_bounds__(NT) void chunk_bwd_state_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// The split backward (bf16 io, scalar decay, after the forward chunk kernel
+// has written S_ck and E).  chunk_bwd_ds_kernel walks the chunks from the
+// last doing only what carries dS: dE = M^T dO + W~ dS_out, dR from
+// (I + L)^T dR = dE (written as dV), and dS_in; it stores dS_out of every
+// chunk.  chunk_bwd_tiles_kernel then takes every chunk at once, one
+// workgroup per (b, h, chunk), and forms the per-(token, key channel)
+// gradients dq, dk, dw and dL/dG from dR, dO, E, S_in and dS_out over all
+// value columns: each is written once, with no atomic accumulation.
+
+// L = strict_lower(D o K W^T), M = lower(D o Q W^T) of a chunk's n tokens
+// into lm, mm (bf16 operands: the bf16 instruction gives the exact fp32
+// sums); D_ji = exp(G_j - G_i)
+template <class Sm>
+__device__ __forceinline__ void form_lm_bf16(Sm& sm, int n, int wave, int lane) {
+  constexpr int PK = Sm::PK, DK = Sm::DKV;
+  const int lr = lane & 15, lg = lane >> 4;
+  for (int tile = wave; tile < 16; tile += NW) {
+    const int tr = tile >> 2, tc = tile & 3;
+    f32x4 al = zero4(), am = zero4();
+    if (tr >= tc) {
+      const uint16_t* kr = sm.k + (16 * tr + lr) * PK;
+      const uint16_t* qr = sm.q + (16 * tr + lr) * PK;
+      const uint16_t* wr = sm.w + (16 * tc + lr) * PK;
+#pragma unroll 4
+      for (int k0 = 0; k0 < DK; k0 += 16) {
+        const int k_ = k0 + 4 * lg;
+        const s16x4 wv = bf4(wr, k_);
+        al = mfma16(bf4(kr, k_), wv, al);
+        am = mfma16(bf4(qr, k_), wv, am);
+      }
+    }
+    const int i = 16 * tc + lr;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int j = 16 * tr + 4 * lg + ii;
+      const float dm = j < n && i <= j ? expf(sm.G[j] - sm.G[i]) : 0.f;
+      sm.lm[j * PC + i] = i < j ? dm * al[ii] : 0.f;
+      sm.mm[j * PC + i] = dm * am[ii];
+    }
+  }
+}
+
+// k, q, w of chunk c (bf16) and its decay: G, exp(G), exp(G_n - G), and a
+// zeroed dL/dG accumulator
+template <class Sm>
+__device__ __forceinline__ void stage_kqw(Sm& sm, const BwdArgs& a, long tok0, int c, int tid, int lane) {
+  constexpr int DK = Sm::DKV, PK = Sm::PK, KV = CH * DK / NT;
+  const int t0 = c * CH, n = min(CH, a.T - t0);
+  const int kt = tid * KV / DK, kd = tid * KV % DK;
+  const long krow = (tok0 + t0 + kt) * DK + kd;
+  const bool kok = kt < n;
+  float kv[KV], qv[KV], wv[KV];
+  load_vec<uint16_t, KV>(a.k, krow, kok, kv);
+  load_vec<uint16_t, KV>(a.q, krow, kok, qv);
+  load_vec<uint16_t, KV>(a.w, krow, kok, wv);
+#pragma unroll
+  for (int j = 0; j < KV; ++j) {
+    sm.k[kt * PK + kd + j] = f2bf(kv[j]);
+    sm.q[kt * PK + kd + j] = f2bf(qv[j]);
+    sm.w[kt * PK + kd + j] = f2bf(wv[j]);
+  }
+  if (tid < 64) {
+    // inclusive prefix sum of log(alpha) over the chunk (padding: alpha = 1)
+    float l = tid < n ? logf(static_cast<const float*>(a.g.alpha)[tok0 + t0 + tid]) : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(l, off);
+      if (lane >= off) l += y;
+    }
+    sm.G[tid] = l;
+    sm.gam[tid] = expf(l);
+    sm.fn[tid] = expf(__shfl(l, CH - 1) - l);
+    sm.sg[tid] = 0.f;
+  }
+}
+
+template <int DK, int DVS_>
+struct SmemD {
+  static constexpr int DKV = DK;
+  static constexpr int DVS = DVS_;   // value columns per workgroup
+  static constexpr int PS = DVS + 4;  // row pitch of [x][DVS] fp32 arrays
+  static constexpr int PK = DK + 2;   // row pitch of the [CH][DK] operand rows
+  uint16_t k[CH * PK], q[CH * PK], w[CH * PK];
+  float dS[DK * PS];  // dS carried backwards
+  float x[CH * PS];   // dO
+  float y[CH * PS];   // dE, then dR in place
+  float lm[CH * PC];  // L
+  float mm[CH * PC];  // M
+  float tb[4 * 16 * PT];
+  float G[CH], gam[CH], fn[CH], sg[CH];
+};
+
+template <int DK, int DVS_>
+__global__ __launch_bounds__(NT) void chunk_bwd_ds_kernel(BwdArgs a) {
+  using Sm = SmemD<DK, DVS_>;
+  constexpr int PK = Sm::PK, PS = Sm::PS, DVS = Sm::DVS;
+  constexpr int NC = DVS / 16, ND = DK / 16;
+  static_assert(offsetof(Sm, dS) % 16 == 0 && offsetof(Sm, x) % 16 == 0 && offsetof(Sm, y) % 16 == 0 &&
+                    offsetof(Sm, lm) % 16 == 0 && offsetof(Sm, mm) % 16 == 0,
+                "16-byte LDS rows");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  DN_LDS_POISON(smem_raw, sizeof(Sm));
+  Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int nsl = a.dv / DVS;
+  const long bh = blockIdx.x / nsl;
+  const int col0 = (blockIdx.x % nsl) * DVS;
+  const int T = a.T, dv = a.dv;
+  const int nch = (T + CH - 1) / CH;
+  const long tok0 = bh * T;
+  auto kf = [&](int t, int d) { return bf2f(sm.k[t * PK + d]); };
+  auto qf = [&](int t, int d) { return bf2f(sm.q[t * PK + d]); };
+  auto wf = [&](int t, int d) { return bf2f(sm.w[t * PK + d]); };
+
+  // (I + L_bb)^-1 of the diagonal blocks, by forward substitution (waves 0..3,
+  // lane c holds column c)
+  auto invert_blocks = [&]() {
+    if (wave < 4 && lane < 16) {
+      const int b = wave, c = lane;
+      float t[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s = r == c ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < r; ++m) s = fmaf(-sm.lm[(16 * b + r) * PC + 16 * b + m], t[m], s);
+        t[r] = s;
+        sm.tb[(16 * b + r) * PT + c] = s;
+      }
+    }
+  };
+  // (I + L)^T Z = X, one wave per column tile: Z_b = T_b^T (X_b - sum_{m>b}
+  // L_mb^T Z_m); the product's k index runs over the rows a lane holds
+  auto solve_upper = [&](float* X) {
+    for (int cb = wave; cb < NC; cb += NW)
+      for (int b = 3; b >= 0; --b) {
+        const f32x4 acc = mm_bf<false, false>(
+            zero4(), 16 * (b + 1), CH, [&](int r, int k_) { return sm.lm[k_ * PC + 16 * b + r]; },
+            [&](int k_, int cc) { return X[k_ * PS + 16 * cb + cc]; }, lane);
+        f32x4 z, u = zero4();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = X[(16 * b + 4 * lg + i) * PS + 16 * cb + lr] - acc[i];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) u = mfma4(sm.tb[(16 * b + 4 * lg + s) * PT + lr], z[s], u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[(16 * b + 4 * lg + i) * PS + 16 * cb + lr] = u[i];
+        wave_lds_sync();
+      }
+  };
+
+  for (int idx = tid; idx < DK * DVS; idx += NT) {
+    const int d = idx / DVS, cc = idx % DVS;
+    sm.dS[d * PS + cc] = a.dS_T ? a.dS_T[(bh * DK + d) * dv + col0 + cc] : 0.f;
+  }
+  constexpr int XV = CH * DVS / NT;
+  for (int c = nch - 1; c >= 0; --c) {
+    const int t0 = c * CH, n = min(CH, T - t0);
+    __syncthreads();  // the previous chunk's readers are done
+    stage_kqw(sm, a, tok0, c, tid, lane);
+    {
+      const int xt = tid * XV / DVS, xc = tid * XV % DVS;
+      float xv[XV];
+      load_vec<uint16_t, XV>(a.dO, (tok0 + t0 + xt) * dv + col0 + xc, xt < n, xv);
+#pragma unroll
+      for (int j = 0; j < XV; ++j) sm.x[xt * PS + xc + j] = xv[j];
+    }
+    __syncthreads();
+    const float gn = sm.gam[CH - 1];
+    form_lm_bf16(sm, n, wave, lane);
+    __syncthreads();
+    invert_blocks();
+    // dE = M^T dO + W~ dS_out (rows past the end zero)
+    for (int tile = wave; tile < 4 * NC; tile += NW) {
+      const int ib = tile / NC, cb = tile % NC;
+      const f32x4 a1 = mm_bf<false, true>(
+          zero4(), 16 * ib, CH, [&](int r, int k_) { return sm.mm[k_ * PC + 16 * ib + r]; },
+          [&](int k_, int cc) { return sm.x[k_ * PS + 16 * cb + cc]; }, lane);
+      const f32x4 a2 = mm_bf<true, false>(
+          zero4(), 0, DK, [&](int r, int k_) { return wf(16 * ib + r, k_); },
+          [&](int k_, int cc) { return sm.dS[k_ * PS + 16 * cb + cc]; }, lane);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 16 * ib + 4 * lg + ii;
+        sm.y[i * PS + 16 * cb + lr] = i < n ? fmaf(sm.fn[i], a2[ii], a1[ii]) : 0.f;
+      }
+    }
+    // dS_out of the chunk for the tile kernel
+    for (int idx = tid; idx < DK * DVS; idx += NT) {
+      const int d = idx / DVS, cc = idx % DVS;
+      a.dS_ck[((bh * nch + c) * DK + d) * dv + col0 + cc] = sm.dS[d * PS + cc];
+    }
+    __syncthreads();
+    solve_upper(sm.y);  // dR
+    __syncthreads();
+    // dV = dR
+    for (int idx = tid; idx < CH * DVS; idx += NT) {
+      const int t = idx / DVS, cc = idx % DVS;
+      if (t < n) a.dv_out[(tok0 + t0 + t) * dv + col0 + cc] = sm.y[t * PS + cc];
+    }
+    // dS_in = g_n dS_out + sum_t g_t (q_t dO_t^T - k_t dR_t^T)
+    for (int tile = wave; tile < ND * NC; tile += NW) {
+      const int db = tile / NC, cb = tile % NC;
+      f32x4 acc = mm_bf<true, false>(
+          zero4(), 0, CH, [&](int r, int k_) { return qf(k_, 16 * db + r); },
+          [&](int k_, int cc) { return sm.gam[k_] * sm.x[k_ * PS + 16 * cb + cc]; }, lane);
+      const f32x4 acc2 = mm_bf<true, false>(
+          zero4(), 0, CH, [&](int r, int k_) { return kf(k_, 16 * db + r); },
+          [&](int k_, int cc) { return sm.gam[k_] * sm.y[k_ * PS + 16 * cb + cc]; }, lane);
+      acc -= acc2;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int d = 16 * db + 4 * lg + ii;
+        float& s = sm.dS[d * PS + 16 * cb + lr];
+        s = fmaf(gn, s, acc[ii]);
+      }
+    }
+  }
+  __syncthreads();
+  if (a.dS0)
+    for (int idx = tid; idx < DK * DVS; idx += NT) {
+      const int d = idx / DVS, cc = idx % DVS;
+      a.dS0[(bh * DK + d) * dv + col0 + cc] = sm.dS[d * PS + cc];
+    }
+}
+
+template <int DK>
+struct SmemT {
+  static constexpr int DKV = DK;
+  static constexpr int VS = 32;      // value columns per slice of the contractions
+  static constexpr int PS = VS + 4;  // row pitch of [x][VS] fp32 arrays
+  static constexpr int PK = DK + 2;
+  uint16_t k[CH * PK], q[CH * PK], w[CH * PK];
+  float S[DK * PS], dS[DK * PS];             // S_in and dS_out, one slice
+  float e[CH * PS], x[CH * PS], y[CH * PS];  // E, dO and dR, one slice
+  float lm[CH * PC];  // L, then D o dL as split words
+  float mm[CH * PC];  // M, then D o dM as split words
+  float G[CH], gam[CH], fn[CH], sg[CH];
+};
+
+template <int DK>
+__global__ __launch_bounds__(NT) void chunk_bwd_tiles_kernel(BwdArgs a) {
+  using Sm = SmemT<DK>;
+  constexpr int PK = Sm::PK, PS = Sm::PS, VS = Sm::VS;
+  constexpr int ND = DK / 16;
+  constexpr int TPW = 4 * ND / NW;  // [token][key] tiles per wavefront
+  static_assert(TPW * NW == 4 * ND, "key tiles per wavefront");
+  static_assert(offsetof(Sm, S) % 16 == 0 && offsetof(Sm, dS) % 16 == 0 && offsetof(Sm, e) % 16 == 0 &&
+                    offsetof(Sm, x) % 16 == 0 && offsetof(Sm, y) % 16 == 0 && offsetof(Sm, lm) % 16 == 0 &&
+                    offsetof(Sm, mm) % 16 == 0,
+                "16-byte LDS rows");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  DN_LDS_POISON(smem_raw, sizeof(Sm));
+  Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int T = a.T, dv = a.dv;
+  const int nch = (T + CH - 1) / CH;
+  const long bh = blockIdx.x / nch;
+  const int c = blockIdx.x % nch;
+  const int t0 = c * CH, n = min(CH, T - t0);
+  const long tok0 = bh * T;
+  auto kf = [&](int t, int d) { return bf2f(sm.k[t * PK + d]); };
+  auto qf = [&](int t, int d) { return bf2f(sm.q[t * PK + d]); };
+  auto wf = [&](int t, int d) { return bf2f(sm.w[t * PK + d]); };
+
+  stage_kqw(sm, a, tok0, c, tid, lane);
+  __syncthreads();
+  form_lm_bf16(sm, n, wave, lane);  // L, M (for the decay's gradient)
+
+  // the contractions over the value columns, 32 at a time: dL = -dR E^T,
+  // dM = dO E^T (this wave's lower tiles of the 16: wave and wave + 8), and
+  // per (token, key) tile dR S_in^T, dO S_in^T, E dS_out^T; and <S_in, dS_out>
+  f32x4 al[2] = {zero4(), zero4()}, am[2] = {zero4(), zero4()};
+  f32x4 akh[TPW], aqh[TPW], atw[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) akh[k] = aqh[k] = atw[k] = zero4();
+  float sdot = 0.f;
+  constexpr int SV = DK * VS / NT, XV = CH * VS / NT;
+  for (int s = 0; s < dv / VS; ++s) {
+    const int col0 = s * VS;
+    __syncthreads();  // the previous slice's readers are done
+    {
+      const int sd = tid * SV / VS, sc = tid * SV % VS;
+      const int xt = tid * XV / VS, xc = tid * XV % VS;
+      const bool xok = xt < n;
+      const long srow = ((bh * nch + c) * DK + sd) * dv + col0 + sc;
+      const long xrow = (tok0 + t0 + xt) * dv + col0 + xc;
+      float sv[SV], dsv[SV], ev[XV], yv[XV], xv[XV];
+      load_vec<float, SV>(a.S_ck, srow, true, sv);
+      load_vec<float, SV>(a.dS_ck, srow, true, dsv);
+      load_vec<float, XV>(a.E, xrow, xok, ev);
+      load_vec<float, XV>(a.dv_out, xrow, xok, yv);  // dR = dV
+      load_vec<uint16_t, XV>(a.dO, xrow, xok, xv);
+#pragma unroll
+      for (int j = 0; j < SV; ++j) {
+        sm.S[sd * PS + sc + j] = sv[j];
+        sm.dS[sd * PS + sc + j] = dsv[j];
+        sdot = fmaf(sv[j], dsv[j], sdot);
+      }
+#pragma unroll
+      for (int j = 0; j < XV; ++j) {
+        sm.e[xt * PS + xc + j] = ev[j];
+        sm.y[xt * PS + xc + j] = yv[j];
+        sm.x[xt * PS + xc + j] = xv[j];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int tile = wave + 8 * k, tr = tile >> 2, tc = tile & 3;
+      if (tr < tc) continue;  // uniform
+#pragma unroll
+      for (int k0 = 0; k0 < VS; k0 += 16) {
+        const int k_ = k0 + 4 * lg;
+        float ev[4], yv[4], xv[4];
+        ld4(ev, &sm.e[(16 * tc + lr) * PS + k_]);
+        ld4(yv, &sm.y[(16 * tr + lr) * PS + k_]);
+        ld4(xv, &sm.x[(16 * tr + lr) * PS + k_]);
+        const s16x4 eh = hi4(ev), el = lo4(ev), yh = hi4(yv), xh = hi4(xv);
+        al[k] = mfma16(yh, eh, mfma16(yh, el, mfma16(lo4(yv), eh, al[k])));
+        am[k] = mfma16(xh, eh, mfma16(xh, el, am[k]));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int tile = wave + NW * k, tb_ = tile / ND, db = tile % ND;
+#pragma unroll
+      for (int k0 = 0; k0 < VS; k0 += 16) {
+        const int k_ = k0 + 4 * lg;
+        float sv[4], dsv[4], yv[4], xv[4], ev[4];
+        ld4(sv, &sm.S[(16 * db + lr) * PS + k_]);
+        ld4(dsv, &sm.dS[(16 * db + lr) * PS + k_]);
+        ld4(yv, &sm.y[(16 * tb_ + lr) * PS + k_]);
+        ld4(xv, &sm.x[(16 * tb_ + lr) * PS + k_]);
+        ld4(ev, &sm.e[(16 * tb_ + lr) * PS + k_]);
+        const s16x4 sh = hi4(sv), sl = lo4(sv), dh = hi4(dsv), yh = hi4(yv), xh = hi4(xv), eh = hi4(ev);
+        akh[k] = mfma16(yh, sh, mfma16(yh, sl, mfma16(lo4(yv), sh, akh[k])));
+        aqh[k] = mfma16(xh, sh, mfma16(xh, sl, aqh[k]));
+        atw[k] = mfma16(eh, dh, mfma16(eh, lo4(dsv), mfma16(lo4(ev), dh, atw[k])));
+      }
+    }
+  }
+  // dL/dG of the chunk end: g_n <S_in, dS_out>
+  sdot = wave_total(sdot);
+  if (lane == 0) atomicAdd(&sm.sg[CH - 1], sm.gam[CH - 1] * sdot);
+  // the decay terms of L and M (L o dL, M o dM: + to the row token, - to the
+  // column token), then D o dL and D o dM as split words (entries not
+  // written stay 0)
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int tile = wave + 8 * k, tr = tile >> 2, tc = tile & 3;
+    if (tr < tc) continue;  // uniform
+    const int i = 16 * tc + lr;
+    float col = 0.f;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int j = 16 * tr + 4 * lg + ii;
+      const bool ok = j < n && i <= j;
+      const float dl = -al[k][ii], dmv = am[k][ii];
+      float tlm = 0.f;
+      if (ok) {
+        const float dm = expf(sm.G[j] - sm.G[i]);
+        tlm = (i < j ? sm.lm[j * PC + i] * dl : 0.f) + sm.mm[j * PC + i] * dmv;
+        if (i == j) tlm = 0.f;  // the diagonal adds and subtracts the same term
+        reinterpret_cast<uint32_t*>(sm.lm)[j * PC + i] = split_bf(i < j ? dm * dl : 0.f);
+        reinterpret_cast<uint32_t*>(sm.mm)[j * PC + i] = split_bf(dm * dmv);
+      }
+      col -= tlm;
+      const float row = row16_sum(tlm);
+      if (lr == 0 && j < n) atomicAdd(&sm.sg[j], row);
+    }
+    col = col4_sum(col);
+    if (lg == 0) atomicAdd(&sm.sg[i], col);
+  }
+  __syncthreads();
+  // per (token, key channel): dk = g (-S_in dR) + (D o dL) W, dq = g S_in dO +
+  // (D o dM) W, dw = (g_n / g) dS_out E + (D o dL)^T K + (D o dM)^T Q, and
+  // their decay terms
+  const uint32_t* lmu = reinterpret_cast<const uint32_t*>(sm.lm);
+  const uint32_t* mmu = reinterpret_cast<const uint32_t*>(sm.mm);
+  float wend = 0.f;  // the chunk end's part of the W~ terms
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {  // unrolled: the accumulators stay in registers
+    const int tile = wave + NW * k, tb_ = tile / ND, db = tile % ND;
+    f32x4 ask = zero4(), asq = zero4(), asw = zero4(), asw2 = zero4();
+    const uint16_t* wb = sm.w + 16 * db + lr;
+    const uint16_t* kb = sm.k + 16 * db + lr;
+    const uint16_t* qb = sm.q + 16 * db + lr;
+#pragma unroll 2
+    for (int k0 = 0; k0 < 16 * (tb_ + 1); k0 += 16) {
+      const int k_ = k0 + 4 * lg;
+      const s16x4 wv = bf4_col(wb + k_ * PK, PK);
+      const u32x4 lw = *reinterpret_cast<const u32x4*>(lmu + (16 * tb_ + lr) * PC + k_);
+      const u32x4 mw = *reinterpret_cast<const u32x4*>(mmu + (16 * tb_ + lr) * PC + k_);
+      s16x4 h, l;
+      split4(lw[0], lw[1], lw[2], lw[3], h, l);
+      ask = mfma16(l, wv, mfma16(h, wv, ask));
+      split4(mw[0], mw[1], mw[2], mw[3], h, l);
+      asq = mfma16(l, wv, mfma16(h, wv, asq));
+    }
+#pragma unroll 2
+    for (int k0 = 16 * tb_; k0 < CH; k0 += 16) {
+      const int k_ = k0 + 4 * lg;
+      const uint32_t* lc = lmu + k_ * PC + 16 * tb_ + lr;
+      const uint32_t* mc = mmu + k_ * PC + 16 * tb_ + lr;
+      s16x4 h, l;
+      split4(lc[0], lc[PC], lc[2 * PC], lc[3 * PC], h, l);
+      const s16x4 kv = bf4_col(kb + k_ * PK, PK);
+      asw = mfma16(l, kv, mfma16(h, kv, asw));
+      split4(mc[0], mc[PC], mc[2 * PC], mc[3 * PC], h, l);
+      const s16x4 qv = bf4_col(qb + k_ * PK, PK);
+      asw2 = mfma16(l, qv, mfma16(h, qv, asw2));
+    }
+    asw += asw2;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int t = 16 * tb_ + 4 * lg + ii, d = 16 * db + lr;
+      const bool ok = t < n;
+      const long gi = (tok0 + t0 + t) * DK + d;
+      const float kh = -akh[k][ii], qh = aqh[k][ii], tw = atw[k][ii];
+      const float kv = kf(t, d), qv = qf(t, d), wv = wf(t, d);
+      const float g = sm.gam[t], f = sm.fn[t];
+      const float wtw = f * wv * tw;
+      if (ok) {
+        a.dk_out[gi] = fmaf(g, kh, ask[ii]);
+        a.dq_out[gi] = fmaf(g, qh, asq[ii]);
+        a.dw_acc[gi] = fmaf(f, tw, asw[ii]);
+        wend += wtw;
+      }
+      const float row = row16_sum(ok ? g * (kv * kh + qv * qh) - wtw : 0.f);
+      if (lr == 0 && ok) atomicAdd(&sm.sg[t], row);
+    }
+  }
+  wend = wave_total(wend);
+  if (lane == 0) atomicAdd(&sm.sg[CH - 1], wend);
+  __syncthreads();
+  // dL/dG of the chunk's tokens; the padding tokens of a partial chunk share
+  // the last real token's decay
+  if (tid < CH) {
+    const float v = sm.sg[tid];
+    float tail = 0.f;
+    if (tid == n - 1)
+      for (int t = n; t < CH; ++t) tail += sm.sg[t];
+    if (tid < n) a.dG[tok0 + t0 + tid] = v + tail;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Back through the write gains with a statistic and the decay.  Thread d owns
 // key channel d.
 template <typename E, int DK, int GAIN, bool CHAN>
@@ -1201,6 +1649,43 @@ static hipError_t launch_bwd_state_c(const BwdArgs& a, int io_bf16, hipStream_t 
 hipError_t launch_chunk_bwd_state(const BwdArgs& a, int io_bf16, bool channel, hipStream_t st) {
   if (a.T == 0 || a.B * a.H == 0) return hipSuccess;
   return channel ? launch_bwd_state_c<true>(a, io_bf16, st) : launch_bwd_state_c<false>(a, io_bf16, st);
+}
+
+template <class Sm, class K>
+static hipError_t launch_lds(K kern, unsigned grid, const BwdArgs& a, hipStream_t st) {
+  static_assert(sizeof(Sm) <= 160 * 1024, "LDS budget");
+  const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(sizeof(Sm)));
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(bwd::NT), sizeof(Sm), st, a);
+  return hipGetLastError();
+}
+// The serial sweep in value slices of 64 columns where they fill the
+// compute units, else of 32 or 16 (more, narrower slices finish sooner while
+// they fit on the device at once); the tile kernel one workgroup per chunk
+template <int DK>
+static hipError_t launch_bwd_split_t(const BwdArgs& a, hipStream_t st) {
+  const long bh = static_cast<long>(a.B) * a.H;
+  const long nch = (a.T + bwd::CH - 1) / bwd::CH;
+  if (a.dv % 32 != 0) return hipErrorInvalidValue;
+  const int dvs = 2 * bh * (a.dv / 32) <= BWD_CU_COUNT                     ? 16
+                  : a.dv % 64 == 0 && bh * (a.dv / 64) >= BWD_CU_COUNT ? 64
+                                                                        : 32;
+  const unsigned grid = static_cast<unsigned>(bh * (a.dv / dvs));
+  const hipError_t err =
+      dvs == 16   ? launch_lds<bwd::SmemD<DK, 16>>(bwd::chunk_bwd_ds_kernel<DK, 16>, grid, a, st)
+      : dvs == 64 ? launch_lds<bwd::SmemD<DK, 64>>(bwd::chunk_bwd_ds_kernel<DK, 64>, grid, a, st)
+                  : launch_lds<bwd::SmemD<DK, 32>>(bwd::chunk_bwd_ds_kernel<DK, 32>, grid, a, st);
+  if (err != hipSuccess) return err;
+  return launch_lds<bwd::SmemT<DK>>(bwd::chunk_bwd_tiles_kernel<DK>, static_cast<unsigned>(bh * nch), a, st);
+}
+
+hipError_t launch_chunk_bwd_split(const BwdArgs& a, hipStream_t st) {
+  if (a.T == 0 || a.B * a.H == 0) return hipSuccess;
+  if (a.dk == 128) return launch_bwd_split_t<128>(a, st);
+  if (a.dk == 64) return launch_bwd_split_t<64>(a, st);
+  return hipErrorInvalidValue;
 }
 
 template <typename E, int DK, bool CHAN>

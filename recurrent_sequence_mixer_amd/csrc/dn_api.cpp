@@ -906,15 +906,27 @@ DN_EXPORT int dn_chunk_fwd_noalloc(const dn_desc* d, const void* q, const void* 
 }
 
 // ---------------------------------------------------------------------------
-// Chunked backward.  Workspace, fp32, each part on a 256-byte boundary: w
-// [B, H, T, dk], S_ck [B, H, nch, dk, dv], E [B, H, T, dv], dw_acc
-// [B, H, T, dk], dG ([B, H, T]; channel decay [B, H, T, dk]), then for the
+// Chunked backward.  Workspace, each part on a 256-byte boundary: w
+// [B, H, T, dk] (fp32, bf16 with bf16 io and scalar decay), S_ck [B, H, nch,
+// dk, dv], E [B, H, T, dv], dw_acc [B, H, T, dk], dG ([B, H, T]; channel decay
+// [B, H, T, dk]), on the split path dS_ck [B, H, nch, dk, dv], then for the
 // gains with a statistic the statistic entering every chunk ([B, H, nch, dk];
 // KDN_ISO [B, H, nch]), and the workspace of the gain scans (as for
-// dn_gain_prep).
+// dn_gain_prep); fp32 where not said.
 struct BwdLayout {
-  size_t w, sck, e, dw, dg, aux, prep, total;
+  size_t w, sck, e, dw, dg, dsck, aux, prep, total;
 };
+
+// The split backward: bf16 io, scalar decay, the gains the forward chunk
+// kernel runs with a write vector per token (KLA, GDN, PGDN, explicit w), dv
+// in 64-column slices.  That kernel writes the checkpoints (the state
+// entering every chunk and the residuals E) in a pass without output; the
+// serial sweep carries only dS, and one workgroup per chunk forms the
+// per-(token, key) gradients.
+static bool bwd_split(const dn_desc* d) {
+  return d->io == DN_BF16 && d->decay == DN_DECAY_SCALAR && d->gain != DN_GAIN_KDN &&
+         d->gain != DN_GAIN_KDN_ISO && d->dv % 64 == 0;
+}
 
 static BwdLayout bwd_layout(const dn_desc* d) {
   BwdLayout L{};
@@ -926,7 +938,8 @@ static BwdLayout bwd_layout(const dn_desc* d) {
   L.e = round256(L.sck + bh * nch * d->dk * d->dv * 4);
   L.dw = round256(L.e + bht * d->dv * 4);
   L.dg = round256(L.dw + bht * d->dk * 4);
-  L.aux = round256(L.dg + bht * gdim * 4);
+  L.dsck = round256(L.dg + bht * gdim * 4);
+  L.aux = round256(L.dsck + (bwd_split(d) ? bh * nch * d->dk * d->dv * 4 : 0));
   L.prep = round256(L.aux + (has_aux_state(d) ? bh * nch * aux_per_head(d) * 4 : 0));
   L.total = L.prep + prep_layout(d).total;
   return L;
@@ -1034,11 +1047,13 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
   float* dw_acc = reinterpret_cast<float*>(wb + lay.dw);
   float* dG = reinterpret_cast<float*>(wb + lay.dg);
   float* aux_chunk = has_aux ? reinterpret_cast<float*>(wb + lay.aux) : nullptr;
-  // the accumulated gradients start at zero
-  if (dn::launch_zero(gr->dq, bht * d->dk, s) != hipSuccess ||
-      dn::launch_zero(gr->dk, bht * d->dk, s) != hipSuccess ||
-      dn::launch_zero(dw_acc, bht * d->dk, s) != hipSuccess ||
-      dn::launch_zero(dG, bht * (chan ? d->dk : 1), s) != hipSuccess ||
+  // the accumulated gradients start at zero (the split path writes dq, dk,
+  // dw_acc and dG once each instead)
+  const bool split = bwd_split(d);
+  if ((!split && (dn::launch_zero(gr->dq, bht * d->dk, s) != hipSuccess ||
+                  dn::launch_zero(gr->dk, bht * d->dk, s) != hipSuccess ||
+                  dn::launch_zero(dw_acc, bht * d->dk, s) != hipSuccess ||
+                  dn::launch_zero(dG, bht * (chan ? d->dk : 1), s) != hipSuccess)) ||
       (pg && dn::launch_zero(gr->dmu_log, d->H, s) != hipSuccess))
     return DN_ERR_HIP;
   const dn::GateArgs ga = gate_args(d, g);
@@ -1072,13 +1087,9 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
   b.dw_acc = dw_acc;
   b.dG = dG;
   b.dS0 = gr->dS0;
-  // bf16 io, scalar decay, gains the forward chunk kernel runs with a write
-  // vector per token (KLA, GDN, PGDN, explicit w), dv in 64-column slices: that
-  // kernel writes the checkpoints (the state entering every chunk and the
-  // residuals E) in a pass without output, and the state kernel runs only its
-  // reverse sweep
-  const bool fwd_ck = d->io == DN_BF16 && !chan && !kd && d->dv % 64 == 0;
-  if (fwd_ck) {
+  // the split path: the forward chunk kernel writes the checkpoints, then the
+  // serial sweep and the per-chunk tile kernel
+  if (split) {
     dn::ChunkArgs ca{};
     ca.B = d->B;
     ca.H = d->H;
@@ -1095,8 +1106,11 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
     ca.E_ck = b.E;
     if (dn::launch_chunk_fwd_bf16_scalar(ca, d->gain, s) != hipSuccess) return DN_ERR_HIP;
     b.ck_given = 1;
+    b.dS_ck = reinterpret_cast<float*>(wb + lay.dsck);
+    if (dn::launch_chunk_bwd_split(b, s) != hipSuccess) return DN_ERR_HIP;
+  } else if (dn::launch_chunk_bwd_state(b, d->io == DN_BF16, chan, s) != hipSuccess) {
+    return DN_ERR_HIP;
   }
-  if (dn::launch_chunk_bwd_state(b, d->io == DN_BF16, chan, s) != hipSuccess) return DN_ERR_HIP;
   // the write gains and the decay backwards
   dn::GainBwdArgs gb;
   gb.B = d->B;
