@@ -1,3 +1,14 @@
+// The split backward (bf16 io, scalar decay, after the forward chunk kernel
+// has written S_ck and E).  Three launches: chunk_bwd_zp_kernel takes every
+// chunk at once and forms what of (I + L)^T dR = M^T dO + W~ dS_out does not
+// depend on dS (Z = (I + L)^-T W~ and P = (I + L)^-T M^T dO, so that
+// dR = P + Z dS_out); chunk_bwd_ds_kernel walks the chunks from the last
+// carrying dS (dR, dS_in) and stores dS_out of every chunk;
+// chunk_bwd_tiles_kernel then takes every chunk at once, one workgroup per
+// (b, h, chunk), and forms the per-(token, key channel) gradients dq, dk, dw
+// and dL/dG from dR, dO, E, S_in and dS_out over all value columns: each is
+// written once, with no atomic accumulation.
+
 // Chunked backward of the gated delta-rule recurrence.
 //
 // Training differentiates the same recurrence the forward evaluates
@@ -900,21 +911,25 @@ __device__ __forceinline__ void stage_kqw(Sm& sm, const BwdArgs& a, long tok0, i
   constexpr int DK = Sm::DKV, PK = Sm::PK, KV = CH * DK / NT;
   const int t0 = c * CH, n = min(CH, a.T - t0);
   const int kt = tid * KV / DK, kd = tid * KV % DK;
-  const long krow = (tok0 + t0 + kt) * DK + kd;
+  // every load unconditional (a load under a branch makes the wavefront wait
+  // for it where the branches join): rows past the end read the last row
+  // and are staged as zeros
+  const long krow = (tok0 + t0 + min(kt, n - 1)) * DK + kd;
   const bool kok = kt < n;
   float kv[KV], qv[KV], wv[KV];
-  load_vec<uint16_t, KV>(a.k, krow, kok, kv);
-  load_vec<uint16_t, KV>(a.q, krow, kok, qv);
-  load_vec<uint16_t, KV>(a.w, krow, kok, wv);
+  load_vec<uint16_t, KV>(a.k, krow, true, kv);
+  load_vec<uint16_t, KV>(a.q, krow, true, qv);
+  load_vec<uint16_t, KV>(a.w, krow, true, wv);
+  const float alv = static_cast<const float*>(a.g.alpha)[tok0 + t0 + min(lane, n - 1)];
 #pragma unroll
   for (int j = 0; j < KV; ++j) {
-    sm.k[kt * PK + kd + j] = f2bf(kv[j]);
-    sm.q[kt * PK + kd + j] = f2bf(qv[j]);
-    sm.w[kt * PK + kd + j] = f2bf(wv[j]);
+    sm.k[kt * PK + kd + j] = kok ? f2bf(kv[j]) : 0;
+    sm.q[kt * PK + kd + j] = kok ? f2bf(qv[j]) : 0;
+    sm.w[kt * PK + kd + j] = kok ? f2bf(wv[j]) : 0;
   }
   if (tid < 64) {
     // inclusive prefix sum of log(alpha) over the chunk (padding: alpha = 1)
-    float l = tid < n ? logf(static_cast<const float*>(a.g.alpha)[tok0 + t0 + tid]) : 0.f;
+    float l = tid < n ? logf(alv) : 0.f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(l, off);
@@ -927,153 +942,417 @@ __device__ __forceinline__ void stage_kqw(Sm& sm, const BwdArgs& a, long tok0, i
   }
 }
 
-template <int DK, int DVS_>
-struct SmemD {
+// (I + L_bb)^-1 of the four diagonal 16x16 blocks of I + L, by forward
+// substitution (waves 0..3, lane c holds column c)
+__device__ __forceinline__ void invert_blocks(const float* lm, float* tb, int wave, int lane) {
+  if (wave < 4 && lane < 16) {
+    const int b = wave, c = lane;
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = r == c ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) s = fmaf(-lm[(16 * b + r) * PC + 16 * b + m], t[m], s);
+      t[r] = s;
+      tb[(16 * b + r) * PT + c] = s;
+    }
+  }
+}
+// (I + L)^T Z = X in place for ncb 16-column tiles of X (row pitch PX), one
+// wave per column tile: Z_b = T_b^T (X_b - sum_{m>b} L_mb^T Z_m), blocks from
+// the last; the product's k index runs over the rows a lane holds
+template <int PX>
+__device__ __forceinline__ void solve_upper(const float* lm, const float* tb, float* X, int ncb, int wave,
+                                            int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+  for (int cb = wave; cb < ncb; cb += NW)
+    for (int b = 3; b >= 0; --b) {
+      const f32x4 acc = mm_bf<false, false>(
+          zero4(), 16 * (b + 1), CH, [&](int r, int k_) { return lm[k_ * PC + 16 * b + r]; },
+          [&](int k_, int cc) { return X[k_ * PX + 16 * cb + cc]; }, lane);
+      f32x4 z, u = zero4();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = X[(16 * b + 4 * lg + i) * PX + 16 * cb + lr] - acc[i];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) u = mfma4(tb[(16 * b + 4 * lg + s) * PT + lr], z[s], u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[(16 * b + 4 * lg + i) * PX + 16 * cb + lr] = u[i];
+      wave_lds_sync();
+    }
+}
+
+// chunk_bwd_zp_kernel: the dS-independent part of every chunk's
+// (I + L)^T dR = M^T dO + W~ dS_out, one workgroup per (b, h, chunk):
+// Z = (I + L)^-T W~ [CH, dk] into the workspace as split bf16 pairs (rows past
+// the end zero), and P = (I + L)^-T M^T dO [n, dv] into dv_out, in 64-column
+// slices.  The serial sweep then needs only dR = P + Z dS_out.
+constexpr int PO = 64 + 4;  // row pitch of the 64-column fp32 slices
+template <int DK>
+struct SmemZ {
   static constexpr int DKV = DK;
-  static constexpr int DVS = DVS_;   // value columns per workgroup
-  static constexpr int PS = DVS + 4;  // row pitch of [x][DVS] fp32 arrays
-  static constexpr int PK = DK + 2;   // row pitch of the [CH][DK] operand rows
+  static constexpr int PK = DK + 2;  // row pitch of the [CH][DK] operand rows
+  static constexpr int PX = DK + 4;  // row pitch of x: W~, then Z
   uint16_t k[CH * PK], q[CH * PK], w[CH * PK];
-  float dS[DK * PS];  // dS carried backwards
-  float x[CH * PS];   // dO
-  float y[CH * PS];   // dE, then dR in place
+  float x[CH * PX];   // W~ solved in place into Z; then M^T dO solved into P (pitch PO)
+  float o[CH * PO];   // dO, one 64-column slice
   float lm[CH * PC];  // L
   float mm[CH * PC];  // M
   float tb[4 * 16 * PT];
   float G[CH], gam[CH], fn[CH], sg[CH];
 };
 
-template <int DK, int DVS_>
-__global__ __launch_bounds__(NT) void chunk_bwd_ds_kernel(BwdArgs a) {
-  using Sm = SmemD<DK, DVS_>;
-  constexpr int PK = Sm::PK, PS = Sm::PS, DVS = Sm::DVS;
-  constexpr int NC = DVS / 16, ND = DK / 16;
-  static_assert(offsetof(Sm, dS) % 16 == 0 && offsetof(Sm, x) % 16 == 0 && offsetof(Sm, y) % 16 == 0 &&
-                    offsetof(Sm, lm) % 16 == 0 && offsetof(Sm, mm) % 16 == 0,
-                "16-byte LDS rows");
+template <int DK>
+__global__ __launch_bounds__(NT) void chunk_bwd_zp_kernel(BwdArgs a) {
+  using Sm = SmemZ<DK>;
+  constexpr int PK = Sm::PK, PX = Sm::PX;
+  static_assert(offsetof(Sm, x) % 16 == 0 && offsetof(Sm, o) % 16 == 0 && PX % 4 == 0, "16-byte LDS rows");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   DN_LDS_POISON(smem_raw, sizeof(Sm));
   Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int nsl = a.dv / DVS;
-  const long bh = blockIdx.x / nsl;
-  const int col0 = (blockIdx.x % nsl) * DVS;
   const int T = a.T, dv = a.dv;
   const int nch = (T + CH - 1) / CH;
+  const long bh = blockIdx.x / nch;
+  const int c = blockIdx.x % nch;
+  const int t0 = c * CH, n = min(CH, T - t0);
   const long tok0 = bh * T;
-  auto kf = [&](int t, int d) { return bf2f(sm.k[t * PK + d]); };
-  auto qf = [&](int t, int d) { return bf2f(sm.q[t * PK + d]); };
-  auto wf = [&](int t, int d) { return bf2f(sm.w[t * PK + d]); };
 
-  // (I + L_bb)^-1 of the diagonal blocks, by forward substitution (waves 0..3,
-  // lane c holds column c)
-  auto invert_blocks = [&]() {
-    if (wave < 4 && lane < 16) {
-      const int b = wave, c = lane;
-      float t[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = r == c ? 1.f : 0.f;
-#pragma unroll
-        for (int m = 0; m < r; ++m) s = fmaf(-sm.lm[(16 * b + r) * PC + 16 * b + m], t[m], s);
-        t[r] = s;
-        sm.tb[(16 * b + r) * PT + c] = s;
-      }
-    }
-  };
-  // (I + L)^T Z = X, one wave per column tile: Z_b = T_b^T (X_b - sum_{m>b}
-  // L_mb^T Z_m); the product's k index runs over the rows a lane holds
-  auto solve_upper = [&](float* X) {
-    for (int cb = wave; cb < NC; cb += NW)
-      for (int b = 3; b >= 0; --b) {
-        const f32x4 acc = mm_bf<false, false>(
-            zero4(), 16 * (b + 1), CH, [&](int r, int k_) { return sm.lm[k_ * PC + 16 * b + r]; },
-            [&](int k_, int cc) { return X[k_ * PS + 16 * cb + cc]; }, lane);
-        f32x4 z, u = zero4();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[i] = X[(16 * b + 4 * lg + i) * PS + 16 * cb + lr] - acc[i];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) u = mfma4(sm.tb[(16 * b + 4 * lg + s) * PT + lr], z[s], u);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) X[(16 * b + 4 * lg + i) * PS + 16 * cb + lr] = u[i];
-        wave_lds_sync();
-      }
-  };
-
-  for (int idx = tid; idx < DK * DVS; idx += NT) {
-    const int d = idx / DVS, cc = idx % DVS;
-    sm.dS[d * PS + cc] = a.dS_T ? a.dS_T[(bh * DK + d) * dv + col0 + cc] : 0.f;
-  }
-  constexpr int XV = CH * DVS / NT;
-  for (int c = nch - 1; c >= 0; --c) {
-    const int t0 = c * CH, n = min(CH, T - t0);
-    __syncthreads();  // the previous chunk's readers are done
-    stage_kqw(sm, a, tok0, c, tid, lane);
-    {
-      const int xt = tid * XV / DVS, xc = tid * XV % DVS;
-      float xv[XV];
-      load_vec<uint16_t, XV>(a.dO, (tok0 + t0 + xt) * dv + col0 + xc, xt < n, xv);
-#pragma unroll
-      for (int j = 0; j < XV; ++j) sm.x[xt * PS + xc + j] = xv[j];
-    }
-    __syncthreads();
-    const float gn = sm.gam[CH - 1];
-    form_lm_bf16(sm, n, wave, lane);
-    __syncthreads();
-    invert_blocks();
-    // dE = M^T dO + W~ dS_out (rows past the end zero)
-    for (int tile = wave; tile < 4 * NC; tile += NW) {
-      const int ib = tile / NC, cb = tile % NC;
-      const f32x4 a1 = mm_bf<false, true>(
-          zero4(), 16 * ib, CH, [&](int r, int k_) { return sm.mm[k_ * PC + 16 * ib + r]; },
-          [&](int k_, int cc) { return sm.x[k_ * PS + 16 * cb + cc]; }, lane);
-      const f32x4 a2 = mm_bf<true, false>(
-          zero4(), 0, DK, [&](int r, int k_) { return wf(16 * ib + r, k_); },
-          [&](int k_, int cc) { return sm.dS[k_ * PS + 16 * cb + cc]; }, lane);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int i = 16 * ib + 4 * lg + ii;
-        sm.y[i * PS + 16 * cb + lr] = i < n ? fmaf(sm.fn[i], a2[ii], a1[ii]) : 0.f;
-      }
-    }
-    // dS_out of the chunk for the tile kernel
-    for (int idx = tid; idx < DK * DVS; idx += NT) {
-      const int d = idx / DVS, cc = idx % DVS;
-      a.dS_ck[((bh * nch + c) * DK + d) * dv + col0 + cc] = sm.dS[d * PS + cc];
-    }
-    __syncthreads();
-    solve_upper(sm.y);  // dR
-    __syncthreads();
-    // dV = dR
-    for (int idx = tid; idx < CH * DVS; idx += NT) {
-      const int t = idx / DVS, cc = idx % DVS;
-      if (t < n) a.dv_out[(tok0 + t0 + t) * dv + col0 + cc] = sm.y[t * PS + cc];
-    }
-    // dS_in = g_n dS_out + sum_t g_t (q_t dO_t^T - k_t dR_t^T)
-    for (int tile = wave; tile < ND * NC; tile += NW) {
-      const int db = tile / NC, cb = tile % NC;
-      f32x4 acc = mm_bf<true, false>(
-          zero4(), 0, CH, [&](int r, int k_) { return qf(k_, 16 * db + r); },
-          [&](int k_, int cc) { return sm.gam[k_] * sm.x[k_ * PS + 16 * cb + cc]; }, lane);
-      const f32x4 acc2 = mm_bf<true, false>(
-          zero4(), 0, CH, [&](int r, int k_) { return kf(k_, 16 * db + r); },
-          [&](int k_, int cc) { return sm.gam[k_] * sm.y[k_ * PS + 16 * cb + cc]; }, lane);
-      acc -= acc2;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int d = 16 * db + 4 * lg + ii;
-        float& s = sm.dS[d * PS + 16 * cb + lr];
-        s = fmaf(gn, s, acc[ii]);
-      }
-    }
+  stage_kqw(sm, a, tok0, c, tid, lane);
+  __syncthreads();
+  form_lm_bf16(sm, n, wave, lane);
+  // W~ = diag(g_n / g) W (rows past the end are zero: w staged as 0)
+  for (int idx = tid; idx < CH * DK; idx += NT) {
+    const int t = idx / DK, d = idx % DK;
+    sm.x[t * PX + d] = sm.fn[t] * bf2f(sm.w[t * PK + d]);
   }
   __syncthreads();
-  if (a.dS0)
-    for (int idx = tid; idx < DK * DVS; idx += NT) {
-      const int d = idx / DVS, cc = idx % DVS;
-      a.dS0[(bh * DK + d) * dv + col0 + cc] = sm.dS[d * PS + cc];
+  invert_blocks(sm.lm, sm.tb, wave, lane);
+  __syncthreads();
+  solve_upper<PX>(sm.lm, sm.tb, sm.x, DK / 16, wave, lane);
+  __syncthreads();
+  {
+    u32x4* zo = reinterpret_cast<u32x4*>(a.Z_ck + (bh * nch + c) * CH * DK);
+    for (int idx = tid; idx < CH * DK / 4; idx += NT) {
+      const int t = idx / (DK / 4), d = idx % (DK / 4) * 4;
+      const float* xr = sm.x + t * PX + d;
+      zo[idx] = u32x4{split_bf(xr[0]), split_bf(xr[1]), split_bf(xr[2]), split_bf(xr[3])};
     }
+  }
+  for (int s0 = 0; s0 < dv; s0 += 64) {
+    __syncthreads();  // the previous readers of x and o are done
+    {
+      // one 8-column piece per thread; rows past the end read the last row and
+      // are stored as zeros (no load under a branch)
+      static_assert(CH * 64 / 8 == NT, "one dO piece per thread");
+      const int t = tid / 8, c8 = tid % 8 * 8;
+      const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.dO) +
+                                                     (tok0 + t0 + min(t, n - 1)) * dv + s0 + c8);
+      float* orow = sm.o + t * PO + c8;
+      const bool ok = t < n;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        orow[2 * j] = ok ? __uint_as_float(u[j] << 16) : 0.f;
+        orow[2 * j + 1] = ok ? __uint_as_float(u[j] & 0xFFFF0000u) : 0.f;
+      }
+    }
+    __syncthreads();
+    // M^T dO (rows past the end zero)
+    for (int tile = wave; tile < 16; tile += NW) {
+      const int ib = tile >> 2, cb = tile & 3;
+      const f32x4 acc = mm_bf<false, true>(
+          zero4(), 16 * ib, CH, [&](int r, int k_) { return sm.mm[k_ * PC + 16 * ib + r]; },
+          [&](int k_, int cc) { return sm.o[k_ * PO + 16 * cb + cc]; }, lane);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) sm.x[(16 * ib + 4 * lg + ii) * PO + 16 * cb + lr] = acc[ii];
+    }
+    __syncthreads();
+    solve_upper<PO>(sm.lm, sm.tb, sm.x, 4, wave, lane);
+    __syncthreads();
+    {
+      const int t = tid / 8, c8 = tid % 8 * 8;
+      if (t < n) {
+        f32x4* dst = reinterpret_cast<f32x4*>(a.dv_out + (tok0 + t0 + t) * dv + s0 + c8);
+        const float* xr = sm.x + t * PO + c8;
+        dst[0] = f32x4{xr[0], xr[1], xr[2], xr[3]};
+        dst[1] = f32x4{xr[4], xr[5], xr[6], xr[7]};
+      }
+    }
+  }
+}
+
+// chunk_bwd_ds_kernel: the serial sweep, one workgroup of four wavefronts per
+// (b, h, 64 value columns); wavefront j owns value columns 16 j .. 16 j + 15
+// of the slice and holds that d_k x 16 slice of dS in registers, in the
+// accumulator layout of a 16x16 tile per 16 key channels.  From the last
+// chunk, per chunk: dR = P + Z dS_out (written to dv_out, where the tile
+// kernel reads it as dR), dS_out stored for the tile kernel, then
+// dS_in = g_n dS_out + Q^T (g dO) - K^T (g dR).  Z, k, q and the decay of the
+// next chunk are loaded while the current chunk runs and staged into the
+// other half of a double buffer after it; P and dO are loaded into registers
+// a step ahead.  Every global access is issued unconditionally: loads and
+// stores of a partial chunk go through buffer resources sized to its n
+// tokens, so rows past the end read as zero and their stores are dropped
+// (a load under a branch makes the wavefront wait for it where the branches
+// join).  Products run on v_mfma_f32_16x16x32_bf16: Z and dS as split pairs
+// (three instructions), q and k exact against the split fp32 side (two).
+// The 32 k-slots of one instruction are taken as rows 4 g + i (i < 4) of the
+// first 16-block and 4 g + i - 4 of the second (g = lane / 16), in both
+// operands.
+constexpr int NTS = 256;  // threads of the serial sweep
+constexpr int DVS_S = 64; // value columns per workgroup of the serial sweep
+typedef short s16x4_lds __attribute__((ext_vector_type(4), address_space(3)));
+// rows r0 + 4 g + j (j < 4), column c0 + lane % 16 of a row-major bf16 array
+// of pitch ld in LDS, in one ds_read_b64_tr_b16 (within each group of 16
+// lanes, lane l receives element l % 4 of the 8-byte piece addressed by lane
+// 4 j + l / 4)
+__device__ __forceinline__ s16x4 read_tr(const uint16_t* p, int ld, int lane, int r0, int c0) {
+  const uint16_t* q = p + (r0 + 4 * (lane >> 4) + ((lane & 15) >> 2)) * ld + c0 + 4 * (lane & 3);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds*)(q));
+}
+__device__ __forceinline__ bf16x8 cat8(s16x4 lo, s16x4 hi) {
+  const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], y[0], y[1]});
+}
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ s16x4 hi4v(f32x4 v) {
+  const float x[4] = {v[0], v[1], v[2], v[3]};
+  return hi4(x);
+}
+__device__ __forceinline__ s16x4 lo4v(f32x4 v) {
+  const float x[4] = {v[0], v[1], v[2], v[3]};
+  return lo4(x);
+}
+// a buffer resource over nbytes from base: loads beyond read as zero,
+// stores beyond are dropped
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* base, long nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(nbytes), 0x00020000);
+}
+
+template <int DK>
+struct SmemS {
+  static constexpr int PZ = DK + 4;   // u32 row pitch of Z: rows 16 banks apart per four
+  static constexpr int PK = DK + 16;  // bf16 row pitch of k and q (transposing reads)
+  uint32_t z[2][CH * PZ];
+  uint16_t k[2][CH * PK], q[2][CH * PK];
+  float gam[2][CH];  // exp(G_t)
+};
+
+template <int DK>
+__global__ __launch_bounds__(NTS) void chunk_bwd_ds_kernel(BwdArgs a) {
+  using Sm = SmemS<DK>;
+  constexpr int PZ = Sm::PZ, PK = Sm::PK, ND = DK / 16, NS = DK / 32;
+  constexpr int ZV = CH * DK / 4 / NTS, KV = CH * DK / 8 / NTS;  // 16-byte pieces per thread
+  static_assert(ZV >= 1 && KV >= 1 && DVS_S == 16 * (NTS / 64), "serial sweep shape");
+  static_assert(offsetof(Sm, z) % 16 == 0 && offsetof(Sm, k) % 16 == 0 && offsetof(Sm, q) % 16 == 0 &&
+                    offsetof(Sm, gam) % 16 == 0 && (CH * PZ * 4) % 16 == 0 && (CH * PK * 2) % 16 == 0,
+                "16-byte LDS rows");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  DN_LDS_POISON(smem_raw, sizeof(Sm));
+  Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4;
+  const int T = a.T, dv = a.dv;
+  const int nch = (T + CH - 1) / CH;
+  const int nsl = dv / DVS_S;
+  // the value slices of one head on one XCD (consecutive workgroup ids go to
+  // the 8 XCDs in turn), so that they share its L2 copy of Z, k and q
+  const unsigned G = gridDim.x;
+  const unsigned lin = G % 8 == 0 ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  const long bh = lin / nsl;
+  const int col = static_cast<int>(lin % nsl) * DVS_S + 16 * wave + (lane & 15);
+  const long tok0 = bh * T;
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k);
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+  const uint16_t* og = static_cast<const uint16_t*>(a.dO);
+  const float* alg = static_cast<const float*>(a.g.alpha);
+  auto nof = [&](int c) { return min(CH, T - c * CH); };
+  // this lane's rows 4 g + i of a [CH][dv] array: byte offset of row 4 g and
+  // column col; the rows 16 ib + i are scalar offsets
+  const int loff = (4 * lg * dv + col);
+
+  u32x4 zr[ZV], kr[KV], qr[KV];
+  float al;
+  float pn[4][4];     // P of this lane's rows
+  uint16_t on[4][4];  // dO of this lane's rows, bf16
+  // Z, k, q and alpha of chunk c, issued at the start of a step and used when
+  // it ends; the decay first, so that waiting for the group waits for nothing
+  // issued later
+  auto fetch_a = [&](int c) {
+    const int t0 = c * CH, n = nof(c);
+    al = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(brsrc(alg + tok0 + t0, 4 * n), 4 * lane, 0, 0));
+    const u32x4* zs = reinterpret_cast<const u32x4*>(a.Z_ck + (bh * nch + c) * CH * DK);
+#pragma unroll
+    for (int m = 0; m < ZV; ++m) zr[m] = zs[tid + NTS * m];
+    const auto rk = brsrc(kg + (tok0 + t0) * DK, 2l * n * DK), rq = brsrc(qg + (tok0 + t0) * DK, 2l * n * DK);
+#pragma unroll
+    for (int m = 0; m < KV; ++m) {
+      kr[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * tid, 16 * NTS * m, 0));
+      qr[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * tid, 16 * NTS * m, 0));
+    }
+  };
+  // P and dO of chunk c, issued just before a step ends and used halfway
+  // through the next
+  auto fetch_b = [&](int c) {
+    const int t0 = c * CH, n = nof(c);
+    const auto rp = brsrc(a.dv_out + (tok0 + t0) * dv, 4l * n * dv);
+    const auto ro = brsrc(og + (tok0 + t0) * dv, 2l * n * dv);
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int so = (16 * ib + i) * dv;
+        pn[ib][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, 4 * loff, 4 * so, 0));
+        on[ib][i] = __builtin_amdgcn_raw_buffer_load_b16(ro, 2 * loff, 2 * so, 0);
+      }
+  };
+  // stage the fetched chunk (n tokens) into half b of the double buffer
+  auto put = [&](int b, int n) {
+#pragma unroll
+    for (int m = 0; m < ZV; ++m) {
+      const int idx = tid + NTS * m, t = idx / (DK / 4), d = idx % (DK / 4) * 4;
+      *reinterpret_cast<u32x4*>(&sm.z[b][t * PZ + d]) = zr[m];
+    }
+#pragma unroll
+    for (int m = 0; m < KV; ++m) {
+      const int idx = tid + NTS * m, t = idx / (DK / 8), d = idx % (DK / 8) * 8;
+      *reinterpret_cast<u32x4*>(&sm.k[b][t * PK + d]) = kr[m];
+      *reinterpret_cast<u32x4*>(&sm.q[b][t * PK + d]) = qr[m];
+    }
+    if (wave == 0) {
+      // inclusive prefix sum of log(alpha) over the chunk (padding: alpha = 1)
+      float l = lane < n ? logf(al) : 0.f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(l, off);
+        if (lane >= off) l += y;
+      }
+      sm.gam[b][lane] = expf(l);
+    }
+  };
+
+  f32x4 dS[ND];
+  {
+    // dS_T (no dS_T: an empty resource, every load reads zero)
+    const auto rt = brsrc(a.dS_T ? a.dS_T + bh * DK * dv : nullptr, a.dS_T ? 4l * DK * dv : 0);
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dS[db][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rt, 4 * loff, 4 * (16 * db + i) * dv, 0));
+  }
+  fetch_a(nch - 1);
+  put((nch - 1) & 1, nof(nch - 1));
+  fetch_b(nch - 1);
+  __syncthreads();
+  for (int c = nch - 1; c >= 0; --c) {
+    const int b = c & 1, t0 = c * CH, n = nof(c);
+    // the next chunk's loads (at the first chunk, harmless repeats of it:
+    // every step issues the same loads, so no wait depends on the path)
+    const int cn = max(c - 1, 0);
+    fetch_a(cn);
+    // keep the scheduler from sinking these loads towards their use
+    __builtin_amdgcn_sched_barrier(0);
+    // dS_out^T [dv][dk] of the chunk for the tile kernel: each lane's four key
+    // channels are one 16-byte piece
+    {
+      f32x4* dsk = reinterpret_cast<f32x4*>(a.dS_ck + ((bh * nch + c) * dv + col) * DK + 4 * lg);
+#pragma unroll
+      for (int db = 0; db < ND; ++db) dsk[4 * db] = dS[db];
+    }
+    // dS_out as split pairs
+    bf16x8 sh[NS], sl[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      sh[s] = cat8(hi4v(dS[2 * s]), hi4v(dS[2 * s + 1]));
+      sl[s] = cat8(lo4v(dS[2 * s]), lo4v(dS[2 * s + 1]));
+    }
+    // Y = Z dS_out; dR = P + Y (to dv_out); the g-scaled split operands of
+    // the dS_in products
+    const uint32_t* zb = sm.z[b];
+    const auto rdr = brsrc(a.dv_out + (tok0 + t0) * dv, 4l * n * dv);
+    f32x4 yt[4];
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      f32x4 y = zero4();
+      const uint32_t* zrow = zb + (16 * ib + (lane & 15)) * PZ + 4 * lg;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const u32x4 z0 = *reinterpret_cast<const u32x4*>(zrow + 32 * s);
+        const u32x4 z1 = *reinterpret_cast<const u32x4*>(zrow + 32 * s + 16);
+        s16x4 h0, l0, h1, l1;
+        split4(z0[0], z0[1], z0[2], z0[3], h0, l0);
+        split4(z1[0], z1[1], z1[2], z1[3], h1, l1);
+        const bf16x8 zh = cat8(h0, h1), zl = cat8(l0, l1);
+        y = mfma32(zh, sh[s], mfma32(zh, sl[s], mfma32(zl, sh[s], y)));
+      }
+      yt[ib] = y;
+    }
+    // P and dO are used only from here
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 oh[2], ol[2], rh[2], rl[2];
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      const f32x4 y = yt[ib];
+      const f32x4 g4 = *reinterpret_cast<const f32x4*>(&sm.gam[b][16 * ib + 4 * lg]);
+      f32x4 go, gr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // rows past the end: P and dO read as zero, Z's rows are zero
+        const float dr = pn[ib][i] + y[i];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dr), rdr, 4 * loff, 4 * (16 * ib + i) * dv, 0);
+        go[i] = g4[i] * bf2f(on[ib][i]);
+        gr[i] = -g4[i] * dr;
+      }
+      // tile ib is half ib % 2 of the 32-token operand ib / 2
+      const s16x4 goh = hi4v(go), gol = lo4v(go), grh = hi4v(gr), grl = lo4v(gr);
+      if (ib % 2 == 0) {
+        oh[ib / 2] = cat8(goh, goh);
+        ol[ib / 2] = cat8(gol, gol);
+        rh[ib / 2] = cat8(grh, grh);
+        rl[ib / 2] = cat8(grl, grl);
+      } else {
+        auto sethi = [](bf16x8& v, s16x4 h) {
+          const u32x2 x = __builtin_bit_cast(u32x2, h);
+          u32x4 u = __builtin_bit_cast(u32x4, v);
+          u[2] = x[0], u[3] = x[1];
+          v = __builtin_bit_cast(bf16x8, u);
+        };
+        sethi(oh[ib / 2], goh);
+        sethi(ol[ib / 2], gol);
+        sethi(rh[ib / 2], grh);
+        sethi(rl[ib / 2], grl);
+      }
+    }
+    // dS_in = g_n dS_out + Q^T (g dO) - K^T (g dR)
+    const float gn = sm.gam[b][CH - 1];
+    const uint16_t *qb = sm.q[b], *kb = sm.k[b];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      f32x4 acc = gn * dS[db];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 qa = cat8(read_tr(qb, PK, lane, 32 * s, 16 * db), read_tr(qb, PK, lane, 32 * s + 16, 16 * db));
+        const bf16x8 ka = cat8(read_tr(kb, PK, lane, 32 * s, 16 * db), read_tr(kb, PK, lane, 32 * s + 16, 16 * db));
+        acc = mfma32(qa, oh[s], mfma32(qa, ol[s], acc));
+        acc = mfma32(ka, rh[s], mfma32(ka, rl[s], acc));
+      }
+      dS[db] = acc;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_b(cn);
+    __builtin_amdgcn_sched_barrier(0);
+    put(b ^ 1, nof(cn));
+    __syncthreads();
+  }
+  if (a.dS0)
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.dS0[(bh * DK + 16 * db + 4 * lg + i) * dv + col] = dS[db][i];
 }
 
 template <int DK>
@@ -1116,8 +1395,33 @@ __global__ __launch_bounds__(NT) void chunk_bwd_tiles_kernel(BwdArgs a) {
   auto qf = [&](int t, int d) { return bf2f(sm.q[t * PK + d]); };
   auto wf = [&](int t, int d) { return bf2f(sm.w[t * PK + d]); };
 
+  // the value slices' operands, each fetched into registers one slice ahead
+  // (the first while L and M are formed): S_in rows sd, columns sc..; dS_out
+  // (stored transposed, [dv][dk] per chunk) SV key channels from tdk of
+  // column tcol; E, dR (= dV) and dO of token xt, columns xc..  Rows past the end
+  // read the last row and are stored as zeros (no load under a branch).
+  constexpr int SV = DK * VS / NT, XV = CH * VS / NT;
+  const int sd = tid * SV / VS, sc = tid * SV % VS;
+  const int xt = tid * XV / VS, xc = tid * XV % VS;
+  const int tcol = tid * SV / DK, tdk = tid * SV % DK;
+  const bool xok = xt < n;
+  const int nsl = dv / VS;
+  float pS[SV], pdS[SV], pE[XV], pR[XV], pO[XV];
+  auto fetch_slice = [&](int s) {
+    const int col0 = s * VS;
+    const long srow = ((bh * nch + c) * DK + sd) * dv + col0 + sc;
+    const long trow = ((bh * nch + c) * dv + col0 + tcol) * DK + tdk;
+    const long xrow = (tok0 + t0 + min(xt, n - 1)) * dv + col0 + xc;
+    load_vec<float, SV>(a.S_ck, srow, true, pS);
+    load_vec<float, SV>(a.dS_ck, trow, true, pdS);
+    load_vec<float, XV>(a.E, xrow, true, pE);
+    load_vec<float, XV>(a.dv_out, xrow, true, pR);  // dR = dV
+    load_vec<uint16_t, XV>(a.dO, xrow, true, pO);
+  };
+
   stage_kqw(sm, a, tok0, c, tid, lane);
   __syncthreads();
+  fetch_slice(0);
   form_lm_bf16(sm, n, wave, lane);  // L, M (for the decay's gradient)
 
   // the contractions over the value columns, 32 at a time: dL = -dR E^T,
@@ -1128,36 +1432,27 @@ __global__ __launch_bounds__(NT) void chunk_bwd_tiles_kernel(BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < TPW; ++k) akh[k] = aqh[k] = atw[k] = zero4();
   float sdot = 0.f;
-  constexpr int SV = DK * VS / NT, XV = CH * VS / NT;
-  for (int s = 0; s < dv / VS; ++s) {
-    const int col0 = s * VS;
+  for (int s = 0; s < nsl; ++s) {
     __syncthreads();  // the previous slice's readers are done
-    {
-      const int sd = tid * SV / VS, sc = tid * SV % VS;
-      const int xt = tid * XV / VS, xc = tid * XV % VS;
-      const bool xok = xt < n;
-      const long srow = ((bh * nch + c) * DK + sd) * dv + col0 + sc;
-      const long xrow = (tok0 + t0 + xt) * dv + col0 + xc;
-      float sv[SV], dsv[SV], ev[XV], yv[XV], xv[XV];
-      load_vec<float, SV>(a.S_ck, srow, true, sv);
-      load_vec<float, SV>(a.dS_ck, srow, true, dsv);
-      load_vec<float, XV>(a.E, xrow, xok, ev);
-      load_vec<float, XV>(a.dv_out, xrow, xok, yv);  // dR = dV
-      load_vec<uint16_t, XV>(a.dO, xrow, xok, xv);
 #pragma unroll
-      for (int j = 0; j < SV; ++j) {
-        sm.S[sd * PS + sc + j] = sv[j];
-        sm.dS[sd * PS + sc + j] = dsv[j];
-        sdot = fmaf(sv[j], dsv[j], sdot);
-      }
-#pragma unroll
-      for (int j = 0; j < XV; ++j) {
-        sm.e[xt * PS + xc + j] = ev[j];
-        sm.y[xt * PS + xc + j] = yv[j];
-        sm.x[xt * PS + xc + j] = xv[j];
-      }
+    for (int j = 0; j < SV; ++j) {
+      sm.S[sd * PS + sc + j] = pS[j];
+      sm.dS[(tdk + j) * PS + tcol] = pdS[j];
     }
+#pragma unroll
+    for (int j = 0; j < XV; ++j) {
+      sm.e[xt * PS + xc + j] = xok ? pE[j] : 0.f;
+      sm.y[xt * PS + xc + j] = xok ? pR[j] : 0.f;
+      sm.x[xt * PS + xc + j] = xok ? pO[j] : 0.f;
+    }
+    // the next slice (at the last, a harmless repeat of it)
+    fetch_slice(min(s + 1, nsl - 1));
     __syncthreads();
+    {
+      // <S_in, dS_out> over this thread's piece of the slice
+#pragma unroll
+      for (int j = 0; j < SV; ++j) sdot = fmaf(sm.S[sd * PS + sc + j], sm.dS[sd * PS + sc + j], sdot);
+    }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int tile = wave + 8 * k, tr = tile >> 2, tc = tile & 3;
@@ -1652,31 +1947,26 @@ hipError_t launch_chunk_bwd_state(const BwdArgs& a, int io_bf16, bool channel, h
 }
 
 template <class Sm, class K>
-static hipError_t launch_lds(K kern, unsigned grid, const BwdArgs& a, hipStream_t st) {
+static hipError_t launch_lds(K kern, unsigned grid, const BwdArgs& a, hipStream_t st, int threads = bwd::NT) {
   static_assert(sizeof(Sm) <= 160 * 1024, "LDS budget");
   const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              static_cast<int>(sizeof(Sm)));
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(bwd::NT), sizeof(Sm), st, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), sizeof(Sm), st, a);
   return hipGetLastError();
 }
-// The serial sweep in value slices of 64 columns where they fill the
-// compute units, else of 32 or 16 (more, narrower slices finish sooner while
-// they fit on the device at once); the tile kernel one workgroup per chunk
+// Z and P for every chunk, the serial sweep in 64-column value slices, the
+// tile kernel one workgroup per chunk
 template <int DK>
 static hipError_t launch_bwd_split_t(const BwdArgs& a, hipStream_t st) {
   const long bh = static_cast<long>(a.B) * a.H;
   const long nch = (a.T + bwd::CH - 1) / bwd::CH;
-  if (a.dv % 32 != 0) return hipErrorInvalidValue;
-  const int dvs = 2 * bh * (a.dv / 32) <= BWD_CU_COUNT                     ? 16
-                  : a.dv % 64 == 0 && bh * (a.dv / 64) >= BWD_CU_COUNT ? 64
-                                                                        : 32;
-  const unsigned grid = static_cast<unsigned>(bh * (a.dv / dvs));
-  const hipError_t err =
-      dvs == 16   ? launch_lds<bwd::SmemD<DK, 16>>(bwd::chunk_bwd_ds_kernel<DK, 16>, grid, a, st)
-      : dvs == 64 ? launch_lds<bwd::SmemD<DK, 64>>(bwd::chunk_bwd_ds_kernel<DK, 64>, grid, a, st)
-                  : launch_lds<bwd::SmemD<DK, 32>>(bwd::chunk_bwd_ds_kernel<DK, 32>, grid, a, st);
+  if (a.dv % bwd::DVS_S != 0 || a.Z_ck == nullptr || a.dS_ck == nullptr) return hipErrorInvalidValue;
+  hipError_t err = launch_lds<bwd::SmemZ<DK>>(bwd::chunk_bwd_zp_kernel<DK>, static_cast<unsigned>(bh * nch), a, st);
+  if (err != hipSuccess) return err;
+  err = launch_lds<bwd::SmemS<DK>>(bwd::chunk_bwd_ds_kernel<DK>, static_cast<unsigned>(bh * (a.dv / bwd::DVS_S)),
+                                   a, st, bwd::NTS);
   if (err != hipSuccess) return err;
   return launch_lds<bwd::SmemT<DK>>(bwd::chunk_bwd_tiles_kernel<DK>, static_cast<unsigned>(bh * nch), a, st);
 }

@@ -909,12 +909,13 @@ DN_EXPORT int dn_chunk_fwd_noalloc(const dn_desc* d, const void* q, const void* 
 // Chunked backward.  Workspace, each part on a 256-byte boundary: w
 // [B, H, T, dk] (fp32, bf16 with bf16 io and scalar decay), S_ck [B, H, nch,
 // dk, dv], E [B, H, T, dv], dw_acc [B, H, T, dk], dG ([B, H, T]; channel decay
-// [B, H, T, dk]), on the split path dS_ck [B, H, nch, dk, dv], then for the
+// [B, H, T, dk]), on the split path dS_ck [B, H, nch, dv, dk] and Z_ck
+// [B, H, nch, 64, dk] (split bf16 pairs, 4 bytes each), then for the
 // gains with a statistic the statistic entering every chunk ([B, H, nch, dk];
 // KDN_ISO [B, H, nch]), and the workspace of the gain scans (as for
 // dn_gain_prep); fp32 where not said.
 struct BwdLayout {
-  size_t w, sck, e, dw, dg, dsck, aux, prep, total;
+  size_t w, sck, e, dw, dg, dsck, zck, aux, prep, total;
 };
 
 // The split backward: bf16 io, scalar decay, the gains the forward chunk
@@ -939,7 +940,8 @@ static BwdLayout bwd_layout(const dn_desc* d) {
   L.dw = round256(L.e + bht * d->dv * 4);
   L.dg = round256(L.dw + bht * d->dk * 4);
   L.dsck = round256(L.dg + bht * gdim * 4);
-  L.aux = round256(L.dsck + (bwd_split(d) ? bh * nch * d->dk * d->dv * 4 : 0));
+  L.zck = round256(L.dsck + (bwd_split(d) ? bh * nch * d->dk * d->dv * 4 : 0));
+  L.aux = round256(L.zck + (bwd_split(d) ? bh * nch * 64 * d->dk * 4 : 0));
   L.prep = round256(L.aux + (has_aux_state(d) ? bh * nch * aux_per_head(d) * 4 : 0));
   L.total = L.prep + prep_layout(d).total;
   return L;
@@ -1107,6 +1109,7 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
     if (dn::launch_chunk_fwd_bf16_scalar(ca, d->gain, s) != hipSuccess) return DN_ERR_HIP;
     b.ck_given = 1;
     b.dS_ck = reinterpret_cast<float*>(wb + lay.dsck);
+    b.Z_ck = reinterpret_cast<uint32_t*>(wb + lay.zck);
     if (dn::launch_chunk_bwd_split(b, s) != hipSuccess) return DN_ERR_HIP;
   } else if (dn::launch_chunk_bwd_state(b, d->io == DN_BF16, chan, s) != hipSuccess) {
     return DN_ERR_HIP;

@@ -159,13 +159,18 @@ struct BwdArgs {
   float* dw_acc;
   float* dG;
   float* dS0;
-  // the split backward (launch_chunk_bwd_split): dS_out of every chunk
-  // [B, H, nch, dk, dv], written by its serial kernel for its tile kernel
+  // the split backward (launch_chunk_bwd_split): dS_out of every chunk,
+  // transposed [B, H, nch, dv, dk], written by its serial kernel for its tile
+  // kernel,
+  // and Z = (I + L)^-T W~ of every chunk [B, H, nch, 64, dk] as split bf16
+  // pairs (hi in the low half)
   float* dS_ck = nullptr;
+  uint32_t* Z_ck = nullptr;
 };
 hipError_t launch_chunk_bwd_state(const BwdArgs& a, int io_bf16, bool channel, hipStream_t st);
 // bf16 io, scalar decay, S_ck and E written by the forward chunk kernel, dv a
-// multiple of 32: the serial sweep for dS, then one workgroup per chunk for
+// multiple of 64: the dS-independent solves of every chunk (Z into Z_ck, P
+// into dv_out), the serial sweep for dS, then one workgroup per chunk for
 // the per-(token, key) gradients, which it writes (no accumulation: dq,
 // dk_out, dw_acc and dG need no zeroing)
 hipError_t launch_chunk_bwd_split(const BwdArgs& a, hipStream_t st);

@@ -286,14 +286,15 @@ def test_chunk_bwd_rejects_bad_arguments():
     assert call(d, ws_=outs[0]) == -8  # workspace on top of dq
     # the workspace: w, S_ck, E, dw, dG (each on a 256-byte boundary); with
     # bf16 io and scalar decay but for the KDN gains (the split path) also
-    # dS_out of every chunk
+    # dS_out and Z of every chunk
     r256 = lambda x: (x + 255) // 256 * 256
     bht, nch = 2 * 3 * 100, 2
     size = r256(r256(r256(r256(bht * 128 * 4) + 6 * nch * 128 * 128 * 4) + bht * 128 * 4) + bht * 128 * 4) + bht * 4
-    dsck = 6 * nch * 128 * 128 * 4
-    assert L.dn_chunk_bwd_workspace(ctypes.byref(d)) == r256(r256(size) + dsck)
+    dsck, zck = 6 * nch * 128 * 128 * 4, 6 * nch * 64 * 128 * 4
+    split = r256(r256(r256(size) + dsck) + zck)
+    assert L.dn_chunk_bwd_workspace(ctypes.byref(d)) == split
     dp = _desc(B=2, H=3, T=100, gain="pgdn")
-    assert L.dn_chunk_bwd_workspace(ctypes.byref(dp)) == r256(r256(size) + dsck) + 6 * nch * 128 * 4
+    assert L.dn_chunk_bwd_workspace(ctypes.byref(dp)) == split + 6 * nch * 128 * 4
     # channel decay: dG per (token, channel); KDN / KDN_ISO: the statistic per chunk
     sizec = r256(r256(r256(r256(bht * 128 * 4) + 6 * nch * 128 * 128 * 4) + bht * 128 * 4) + bht * 128 * 4) + bht * 128 * 4
     dc = _desc(B=2, H=3, T=100, decay="channel")
