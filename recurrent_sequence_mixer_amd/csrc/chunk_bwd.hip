@@ -205,6 +205,10 @@ __device__ __forceinline__ uint32_t split_bf(float v) {
   const uint16_t hi = f2bf(v);
   return static_cast<uint32_t>(hi) | (static_cast<uint32_t>(f2bf(v - bf2f(hi))) << 16);
 }
+// two bf16 in one word, a in the low half
+__device__ __forceinline__ uint32_t pack16(uint16_t a, uint16_t b) {
+  return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+}
 // the hi and lo halves of four split words as two bf16x4 operands
 __device__ __forceinline__ void split4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, s16x4& hi,
                                        s16x4& lo) {
@@ -1359,11 +1363,13 @@ template <int DK>
 struct SmemT {
   static constexpr int DKV = DK;
   static constexpr int VS = 32;      // value columns per slice of the contractions
-  static constexpr int PS = VS + 4;  // row pitch of [x][VS] fp32 arrays
-  static constexpr int PK = DK + 2;
+  static constexpr int PH = VS + 8;  // bf16 row pitch of the split planes (16-byte pieces)
+  static constexpr int PK = DK + 16; // bf16 row pitch of k, q, w (transposing reads)
   uint16_t k[CH * PK], q[CH * PK], w[CH * PK];
-  float S[DK * PS], dS[DK * PS];             // S_in and dS_out, one slice
-  float e[CH * PS], x[CH * PS], y[CH * PS];  // E, dO and dR, one slice
+  // one value slice as bf16 planes: hi = bf16(v), lo = bf16(v - hi)
+  uint16_t Sh[DK * PH], Sl[DK * PH], dSh[DK * PH], dSl[DK * PH];  // S_in, dS_out [key][col]
+  uint16_t eh[CH * PH], el[CH * PH], yh[CH * PH], yl[CH * PH];    // E, dR [token][col]
+  uint16_t xh[CH * PH];                                           // dO (bf16)
   float lm[CH * PC];  // L, then D o dL as split words
   float mm[CH * PC];  // M, then D o dM as split words
   float G[CH], gam[CH], fn[CH], sg[CH];
@@ -1372,13 +1378,15 @@ struct SmemT {
 template <int DK>
 __global__ __launch_bounds__(NT) void chunk_bwd_tiles_kernel(BwdArgs a) {
   using Sm = SmemT<DK>;
-  constexpr int PK = Sm::PK, PS = Sm::PS, VS = Sm::VS;
+  constexpr int PK = Sm::PK, VS = Sm::VS, PH = Sm::PH;
   constexpr int ND = DK / 16;
   constexpr int TPW = 4 * ND / NW;  // [token][key] tiles per wavefront
   static_assert(TPW * NW == 4 * ND, "key tiles per wavefront");
-  static_assert(offsetof(Sm, S) % 16 == 0 && offsetof(Sm, dS) % 16 == 0 && offsetof(Sm, e) % 16 == 0 &&
-                    offsetof(Sm, x) % 16 == 0 && offsetof(Sm, y) % 16 == 0 && offsetof(Sm, lm) % 16 == 0 &&
-                    offsetof(Sm, mm) % 16 == 0,
+  static_assert(offsetof(Sm, Sh) % 16 == 0 && offsetof(Sm, Sl) % 16 == 0 && offsetof(Sm, dSh) % 16 == 0 &&
+                    offsetof(Sm, dSl) % 16 == 0 && offsetof(Sm, eh) % 16 == 0 && offsetof(Sm, el) % 16 == 0 &&
+                    offsetof(Sm, yh) % 16 == 0 && offsetof(Sm, yl) % 16 == 0 && offsetof(Sm, xh) % 16 == 0 &&
+                    offsetof(Sm, lm) % 16 == 0 && offsetof(Sm, mm) % 16 == 0 && (PH * 2) % 16 == 0 &&
+                    (PK * 2) % 8 == 0,
                 "16-byte LDS rows");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   DN_LDS_POISON(smem_raw, sizeof(Sm));
@@ -1432,60 +1440,87 @@ __global__ __launch_bounds__(NT) void chunk_bwd_tiles_kernel(BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < TPW; ++k) akh[k] = aqh[k] = atw[k] = zero4();
   float sdot = 0.f;
+  // the split planes of one value: hi = bf16(v) (RNE), lo = bf16(v - hi)
+  auto hl = [](float v, uint16_t& h, uint16_t& l) {
+    h = f2bf(v);
+    l = f2bf(v - bf2f(h));
+  };
+  // 8 consecutive k (value columns 8 g .. 8 g + 7 of the slice) of a plane's
+  // row, as one v_mfma_f32_16x16x32_bf16 operand
+  auto frag = [&](const uint16_t* plane, int row) {
+    return *reinterpret_cast<const bf16x8*>(plane + row * PH + 8 * lg);
+  };
   for (int s = 0; s < nsl; ++s) {
     __syncthreads();  // the previous slice's readers are done
+    {
+      static_assert((SV == 8 || SV == 4) && XV == 4, "staging pieces");
+      uint16_t h[SV], l[SV];
 #pragma unroll
-    for (int j = 0; j < SV; ++j) {
-      sm.S[sd * PS + sc + j] = pS[j];
-      sm.dS[(tdk + j) * PS + tcol] = pdS[j];
-    }
+      for (int j = 0; j < SV; ++j) hl(pS[j], h[j], l[j]);
+      auto stS = [&](uint16_t* plane, const uint16_t (&v)[SV]) {
+        if constexpr (SV == 8)
+          *reinterpret_cast<u32x4*>(&plane[sd * PH + sc]) =
+              u32x4{pack16(v[0], v[1]), pack16(v[2], v[3]), pack16(v[4], v[5]), pack16(v[6], v[7])};
+        else
+          *reinterpret_cast<u32x2*>(&plane[sd * PH + sc]) = u32x2{pack16(v[0], v[1]), pack16(v[2], v[3])};
+      };
+      stS(sm.Sh, h);
+      stS(sm.Sl, l);
 #pragma unroll
-    for (int j = 0; j < XV; ++j) {
-      sm.e[xt * PS + xc + j] = xok ? pE[j] : 0.f;
-      sm.y[xt * PS + xc + j] = xok ? pR[j] : 0.f;
-      sm.x[xt * PS + xc + j] = xok ? pO[j] : 0.f;
+      for (int j = 0; j < SV; ++j) {
+        uint16_t hh, ll;
+        hl(pdS[j], hh, ll);
+        sm.dSh[(tdk + j) * PH + tcol] = hh;
+        sm.dSl[(tdk + j) * PH + tcol] = ll;
+      }
+      uint16_t eh4[XV], el4[XV], yh4[XV], yl4[XV], xh4[XV];
+#pragma unroll
+      for (int j = 0; j < XV; ++j) {
+        hl(xok ? pE[j] : 0.f, eh4[j], el4[j]);
+        hl(xok ? pR[j] : 0.f, yh4[j], yl4[j]);
+        xh4[j] = xok ? f2bf(pO[j]) : 0;  // dO is a bf16 number
+      }
+      auto st4 = [&](uint16_t* plane, const uint16_t (&v)[XV]) {
+        *reinterpret_cast<u32x2*>(&plane[xt * PH + xc]) = u32x2{pack16(v[0], v[1]), pack16(v[2], v[3])};
+      };
+      st4(sm.eh, eh4);
+      st4(sm.el, el4);
+      st4(sm.yh, yh4);
+      st4(sm.yl, yl4);
+      st4(sm.xh, xh4);
     }
     // the next slice (at the last, a harmless repeat of it)
     fetch_slice(min(s + 1, nsl - 1));
     __syncthreads();
     {
-      // <S_in, dS_out> over this thread's piece of the slice
+      // <S_in, dS_out> over this thread's piece of the slice (hi + lo within
+      // 2^-17 of each value)
 #pragma unroll
-      for (int j = 0; j < SV; ++j) sdot = fmaf(sm.S[sd * PS + sc + j], sm.dS[sd * PS + sc + j], sdot);
+      for (int j = 0; j < SV; ++j) {
+        const int o = sd * PH + sc + j;
+        sdot = fmaf(bf2f(sm.Sh[o]) + bf2f(sm.Sl[o]), bf2f(sm.dSh[o]) + bf2f(sm.dSl[o]), sdot);
+      }
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int tile = wave + 8 * k, tr = tile >> 2, tc = tile & 3;
       if (tr < tc) continue;  // uniform
-#pragma unroll
-      for (int k0 = 0; k0 < VS; k0 += 16) {
-        const int k_ = k0 + 4 * lg;
-        float ev[4], yv[4], xv[4];
-        ld4(ev, &sm.e[(16 * tc + lr) * PS + k_]);
-        ld4(yv, &sm.y[(16 * tr + lr) * PS + k_]);
-        ld4(xv, &sm.x[(16 * tr + lr) * PS + k_]);
-        const s16x4 eh = hi4(ev), el = lo4(ev), yh = hi4(yv), xh = hi4(xv);
-        al[k] = mfma16(yh, eh, mfma16(yh, el, mfma16(lo4(yv), eh, al[k])));
-        am[k] = mfma16(xh, eh, mfma16(xh, el, am[k]));
-      }
+      const bf16x8 eh = frag(sm.eh, 16 * tc + lr), el = frag(sm.el, 16 * tc + lr);
+      const bf16x8 yh = frag(sm.yh, 16 * tr + lr), yl = frag(sm.yl, 16 * tr + lr), xh = frag(sm.xh, 16 * tr + lr);
+      al[k] = mfma32(yh, eh, mfma32(yh, el, mfma32(yl, eh, al[k])));
+      am[k] = mfma32(xh, eh, mfma32(xh, el, am[k]));
     }
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
       const int tile = wave + NW * k, tb_ = tile / ND, db = tile % ND;
-#pragma unroll
-      for (int k0 = 0; k0 < VS; k0 += 16) {
-        const int k_ = k0 + 4 * lg;
-        float sv[4], dsv[4], yv[4], xv[4], ev[4];
-        ld4(sv, &sm.S[(16 * db + lr) * PS + k_]);
-        ld4(dsv, &sm.dS[(16 * db + lr) * PS + k_]);
-        ld4(yv, &sm.y[(16 * tb_ + lr) * PS + k_]);
-        ld4(xv, &sm.x[(16 * tb_ + lr) * PS + k_]);
-        ld4(ev, &sm.e[(16 * tb_ + lr) * PS + k_]);
-        const s16x4 sh = hi4(sv), sl = lo4(sv), dh = hi4(dsv), yh = hi4(yv), xh = hi4(xv), eh = hi4(ev);
-        akh[k] = mfma16(yh, sh, mfma16(yh, sl, mfma16(lo4(yv), sh, akh[k])));
-        aqh[k] = mfma16(xh, sh, mfma16(xh, sl, aqh[k]));
-        atw[k] = mfma16(eh, dh, mfma16(eh, lo4(dsv), mfma16(lo4(ev), dh, atw[k])));
-      }
+      const bf16x8 sh = frag(sm.Sh, 16 * db + lr), sl = frag(sm.Sl, 16 * db + lr);
+      const bf16x8 dh = frag(sm.dSh, 16 * db + lr), dl = frag(sm.dSl, 16 * db + lr);
+      const bf16x8 yh = frag(sm.yh, 16 * tb_ + lr), yl = frag(sm.yl, 16 * tb_ + lr);
+      const bf16x8 xh = frag(sm.xh, 16 * tb_ + lr);
+      const bf16x8 eh = frag(sm.eh, 16 * tb_ + lr), el = frag(sm.el, 16 * tb_ + lr);
+      akh[k] = mfma32(yh, sh, mfma32(yh, sl, mfma32(yl, sh, akh[k])));
+      aqh[k] = mfma32(xh, sh, mfma32(xh, sl, aqh[k]));
+      atw[k] = mfma32(eh, dh, mfma32(eh, dl, mfma32(el, dh, atw[k])));
     }
   }
   // dL/dG of the chunk end: g_n <S_in, dS_out>
@@ -1531,13 +1566,10 @@ __global__ __launch_bounds__(NT) void chunk_bwd_tiles_kernel(BwdArgs a) {
   for (int k = 0; k < TPW; ++k) {  // unrolled: the accumulators stay in registers
     const int tile = wave + NW * k, tb_ = tile / ND, db = tile % ND;
     f32x4 ask = zero4(), asq = zero4(), asw = zero4(), asw2 = zero4();
-    const uint16_t* wb = sm.w + 16 * db + lr;
-    const uint16_t* kb = sm.k + 16 * db + lr;
-    const uint16_t* qb = sm.q + 16 * db + lr;
 #pragma unroll 2
     for (int k0 = 0; k0 < 16 * (tb_ + 1); k0 += 16) {
       const int k_ = k0 + 4 * lg;
-      const s16x4 wv = bf4_col(wb + k_ * PK, PK);
+      const s16x4 wv = read_tr(sm.w, PK, lane, k0, 16 * db);
       const u32x4 lw = *reinterpret_cast<const u32x4*>(lmu + (16 * tb_ + lr) * PC + k_);
       const u32x4 mw = *reinterpret_cast<const u32x4*>(mmu + (16 * tb_ + lr) * PC + k_);
       s16x4 h, l;
@@ -1553,10 +1585,10 @@ __global__ __launch_bounds__(NT) void chunk_bwd_tiles_kernel(BwdArgs a) {
       const uint32_t* mc = mmu + k_ * PC + 16 * tb_ + lr;
       s16x4 h, l;
       split4(lc[0], lc[PC], lc[2 * PC], lc[3 * PC], h, l);
-      const s16x4 kv = bf4_col(kb + k_ * PK, PK);
+      const s16x4 kv = read_tr(sm.k, PK, lane, k0, 16 * db);
       asw = mfma16(l, kv, mfma16(h, kv, asw));
       split4(mc[0], mc[PC], mc[2 * PC], mc[3 * PC], h, l);
-      const s16x4 qv = bf4_col(qb + k_ * PK, PK);
+      const s16x4 qv = read_tr(sm.q, PK, lane, k0, 16 * db);
       asw2 = mfma16(l, qv, mfma16(h, qv, asw2));
     }
     asw += asw2;
