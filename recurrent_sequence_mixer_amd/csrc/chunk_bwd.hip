@@ -1022,7 +1022,18 @@ __global__ __launch_bounds__(NT) void chunk_bwd_zp_kernel(BwdArgs a) {
   const int t0 = c * CH, n = min(CH, T - t0);
   const long tok0 = bh * T;
 
+  // dO of a 64-column slice, one 8-column piece per thread, fetched into
+  // registers a slice ahead (the first with k, q, w); rows past the end read
+  // the last row and are staged as zeros (no load under a branch)
+  static_assert(CH * 64 / 8 == NT, "one dO piece per thread");
+  const int ot = tid / 8, oc8 = tid % 8 * 8;
+  u32x4 od;
+  auto fetch_o = [&](int s0) {
+    od = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.dO) + (tok0 + t0 + min(ot, n - 1)) * dv +
+                                         s0 + oc8);
+  };
   stage_kqw(sm, a, tok0, c, tid, lane);
+  fetch_o(0);
   __syncthreads();
   form_lm_bf16(sm, n, wave, lane);
   // W~ = diag(g_n / g) W (rows past the end are zero: w staged as 0)
@@ -1046,20 +1057,16 @@ __global__ __launch_bounds__(NT) void chunk_bwd_zp_kernel(BwdArgs a) {
   for (int s0 = 0; s0 < dv; s0 += 64) {
     __syncthreads();  // the previous readers of x and o are done
     {
-      // one 8-column piece per thread; rows past the end read the last row and
-      // are stored as zeros (no load under a branch)
-      static_assert(CH * 64 / 8 == NT, "one dO piece per thread");
-      const int t = tid / 8, c8 = tid % 8 * 8;
-      const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.dO) +
-                                                     (tok0 + t0 + min(t, n - 1)) * dv + s0 + c8);
-      float* orow = sm.o + t * PO + c8;
-      const bool ok = t < n;
+      float* orow = sm.o + ot * PO + oc8;
+      const bool ok = ot < n;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        orow[2 * j] = ok ? __uint_as_float(u[j] << 16) : 0.f;
-        orow[2 * j + 1] = ok ? __uint_as_float(u[j] & 0xFFFF0000u) : 0.f;
+        orow[2 * j] = ok ? __uint_as_float(od[j] << 16) : 0.f;
+        orow[2 * j + 1] = ok ? __uint_as_float(od[j] & 0xFFFF0000u) : 0.f;
       }
     }
+    // the next slice (at the last, a harmless repeat of it)
+    fetch_o(min(s0 + 64, dv - 64));
     __syncthreads();
     // M^T dO (rows past the end zero)
     for (int tile = wave; tile < 16; tile += NW) {
