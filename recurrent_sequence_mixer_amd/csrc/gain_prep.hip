@@ -26,14 +26,30 @@ template <> __device__ __forceinline__ float io_at<float>(const void* p, long i)
 }
 
 // The gains with a statistic (PGDN, KDN, isotropic KDN); the others take
-// gain_prep_tok_kernel below.
+// gain_prep_tok_kernel below.  The tokens are walked in blocks of TB: each
+// block's k (and per-channel decay and KDN omega) rows and per-token gates
+// are staged into LDS with 16-byte loads first, so that a block costs one
+// round trip to memory rather than one per token.
 template <typename IO, int DK, int GAIN, bool CHANNEL>
 __global__ __launch_bounds__(DK) void gain_prep_kernel(GainPrepArgs a) {
   constexpr int NW = DK / 64;
-  constexpr bool ISO = GAIN == GAIN_KDN_ISO;
-  constexpr bool AUX = GAIN == GAIN_PGDN || GAIN == GAIN_KDN || ISO;
+  constexpr bool ISO = GAIN == GAIN_KDN_ISO, KD = GAIN == GAIN_KDN, PG = GAIN == GAIN_PGDN;
+  constexpr bool AUX = PG || KD || ISO;
+  constexpr int TB = 128 / sizeof(IO);  // tokens per staged block: 16 KiB of k rows at d_k 128
+  constexpr int PV = 16 / sizeof(IO);   // elements per 16-byte piece
+  constexpr int NP = TB * DK / PV / DK; // pieces per thread and array
   __shared__ float s_part[2][2][NW];
+  __shared__ __align__(16) IO s_k[TB * DK];
+  __shared__ __align__(16) IO s_a[CHANNEL ? TB * DK : PV];  // per-channel decay
+  __shared__ __align__(16) IO s_o[KD ? TB * DK : PV];       // KDN omega
+  // per token: 0 alpha (scalar decay); 1 eta (PGDN) or r (KDN modes); 2
+  // alphaP (PGDN) or omega (isotropic KDN); 3 betaP (PGDN)
+  __shared__ float s_g[4][TB];
   DN_LDS_POISON(s_part, sizeof(s_part));
+  DN_LDS_POISON(s_k, sizeof(s_k));
+  DN_LDS_POISON(s_a, sizeof(s_a));
+  DN_LDS_POISON(s_o, sizeof(s_o));
+  DN_LDS_POISON(s_g, sizeof(s_g));
   const int d = threadIdx.x, wave = d >> 6, lane = d & 63;
   const long bh = blockIdx.x;
   const int h = static_cast<int>(bh % a.H);
@@ -41,62 +57,99 @@ __global__ __launch_bounds__(DK) void gain_prep_kernel(GainPrepArgs a) {
   const int C = a.C;
   float st = a.aux0 ? a.aux0[ISO ? bh : bh * DK + d] : 1.f;
   float G = 0.f;
-  const float mu = GAIN == GAIN_PGDN ? a.g.mu_log[h] : 0.f;
-  for (int t = 0; t < T; ++t) {
-    const long ti = bh * T + t;
-    if (t % C == 0) {
-      G = 0.f;
-      if (a.aux_chunk && AUX && (!ISO || d == 0))
-        a.aux_chunk[ISO ? bh * ((T + C - 1) / C) + t / C : (bh * ((T + C - 1) / C) + t / C) * DK + d] = st;
-    }
-    const float kk = io_at<IO>(a.k, ti * DK + d);
-    const float al = CHANNEL ? io_at<IO>(a.g.alpha, ti * DK + d)
-                             : static_cast<const float*>(a.g.alpha)[ti];
-    G += logf(al);
-    if (a.g_out) {
-      if (CHANNEL) a.g_out[ti * DK + d] = G;
-      else if (d == 0) a.g_out[ti] = G;
-    }
-    float pre = 0.f, red = 0.f, red2 = 0.f, wv = 0.f;
-    if (ISO) {
-      red = kk * kk;
-      red2 = al * al;
-    } else if (GAIN == GAIN_PGDN) {
-      st = pgdn_stat(st, a.g.alphaP[ti], a.g.betaP[ti], kk);
-      wv = a.g.eta[ti] * pgdn_scale(st, mu, a.g.log2x) * kk;
-    } else if (GAIN == GAIN_KDN) {
-      const float ph = kdn_predict(al, st, io_at<IO>(a.g.omega, ti * DK + d));
-      pre = ph * kk;
-      red = pre * kk;
-      st = kdn_update(ph, kk, a.g.mu_info / a.g.r[ti]);
-    }
-    if (GAIN == GAIN_KDN || ISO) {
-      const float s = wave_sum(red);
-      const float s2 = ISO && CHANNEL ? wave_sum(red2) : 0.f;
-      if (lane == 0) {
-        s_part[t & 1][0][wave] = s;
-        s_part[t & 1][1][wave] = s2;
-      }
-      __syncthreads();
-      float tot = 0.f, tot2 = 0.f;
+  const float mu = PG ? a.g.mu_log[h] : 0.f;
+  for (int tb0 = 0; tb0 < T; tb0 += TB) {
+    const int nb = min(TB, T - tb0);
+    const long r0 = bh * T + tb0;
+    __syncthreads();  // the previous block's readers are done
+    {
+      // every load unconditional: rows past the block's end read its last row
+      // (never used)
+      auto stage = [&](const void* src, IO* dst) {
+        u32x4 v[NP];
 #pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        tot += s_part[t & 1][0][i];
-        tot2 += s_part[t & 1][1][i];
-      }
-      if constexpr (ISO) {
-        const float bh_ = kdn_iso_predict(CHANNEL ? tot2 * (1.0f / DK) : al * al, st,
-                                          static_cast<const float*>(a.g.omega)[ti]);
-        wv = kdn_iso_beta(bh_, a.g.r[ti], tot) * kk;
-        st = kdn_iso_update(bh_, tot, a.g.mu_info / (DK * a.g.r[ti]));
-      } else {
-        wv = pre / (a.g.r[ti] + tot);
+        for (int m = 0; m < NP; ++m) {
+          const int i = d + DK * m, t = i / (DK / PV), c = i % (DK / PV) * PV;
+          v[m] = *reinterpret_cast<const u32x4*>(static_cast<const IO*>(src) + (r0 + min(t, nb - 1)) * DK + c);
+        }
+#pragma unroll
+        for (int m = 0; m < NP; ++m) {
+          const int i = d + DK * m, t = i / (DK / PV), c = i % (DK / PV) * PV;
+          *reinterpret_cast<u32x4*>(dst + t * DK + c) = v[m];
+        }
+      };
+      stage(a.k, s_k);
+      if constexpr (CHANNEL) stage(a.g.alpha, s_a);
+      if constexpr (KD) stage(a.g.omega, s_o);
+      for (int i = d; i < TB; i += DK) {
+        const long ti = r0 + min(i, nb - 1);
+        if constexpr (!CHANNEL) s_g[0][i] = static_cast<const float*>(a.g.alpha)[ti];
+        if constexpr (PG) {
+          s_g[1][i] = a.g.eta[ti];
+          s_g[2][i] = a.g.alphaP[ti];
+          s_g[3][i] = a.g.betaP[ti];
+        } else {
+          s_g[1][i] = a.g.r[ti];
+          if constexpr (ISO) s_g[2][i] = static_cast<const float*>(a.g.omega)[ti];
+        }
       }
     }
-    if (a.w_bf16)
-      a.w_bf16[ti * DK + d] = f2bf(wv);
-    else
-      a.w_out[ti * DK + d] = wv;
+    __syncthreads();
+    for (int tt = 0; tt < nb; ++tt) {
+      const int t = tb0 + tt;
+      const long ti = r0 + tt;
+      if (t % C == 0) {
+        G = 0.f;
+        if (a.aux_chunk && AUX && (!ISO || d == 0))
+          a.aux_chunk[ISO ? bh * ((T + C - 1) / C) + t / C : (bh * ((T + C - 1) / C) + t / C) * DK + d] = st;
+      }
+      const float kk = Elem<IO>::get(s_k[tt * DK + d]);
+      const float al = CHANNEL ? Elem<IO>::get(s_a[tt * DK + d]) : s_g[0][tt];
+      if (a.g_out) {
+        G += logf(al);
+        if (CHANNEL) a.g_out[ti * DK + d] = G;
+        else if (d == 0) a.g_out[ti] = G;
+      }
+      float pre = 0.f, red = 0.f, red2 = 0.f, wv = 0.f;
+      if (ISO) {
+        red = kk * kk;
+        red2 = al * al;
+      } else if (PG) {
+        st = pgdn_stat(st, s_g[2][tt], s_g[3][tt], kk);
+        wv = s_g[1][tt] * pgdn_scale(st, mu, a.g.log2x) * kk;
+      } else if (KD) {
+        const float ph = kdn_predict(al, st, Elem<IO>::get(s_o[tt * DK + d]));
+        pre = ph * kk;
+        red = pre * kk;
+        st = kdn_update(ph, kk, a.g.mu_info / s_g[1][tt]);
+      }
+      if (KD || ISO) {
+        const float sm = wave_sum(red);
+        const float s2 = ISO && CHANNEL ? wave_sum(red2) : 0.f;
+        if (lane == 0) {
+          s_part[t & 1][0][wave] = sm;
+          s_part[t & 1][1][wave] = s2;
+        }
+        __syncthreads();
+        float tot = 0.f, tot2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+          tot += s_part[t & 1][0][i];
+          tot2 += s_part[t & 1][1][i];
+        }
+        if constexpr (ISO) {
+          const float bh_ = kdn_iso_predict(CHANNEL ? tot2 * (1.0f / DK) : al * al, st, s_g[2][tt]);
+          wv = kdn_iso_beta(bh_, s_g[1][tt], tot) * kk;
+          st = kdn_iso_update(bh_, tot, a.g.mu_info / (DK * s_g[1][tt]));
+        } else {
+          wv = pre / (s_g[1][tt] + tot);
+        }
+      }
+      if (a.w_bf16)
+        a.w_bf16[ti * DK + d] = f2bf(wv);
+      else
+        a.w_out[ti * DK + d] = wv;
+    }
   }
   if (a.aux_final && AUX && (!ISO || d == 0)) a.aux_final[ISO ? bh : bh * DK + d] = st;
 }
