@@ -74,6 +74,17 @@ def test_chunk_bwd_against_oracle(gain, keys, io, dk, dv, T):
     _compare(wl, got, ref, _names(gain))
 
 
+@pytest.mark.parametrize("T", [1, 63, 65, 129])
+def test_chunk_bwd_split_path_ragged(T):
+    """bf16 io with scalar decay (the path whose serial sweep carries only dS,
+    with the chunks' solves done in parallel beforehand) at lengths around
+    the chunk boundary, three heads (a workgroup count that is not a multiple
+    of 8), with and without dS_T."""
+    wl = W.Workload(f"bwd_split_T{T}", "kla", "scalar", "bf16", 1, 3, T, 128, 64, keys="scaled", seed=700 + T)
+    got, ref = _run(wl, wl.seed + 1, with_dS=T % 2 == 1)
+    _compare(wl, got, ref, _names("kla"))
+
+
 def _names(gain):
     return ["q", "k", "v", "alpha", "S0"] + {
         "kla": ["eta"], "gdn": ["eta"], "explicit": ["w"],
