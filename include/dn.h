@@ -57,7 +57,10 @@
  * structs, read before the call returns) is a device pointer owned by the
  * caller, 16-byte aligned (as hipMalloc and tensor allocators return them:
  * the kernels move rows in 16-byte vectors).  The library allocates no device memory, never synchronises, and
- * enqueues all work on `stream` (a hipStream_t; NULL = the null stream).
+ * enqueues all work on `stream` (a hipStream_t; NULL = the null stream) -
+ * except that dn_chunk_bwd may run one pass on a second stream of its own,
+ * ordered after the work already on `stream` and before the rest of the
+ * call's work there by two events (see dn_chunk_bwd).
  *
  * ERRORS.  Arguments are validated on the host before anything is launched;
  * on a negative status nothing has been enqueued.  DN_ERR_HIP reports a
@@ -340,9 +343,16 @@ typedef struct dn_grads {
  * from them the gradients of k, q, w and the decay (per key channel for
  * channel decay, the decay then applied inside the products); the chunks are
  * walked from the last, after a forward sweep that keeps the state entering
- * each chunk and the residuals E (with bf16 io and scalar decay, for KLA, GDN,
- * PGDN and explicit w with dv a multiple of 64, the chunked forward's kernel
- * runs that sweep without output).  The write gain is then differentiated token by token
+ * each chunk and the residuals E.  With bf16 io and scalar decay, for KLA,
+ * GDN, PGDN and explicit w with dv a multiple of 64, the chunked forward's
+ * kernel runs that sweep without output; what of dR does not depend on dS
+ * (dR = P + Z dS_out, Z = (I + L)^-T W~, P = (I + L)^-T M^T dO) is solved
+ * for every chunk at once, so that the reverse walk carries only dS; and
+ * when the forward sweep fills at most half of the compute units (B H dv/64
+ * <= 128) it runs on a second stream of the library (one per device,
+ * created at its first use), forked from `stream` by an event after the work
+ * already queued there and joined back by another before the gradients that
+ * read its checkpoints.  The write gain is then differentiated token by token
  * backwards (KLA, GDN: Kaczmarz Linear Attention §2.1; PGDN: Preconditioned
  * DeltaNet §2.4, Eq. 9, through the statistic A_t, its centre mu and its
  * gates; KDN: Kalman Delta Networks §2.4, Eqs. 23-30 and §2.5, through the
@@ -366,12 +376,16 @@ typedef struct dn_grads {
  *   decay, bf16; fp32: the state entering every chunk
  *   [B, H, ceil(T/C), dk, dv], the residuals [B, H, T, dv], the write vectors'
  *   gradient [B, H, T, dk], the decay's per token ([B, H, T], channel decay
- *   [B, H, T, dk]) and for the gains with a statistic the statistic entering
- *   every chunk; 1.3 GB at B8 H16 T4096 d128, scalar decay).  No gradient
+ *   [B, H, T, dk]), on the bf16 scalar-decay path above dS_out of every chunk
+ *   [B, H, ceil(T/C), dv, dk] and Z of every chunk [B, H, ceil(T/C), C, dk]
+ *   (bf16 pairs, 4 bytes each), and for the gains with a statistic the
+ *   statistic entering every chunk; 2.15 GB at B8 H16 T4096 d128 with bf16
+ *   io and scalar decay).  No gradient
  *   buffer may overlap an input, another gradient or the workspace
  *   (DN_ERR_ALIAS).  dmu_log is summed over the batch rows with atomic
  *   additions: its last bits may vary from run to run, as may those of dq,
- *   dk, dw and dalpha (summed over value-column slices). */
+ *   dk, dw and dalpha (summed over value-column slices, or on the bf16
+ *   scalar-decay path through shared-memory atomic additions). */
 size_t dn_chunk_bwd_workspace(const dn_desc* desc);
 int dn_chunk_bwd(const dn_desc* desc, const void* q, const void* k, const void* v,
                  const dn_gates* gates, const float* S0, const float* aux0, const void* dO,

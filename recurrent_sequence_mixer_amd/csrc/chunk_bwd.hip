@@ -1998,22 +1998,24 @@ static hipError_t launch_lds(K kern, unsigned grid, const BwdArgs& a, hipStream_
 // Z and P for every chunk, the serial sweep in 64-column value slices, the
 // tile kernel one workgroup per chunk
 template <int DK>
-static hipError_t launch_bwd_split_t(const BwdArgs& a, hipStream_t st) {
+static hipError_t launch_bwd_split_t(const BwdArgs& a, hipStream_t st, int part) {
   const long bh = static_cast<long>(a.B) * a.H;
   const long nch = (a.T + bwd::CH - 1) / bwd::CH;
   if (a.dv % bwd::DVS_S != 0 || a.Z_ck == nullptr || a.dS_ck == nullptr) return hipErrorInvalidValue;
-  hipError_t err = launch_lds<bwd::SmemZ<DK>>(bwd::chunk_bwd_zp_kernel<DK>, static_cast<unsigned>(bh * nch), a, st);
-  if (err != hipSuccess) return err;
-  err = launch_lds<bwd::SmemS<DK>>(bwd::chunk_bwd_ds_kernel<DK>, static_cast<unsigned>(bh * (a.dv / bwd::DVS_S)),
-                                   a, st, bwd::NTS);
-  if (err != hipSuccess) return err;
+  if (part == 1) {
+    const hipError_t err =
+        launch_lds<bwd::SmemZ<DK>>(bwd::chunk_bwd_zp_kernel<DK>, static_cast<unsigned>(bh * nch), a, st);
+    if (err != hipSuccess) return err;
+    return launch_lds<bwd::SmemS<DK>>(bwd::chunk_bwd_ds_kernel<DK>, static_cast<unsigned>(bh * (a.dv / bwd::DVS_S)),
+                                      a, st, bwd::NTS);
+  }
   return launch_lds<bwd::SmemT<DK>>(bwd::chunk_bwd_tiles_kernel<DK>, static_cast<unsigned>(bh * nch), a, st);
 }
 
-hipError_t launch_chunk_bwd_split(const BwdArgs& a, hipStream_t st) {
+hipError_t launch_chunk_bwd_split(const BwdArgs& a, hipStream_t st, int part) {
   if (a.T == 0 || a.B * a.H == 0) return hipSuccess;
-  if (a.dk == 128) return launch_bwd_split_t<128>(a, st);
-  if (a.dk == 64) return launch_bwd_split_t<64>(a, st);
+  if (a.dk == 128) return launch_bwd_split_t<128>(a, st, part);
+  if (a.dk == 64) return launch_bwd_split_t<64>(a, st, part);
   return hipErrorInvalidValue;
 }
 

@@ -173,7 +173,9 @@ hipError_t launch_chunk_bwd_state(const BwdArgs& a, int io_bf16, bool channel, h
 // into dv_out), the serial sweep for dS, then one workgroup per chunk for
 // the per-(token, key) gradients, which it writes (no accumulation: dq,
 // dk_out, dw_acc and dG need no zeroing)
-hipError_t launch_chunk_bwd_split(const BwdArgs& a, hipStream_t st);
+// part 1: the Z / P kernel and the serial sweep (S_ck and E not read); part 2:
+// the tile kernel
+hipError_t launch_chunk_bwd_split(const BwdArgs& a, hipStream_t st, int part);
 
 // Back through the gains (chunk_bwd.hip), one workgroup per (b, h): adds the
 // gain's part to dk and forms the gates' gradients from dw_acc and dG.

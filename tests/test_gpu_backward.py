@@ -85,6 +85,37 @@ def test_chunk_bwd_split_path_ragged(T):
     _compare(wl, got, ref, _names("kla"))
 
 
+def test_chunk_bwd_on_a_caller_stream():
+    """With few heads the split path runs its forward checkpoint pass on a
+    second stream of the library, forked from and joined back into the
+    caller's stream.  On a non-default caller stream, with the inputs written
+    on that stream just before the call and the gradients read on it just
+    after, the results equal those of a call on the default stream (up to
+    the order of the fp32 sums in shared-memory atomics)."""
+    from recurrent_sequence_mixer_amd import dn
+    wl = W.Workload("bwd_stream", "kla", "scalar", "bf16", 1, 2, 256, 128, 64, keys="scaled", seed=77)
+    t = dn.to_device(W.generate(wl), torch.bfloat16)
+    dO = torch.randn(wl.B, wl.H, wl.T, wl.dv, device="cuda").to(torch.bfloat16)
+    gates = {n: t[n] for n in ("alpha", "eta")}
+    kw = dict(gain="kla", eps=wl.eps)
+    ref = dn.chunk_bwd(t["q"], t["k"], t["v"], gates, dO, S0=t["S0"], **kw)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q, k, v, S0, d2 = (x.clone() for x in (t["q"], t["k"], t["v"], t["S0"], dO))
+        g2 = {n: x.clone() for n, x in gates.items()}
+        got = dn.chunk_bwd(q, k, v, g2, d2, S0=S0, **kw)
+        got = {n: x.clone() for n, x in got.items()}
+    torch.cuda.synchronize()
+    for n, r in ref.items():
+        if r is None:
+            continue
+        r, g = r.float(), got[n].float()
+        err = ((g - r).abs().max() / r.abs().max().clamp_min(1e-30)).item()
+        assert err <= 1e-5, (n, err)
+
+
 def _names(gain):
     return ["q", "k", "v", "alpha", "S0"] + {
         "kla": ["eta"], "gdn": ["eta"], "explicit": ["w"],
