@@ -1152,7 +1152,7 @@ struct SmemS {
   float gam[2][CH];  // exp(G_t)
 };
 
-template <int DK>
+template <int DK, bool SUMMARY>
 __global__ __launch_bounds__(NTS) void chunk_bwd_ds_kernel(BwdArgs a) {
   using Sm = SmemS<DK>;
   constexpr int PZ = Sm::PZ, PK = Sm::PK, ND = DK / 16, NS = DK / 32;
@@ -1168,13 +1168,30 @@ __global__ __launch_bounds__(NTS) void chunk_bwd_ds_kernel(BwdArgs a) {
   const int lg = lane >> 4;
   const int T = a.T, dv = a.dv;
   const int nch = (T + CH - 1) / CH;
-  const int nsl = dv / DVS_S;
-  // the value slices of one head on one XCD (consecutive workgroup ids go to
-  // the 8 XCDs in turn), so that they share its L2 copy of Z, k and q
+  // Segments: chunks [seg nch / nseg, (seg + 1) nch / nseg) of a head (nseg =
+  // 1: the whole sequence).  SUMMARY: from dS_out = 0 over the value slices
+  // (B of the segment's affine map dS_in = A dS_out + B) and from the
+  // identity over DK more columns with dO = P = 0 (A), written to segB and
+  // segA under the index nseg - 1 - seg (the order segment_combine_kernel
+  // chains them in, from dS_T).  Otherwise from dS_T (nseg = 1) or from the
+  // chained dS_out of the segment (seg_in), storing dS_out and dR per chunk.
+  const int nseg = a.nseg;
+  const int nslv = dv / DVS_S;
+  const int nsl = SUMMARY ? nslv + DK / DVS_S : nslv;
+  // the slices of one head and segment on one XCD (consecutive workgroup ids
+  // go to the 8 XCDs in turn), so that they share its L2 copy of Z, k and q
   const unsigned G = gridDim.x;
   const unsigned lin = G % 8 == 0 ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
-  const long bh = lin / nsl;
-  const int col = static_cast<int>(lin % nsl) * DVS_S + 16 * wave + (lane & 15);
+  const long hs = lin / nsl;
+  const int sl = static_cast<int>(lin % nsl);
+  const long bh = hs / nseg;
+  const int seg = static_cast<int>(hs % nseg);
+  const int rs = nseg - 1 - seg;
+  const bool tmap = SUMMARY && sl >= nslv;  // identity columns: the transfer map A
+  // this lane's value column (identity column of A on a tmap slice)
+  const int col = (tmap ? sl - nslv : sl) * DVS_S + 16 * wave + (lane & 15);
+  const int c_lo = static_cast<int>(static_cast<long>(seg) * nch / nseg);
+  const int c_hi = static_cast<int>(static_cast<long>(seg + 1) * nch / nseg);
   const long tok0 = bh * T;
   const uint16_t* kg = static_cast<const uint16_t*>(a.k);
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
@@ -1209,8 +1226,9 @@ __global__ __launch_bounds__(NTS) void chunk_bwd_ds_kernel(BwdArgs a) {
   // through the next
   auto fetch_b = [&](int c) {
     const int t0 = c * CH, n = nof(c);
-    const auto rp = brsrc(a.dv_out + (tok0 + t0) * dv, 4l * n * dv);
-    const auto ro = brsrc(og + (tok0 + t0) * dv, 2l * n * dv);
+    // (no P or dO on the identity columns: empty resources, loads read zero)
+    const auto rp = brsrc(a.dv_out + (tok0 + t0) * dv, tmap ? 0 : 4l * n * dv);
+    const auto ro = brsrc(og + (tok0 + t0) * dv, tmap ? 0 : 2l * n * dv);
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
@@ -1247,29 +1265,34 @@ __global__ __launch_bounds__(NTS) void chunk_bwd_ds_kernel(BwdArgs a) {
 
   f32x4 dS[ND];
   {
-    // dS_T (no dS_T: an empty resource, every load reads zero)
-    const auto rt = brsrc(a.dS_T ? a.dS_T + bh * DK * dv : nullptr, a.dS_T ? 4l * DK * dv : 0);
+    // the entering dS_out: dS_T or seg_in (none: an empty resource, every
+    // load reads zero; SUMMARY: zero, or the identity on the tmap slices)
+    const float* src = SUMMARY ? nullptr : nseg > 1 ? a.seg_in + (bh * nseg + rs) * DK * dv
+                                                    : a.dS_T ? a.dS_T + bh * DK * dv : nullptr;
+    const auto rt = brsrc(src, src ? 4l * DK * dv : 0);
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dS[db][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rt, 4 * loff, 4 * (16 * db + i) * dv, 0));
+      for (int i = 0; i < 4; ++i) {
+        const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rt, 4 * loff, 4 * (16 * db + i) * dv, 0));
+        dS[db][i] = tmap ? (16 * db + 4 * lg + i == col ? 1.f : 0.f) : x;
+      }
   }
-  fetch_a(nch - 1);
-  put((nch - 1) & 1, nof(nch - 1));
-  fetch_b(nch - 1);
+  fetch_a(c_hi - 1);
+  put((c_hi - 1) & 1, nof(c_hi - 1));
+  fetch_b(c_hi - 1);
   __syncthreads();
-  for (int c = nch - 1; c >= 0; --c) {
+  for (int c = c_hi - 1; c >= c_lo; --c) {
     const int b = c & 1, t0 = c * CH, n = nof(c);
-    // the next chunk's loads (at the first chunk, harmless repeats of it:
-    // every step issues the same loads, so no wait depends on the path)
-    const int cn = max(c - 1, 0);
+    // the next chunk's loads (at the segment's first chunk, harmless repeats
+    // of it: every step issues the same loads, so no wait depends on the path)
+    const int cn = max(c - 1, c_lo);
     fetch_a(cn);
     // keep the scheduler from sinking these loads towards their use
     __builtin_amdgcn_sched_barrier(0);
     // dS_out^T [dv][dk] of the chunk for the tile kernel: each lane's four key
     // channels are one 16-byte piece
-    {
+    if constexpr (!SUMMARY) {
       f32x4* dsk = reinterpret_cast<f32x4*>(a.dS_ck + ((bh * nch + c) * dv + col) * DK + 4 * lg);
 #pragma unroll
       for (int db = 0; db < ND; ++db) dsk[4 * db] = dS[db];
@@ -1314,7 +1337,8 @@ __global__ __launch_bounds__(NTS) void chunk_bwd_ds_kernel(BwdArgs a) {
       for (int i = 0; i < 4; ++i) {
         // rows past the end: P and dO read as zero, Z's rows are zero
         const float dr = pn[ib][i] + y[i];
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dr), rdr, 4 * loff, 4 * (16 * ib + i) * dv, 0);
+        if constexpr (!SUMMARY)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dr), rdr, 4 * loff, 4 * (16 * ib + i) * dv, 0);
         go[i] = g4[i] * bf2f(on[ib][i]);
         gr[i] = -g4[i] * dr;
       }
@@ -1359,11 +1383,20 @@ __global__ __launch_bounds__(NTS) void chunk_bwd_ds_kernel(BwdArgs a) {
     put(b ^ 1, nof(cn));
     __syncthreads();
   }
-  if (a.dS0)
+  if constexpr (SUMMARY) {
+    // A [DK][DK] (row d, identity column col) or B [DK][dv] of the segment
+    float* dst = tmap ? a.segA + (bh * nseg + rs) * DK * DK : a.segB + (bh * nseg + rs) * DK * dv;
+    const int ld = tmap ? DK : dv;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(16 * db + 4 * lg + i) * ld + col] = dS[db][i];
+  } else if (nseg == 1 && a.dS0) {
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) a.dS0[(bh * DK + 16 * db + 4 * lg + i) * dv + col] = dS[db][i];
+  }
 }
 
 template <int DK>
@@ -2001,13 +2034,34 @@ template <int DK>
 static hipError_t launch_bwd_split_t(const BwdArgs& a, hipStream_t st, int part) {
   const long bh = static_cast<long>(a.B) * a.H;
   const long nch = (a.T + bwd::CH - 1) / bwd::CH;
-  if (a.dv % bwd::DVS_S != 0 || a.Z_ck == nullptr || a.dS_ck == nullptr) return hipErrorInvalidValue;
+  if (a.dv % bwd::DVS_S != 0 || a.Z_ck == nullptr || a.dS_ck == nullptr || a.nseg < 1 || a.nseg > nch ||
+      (a.nseg > 1 && (a.segA == nullptr || a.segB == nullptr || a.seg_in == nullptr)))
+    return hipErrorInvalidValue;
   if (part == 1) {
-    const hipError_t err =
+    hipError_t err =
         launch_lds<bwd::SmemZ<DK>>(bwd::chunk_bwd_zp_kernel<DK>, static_cast<unsigned>(bh * nch), a, st);
     if (err != hipSuccess) return err;
-    return launch_lds<bwd::SmemS<DK>>(bwd::chunk_bwd_ds_kernel<DK>, static_cast<unsigned>(bh * (a.dv / bwd::DVS_S)),
-                                      a, st, bwd::NTS);
+    const unsigned nv = static_cast<unsigned>(bh * a.nseg * (a.dv / bwd::DVS_S));
+    if (a.nseg > 1) {
+      // every segment's affine map, then the maps chained from dS_T (which
+      // also gives dS0), then every segment from its own dS_out
+      err = launch_lds<bwd::SmemS<DK>>(bwd::chunk_bwd_ds_kernel<DK, true>,
+                                       nv + static_cast<unsigned>(bh * a.nseg * (DK / bwd::DVS_S)), a, st, bwd::NTS);
+      if (err != hipSuccess) return err;
+      CombineArgs ca;
+      ca.B = a.B;
+      ca.H = a.H;
+      ca.nseg = a.nseg;
+      ca.dk = DK;
+      ca.dv = a.dv;
+      ca.A = a.segA;
+      ca.Bs = a.segB;
+      ca.S0 = a.dS_T;
+      ca.S_in = a.seg_in;
+      ca.S_final = a.dS0;
+      if ((err = launch_segment_combine(ca, st)) != hipSuccess) return err;
+    }
+    return launch_lds<bwd::SmemS<DK>>(bwd::chunk_bwd_ds_kernel<DK, false>, nv, a, st, bwd::NTS);
   }
   return launch_lds<bwd::SmemT<DK>>(bwd::chunk_bwd_tiles_kernel<DK>, static_cast<unsigned>(bh * nch), a, st);
 }

@@ -947,12 +947,14 @@ SideStream* side_stream(std::unique_lock<std::mutex>& lk) {
 // [B, H, T, dk] (fp32, bf16 with bf16 io and scalar decay), S_ck [B, H, nch,
 // dk, dv], E [B, H, T, dv], dw_acc [B, H, T, dk], dG ([B, H, T]; channel decay
 // [B, H, T, dk]), on the split path dS_ck [B, H, nch, dv, dk] and Z_ck
-// [B, H, nch, 64, dk] (split bf16 pairs, 4 bytes each), then for the
+// [B, H, nch, 64, dk] (split bf16 pairs, 4 bytes each) and with a segmented
+// sweep its segment maps A [B, H nseg, dk, dk], B and the chained dS_out
+// [B, H nseg, dk, dv], then for the
 // gains with a statistic the statistic entering every chunk ([B, H, nch, dk];
 // KDN_ISO [B, H, nch]), and the workspace of the gain scans (as for
 // dn_gain_prep); fp32 where not said.
 struct BwdLayout {
-  size_t w, sck, e, dw, dg, dsck, zck, aux, prep, total;
+  size_t w, sck, e, dw, dg, dsck, zck, sega, segb, segin, aux, prep, total;
 };
 
 // The split backward: bf16 io, scalar decay, the gains the forward chunk
@@ -964,6 +966,26 @@ struct BwdLayout {
 static bool bwd_split(const dn_desc* d) {
   return d->io == DN_BF16 && d->decay == DN_DECAY_SCALAR && d->gain != DN_GAIN_KDN &&
          d->gain != DN_GAIN_KDN_ISO && d->dv % 64 == 0;
+}
+
+// Segments of the split path's serial sweep.  With few heads its
+// workgroups (one per head and 64 value columns) leave most compute units
+// idle while they walk every chunk in turn; then the chunks are cut into
+// nseg segments whose affine maps dS_in = A dS_out + B are formed in
+// parallel, chained, and each segment is swept again from its own dS_out
+// (two passes of nch / nseg steps and a chain of nseg steps instead of one
+// pass of nch steps).  nseg: the largest power of two with at least four
+// chunks per segment whose map pass (value and identity columns) fits on
+// the compute units at once; 1 when the plain sweep already fills a quarter
+// of them or the sequence has fewer than 16 chunks.
+static int bwd_nseg(const dn_desc* d) {
+  if (!bwd_split(d)) return 1;
+  const long bh = static_cast<long>(d->B) * d->H;
+  const long nch = (static_cast<long>(d->T) + 63) / 64;
+  if (4 * bh * (d->dv / 64) > CU_COUNT || nch < 16) return 1;
+  int nseg = 1;
+  while (2 * nseg <= nch / 4 && bh * 2 * nseg * ((d->dv + d->dk) / 64) <= CU_COUNT) nseg *= 2;
+  return nseg;
 }
 
 static BwdLayout bwd_layout(const dn_desc* d) {
@@ -978,7 +1000,12 @@ static BwdLayout bwd_layout(const dn_desc* d) {
   L.dg = round256(L.dw + bht * d->dk * 4);
   L.dsck = round256(L.dg + bht * gdim * 4);
   L.zck = round256(L.dsck + (bwd_split(d) ? bh * nch * d->dk * d->dv * 4 : 0));
-  L.aux = round256(L.zck + (bwd_split(d) ? bh * nch * 64 * d->dk * 4 : 0));
+  const int nseg = bwd_nseg(d);
+  const size_t ns = nseg > 1 ? bh * nseg : 0;
+  L.sega = round256(L.zck + (bwd_split(d) ? bh * nch * 64 * d->dk * 4 : 0));
+  L.segb = round256(L.sega + ns * d->dk * d->dk * 4);
+  L.segin = round256(L.segb + ns * d->dk * d->dv * 4);
+  L.aux = round256(L.segin + ns * d->dk * d->dv * 4);
   L.prep = round256(L.aux + (has_aux_state(d) ? bh * nch * aux_per_head(d) * 4 : 0));
   L.total = L.prep + prep_layout(d).total;
   return L;
@@ -1157,6 +1184,12 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
     b.ck_given = 1;
     b.dS_ck = reinterpret_cast<float*>(wb + lay.dsck);
     b.Z_ck = reinterpret_cast<uint32_t*>(wb + lay.zck);
+    b.nseg = bwd_nseg(d);
+    if (b.nseg > 1) {
+      b.segA = reinterpret_cast<float*>(wb + lay.sega);
+      b.segB = reinterpret_cast<float*>(wb + lay.segb);
+      b.seg_in = reinterpret_cast<float*>(wb + lay.segin);
+    }
     // meanwhile Z, P and the dS sweep on the caller's stream; the tile kernel
     // reads the checkpoints
     if (dn::launch_chunk_bwd_split(b, s, 1) != hipSuccess) return DN_ERR_HIP;

@@ -166,6 +166,13 @@ struct BwdArgs {
   // pairs (hi in the low half)
   float* dS_ck = nullptr;
   uint32_t* Z_ck = nullptr;
+  // the segmented sweep (nseg > 1): segment maps segA [B, H nseg, dk, dk] and
+  // segB [B, H nseg, dk, dv], and the chained dS_out of every segment seg_in
+  // [B, H nseg, dk, dv], all in segment_combine_kernel's (reversed) order
+  int nseg = 1;
+  float* segA = nullptr;
+  float* segB = nullptr;
+  float* seg_in = nullptr;
 };
 hipError_t launch_chunk_bwd_state(const BwdArgs& a, int io_bf16, bool channel, hipStream_t st);
 // bf16 io, scalar decay, S_ck and E written by the forward chunk kernel, dv a

@@ -85,6 +85,19 @@ def test_chunk_bwd_split_path_ragged(T):
     _compare(wl, got, ref, _names("kla"))
 
 
+@pytest.mark.parametrize("gain,T,with_dS", [("kla", 1100, True), ("pgdn", 2048, False), ("gdn", 2048, True)])
+def test_chunk_bwd_segmented_sweep(gain, T, with_dS):
+    """Few heads and at least 16 chunks: the serial dS sweep runs by segments
+    (each segment's affine map from zero and from the identity, the maps
+    chained from dS_T, every segment swept again from its own dS_out).
+    T 1100: four segments of 4-5 chunks, the last chunk partial; T 2048:
+    eight segments of 4 chunks."""
+    wl = W.Workload(f"bwd_seg_{gain}", gain, "scalar", "bf16", 1, 2, T, 128, 64,
+                    keys="unit" if gain != "kla" else "scaled", mu_spread=0.5, seed=900 + T)
+    got, ref = _run(wl, wl.seed + 1, with_dS=with_dS)
+    _compare(wl, got, ref, _names(gain))
+
+
 def test_chunk_bwd_on_a_caller_stream():
     """With few heads the split path runs its forward checkpoint pass on a
     second stream of the library, forked from and joined back into the
