@@ -262,9 +262,13 @@ static int check_long_aliases(const dn_desc* d, const dn_gates* g, const void* q
 
 // The segmented forward (already validated): steps (0) to (3) of
 // dn_chunk_fwd_long on `ws`, laid out by long_layout(d, nseg).
+// S_ck / E_ck (nullable, with o null): step (3) writes the state entering
+// every chunk [B, H, T / C, dk, dv] and the residuals [B, H, T, dv] instead
+// of o (the checkpoints of dn_chunk_bwd).
 static int run_long(const dn_desc* d, int nseg, const void* q, const void* k, const void* v,
                     const dn_gates* g, const float* S0, const float* aux0, void* o, float* S_final,
-                    float* aux_final, void* ws, const LongLayout& lay, hipStream_t s) {
+                    float* aux_final, void* ws, const LongLayout& lay, hipStream_t s,
+                    float* S_ck = nullptr, float* E_ck = nullptr) {
   const bool has_aux = has_aux_state(d);
   // the [B, H, T, d] tensors read as [B, H nseg, T / nseg, d]: segment s of
   // head h is head h nseg + s of the view (and likewise the per-token gates)
@@ -339,10 +343,14 @@ static int run_long(const dn_desc* d, int nseg, const void* q, const void* k, co
   c.S_final = S_final;
   c.oor = oor;
   if ((e = dn::launch_segment_combine(c, s)) != hipSuccess) return DN_ERR_HIP;
-  // (3) every segment from its entering state, writing o
+  // (3) every segment from its entering state, writing o (or the
+  // checkpoints: the view's [B, H nseg, T / (nseg C), ...] layouts are the
+  // sequence's [B, H, T / C, ...])
   a.S0 = wS;
   a.S_final = nullptr;
   a.o = o;
+  a.S_ck = S_ck;
+  a.E_ck = E_ck;
   if ((e = launch()) != hipSuccess) return DN_ERR_HIP;
   // (4) per-channel decay: the flagged heads token by token, from S0 and the
   // statistic entering segment 0
@@ -954,7 +962,7 @@ SideStream* side_stream(std::unique_lock<std::mutex>& lk) {
 // KDN_ISO [B, H, nch]), and the workspace of the gain scans (as for
 // dn_gain_prep); fp32 where not said.
 struct BwdLayout {
-  size_t w, sck, e, dw, dg, dsck, zck, sega, segb, segin, aux, prep, total;
+  size_t w, sck, e, dw, dg, dsck, zck, sega, segb, segin, ckl, aux, prep, total;
 };
 
 // The split backward: bf16 io, scalar decay, the gains the forward chunk
@@ -988,6 +996,11 @@ static int bwd_nseg(const dn_desc* d) {
   return nseg;
 }
 
+// Segments of the split path's checkpoint pass: the forward's own schedule
+// (auto_nseg), run as by dn_chunk_fwd_long with the checkpoints written by
+// its last step.
+static int bwd_ck_nseg(const dn_desc* d) { return bwd_split(d) && d->C == 64 ? auto_nseg(d) : 1; }
+
 static BwdLayout bwd_layout(const dn_desc* d) {
   BwdLayout L{};
   const size_t bh = static_cast<size_t>(d->B) * d->H, bht = bh * d->T;
@@ -1005,7 +1018,9 @@ static BwdLayout bwd_layout(const dn_desc* d) {
   L.sega = round256(L.zck + (bwd_split(d) ? bh * nch * 64 * d->dk * 4 : 0));
   L.segb = round256(L.sega + ns * d->dk * d->dk * 4);
   L.segin = round256(L.segb + ns * d->dk * d->dv * 4);
-  L.aux = round256(L.segin + ns * d->dk * d->dv * 4);
+  const int cks = bwd_ck_nseg(d);
+  L.ckl = round256(L.segin + ns * d->dk * d->dv * 4);
+  L.aux = round256(L.ckl + (cks > 1 ? long_layout(d, cks).total : 0));
   L.prep = round256(L.aux + (has_aux_state(d) ? bh * nch * aux_per_head(d) * 4 : 0));
   L.total = L.prep + prep_layout(d).total;
   return L;
@@ -1179,7 +1194,15 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
     SideStream* ss = 2 * static_cast<long>(bh) * (d->dv / 64) <= CU_COUNT ? side_stream(lk) : nullptr;
     if (ss && (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess))
       return DN_ERR_HIP;
-    if (dn::launch_chunk_fwd_bf16_scalar(ca, d->gain, ss ? ss->s : s) != hipSuccess) return DN_ERR_HIP;
+    // (by segments, as the forward with few heads, when that is cheaper)
+    const int cks = bwd_ck_nseg(d);
+    if (cks > 1) {
+      if ((st = run_long(d, cks, q, k, v, g, S0, pg ? aux0 : nullptr, nullptr, nullptr, nullptr, wb + lay.ckl,
+                         long_layout(d, cks), ss ? ss->s : s, b.S_ck, b.E)) != DN_OK)
+        return st;
+    } else if (dn::launch_chunk_fwd_bf16_scalar(ca, d->gain, ss ? ss->s : s) != hipSuccess) {
+      return DN_ERR_HIP;
+    }
     if (ss && hipEventRecord(ss->join, ss->s) != hipSuccess) return DN_ERR_HIP;
     b.ck_given = 1;
     b.dS_ck = reinterpret_cast<float*>(wb + lay.dsck);
