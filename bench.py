@@ -459,10 +459,14 @@ def main():
         if want("bwd"):
             # the chunked backward at the headline shape and at the pages' operator
             # shape (Preconditioned DeltaNet Fig. 4: batch 1, 8 heads, head dim 128)
+            long_op = W.Workload("kla_B1H8T32768d128", "kla", "scalar", "bf16", 1, 8, 32768, 128, 128, seed=55)
             for key, w2 in (("bwd_kla", W.WORKLOADS[1]),
                             ("bwd_kla_B1H8", W.Workload("kla_bwd_B1H8T4096d128", "kla", "scalar", "bf16",
-                                                        1, 8, 4096, 128, 128, seed=54))):
+                                                        1, 8, 4096, 128, 128, seed=54)),
+                            ("bwd_kla_B1H8T32768", long_op)):
                 extra[key] = extra_bwd(w2, 3, 1, 0.0)
+            # and the forward of the longest operator shape, for forward + backward
+            extra["fwd_kla_B1H8T32768"] = extra_chunk(long_op, 5, 1, 0.0)
         if want("decode"):
             dwl = W.WORKLOADS[4]
             dms = time_decode(dwl, args.decode_steps, args.settle_s)
