@@ -352,7 +352,11 @@ typedef struct dn_grads {
  * <= 128) it runs on a second stream of the library (one per device,
  * created at its first use), forked from `stream` by an event after the work
  * already queued there and joined back by another before the gradients that
- * read its checkpoints.  The write gain is then differentiated token by token
+ * read its checkpoints.  With few heads (B H dv/64 <= 64) and at least 16
+ * chunks both serial passes run by segments: the forward sweep as
+ * dn_chunk_fwd_long's schedule, and the reverse walk as every segment's
+ * affine map (dS_in = A dS_out + B) formed in parallel, the maps chained from
+ * dS_T, and every segment walked again from its own dS_out.  The write gain is then differentiated token by token
  * backwards (KLA, GDN: Kaczmarz Linear Attention §2.1; PGDN: Preconditioned
  * DeltaNet §2.4, Eq. 9, through the statistic A_t, its centre mu and its
  * gates; KDN: Kalman Delta Networks §2.4, Eqs. 23-30 and §2.5, through the
@@ -378,7 +382,8 @@ typedef struct dn_grads {
  *   gradient [B, H, T, dk], the decay's per token ([B, H, T], channel decay
  *   [B, H, T, dk]), on the bf16 scalar-decay path above dS_out of every chunk
  *   [B, H, ceil(T/C), dv, dk] and Z of every chunk [B, H, ceil(T/C), C, dk]
- *   (bf16 pairs, 4 bytes each), and for the gains with a statistic the
+ *   (bf16 pairs, 4 bytes each), with segments their maps and entering dS
+ *   and the forward schedule's workspace, and for the gains with a statistic the
  *   statistic entering every chunk; 2.15 GB at B8 H16 T4096 d128 with bf16
  *   io and scalar decay).  No gradient
  *   buffer may overlap an input, another gradient or the workspace
