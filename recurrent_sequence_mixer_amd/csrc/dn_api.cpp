@@ -980,20 +980,30 @@ static bool bwd_split(const dn_desc* d) {
 // workgroups (one per head and 64 value columns) leave most compute units
 // idle while they walk every chunk in turn; then the chunks are cut into
 // nseg segments whose affine maps dS_in = A dS_out + B are formed in
-// parallel, chained, and each segment is swept again from its own dS_out
-// (two passes of nch / nseg steps and a chain of nseg steps instead of one
-// pass of nch steps).  nseg: the largest power of two with at least four
-// chunks per segment whose map pass (value and identity columns) fits on
-// the compute units at once; 1 when the plain sweep already fills a quarter
-// of them or the sequence has fewer than 16 chunks.
+// parallel, chained, and each segment is swept again from its own dS_out.
+// Cost in chunk steps: the map pass (value and identity columns) and the
+// second pass each take a chunk step per segment chunk and round of
+// CU_COUNT workgroups, a link of the chain about 0.6 of a step.  nseg: the
+// cheapest power of two with at least four chunks per segment, taken when it
+// saves at least a fifth of the plain sweep; 1 below 16 chunks.
 static int bwd_nseg(const dn_desc* d) {
   if (!bwd_split(d)) return 1;
-  const long bh = static_cast<long>(d->B) * d->H;
-  const long nch = (static_cast<long>(d->T) + 63) / 64;
-  if (4 * bh * (d->dv / 64) > CU_COUNT || nch < 16) return 1;
-  int nseg = 1;
-  while (2 * nseg <= nch / 4 && bh * 2 * nseg * ((d->dv + d->dk) / 64) <= CU_COUNT) nseg *= 2;
-  return nseg;
+  const long long bh = static_cast<long long>(d->B) * d->H;
+  const long long nch = (static_cast<long long>(d->T) + 63) / 64;
+  if (nch < 16) return 1;
+  const long long wv = bh * (d->dv / 64), wm = bh * ((d->dv + d->dk) / 64);
+  const double one = rounds(wv) * static_cast<double>(nch);
+  double best = one;
+  int pick = 1;
+  for (int nseg = 2; 4 * nseg <= nch && bh * nseg <= 65535; nseg *= 2) {
+    const double len = static_cast<double>((nch + nseg - 1) / nseg);
+    const double cost = (rounds(wm * nseg) + rounds(wv * nseg)) * len + 0.6 * nseg;
+    if (cost < best) {
+      best = cost;
+      pick = nseg;
+    }
+  }
+  return best <= 0.8 * one ? pick : 1;
 }
 
 // Segments of the split path's checkpoint pass: the forward's own schedule
