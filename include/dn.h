@@ -352,8 +352,8 @@ typedef struct dn_grads {
  * <= 128) it runs on a second stream of the library (one per device,
  * created at its first use), forked from `stream` by an event after the work
  * already queued there and joined back by another before the gradients that
- * read its checkpoints.  With few heads (B H dv/64 <= 64) and at least 16
- * chunks both serial passes run by segments: the forward sweep as
+ * read its checkpoints.  With few heads and at least 16 chunks (when a
+ * chunk-step cost model finds it cheaper) both serial passes run by segments: the forward sweep as
  * dn_chunk_fwd_long's schedule, and the reverse walk as every segment's
  * affine map (dS_in = A dS_out + B) formed in parallel, the maps chained from
  * dS_T, and every segment walked again from its own dS_out.  The write gain is then differentiated token by token
