@@ -990,26 +990,38 @@ __device__ __forceinline__ void solve_upper(const float* lm, const float* tb, fl
 // Z = (I + L)^-T W~ [CH, dk] into the workspace as split bf16 pairs (rows past
 // the end zero), and P = (I + L)^-T M^T dO [n, dv] into dv_out, in 64-column
 // slices.  The serial sweep then needs only dR = P + Z dS_out.
-constexpr int PO = 64 + 4;  // row pitch of the 64-column fp32 slices
+constexpr int PO = 64 + 4;   // row pitch of the 64-column fp32 slices
+constexpr int POB = 64 + 8;  // row pitch of the 64-column bf16 dO slice
+// At most 80 KiB, so that two workgroups share a compute unit and one's
+// memory phases overlap the other's products: k and q take turns in one
+// buffer, and W~ / Z, then P and the dO slice, reuse the k / q and w rows
+// once L and M are formed.
 template <int DK>
 struct SmemZ {
-  static constexpr int DKV = DK;
-  static constexpr int PK = DK + 2;  // row pitch of the [CH][DK] operand rows
-  static constexpr int PX = DK + 4;  // row pitch of x: W~, then Z
-  uint16_t k[CH * PK], q[CH * PK], w[CH * PK];
-  float x[CH * PX];   // W~ solved in place into Z; then M^T dO solved into P (pitch PO)
-  float o[CH * PO];   // dO, one 64-column slice
+  static constexpr int PK = DK + 2;  // bf16 row pitch of the operand rows
+  static constexpr int PX = DK + 2;  // fp32 row pitch of x (W~, then Z): the size of kq and w
+  static constexpr int XS = CH * PX > CH * PO + CH * POB / 2 ? CH * PX : CH * PO + CH * POB / 2;
+  union {
+    struct {
+      uint16_t kq[CH * PK];  // k, then q
+      uint16_t w[CH * PK];
+    } r;
+    float x[XS];  // W~ solved in place into Z; then P (pitch PO) and dO (bf16, pitch POB)
+  } u;
   float lm[CH * PC];  // L
   float mm[CH * PC];  // M
   float tb[4 * 16 * PT];
-  float G[CH], gam[CH], fn[CH], sg[CH];
+  float G[CH], fn[CH];
 };
 
 template <int DK>
-__global__ __launch_bounds__(NT) void chunk_bwd_zp_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT, 2) void chunk_bwd_zp_kernel(BwdArgs a) {
   using Sm = SmemZ<DK>;
   constexpr int PK = Sm::PK, PX = Sm::PX;
-  static_assert(offsetof(Sm, x) % 16 == 0 && offsetof(Sm, o) % 16 == 0 && PX % 4 == 0, "16-byte LDS rows");
+  static_assert(sizeof(Sm) <= 80 * 1024, "two workgroups per compute unit");
+  static_assert(CH * PO + CH * POB / 2 <= Sm::XS && CH * PX <= Sm::XS, "P and dO in x");
+  static_assert(offsetof(Sm, lm) % 16 == 0 && offsetof(Sm, mm) % 16 == 0 && (CH * PO * 4) % 16 == 0,
+                "16-byte LDS rows");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   DN_LDS_POISON(smem_raw, sizeof(Sm));
   Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
@@ -1021,10 +1033,30 @@ __global__ __launch_bounds__(NT) void chunk_bwd_zp_kernel(BwdArgs a) {
   const int c = blockIdx.x % nch;
   const int t0 = c * CH, n = min(CH, T - t0);
   const long tok0 = bh * T;
+  float* const P = sm.u.x;  // [CH][PO] after Z is out
+  uint16_t* const O = reinterpret_cast<uint16_t*>(sm.u.x + CH * PO);  // [CH][POB]
 
-  // dO of a 64-column slice, one 8-column piece per thread, fetched into
-  // registers a slice ahead (the first with k, q, w); rows past the end read
-  // the last row and are staged as zeros (no load under a branch)
+  // k, q, w rows of the chunk (16-byte pieces, rows past the end read the
+  // last row and are staged as zeros: no load under a branch), the decay,
+  // and the first dO slice, all in one round trip
+  constexpr int KP = CH * DK / 8 / NT;  // pieces per thread and array
+  static_assert(KP >= 1, "k, q, w pieces");
+  u32x4 kr[KP], qr[KP], wr[KP];
+  auto piece = [&](int m, int& t, int& d) {
+    const int i = tid + NT * m;
+    t = i / (DK / 8);
+    d = i % (DK / 8) * 8;
+  };
+#pragma unroll
+  for (int m = 0; m < KP; ++m) {
+    int t, d;
+    piece(m, t, d);
+    const long off = (tok0 + t0 + min(t, n - 1)) * DK + d;
+    kr[m] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k) + off);
+    qr[m] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + off);
+    wr[m] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.w) + off);
+  }
+  const float alv = static_cast<const float*>(a.g.alpha)[tok0 + t0 + min(lane, n - 1)];
   static_assert(CH * 64 / 8 == NT, "one dO piece per thread");
   const int ot = tid / 8, oc8 = tid % 8 * 8;
   u32x4 od;
@@ -1032,39 +1064,88 @@ __global__ __launch_bounds__(NT) void chunk_bwd_zp_kernel(BwdArgs a) {
     od = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.dO) + (tok0 + t0 + min(ot, n - 1)) * dv +
                                          s0 + oc8);
   };
-  stage_kqw(sm, a, tok0, c, tid, lane);
   fetch_o(0);
+  auto put_rows = [&](uint16_t* dst, const u32x4 (&v)[KP]) {
+#pragma unroll
+    for (int m = 0; m < KP; ++m) {
+      int t, d;
+      piece(m, t, d);
+      // rows at an odd pitch of 2-byte elements: 4-byte stores
+      uint32_t* q4 = reinterpret_cast<uint32_t*>(dst + t * PK + d);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q4[j] = t < n ? v[m][j] : 0u;
+    }
+  };
+  put_rows(sm.u.r.kq, kr);
+  put_rows(sm.u.r.w, wr);
+  if (tid < 64) {
+    // inclusive prefix sum of log(alpha) over the chunk (padding: alpha = 1)
+    float l = tid < n ? logf(alv) : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(l, off);
+      if (lane >= off) l += y;
+    }
+    sm.G[tid] = l;
+    sm.fn[tid] = expf(__shfl(l, CH - 1) - l);
+  }
   __syncthreads();
-  form_lm_bf16(sm, n, wave, lane);
-  // W~ = diag(g_n / g) W (rows past the end are zero: w staged as 0)
-  for (int idx = tid; idx < CH * DK; idx += NT) {
-    const int t = idx / DK, d = idx % DK;
-    sm.x[t * PX + d] = sm.fn[t] * bf2f(sm.w[t * PK + d]);
+  // L = strict_lower(D o K W^T), then M = lower(D o Q W^T), bf16 products
+  // (exact in fp32), D_ji = exp(G_j - G_i)
+  auto form = [&](float* out, bool strict) {
+    for (int tile = wave; tile < 16; tile += NW) {
+      const int tr = tile >> 2, tc = tile & 3;
+      f32x4 acc = zero4();
+      if (tr >= tc) {
+        const uint16_t* ar = sm.u.r.kq + (16 * tr + lr) * PK;
+        const uint16_t* wr_ = sm.u.r.w + (16 * tc + lr) * PK;
+#pragma unroll 4
+        for (int k0 = 0; k0 < DK; k0 += 16) acc = mfma16(bf4(ar, k0 + 4 * lg), bf4(wr_, k0 + 4 * lg), acc);
+      }
+      const int i = 16 * tc + lr;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int j = 16 * tr + 4 * lg + ii;
+        const float dm = j < n && i <= j ? expf(sm.G[j] - sm.G[i]) : 0.f;
+        out[j * PC + i] = !strict || i < j ? dm * acc[ii] : 0.f;
+      }
+    }
+  };
+  form(sm.lm, true);
+  __syncthreads();
+  put_rows(sm.u.r.kq, qr);
+  __syncthreads();
+  form(sm.mm, false);
+  // W~ = diag(g_n / g) W into registers (rows past the end zero: w staged as
+  // 0), then into x once every reader of the rows is done
+  constexpr int XV = CH * DK / NT;
+  float wt[XV];
+#pragma unroll
+  for (int j = 0; j < XV; ++j) {
+    const int idx = tid * XV + j, t = idx / DK, d = idx % DK;
+    wt[j] = sm.fn[t] * bf2f(sm.u.r.w[t * PK + d]);
   }
   __syncthreads();
   invert_blocks(sm.lm, sm.tb, wave, lane);
+#pragma unroll
+  for (int j = 0; j < XV; ++j) {
+    const int idx = tid * XV + j, t = idx / DK, d = idx % DK;
+    sm.u.x[t * PX + d] = wt[j];
+  }
   __syncthreads();
-  solve_upper<PX>(sm.lm, sm.tb, sm.x, DK / 16, wave, lane);
+  solve_upper<PX>(sm.lm, sm.tb, sm.u.x, DK / 16, wave, lane);
   __syncthreads();
   {
     u32x4* zo = reinterpret_cast<u32x4*>(a.Z_ck + (bh * nch + c) * CH * DK);
     for (int idx = tid; idx < CH * DK / 4; idx += NT) {
       const int t = idx / (DK / 4), d = idx % (DK / 4) * 4;
-      const float* xr = sm.x + t * PX + d;
+      const float* xr = sm.u.x + t * PX + d;
       zo[idx] = u32x4{split_bf(xr[0]), split_bf(xr[1]), split_bf(xr[2]), split_bf(xr[3])};
     }
   }
   for (int s0 = 0; s0 < dv; s0 += 64) {
-    __syncthreads();  // the previous readers of x and o are done
-    {
-      float* orow = sm.o + ot * PO + oc8;
-      const bool ok = ot < n;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        orow[2 * j] = ok ? __uint_as_float(od[j] << 16) : 0.f;
-        orow[2 * j + 1] = ok ? __uint_as_float(od[j] & 0xFFFF0000u) : 0.f;
-      }
-    }
+    __syncthreads();  // the previous readers of x (Z, then P) are done
+    *reinterpret_cast<u32x4*>(O + ot * POB + oc8) = ot < n ? od : u32x4{0u, 0u, 0u, 0u};
     // the next slice (at the last, a harmless repeat of it)
     fetch_o(min(s0 + 64, dv - 64));
     __syncthreads();
@@ -1073,18 +1154,18 @@ __global__ __launch_bounds__(NT) void chunk_bwd_zp_kernel(BwdArgs a) {
       const int ib = tile >> 2, cb = tile & 3;
       const f32x4 acc = mm_bf<false, true>(
           zero4(), 16 * ib, CH, [&](int r, int k_) { return sm.mm[k_ * PC + 16 * ib + r]; },
-          [&](int k_, int cc) { return sm.o[k_ * PO + 16 * cb + cc]; }, lane);
+          [&](int k_, int cc) { return bf2f(O[k_ * POB + 16 * cb + cc]); }, lane);
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) sm.x[(16 * ib + 4 * lg + ii) * PO + 16 * cb + lr] = acc[ii];
+      for (int ii = 0; ii < 4; ++ii) P[(16 * ib + 4 * lg + ii) * PO + 16 * cb + lr] = acc[ii];
     }
     __syncthreads();
-    solve_upper<PO>(sm.lm, sm.tb, sm.x, 4, wave, lane);
+    solve_upper<PO>(sm.lm, sm.tb, P, 4, wave, lane);
     __syncthreads();
     {
       const int t = tid / 8, c8 = tid % 8 * 8;
       if (t < n) {
         f32x4* dst = reinterpret_cast<f32x4*>(a.dv_out + (tok0 + t0 + t) * dv + s0 + c8);
-        const float* xr = sm.x + t * PO + c8;
+        const float* xr = P + t * PO + c8;
         dst[0] = f32x4{xr[0], xr[1], xr[2], xr[3]};
         dst[1] = f32x4{xr[4], xr[5], xr[6], xr[7]};
       }
