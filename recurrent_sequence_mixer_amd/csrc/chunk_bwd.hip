@@ -1496,7 +1496,7 @@ struct SmemT {
   float G[CH], gam[CH], fn[CH], sg[CH];
 };
 
-template <int DK>
+template <int DK, int FUSE>
 __global__ __launch_bounds__(NT) void chunk_bwd_tiles_kernel(BwdArgs a) {
   using Sm = SmemT<DK>;
   constexpr int PK = Sm::PK, VS = Sm::VS, PH = Sm::PH;
@@ -1683,6 +1683,13 @@ __global__ __launch_bounds__(NT) void chunk_bwd_tiles_kernel(BwdArgs a) {
   const uint32_t* lmu = reinterpret_cast<const uint32_t*>(sm.lm);
   const uint32_t* mmu = reinterpret_cast<const uint32_t*>(sm.mm);
   float wend = 0.f;  // the chunk end's part of the W~ terms
+  // FUSE (KLA, GDN): the state part of dk and dw per (token, key channel) go
+  // to LDS, over the value-slice planes (no longer read), for the write
+  // gain's backward below; otherwise dk and dw_acc go to memory
+  constexpr int PSC = DK + 1;
+  static_assert(2 * CH * PSC * 4 <= offsetof(Sm, lm) - offsetof(Sm, Sh), "dk / dw scratch");
+  float* const scr_dk = reinterpret_cast<float*>(sm.Sh);
+  float* const scr_dw = scr_dk + CH * PSC;
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {  // unrolled: the accumulators stay in registers
     const int tile = wave + NW * k, tb_ = tile / ND, db = tile % ND;
@@ -1723,9 +1730,14 @@ __global__ __launch_bounds__(NT) void chunk_bwd_tiles_kernel(BwdArgs a) {
       const float g = sm.gam[t], f = sm.fn[t];
       const float wtw = f * wv * tw;
       if (ok) {
-        a.dk_out[gi] = fmaf(g, kh, ask[ii]);
         a.dq_out[gi] = fmaf(g, qh, asq[ii]);
-        a.dw_acc[gi] = fmaf(f, tw, asw[ii]);
+        if constexpr (FUSE != FUSE_NONE) {
+          scr_dk[t * PSC + d] = fmaf(g, kh, ask[ii]);
+          scr_dw[t * PSC + d] = fmaf(f, tw, asw[ii]);
+        } else {
+          a.dk_out[gi] = fmaf(g, kh, ask[ii]);
+          a.dw_acc[gi] = fmaf(f, tw, asw[ii]);
+        }
         wend += wtw;
       }
       const float row = row16_sum(ok ? g * (kv * kh + qv * qh) - wtw : 0.f);
@@ -1735,9 +1747,70 @@ __global__ __launch_bounds__(NT) void chunk_bwd_tiles_kernel(BwdArgs a) {
   wend = wave_total(wend);
   if (lane == 0) atomicAdd(&sm.sg[CH - 1], wend);
   __syncthreads();
-  // dL/dG of the chunk's tokens; the padding tokens of a partial chunk share
-  // the last real token's decay
-  if (tid < CH) {
+  if constexpr (FUSE != FUSE_NONE) {
+    // the write gain's backward (as gain_bwd_tok_kernel): DK / 16 threads
+    // per token, 16 key channels each; k . dw and ||k||^2 summed over those
+    // lanes.  KLA: w = beta k, beta = eta / (||k||^2 + eps); GDN: w = eta k.
+    // (DK 64: threads past the chunk's 64 tokens read its last row, write
+    // nothing)
+    constexpr int TPT = DK / 16;
+    static_assert(NT / TPT >= CH, "a thread group per token");
+    const int t = tid / TPT, d0 = tid % TPT * 16, tr = min(t, CH - 1);
+    float dkv[16], dwv[16], kv[16];
+    float db = 0.f, n2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      kv[j] = kf(tr, d0 + j);
+      dkv[j] = scr_dk[tr * PSC + d0 + j];
+      dwv[j] = scr_dw[tr * PSC + d0 + j];
+      db = fmaf(dwv[j], kv[j], db);
+      n2 = fmaf(kv[j], kv[j], n2);
+    }
+#pragma unroll
+    for (int m = 1; m < TPT; m <<= 1) {
+      db += __shfl_xor(db, m);
+      n2 += __shfl_xor(n2, m);
+    }
+    if (t < n) {
+      const long ti = tok0 + t0 + t;
+      const float et = a.g.eta[ti];
+      float deta;
+      if constexpr (FUSE == FUSE_KLA) {
+        const float den = n2 + a.g.eps, beta = et / den, g2 = db * (-et / (den * den));
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dkv[j] = fmaf(beta, dwv[j], fmaf(2.f * kv[j], g2, dkv[j]));
+        deta = db / den;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dkv[j] = fmaf(et, dwv[j], dkv[j]);
+        deta = db;
+      }
+      f32x4* dst = reinterpret_cast<f32x4*>(a.dk_out + ti * DK + d0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[j] = f32x4{dkv[4 * j], dkv[4 * j + 1], dkv[4 * j + 2], dkv[4 * j + 3]};
+      if (d0 == 0) a.deta[ti] = deta;
+    }
+    // dL/dalpha_t = (sum of dL/dG_j over the chunk's j >= t) / alpha_t: lane
+    // l of wavefront 0 takes token n - 1 - l, so that its prefix sum over the
+    // lanes is the suffix sum over the tokens; the padding tokens of a
+    // partial chunk share the last real token's decay
+    if (tid < CH) {
+      const int tt = n - 1 - tid;
+      float tail = 0.f;
+      if (tid == 0)
+        for (int u = n; u < CH; ++u) tail += sm.sg[u];
+      float sfx = tt >= 0 ? sm.sg[tt] + tail : 0.f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(sfx, off);
+        if (lane >= off) sfx += y;
+      }
+      if (tt >= 0)
+        a.dalpha[tok0 + t0 + tt] = sfx / static_cast<const float*>(a.g.alpha)[tok0 + t0 + tt];
+    }
+  } else if (tid < CH) {
+    // dL/dG of the chunk's tokens; the padding tokens of a partial chunk share
+    // the last real token's decay
     const float v = sm.sg[tid];
     float tail = 0.f;
     if (tid == n - 1)
@@ -2144,7 +2217,10 @@ static hipError_t launch_bwd_split_t(const BwdArgs& a, hipStream_t st, int part)
     }
     return launch_lds<bwd::SmemS<DK>>(bwd::chunk_bwd_ds_kernel<DK, false>, nv, a, st, bwd::NTS);
   }
-  return launch_lds<bwd::SmemT<DK>>(bwd::chunk_bwd_tiles_kernel<DK>, static_cast<unsigned>(bh * nch), a, st);
+  const unsigned gt = static_cast<unsigned>(bh * nch);
+  if (a.fuse_gain == FUSE_KLA) return launch_lds<bwd::SmemT<DK>>(bwd::chunk_bwd_tiles_kernel<DK, FUSE_KLA>, gt, a, st);
+  if (a.fuse_gain == FUSE_GDN) return launch_lds<bwd::SmemT<DK>>(bwd::chunk_bwd_tiles_kernel<DK, FUSE_GDN>, gt, a, st);
+  return launch_lds<bwd::SmemT<DK>>(bwd::chunk_bwd_tiles_kernel<DK, FUSE_NONE>, gt, a, st);
 }
 
 hipError_t launch_chunk_bwd_split(const BwdArgs& a, hipStream_t st, int part) {

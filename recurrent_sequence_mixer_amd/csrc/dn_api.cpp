@@ -1227,7 +1227,16 @@ DN_EXPORT int dn_chunk_bwd(const dn_desc* d, const void* q, const void* k, const
     // reads the checkpoints
     if (dn::launch_chunk_bwd_split(b, s, 1) != hipSuccess) return DN_ERR_HIP;
     if (ss && hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return DN_ERR_HIP;
+    // KLA and GDN: the tile kernel also runs the write gain's and the decay's
+    // backward (no per-token statistic; dk, deta and dalpha final there)
+    const bool fuse = d->gain == DN_GAIN_KLA || d->gain == DN_GAIN_GDN;
+    if (fuse) {
+      b.fuse_gain = d->gain == DN_GAIN_KLA ? dn::FUSE_KLA : dn::FUSE_GDN;
+      b.deta = gr->deta;
+      b.dalpha = gr->dalpha;
+    }
     if (dn::launch_chunk_bwd_split(b, s, 2) != hipSuccess) return DN_ERR_HIP;
+    if (fuse) return DN_OK;
   } else if (dn::launch_chunk_bwd_state(b, d->io == DN_BF16, chan, s) != hipSuccess) {
     return DN_ERR_HIP;
   }

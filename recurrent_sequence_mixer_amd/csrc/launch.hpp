@@ -140,6 +140,7 @@ struct GainPrepArgs {
 // are accumulated over value slices and must start at zero; dv [B, H, T, dv]
 // and dS0 (nullable) are written.  Workspace: the state entering every chunk
 // S_ck [B, H, nch, dk, dv] and the residuals E [B, H, T, dv].
+enum BwdFuse { FUSE_NONE = 0, FUSE_KLA = 1, FUSE_GDN = 2 };
 struct BwdArgs {
   int B, H, T, dk, dv;
   // S_ck and E already hold the forward's checkpoints (written by the
@@ -173,6 +174,13 @@ struct BwdArgs {
   float* segA = nullptr;
   float* segB = nullptr;
   float* seg_in = nullptr;
+  // the split path's tile kernel runs the write gain's backward itself
+  // (FUSE_KLA or FUSE_GDN; FUSE_NONE: it writes dk and dw_acc for
+  // launch_gain_bwd): dk final, deta and dalpha written there, dw_acc and dG
+  // not
+  int fuse_gain = 0;
+  float* deta = nullptr;
+  float* dalpha = nullptr;
 };
 hipError_t launch_chunk_bwd_state(const BwdArgs& a, int io_bf16, bool channel, hipStream_t st);
 // bf16 io, scalar decay, S_ck and E written by the forward chunk kernel, dv a
