@@ -390,7 +390,10 @@ typedef struct dn_grads {
  *   (DN_ERR_ALIAS).  dmu_log is summed over the batch rows with atomic
  *   additions: its last bits may vary from run to run, as may those of dq,
  *   dk, dw and dalpha (summed over value-column slices, or on the bf16
- *   scalar-decay path through shared-memory atomic additions). */
+ *   scalar-decay path through shared-memory atomic additions; there, for
+ *   KLA and GDN, the kernel that forms dk also runs the gain's and the
+ *   decay's backward, and the write vectors' and decay's gradients in the
+ *   workspace are left unwritten). */
 size_t dn_chunk_bwd_workspace(const dn_desc* desc);
 int dn_chunk_bwd(const dn_desc* desc, const void* q, const void* k, const void* v,
                  const dn_gates* gates, const float* S0, const float* aux0, const void* dO,
